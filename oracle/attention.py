@@ -1,0 +1,83 @@
+"""Exact attention in float64: the result the quantized path approximates.
+
+SageAttention is used as a drop-in replacement for FlashAttention (podcast
+notes, section "37:54 One line of code, twice the speed"), and FlashAttention
+computes exact softmax attention.  So the reference is the plain definition
+
+    O = softmax(Q K^T * sm_scale + M) V,   M[i,j] = 0 if visible else -inf,
+
+evaluated entirely in float64 with no quantization.
+
+Mask.  Streaming generation produces a video frame by frame under a causal
+attention mask, each frame attending to the condition and to earlier frames
+through a KV cache (Vidu S1 blog, sections "模型架构" and "训练方法"; podcast
+notes on the KV cache of streaming diffusion).  The reading taken here is the
+frame-block-causal mask: with frame length F > 0, query token i (absolute
+position q_pos0[b] + i) sees key j iff j < kv_len[b] and
+floor(j / F) <= floor((q_pos0[b] + i) / F) -- every earlier frame and all of
+its own frame.  F = 0 means full (non-causal) attention over kv_len[b] keys.
+"""
+
+import numpy as np
+
+
+def row_end(i_rows, kv_len_b, q_pos0_b, frame_len):
+    """Exclusive end of the visible key range of each query row.
+
+    The frame-block-causal mask makes every row's visible set a prefix
+    [0, end) of the keys: end = min(kv_len, (floor((q_pos0+i)/F) + 1) * F).
+    """
+    i = np.asarray(i_rows, dtype=np.int64)
+    if frame_len == 0:
+        return np.full(i.shape, int(kv_len_b), dtype=np.int64)
+    f = (int(q_pos0_b) + i) // int(frame_len)
+    return np.minimum(int(kv_len_b), (f + 1) * int(frame_len))
+
+
+def visible(i_rows, Nkv, kv_len_b, q_pos0_b, frame_len):
+    """Boolean [len(i_rows), Nkv]: the mask of the frame-block-causal rule."""
+    i = np.asarray(i_rows, dtype=np.int64)
+    j = np.arange(Nkv, dtype=np.int64)
+    vis = np.broadcast_to(j[None, :] < int(kv_len_b), (i.shape[0], Nkv)).copy()
+    if frame_len:
+        fq = (int(q_pos0_b) + i) // int(frame_len)
+        vis = vis & ((j[None, :] // int(frame_len)) <= fq[:, None])
+    return vis
+
+
+def default_q_pos0(Nq, kv_len, frame_len):
+    """Absent an explicit q_pos0, the query chunk is the tail of the keys."""
+    kv = np.asarray(kv_len, dtype=np.int64)
+    if frame_len == 0:
+        return np.zeros_like(kv)
+    return kv - int(Nq)
+
+
+def attention_fp64(Q, K, V, sm_scale=None, frame_len=0, kv_len=None,
+                   q_pos0=None, rows=None):
+    """softmax(Q K^T * sm_scale + M) V in float64 for the selected rows.
+
+    Q [B,H,Nq,d], K and V [B,H,Nkv,d] (any float dtype; widened exactly).
+    rows: indices of the query rows to compute (all when None).
+    Returns float64 [B,H,len(rows),d].
+    """
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    B, H, Nq, d = Q.shape
+    Nkv = K.shape[2]
+    scale = 1.0 / np.sqrt(d) if sm_scale is None else float(sm_scale)
+    kv = np.full(B, Nkv, np.int64) if kv_len is None else np.asarray(kv_len, np.int64)
+    qp = default_q_pos0(Nq, kv, frame_len) if q_pos0 is None else np.asarray(q_pos0, np.int64)
+    rows = np.arange(Nq) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = np.empty((B, H, len(rows), d), dtype=np.float64)
+    for b in range(B):
+        vis = visible(rows, Nkv, kv[b], qp[b], frame_len)
+        for h in range(H):
+            s = (Q[b, h, rows, :] @ K[b, h].T) * scale
+            s = np.where(vis, s, -np.inf)
+            s = s - np.max(s, axis=1, keepdims=True)
+            w = np.exp(s)
+            w = w / np.sum(w, axis=1, keepdims=True)
+            out[b, h] = w @ V[b, h]
+    return out

@@ -1,0 +1,194 @@
+"""Quantized attention, emulated on the CPU step by step.
+
+The pages describe SageAttention only as low-bit quantized attention that
+keeps the output of the FlashAttention it replaces ("37:54 One line of code,
+twice the speed"; "02:48 There were clearly faster compute units on the
+hardware").  This module is the library's own stated algorithm, written out so
+that each rounding the GPU performs happens here in the same precision:
+
+Given the INT8 codes and scales of ``quant`` (and V^, the P.V operand:
+V itself in 16-bit mode, or its dequantized FP8 codes), for every query row i
+of head (b,h), with state m = -inf, l = 0, acc = 0, the keys are taken in
+chunks of BK = 64 (chunk t = keys [64t, 64t+64)), in ascending order:
+
+  1. S[i,j]   = sum_c qcode[i,c] * kcode[j,c]            (exact integers)
+  2. sigma    = fp32(sm_scale * log2 e);  qs = fp32(dq[i // 128] * sigma)
+     c_t      = fp32(qs * dk[t])             (log2-domain scale of chunk t)
+  3. tm       = max over visible j of fp32(S[i,j] * c_t)  (-inf if none)
+  4. lazy running max: if tm > fp32(m + TAU) the row adopts m' = tm and
+     rescales its state by alpha = exp2(fp32(m - m')) (0 when m = -inf);
+     otherwise m, l and acc are kept as they are.
+  5. x[i,j]   = fp32(S[i,j] * c_t - fp32(m - s))  with ONE rounding (an FMA),
+     s = 4 in FP8 mode, 0 in 16-bit mode;  p = fp32(2^x), 0 if not visible.
+  6. l       += sum_j p                      (unrounded p)
+  7. p~       = p rounded to the P.V operand type: e4m3fn in FP8 mode (where
+     p already carries the 2^s pre-scale), else the input's fp16/bf16
+  8. acc     += sum_j p~[i,j] * V^[j,:]
+Finally O[i] = acc / l; the 2^s pre-scale cancels in that ratio.  The output
+is rounded (RNE) to the input dtype.
+
+Because m only moves when a chunk maximum exceeds it by more than TAU, the
+exponent argument is at most TAU + s = 8, so p~ never exceeds 2^8 -- inside
+both e4m3fn (448) and the 16-bit types.
+
+Split-KV: when ``splits`` lists chunk ranges, each range runs steps 1-8 from a
+fresh state and the partial results are merged exactly (float64):
+M = max_s m_s, O = sum_s acc_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
+
+Accumulations (l, acc) are float64 here; the GPU keeps them in float32.  That,
+the GPU's hardware exp2 (within ~1 ulp) and the final division are the only
+places where the two may differ, all far below the acceptance tolerance.
+"""
+
+import numpy as np
+
+from .constants import BQ, BK, TAU, PSHIFT_FP8, PSHIFT_16, LOG2E, PV_16, PV_FP8
+from . import codecs
+from .fp32 import fma_f32
+from .attention import row_end, default_q_pos0
+
+_F32 = np.float32
+
+
+def log2_scale(sm_scale, d):
+    """sigma = fp32(float64(sm_scale) * log2 e); sm_scale 0/None -> 1/sqrt(d)."""
+    if not sm_scale:
+        sm_scale = float(_F32(1.0 / np.sqrt(d)))
+    return _F32(np.float64(_F32(sm_scale)) * LOG2E)
+
+
+def _run_rows(S_full, c_row, dk_bh, vis_end, Vhat_bh, chunk_lo, chunk_hi,
+              pv_mode, p_dtype, trace=None):
+    """Steps 1-8 over chunks [chunk_lo, chunk_hi) for a set of rows.
+
+    trace: optional list; receives the running max m after every chunk.
+    """
+    R = S_full.shape[0]
+    d = Vhat_bh.shape[1]
+    m = np.full(R, -np.inf, dtype=_F32)
+    l = np.zeros(R, dtype=np.float64)
+    acc = np.zeros((R, d), dtype=np.float64)
+    for t in range(chunk_lo, chunk_hi):
+        j0 = t * BK
+        j1 = min(j0 + BK, S_full.shape[1])
+        if j0 >= j1:
+            break
+        j = np.arange(j0, j1)
+        vis = j[None, :] < vis_end[:, None]
+        if not vis.any():
+            continue
+        c_t = (c_row * _F32(dk_bh[t])).astype(_F32)          # [R] fp32
+        S = S_full[:, j0:j1]
+        m, l, acc = _chunk_step(S, c_t, vis, m, l, acc, Vhat_bh[j0:j1], pv_mode, p_dtype)
+        if trace is not None:
+            trace.append(m.copy())
+    return m, l, acc
+
+
+def _chunk_step(S, c_t, vis, m, l, acc, Vc, pv_mode, p_dtype):
+    """Steps 3-8 for one chunk; c_t is per row (rows may span Q blocks)."""
+    shift = PSHIFT_FP8 if pv_mode == PV_FP8 else PSHIFT_16
+    c64 = c_t.astype(np.float64)[:, None]
+    logit = (S * c64).astype(_F32)
+    tm = np.where(vis, logit, -np.inf).max(axis=1).astype(_F32)
+    upd = tm > (m + _F32(TAU)).astype(_F32)
+    with np.errstate(invalid="ignore"):
+        diff = (m - tm).astype(_F32)
+    alpha = np.where(np.isneginf(m), _F32(0.0),
+                     np.exp2(np.where(upd, diff, _F32(0)).astype(np.float64)).astype(_F32))
+    alpha = np.where(upd, alpha, _F32(1.0)).astype(np.float64)
+    m = np.where(upd, tm, m).astype(_F32)
+    l = l * alpha
+    acc = acc * alpha[:, None]
+    # a row still at m = -inf has no visible key in this chunk; its p is 0
+    mref = np.where(np.isneginf(m), _F32(0.0), (m - _F32(shift)).astype(_F32)).astype(_F32)
+    x = fma_f32(S, np.broadcast_to(c_t[:, None], S.shape),
+                np.broadcast_to(-mref[:, None], S.shape))
+    p = np.exp2(x.astype(np.float64)).astype(_F32)
+    p = np.where(vis, p, _F32(0.0))
+    l = l + p.astype(np.float64).sum(axis=1)
+    if pv_mode == PV_FP8:
+        pt = codecs.round_e4m3(p.astype(np.float64))
+    else:
+        pt = codecs.round_to(p, p_dtype).astype(np.float64)
+    acc = acc + pt @ Vc
+    return m, l, acc
+
+
+def sage_attention_emulated(qcodes, dq, kcodes, dk, Vhat, pv_mode, dtype,
+                            sm_scale=None, frame_len=0, kv_len=None,
+                            q_pos0=None, rows=None, splits=None):
+    """Emulate the quantized attention for the selected query rows.
+
+    qcodes int8 [B,H,Nq,d], dq float32 [B,H,ceil(Nq/128)];
+    kcodes int8 [B,H,Nkv,d], dk float32 [B,H,ceil(Nkv/64)];
+    Vhat: the P.V right operand as exact values [B,H,Nkv,d] -- V (16-bit
+    mode) or dequant_v_fp8(...) (FP8 mode);  dtype: 'bf16' | 'f16' (input and
+    output type, and P's type in 16-bit mode).
+    splits: optional list of (chunk_lo, chunk_hi) ranges covering the keys.
+    Returns (O64 float64 [B,H,R,d], O rounded to dtype as float32).
+    """
+    qcodes = np.asarray(qcodes)
+    kcodes = np.asarray(kcodes)
+    B, H, Nq, d = qcodes.shape
+    Nkv = kcodes.shape[2]
+    sigma = log2_scale(sm_scale, d)
+    kv = np.full(B, Nkv, np.int64) if kv_len is None else np.asarray(kv_len, np.int64)
+    qp = default_q_pos0(Nq, kv, frame_len) if q_pos0 is None else np.asarray(q_pos0, np.int64)
+    rows = np.arange(Nq) if rows is None else np.asarray(rows, dtype=np.int64)
+    nchunks = -(-Nkv // BK)
+    if splits is None:
+        splits = [(0, nchunks)]
+    out = np.empty((B, H, len(rows), d), dtype=np.float64)
+    for b in range(B):
+        vis_end = row_end(rows, kv[b], qp[b], frame_len)
+        jmax = int(vis_end.max())
+        for h in range(H):
+            qs = (dq[b, h, rows // BQ].astype(_F32) * sigma).astype(_F32)   # [R]
+            S_full = qcodes[b, h, rows, :].astype(np.float64) @ \
+                kcodes[b, h, :jmax, :].astype(np.float64).T                # exact
+            Vh = np.asarray(Vhat[b, h, :jmax, :], dtype=np.float64)
+            parts = [_run_rows(S_full, qs, dk[b, h], vis_end, Vh, lo, hi, pv_mode, dtype)
+                     for (lo, hi) in splits]
+            ms = np.stack([p[0] for p in parts]).astype(np.float64)        # [P, R]
+            ls = np.stack([p[1] for p in parts])
+            accs = np.stack([p[2] for p in parts])
+            M = np.max(ms, axis=0)
+            w = np.where(np.isneginf(ms), 0.0, np.exp2(ms - M[None, :]))
+            L = np.sum(w * ls, axis=0)
+            out[b, h] = np.sum(w[:, :, None] * accs, axis=0) / L[:, None]
+    rounded = codecs.round_to(out.astype(_F32), dtype)
+    return out, rounded
+
+
+def scores_int(qcodes, kcodes):
+    """Exact integer scores S = qcodes . kcodes^T for one (b,h): int64 [Nq,Nkv].
+
+    Computed as a float64 matrix product of integer-valued operands, which is
+    exact because |S| <= 127^2 * d < 2^53.
+    """
+    q = np.asarray(qcodes, dtype=np.float64)
+    k = np.asarray(kcodes, dtype=np.float64)
+    return (q @ k.T).astype(np.int64)
+
+
+def emulate_from_inputs(Q, K, V, pv_mode, dtype, sm_scale=None, frame_len=0,
+                        kv_len=None, q_pos0=None, rows=None, splits=None,
+                        mu=None):
+    """Quantize the 16-bit inputs with ``quant`` and run the emulation."""
+    from . import quant
+    Qf = np.asarray(Q, dtype=np.float32)
+    Kf = np.asarray(K, dtype=np.float32)
+    Vf = np.asarray(V, dtype=np.float32)
+    if mu is None:
+        mu = quant.k_mean(Kf, kv_len)
+    a = quant.channel_shift(Qf, Kf, mu, kv_len)
+    qc, dq = quant.quantize_q(Qf, a)
+    kc, dk = quant.quantize_k(Kf, mu, kv_len, a)
+    if pv_mode == PV_FP8:
+        vc, ve, _ = quant.quantize_v_fp8(Vf, kv_len)
+        Vhat = quant.dequant_v_fp8(vc, ve)
+    else:
+        Vhat = Vf.astype(np.float64)
+    return sage_attention_emulated(qc, dq, kc, dk, Vhat, pv_mode, dtype, sm_scale,
+                                   frame_len, kv_len, q_pos0, rows, splits)

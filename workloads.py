@@ -1,0 +1,187 @@
+"""Seeded synthetic inputs shaped like video-DiT attention.
+
+This module only draws random numbers; it holds none of the quantized
+attention's arithmetic.  Both the CPU oracle (through the tests and the bench's
+CPU leg) and the HIP library consume what it produces.
+
+The pages' workloads are video-diffusion transformers: 5-second 480p/720p
+clips (TurboDiffusion digests on the reportify page) and a 540p frame-by-frame
+stream with a KV cache (Vidu S1 blog, sections "Infra" and "评测 benchmark").
+Their latents and models are not available, so these seeded Gaussian tensors
+stand in for them, with the token grids of such clips:
+
+  tiny     B1 H2  N 1024             d64  fp16  K += per-channel offset ~ N(0, 2^2)
+  small    B1 H12 N 32760 (21x30x52) d128 bf16  K += per-channel bias ~ N(0, 3)
+  large    B1 H40 N 75600 (21x45x80) d128 bf16  51 of the 40*128 (head, channel)
+                                                 K channels scaled x8 (1%)
+  stream   B1 H24 Nq 2040 (34x60 frame), Nkv 34680 = 16 cached frames + itself,
+           d128 bf16, frame-block-causal mask with F = 2040
+  batched  B8 H24 Nq 2040, each session's cache L_b ~ U{4..32} frames plus its
+           own frame (kv_len = (L_b+1)*2040), KV allocated for 33 frames,
+           d128 bf16, frame-block-causal, P.V in FP8
+
+Values are N(0,1) float32, then rounded to the 16-bit dtype.  Each (tensor,
+batch, head) slice has its own seed, so any subset of heads can be drawn on
+its own; the small per-config draws (offsets, outlier channels, cache
+lengths) use numpy's default_rng and do not depend on the device.
+"""
+
+import hashlib
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+FRAME = 2040  # tokens per 34x60 latent frame
+
+
+@dataclass
+class Workload:
+    name: str
+    B: int
+    H: int
+    Nq: int
+    Nkv: int
+    d: int
+    dtype: str                 # 'f16' | 'bf16'
+    pv_mode: int               # 0: 16-bit P.V, 1: FP8 P.V
+    frame_len: int = 0
+    kv_len: list = None        # per batch; None -> Nkv for all
+    q_pos0: list = None        # per batch; None -> default
+    seed: int = 0
+    k_offset_std: float = 0.0
+    outlier_frac: float = 0.0
+    outlier_gain: float = 8.0
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def torch_dtype(self):
+        return torch.float16 if self.dtype == "f16" else torch.bfloat16
+
+    def kv_lens(self):
+        return list(self.kv_len) if self.kv_len is not None else [self.Nkv] * self.B
+
+    def q_pos0s(self):
+        if self.q_pos0 is not None:
+            return list(self.q_pos0)
+        if self.frame_len == 0:
+            return [0] * self.B
+        return [kv - self.Nq for kv in self.kv_lens()]
+
+    def visible_pairs(self):
+        """Number of visible (query, key) pairs over all batches and heads."""
+        total = 0
+        for kv, qp in zip(self.kv_lens(), self.q_pos0s()):
+            i = np.arange(self.Nq, dtype=np.int64)
+            if self.frame_len:
+                end = np.minimum(kv, ((qp + i) // self.frame_len + 1) * self.frame_len)
+            else:
+                end = np.full(self.Nq, kv, dtype=np.int64)
+            total += int(end.sum())
+        return total * self.H
+
+    def ops(self):
+        """Algorithmic operations: 4*d per visible pair (QK^T and P.V)."""
+        return 4 * self.d * self.visible_pairs()
+
+
+def get(name, **override):
+    """The named workload (see module docstring), fields overridable."""
+    if name == "tiny":
+        w = Workload("tiny", 1, 2, 1024, 1024, 64, "f16", 0, seed=101, k_offset_std=2.0)
+    elif name == "small":
+        w = Workload("small", 1, 12, 32760, 32760, 128, "bf16", 0, seed=202,
+                     k_offset_std=float(np.sqrt(3.0)))
+    elif name == "large":
+        w = Workload("large", 1, 40, 75600, 75600, 128, "bf16", 0, seed=303,
+                     outlier_frac=0.01)
+    elif name == "stream":
+        w = Workload("stream", 1, 24, FRAME, 17 * FRAME, 128, "bf16", 0,
+                     frame_len=FRAME, kv_len=[17 * FRAME], q_pos0=[16 * FRAME], seed=404)
+    elif name == "batched":
+        L = np.random.default_rng(505).integers(4, 33, 8)
+        kv = [int((x + 1) * FRAME) for x in L]
+        w = Workload("batched", 8, 24, FRAME, 33 * FRAME, 128, "bf16", 1,
+                     frame_len=FRAME, kv_len=kv, q_pos0=[int(x * FRAME) for x in L],
+                     seed=505)
+    else:
+        raise KeyError(name)
+    for k, v in override.items():
+        setattr(w, k, v)
+    return w
+
+
+NAMES = ("tiny", "small", "large", "stream", "batched")
+
+
+def _slice_seed(seed, tensor, b, h):
+    s = hashlib.sha256(f"{seed}:{tensor}:{b}:{h}".encode()).digest()
+    return int.from_bytes(s[:8], "little") & ((1 << 63) - 1)
+
+
+def k_offsets(w):
+    """Per-(head, channel) K offsets [H, d] float32 (zeros if none)."""
+    if w.k_offset_std == 0:
+        return np.zeros((w.H, w.d), np.float32)
+    rng = np.random.default_rng(w.seed * 7 + 1)
+    return (rng.standard_normal((w.H, w.d)) * w.k_offset_std).astype(np.float32)
+
+
+def outlier_channels(w):
+    """Sorted flat (head*d + channel) indices of the scaled K channels."""
+    if w.outlier_frac == 0:
+        return np.zeros(0, np.int64)
+    n = int(round(w.outlier_frac * w.H * w.d))
+    rng = np.random.default_rng(w.seed * 7 + 2)
+    return np.sort(rng.choice(w.H * w.d, size=n, replace=False))
+
+
+def make(w, device="cpu", heads=None, batches=None, tensors="qkv"):
+    """Draw the inputs of workload ``w`` on ``device``.
+
+    Returns a dict with 'q' [B,H,Nq,d], 'k' and 'v' [B,H,Nkv,d] in the
+    workload's 16-bit dtype (only the requested tensors), restricted to the
+    given heads / batches when those are lists.  Key positions at or beyond
+    kv_len[b] are zero.
+    """
+    heads = list(range(w.H)) if heads is None else list(heads)
+    batches = list(range(w.B)) if batches is None else list(batches)
+    off = torch.from_numpy(k_offsets(w))
+    gain = torch.ones(w.H * w.d)
+    gain[torch.from_numpy(outlier_channels(w))] = w.outlier_gain
+    gain = gain.view(w.H, w.d)
+    kvl = w.kv_lens()
+    out = {}
+    for name in tensors:
+        n = w.Nq if name == "q" else w.Nkv
+        t = torch.empty((len(batches), len(heads), n, w.d), dtype=w.torch_dtype, device=device)
+        for bi, b in enumerate(batches):
+            for hi, h in enumerate(heads):
+                g = torch.Generator(device=device)
+                g.manual_seed(_slice_seed(w.seed, name, b, h))
+                x = torch.randn((n, w.d), generator=g, device=device, dtype=torch.float32)
+                if name == "k":
+                    x = x * gain[h].to(device) + off[h].to(device)
+                if name != "q" and kvl[b] < n:
+                    x[kvl[b]:] = 0
+                t[bi, hi] = x.to(w.torch_dtype)
+        out[name] = t
+    return out
+
+
+def sample_rows(w, R=512, seed=0):
+    """R query rows per (b,h) for sampled checks: always row 0, the last row,
+    rows on both sides of every 128-token Q block edge near the ends, and of
+    the frame edges; the rest drawn without replacement (seeded)."""
+    n = w.Nq
+    if R >= n:
+        return np.arange(n)
+    must = {0, n - 1, 127, 128, min(n - 1, 255), n - 128 if n > 128 else 0}
+    if w.frame_len:
+        for f in range(w.frame_len, n, w.frame_len):
+            must.update({f - 1, f})
+    must = sorted(x for x in must if 0 <= x < n)
+    rng = np.random.default_rng(seed)
+    rest = np.setdiff1d(np.arange(n), must)
+    pick = rng.choice(rest, size=max(0, R - len(must)), replace=False)
+    return np.sort(np.concatenate([np.asarray(must, np.int64), pick]))
