@@ -1,0 +1,176 @@
+"""Throughput of the quantized attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload large] [--pv 16|fp8]
+
+One step = one sage_attn_fwd call: the quantize pass (K mean, channel balance,
+INT8 Q/K codes and scales, V layout) plus the fused attention kernel, over the
+workload's whole batch, with the inputs already resident in HBM.  Prints ONE
+JSON line: TOPS = 4*d*(visible query-key pairs) / time, the roofline of the
+dominant kernel (the fused attention, timed with HIP events on its own stream)
+and the CPU oracle timed on a bounded sample of the same workload.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "quantized-attention TOPS (4·B·H·Nq·Nkv·d) + % of peak MFMA, 75.6k-token 720p shape"
+INT8_PEAK_TOPS = 5000.0   # MI355X dense INT8 MFMA, 5.0 POP/s
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="large")
+    p.add_argument("--pv", default=None, choices=["16", "fp8"])
+    p.add_argument("--cpu-heads", type=int, default=2, help="heads in the CPU oracle sample")
+    p.add_argument("--cpu-rows", type=int, default=256, help="query rows per head in the CPU sample")
+    p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--profile", action="store_true", help="few steps, no CPU leg (for rocprofv3)")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the path is "
+              "data-parallel over (batch, head) and needs no collectives; see DESIGN.md for sharding)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import bit_quantized_attention_sage_amd as sage
+    import workloads
+
+    sage.load()
+    w = workloads.get(args.workload)
+    if args.pv is not None:
+        w.pv_mode = 1 if args.pv == "fp8" else 0
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x = workloads.make(w, dev)
+    q, k, v = x["q"], x["k"], x["v"]
+    o = torch.empty_like(q)
+    desc = sage.Desc.for_tensors(q, k, v, o, pv_mode=w.pv_mode, frame_len=w.frame_len,
+                                 kv_len=w.kv_len, q_pos0=w.q_pos0)
+    ws = sage.new_workspace(desc, dev)
+    bufs = sage.sage_attn_quant_layout(desc, ws)
+    stream = torch.cuda.current_stream()
+    steps = 2 if args.profile else args.steps
+    warm = 1 if args.profile else args.warmup
+    # one step = the whole path (same work as sage_attn_fwd), with HIP events on
+    # the launch stream around each of its two parts
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+
+    def step(i=None):
+        if i is not None:
+            ev[i][0].record(stream)
+        sage.sage_attn_quantize(desc, q, k, v, bufs, stream)
+        if i is not None:
+            ev[i][1].record(stream)
+        sage.sage_attn_fwd_quantized(desc, bufs, o, stream)
+        if i is not None:
+            ev[i][2].record(stream)
+
+    for _ in range(warm):
+        step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        step(i)
+    end.record(stream)
+    end.synchronize()
+    ms_step = start.elapsed_time(end) / steps
+    ms_quant = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    ms_attn = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    ops = w.ops()
+    tops = ops / (ms_step * 1e-3) / 1e12
+
+    splits = sage.sage_attn_kv_splits(desc)
+    attn_tops = ops / (ms_attn * 1e-3) / 1e12
+    # quantize pass algorithmic bytes: read Q, K twice (statistics, then codes),
+    # V once; write Q/K codes, V layout (16-bit or e4m3) and scales
+    esz = 2
+    nq = w.B * w.H * w.Nq * w.d
+    nk = w.B * w.H * w.Nkv * w.d
+    vbytes = nk * (1 if w.pv_mode == 1 else 2)
+    qbytes = 2 * nq * esz + 2 * nk * esz + nk * esz + nq + nk + vbytes
+    record = {
+        "metric": METRIC,
+        "value": round(tops, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8+fp8" if w.pv_mode == 1 else ("int8+" + w.dtype),
+        "data": "synthetic (seeded Gaussian, video-DiT token grid)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nkv": w.Nkv, "d": w.d,
+                   "in_dtype": w.dtype, "pv": "fp8" if w.pv_mode == 1 else "16",
+                   "frame_len": w.frame_len, "kv_splits": splits,
+                   "ops_per_step": ops, "pct_int8_peak": round(100 * tops / INT8_PEAK_TOPS, 2)},
+        "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel", "achieved": round(attn_tops, 2),
+                     "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s", "frac": round(attn_tops / INT8_PEAK_TOPS, 4),
+                     "traffic": None, "ms_per_launch": round(ms_attn, 4)},
+        "quantize": {"ms": round(ms_quant, 4), "algorithmic_bytes": qbytes,
+                     "GB_per_s": round(qbytes / (ms_quant * 1e-3) / 1e9, 1),
+                     "hbm_frac": round(qbytes / (ms_quant * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+    }
+    if not args.no_cpu and not args.profile:
+        record["cpu_baseline"], record["parity"] = cpu_leg(w, x, o, desc, args, sage, torch)
+    print(json.dumps(record), flush=True)
+
+
+def cpu_leg(w, x, o, desc, args, sage, torch):
+    """Time the oracle (as it stands) on a bounded sample of the same workload,
+    and compare the GPU output on the same rows."""
+    from threadpoolctl import threadpool_info
+    from oracle import emulate, attention
+    import workloads
+
+    heads = list(range(min(args.cpu_heads, w.H)))
+    rows = workloads.sample_rows(w, args.cpu_rows)
+    S = sage.sage_attn_kv_splits(desc)
+    b = 0
+    Q = x["q"][b:b + 1, heads].float().cpu().numpy()
+    K = x["k"][b:b + 1, heads].float().cpu().numpy()
+    V = x["v"][b:b + 1, heads].float().cpu().numpy()
+    kv = [w.kv_lens()[b]]
+    qp = [w.q_pos0s()[b]]
+    n = -(-kv[0] // 64)
+    splits = [(s * n // S, (s + 1) * n // S) for s in range(S)] if S > 1 else None
+    t0 = time.perf_counter()
+    o64, _ = emulate.emulate_from_inputs(Q, K, V, w.pv_mode, w.dtype, frame_len=w.frame_len, kv_len=kv,
+                                         q_pos0=qp, rows=rows, splits=splits)
+    t_cpu = time.perf_counter() - t0
+    ref = attention.attention_fp64(Q, K, V, frame_len=w.frame_len, kv_len=kv, q_pos0=qp, rows=rows)
+    og = o[b:b + 1, heads][:, :, rows].float().cpu().numpy()
+    i = np.asarray(rows)
+    ends = np.minimum(kv[0], ((qp[0] + i) // w.frame_len + 1) * w.frame_len) if w.frame_len else np.full(len(i), kv[0])
+    sample_ops = 4 * w.d * int(ends.sum()) * len(heads)
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    cos = float((og * ref).sum() / np.sqrt((og ** 2).sum() * (ref ** 2).sum()))
+    cpu = {"value": round(sample_ops / t_cpu / 1e12, 6), "unit": "TOPS", "cores": threads, "kind": "oracle",
+           "sample": f"batch 0, heads {heads[0]}..{heads[-1]}, {len(rows)} query rows each "
+                     f"(all keys), quantize + emulated attention, {t_cpu:.1f} s"}
+    parity = {"rows": len(rows) * len(heads), "max_abs_vs_emulation": float(np.abs(og - o64).max()),
+              "cosine_vs_fp64": round(cos, 6)}
+    return cpu, parity
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,268 @@
+"""Python binding of libsage_attn.so: argument marshalling only.
+
+Every step of the quantized attention runs in the HIP kernels behind the C ABI
+declared in include/sage_attn.h; this module only turns torch tensors (device
+memory and streams) into the plain pointers and sizes that ABI takes.  There
+is no fallback: when the library is missing, every call raises.
+
+Functions named like the C entry points take the same arguments (a
+``Desc`` in place of ``const sage_attn_desc*``).  ``attention`` is the
+one-line drop-in for exact attention (the pages' "one line of code" swap, in
+the podcast notes' section "37:54 One line of code, twice the speed").
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsage_attn.so")
+
+SAGE_ATTN_ABI_VERSION = 1
+SAGE_F16, SAGE_BF16 = 0, 1
+SAGE_PV_16, SAGE_PV_FP8 = 0, 1
+SAGE_FLAG_DEBUG_SYNC = 0x1
+SAGE_MAX_BATCH = 128
+STATUS = {0: "SAGE_OK", 1: "SAGE_E_NULL", 2: "SAGE_E_SHAPE", 3: "SAGE_E_DTYPE", 4: "SAGE_E_STRIDE",
+          5: "SAGE_E_ALIGN", 6: "SAGE_E_MASK", 7: "SAGE_E_UNSUPPORTED", 8: "SAGE_E_WORKSPACE",
+          9: "SAGE_E_VERSION", 10: "SAGE_E_HIP"}
+
+_i64x3 = ctypes.c_int64 * 3
+
+
+class sage_attn_desc(ctypes.Structure):
+    _fields_ = [("abi_version", ctypes.c_int32), ("dtype", ctypes.c_int32), ("pv_mode", ctypes.c_int32),
+                ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("Nq", ctypes.c_int32),
+                ("Nkv", ctypes.c_int32), ("d", ctypes.c_int32), ("frame_len", ctypes.c_int32),
+                ("kv_splits", ctypes.c_int32), ("sm_scale", ctypes.c_float), ("flags", ctypes.c_uint32),
+                ("q_stride", _i64x3), ("k_stride", _i64x3), ("v_stride", _i64x3), ("o_stride", _i64x3),
+                ("kv_len", ctypes.POINTER(ctypes.c_int32)), ("q_pos0", ctypes.POINTER(ctypes.c_int32)),
+                ("k_mean_in", ctypes.c_void_p)]
+
+
+class sage_quant_bufs(ctypes.Structure):
+    _fields_ = [("q_codes", ctypes.c_void_p), ("q_scale", ctypes.c_void_p), ("k_codes", ctypes.c_void_p),
+                ("k_scale", ctypes.c_void_p), ("k_mean", ctypes.c_void_p), ("chan_shift", ctypes.c_void_p),
+                ("v_t", ctypes.c_void_p), ("v_e8m0", ctypes.c_void_p), ("stats", ctypes.c_void_p),
+                ("partial", ctypes.c_void_p)]
+
+
+class SageError(RuntimeError):
+    def __init__(self, status, fn, detail):
+        super().__init__(f"{fn}: {STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+_lib = None
+_DESC_P = ctypes.POINTER(sage_attn_desc)
+_BUFS_P = ctypes.POINTER(sage_quant_bufs)
+
+
+def load(path=None):
+    """Load the HIP library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m bit_quantized_attention_sage_amd.build`")
+    lib = ctypes.CDLL(path)
+    sig = {
+        "sage_attn_abi_version": (ctypes.c_int, []),
+        "sage_attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "sage_attn_last_error": (ctypes.c_char_p, []),
+        "sage_attn_constant": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double)]),
+        "sage_attn_kv_splits": (ctypes.c_int, [_DESC_P, ctypes.POINTER(ctypes.c_int32)]),
+        "sage_attn_workspace_size": (ctypes.c_int, [_DESC_P, ctypes.POINTER(ctypes.c_size_t)]),
+        "sage_attn_quant_layout": (ctypes.c_int, [_DESC_P, ctypes.c_void_p, ctypes.c_size_t, _BUFS_P]),
+        "sage_attn_quantize": (ctypes.c_int, [_DESC_P, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                              _BUFS_P, ctypes.c_void_p]),
+        "sage_attn_fwd_quantized": (ctypes.c_int, [_DESC_P, _BUFS_P, ctypes.c_void_p, ctypes.c_void_p]),
+        "sage_attn_fwd": (ctypes.c_int, [_DESC_P, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+        "sage_attn_debug_scores": (ctypes.c_int, [_DESC_P, _BUFS_P, ctypes.POINTER(ctypes.c_int32),
+                                                  ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]),
+        "sage_attn_debug_convert": (ctypes.c_int, [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                                   ctypes.c_int64, ctypes.c_void_p]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    if lib.sage_attn_abi_version() != SAGE_ATTN_ABI_VERSION:
+        raise RuntimeError("libsage_attn.so ABI version mismatch")
+    _lib = lib
+    return lib
+
+
+def _check(status, fn):
+    if status != 0:
+        raise SageError(status, fn, load().sage_attn_last_error().decode())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+class Desc:
+    """A sage_attn_desc plus the host arrays it points to (kept alive here)."""
+
+    def __init__(self, B, H, Nq, Nkv, d, dtype, pv_mode=SAGE_PV_16, frame_len=0, kv_len=None,
+                 q_pos0=None, sm_scale=0.0, kv_splits=0, flags=0, k_mean_in=None,
+                 q_stride=None, k_stride=None, v_stride=None, o_stride=None):
+        c = sage_attn_desc()
+        c.abi_version = SAGE_ATTN_ABI_VERSION
+        c.dtype = dtype
+        c.pv_mode = pv_mode
+        c.B, c.H, c.Nq, c.Nkv, c.d = B, H, Nq, Nkv, d
+        c.frame_len = frame_len
+        c.kv_splits = kv_splits
+        c.sm_scale = sm_scale
+        c.flags = flags
+        c.q_stride = _i64x3(*(q_stride or (H * Nq * d, Nq * d, d)))
+        c.k_stride = _i64x3(*(k_stride or (H * Nkv * d, Nkv * d, d)))
+        c.v_stride = _i64x3(*(v_stride or (H * Nkv * d, Nkv * d, d)))
+        c.o_stride = _i64x3(*(o_stride or (H * Nq * d, Nq * d, d)))
+        self._kv = (ctypes.c_int32 * B)(*kv_len) if kv_len is not None else None
+        self._qp = (ctypes.c_int32 * B)(*q_pos0) if q_pos0 is not None else None
+        c.kv_len = ctypes.cast(self._kv, ctypes.POINTER(ctypes.c_int32)) if self._kv else None
+        c.q_pos0 = ctypes.cast(self._qp, ctypes.POINTER(ctypes.c_int32)) if self._qp else None
+        self._k_mean_in = k_mean_in
+        c.k_mean_in = k_mean_in.data_ptr() if k_mean_in is not None else None
+        self.c = c
+        self.B, self.H, self.Nq, self.Nkv, self.d = B, H, Nq, Nkv, d
+        self.dtype, self.pv_mode, self.frame_len = dtype, pv_mode, frame_len
+        self.Nq_pad = (Nq + 127) // 128 * 128
+        self.Nkv_pad = (Nkv + 127) // 128 * 128
+
+    @property
+    def ptr(self):
+        return ctypes.byref(self.c)
+
+    @classmethod
+    def for_tensors(cls, q, k, v, o=None, **kw):
+        """Describe [B,H,N,d] tensors (channel dim contiguous, any b/h/n strides)."""
+        B, H, Nq, d = q.shape
+        Nkv = k.shape[2]
+        for t in (q, k, v) + ((o,) if o is not None else ()):
+            if t.stride(3) != 1:
+                raise ValueError("the channel dimension must be contiguous")
+        if q.dtype not in (torch.float16, torch.bfloat16):
+            raise ValueError("q, k, v must be float16 or bfloat16")
+        dt = SAGE_F16 if q.dtype == torch.float16 else SAGE_BF16
+        st = lambda t: tuple(t.stride()[:3])  # noqa: E731
+        return cls(B, H, Nq, Nkv, d, dt, q_stride=st(q), k_stride=st(k), v_stride=st(v),
+                   o_stride=st(o) if o is not None else None, **kw)
+
+
+def sage_attn_constant(name):
+    v = ctypes.c_double()
+    _check(load().sage_attn_constant(name.encode(), ctypes.byref(v)), "sage_attn_constant")
+    return v.value
+
+
+def sage_attn_kv_splits(desc):
+    s = ctypes.c_int32()
+    _check(load().sage_attn_kv_splits(desc.ptr, ctypes.byref(s)), "sage_attn_kv_splits")
+    return s.value
+
+
+def sage_attn_workspace_size(desc):
+    n = ctypes.c_size_t()
+    _check(load().sage_attn_workspace_size(desc.ptr, ctypes.byref(n)), "sage_attn_workspace_size")
+    return n.value
+
+
+def sage_attn_quant_layout(desc, ws):
+    b = sage_quant_bufs()
+    _check(load().sage_attn_quant_layout(desc.ptr, ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(),
+                                         ctypes.byref(b)), "sage_attn_quant_layout")
+    return b
+
+
+def sage_attn_quantize(desc, q, k, v, bufs, stream=None):
+    _check(load().sage_attn_quantize(desc.ptr, ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+                                     ctypes.c_void_p(v.data_ptr()), ctypes.byref(bufs), _stream(stream)),
+           "sage_attn_quantize")
+
+
+def sage_attn_fwd_quantized(desc, bufs, o, stream=None):
+    _check(load().sage_attn_fwd_quantized(desc.ptr, ctypes.byref(bufs), ctypes.c_void_p(o.data_ptr()),
+                                          _stream(stream)), "sage_attn_fwd_quantized")
+
+
+def sage_attn_fwd(desc, q, k, v, o, ws, stream=None):
+    _check(load().sage_attn_fwd(desc.ptr, ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+                                ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(o.data_ptr()),
+                                ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(), _stream(stream)),
+           "sage_attn_fwd")
+
+
+def sage_attn_debug_scores(desc, bufs, tiles, out, stream=None):
+    """tiles: list of (b*H + h, q0, k0); out: int32 device tensor [n, 32, 64]."""
+    flat = [int(x) for t in tiles for x in t]
+    arr = (ctypes.c_int32 * max(1, len(flat)))(*flat)
+    _check(load().sage_attn_debug_scores(desc.ptr, ctypes.byref(bufs), arr, len(tiles),
+                                         ctypes.c_void_p(out.data_ptr()), _stream(stream)),
+           "sage_attn_debug_scores")
+
+
+def sage_attn_debug_convert(kind, x, out, stream=None):
+    _check(load().sage_attn_debug_convert(kind, ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                                          x.numel(), _stream(stream)), "sage_attn_debug_convert")
+
+
+def new_workspace(desc, device="cuda"):
+    """A device workspace of the size sage_attn_fwd needs (256-byte aligned)."""
+    n = sage_attn_workspace_size(desc)
+    ws = torch.empty(n + 256, dtype=torch.uint8, device=device)
+    off = (-ws.data_ptr()) % 256
+    return ws[off:off + n]
+
+
+def quant_views(desc, ws, bufs):
+    """Torch views of the quantized operands inside workspace ``ws``."""
+    base = ws.data_ptr()
+    B, H, d = desc.B, desc.H, desc.d
+
+    def view(ptr, n, dtype, shape):
+        off = ptr - base
+        esz = torch.empty(0, dtype=dtype).element_size()
+        return ws[off:off + n * esz].view(dtype).view(*shape)
+
+    fp8 = desc.pv_mode == SAGE_PV_FP8
+    out = {
+        "q_codes": view(bufs.q_codes, B * H * desc.Nq_pad * d, torch.int8, (B, H, desc.Nq_pad, d)),
+        "q_scale": view(bufs.q_scale, B * H * desc.Nq_pad // 128, torch.float32, (B, H, desc.Nq_pad // 128)),
+        "k_codes": view(bufs.k_codes, B * H * desc.Nkv_pad * d, torch.int8, (B, H, desc.Nkv_pad, d)),
+        "k_scale": view(bufs.k_scale, B * H * desc.Nkv_pad // 64, torch.float32, (B, H, desc.Nkv_pad // 64)),
+        "k_mean": view(bufs.k_mean, B * H * d, torch.float32, (B, H, d)),
+        "chan_shift": view(bufs.chan_shift, B * H * d, torch.int8, (B, H, d)),
+        "v_t": view(bufs.v_t, B * H * desc.Nkv_pad * d, torch.uint8 if fp8 else torch.int16,
+                    (B, H, desc.Nkv_pad // 64, d, 64)),
+    }
+    if fp8:
+        out["v_e8m0"] = view(bufs.v_e8m0, B * H * desc.Nkv_pad // 32 * d, torch.uint8,
+                             (B, H, desc.Nkv_pad // 32, d))
+    return out
+
+
+def attention(q, k, v, pv_mode=SAGE_PV_16, frame_len=0, kv_len=None, q_pos0=None, sm_scale=0.0,
+              kv_splits=0, k_mean_in=None, out=None, workspace=None, stream=None):
+    """Quantized attention on [B,H,N,d] fp16/bf16 device tensors; returns O.
+
+    A drop-in for softmax(Q K^T * sm_scale) V with an optional
+    frame-block-causal mask (frame_len > 0) against a KV cache of kv_len[b]
+    valid keys.  Allocates the output and workspace with torch when not given.
+    """
+    if out is None:
+        out = torch.empty_like(q)
+    desc = Desc.for_tensors(q, k, v, out, pv_mode=pv_mode, frame_len=frame_len, kv_len=kv_len,
+                            q_pos0=q_pos0, sm_scale=sm_scale, kv_splits=kv_splits, k_mean_in=k_mean_in)
+    ws = workspace if workspace is not None else new_workspace(desc, q.device)
+    sage_attn_fwd(desc, q, k, v, out, ws, stream)
+    return out

@@ -1,0 +1,393 @@
+// C ABI of the quantized attention library: argument validation, workspace
+// layout, launch planning.  Host code only; every kernel is enqueued on the
+// caller's stream and nothing here allocates or synchronizes (unless
+// SAGE_FLAG_DEBUG_SYNC is set).  See include/sage_attn.h for the contract.
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+#include <exception>
+#include <string>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const std::string& msg) {
+  g_last_error = msg;
+  return status;
+}
+
+constexpr size_t ALIGN = 256;
+size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+int64_t pad128(int64_t n) { return (n + 127) / 128 * 128; }
+
+struct Plan {
+  int B, H, Nq, Nkv, d, Nq_pad, Nkv_pad, splits, frame_len, dtype, pv_mode;
+  float sigma;
+  sage::BatchInfo bi;
+  int order[sage::MAXB_ARGS];
+};
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int choose_splits(const Plan& p) {
+  const int64_t work = static_cast<int64_t>(p.B) * p.H * (p.Nq_pad / 128);
+  int maxkv = 0;
+  for (int b = 0; b < p.B; ++b) maxkv = std::max(maxkv, p.bi.kv_len[b]);
+  const int nch = (maxkv + 63) / 64;
+  if (work >= 768) return 1;
+  int s = static_cast<int>((1024 + work - 1) / work);
+  s = std::min(s, nch / 8);
+  s = std::min(s, SAGE_MAX_SPLITS);
+  return std::max(s, 1);
+}
+
+// Validate *d and fill *p.  Pure host code; touches no device memory.
+int make_plan(const sage_attn_desc* d, Plan* p) {
+  if (!d) return fail(SAGE_E_NULL, "desc is NULL");
+  if (d->abi_version != SAGE_ATTN_ABI_VERSION)
+    return fail(SAGE_E_VERSION, "abi_version " + std::to_string(d->abi_version) + " != " +
+                                    std::to_string(SAGE_ATTN_ABI_VERSION));
+  if (d->dtype != SAGE_F16 && d->dtype != SAGE_BF16) return fail(SAGE_E_DTYPE, "dtype must be SAGE_F16 or SAGE_BF16");
+  if (d->pv_mode != SAGE_PV_16 && d->pv_mode != SAGE_PV_FP8) return fail(SAGE_E_DTYPE, "pv_mode must be SAGE_PV_16 or SAGE_PV_FP8");
+  if (d->d != 64 && d->d != 128) return fail(SAGE_E_UNSUPPORTED, "head dim d must be 64 or 128");
+  if (d->B < 1 || d->H < 1 || d->Nq < 1 || d->Nkv < 1) return fail(SAGE_E_SHAPE, "B, H, Nq and Nkv must be >= 1");
+  if (d->B > SAGE_MAX_BATCH) return fail(SAGE_E_UNSUPPORTED, "B > SAGE_MAX_BATCH");
+  if (d->Nq > (1 << 28) || d->Nkv > (1 << 28)) return fail(SAGE_E_SHAPE, "sequence length too large");
+  const int64_t bh = static_cast<int64_t>(d->B) * d->H;
+  if (bh * pad128(d->Nq) / 128 * SAGE_MAX_SPLITS > 0x7FFFFFFF) return fail(SAGE_E_SHAPE, "too many work items");
+  if (d->frame_len < 0) return fail(SAGE_E_MASK, "frame_len must be >= 0");
+  if (d->kv_splits < 0 || d->kv_splits > SAGE_MAX_SPLITS) return fail(SAGE_E_SHAPE, "kv_splits out of range");
+  if (!(d->sm_scale >= 0.f) || isinf(d->sm_scale)) return fail(SAGE_E_SHAPE, "sm_scale must be finite and >= 0");
+  const int64_t* strides[4] = {d->q_stride, d->k_stride, d->v_stride, d->o_stride};
+  const char* names[4] = {"q", "k", "v", "o"};
+  for (int t = 0; t < 4; ++t)
+    for (int i = 0; i < 3; ++i)
+      if (strides[t][i] < 0 || strides[t][i] % 8 != 0)
+        return fail(SAGE_E_STRIDE, std::string(names[t]) + "_stride[" + std::to_string(i) +
+                                       "] must be a non-negative multiple of 8 elements");
+  p->B = d->B;
+  p->H = d->H;
+  p->Nq = d->Nq;
+  p->Nkv = d->Nkv;
+  p->d = d->d;
+  p->Nq_pad = static_cast<int>(pad128(d->Nq));
+  p->Nkv_pad = static_cast<int>(pad128(d->Nkv));
+  p->frame_len = d->frame_len;
+  p->dtype = d->dtype;
+  p->pv_mode = d->pv_mode;
+  memset(&p->bi, 0, sizeof(p->bi));
+  for (int b = 0; b < d->B; ++b) {
+    const int kv = d->kv_len ? d->kv_len[b] : d->Nkv;
+    if (kv < 1 || kv > d->Nkv) return fail(SAGE_E_MASK, "kv_len[" + std::to_string(b) + "] must be in [1, Nkv]");
+    int qp = 0;
+    if (d->frame_len > 0) {
+      qp = d->q_pos0 ? d->q_pos0[b] : kv - d->Nq;
+      if (qp < 0 || static_cast<int64_t>(qp) + d->Nq > kv)
+        return fail(SAGE_E_MASK, "q_pos0[" + std::to_string(b) + "] must satisfy 0 <= q_pos0 and q_pos0 + Nq <= kv_len");
+    }
+    p->bi.kv_len[b] = kv;
+    p->bi.q_pos0[b] = qp;
+  }
+  for (int b = 0; b < sage::MAXB_ARGS; ++b) p->order[b] = b < d->B ? b : 0;
+  std::stable_sort(p->order, p->order + d->B,
+                   [&](int x, int y) { return p->bi.kv_len[x] > p->bi.kv_len[y]; });
+  const double sm = d->sm_scale > 0.f ? static_cast<double>(d->sm_scale)
+                                      : static_cast<double>(static_cast<float>(1.0 / sqrt(static_cast<double>(d->d))));
+  p->sigma = static_cast<float>(sm * 1.4426950408889634);
+  p->splits = d->kv_splits > 0 ? d->kv_splits : choose_splits(*p);
+  return SAGE_OK;
+}
+
+struct Layout {
+  size_t q_codes, q_scale, k_codes, k_scale, k_mean, chan_shift, v_t, v_e8m0, stats, partial, total;
+  size_t ksum, kmax, kmin, qamax;  // offsets inside stats
+};
+
+Layout layout_of(const Plan& p) {
+  Layout L{};
+  const size_t bh = static_cast<size_t>(p.B) * p.H;
+  const size_t nck = (p.Nkv + sage::KMEAN_CHUNK - 1) / sage::KMEAN_CHUNK;
+  const size_t ncq = (p.Nq + sage::KMEAN_CHUNK - 1) / sage::KMEAN_CHUNK;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  L.q_codes = take(bh * p.Nq_pad * p.d);
+  L.q_scale = take(bh * (p.Nq_pad / 128) * 4);
+  L.k_codes = take(bh * p.Nkv_pad * p.d);
+  L.k_scale = take(bh * (p.Nkv_pad / 64) * 4);
+  L.k_mean = take(bh * p.d * 4);
+  L.chan_shift = take(bh * p.d);
+  L.v_t = take(bh * p.Nkv_pad * p.d * (p.pv_mode == SAGE_PV_FP8 ? 1 : 2));
+  L.v_e8m0 = take(p.pv_mode == SAGE_PV_FP8 ? bh * (p.Nkv_pad / 32) * p.d : 0);
+  L.ksum = 0;
+  L.kmax = align_up(bh * nck * p.d * 8);
+  L.kmin = L.kmax + align_up(bh * nck * p.d * 4);
+  L.qamax = L.kmin + align_up(bh * nck * p.d * 4);
+  L.stats = take(L.qamax + bh * ncq * p.d * 4);
+  L.partial = take(p.splits > 1 ? static_cast<size_t>(p.splits) * bh * p.Nq_pad * (p.d + 2) * 4 : 0);
+  L.total = off;
+  return L;
+}
+
+sage_quant_bufs bufs_of(const Layout& L, const Plan& p, void* ws) {
+  char* base = static_cast<char*>(ws);
+  sage_quant_bufs b{};
+  b.q_codes = reinterpret_cast<int8_t*>(base + L.q_codes);
+  b.q_scale = reinterpret_cast<float*>(base + L.q_scale);
+  b.k_codes = reinterpret_cast<int8_t*>(base + L.k_codes);
+  b.k_scale = reinterpret_cast<float*>(base + L.k_scale);
+  b.k_mean = reinterpret_cast<float*>(base + L.k_mean);
+  b.chan_shift = reinterpret_cast<int8_t*>(base + L.chan_shift);
+  b.v_t = base + L.v_t;
+  b.v_e8m0 = p.pv_mode == SAGE_PV_FP8 ? reinterpret_cast<uint8_t*>(base + L.v_e8m0) : nullptr;
+  b.stats = base + L.stats;
+  b.partial = p.splits > 1 ? base + L.partial : nullptr;
+  return b;
+}
+
+int check_bufs(const sage_quant_bufs* b, const Plan& p, bool need_stats) {
+  if (!b) return fail(SAGE_E_NULL, "bufs is NULL");
+  if (!b->q_codes || !b->q_scale || !b->k_codes || !b->k_scale || !b->k_mean || !b->chan_shift || !b->v_t)
+    return fail(SAGE_E_NULL, "a quantized-operand buffer is NULL");
+  if (p.pv_mode == SAGE_PV_FP8 && !b->v_e8m0) return fail(SAGE_E_NULL, "v_e8m0 is NULL in FP8 mode");
+  if (need_stats && !b->stats) return fail(SAGE_E_NULL, "stats buffer is NULL");
+  if (p.splits > 1 && !need_stats && !b->partial) return fail(SAGE_E_NULL, "partial buffer is NULL with kv_splits > 1");
+  if (!aligned16(b->q_codes) || !aligned16(b->k_codes) || !aligned16(b->v_t) ||
+      (b->v_e8m0 && !aligned16(b->v_e8m0)) || (b->partial && !aligned16(b->partial)))
+    return fail(SAGE_E_ALIGN, "quantized-operand buffers must be 16-byte aligned");
+  return SAGE_OK;
+}
+
+int finish(hipError_t e, const sage_attn_desc* d, hipStream_t st) {
+  if (e == hipSuccess && d && (d->flags & SAGE_FLAG_DEBUG_SYNC)) {
+    e = hipStreamSynchronize(st);
+    if (e == hipSuccess) e = hipGetLastError();
+  }
+  if (e != hipSuccess) return fail(SAGE_E_HIP, std::string("HIP error: ") + hipGetErrorString(e));
+  return SAGE_OK;
+}
+
+sage::AttnLaunch attn_launch_of(const Plan& p, const sage_quant_bufs& b, void* o, const sage_attn_desc* d) {
+  sage::AttnLaunch L{};
+  L.dtype = p.dtype;
+  L.pv_mode = p.pv_mode;
+  L.d = p.d;
+  L.B = p.B;
+  L.H = p.H;
+  L.Nq = p.Nq;
+  L.Nkv = p.Nkv;
+  L.Nq_pad = p.Nq_pad;
+  L.Nkv_pad = p.Nkv_pad;
+  L.frame_len = p.frame_len;
+  L.splits = p.splits;
+  L.sigma = p.sigma;
+  L.bi = p.bi;
+  for (int i = 0; i < sage::MAXB_ARGS; ++i) L.order[i] = p.order[i];
+  L.bufs = b;
+  L.o = o;
+  for (int i = 0; i < 3; ++i) L.os[i] = d->o_stride[i];
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sage_attn_abi_version(void) { return SAGE_ATTN_ABI_VERSION; }
+
+const char* sage_attn_status_string(int s) {
+  switch (s) {
+    case SAGE_OK: return "ok";
+    case SAGE_E_NULL: return "null pointer";
+    case SAGE_E_SHAPE: return "bad shape";
+    case SAGE_E_DTYPE: return "bad dtype or pv_mode";
+    case SAGE_E_STRIDE: return "bad stride";
+    case SAGE_E_ALIGN: return "misaligned pointer";
+    case SAGE_E_MASK: return "inconsistent mask parameters";
+    case SAGE_E_UNSUPPORTED: return "unsupported configuration";
+    case SAGE_E_WORKSPACE: return "workspace missing or too small";
+    case SAGE_E_VERSION: return "ABI version mismatch";
+    case SAGE_E_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+const char* sage_attn_last_error(void) { return g_last_error.c_str(); }
+
+int sage_attn_constant(const char* name, double* value) {
+  if (!name || !value) return fail(SAGE_E_NULL, "name/value is NULL");
+  const struct { const char* n; double v; } table[] = {
+      {"BQ", sage::BQ}, {"BK", sage::BK}, {"VB", sage::VB}, {"QMAX", sage::QMAX},
+      {"TAU", sage::TAU}, {"PSHIFT_FP8", sage::PSHIFT_FP8}, {"PSHIFT_16", sage::PSHIFT_16},
+      {"KMEAN_CHUNK", sage::KMEAN_CHUNK}};
+  for (const auto& e : table)
+    if (strcmp(e.n, name) == 0) {
+      *value = e.v;
+      return SAGE_OK;
+    }
+  return fail(SAGE_E_UNSUPPORTED, std::string("unknown constant ") + name);
+}
+
+int sage_attn_kv_splits(const sage_attn_desc* desc, int32_t* splits) {
+  try {
+    if (!splits) return fail(SAGE_E_NULL, "splits is NULL");
+    Plan p;
+    const int s = make_plan(desc, &p);
+    if (s != SAGE_OK) return s;
+    *splits = p.splits;
+    return SAGE_OK;
+  } catch (const std::exception& e) {
+    return fail(SAGE_E_HIP, e.what());
+  }
+}
+
+int sage_attn_workspace_size(const sage_attn_desc* desc, size_t* bytes) {
+  try {
+    if (!bytes) return fail(SAGE_E_NULL, "bytes is NULL");
+    Plan p;
+    const int s = make_plan(desc, &p);
+    if (s != SAGE_OK) return s;
+    *bytes = layout_of(p).total;
+    return SAGE_OK;
+  } catch (const std::exception& e) {
+    return fail(SAGE_E_HIP, e.what());
+  }
+}
+
+int sage_attn_quant_layout(const sage_attn_desc* desc, void* ws, size_t ws_bytes, sage_quant_bufs* out) {
+  try {
+    if (!out) return fail(SAGE_E_NULL, "out is NULL");
+    Plan p;
+    const int s = make_plan(desc, &p);
+    if (s != SAGE_OK) return s;
+    const Layout L = layout_of(p);
+    if (!ws) return fail(SAGE_E_WORKSPACE, "workspace is NULL");
+    if (reinterpret_cast<uintptr_t>(ws) % ALIGN) return fail(SAGE_E_ALIGN, "workspace must be 256-byte aligned");
+    if (ws_bytes < L.total)
+      return fail(SAGE_E_WORKSPACE, "workspace has " + std::to_string(ws_bytes) + " bytes, needs " + std::to_string(L.total));
+    *out = bufs_of(L, p, ws);
+    return SAGE_OK;
+  } catch (const std::exception& e) {
+    return fail(SAGE_E_HIP, e.what());
+  }
+}
+
+int sage_attn_quantize(const sage_attn_desc* desc, const void* q, const void* k, const void* v,
+                       const sage_quant_bufs* bufs, void* stream) {
+  try {
+    Plan p;
+    int s = make_plan(desc, &p);
+    if (s != SAGE_OK) return s;
+    if (!q || !k || !v) return fail(SAGE_E_NULL, "q, k and v must be non-NULL");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return fail(SAGE_E_ALIGN, "q, k and v must be 16-byte aligned");
+    if ((s = check_bufs(bufs, p, true)) != SAGE_OK) return s;
+    if (desc->k_mean_in && (reinterpret_cast<uintptr_t>(desc->k_mean_in) & 3u))
+      return fail(SAGE_E_ALIGN, "k_mean_in must be 4-byte aligned");
+    sage::QuantLaunch L{};
+    L.dtype = p.dtype;
+    L.pv_mode = p.pv_mode;
+    L.d = p.d;
+    L.B = p.B;
+    L.H = p.H;
+    L.Nq = p.Nq;
+    L.Nkv = p.Nkv;
+    L.Nq_pad = p.Nq_pad;
+    L.Nkv_pad = p.Nkv_pad;
+    L.q = q;
+    L.k = k;
+    L.v = v;
+    for (int i = 0; i < 3; ++i) {
+      L.qs[i] = desc->q_stride[i];
+      L.ks[i] = desc->k_stride[i];
+      L.vs[i] = desc->v_stride[i];
+    }
+    L.k_mean_in = desc->k_mean_in;
+    L.bi = p.bi;
+    L.bufs = *bufs;
+    const Layout lay = layout_of(p);
+    char* st = static_cast<char*>(bufs->stats);
+    L.stat_ksum = reinterpret_cast<double*>(st + lay.ksum);
+    L.stat_kmax = reinterpret_cast<float*>(st + lay.kmax);
+    L.stat_kmin = reinterpret_cast<float*>(st + lay.kmin);
+    L.stat_qamax = reinterpret_cast<float*>(st + lay.qamax);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    return finish(sage::launch_quantize(L, hs), desc, hs);
+  } catch (const std::exception& e) {
+    return fail(SAGE_E_HIP, e.what());
+  }
+}
+
+int sage_attn_fwd_quantized(const sage_attn_desc* desc, const sage_quant_bufs* bufs, void* o, void* stream) {
+  try {
+    Plan p;
+    int s = make_plan(desc, &p);
+    if (s != SAGE_OK) return s;
+    if (!o) return fail(SAGE_E_NULL, "o is NULL");
+    if (!aligned16(o)) return fail(SAGE_E_ALIGN, "o must be 16-byte aligned");
+    if ((s = check_bufs(bufs, p, false)) != SAGE_OK) return s;
+    const sage::AttnLaunch L = attn_launch_of(p, *bufs, o, desc);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    return finish(sage::launch_attention(L, hs), desc, hs);
+  } catch (const std::exception& e) {
+    return fail(SAGE_E_HIP, e.what());
+  }
+}
+
+int sage_attn_fwd(const sage_attn_desc* desc, const void* q, const void* k, const void* v, void* o, void* ws,
+                  size_t ws_bytes, void* stream) {
+  sage_quant_bufs b;
+  int s = sage_attn_quant_layout(desc, ws, ws_bytes, &b);
+  if (s != SAGE_OK) return s;
+  if (!o) return fail(SAGE_E_NULL, "o is NULL");
+  if (!aligned16(o)) return fail(SAGE_E_ALIGN, "o must be 16-byte aligned");
+  s = sage_attn_quantize(desc, q, k, v, &b, stream);
+  if (s != SAGE_OK) return s;
+  return sage_attn_fwd_quantized(desc, &b, o, stream);
+}
+
+int sage_attn_debug_scores(const sage_attn_desc* desc, const sage_quant_bufs* bufs, const int32_t* tiles,
+                           int32_t ntiles, int32_t* out, void* stream) {
+  try {
+    Plan p;
+    int s = make_plan(desc, &p);
+    if (s != SAGE_OK) return s;
+    if (!tiles || !out) return fail(SAGE_E_NULL, "tiles/out is NULL");
+    if (ntiles < 0) return fail(SAGE_E_SHAPE, "ntiles < 0");
+    if (!bufs || !bufs->q_codes || !bufs->k_codes) return fail(SAGE_E_NULL, "codes are NULL");
+    if (!aligned16(bufs->q_codes) || !aligned16(bufs->k_codes) || !aligned16(out))
+      return fail(SAGE_E_ALIGN, "codes and out must be 16-byte aligned");
+    for (int i = 0; i < ntiles; ++i) {
+      const int bh = tiles[3 * i], q0 = tiles[3 * i + 1], k0 = tiles[3 * i + 2];
+      if (bh < 0 || bh >= p.B * p.H || q0 < 0 || q0 % 32 || q0 + 32 > p.Nq_pad || k0 < 0 || k0 % 64 ||
+          k0 + 64 > p.Nkv_pad)
+        return fail(SAGE_E_SHAPE, "tile " + std::to_string(i) + " out of range");
+    }
+    const sage::AttnLaunch L = attn_launch_of(p, *bufs, nullptr, desc);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    return finish(sage::launch_debug_scores(L, tiles, ntiles, out, hs), desc, hs);
+  } catch (const std::exception& e) {
+    return fail(SAGE_E_HIP, e.what());
+  }
+}
+
+int sage_attn_debug_convert(int kind, const float* in, void* out, int64_t n, void* stream) {
+  try {
+    if (kind < 0 || kind > 2) return fail(SAGE_E_UNSUPPORTED, "kind must be 0, 1 or 2");
+    if (n < 0) return fail(SAGE_E_SHAPE, "n < 0");
+    if (n == 0) return SAGE_OK;
+    if (!in || !out) return fail(SAGE_E_NULL, "in/out is NULL");
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    return finish(sage::launch_convert(kind, in, out, n, hs), nullptr, hs);
+  } catch (const std::exception& e) {
+    return fail(SAGE_E_HIP, e.what());
+  }
+}
+
+}  // extern "C"

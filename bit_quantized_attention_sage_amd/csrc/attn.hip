@@ -1,0 +1,449 @@
+// Fused quantized attention for gfx950: INT8 S^T = K Q^T on matrix cores with
+// int32 accumulation, fp32 dequantization and online softmax, and O^T = V^T P^T
+// on 16-bit or scaled-FP8 matrix cores.
+//
+// Why quantized: video-generation attention is compute-bound and low-precision
+// matrix units sit idle under exact attention (podcast notes "Faster! Even
+// faster! ...", section "02:48 There were clearly faster compute units on the
+// hardware").  Why a frame-block-causal mask and a KV cache: streaming
+// generation attends frame by frame to cached history (Vidu S1 blog, sections
+// "模型架构", "训练方法" and "Infra").  The scheme itself is this library's own
+// (the pages give none).
+//
+// Work decomposition.  One workgroup = 4 waves = one 128-row query block (one
+// Q scale) of one (b, h), optionally one of several KV splits.  Each wave owns
+// 32 query rows.  Keys are streamed in 64-key chunks (one K scale each)
+// through LDS; per chunk a wave runs 8 i8 MFMAs 32x32x32 for S, the softmax on
+// its 32x64 scores, and the P.V MFMAs.
+//
+// Register layouts (32x32 MFMA, lane l, h2 = l / 32, r32 = l % 32):
+//  * S^T = K Q^T: the B operand is Q^T, so lane l holds query r32 and channel
+//    bytes [32*ks + 16*h2, +16); the A operand row r (lane r32) loads key
+//    32*u + 16*((r>>2)&1) + 4*(r>>3) + (r&3) of subtile u.  With that row
+//    order, accumulator register i of lane l (row 8*(i/4) + 4*h2 + i%4) holds
+//    key 32*u + 16*h2 + i: lane half h2 owns keys [16*h2, +16) and
+//    [32 + 16*h2, +16) of the chunk for its query.
+//  * The scaled FP8 MFMA 32x32x64 pairs byte e of lane half h2 with K index
+//    16*h2 + e (e < 16) or 32 + 16*h2 + (e - 16), and takes the E8M0 scale of
+//    K block b (indices [32b, 32b+32)) for row r from lane r + 32*b.  So P^T
+//    is already in B-operand form for O^T = V^T P^T with K index == key
+//    offset in the chunk, each E8M0 block is 32 consecutive keys, and V
+//    stored per chunk channel-major makes the A operand two contiguous
+//    16-byte reads.  The 16-bit P.V MFMAs (K = 16) take keys
+//    32*(mu/2) + 16*h2 + 8*(mu%2) + [0, 8) in lane half h2 for step mu.
+//  * O^T accumulator: lane l holds query r32 and channels
+//    32*cb + 8*(i/4) + 4*h2 + i%4, so per-row factors (alpha, 1/l) are per lane.
+#include "common.h"
+#include "kernels.h"
+
+namespace sage {
+
+constexpr int SENTINEL = -(1 << 30);  // masked score before the row maximum
+
+// Key held by row r of subtile u of a chunk's A operand (see above).
+__device__ __forceinline__ int a_row_key(int r, int u) {
+  return 32 * u + 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3);
+}
+
+// 16-byte granule swizzle of the K chunk in LDS: granule g of key k is
+// stored at slot g ^ swz(k), spreading the 8 keys one ds_read_b128 phase
+// touches over distinct banks.
+template <int D>
+__device__ __forceinline__ int k_swz(int key) {
+  constexpr int G = D / 16;
+  return ((key & 3) | (((key >> 4) & 1) << 2)) & (G - 1);
+}
+
+// S^T for one 64-key chunk held in LDS (row-major [64][D], swizzled):
+// s0 = keys 16*h2 + [0,16), s1 = keys 32 + 16*h2 + [0,16), per the layout above.
+template <int D>
+__device__ __forceinline__ void qk_chunk(const int8_t* __restrict__ klds, const v4i* qv, int lane,
+                                         v16i& s0, v16i& s1) {
+  const int h2 = lane >> 5, r32 = lane & 31;
+  const int key0 = a_row_key(r32, 0), key1 = a_row_key(r32, 1);
+  const int sw0 = k_swz<D>(key0), sw1 = k_swz<D>(key1);
+  s0 = v16i{0};
+  s1 = v16i{0};
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) {
+    const int g = 2 * ks + h2;
+    const v4i a0 = *reinterpret_cast<const v4i*>(klds + key0 * D + ((g ^ sw0) << 4));
+    const v4i a1 = *reinterpret_cast<const v4i*>(klds + key1 * D + ((g ^ sw1) << 4));
+    s0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, qv[ks], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, qv[ks], s1, 0, 0, 0);
+  }
+}
+
+// Copy one 64-key K chunk (row-major, D bytes per key) into LDS, swizzled.
+template <int D, int NT>
+__device__ __forceinline__ void load_k_chunk(int8_t* __restrict__ klds, const int8_t* __restrict__ src,
+                                             int tid) {
+  constexpr int G = D / 16;
+  constexpr int NG = 64 * G;
+#pragma unroll
+  for (int gi = tid; gi < NG; gi += NT) {
+    const int key = gi / G, g = gi % G;
+    const uint4 v = *reinterpret_cast<const uint4*>(src + gi * 16);
+    *reinterpret_cast<uint4*>(klds + key * D + ((g ^ k_swz<D>(key)) << 4)) = v;
+  }
+}
+
+// Load the 32 query rows' Q codes of a wave as B operands (16 bytes per k-step).
+template <int D>
+__device__ __forceinline__ void load_q(v4i* qv, const int8_t* __restrict__ qrow, int h2) {
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks)
+    qv[ks] = *reinterpret_cast<const v4i*>(qrow + 32 * ks + 16 * h2);
+}
+
+struct AttnArgs {
+  const int8_t* qc;
+  const float* qscale;
+  const int8_t* kc;
+  const float* kscale;
+  const void* vt;
+  const uint8_t* ve;
+  void* o;
+  int64_t os_b, os_h, os_n;
+  float* part_o;   // [splits][B*H][Nq_pad][D] fp32, when splits > 1
+  float* part_ml;  // [splits][B*H][Nq_pad][2]  (m, l)
+  int B, H, Nq, Nq_pad, Nkv_pad, nqt, splits, total;
+  float sigma;
+  int frame_len;
+  BatchInfo bi;
+  int order[MAXB_ARGS];
+};
+
+template <int D, int PV, int DT>
+__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
+  constexpr int NCB = D / 32;                    // 32-channel blocks of O
+  constexpr int VBYTES = (PV == PVFP8) ? 1 : 2;  // bytes per V element
+  constexpr int SHIFT = (PV == PVFP8) ? PSHIFT_FP8 : PSHIFT_16;
+  __shared__ __attribute__((aligned(16))) int8_t klds[64 * D];
+  __shared__ __attribute__((aligned(16))) uint8_t vlds[64 * D * VBYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t elds[2 * D];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int h2 = lane >> 5, r32 = lane & 31;
+
+  // ---- work item: (batch by decreasing kv_len, head, split, query tile)
+  const int L = xcd_remap(blockIdx.x, A.total);
+  const int per_b = A.H * A.splits * A.nqt;
+  const int b = A.order[L / per_b];
+  int rem = L % per_b;
+  const int h = rem / (A.splits * A.nqt);
+  rem %= A.splits * A.nqt;
+  const int split = rem / A.nqt;
+  const int qt = rem % A.nqt;
+  const int bh = b * A.H + h;
+
+  const int kv_len = A.bi.kv_len[b];
+  const int q_pos0 = A.bi.q_pos0[b];
+  const int nch_b = (kv_len + 63) / 64;
+  const int c_lo = split * nch_b / A.splits;
+  const int c_hi = (split + 1) * nch_b / A.splits;
+
+  // ---- this lane's query row and the end of its visible key range
+  const int qi = qt * BQ + w * 32 + r32;
+  const int qi_valid = min(qi, A.Nq - 1);
+  int re = kv_len;
+  if (A.frame_len > 0) re = min(kv_len, ((q_pos0 + qi_valid) / A.frame_len + 1) * A.frame_len);
+  const int wave_end = wave_max_i(re);
+  const int wave_min = wave_min_i(re);
+  const int wg_end = A.frame_len > 0
+                         ? min(kv_len, ((q_pos0 + min(qt * BQ + BQ - 1, A.Nq - 1)) / A.frame_len + 1) *
+                                           A.frame_len)
+                         : kv_len;
+  const int wave_hi = min(c_hi, (wave_end + 63) / 64);
+  const int wave_full = wave_min / 64;  // chunks below this are visible to every row
+  const int wg_hi = min(c_hi, (wg_end + 63) / 64);
+
+  v4i qv[D / 32];
+  load_q<D>(qv, A.qc + (static_cast<int64_t>(bh) * A.Nq_pad + qi) * D, h2);
+  const float qsc = A.qscale[static_cast<int64_t>(bh) * A.nqt + qt] * A.sigma;
+
+  v16f o[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) o[cb] = v16f{0.f};
+  float m = -__builtin_inff();
+  float l = 0.f;
+
+  const int nkc = A.Nkv_pad / 64;
+  const int8_t* kbase = A.kc + static_cast<int64_t>(bh) * A.Nkv_pad * D;
+  const uint8_t* vbase = static_cast<const uint8_t*>(A.vt) + static_cast<int64_t>(bh) * nkc * 64 * D * VBYTES;
+  const float* ksc = A.kscale + static_cast<int64_t>(bh) * nkc;
+
+  for (int ch = c_lo; ch < wg_hi; ++ch) {
+    // ---- stage the chunk: K codes (swizzled), V^T, E8M0 scales
+    load_k_chunk<D, 256>(klds, kbase + static_cast<int64_t>(ch) * 64 * D, tid);
+    {
+      const uint8_t* src = vbase + static_cast<int64_t>(ch) * 64 * D * VBYTES;
+      constexpr int NG = 64 * D * VBYTES / 16;
+#pragma unroll
+      for (int gi = tid; gi < NG; gi += 256)
+        *reinterpret_cast<uint4*>(vlds + gi * 16) = *reinterpret_cast<const uint4*>(src + gi * 16);
+      if (PV == PVFP8 && tid < 2 * D / 16)
+        *reinterpret_cast<uint4*>(elds + tid * 16) = *reinterpret_cast<const uint4*>(
+            A.ve + (static_cast<int64_t>(bh) * (A.Nkv_pad / 32) + 2 * ch) * D + tid * 16);
+    }
+    __syncthreads();
+
+    if (ch < wave_hi) {
+      v16i s0, s1;
+      qk_chunk<D>(klds, qv, lane, s0, s1);
+      const bool masked = ch >= wave_full;
+      const int kb = ch * 64 + 16 * h2;  // key of s0[0] in this lane; s1[0] is kb + 32
+      if (masked) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          if (kb + i >= re) s0[i] = SENTINEL;
+          if (kb + 32 + i >= re) s1[i] = SENTINEL;
+        }
+      }
+      int mx = max(s0[0], s1[0]);
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = max(mx, max(s0[i], s1[i]));
+      mx = max(mx, __shfl_xor(mx, 32, 64));
+      const float c = qsc * ksc[ch];
+      const float tm = static_cast<float>(mx) * c;
+      const bool has = ch * 64 < re;
+      const bool upd = has && (tm > m + TAU);
+      if (__any(upd)) {
+        const float alpha = upd ? __builtin_amdgcn_exp2f(m - tm) : 1.0f;
+        m = upd ? tm : m;
+        l *= alpha;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[cb][i] *= alpha;
+      }
+      const float nmref = -(m - static_cast<float>(SHIFT));
+      float p0[16], p1[16];
+      float lsum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        p0[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(static_cast<float>(s0[i]), c, nmref));
+        p1[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(static_cast<float>(s1[i]), c, nmref));
+        if (masked) {
+          if (kb + i >= re) p0[i] = 0.f;
+          if (kb + 32 + i >= re) p1[i] = 0.f;
+        }
+        lsum += p0[i] + p1[i];
+      }
+      l += lsum;
+
+      if (PV == PVFP8) {
+        v8i pb;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          pb[k] = static_cast<int>(pack_e4m3x4(p0[4 * k], p0[4 * k + 1], p0[4 * k + 2], p0[4 * k + 3]));
+          pb[4 + k] = static_cast<int>(pack_e4m3x4(p1[4 * k], p1[4 * k + 1], p1[4 * k + 2], p1[4 * k + 3]));
+        }
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          const int chn = 32 * cb + r32;
+          const uint8_t* vrow = vlds + chn * 64 + 16 * h2;
+          const v4i lo = *reinterpret_cast<const v4i*>(vrow);
+          const v4i hi = *reinterpret_cast<const v4i*>(vrow + 32);
+          const v8i va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          const int sc = static_cast<int>(elds[h2 * D + chn]);
+          o[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, o[cb], 0, 0, 0, sc, 0, 127);
+        }
+      } else {
+        uint32_t pw[16];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          pw[k] = Pack16<DT>::pack(p0[2 * k], p0[2 * k + 1]);
+          pw[8 + k] = Pack16<DT>::pack(p1[2 * k], p1[2 * k + 1]);
+        }
+#pragma unroll
+        for (int mu = 0; mu < 4; ++mu) {
+          const v4i pbv = {static_cast<int>(pw[4 * mu]), static_cast<int>(pw[4 * mu + 1]),
+                           static_cast<int>(pw[4 * mu + 2]), static_cast<int>(pw[4 * mu + 3])};
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) {
+            const int chn = 32 * cb + r32;
+            const v4i va = *reinterpret_cast<const v4i*>(
+                vlds + (chn * 64 + 32 * (mu >> 1) + 16 * h2 + 8 * (mu & 1)) * 2);
+            if (DT == DT_BF16)
+              o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, va),
+                                                              __builtin_bit_cast(v8bf, pbv), o[cb], 0, 0, 0);
+            else
+              o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, va),
+                                                             __builtin_bit_cast(v8h, pbv), o[cb], 0, 0, 0);
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue: combine the two lane halves' row sums, normalise, store
+  const float ltot = l + __shfl_xor(l, 32, 64);
+  if (qi >= A.Nq) return;
+  if (A.splits == 1) {
+    const float inv = 1.0f / ltot;
+    uint16_t* orow = static_cast<uint16_t*>(A.o) + b * A.os_b + h * A.os_h + static_cast<int64_t>(qi) * A.os_n;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int chn = 32 * cb + 8 * g + 4 * h2;
+        const uint32_t w0 = Pack16<DT>::pack(o[cb][4 * g] * inv, o[cb][4 * g + 1] * inv);
+        const uint32_t w1 = Pack16<DT>::pack(o[cb][4 * g + 2] * inv, o[cb][4 * g + 3] * inv);
+        *reinterpret_cast<uint2*>(orow + chn) = make_uint2(w0, w1);
+      }
+  } else {
+    const int64_t prow = (static_cast<int64_t>(split) * A.B * A.H + bh) * A.Nq_pad + qi;
+    const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
+    float* po = A.part_o + prow * D;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int chn = 32 * cb + 8 * g + 4 * h2;
+        *reinterpret_cast<float4*>(po + chn) =
+            make_float4(o[cb][4 * g] * inv, o[cb][4 * g + 1] * inv, o[cb][4 * g + 2] * inv, o[cb][4 * g + 3] * inv);
+      }
+    if (h2 == 0) *reinterpret_cast<float2*>(A.part_ml + 2 * prow) = make_float2(m, ltot);
+  }
+}
+
+// Merge split partials: O = sum_s w_s O_s / sum_s w_s with w_s = l_s 2^(m_s - M).
+// One thread per (row, 4 channels).
+template <int D, int DT>
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs A) {
+  constexpr int G = D / 4;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t rows = static_cast<int64_t>(A.B) * A.H * A.Nq_pad;
+  if (t >= rows * G) return;
+  const int64_t row = t / G;
+  const int g = t % G;
+  const int bh = row / A.Nq_pad;
+  const int qi = row % A.Nq_pad;
+  if (qi >= A.Nq) return;
+  const int b = bh / A.H, h = bh % A.H;
+  float M = -__builtin_inff();
+  for (int s = 0; s < A.splits; ++s) {
+    const float2 ml = *reinterpret_cast<const float2*>(A.part_ml + 2 * ((static_cast<int64_t>(s) * A.B * A.H) * A.Nq_pad + row));
+    if (ml.y > 0.f) M = fmaxf(M, ml.x);
+  }
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+  for (int s = 0; s < A.splits; ++s) {
+    const int64_t prow = (static_cast<int64_t>(s) * A.B * A.H) * A.Nq_pad + row;
+    const float2 ml = *reinterpret_cast<const float2*>(A.part_ml + 2 * prow);
+    if (!(ml.y > 0.f)) continue;
+    const float wgt = ml.y * __builtin_amdgcn_exp2f(ml.x - M);
+    const float4 v = *reinterpret_cast<const float4*>(A.part_o + prow * D + 4 * g);
+    acc[0] += wgt * v.x;
+    acc[1] += wgt * v.y;
+    acc[2] += wgt * v.z;
+    acc[3] += wgt * v.w;
+    wsum += wgt;
+  }
+  const float inv = 1.0f / wsum;
+  uint16_t* orow = static_cast<uint16_t*>(A.o) + b * A.os_b + h * A.os_h + static_cast<int64_t>(qi) * A.os_n;
+  *reinterpret_cast<uint2*>(orow + 4 * g) =
+      make_uint2(Pack16<DT>::pack(acc[0] * inv, acc[1] * inv), Pack16<DT>::pack(acc[2] * inv, acc[3] * inv));
+}
+
+// Exact int32 scores of 32x64 tiles through qk_chunk (test support).
+struct DebugTiles {
+  int n;
+  int t[128][3];
+};
+
+template <int D>
+__global__ __launch_bounds__(64) void debug_scores_kernel(AttnArgs A, DebugTiles T, int32_t* out) {
+  __shared__ __attribute__((aligned(16))) int8_t klds[64 * D];
+  const int lane = threadIdx.x, h2 = lane >> 5, r32 = lane & 31;
+  const int bh = T.t[blockIdx.x][0], q0 = T.t[blockIdx.x][1], k0 = T.t[blockIdx.x][2];
+  load_k_chunk<D, 64>(klds, A.kc + (static_cast<int64_t>(bh) * A.Nkv_pad + k0) * D, lane);
+  __syncthreads();
+  v4i qv[D / 32];
+  load_q<D>(qv, A.qc + (static_cast<int64_t>(bh) * A.Nq_pad + q0 + r32) * D, h2);
+  v16i s0, s1;
+  qk_chunk<D>(klds, qv, lane, s0, s1);
+  int32_t* o = out + static_cast<int64_t>(blockIdx.x) * 32 * 64 + r32 * 64 + 16 * h2;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    o[i] = s0[i];
+    o[32 + i] = s1[i];
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+static AttnArgs make_args(const AttnLaunch& L) {
+  AttnArgs A{};
+  A.qc = L.bufs.q_codes;
+  A.qscale = L.bufs.q_scale;
+  A.kc = L.bufs.k_codes;
+  A.kscale = L.bufs.k_scale;
+  A.vt = L.bufs.v_t;
+  A.ve = L.bufs.v_e8m0;
+  A.o = L.o;
+  A.os_b = L.os[0];
+  A.os_h = L.os[1];
+  A.os_n = L.os[2];
+  A.part_o = static_cast<float*>(L.bufs.partial);
+  A.part_ml = L.bufs.partial
+                  ? static_cast<float*>(L.bufs.partial) +
+                        static_cast<int64_t>(L.splits) * L.B * L.H * L.Nq_pad * L.d
+                  : nullptr;
+  A.B = L.B;
+  A.H = L.H;
+  A.Nq = L.Nq;
+  A.Nq_pad = L.Nq_pad;
+  A.Nkv_pad = L.Nkv_pad;
+  A.nqt = L.Nq_pad / BQ;
+  A.splits = L.splits;
+  A.total = L.B * L.H * L.splits * A.nqt;
+  A.sigma = L.sigma;
+  A.frame_len = L.frame_len;
+  A.bi = L.bi;
+  for (int i = 0; i < MAXB_ARGS; ++i) A.order[i] = L.order[i];
+  return A;
+}
+
+template <int D, int PV, int DT>
+static hipError_t attn_impl(const AttnLaunch& L, hipStream_t st) {
+  const AttnArgs A = make_args(L);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, PV, DT>), dim3(A.total), dim3(256), 0, st, A);
+  if (L.splits > 1) {
+    const int64_t threads = static_cast<int64_t>(L.B) * L.H * L.Nq_pad * (D / 4);
+    hipLaunchKernelGGL((attn_combine_kernel<D, DT>), dim3(static_cast<unsigned>((threads + 255) / 256)),
+                       dim3(256), 0, st, A);
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t attn_d(const AttnLaunch& L, hipStream_t st) {
+  if (L.pv_mode == PVFP8)
+    return L.dtype == DT_BF16 ? attn_impl<D, PVFP8, DT_BF16>(L, st) : attn_impl<D, PVFP8, DT_F16>(L, st);
+  return L.dtype == DT_BF16 ? attn_impl<D, PV16, DT_BF16>(L, st) : attn_impl<D, PV16, DT_F16>(L, st);
+}
+
+hipError_t launch_attention(const AttnLaunch& L, hipStream_t st) {
+  return L.d == 128 ? attn_d<128>(L, st) : attn_d<64>(L, st);
+}
+
+hipError_t launch_debug_scores(const AttnLaunch& L, const int32_t* tiles, int ntiles, int32_t* out,
+                               hipStream_t st) {
+  const AttnArgs A = make_args(L);
+  for (int base = 0; base < ntiles; base += 128) {
+    DebugTiles T{};
+    T.n = ntiles - base < 128 ? ntiles - base : 128;
+    for (int i = 0; i < T.n; ++i)
+      for (int k = 0; k < 3; ++k) T.t[i][k] = tiles[3 * (base + i) + k];
+    int32_t* o = out + static_cast<int64_t>(base) * 32 * 64;
+    if (L.d == 128)
+      hipLaunchKernelGGL(debug_scores_kernel<128>, dim3(T.n), dim3(64), 0, st, A, T, o);
+    else
+      hipLaunchKernelGGL(debug_scores_kernel<64>, dim3(T.n), dim3(64), 0, st, A, T, o);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sage

@@ -1,0 +1,117 @@
+// Shared device-side definitions of the quantized attention library (gfx950).
+//
+// The scheme's constants live here and only here on the GPU side.  The pages
+// fix none of them (podcast notes, section "02:48 There were clearly faster
+// compute units on the hardware": only "low-bit"); they are this library's
+// stated design.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sage {
+
+constexpr int BQ = 128;          // query tokens per Q scale block (= one workgroup)
+constexpr int BK = 64;           // key tokens per K scale block = softmax chunk
+constexpr int VB = 32;           // key tokens per FP8 V scale (E8M0) block
+constexpr int QMAX = 127;        // symmetric INT8 range
+constexpr int KMEAN_CHUNK = 128; // tokens per first-level partial sum of the K mean
+constexpr float TAU = 4.0f;      // lazy running-max threshold (log2 units)
+constexpr int PSHIFT_FP8 = 4;    // P stored as e4m3(p * 2^4) in FP8 mode
+constexpr int PSHIFT_16 = 0;
+constexpr int NPAD = 128;        // Nq and Nkv are padded to multiples of this
+constexpr int MAXB = 256;        // largest batch handled through kernel arguments
+
+enum { DT_F16 = 0, DT_BF16 = 1 };
+enum { PV16 = 0, PVFP8 = 1 };
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+
+// 16-bit storage types; conversions below are explicit and round to nearest even.
+struct bf16_t { uint16_t x; };
+struct f16_t { uint16_t x; };
+
+__device__ __forceinline__ float to_f32(bf16_t v) {
+  return __uint_as_float(static_cast<uint32_t>(v.x) << 16);
+}
+__device__ __forceinline__ float to_f32(f16_t v) {
+  _Float16 h;
+  __builtin_memcpy(&h, &v.x, 2);
+  return static_cast<float>(h);
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t bits16) {
+  _Float16 h;
+  uint16_t b = static_cast<uint16_t>(bits16);
+  __builtin_memcpy(&h, &b, 2);
+  return static_cast<float>(h);
+}
+
+// Two floats -> packed pair of bf16 (RNE; v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  bf2 v;
+  v[0] = static_cast<__bf16>(a);
+  v[1] = static_cast<__bf16>(b);
+  uint32_t r;
+  __builtin_memcpy(&r, &v, 4);
+  return r;
+}
+// Two floats -> packed pair of fp16 (RNE, v_cvt_f16_f32).
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  _Float16 ha = static_cast<_Float16>(a), hb = static_cast<_Float16>(b);
+  uint16_t ua, ub;
+  __builtin_memcpy(&ua, &ha, 2);
+  __builtin_memcpy(&ub, &hb, 2);
+  return static_cast<uint32_t>(ua) | (static_cast<uint32_t>(ub) << 16);
+}
+// Four floats (|x| <= 448) -> four OCP e4m3fn bytes, RNE (v_cvt_pk_fp8_f32).
+__device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
+  return static_cast<uint32_t>(r);
+}
+
+template <int DT> struct Pack16;
+template <> struct Pack16<DT_BF16> {
+  static __device__ __forceinline__ uint32_t pack(float a, float b) { return pack_bf16x2(a, b); }
+  static __device__ __forceinline__ float lo(uint32_t w) { return bf16_bits_to_f32(w & 0xFFFFu); }
+  static __device__ __forceinline__ float hi(uint32_t w) { return bf16_bits_to_f32(w >> 16); }
+};
+template <> struct Pack16<DT_F16> {
+  static __device__ __forceinline__ uint32_t pack(float a, float b) { return pack_f16x2(a, b); }
+  static __device__ __forceinline__ float lo(uint32_t w) { return f16_bits_to_f32(w & 0xFFFFu); }
+  static __device__ __forceinline__ float hi(uint32_t w) { return f16_bits_to_f32(w >> 16); }
+};
+
+// Wave-wide (64 lanes) reductions.
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ int wave_max_i(int v) {
+  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ int wave_min_i(int v) {
+  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Logical tile index of a physical workgroup id so that the workgroups one XCD
+// runs (ids x, x+8, x+16, ... go to XCD x) form one contiguous logical range:
+// neighbouring query tiles of the same head then share K/V in that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int pid, int total) {
+  const int q = total / 8, r = total % 8;
+  const int x = pid % 8, k = pid / 8;
+  return x * q + (x < r ? x : r) + k;
+}
+
+}  // namespace sage

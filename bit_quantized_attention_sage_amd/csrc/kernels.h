@@ -1,0 +1,52 @@
+// Host-side launch descriptions shared by the C ABI (api.cpp) and the kernel
+// translation units.  Plain structs; no allocation anywhere.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/sage_attn.h"
+#include "common.h"
+
+namespace sage {
+
+constexpr int MAXB_ARGS = 128;  // batches passed by value in kernel arguments
+
+// Per-batch mask data, copied into the kernel arguments of every launch.
+struct BatchInfo {
+  int kv_len[MAXB_ARGS];
+  int q_pos0[MAXB_ARGS];
+};
+
+struct QuantLaunch {
+  int dtype, pv_mode, d;
+  int B, H, Nq, Nkv, Nq_pad, Nkv_pad;
+  const void *q, *k, *v;
+  int64_t qs[3], ks[3], vs[3];
+  const float* k_mean_in;
+  BatchInfo bi;
+  sage_quant_bufs bufs;
+  // views into bufs.stats
+  double* stat_ksum;
+  float *stat_kmax, *stat_kmin, *stat_qamax;
+};
+
+struct AttnLaunch {
+  int dtype, pv_mode, d;
+  int B, H, Nq, Nkv, Nq_pad, Nkv_pad;
+  int frame_len, splits;
+  float sigma;  // fp32(sm_scale * log2 e)
+  BatchInfo bi;
+  int order[MAXB_ARGS];  // batches by decreasing kv_len (longest first)
+  sage_quant_bufs bufs;
+  void* o;
+  int64_t os[3];
+};
+
+hipError_t launch_quantize(const QuantLaunch& L, hipStream_t st);
+hipError_t launch_attention(const AttnLaunch& L, hipStream_t st);
+hipError_t launch_debug_scores(const AttnLaunch& L, const int32_t* tiles, int ntiles,
+                               int32_t* out, hipStream_t st);
+hipError_t launch_convert(int kind, const float* in, void* out, int64_t n, hipStream_t st);
+
+}  // namespace sage

@@ -1,0 +1,310 @@
+// Quantize pass: K mean-smoothing, channel balance, per-block INT8 codes for Q
+// and K, and V laid out (and, in FP8 mode, encoded) for the P.V matrix cores.
+//
+// The pages ask SageAttention to beat the precision loss of low-bit compute
+// (podcast notes, section "02:48 There were clearly faster compute units on
+// the hardware") but give no scheme; this is the library's stated one.  Every
+// step is HBM-bound: each kernel streams its tensor once with 16-byte loads.
+// This translation unit is compiled with floating-point contraction off so
+// each operation rounds exactly as written.
+#include "common.h"
+#include "kernels.h"
+
+namespace sage {
+
+// ---------------------------------------------------------------- statistics
+// One thread per (128-token chunk, group of 8 channels).  K: float64 sums in
+// ascending token order, plus max and min; Q: max |x|.  Tokens at or beyond
+// n_valid take no part.
+template <typename T, int D, bool IS_K>
+__global__ __launch_bounds__(256) void stats_partial_kernel(
+    const T* __restrict__ x, int64_t sb, int64_t sh, int64_t sn, int H, int nchunk,
+    BatchInfo bi, int n_all, double* __restrict__ psum, float* __restrict__ pmax,
+    float* __restrict__ pmin) {
+  constexpr int G = D / 8;
+  constexpr int CPB = 256 / G;
+  const int b = blockIdx.z, h = blockIdx.y;
+  const int chunk = blockIdx.x * CPB + threadIdx.x / G;
+  const int g = threadIdx.x % G;
+  if (chunk >= nchunk) return;
+  const int n_valid = IS_K ? bi.kv_len[b] : n_all;
+  const int j0 = chunk * KMEAN_CHUNK;
+  const int j1 = min(j0 + KMEAN_CHUNK, n_valid);
+  const T* base = x + b * sb + h * sh + 8 * g;
+  double s[8];
+  float mx[8], mn[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    s[c] = 0.0;
+    mx[c] = -__builtin_inff();
+    mn[c] = __builtin_inff();
+  }
+#pragma unroll 4
+  for (int j = j0; j < j1; ++j) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(base + j * sn);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const uint32_t bits = (w[c / 2] >> (16 * (c % 2))) & 0xFFFFu;
+      const float v = to_f32(T{static_cast<uint16_t>(bits)});
+      if (IS_K) {
+        s[c] += static_cast<double>(v);
+        mx[c] = fmaxf(mx[c], v);
+        mn[c] = fminf(mn[c], v);
+      } else {
+        mx[c] = fmaxf(mx[c], fabsf(v));
+      }
+    }
+  }
+  const int64_t o = ((static_cast<int64_t>(b) * H + h) * nchunk + chunk) * D + 8 * g;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    if (IS_K) {
+      psum[o + c] = s[c];
+      pmin[o + c] = mn[c];
+    }
+    pmax[o + c] = mx[c];
+  }
+}
+
+// One thread per (b, h, channel): mean, then the channel-balance exponent.
+__global__ void stats_final_kernel(int H, int D, int nchunk_k, int nchunk_q, BatchInfo bi,
+                                   const double* __restrict__ ksum,
+                                   const float* __restrict__ kmax,
+                                   const float* __restrict__ kmin,
+                                   const float* __restrict__ qamax,
+                                   const float* __restrict__ k_mean_in,
+                                   float* __restrict__ mu_out, int8_t* __restrict__ shift_out) {
+  const int bh = blockIdx.x, c = threadIdx.x;
+  if (c >= D) return;
+  const int b = bh / H;
+  const int n = bi.kv_len[b];
+  const int nch = (n + KMEAN_CHUNK - 1) / KMEAN_CHUNK;
+  double s = 0.0;
+  float mx = -__builtin_inff(), mn = __builtin_inff();
+  for (int t = 0; t < nch; ++t) {  // ascending chunk order
+    const int64_t o = (static_cast<int64_t>(bh) * nchunk_k + t) * D + c;
+    s += ksum[o];
+    mx = fmaxf(mx, kmax[o]);
+    mn = fminf(mn, kmin[o]);
+  }
+  float qa = 0.f;
+  for (int t = 0; t < nchunk_q; ++t)
+    qa = fmaxf(qa, qamax[(static_cast<int64_t>(bh) * nchunk_q + t) * D + c]);
+  const float mu = k_mean_in ? k_mean_in[static_cast<int64_t>(bh) * D + c]
+                             : static_cast<float>(s / static_cast<double>(n));
+  // fp32 rounding of K - mu is monotone in K, so the extreme smoothed values
+  // are those of the extreme raw values.
+  const float ka = fmaxf(fabsf(mx - mu), fabsf(mn - mu));
+  int a = 0;
+  if (qa > 0.f && ka > 0.f) {
+    int eq, ek;
+    const float mq = frexpf(qa, &eq);
+    const float mk = frexpf(ka, &ek);
+    const int k = ek - eq - (mk < mq ? 1 : 0);   // floor(log2(ka / qa))
+    a = (k + 1) >= 0 ? (k + 1) / 2 : -((-(k + 1) + 1) / 2);  // floor((k+1)/2)
+  }
+  mu_out[static_cast<int64_t>(bh) * D + c] = mu;
+  shift_out[static_cast<int64_t>(bh) * D + c] = static_cast<int8_t>(a);
+}
+
+// ---------------------------------------------------------------- INT8 blocks
+// One workgroup per block of ROWS tokens of one (b, h).  Each thread holds 8
+// channels of ROWS*D/2048 rows in registers between the amax and the encode.
+template <typename T, int D, int ROWS, bool IS_K>
+__global__ __launch_bounds__(256) void quant_i8_kernel(
+    const T* __restrict__ x, int64_t sb, int64_t sh, int64_t sn, int H, int n_all,
+    int n_pad, BatchInfo bi, const float* __restrict__ mu, const int8_t* __restrict__ shift,
+    int8_t* __restrict__ codes, float* __restrict__ scale) {
+  constexpr int G = D / 8;
+  constexpr int RPP = 256 / G;       // rows per pass
+  constexpr int PASSES = ROWS / RPP;
+  static_assert(ROWS % RPP == 0, "block shape");
+  const int b = blockIdx.z, h = blockIdx.y, blk = blockIdx.x;
+  const int bh = b * H + h;
+  const int g = threadIdx.x % G, r0 = threadIdx.x / G;
+  const int n_valid = IS_K ? bi.kv_len[b] : n_all;
+  float sh_mul[8], m8[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int a = shift[static_cast<int64_t>(bh) * D + 8 * g + c];
+    sh_mul[c] = ldexpf(1.0f, IS_K ? -a : a);   // exact power of two
+    m8[c] = IS_K ? mu[static_cast<int64_t>(bh) * D + 8 * g + c] : 0.f;
+  }
+  float v[PASSES][8];
+  float amax = 0.f;
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int j = blk * ROWS + p * RPP + r0;
+    if (j < n_valid) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(x + b * sb + h * sh + j * sn + 8 * g);
+      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        float f = to_f32(T{static_cast<uint16_t>((w[c / 2] >> (16 * (c % 2))) & 0xFFFFu)});
+        if (IS_K) f = f - m8[c];
+        f = f * sh_mul[c];
+        v[p][c] = f;
+        amax = fmaxf(amax, fabsf(f));
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) v[p][c] = 0.f;
+    }
+  }
+  __shared__ float red[4];
+  amax = wave_max(amax);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float delta = amax > 0.f ? amax / 127.0f : 0.f;
+  const float inv = amax > 0.f ? 127.0f / amax : 0.f;
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int j = blk * ROWS + p * RPP + r0;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      float q = rintf(v[p][c] * inv);
+      q = fminf(fmaxf(q, -127.f), 127.f);
+      const uint32_t byte = static_cast<uint32_t>(static_cast<int>(q)) & 0xFFu;
+      if (c < 4) lo |= byte << (8 * c);
+      else hi |= byte << (8 * (c - 4));
+    }
+    *reinterpret_cast<uint2*>(codes + (static_cast<int64_t>(bh) * n_pad + j) * D + 8 * g) =
+        make_uint2(lo, hi);
+  }
+  if (threadIdx.x == 0) scale[static_cast<int64_t>(bh) * (n_pad / ROWS) + blk] = delta;
+}
+
+// ---------------------------------------------------------------- V layout
+// One workgroup per 64-key chunk of one (b, h); 2*D threads.  Writes the chunk
+// channel-major ([D][64]) so that each lane of the P.V matrix-core operand
+// reads its keys contiguously.  FP8 mode: one E8M0 scale per (32-key block,
+// channel) -- the smallest power of two 2^e with amax * 2^-e <= 448 -- and
+// e4m3fn codes of v * 2^-e.
+template <typename T, int D, bool FP8>
+__global__ __launch_bounds__(2 * D) void prep_v_kernel(
+    const T* __restrict__ x, int64_t sb, int64_t sh, int64_t sn, int H, int n_pad,
+    BatchInfo bi, void* __restrict__ vt, uint8_t* __restrict__ e8m0) {
+  __shared__ uint16_t tile[64][D + 2];
+  const int b = blockIdx.z, h = blockIdx.y, ch = blockIdx.x;
+  const int bh = b * H + h;
+  const int n_valid = bi.kv_len[b];
+  constexpr int GR = D / 8;  // 16-byte granules per key row
+  for (int gi = threadIdx.x; gi < 64 * GR; gi += 2 * D) {
+    const int r = gi / GR, g = gi % GR;
+    const int j = ch * 64 + r;
+    uint4 raw = make_uint4(0, 0, 0, 0);
+    if (j < n_valid) raw = *reinterpret_cast<const uint4*>(x + b * sb + h * sh + j * sn + 8 * g);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) tile[r][8 * g + c] = static_cast<uint16_t>((w[c / 2] >> (16 * (c % 2))) & 0xFFFFu);
+  }
+  __syncthreads();
+  const int c = threadIdx.x >> 1, kh = threadIdx.x & 1;
+  const int64_t chunk_base = (static_cast<int64_t>(bh) * (n_pad / 64) + ch) * D * 64;
+  if (!FP8) {
+    uint32_t w[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      w[k] = static_cast<uint32_t>(tile[32 * kh + 2 * k][c]) |
+             (static_cast<uint32_t>(tile[32 * kh + 2 * k + 1][c]) << 16);
+    uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(vt) + chunk_base + c * 64 + 32 * kh);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) dst[k] = make_uint4(w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]);
+  } else {
+    float f[32];
+    float amax = 0.f;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      f[k] = to_f32(T{tile[32 * kh + k][c]});
+      amax = fmaxf(amax, fabsf(f[k]));
+    }
+    int e = 0;
+    if (amax > 0.f) {
+      int k2;
+      const float m = frexpf(amax, &k2);
+      e = (m <= 0.875f) ? k2 - 9 : k2 - 8;
+    }
+    const float sc = ldexpf(1.0f, -e);
+    uint32_t w[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      w[k] = pack_e4m3x4(f[4 * k] * sc, f[4 * k + 1] * sc, f[4 * k + 2] * sc, f[4 * k + 3] * sc);
+    uint4* dst = reinterpret_cast<uint4*>(static_cast<uint8_t*>(vt) + chunk_base + c * 64 + 32 * kh);
+    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    e8m0[(static_cast<int64_t>(bh) * (n_pad / 32) + 2 * ch + kh) * D + c] = static_cast<uint8_t>(e + 127);
+  }
+}
+
+// ---------------------------------------------------------------- conversions
+template <int KIND>
+__global__ void convert_kernel(const float* __restrict__ in, void* __restrict__ out, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t k = 4 * i;
+  if (k >= n) return;
+  float f[4];
+  for (int t = 0; t < 4; ++t) f[t] = (k + t < n) ? in[k + t] : 0.f;
+  if (KIND == 0) {
+    const uint32_t w = pack_e4m3x4(f[0], f[1], f[2], f[3]);
+    for (int t = 0; t < 4 && k + t < n; ++t) static_cast<uint8_t*>(out)[k + t] = (w >> (8 * t)) & 0xFF;
+  } else {
+    const uint32_t w0 = KIND == 1 ? pack_bf16x2(f[0], f[1]) : pack_f16x2(f[0], f[1]);
+    const uint32_t w1 = KIND == 1 ? pack_bf16x2(f[2], f[3]) : pack_f16x2(f[2], f[3]);
+    const uint16_t hv[4] = {static_cast<uint16_t>(w0 & 0xFFFF), static_cast<uint16_t>(w0 >> 16),
+                            static_cast<uint16_t>(w1 & 0xFFFF), static_cast<uint16_t>(w1 >> 16)};
+    for (int t = 0; t < 4 && k + t < n; ++t) static_cast<uint16_t*>(out)[k + t] = hv[t];
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+template <typename T, int D>
+static hipError_t quantize_impl(const QuantLaunch& L, hipStream_t st) {
+  const dim3 blk(256);
+  constexpr int CPB = 256 / (D / 8);
+  const int nck = (L.Nkv + KMEAN_CHUNK - 1) / KMEAN_CHUNK;
+  const int ncq = (L.Nq + KMEAN_CHUNK - 1) / KMEAN_CHUNK;
+  hipLaunchKernelGGL((stats_partial_kernel<T, D, true>), dim3((nck + CPB - 1) / CPB, L.H, L.B), blk, 0, st,
+                     static_cast<const T*>(L.k), L.ks[0], L.ks[1], L.ks[2], L.H, nck, L.bi, L.Nkv,
+                     L.stat_ksum, L.stat_kmax, L.stat_kmin);
+  hipLaunchKernelGGL((stats_partial_kernel<T, D, false>), dim3((ncq + CPB - 1) / CPB, L.H, L.B), blk, 0, st,
+                     static_cast<const T*>(L.q), L.qs[0], L.qs[1], L.qs[2], L.H, ncq, L.bi, L.Nq,
+                     nullptr, L.stat_qamax, nullptr);
+  hipLaunchKernelGGL(stats_final_kernel, dim3(L.B * L.H), dim3(D), 0, st, L.H, D, nck, ncq, L.bi,
+                     L.stat_ksum, L.stat_kmax, L.stat_kmin, L.stat_qamax, L.k_mean_in,
+                     L.bufs.k_mean, L.bufs.chan_shift);
+  hipLaunchKernelGGL((quant_i8_kernel<T, D, BQ, false>), dim3(L.Nq_pad / BQ, L.H, L.B), blk, 0, st,
+                     static_cast<const T*>(L.q), L.qs[0], L.qs[1], L.qs[2], L.H, L.Nq, L.Nq_pad, L.bi,
+                     L.bufs.k_mean, L.bufs.chan_shift, L.bufs.q_codes, L.bufs.q_scale);
+  hipLaunchKernelGGL((quant_i8_kernel<T, D, BK, true>), dim3(L.Nkv_pad / BK, L.H, L.B), blk, 0, st,
+                     static_cast<const T*>(L.k), L.ks[0], L.ks[1], L.ks[2], L.H, L.Nkv, L.Nkv_pad, L.bi,
+                     L.bufs.k_mean, L.bufs.chan_shift, L.bufs.k_codes, L.bufs.k_scale);
+  if (L.pv_mode == PVFP8)
+    hipLaunchKernelGGL((prep_v_kernel<T, D, true>), dim3(L.Nkv_pad / 64, L.H, L.B), dim3(2 * D), 0, st,
+                       static_cast<const T*>(L.v), L.vs[0], L.vs[1], L.vs[2], L.H, L.Nkv_pad, L.bi,
+                       L.bufs.v_t, L.bufs.v_e8m0);
+  else
+    hipLaunchKernelGGL((prep_v_kernel<T, D, false>), dim3(L.Nkv_pad / 64, L.H, L.B), dim3(2 * D), 0, st,
+                       static_cast<const T*>(L.v), L.vs[0], L.vs[1], L.vs[2], L.H, L.Nkv_pad, L.bi,
+                       L.bufs.v_t, L.bufs.v_e8m0);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize(const QuantLaunch& L, hipStream_t st) {
+  if (L.dtype == DT_BF16)
+    return L.d == 128 ? quantize_impl<bf16_t, 128>(L, st) : quantize_impl<bf16_t, 64>(L, st);
+  return L.d == 128 ? quantize_impl<f16_t, 128>(L, st) : quantize_impl<f16_t, 64>(L, st);
+}
+
+hipError_t launch_convert(int kind, const float* in, void* out, int64_t n, hipStream_t st) {
+  const int64_t threads = (n + 3) / 4;
+  const dim3 grid(static_cast<unsigned>((threads + 255) / 256));
+  if (kind == 0) hipLaunchKernelGGL(convert_kernel<0>, grid, dim3(256), 0, st, in, out, n);
+  else if (kind == 1) hipLaunchKernelGGL(convert_kernel<1>, grid, dim3(256), 0, st, in, out, n);
+  else hipLaunchKernelGGL(convert_kernel<2>, grid, dim3(256), 0, st, in, out, n);
+  return hipGetLastError();
+}
+
+}  // namespace sage

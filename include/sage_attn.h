@@ -1,0 +1,179 @@
+/*
+ * sage_attn.h -- C ABI of a low-bit (SageAttention-style) quantized attention
+ * library for AMD Instinct MI355X (gfx950).
+ *
+ * What it computes.  Quantized softmax attention meant as a drop-in for exact
+ * attention: the podcast notes "Faster! Even faster! ..." (section "37:54 One
+ * line of code, twice the speed") describe replacing FlashAttention with
+ * SageAttention by changing one line, and (section "02:48 There were clearly
+ * faster compute units on the hardware") motivate it by the low-precision
+ * matrix units that exact attention leaves idle while video-generation
+ * attention is compute-bound.  The pages give no quantization scheme; the
+ * scheme of this library is:
+ *   - K mean-smoothing: mu[b,h,:] = mean of the valid keys, subtracted from K;
+ *   - channel balance: per (b,h,channel) power-of-two exponent a moving range
+ *     between Q (x 2^a) and K (x 2^-a), exact in binary floating point;
+ *   - symmetric INT8 per block: Q in blocks of 128 tokens, K in blocks of 64,
+ *     scale = amax/127, code = rint(x * (127/amax));
+ *   - S = Q K^T on INT8 matrix cores with int32 accumulation, dequantized in
+ *     fp32, online softmax in fp32 over 64-key chunks with a lazy running max;
+ *   - P V on 16-bit matrix cores (P rounded to the input type) or, in FP8
+ *     mode, on scaled FP8 matrix cores: P as OCP e4m3fn (pre-scaled by 2^4),
+ *     V as e4m3fn with one E8M0 scale per (32-key block, channel).
+ * Frame-block-causal mask for streaming against a KV cache (the Vidu S1 blog,
+ * sections "模型架构", "训练方法" and "Infra": frame-by-frame causal
+ * generation over cached history): with frame length F > 0, query i
+ * (absolute position q_pos0[b] + i) sees key j iff j < kv_len[b] and
+ * floor(j/F) <= floor((q_pos0[b]+i)/F).  F = 0: every key j < kv_len[b].
+ *
+ * Tensors.  Q [B,H,Nq,d], K and V [B,H,Nkv,d], O [B,H,Nq,d], all of one
+ * 16-bit type (fp16 or bf16), device memory, channel dimension contiguous,
+ * strides of the b, h and n dimensions given in ELEMENTS.  d is 64 or 128.
+ *
+ * Ownership.  The caller allocates every device buffer (inputs, output,
+ * workspace); the library never allocates, frees or synchronizes (except
+ * under SAGE_FLAG_DEBUG_SYNC).  Host arrays (kv_len, q_pos0) are read during
+ * the call only.  Buffers must stay alive until the enqueued work completes.
+ * O must not alias Q, K, V or the workspace.
+ *
+ * Errors.  Every entry point returns a sage_status.  Arguments are validated
+ * on the host before anything is enqueued; on an error nothing is enqueued
+ * and sage_attn_last_error() (thread-local) describes it.  SAGE_OK means
+ * "enqueued"; a fault inside a kernel surfaces at the caller's next
+ * synchronization.  No C++ exception crosses this boundary.
+ *
+ * Streams.  `stream` is a hipStream_t (NULL = the default stream).  Calls are
+ * thread-safe and contain no allocation or synchronization, so they can be
+ * captured into a hipGraph.
+ */
+#ifndef SAGE_ATTN_H
+#define SAGE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SAGE_ATTN_ABI_VERSION 1
+
+typedef enum {
+  SAGE_OK = 0,
+  SAGE_E_NULL = 1,        /* a required pointer is NULL                      */
+  SAGE_E_SHAPE = 2,       /* a size is out of range                          */
+  SAGE_E_DTYPE = 3,       /* unknown dtype or pv_mode                        */
+  SAGE_E_STRIDE = 4,      /* a stride is not a multiple of 8 elements        */
+  SAGE_E_ALIGN = 5,       /* a device pointer is not 16-byte aligned         */
+  SAGE_E_MASK = 6,        /* kv_len / q_pos0 / frame_len inconsistent        */
+  SAGE_E_UNSUPPORTED = 7, /* d not in {64,128}, B > SAGE_MAX_BATCH, ...      */
+  SAGE_E_WORKSPACE = 8,   /* workspace missing or too small                  */
+  SAGE_E_VERSION = 9,     /* desc->abi_version != SAGE_ATTN_ABI_VERSION      */
+  SAGE_E_HIP = 10         /* a kernel launch failed (see last_error)         */
+} sage_status;
+
+enum { SAGE_F16 = 0, SAGE_BF16 = 1 };       /* sage_attn_desc.dtype          */
+enum { SAGE_PV_16 = 0, SAGE_PV_FP8 = 1 };   /* sage_attn_desc.pv_mode        */
+
+#define SAGE_FLAG_DEBUG_SYNC 0x1u  /* synchronize the stream after each launch */
+#define SAGE_MAX_BATCH 128
+#define SAGE_MAX_SPLITS 16
+
+typedef struct sage_attn_desc {
+  int32_t abi_version;  /* must be SAGE_ATTN_ABI_VERSION                      */
+  int32_t dtype;        /* SAGE_F16 | SAGE_BF16: Q, K, V and O share it       */
+  int32_t pv_mode;      /* SAGE_PV_16 | SAGE_PV_FP8                           */
+  int32_t B, H, Nq, Nkv, d; /* Nkv = allocated key length (>= every kv_len) */
+  int32_t frame_len;    /* 0: no mask; > 0: frame-block-causal, F tokens      */
+  int32_t kv_splits;    /* 0: chosen by the library; 1..SAGE_MAX_SPLITS       */
+  float sm_scale;       /* softmax scale; 0 -> 1/sqrt(d)                      */
+  uint32_t flags;       /* SAGE_FLAG_*                                        */
+  int64_t q_stride[3], k_stride[3], v_stride[3], o_stride[3]; /* b, h, n     */
+  const int32_t *kv_len; /* host [B] valid keys per batch, or NULL (all Nkv)  */
+  const int32_t *q_pos0; /* host [B] absolute position of query 0, or NULL:
+                            kv_len[b] - Nq when frame_len > 0                 */
+  const float *k_mean_in; /* device [B,H,d] fixed mean to use, or NULL      */
+} sage_attn_desc;
+
+/* Quantized operands, in caller-owned device memory (normally carved out of
+ * the workspace by sage_attn_quant_layout).  Nq_pad = ceil(Nq/128)*128 and
+ * Nkv_pad = ceil(Nkv/128)*128; padding positions hold code 0 and scale 0. */
+typedef struct sage_quant_bufs {
+  int8_t *q_codes;     /* [B,H,Nq_pad,d] row-major                            */
+  float *q_scale;      /* [B,H,Nq_pad/128]                                    */
+  int8_t *k_codes;     /* [B,H,Nkv_pad,d] row-major                           */
+  float *k_scale;      /* [B,H,Nkv_pad/64]                                    */
+  float *k_mean;       /* [B,H,d]                                             */
+  int8_t *chan_shift;  /* [B,H,d] channel-balance exponents a                 */
+  void *v_t;           /* [B,H,Nkv_pad/64,d,64]: per 64-key chunk, V transposed
+                          (channel-major); 16-bit values in SAGE_PV_16 mode,
+                          e4m3fn codes in SAGE_PV_FP8 mode                    */
+  uint8_t *v_e8m0;     /* [B,H,Nkv_pad/32,d] E8M0 bytes (FP8 mode), else NULL */
+  void *stats;         /* internal: partial statistics of the quantize pass   */
+  void *partial;       /* internal: split-KV partial results                  */
+} sage_quant_bufs;
+
+/* Version of the library's ABI (SAGE_ATTN_ABI_VERSION it was built with). */
+int sage_attn_abi_version(void);
+
+/* Static description of a status code. */
+const char *sage_attn_status_string(int status);
+
+/* Thread-local text of the last error reported by this thread. */
+const char *sage_attn_last_error(void);
+
+/* Value of a named scheme constant ("BQ", "BK", "VB", "QMAX", "TAU",
+ * "PSHIFT_FP8", "PSHIFT_16", "KMEAN_CHUNK"), for cross-checks.
+ * Returns SAGE_E_UNSUPPORTED for an unknown name. */
+int sage_attn_constant(const char *name, double *value);
+
+/* Number of KV splits the library will use for *desc (kv_splits, or its own
+ * choice when kv_splits == 0).  Split s of batch b covers the 64-key chunks
+ * [s*n/S, (s+1)*n/S) with n = ceil(kv_len[b]/64); partial results are merged
+ * exactly as the online softmax would. */
+int sage_attn_kv_splits(const sage_attn_desc *desc, int32_t *splits);
+
+/* Bytes of workspace sage_attn_fwd needs for *desc (validated first). */
+int sage_attn_workspace_size(const sage_attn_desc *desc, size_t *bytes);
+
+/* Carve the quantized-operand buffers out of a workspace of ws_bytes bytes
+ * (256-byte aligned sub-buffers).  Host-only: enqueues nothing. */
+int sage_attn_quant_layout(const sage_attn_desc *desc, void *ws, size_t ws_bytes,
+                           sage_quant_bufs *out);
+
+/* Quantize: K mean (unless k_mean_in), channel balance, INT8 Q and K codes and
+ * scales, V prepared for P.V (transposed; FP8 codes and E8M0 scales in FP8
+ * mode).  q, k, v: device inputs as described by desc. */
+int sage_attn_quantize(const sage_attn_desc *desc, const void *q, const void *k,
+                       const void *v, const sage_quant_bufs *bufs, void *stream);
+
+/* Fused attention on already-quantized operands: writes O [B,H,Nq,d]. */
+int sage_attn_fwd_quantized(const sage_attn_desc *desc, const sage_quant_bufs *bufs,
+                            void *o, void *stream);
+
+/* Drop-in call: quantize into the workspace, then attend.  Equivalent to
+ * sage_attn_quant_layout + sage_attn_quantize + sage_attn_fwd_quantized. */
+int sage_attn_fwd(const sage_attn_desc *desc, const void *q, const void *k,
+                  const void *v, void *o, void *ws, size_t ws_bytes, void *stream);
+
+/* Test support: exact int32 scores S = qcodes . kcodes^T of ntiles tiles of
+ * 32 queries x 64 keys, computed by the same matrix-core routine as the fused
+ * kernel.  tiles: host [ntiles][3] = {b*H + h, q0 (multiple of 32),
+ * k0 (multiple of 64)} within the padded sizes; out: device [ntiles][32][64]
+ * int32, row = query q0+r, column = key k0+c. */
+int sage_attn_debug_scores(const sage_attn_desc *desc, const sage_quant_bufs *bufs,
+                           const int32_t *tiles, int32_t ntiles, int32_t *out,
+                           void *stream);
+
+/* Test support: convert n float32 values with the kernels' own conversion
+ * routines.  kind 0: e4m3fn bytes (as P is converted in FP8 mode);
+ * 1: bf16 bits; 2: fp16 bits (uint16).  Inputs for kind 0 must satisfy
+ * |x| <= 448. */
+int sage_attn_debug_convert(int kind, const float *in, void *out, int64_t n,
+                            void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAGE_ATTN_H */

@@ -1,0 +1,118 @@
+"""CPU checks of the C ABI: the library loads, exports every declared entry
+point, agrees with the oracle on the scheme's constants, and rejects bad
+arguments on the host before anything would be enqueued.  No kernel runs."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_quantized_attention_sage_amd as sage
+from oracle import constants as oc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sage_attn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sage.LIB_PATH):
+        pytest.skip("libsage_attn.so not built")
+    return sage.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sage_attn_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ("sage_attn_quantize", "sage_attn_fwd", "sage_attn_fwd_quantized",
+                 "sage_attn_workspace_size", "sage_attn_quant_layout", "sage_attn_debug_scores"):
+        assert must in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    raw = ctypes.CDLL(sage.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+
+
+def test_constants_agree_with_oracle(lib):
+    for name in ("BQ", "BK", "VB", "QMAX", "TAU", "PSHIFT_FP8", "PSHIFT_16", "KMEAN_CHUNK"):
+        assert sage.sage_attn_constant(name) == getattr(oc, name), name
+    with pytest.raises(sage.SageError):
+        sage.sage_attn_constant("NOPE")
+
+
+def _desc(**kw):
+    base = dict(B=1, H=2, Nq=100, Nkv=300, d=128, dtype=sage.SAGE_BF16)
+    base.update(kw)
+    return sage.Desc(**base)
+
+
+def _status(desc):
+    n = ctypes.c_size_t()
+    return sage.load().sage_attn_workspace_size(desc.ptr, ctypes.byref(n)), n.value
+
+
+def test_valid_desc_and_workspace(lib):
+    st, n = _status(_desc())
+    assert st == 0 and n > 0
+    st8, n8 = _status(_desc(pv_mode=sage.SAGE_PV_FP8))
+    assert st8 == 0 and n8 != n
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=96), 7), (dict(B=0), 2), (dict(Nq=0), 2), (dict(dtype=5), 3), (dict(pv_mode=3), 3),
+    (dict(frame_len=-1), 6), (dict(kv_splits=99), 2), (dict(B=1, kv_len=[301]), 6),
+    (dict(B=1, kv_len=[0]), 6), (dict(B=1, frame_len=50, kv_len=[120], q_pos0=[30]), 6),
+    (dict(q_stride=(100 * 128 * 2, 100 * 128, 127)), 4), (dict(B=129), 7),
+    (dict(sm_scale=float("nan")), 2),
+])
+def test_bad_descriptors_are_rejected(lib, kw, code):
+    st, _ = _status(_desc(**kw))
+    assert st == code, sage.load().sage_attn_last_error()
+    assert sage.load().sage_attn_last_error()
+
+
+def test_version_mismatch(lib):
+    d = _desc()
+    d.c.abi_version = 7
+    assert _status(d)[0] == 9
+
+
+def test_null_and_small_workspace_rejected(lib):
+    d = _desc()
+    b = sage.sage_quant_bufs()
+    L = sage.load()
+    assert L.sage_attn_quant_layout(d.ptr, None, 0, ctypes.byref(b)) == 8
+    assert L.sage_attn_quant_layout(d.ptr, ctypes.c_void_p(256), 16, ctypes.byref(b)) == 8
+    assert L.sage_attn_quant_layout(d.ptr, ctypes.c_void_p(257), 1 << 40, ctypes.byref(b)) == 5
+    assert L.sage_attn_quantize(d.ptr, None, None, None, ctypes.byref(b), None) == 1
+    assert L.sage_attn_fwd_quantized(d.ptr, ctypes.byref(b), None, None) == 1
+    assert L.sage_attn_fwd(d.ptr, None, None, None, None, None, 0, None) == 8
+
+
+def test_layout_is_host_only_and_aligned(lib):
+    d = _desc(pv_mode=sage.SAGE_PV_FP8)
+    st, n = _status(d)
+    b = sage.sage_quant_bufs()
+    fake = 1 << 20  # never dereferenced: layout only does pointer arithmetic
+    assert sage.load().sage_attn_quant_layout(d.ptr, ctypes.c_void_p(fake), n, ctypes.byref(b)) == 0
+    ptrs = [b.q_codes, b.q_scale, b.k_codes, b.k_scale, b.k_mean, b.chan_shift, b.v_t, b.v_e8m0, b.stats]
+    assert all(p % 256 == 0 and fake <= p < fake + n for p in ptrs)
+    assert len(set(ptrs)) == len(ptrs)
+
+
+def test_auto_splits(lib):
+    # 24 heads x 16 query tiles leave the 256 CUs short of work: split the keys
+    d = sage.Desc(1, 24, 2040, 34680, 128, sage.SAGE_BF16, frame_len=2040)
+    assert sage.sage_attn_kv_splits(d) > 1
+    big = sage.Desc(1, 40, 75600, 75600, 128, sage.SAGE_BF16)
+    assert sage.sage_attn_kv_splits(big) == 1
+    fixed = sage.Desc(1, 2, 1024, 1024, 64, sage.SAGE_F16, kv_splits=3)
+    assert sage.sage_attn_kv_splits(fixed) == 3

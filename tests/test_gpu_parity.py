@@ -1,0 +1,183 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Integer and byte results (K mean, channel shifts, INT8 codes and scales, V
+layout / FP8 codes and E8M0 scales, int32 scores) must be bit-exact; outputs
+must be within max-abs 2e-3 of the oracle's emulation of the same scheme and
+reach cosine >= 0.999 against float64 attention on the workload shapes.
+Shapes here are small enough for the oracle to finish in seconds while
+spanning several tiles and ragged tails; full-size workloads are in
+test_gpu_workloads.py.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import bit_quantized_attention_sage_amd as sage
+import workloads
+from oracle import quant, emulate, attention, codecs
+from oracle.constants import PV_16, PV_FP8
+from gpu_util import (run_gpu, host, check_quantized, emulate_like_gpu, compare_output, cosine, NAME_DT)
+
+pytestmark = pytest.mark.gpu
+
+
+def _assert_close(og, o64, dtype, pv_mode):
+    mx, excess, frac, rel, rel_bound = compare_output(og, o64, dtype, pv_mode)
+    print(f"  max-abs {mx:.3e} excess {excess:.2e} beyond-rounding {frac:.2e} "
+          f"rel-L2 {rel:.3e} (bound {rel_bound:.1e})")
+    assert excess <= 0
+    assert frac <= (1e-4 if pv_mode == PV_16 else 2e-2)
+    assert rel <= rel_bound
+
+
+def _rand(shape, dtype, seed, scale=1.0, offset=None):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(shape, generator=g) * scale
+    if offset is not None:
+        x = x + offset
+    return x.to(dtype)
+
+
+def test_convert_e4m3_exhaustive(lib):
+    pos = codecs.e4m3_decode(np.arange(127, dtype=np.uint8))
+    mids = (pos[1:] + pos[:-1]) / 2
+    vals = np.concatenate([pos, mids, np.nextafter(mids, 0), np.nextafter(mids, 1e9),
+                           np.random.default_rng(0).uniform(0, 448, 100000)])
+    vals = np.concatenate([vals, -vals]).astype(np.float32)
+    vals = vals[np.abs(vals) <= 448]
+    x = torch.from_numpy(vals).cuda()
+    out = torch.empty(len(vals), dtype=torch.uint8, device="cuda")
+    sage.sage_attn_debug_convert(0, x, out)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.cpu().numpy(), codecs.e4m3_encode(vals.astype(np.float64)))
+
+
+@pytest.mark.parametrize("kind", [1, 2])
+def test_convert_16bit(lib, kind):
+    rng = np.random.default_rng(kind)
+    x = (rng.standard_normal(200000) * 2.0 ** rng.integers(-20, 12, 200000)).astype(np.float32)
+    u = rng.integers(0, 2 ** 30, 4000).astype(np.uint32)
+    ties = ((u & np.uint32(0x3F7F0000)) | np.uint32(0x8000)).view(np.float32)
+    x = np.concatenate([x, ties, -ties])
+    out = torch.empty(len(x), dtype=torch.int16, device="cuda")
+    sage.sage_attn_debug_convert(kind, torch.from_numpy(x).cuda(), out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint16)
+    ref = codecs.bf16_bits(x) if kind == 1 else x.astype(np.float16).view(np.uint16)
+    np.testing.assert_array_equal(got, ref)
+
+
+CASES = [
+    # (B, H, Nq, Nkv, d, dtype, frame_len, kv_len, q_pos0, kv_splits)
+    (1, 2, 1024, 1024, 64, torch.float16, 0, None, None, 1),      # the tiny workload's shape
+    (1, 1, 1, 1, 128, torch.bfloat16, 0, None, None, 1),          # one query, one key
+    (1, 1, 65, 63, 128, torch.bfloat16, 0, None, None, 1),        # sub-tile tails
+    (1, 2, 129, 1000, 128, torch.bfloat16, 0, None, None, 1),     # ragged, many chunks
+    (2, 1, 300, 777, 64, torch.float16, 0, [777, 131], None, 1),  # ragged kv_len per batch
+    (3, 2, 200, 700, 128, torch.bfloat16, 100, [700, 350, 213], None, 1),  # frames inside a tile
+    (1, 2, 250, 900, 128, torch.bfloat16, 64, None, [500], 1),    # explicit q_pos0, 64-key frames
+    (2, 2, 256, 2000, 128, torch.bfloat16, 0, [2000, 1500], None, 4),     # forced KV splits
+    (1, 3, 300, 1300, 128, torch.bfloat16, 250, None, None, 3),   # splits with a causal mask
+]
+
+
+def _ids(c):
+    return f"B{c[0]}H{c[1]}q{c[2]}k{c[3]}d{c[4]}{'f16' if c[5] == torch.float16 else 'bf16'}F{c[6]}s{c[9]}"
+
+
+@pytest.mark.parametrize("pv_mode", [PV_16, PV_FP8], ids=["pv16", "pvfp8"])
+@pytest.mark.parametrize("case", CASES, ids=[_ids(c) for c in CASES])
+def test_parity(lib, case, pv_mode):
+    B, H, Nq, Nkv, d, dt, F, kv_len, q_pos0, splits = case
+    seed = hash((B, H, Nq, Nkv, d, F, pv_mode)) % 10000
+    q = _rand((B, H, Nq, d), dt, seed)
+    k = _rand((B, H, Nkv, d), dt, seed + 1, offset=_rand((1, H, 1, d), torch.float32, seed + 2) * 2)
+    v = _rand((B, H, Nkv, d), dt, seed + 3)
+    if kv_len is not None:
+        for b in range(B):
+            k[b, :, kv_len[b]:] = 0
+            v[b, :, kv_len[b]:] = 0
+    print(f"case {_ids(case)} pv {pv_mode}", flush=True)
+    out, views, desc, _, _ = run_gpu(q.cuda(), k.cuda(), v.cuda(), pv_mode, F, kv_len, q_pos0, splits)
+    Q, K, V = host(q), host(k), host(v)
+    check_quantized(views, Q, K, V, pv_mode, NAME_DT[dt], kv_len)
+    o64 = emulate_like_gpu(Q, K, V, pv_mode, NAME_DT[dt], desc, F, kv_len, q_pos0)
+    og = host(out)
+    _assert_close(og, o64, NAME_DT[dt], pv_mode)
+    ref = attention.attention_fp64(Q, K, V, frame_len=F, kv_len=kv_len, q_pos0=q_pos0)
+    cs = cosine(og, ref)
+    print(f"  cosine vs fp64 {cs:.6f}")
+    assert cs >= (0.999 if pv_mode == PV_16 else 0.998)
+
+
+def test_strided_inputs_and_frozen_mean(lib):
+    """[B,N,H,d] tensors viewed as [B,H,N,d] (non-contiguous strides), and a
+    caller-given K mean (a frozen cache mean): codes follow that mean."""
+    B, H, N, d = 2, 3, 333, 128
+    qb = _rand((B, N, H, d), torch.bfloat16, 7)
+    kb = _rand((B, N, H, d), torch.bfloat16, 8, offset=1.5)
+    vb = _rand((B, N, H, d), torch.bfloat16, 9)
+    q, k, v = (t.cuda().permute(0, 2, 1, 3) for t in (qb, kb, vb))
+    Q, K, V = (host(t) for t in (q, k, v))
+    mu = (quant.k_mean(K) + np.float32(0.25)).astype(np.float32)
+    out, views, desc, _, _ = run_gpu(q, k, v, PV_16, k_mean_in=torch.from_numpy(mu).cuda())
+    np.testing.assert_array_equal(views["k_mean"].cpu().numpy(), mu)
+    check_quantized(views, Q, K, V, PV_16, "bf16", None, mu_in=mu)
+    o64 = emulate_like_gpu(Q, K, V, PV_16, "bf16", desc, mu=mu)
+    _assert_close(host(out), o64, "bf16", PV_16)
+
+
+def test_int32_scores_bit_exact(lib):
+    B, H, Nq, Nkv, d = 1, 2, 300, 700, 128
+    q = _rand((B, H, Nq, d), torch.bfloat16, 11).cuda()
+    k = _rand((B, H, Nkv, d), torch.bfloat16, 12, scale=3.0).cuda()
+    v = _rand((B, H, Nkv, d), torch.bfloat16, 13).cuda()
+    _, views, desc, ws, bufs = run_gpu(q, k, v, PV_16)
+    rng = np.random.default_rng(5)
+    tiles = [(int(rng.integers(0, B * H)), 32 * int(rng.integers(0, desc.Nq_pad // 32)),
+              64 * int(rng.integers(0, desc.Nkv_pad // 64))) for _ in range(40)]
+    tiles += [(1, desc.Nq_pad - 32, desc.Nkv_pad - 64), (0, 288, 640)]   # tails
+    out = torch.empty((len(tiles), 32, 64), dtype=torch.int32, device="cuda")
+    sage.sage_attn_debug_scores(desc, bufs, tiles, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    Q, K = host(q), host(k)
+    mu = quant.k_mean(K)
+    a = quant.channel_shift(Q, K, mu)
+    qc, _ = quant.quantize_q(Q, a)
+    kc, _ = quant.quantize_k(K, mu, None, a)
+    qcp = np.zeros((B, H, desc.Nq_pad, d), np.int8)
+    qcp[:, :, :Nq] = qc
+    kcp = np.zeros((B, H, desc.Nkv_pad, d), np.int8)
+    kcp[:, :, :Nkv] = kc
+    for t, (bh, q0, k0) in enumerate(tiles):
+        ref = emulate.scores_int(qcp[0, bh, q0:q0 + 32], kcp[0, bh, k0:k0 + 64])
+        np.testing.assert_array_equal(got[t], ref)
+
+
+def test_repeatable_and_stream(lib):
+    """Two runs give bit-identical output; a non-default stream works."""
+    w = workloads.get("tiny")
+    x = workloads.make(w, "cuda")
+    o1 = sage.attention(x["q"], x["k"], x["v"], pv_mode=PV_FP8)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o2 = sage.attention(x["q"], x["k"], x["v"], pv_mode=PV_FP8, stream=s)
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+def test_guard_canaries(lib):
+    """The output of a ragged shape written inside a larger buffer: nothing
+    outside [B,H,Nq,d] changes."""
+    B, H, Nq, Nkv, d = 1, 2, 77, 200, 128
+    q = _rand((B, H, Nq, d), torch.bfloat16, 21).cuda()
+    k = _rand((B, H, Nkv, d), torch.bfloat16, 22).cuda()
+    v = _rand((B, H, Nkv, d), torch.bfloat16, 23).cuda()
+    big = torch.full((B * H * Nq * d + 4096,), 7.0, dtype=torch.bfloat16, device="cuda")
+    o = big[2048:2048 + B * H * Nq * d].view(B, H, Nq, d)
+    sage.attention(q, k, v, out=o)
+    torch.cuda.synchronize()
+    assert torch.all(big[:2048] == 7.0) and torch.all(big[2048 + B * H * Nq * d:] == 7.0)
