@@ -114,17 +114,144 @@ struct AttnArgs {
   int order[MAXB_ARGS];
 };
 
+// LDS layout of a staged chunk.  K: [64 keys][D] bytes with the granule
+// swizzle above.  V^T: [D channels][64 keys] with each channel row padded by
+// 16 bytes (80 B in FP8, 144 B in 16-bit mode) so that the 8 lanes of one
+// ds_read_b128 phase, which read consecutive channels, hit distinct banks.
+template <int PV>
+struct VRow {
+  static constexpr int BYTES = (PV == PVFP8) ? 64 : 128;  // payload per channel row
+  static constexpr int STRIDE = BYTES + 16;
+};
+
+// Per-wave online-softmax state and the math of one chunk.
+template <int D, int PV, int DT>
+struct WaveState {
+  static constexpr int NCB = D / 32;
+  static constexpr int SHIFT = (PV == PVFP8) ? PSHIFT_FP8 : PSHIFT_16;
+  static constexpr int VS = VRow<PV>::STRIDE;
+  v16f o[NCB];
+  float m, l;
+
+  // One 64-key chunk: S^T on i8 MFMAs, dequantize, lazy running max, p = 2^x,
+  // P.V on 16-bit or scaled FP8 MFMAs.  masked (wave-uniform): keys at or
+  // beyond this row's visible end `re` get p = 0 and do not enter the maximum.
+  __device__ __forceinline__ void chunk(const int8_t* klds, const uint8_t* vlds, const uint8_t* elds,
+                                        const v4i* qv, float c, bool masked, int kb, int re, int lane) {
+    const int h2 = lane >> 5, r32 = lane & 31;
+    v16i s0, s1;
+    qk_chunk<D>(klds, qv, lane, s0, s1);
+    if (masked) {  // boundary chunk only: invisible keys get the sentinel score
+      asm volatile("");  // keep this a real branch: no if-conversion into every chunk
+      const int lim = re - kb;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        s0[i] = (i < lim) ? s0[i] : SENTINEL;
+        s1[i] = (32 + i < lim) ? s1[i] : SENTINEL;
+      }
+    }
+    int mx = max(s0[0], s1[0]);
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = max(mx, max(s0[i], s1[i]));
+    {  // combine the two lane halves, which hold the same query
+      const auto sw = __builtin_amdgcn_permlane32_swap(mx, mx, false, false);
+      mx = max(static_cast<int>(sw[0]), static_cast<int>(sw[1]));
+    }
+    const float tm = static_cast<float>(mx) * c;
+    const bool upd = (!masked || kb - 16 * h2 < re) && (tm > m + TAU);
+    if (__any(upd)) {
+      const float alpha = upd ? __builtin_amdgcn_exp2f(m - tm) : 1.0f;
+      m = upd ? tm : m;
+      l *= alpha;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[cb][i] *= alpha;
+    }
+    const float nmref = -(m - static_cast<float>(SHIFT));
+    float p0[16], p1[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      p0[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(static_cast<float>(s0[i]), c, nmref));
+      p1[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(static_cast<float>(s1[i]), c, nmref));
+    }
+    if (masked) {  // the sentinel marks the invisible keys: exactly p = 0 there
+      asm volatile("");
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        p0[i] = (s0[i] != SENTINEL) ? p0[i] : 0.f;
+        p1[i] = (s1[i] != SENTINEL) ? p1[i] : 0.f;
+      }
+    }
+    float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      ls0 += p0[i];
+      ls1 += p1[i];
+    }
+    l += ls0 + ls1;
+
+    if (PV == PVFP8) {
+      v8i pb;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        pb[k] = static_cast<int>(pack_e4m3x4(p0[4 * k], p0[4 * k + 1], p0[4 * k + 2], p0[4 * k + 3]));
+        pb[4 + k] = static_cast<int>(pack_e4m3x4(p1[4 * k], p1[4 * k + 1], p1[4 * k + 2], p1[4 * k + 3]));
+      }
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const int chn = 32 * cb + r32;
+        const uint8_t* vrow = vlds + chn * VS + 16 * h2;
+        const v4i lo = *reinterpret_cast<const v4i*>(vrow);
+        const v4i hi = *reinterpret_cast<const v4i*>(vrow + 32);
+        const v8i va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        const int sc = static_cast<int>(elds[h2 * D + chn]);
+        o[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, o[cb], 0, 0, 0, sc, 0, 127);
+      }
+    } else {
+      uint32_t pw[16];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        pw[k] = Pack16<DT>::pack(p0[2 * k], p0[2 * k + 1]);
+        pw[8 + k] = Pack16<DT>::pack(p1[2 * k], p1[2 * k + 1]);
+      }
+#pragma unroll
+      for (int mu = 0; mu < 4; ++mu) {
+        const v4i pbv = {static_cast<int>(pw[4 * mu]), static_cast<int>(pw[4 * mu + 1]),
+                         static_cast<int>(pw[4 * mu + 2]), static_cast<int>(pw[4 * mu + 3])};
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          const int chn = 32 * cb + r32;
+          const v4i va = *reinterpret_cast<const v4i*>(
+              vlds + chn * VS + (32 * (mu >> 1) + 16 * h2 + 8 * (mu & 1)) * 2);
+          if (DT == DT_BF16)
+            o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, va),
+                                                            __builtin_bit_cast(v8bf, pbv), o[cb], 0, 0, 0);
+          else
+            o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, va),
+                                                           __builtin_bit_cast(v8h, pbv), o[cb], 0, 0, 0);
+        }
+      }
+    }
+  }
+};
+
 template <int D, int PV, int DT>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
   constexpr int NCB = D / 32;                    // 32-channel blocks of O
   constexpr int VBYTES = (PV == PVFP8) ? 1 : 2;  // bytes per V element
-  constexpr int SHIFT = (PV == PVFP8) ? PSHIFT_FP8 : PSHIFT_16;
-  __shared__ __attribute__((aligned(16))) int8_t klds[64 * D];
-  __shared__ __attribute__((aligned(16))) uint8_t vlds[64 * D * VBYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t elds[2 * D];
+  constexpr int VS = VRow<PV>::STRIDE;
+  constexpr int VGR = VRow<PV>::BYTES / 16;      // 16-byte granules per V^T channel row
+  constexpr int KG = 64 * D / 16 / 256;          // K granules each thread stages
+  constexpr int VG = 64 * D * VBYTES / 16 / 256; // V granules each thread stages
+  static_assert(KG >= 1 && KG <= 2 && VG >= 1 && VG <= 4, "staging shape");
+  __shared__ __attribute__((aligned(16))) int8_t klds[2][64 * D];
+  __shared__ __attribute__((aligned(16))) uint8_t vlds[2][D * VS];
+  __shared__ __attribute__((aligned(16))) uint8_t elds[2][2 * D];
+  __shared__ float kslds[2];  // the staged chunk's K scale
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int h2 = lane >> 5, r32 = lane & 31;
+  const int h2 = lane >> 5;
 
   // ---- work item: (batch by decreasing kv_len, head, split, query tile)
   const int L = xcd_remap(blockIdx.x, A.total);
@@ -144,139 +271,99 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
   const int c_hi = (split + 1) * nch_b / A.splits;
 
   // ---- this lane's query row and the end of its visible key range
-  const int qi = qt * BQ + w * 32 + r32;
+  const int qi = qt * BQ + w * 32 + (lane & 31);
   const int qi_valid = min(qi, A.Nq - 1);
   int re = kv_len;
   if (A.frame_len > 0) re = min(kv_len, ((q_pos0 + qi_valid) / A.frame_len + 1) * A.frame_len);
-  const int wave_end = wave_max_i(re);
-  const int wave_min = wave_min_i(re);
   const int wg_end = A.frame_len > 0
                          ? min(kv_len, ((q_pos0 + min(qt * BQ + BQ - 1, A.Nq - 1)) / A.frame_len + 1) *
                                            A.frame_len)
                          : kv_len;
-  const int wave_hi = min(c_hi, (wave_end + 63) / 64);
-  const int wave_full = wave_min / 64;  // chunks below this are visible to every row
+  // wave-uniform loop bounds, kept in scalar registers
+  const int wave_hi = __builtin_amdgcn_readfirstlane(min(c_hi, (wave_max_i(re) + 63) / 64));
+  const int wave_full = __builtin_amdgcn_readfirstlane(wave_min_i(re) / 64);  // unmasked below this
   const int wg_hi = min(c_hi, (wg_end + 63) / 64);
 
   v4i qv[D / 32];
   load_q<D>(qv, A.qc + (static_cast<int64_t>(bh) * A.Nq_pad + qi) * D, h2);
   const float qsc = A.qscale[static_cast<int64_t>(bh) * A.nqt + qt] * A.sigma;
 
-  v16f o[NCB];
+  WaveState<D, PV, DT> st;
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) o[cb] = v16f{0.f};
-  float m = -__builtin_inff();
-  float l = 0.f;
+  for (int cb = 0; cb < NCB; ++cb) st.o[cb] = v16f{0.f};
+  st.m = -__builtin_inff();
+  st.l = 0.f;
 
   const int nkc = A.Nkv_pad / 64;
   const int8_t* kbase = A.kc + static_cast<int64_t>(bh) * A.Nkv_pad * D;
   const uint8_t* vbase = static_cast<const uint8_t*>(A.vt) + static_cast<int64_t>(bh) * nkc * 64 * D * VBYTES;
+  const uint8_t* ebase = A.ve + static_cast<int64_t>(bh) * (A.Nkv_pad / 32) * D;
   const float* ksc = A.kscale + static_cast<int64_t>(bh) * nkc;
 
+  // Staging of chunk `ch` through registers: buffer loads (per-thread offsets
+  // fixed in VGPRs, the chunk offset in an SGPR) are issued one chunk ahead
+  // and written to the other LDS buffer after the current chunk's math.
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(kbase), 0, nkc * 64 * D, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(vbase), 0, nkc * 64 * D * VBYTES, 0x00020000);
+  const __amdgpu_buffer_rsrc_t ers = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(ebase), 0, PV == PVFP8 ? (A.Nkv_pad / 32) * D : 0, 0x00020000);
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(ksc), 0, nkc * 4, 0x00020000);
+  const int voff = tid * 16;
+  v4i rk0, rk1, rv0, rv1, rv2, rv3, re8;
+  float rks;
+  auto fetch = [&](int ch) {
+    const int ko = ch * 64 * D, vo = ch * 64 * D * VBYTES;
+    rk0 = __builtin_amdgcn_raw_buffer_load_b128(krs, voff, ko, 0);
+    if (KG > 1) rk1 = __builtin_amdgcn_raw_buffer_load_b128(krs, voff, ko + 4096, 0);
+    rv0 = __builtin_amdgcn_raw_buffer_load_b128(vrs, voff, vo, 0);
+    if (VG > 1) rv1 = __builtin_amdgcn_raw_buffer_load_b128(vrs, voff, vo + 4096, 0);
+    if (VG > 2) rv2 = __builtin_amdgcn_raw_buffer_load_b128(vrs, voff, vo + 8192, 0);
+    if (VG > 3) rv3 = __builtin_amdgcn_raw_buffer_load_b128(vrs, voff, vo + 12288, 0);
+    if (PV == PVFP8 && tid < 2 * D / 16) re8 = __builtin_amdgcn_raw_buffer_load_b128(ers, voff, 2 * ch * D, 0);
+    if (tid == 0) rks = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, 0, ch * 4, 0));
+  };
+  auto put_k = [&](int8_t* kl, int gi, v4i v) {
+    constexpr int G = D / 16;
+    const int key = gi / G, g = gi % G;
+    *reinterpret_cast<v4i*>(kl + key * D + ((g ^ k_swz<D>(key)) << 4)) = v;
+  };
+  auto put_v = [&](uint8_t* vl, int gi, v4i v) {
+    *reinterpret_cast<v4i*>(vl + (gi / VGR) * VS + (gi % VGR) * 16) = v;
+  };
+  auto store = [&](int buf) {
+    put_k(klds[buf], tid, rk0);
+    if (KG > 1) put_k(klds[buf], tid + 256, rk1);
+    put_v(vlds[buf], tid, rv0);
+    if (VG > 1) put_v(vlds[buf], tid + 256, rv1);
+    if (VG > 2) put_v(vlds[buf], tid + 512, rv2);
+    if (VG > 3) put_v(vlds[buf], tid + 768, rv3);
+    if (PV == PVFP8 && tid < 2 * D / 16) reinterpret_cast<v4i*>(elds[buf])[tid] = re8;
+    if (tid == 0) kslds[buf] = rks;
+  };
+
+  if (c_lo < wg_hi) {
+    fetch(c_lo);
+    store(0);
+  }
+  __syncthreads();
+  // Every load issued so far (the Q operands, the first stage) has completed;
+  // saying so keeps the loop's own prefetch loads from being waited on early.
+  __builtin_amdgcn_s_waitcnt(0);
   for (int ch = c_lo; ch < wg_hi; ++ch) {
-    // ---- stage the chunk: K codes (swizzled), V^T, E8M0 scales
-    load_k_chunk<D, 256>(klds, kbase + static_cast<int64_t>(ch) * 64 * D, tid);
-    {
-      const uint8_t* src = vbase + static_cast<int64_t>(ch) * 64 * D * VBYTES;
-      constexpr int NG = 64 * D * VBYTES / 16;
-#pragma unroll
-      for (int gi = tid; gi < NG; gi += 256)
-        *reinterpret_cast<uint4*>(vlds + gi * 16) = *reinterpret_cast<const uint4*>(src + gi * 16);
-      if (PV == PVFP8 && tid < 2 * D / 16)
-        *reinterpret_cast<uint4*>(elds + tid * 16) = *reinterpret_cast<const uint4*>(
-            A.ve + (static_cast<int64_t>(bh) * (A.Nkv_pad / 32) + 2 * ch) * D + tid * 16);
-    }
-    __syncthreads();
-
-    if (ch < wave_hi) {
-      v16i s0, s1;
-      qk_chunk<D>(klds, qv, lane, s0, s1);
-      const bool masked = ch >= wave_full;
-      const int kb = ch * 64 + 16 * h2;  // key of s0[0] in this lane; s1[0] is kb + 32
-      if (masked) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          if (kb + i >= re) s0[i] = SENTINEL;
-          if (kb + 32 + i >= re) s1[i] = SENTINEL;
-        }
-      }
-      int mx = max(s0[0], s1[0]);
-#pragma unroll
-      for (int i = 1; i < 16; ++i) mx = max(mx, max(s0[i], s1[i]));
-      mx = max(mx, __shfl_xor(mx, 32, 64));
-      const float c = qsc * ksc[ch];
-      const float tm = static_cast<float>(mx) * c;
-      const bool has = ch * 64 < re;
-      const bool upd = has && (tm > m + TAU);
-      if (__any(upd)) {
-        const float alpha = upd ? __builtin_amdgcn_exp2f(m - tm) : 1.0f;
-        m = upd ? tm : m;
-        l *= alpha;
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) o[cb][i] *= alpha;
-      }
-      const float nmref = -(m - static_cast<float>(SHIFT));
-      float p0[16], p1[16];
-      float lsum = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        p0[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(static_cast<float>(s0[i]), c, nmref));
-        p1[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(static_cast<float>(s1[i]), c, nmref));
-        if (masked) {
-          if (kb + i >= re) p0[i] = 0.f;
-          if (kb + 32 + i >= re) p1[i] = 0.f;
-        }
-        lsum += p0[i] + p1[i];
-      }
-      l += lsum;
-
-      if (PV == PVFP8) {
-        v8i pb;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          pb[k] = static_cast<int>(pack_e4m3x4(p0[4 * k], p0[4 * k + 1], p0[4 * k + 2], p0[4 * k + 3]));
-          pb[4 + k] = static_cast<int>(pack_e4m3x4(p1[4 * k], p1[4 * k + 1], p1[4 * k + 2], p1[4 * k + 3]));
-        }
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-          const int chn = 32 * cb + r32;
-          const uint8_t* vrow = vlds + chn * 64 + 16 * h2;
-          const v4i lo = *reinterpret_cast<const v4i*>(vrow);
-          const v4i hi = *reinterpret_cast<const v4i*>(vrow + 32);
-          const v8i va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          const int sc = static_cast<int>(elds[h2 * D + chn]);
-          o[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, o[cb], 0, 0, 0, sc, 0, 127);
-        }
-      } else {
-        uint32_t pw[16];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          pw[k] = Pack16<DT>::pack(p0[2 * k], p0[2 * k + 1]);
-          pw[8 + k] = Pack16<DT>::pack(p1[2 * k], p1[2 * k + 1]);
-        }
-#pragma unroll
-        for (int mu = 0; mu < 4; ++mu) {
-          const v4i pbv = {static_cast<int>(pw[4 * mu]), static_cast<int>(pw[4 * mu + 1]),
-                           static_cast<int>(pw[4 * mu + 2]), static_cast<int>(pw[4 * mu + 3])};
-#pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) {
-            const int chn = 32 * cb + r32;
-            const v4i va = *reinterpret_cast<const v4i*>(
-                vlds + (chn * 64 + 32 * (mu >> 1) + 16 * h2 + 8 * (mu & 1)) * 2);
-            if (DT == DT_BF16)
-              o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, va),
-                                                              __builtin_bit_cast(v8bf, pbv), o[cb], 0, 0, 0);
-            else
-              o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, va),
-                                                             __builtin_bit_cast(v8h, pbv), o[cb], 0, 0, 0);
-          }
-        }
-      }
-    }
+    const int buf = (ch - c_lo) & 1;
+    const bool more = ch + 1 < wg_hi;
+    const float kscale = kslds[buf];
+    if (more) fetch(ch + 1);
+    if (ch < wave_hi)
+      st.chunk(klds[buf], vlds[buf], elds[buf], qv, qsc * kscale, ch >= wave_full, ch * 64 + 16 * h2, re, lane);
+    if (more) store(buf ^ 1);
     __syncthreads();
   }
+  v16f* o = st.o;
+  const float m = st.m, l = st.l;
 
   // ---- epilogue: combine the two lane halves' row sums, normalise, store
   const float ltot = l + __shfl_xor(l, 32, 64);
