@@ -33,10 +33,12 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="large")
     p.add_argument("--pv", default=None, choices=["16", "fp8"])
-    p.add_argument("--cpu-heads", type=int, default=2, help="heads in the CPU oracle sample")
-    p.add_argument("--cpu-rows", type=int, default=256, help="query rows per head in the CPU sample")
+    p.add_argument("--cpu-heads", type=int, default=8, help="heads in the CPU oracle sample")
+    p.add_argument("--cpu-rows", type=int, default=512, help="query rows per head in the CPU sample")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--profile", action="store_true", help="few steps, no CPU leg (for rocprofv3)")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="also run one plain 256 MiB device copy (reference for HBM byte counters)")
     return p.parse_args()
 
 
@@ -81,6 +83,12 @@ def main():
         if i is not None:
             ev[i][2].record(stream)
 
+    if args.calibrate_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(warm):
         step()
     torch.cuda.synchronize()

@@ -246,8 +246,8 @@ def quant_views(desc, ws, bufs):
                     (B, H, desc.Nkv_pad // 64, d, 64)),
     }
     if fp8:
-        out["v_e8m0"] = view(bufs.v_e8m0, B * H * desc.Nkv_pad // 32 * d, torch.uint8,
-                             (B, H, desc.Nkv_pad // 32, d))
+        out["v_e8m0"] = view(bufs.v_e8m0, B * H * desc.Nkv_pad // 64 * 256, torch.uint8,
+                             (B, H, desc.Nkv_pad // 64, 64, 4))
     return out
 
 

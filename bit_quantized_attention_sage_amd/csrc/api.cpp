@@ -125,7 +125,7 @@ Layout layout_of(const Plan& p) {
   L.k_mean = take(bh * p.d * 4);
   L.chan_shift = take(bh * p.d);
   L.v_t = take(bh * p.Nkv_pad * p.d * (p.pv_mode == SAGE_PV_FP8 ? 1 : 2));
-  L.v_e8m0 = take(p.pv_mode == SAGE_PV_FP8 ? bh * (p.Nkv_pad / 32) * p.d : 0);
+  L.v_e8m0 = take(p.pv_mode == SAGE_PV_FP8 ? bh * (p.Nkv_pad / 64) * 256 : 0);
   L.ksum = 0;
   L.kmax = align_up(bh * nck * p.d * 8);
   L.kmin = L.kmax + align_up(bh * nck * p.d * 4);

@@ -124,6 +124,24 @@ struct VRow {
   static constexpr int STRIDE = BYTES + 16;
 };
 
+// P operand of the P.V MFMAs for one chunk: 32 e4m3 bytes (FP8 mode) or 16
+// packed 16-bit pairs, in the key order described at the top of the file.
+template <int PV>
+struct PTile;
+template <>
+struct PTile<PVFP8> {
+  v8i b;
+  __device__ __forceinline__ void pin() { asm volatile("" : "+v"(b)); }
+};
+template <>
+struct PTile<PV16> {
+  uint32_t w[16];
+  __device__ __forceinline__ void pin() {
+#pragma unroll
+    for (int i = 0; i < 16; i += 4) asm volatile("" : "+v"(w[i]), "+v"(w[i + 1]), "+v"(w[i + 2]), "+v"(w[i + 3]));
+  }
+};
+
 // Per-wave online-softmax state and the math of one chunk.
 template <int D, int PV, int DT>
 struct WaveState {
@@ -133,41 +151,39 @@ struct WaveState {
   v16f o[NCB];
   float m, l;
 
-  // One 64-key chunk: S^T on i8 MFMAs, dequantize, lazy running max, p = 2^x,
-  // P.V on 16-bit or scaled FP8 MFMAs.  masked (wave-uniform): keys at or
-  // beyond this row's visible end `re` get p = 0 and do not enter the maximum.
-  __device__ __forceinline__ void chunk(const int8_t* klds, const uint8_t* vlds, const uint8_t* elds,
-                                        const v4i* qv, float c, bool masked, int kb, int re, int lane) {
-    const int h2 = lane >> 5, r32 = lane & 31;
-    v16i s0, s1;
-    qk_chunk<D>(klds, qv, lane, s0, s1);
-    if (masked) {  // boundary chunk only: invisible keys get the sentinel score
-      asm volatile("");  // keep this a real branch: no if-conversion into every chunk
-      const int lim = re - kb;
+  // Masking of a boundary chunk: keys at or beyond this row's visible end
+  // `re` get the sentinel score (they then take no part in the maximum, and
+  // softmax() gives them p = 0).
+  __device__ __forceinline__ void mask(v16i& s0, v16i& s1, int kb, int re) {
+    asm volatile("");  // keep this a real branch: no if-conversion into every chunk
+    const int lim = re - kb;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        s0[i] = (i < lim) ? s0[i] : SENTINEL;
-        s1[i] = (32 + i < lim) ? s1[i] : SENTINEL;
-      }
+    for (int i = 0; i < 16; ++i) {
+      s0[i] = (i < lim) ? s0[i] : SENTINEL;
+      s1[i] = (32 + i < lim) ? s1[i] : SENTINEL;
     }
+  }
+
+  // Softmax step of one chunk on its integer scores: the row maximum (the
+  // two lane halves hold the same query), the lazy running-max update (the
+  // row adopts the chunk maximum only when it exceeds m by more than TAU),
+  // p = 2^(S c - (m - s)), l = alpha l + sum p, and P rounded to the P.V
+  // operand type.  Returns alpha (1 for rows that kept m); the caller
+  // rescales O by it when any row of the wave moved.
+  __device__ __forceinline__ float softmax(const v16i& s0, const v16i& s1, float c, bool has, bool masked,
+                                           PTile<PV>& P) {
     int mx = max(s0[0], s1[0]);
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mx = max(mx, max(s0[i], s1[i]));
-    {  // combine the two lane halves, which hold the same query
+    for (int i = 1; i < 15; i += 2) mx = max(mx, max(max(s0[i], s1[i]), max(s0[i + 1], s1[i + 1])));
+    mx = max(mx, max(s0[15], s1[15]));
+    {
       const auto sw = __builtin_amdgcn_permlane32_swap(mx, mx, false, false);
       mx = max(static_cast<int>(sw[0]), static_cast<int>(sw[1]));
     }
     const float tm = static_cast<float>(mx) * c;
-    const bool upd = (!masked || kb - 16 * h2 < re) && (tm > m + TAU);
-    if (__any(upd)) {
-      const float alpha = upd ? __builtin_amdgcn_exp2f(m - tm) : 1.0f;
-      m = upd ? tm : m;
-      l *= alpha;
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[cb][i] *= alpha;
-    }
+    const bool upd = has && (tm > m + TAU);
+    const float alpha = upd ? __builtin_amdgcn_exp2f(m - tm) : 1.0f;
+    m = upd ? tm : m;
     const float nmref = -(m - static_cast<float>(SHIFT));
     float p0[16], p1[16];
 #pragma unroll
@@ -189,41 +205,57 @@ struct WaveState {
       ls0 += p0[i];
       ls1 += p1[i];
     }
-    l += ls0 + ls1;
-
-    if (PV == PVFP8) {
-      v8i pb;
+    l = alpha * l + (ls0 + ls1);
+    if constexpr (PV == PVFP8) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        pb[k] = static_cast<int>(pack_e4m3x4(p0[4 * k], p0[4 * k + 1], p0[4 * k + 2], p0[4 * k + 3]));
-        pb[4 + k] = static_cast<int>(pack_e4m3x4(p1[4 * k], p1[4 * k + 1], p1[4 * k + 2], p1[4 * k + 3]));
+        P.b[k] = static_cast<int>(pack_e4m3x4(p0[4 * k], p0[4 * k + 1], p0[4 * k + 2], p0[4 * k + 3]));
+        P.b[4 + k] = static_cast<int>(pack_e4m3x4(p1[4 * k], p1[4 * k + 1], p1[4 * k + 2], p1[4 * k + 3]));
       }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        P.w[k] = Pack16<DT>::pack(p0[2 * k], p0[2 * k + 1]);
+        P.w[8 + k] = Pack16<DT>::pack(p1[2 * k], p1[2 * k + 1]);
+      }
+    }
+    return alpha;
+  }
+
+  __device__ __forceinline__ void rescale(float alpha) {
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[cb][i] *= alpha;
+    }
+  }
+
+  // O += P V over the chunk; e8: this lane's four E8M0 bytes (FP8 mode; byte
+  // cb scales channel block cb of the lane's 32-key block).
+  __device__ __forceinline__ void pv(const PTile<PV>& P, const uint8_t* vlds, int e8, int lane) {
+    const int h2 = lane >> 5, r32 = lane & 31;
+    if constexpr (PV == PVFP8) {
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
-        const int chn = 32 * cb + r32;
-        const uint8_t* vrow = vlds + chn * VS + 16 * h2;
+        const uint8_t* vrow = vlds + (32 * cb + r32) * VS + 16 * h2;
         const v4i lo = *reinterpret_cast<const v4i*>(vrow);
         const v4i hi = *reinterpret_cast<const v4i*>(vrow + 32);
         const v8i va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        const int sc = static_cast<int>(elds[h2 * D + chn]);
-        o[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, o[cb], 0, 0, 0, sc, 0, 127);
+        if (cb == 0) o[0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, P.b, o[0], 0, 0, 0, e8, 0, 127);
+        if (cb == 1) o[1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, P.b, o[1], 0, 0, 1, e8, 0, 127);
+        if (cb == 2) o[2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, P.b, o[2], 0, 0, 2, e8, 0, 127);
+        if (cb == 3) o[3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, P.b, o[3], 0, 0, 3, e8, 0, 127);
       }
     } else {
-      uint32_t pw[16];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        pw[k] = Pack16<DT>::pack(p0[2 * k], p0[2 * k + 1]);
-        pw[8 + k] = Pack16<DT>::pack(p1[2 * k], p1[2 * k + 1]);
-      }
 #pragma unroll
       for (int mu = 0; mu < 4; ++mu) {
-        const v4i pbv = {static_cast<int>(pw[4 * mu]), static_cast<int>(pw[4 * mu + 1]),
-                         static_cast<int>(pw[4 * mu + 2]), static_cast<int>(pw[4 * mu + 3])};
+        const v4i pbv = {static_cast<int>(P.w[4 * mu]), static_cast<int>(P.w[4 * mu + 1]),
+                         static_cast<int>(P.w[4 * mu + 2]), static_cast<int>(P.w[4 * mu + 3])};
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
-          const int chn = 32 * cb + r32;
           const v4i va = *reinterpret_cast<const v4i*>(
-              vlds + chn * VS + (32 * (mu >> 1) + 16 * h2 + 8 * (mu & 1)) * 2);
+              vlds + (32 * cb + r32) * VS + (32 * (mu >> 1) + 16 * h2 + 8 * (mu & 1)) * 2);
           if (DT == DT_BF16)
             o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, va),
                                                             __builtin_bit_cast(v8bf, pbv), o[cb], 0, 0, 0);
@@ -234,7 +266,27 @@ struct WaveState {
       }
     }
   }
+
+  // A whole chunk in one go (boundary chunks and the tail of the key range).
+  __device__ __forceinline__ void chunk(const int8_t* klds, const uint8_t* vlds, int e8, const v4i* qv, float c,
+                                        bool masked, int kb, int re, int lane) {
+    v16i s0, s1;
+    qk_chunk<D>(klds, qv, lane, s0, s1);
+    if (masked) mask(s0, s1, kb, re);
+    PTile<PV> P;
+    const float alpha = softmax(s0, s1, c, !masked || kb - 16 * (lane >> 5) < re, masked, P);
+    rescale(alpha);
+    pv(P, vlds, e8, lane);
+  }
 };
+
+// Number of leading 64-key chunks that every query row of tile qt sees in
+// full: the smallest visible end over the tile's rows, in whole chunks.
+__device__ __forceinline__ int wg_full_of(const AttnArgs& A, int kv_len, int q_pos0, int qt) {
+  int end = kv_len;
+  if (A.frame_len > 0) end = min(kv_len, ((q_pos0 + qt * BQ) / A.frame_len + 1) * A.frame_len);
+  return end / 64;
+}
 
 template <int D, int PV, int DT>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
@@ -247,7 +299,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
   static_assert(KG >= 1 && KG <= 2 && VG >= 1 && VG <= 4, "staging shape");
   __shared__ __attribute__((aligned(16))) int8_t klds[2][64 * D];
   __shared__ __attribute__((aligned(16))) uint8_t vlds[2][D * VS];
-  __shared__ __attribute__((aligned(16))) uint8_t elds[2][2 * D];
   __shared__ float kslds[2];  // the staged chunk's K scale
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -297,33 +348,41 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
   const int nkc = A.Nkv_pad / 64;
   const int8_t* kbase = A.kc + static_cast<int64_t>(bh) * A.Nkv_pad * D;
   const uint8_t* vbase = static_cast<const uint8_t*>(A.vt) + static_cast<int64_t>(bh) * nkc * 64 * D * VBYTES;
-  const uint8_t* ebase = A.ve + static_cast<int64_t>(bh) * (A.Nkv_pad / 32) * D;
+  const uint8_t* ebase = A.ve + static_cast<int64_t>(bh) * nkc * 256;
   const float* ksc = A.kscale + static_cast<int64_t>(bh) * nkc;
 
-  // Staging of chunk `ch` through registers: buffer loads (per-thread offsets
-  // fixed in VGPRs, the chunk offset in an SGPR) are issued one chunk ahead
-  // and written to the other LDS buffer after the current chunk's math.
+  // Staging through registers with raw buffer loads (per-thread offsets fixed
+  // in VGPRs, the chunk offset in an SGPR; reads past the end return 0): the
+  // loads are issued one step ahead and written to LDS after the step's math.
+  // K (with its scale) and V are staged separately because the main loop runs
+  // the K side one chunk ahead of the V side.  Each lane loads its own four
+  // E8M0 bytes of a chunk straight into a register.
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<int8_t*>(kbase), 0, nkc * 64 * D, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(vbase), 0, nkc * 64 * D * VBYTES, 0x00020000);
   const __amdgpu_buffer_rsrc_t ers = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(ebase), 0, PV == PVFP8 ? (A.Nkv_pad / 32) * D : 0, 0x00020000);
+      const_cast<uint8_t*>(ebase), 0, PV == PVFP8 ? nkc * 256 : 0, 0x00020000);
   const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float*>(ksc), 0, nkc * 4, 0x00020000);
   const int voff = tid * 16;
-  v4i rk0, rk1, rv0, rv1, rv2, rv3, re8;
+  v4i rk0, rk1, rv0, rv1, rv2, rv3;
   float rks;
-  auto fetch = [&](int ch) {
-    const int ko = ch * 64 * D, vo = ch * 64 * D * VBYTES;
+  auto fetch_k = [&](int ch) {
+    const int ko = ch * 64 * D;
     rk0 = __builtin_amdgcn_raw_buffer_load_b128(krs, voff, ko, 0);
     if (KG > 1) rk1 = __builtin_amdgcn_raw_buffer_load_b128(krs, voff, ko + 4096, 0);
+    rks = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, 0, ch * 4, 0));
+  };
+  auto fetch_v = [&](int ch) {
+    const int vo = ch * 64 * D * VBYTES;
     rv0 = __builtin_amdgcn_raw_buffer_load_b128(vrs, voff, vo, 0);
     if (VG > 1) rv1 = __builtin_amdgcn_raw_buffer_load_b128(vrs, voff, vo + 4096, 0);
     if (VG > 2) rv2 = __builtin_amdgcn_raw_buffer_load_b128(vrs, voff, vo + 8192, 0);
     if (VG > 3) rv3 = __builtin_amdgcn_raw_buffer_load_b128(vrs, voff, vo + 12288, 0);
-    if (PV == PVFP8 && tid < 2 * D / 16) re8 = __builtin_amdgcn_raw_buffer_load_b128(ers, voff, 2 * ch * D, 0);
-    if (tid == 0) rks = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, 0, ch * 4, 0));
+  };
+  auto fetch_e = [&](int ch) -> int {
+    return PV == PVFP8 ? __builtin_amdgcn_raw_buffer_load_b32(ers, lane * 4, ch * 256, 0) : 0;
   };
   auto put_k = [&](int8_t* kl, int gi, v4i v) {
     constexpr int G = D / 16;
@@ -333,34 +392,110 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
   auto put_v = [&](uint8_t* vl, int gi, v4i v) {
     *reinterpret_cast<v4i*>(vl + (gi / VGR) * VS + (gi % VGR) * 16) = v;
   };
-  auto store = [&](int buf) {
+  auto store_k = [&](int buf) {
     put_k(klds[buf], tid, rk0);
     if (KG > 1) put_k(klds[buf], tid + 256, rk1);
+    kslds[buf] = rks;  // every thread writes the same value
+  };
+  auto store_v = [&](int buf) {
     put_v(vlds[buf], tid, rv0);
     if (VG > 1) put_v(vlds[buf], tid + 256, rv1);
     if (VG > 2) put_v(vlds[buf], tid + 512, rv2);
     if (VG > 3) put_v(vlds[buf], tid + 768, rv3);
-    if (PV == PVFP8 && tid < 2 * D / 16) reinterpret_cast<v4i*>(elds[buf])[tid] = re8;
-    if (tid == 0) kslds[buf] = rks;
   };
 
+  // Chunks every row of the workgroup sees in full run through the main loop;
+  // the rest (the partial last chunk, frame boundaries) through the tail loop.
+  const int main_hi = max(c_lo, min(wg_hi, wg_full_of(A, kv_len, q_pos0, qt)));
+
+  // Prologue: K and V of chunk c_lo in buffers 0, K of chunk c_lo + 1 in buffer 1.
+  int e_cur = 0;
   if (c_lo < wg_hi) {
-    fetch(c_lo);
-    store(0);
+    fetch_k(c_lo);
+    fetch_v(c_lo);
+    e_cur = fetch_e(c_lo);
+    store_k(0);
+    store_v(0);
+    fetch_k(c_lo + 1);
+    store_k(1);
   }
   __syncthreads();
-  // Every load issued so far (the Q operands, the first stage) has completed;
-  // saying so keeps the loop's own prefetch loads from being waited on early.
+  // Every load issued so far has completed; saying so keeps the loops' own
+  // prefetch loads from being waited on before the first MFMA.
   __builtin_amdgcn_s_waitcnt(0);
-  for (int ch = c_lo; ch < wg_hi; ++ch) {
-    const int buf = (ch - c_lo) & 1;
-    const bool more = ch + 1 < wg_hi;
-    const float kscale = kslds[buf];
-    if (more) fetch(ch + 1);
-    if (ch < wave_hi)
-      st.chunk(klds[buf], vlds[buf], elds[buf], qv, qsc * kscale, ch >= wave_full, ch * 64 + 16 * h2, re, lane);
-    if (more) store(buf ^ 1);
+
+  // Main loop, software-pipelined within each wave: at step j (chunk
+  // n = c_lo + j) K(n+1) sits in K buffer (j+1)&1 and V(n) in V buffer j&1,
+  // and S(n) is already in registers.  One straight-line block issues the
+  // loads of K(n+2) and V(n+1), the S MFMAs of chunk n+1 and the softmax of
+  // chunk n, so the matrix cores and the vector ALUs overlap; P(n) V(n) and
+  // the LDS stores follow.  Loads past the key range read zeros and their
+  // stores land in buffers nothing reads again.
+  v16i sa0{}, sa1{}, sb0{}, sb1{};
+  float ca = 0.f, cb_ = 0.f;
+  if (c_lo < main_hi) {
+    qk_chunk<D>(klds[0], qv, lane, sa0, sa1);
+    ca = qsc * kslds[0];
+  }
+  int j = 0;
+  auto step = [&](int n, v16i& cs0, v16i& cs1, float& c_cur, v16i& ns0, v16i& ns1, float& c_nxt) {
+    const int kb_nxt = (j + 1) & 1, vb_cur = j & 1;
+    // Region 1: the loads one chunk ahead, the S MFMAs of chunk n+1 and the
+    // softmax of chunk n, interleaved so the matrix cores and the vector
+    // ALUs work at the same time.
+    __builtin_amdgcn_sched_barrier(0);
+    fetch_k(n + 2);
+    fetch_v(n + 1);
+    const int e_nxt = fetch_e(n + 1);
+    qk_chunk<D>(klds[kb_nxt], qv, lane, ns0, ns1);
+    PTile<PV> P;
+    const float alpha = st.softmax(cs0, cs1, c_cur, true, false, P);
+    __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);  // the buffer loads
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // the first K reads
+#pragma unroll
+    for (int g = 0; g < 2 * D / 32; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one S MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);  // a slice of the softmax
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // the next K read
+    }
+    // Pin the region's results here so that no earlier pass moves the MFMAs
+    // or the softmax out of it.
+    asm volatile("" : "+v"(ns0), "+v"(ns1));
+    P.pin();
+    __builtin_amdgcn_sched_barrier(0);
+    // Region 2 (rare): rescale O when some row's running max moved.
+    st.rescale(alpha);
+    // Region 3: P(n) V(n), the LDS stores of the prefetched chunks, barrier.
+    c_nxt = qsc * kslds[kb_nxt];
+    st.pv(P, vlds[vb_cur], e_cur, lane);
+    store_k(vb_cur);
+    store_v(kb_nxt);
     __syncthreads();
+    e_cur = e_nxt;
+    ++j;
+  };
+  int n = c_lo;
+  for (; n + 1 < main_hi; n += 2) {
+    step(n, sa0, sa1, ca, sb0, sb1, cb_);
+    step(n + 1, sb0, sb1, cb_, sa0, sa1, ca);
+  }
+  if (n < main_hi) {
+    step(n, sa0, sa1, ca, sb0, sb1, cb_);
+    ++n;
+  }
+  // Tail loop: chunk n with K and V both in buffers j&1 (and its E8M0 bytes
+  // in e_cur); the next chunk's K and V are (re)staged into the other buffers.
+  for (; n < wg_hi; ++n, ++j) {
+    const int buf = j & 1;
+    fetch_k(n + 1);
+    fetch_v(n + 1);
+    const int e_nxt = fetch_e(n + 1);
+    if (n < wave_hi)
+      st.chunk(klds[buf], vlds[buf], e_cur, qv, qsc * kslds[buf], n >= wave_full, n * 64 + 16 * h2, re, lane);
+    store_k(buf ^ 1);
+    store_v(buf ^ 1);
+    __syncthreads();
+    e_cur = e_nxt;
   }
   v16f* o = st.o;
   const float m = st.m, l = st.l;

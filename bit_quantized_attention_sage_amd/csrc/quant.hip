@@ -182,7 +182,8 @@ __global__ __launch_bounds__(256) void quant_i8_kernel(
 // channel-major ([D][64]) so that each lane of the P.V matrix-core operand
 // reads its keys contiguously.  FP8 mode: one E8M0 scale per (32-key block,
 // channel) -- the smallest power of two 2^e with amax * 2^-e <= 448 -- and
-// e4m3fn codes of v * 2^-e.
+// e4m3fn codes of v * 2^-e; the scales of a chunk are stored as 64 lanes x 4
+// bytes (lane 32*k + r holds channels r, r+32, r+64, r+96 of key block k).
 template <typename T, int D, bool FP8>
 __global__ __launch_bounds__(2 * D) void prep_v_kernel(
     const T* __restrict__ x, int64_t sb, int64_t sh, int64_t sn, int H, int n_pad,
@@ -235,7 +236,11 @@ __global__ __launch_bounds__(2 * D) void prep_v_kernel(
     uint4* dst = reinterpret_cast<uint4*>(static_cast<uint8_t*>(vt) + chunk_base + c * 64 + 32 * kh);
     dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
     dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
-    e8m0[(static_cast<int64_t>(bh) * (n_pad / 32) + 2 * ch + kh) * D + c] = static_cast<uint8_t>(e + 127);
+    // E8M0 layout per chunk: [lane = 32*kh + c%32][byte = c/32], four bytes per
+    // lane, so each lane of the P.V MFMA loads its scales as one dword.
+    uint8_t* eb = e8m0 + (static_cast<int64_t>(bh) * (n_pad / 64) + ch) * 256 + (32 * kh + c % 32) * 4;
+    eb[c / 32] = static_cast<uint8_t>(e + 127);
+    if (D == 64) eb[c / 32 + 2] = 127;  // unused byte positions hold the scale 1
   }
 }
 

@@ -108,7 +108,9 @@ typedef struct sage_quant_bufs {
   void *v_t;           /* [B,H,Nkv_pad/64,d,64]: per 64-key chunk, V transposed
                           (channel-major); 16-bit values in SAGE_PV_16 mode,
                           e4m3fn codes in SAGE_PV_FP8 mode                    */
-  uint8_t *v_e8m0;     /* [B,H,Nkv_pad/32,d] E8M0 bytes (FP8 mode), else NULL */
+  uint8_t *v_e8m0;     /* FP8 mode: E8M0 scale bytes, [B,H,Nkv_pad/64,64,4]:
+                          per 64-key chunk, byte [32k + r][cb] scales channel
+                          32cb + r of keys [32k, 32k+32); else NULL           */
   void *stats;         /* internal: partial statistics of the quantize pass   */
   void *partial;       /* internal: split-KV partial results                  */
 } sage_quant_bufs;

@@ -64,8 +64,12 @@ def check_quantized(views, Q, K, V, pv_mode, dtype, kv_len=None, mu_in=None):
         g = untiled.numpy().astype(np.uint8)
         np.testing.assert_array_equal(g[:, :, :Nkv], vc)
         assert not g[:, :, Nkv:].any()
-        ge = views["v_e8m0"].cpu().numpy()
-        np.testing.assert_array_equal(ge[:, :, :e8.shape[2]], e8)
+        # per chunk: byte [32k + r][cb] is block 2*chunk + k, channel 32*cb + r
+        ge = views["v_e8m0"].cpu().numpy()                      # [B,H,nch,64,4]
+        nch = ge.shape[2]
+        g5 = ge.reshape(B, H, nch, 2, 32, 4)[..., : d // 32]     # [B,H,nch,k,r,cb]
+        ge_std = g5.transpose(0, 1, 2, 3, 5, 4).reshape(B, H, 2 * nch, d)
+        np.testing.assert_array_equal(ge_std[:, :, :e8.shape[2]], e8)
     else:
         g = untiled.numpy().view(np.uint16)
         vv = V.copy()
