@@ -33,6 +33,8 @@
 //    32*(mu/2) + 16*h2 + 8*(mu%2) + [0, 8) in lane half h2 for step mu.
 //  * O^T accumulator: lane l holds query r32 and channels
 //    32*cb + 8*(i/4) + 4*h2 + i%4, so per-row factors (alpha, 1/l) are per lane.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -115,13 +117,16 @@ struct AttnArgs {
 };
 
 // LDS layout of a staged chunk.  K: [64 keys][D] bytes with the granule
-// swizzle above.  V^T: [D channels][64 keys] with each channel row padded by
-// 16 bytes (80 B in FP8, 144 B in 16-bit mode) so that the 8 lanes of one
-// ds_read_b128 phase, which read consecutive channels, hit distinct banks.
+// swizzle above.  V^T: [D channels][64 keys], 64 B (FP8) or 128 B (16-bit)
+// per channel row, granule g of row c stored at slot g ^ v_swz(c), so that the
+// 8 lanes of one ds_read_b128 phase, which read the same granule of 8
+// consecutive channels, hit distinct banks.
 template <int PV>
 struct VRow {
-  static constexpr int BYTES = (PV == PVFP8) ? 64 : 128;  // payload per channel row
-  static constexpr int STRIDE = BYTES + 16;
+  static constexpr int BYTES = (PV == PVFP8) ? 64 : 128;  // bytes per channel row
+  static constexpr int GR = BYTES / 16;                    // granules per row
+  static __device__ __forceinline__ int swz(int c) { return (PV == PVFP8) ? ((c >> 1) & 3) : (c & 7); }
+  static __device__ __forceinline__ int addr(int c, int g) { return c * BYTES + ((g ^ swz(c)) << 4); }
 };
 
 // P operand of the P.V MFMAs for one chunk: 32 e4m3 bytes (FP8 mode) or 16
@@ -147,7 +152,6 @@ template <int D, int PV, int DT>
 struct WaveState {
   static constexpr int NCB = D / 32;
   static constexpr int SHIFT = (PV == PVFP8) ? PSHIFT_FP8 : PSHIFT_16;
-  static constexpr int VS = VRow<PV>::STRIDE;
   v16f o[NCB];
   float m, l;
 
@@ -172,10 +176,13 @@ struct WaveState {
   // rescales O by it when any row of the wave moved.
   __device__ __forceinline__ float softmax(const v16i& s0, const v16i& s1, float c, bool has, bool masked,
                                            PTile<PV>& P) {
-    int mx = max(s0[0], s1[0]);
+    int ma = max(s0[0], s0[1]), mb = max(s1[0], s1[1]);  // two v_max3 chains
 #pragma unroll
-    for (int i = 1; i < 15; i += 2) mx = max(mx, max(max(s0[i], s1[i]), max(s0[i + 1], s1[i + 1])));
-    mx = max(mx, max(s0[15], s1[15]));
+    for (int i = 2; i < 16; i += 2) {
+      ma = max(ma, max(s0[i], s0[i + 1]));
+      mb = max(mb, max(s1[i], s1[i + 1]));
+    }
+    int mx = max(ma, mb);
     {
       const auto sw = __builtin_amdgcn_permlane32_swap(mx, mx, false, false);
       mx = max(static_cast<int>(sw[0]), static_cast<int>(sw[1]));
@@ -209,8 +216,8 @@ struct WaveState {
     if constexpr (PV == PVFP8) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        P.b[k] = static_cast<int>(pack_e4m3x4(p0[4 * k], p0[4 * k + 1], p0[4 * k + 2], p0[4 * k + 3]));
-        P.b[4 + k] = static_cast<int>(pack_e4m3x4(p1[4 * k], p1[4 * k + 1], p1[4 * k + 2], p1[4 * k + 3]));
+        P.b[k] = static_cast<int>(pack_e4m3x4_into(p0[4 * k], p0[4 * k + 1], p0[4 * k + 2], p0[4 * k + 3]));
+        P.b[4 + k] = static_cast<int>(pack_e4m3x4_into(p1[4 * k], p1[4 * k + 1], p1[4 * k + 2], p1[4 * k + 3]));
       }
     } else {
 #pragma unroll
@@ -236,16 +243,20 @@ struct WaveState {
   __device__ __forceinline__ void pv(const PTile<PV>& P, const uint8_t* vlds, int e8, int lane) {
     const int h2 = lane >> 5, r32 = lane & 31;
     if constexpr (PV == PVFP8) {
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-        const uint8_t* vrow = vlds + (32 * cb + r32) * VS + 16 * h2;
-        const v4i lo = *reinterpret_cast<const v4i*>(vrow);
-        const v4i hi = *reinterpret_cast<const v4i*>(vrow + 32);
+      // channel block cb takes byte cb of the lane's scale register (op_sel)
+      auto one = [&](auto cbc) {
+        constexpr int cb = decltype(cbc)::value;
+        const int c = 32 * cb + r32;
+        const v4i lo = *reinterpret_cast<const v4i*>(vlds + VRow<PV>::addr(c, h2));
+        const v4i hi = *reinterpret_cast<const v4i*>(vlds + VRow<PV>::addr(c, 2 + h2));
         const v8i va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        if (cb == 0) o[0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, P.b, o[0], 0, 0, 0, e8, 0, 127);
-        if (cb == 1) o[1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, P.b, o[1], 0, 0, 1, e8, 0, 127);
-        if (cb == 2) o[2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, P.b, o[2], 0, 0, 2, e8, 0, 127);
-        if (cb == 3) o[3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, P.b, o[3], 0, 0, 3, e8, 0, 127);
+        o[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, P.b, o[cb], 0, 0, cb, e8, 0, 127);
+      };
+      one(std::integral_constant<int, 0>{});
+      one(std::integral_constant<int, 1>{});
+      if constexpr (NCB > 2) {
+        one(std::integral_constant<int, 2>{});
+        one(std::integral_constant<int, 3>{});
       }
     } else {
 #pragma unroll
@@ -255,7 +266,7 @@ struct WaveState {
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
           const v4i va = *reinterpret_cast<const v4i*>(
-              vlds + (32 * cb + r32) * VS + (32 * (mu >> 1) + 16 * h2 + 8 * (mu & 1)) * 2);
+              vlds + VRow<PV>::addr(32 * cb + r32, 4 * (mu >> 1) + 2 * h2 + (mu & 1)));
           if (DT == DT_BF16)
             o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, va),
                                                             __builtin_bit_cast(v8bf, pbv), o[cb], 0, 0, 0);
@@ -292,16 +303,20 @@ template <int D, int PV, int DT>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
   constexpr int NCB = D / 32;                    // 32-channel blocks of O
   constexpr int VBYTES = (PV == PVFP8) ? 1 : 2;  // bytes per V element
-  constexpr int VS = VRow<PV>::STRIDE;
-  constexpr int VGR = VRow<PV>::BYTES / 16;      // 16-byte granules per V^T channel row
-  constexpr int KG = 64 * D / 16 / 256;          // K granules each thread stages
-  constexpr int VG = 64 * D * VBYTES / 16 / 256; // V granules each thread stages
-  static_assert(KG >= 1 && KG <= 2 && VG >= 1 && VG <= 4, "staging shape");
-  __shared__ __attribute__((aligned(16))) int8_t klds[2][64 * D];
-  __shared__ __attribute__((aligned(16))) uint8_t vlds[2][D * VS];
-  __shared__ float kslds[2];  // the staged chunk's K scale
+  constexpr int KB = 64 * D;                     // bytes of a K chunk
+  constexpr int VBC = 64 * D * VBYTES;           // bytes of a V^T chunk
+  constexpr int KI = KB / 4096;                  // 1 KB DMA instructions per wave, K
+  constexpr int VI = VBC / 4096;                 // ... and V
+  static_assert(KI >= 1 && KI <= 2 && VI >= 1 && VI <= 4, "staging shape");
+  // Two buffers each, as separate objects so that the compiler can tell the
+  // buffer being filled by DMA from the one being read.
+  __shared__ __attribute__((aligned(16))) int8_t kL0[KB];
+  __shared__ __attribute__((aligned(16))) int8_t kL1[KB];
+  __shared__ __attribute__((aligned(16))) uint8_t vL0[VBC];
+  __shared__ __attribute__((aligned(16))) uint8_t vL1[VBC];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h2 = lane >> 5;
 
   // ---- work item: (batch by decreasing kv_len, head, split, query tile)
@@ -347,78 +362,78 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
 
   const int nkc = A.Nkv_pad / 64;
   const int8_t* kbase = A.kc + static_cast<int64_t>(bh) * A.Nkv_pad * D;
-  const uint8_t* vbase = static_cast<const uint8_t*>(A.vt) + static_cast<int64_t>(bh) * nkc * 64 * D * VBYTES;
+  const uint8_t* vbase = static_cast<const uint8_t*>(A.vt) + static_cast<int64_t>(bh) * nkc * VBC;
   const uint8_t* ebase = A.ve + static_cast<int64_t>(bh) * nkc * 256;
   const float* ksc = A.kscale + static_cast<int64_t>(bh) * nkc;
 
-  // Staging through registers with raw buffer loads (per-thread offsets fixed
-  // in VGPRs, the chunk offset in an SGPR; reads past the end return 0): the
-  // loads are issued one step ahead and written to LDS after the step's math.
-  // K (with its scale) and V are staged separately because the main loop runs
-  // the K side one chunk ahead of the V side.  Each lane loads its own four
-  // E8M0 bytes of a chunk straight into a register.
+  // Staging: raw buffer loads that write straight into LDS (no registers),
+  // issued one step ahead.  Lane l of DMA instruction i of wave w fills LDS
+  // granule (4i + w)*64 + l of the buffer; its global source is chosen so that
+  // the buffer ends up in the swizzled layouts above.  Every chunk index is
+  // clamped to the head's last padded chunk, so all reads stay inside the
+  // head's slice; the prefetches that the clamp redirects are never consumed.
+  // The K scale and this lane's four E8M0 bytes of a chunk are plain loads
+  // into registers.
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<int8_t*>(kbase), 0, nkc * 64 * D, 0x00020000);
+      const_cast<int8_t*>(kbase), 0, nkc * KB, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(vbase), 0, nkc * 64 * D * VBYTES, 0x00020000);
+      const_cast<uint8_t*>(vbase), 0, nkc * VBC, 0x00020000);
   const __amdgpu_buffer_rsrc_t ers = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(ebase), 0, PV == PVFP8 ? nkc * 256 : 0, 0x00020000);
   const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float*>(ksc), 0, nkc * 4, 0x00020000);
-  const int voff = tid * 16;
-  v4i rk0, rk1, rv0, rv1, rv2, rv3;
-  float rks;
-  auto fetch_k = [&](int ch) {
-    const int ko = ch * 64 * D;
-    rk0 = __builtin_amdgcn_raw_buffer_load_b128(krs, voff, ko, 0);
-    if (KG > 1) rk1 = __builtin_amdgcn_raw_buffer_load_b128(krs, voff, ko + 4096, 0);
-    rks = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, 0, ch * 4, 0));
+  int koff[KI], voff[VI];
+#pragma unroll
+  for (int i = 0; i < KI; ++i) {
+    constexpr int G = D / 16;
+    const int sidx = (4 * i + w) * 64 + lane, key = sidx / G, gp = sidx % G;
+    koff[i] = key * D + ((gp ^ k_swz<D>(key)) << 4);
+  }
+#pragma unroll
+  for (int i = 0; i < VI; ++i) {
+    constexpr int GR = VRow<PV>::GR;
+    const int sidx = (4 * i + w) * 64 + lane, c = sidx / GR, gp = sidx % GR;
+    voff[i] = c * VRow<PV>::BYTES + ((gp ^ VRow<PV>::swz(c)) << 4);
+  }
+  const int last = nkc - 1;  // chunk indices are clamped: prefetches past the end go unused
+  auto dma_k = [&](int8_t* dst, int ch) {
+    ch = min(ch, last);
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      const int off = koff[i];  // an array element as the builtin's argument drops the host stub
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, dst + (4 * i + w) * 1024, 16, off, ch * KB, 0, 0);
+    }
   };
-  auto fetch_v = [&](int ch) {
-    const int vo = ch * 64 * D * VBYTES;
-    rv0 = __builtin_amdgcn_raw_buffer_load_b128(vrs, voff, vo, 0);
-    if (VG > 1) rv1 = __builtin_amdgcn_raw_buffer_load_b128(vrs, voff, vo + 4096, 0);
-    if (VG > 2) rv2 = __builtin_amdgcn_raw_buffer_load_b128(vrs, voff, vo + 8192, 0);
-    if (VG > 3) rv3 = __builtin_amdgcn_raw_buffer_load_b128(vrs, voff, vo + 12288, 0);
+  auto dma_v = [&](uint8_t* dst, int ch) {
+    ch = min(ch, last);
+#pragma unroll
+    for (int i = 0; i < VI; ++i) {
+      const int off = voff[i];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, dst + (4 * i + w) * 1024, 16, off, ch * VBC, 0, 0);
+    }
   };
-  auto fetch_e = [&](int ch) -> int {
+  auto load_ks = [&](int ch) -> float {
+    ch = min(ch, last);
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, 0, ch * 4, 0));
+  };
+  auto load_e = [&](int ch) -> int {
+    ch = min(ch, last);
     return PV == PVFP8 ? __builtin_amdgcn_raw_buffer_load_b32(ers, lane * 4, ch * 256, 0) : 0;
   };
-  auto put_k = [&](int8_t* kl, int gi, v4i v) {
-    constexpr int G = D / 16;
-    const int key = gi / G, g = gi % G;
-    *reinterpret_cast<v4i*>(kl + key * D + ((g ^ k_swz<D>(key)) << 4)) = v;
-  };
-  auto put_v = [&](uint8_t* vl, int gi, v4i v) {
-    *reinterpret_cast<v4i*>(vl + (gi / VGR) * VS + (gi % VGR) * 16) = v;
-  };
-  auto store_k = [&](int buf) {
-    put_k(klds[buf], tid, rk0);
-    if (KG > 1) put_k(klds[buf], tid + 256, rk1);
-    kslds[buf] = rks;  // every thread writes the same value
-  };
-  auto store_v = [&](int buf) {
-    put_v(vlds[buf], tid, rv0);
-    if (VG > 1) put_v(vlds[buf], tid + 256, rv1);
-    if (VG > 2) put_v(vlds[buf], tid + 512, rv2);
-    if (VG > 3) put_v(vlds[buf], tid + 768, rv3);
-  };
+  auto dma_wait = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0): this wave's DMA landed
 
   // Chunks every row of the workgroup sees in full run through the main loop;
   // the rest (the partial last chunk, frame boundaries) through the tail loop.
   const int main_hi = max(c_lo, min(wg_hi, wg_full_of(A, kv_len, q_pos0, qt)));
 
-  // Prologue: K and V of chunk c_lo in buffers 0, K of chunk c_lo + 1 in buffer 1.
-  int e_cur = 0;
-  if (c_lo < wg_hi) {
-    fetch_k(c_lo);
-    fetch_v(c_lo);
-    e_cur = fetch_e(c_lo);
-    store_k(0);
-    store_v(0);
-    fetch_k(c_lo + 1);
-    store_k(1);
-  }
+  // Prologue: K(c_lo) and V(c_lo) in buffers 0, K(c_lo + 1) in K buffer 1.
+  dma_k(kL0, c_lo);
+  dma_v(vL0, c_lo);
+  dma_k(kL1, c_lo + 1);
+  int e_cur = load_e(c_lo);
+  float ks_cur = load_ks(c_lo);
+  float ks_nxt = load_ks(c_lo + 1);
+  dma_wait();
   __syncthreads();
   // Every load issued so far has completed; saying so keeps the loops' own
   // prefetch loads from being waited on before the first MFMA.
@@ -426,76 +441,83 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
 
   // Main loop, software-pipelined within each wave: at step j (chunk
   // n = c_lo + j) K(n+1) sits in K buffer (j+1)&1 and V(n) in V buffer j&1,
-  // and S(n) is already in registers.  One straight-line block issues the
-  // loads of K(n+2) and V(n+1), the S MFMAs of chunk n+1 and the softmax of
-  // chunk n, so the matrix cores and the vector ALUs overlap; P(n) V(n) and
-  // the LDS stores follow.  Loads past the key range read zeros and their
-  // stores land in buffers nothing reads again.
+  // and S(n) is already in registers.  One straight-line region issues the
+  // DMA of K(n+2) and V(n+1), the S MFMAs of chunk n+1 and the softmax of
+  // chunk n, so the matrix cores and the vector ALUs overlap; P(n) V(n)
+  // follows, then the wait for this step's DMA and the barrier.
   v16i sa0{}, sa1{}, sb0{}, sb1{};
-  float ca = 0.f, cb_ = 0.f;
-  if (c_lo < main_hi) {
-    qk_chunk<D>(klds[0], qv, lane, sa0, sa1);
-    ca = qsc * kslds[0];
-  }
-  int j = 0;
-  auto step = [&](int n, v16i& cs0, v16i& cs1, float& c_cur, v16i& ns0, v16i& ns1, float& c_nxt) {
-    const int kb_nxt = (j + 1) & 1, vb_cur = j & 1;
-    // Region 1: the loads one chunk ahead, the S MFMAs of chunk n+1 and the
-    // softmax of chunk n, interleaved so the matrix cores and the vector
-    // ALUs work at the same time.
+  float ca = qsc * ks_cur;
+  if (c_lo < main_hi) qk_chunk<D>(kL0, qv, lane, sa0, sa1);
+  int n = c_lo;
+  auto step = [&](auto par, v16i& cs0, v16i& cs1, float& c_cur, v16i& ns0, v16i& ns1, float& c_nxt) {
+    constexpr int P = decltype(par)::value;  // parity of the step
+    int8_t* k_rd = P ? kL0 : kL1;            // K(n+1)
+    int8_t* k_wr = P ? kL1 : kL0;            // receives K(n+2)
+    uint8_t* v_rd = P ? vL1 : vL0;           // V(n)
+    uint8_t* v_wr = P ? vL0 : vL1;           // receives V(n+1)
     __builtin_amdgcn_sched_barrier(0);
-    fetch_k(n + 2);
-    fetch_v(n + 1);
-    const int e_nxt = fetch_e(n + 1);
-    qk_chunk<D>(klds[kb_nxt], qv, lane, ns0, ns1);
-    PTile<PV> P;
-    const float alpha = st.softmax(cs0, cs1, c_cur, true, false, P);
-    __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);  // the buffer loads
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // the first K reads
+    dma_k(k_wr, n + 2);
+    dma_v(v_wr, n + 1);
+    const int e_nxt = load_e(n + 1);
+    const float ks_2 = load_ks(n + 2);
+    qk_chunk<D>(k_rd, qv, lane, ns0, ns1);
+    PTile<PV> Pt;
+    const float alpha = st.softmax(cs0, cs1, c_cur, true, false, Pt);
+    __builtin_amdgcn_sched_group_barrier(0x020, 2 + KI + VI, 0);  // the loads
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);            // the first K reads
 #pragma unroll
     for (int g = 0; g < 2 * D / 32; ++g) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one S MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);  // a slice of the softmax
+      __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);  // a slice of the softmax
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // the next K read
     }
     // Pin the region's results here so that no earlier pass moves the MFMAs
     // or the softmax out of it.
     asm volatile("" : "+v"(ns0), "+v"(ns1));
-    P.pin();
+    Pt.pin();
     __builtin_amdgcn_sched_barrier(0);
-    // Region 2 (rare): rescale O when some row's running max moved.
-    st.rescale(alpha);
-    // Region 3: P(n) V(n), the LDS stores of the prefetched chunks, barrier.
-    c_nxt = qsc * kslds[kb_nxt];
-    st.pv(P, vlds[vb_cur], e_cur, lane);
-    store_k(vb_cur);
-    store_v(kb_nxt);
+    st.rescale(alpha);  // rare: some row's running max moved
+    c_nxt = qsc * ks_nxt;
+    st.pv(Pt, v_rd, e_cur, lane);
+    dma_wait();
     __syncthreads();
     e_cur = e_nxt;
-    ++j;
-  };
-  int n = c_lo;
-  for (; n + 1 < main_hi; n += 2) {
-    step(n, sa0, sa1, ca, sb0, sb1, cb_);
-    step(n + 1, sb0, sb1, cb_, sa0, sa1, ca);
-  }
-  if (n < main_hi) {
-    step(n, sa0, sa1, ca, sb0, sb1, cb_);
+    ks_nxt = ks_2;
     ++n;
+  };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  float cb_ = 0.f;
+  while (n + 1 < main_hi) {
+    step(P0{}, sa0, sa1, ca, sb0, sb1, cb_);
+    step(P1{}, sb0, sb1, cb_, sa0, sa1, ca);
   }
-  // Tail loop: chunk n with K and V both in buffers j&1 (and its E8M0 bytes
-  // in e_cur); the next chunk's K and V are (re)staged into the other buffers.
-  for (; n < wg_hi; ++n, ++j) {
-    const int buf = j & 1;
-    fetch_k(n + 1);
-    fetch_v(n + 1);
-    const int e_nxt = fetch_e(n + 1);
-    if (n < wave_hi)
-      st.chunk(klds[buf], vlds[buf], e_cur, qv, qsc * kslds[buf], n >= wave_full, n * 64 + 16 * h2, re, lane);
-    store_k(buf ^ 1);
-    store_v(buf ^ 1);
+  int j = n - c_lo;
+  if (n < main_hi) {
+    step(P0{}, sa0, sa1, ca, sb0, sb1, cb_);
+    j = n - c_lo;
+  }
+  // Tail loop: chunk n with K and V both in buffers j&1; the next chunk's K
+  // and V are staged into the other buffers.
+  auto tail = [&](auto par) {
+    constexpr int P = decltype(par)::value;
+    int8_t* k_rd = P ? kL1 : kL0;
+    int8_t* k_wr = P ? kL0 : kL1;
+    uint8_t* v_rd = P ? vL1 : vL0;
+    uint8_t* v_wr = P ? vL0 : vL1;
+    const float c = qsc * load_ks(n);
+    dma_k(k_wr, n + 1);
+    dma_v(v_wr, n + 1);
+    const int e_nxt = load_e(n + 1);
+    if (n < wave_hi) st.chunk(k_rd, v_rd, e_cur, qv, c, n >= wave_full, n * 64 + 16 * h2, re, lane);
+    dma_wait();
     __syncthreads();
     e_cur = e_nxt;
+    ++n;
+  };
+  while (n < wg_hi) {
+    if (((n - c_lo) & 1) == 0) tail(P0{});
+    else tail(P1{});
   }
   v16f* o = st.o;
   const float m = st.m, l = st.l;

@@ -79,6 +79,14 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float
   return static_cast<uint32_t>(r);
 }
 
+// As pack_e4m3x4, without first zeroing the destination: the first convert
+// keeps the upper half of its `old` operand, which the second overwrites.
+__device__ __forceinline__ uint32_t pack_e4m3x4_into(float a, float b, float c, float d) {
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __builtin_bit_cast(int, c), false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
+  return static_cast<uint32_t>(r);
+}
+
 template <int DT> struct Pack16;
 template <> struct Pack16<DT_BF16> {
   static __device__ __forceinline__ uint32_t pack(float a, float b) { return pack_bf16x2(a, b); }
