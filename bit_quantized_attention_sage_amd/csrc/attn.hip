@@ -48,12 +48,15 @@ __device__ __forceinline__ int a_row_key(int r, int u) {
 }
 
 // 16-byte granule swizzle of the K chunk in LDS: granule g of key k is
-// stored at slot g ^ swz(k), spreading the 8 keys one ds_read_b128 phase
-// touches over distinct banks.
+// stored at slot g ^ swz(k).  A ds_read_b128 is served 16 lanes at a time
+// from 64 four-byte banks; the 16 keys such a group reads (a_row_key order:
+// {0..3, 16..19, 4..7, 20..23} + 8t) then land on 16 distinct 16-byte bank
+// slots.  The same holds for 8-lane groups over 32 banks.
 template <int D>
 __device__ __forceinline__ int k_swz(int key) {
-  constexpr int G = D / 16;
-  return ((key & 3) | (((key >> 4) & 1) << 2)) & (G - 1);
+  const int b0 = key & 1, b1 = (key >> 1) & 1, b2 = (key >> 2) & 1, b4 = (key >> 4) & 1;
+  if constexpr (D == 128) return b1 | (b4 << 1) | ((b0 ^ b2) << 2);
+  else return (b1 ^ b2) | (b4 << 1);
 }
 
 // S^T for one 64-key chunk held in LDS (row-major [64][D], swizzled):
@@ -118,14 +121,19 @@ struct AttnArgs {
 
 // LDS layout of a staged chunk.  K: [64 keys][D] bytes with the granule
 // swizzle above.  V^T: [D channels][64 keys], 64 B (FP8) or 128 B (16-bit)
-// per channel row, granule g of row c stored at slot g ^ v_swz(c), so that the
-// 8 lanes of one ds_read_b128 phase, which read the same granule of 8
-// consecutive channels, hit distinct banks.
+// per channel row, granule g of row c stored at slot g ^ swz(c); a P.V
+// operand read takes the same granule of consecutive channel rows.
 template <int PV>
 struct VRow {
   static constexpr int BYTES = (PV == PVFP8) ? 64 : 128;  // bytes per channel row
   static constexpr int GR = BYTES / 16;                    // granules per row
-  static __device__ __forceinline__ int swz(int c) { return (PV == PVFP8) ? ((c >> 1) & 3) : (c & 7); }
+  // granule swizzle: the 16 channel rows c = 16t..16t+15 one read group
+  // touches (and any 8 consecutive ones) fall on distinct bank slots
+  static __device__ __forceinline__ int swz(int c) {
+    const int b0 = c & 1, b1 = (c >> 1) & 1, b2 = (c >> 2) & 1, b3 = (c >> 3) & 1;
+    if constexpr (PV == PVFP8) return (b1 ^ b3) | (b2 << 1);
+    else return b1 | (b2 << 1) | ((b0 ^ b3) << 2);
+  }
   static __device__ __forceinline__ int addr(int c, int g) { return c * BYTES + ((g ^ swz(c)) << 4); }
 };
 
