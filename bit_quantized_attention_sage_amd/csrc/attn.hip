@@ -156,12 +156,25 @@ struct PTile<PV16> {
 };
 
 // Per-wave online-softmax state and the math of one chunk.
+// Constant A operand of the row-sum MFMAs (16x16, K = 128 e4m3 or 32 16-bit
+// values).  A 16x16 MFMA pairs lane m + 16g of A with lane n + 16g of B (same
+// K indices) and returns D[4*(l/16) + j][l%16] to lane l.  The P tile, read
+// as such a B operand, has query row n + 16*(g&1) in lane group g.  Row m of
+// A is all ones where m%4 == 0 and (m/4)&1 == g&1, zero elsewhere, so D[4k][n]
+// sums row n + 16*(k&1) over both lane halves: register 0 of lane l ends up
+// with the P sum of its own query row l%32.
+__device__ __forceinline__ int lsum_select(int lane, int one4) {
+  const int m = lane & 15, g = lane >> 4;
+  return ((m & 3) == 0 && ((m >> 2) & 1) == (g & 1)) ? one4 : 0;
+}
+
 template <int D, int PV, int DT>
 struct WaveState {
   static constexpr int NCB = D / 32;
   static constexpr int SHIFT = (PV == PVFP8) ? PSHIFT_FP8 : PSHIFT_16;
   v16f o[NCB];
-  float m, l;
+  v4f ls;  // row sums of P as the P.V MFMAs see it (register 0; see lsum_select)
+  float m;
 
   // Masking of a boundary chunk: keys at or beyond this row's visible end
   // `re` get the sentinel score (they then take no part in the maximum, and
@@ -179,9 +192,10 @@ struct WaveState {
   // Softmax step of one chunk on its integer scores: the row maximum (the
   // two lane halves hold the same query), the lazy running-max update (the
   // row adopts the chunk maximum only when it exceeds m by more than TAU),
-  // p = 2^(S c - (m - s)), l = alpha l + sum p, and P rounded to the P.V
-  // operand type.  Returns alpha (1 for rows that kept m); the caller
-  // rescales O by it when any row of the wave moved.
+  // p = 2^(S c - (m - s)) and P rounded to the P.V operand type.  Returns
+  // alpha (1 for rows that kept m); the caller rescales O and the row sums
+  // by it when any row of the wave moved.  The row sums of the rounded P are
+  // taken on the matrix cores in pv().
   __device__ __forceinline__ float softmax(const v16i& s0, const v16i& s1, float c, bool has, bool masked,
                                            PTile<PV>& P) {
     int ma = max(s0[0], s0[1]), mb = max(s1[0], s1[1]);  // two v_max3 chains
@@ -214,13 +228,6 @@ struct WaveState {
         p1[i] = (s1[i] != SENTINEL) ? p1[i] : 0.f;
       }
     }
-    float ls0 = 0.f, ls1 = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      ls0 += p0[i];
-      ls1 += p1[i];
-    }
-    l = alpha * l + (ls0 + ls1);
     if constexpr (PV == PVFP8) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -243,11 +250,13 @@ struct WaveState {
       for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[cb][i] *= alpha;
+      ls[0] *= alpha;
     }
   }
 
-  // O += P V over the chunk; e8: this lane's four E8M0 bytes (FP8 mode; byte
-  // cb scales channel block cb of the lane's 32-key block).
+  // O += P V over the chunk, and the row sums of P; e8: this lane's four E8M0
+  // bytes (FP8 mode; byte cb scales channel block cb of the lane's 32-key
+  // block).
   __device__ __forceinline__ void pv(const PTile<PV>& P, const uint8_t* vlds, int e8, int lane) {
     const int h2 = lane >> 5, r32 = lane & 31;
     if constexpr (PV == PVFP8) {
@@ -266,7 +275,12 @@ struct WaveState {
         one(std::integral_constant<int, 2>{});
         one(std::integral_constant<int, 3>{});
       }
+      const int s1 = lsum_select(lane, 0x38383838);  // e4m3 1.0 = 0x38
+      const v8i sel = {s1, s1, s1, s1, s1, s1, s1, s1};
+      ls = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sel, P.b, ls, 0, 0, 0, 127, 0, 127);
     } else {
+      const int s1 = lsum_select(lane, DT == DT_BF16 ? 0x3F803F80 : 0x3C003C00);  // 1.0 pairs
+      const v4i sel = {s1, s1, s1, s1};
 #pragma unroll
       for (int mu = 0; mu < 4; ++mu) {
         const v4i pbv = {static_cast<int>(P.w[4 * mu]), static_cast<int>(P.w[4 * mu + 1]),
@@ -282,6 +296,12 @@ struct WaveState {
             o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, va),
                                                            __builtin_bit_cast(v8h, pbv), o[cb], 0, 0, 0);
         }
+        if (DT == DT_BF16)
+          ls = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, sel),
+                                                       __builtin_bit_cast(v8bf, pbv), ls, 0, 0, 0);
+        else
+          ls = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, sel),
+                                                      __builtin_bit_cast(v8h, pbv), ls, 0, 0, 0);
       }
     }
   }
@@ -365,8 +385,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
   WaveState<D, PV, DT> st;
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) st.o[cb] = v16f{0.f};
+  st.ls = v4f{0.f, 0.f, 0.f, 0.f};
   st.m = -__builtin_inff();
-  st.l = 0.f;
 
   const int nkc = A.Nkv_pad / 64;
   const int8_t* kbase = A.kc + static_cast<int64_t>(bh) * A.Nkv_pad * D;
@@ -528,10 +548,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
     else tail(P1{});
   }
   v16f* o = st.o;
-  const float m = st.m, l = st.l;
+  const float m = st.m;
 
-  // ---- epilogue: combine the two lane halves' row sums, normalise, store
-  const float ltot = l + __shfl_xor(l, 32, 64);
+  // ---- epilogue: normalise, store
+  const float ltot = st.ls[0];  // already summed over both lane halves
   if (qi >= A.Nq) return;
   if (A.splits == 1) {
     const float inv = 1.0f / ltot;

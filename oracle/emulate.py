@@ -20,12 +20,14 @@ chunks of BK = 64 (chunk t = keys [64t, 64t+64)), in ascending order:
      otherwise m, l and acc are kept as they are.
   5. x[i,j]   = fp32(S[i,j] * c_t - fp32(m - s))  with ONE rounding (an FMA),
      s = 4 in FP8 mode, 0 in 16-bit mode;  p = fp32(2^x), 0 if not visible.
-  6. l       += sum_j p                      (unrounded p)
-  7. p~       = p rounded to the P.V operand type: e4m3fn in FP8 mode (where
+  6. p~       = p rounded to the P.V operand type: e4m3fn in FP8 mode (where
      p already carries the 2^s pre-scale), else the input's fp16/bf16
+  7. l       += sum_j p~                     (the rounded operand itself)
   8. acc     += sum_j p~[i,j] * V^[j,:]
 Finally O[i] = acc / l; the 2^s pre-scale cancels in that ratio.  The output
-is rounded (RNE) to the input dtype.
+is rounded (RNE) to the input dtype.  Because l sums exactly the weights that
+multiply V^, every output row is a convex combination of the visible V^ rows
+(a constant V^ column comes out unchanged).
 
 Because m only moves when a chunk maximum exceeds it by more than TAU, the
 exponent argument is at most TAU + s = 8, so p~ never exceeds 2^8 -- inside
@@ -106,11 +108,11 @@ def _chunk_step(S, c_t, vis, m, l, acc, Vc, pv_mode, p_dtype):
                 np.broadcast_to(-mref[:, None], S.shape))
     p = np.exp2(x.astype(np.float64)).astype(_F32)
     p = np.where(vis, p, _F32(0.0))
-    l = l + p.astype(np.float64).sum(axis=1)
     if pv_mode == PV_FP8:
         pt = codecs.round_e4m3(p.astype(np.float64))
     else:
         pt = codecs.round_to(p, p_dtype).astype(np.float64)
+    l = l + pt.sum(axis=1)
     acc = acc + pt @ Vc
     return m, l, acc
 

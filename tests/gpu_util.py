@@ -109,20 +109,37 @@ def ulp16(x, dtype):
     return np.exp2(np.maximum(e, -14) - 10)
 
 
-def compare_output(out_gpu, o64, dtype, pv_mode):
+# Accumulation of the scaled FP8 matrix-core products (measured on gfx950 with
+# one-wave probes of v_mfma_scale_f32_32x32x64_f8f6f4): products are summed in
+# groups of 8 consecutive K indices, aligned to the group's largest product
+# with 13 fractional bits; bits below that are dropped (terms 2^-14 of the
+# group maximum vanish, terms 2^-13 survive).  A group therefore loses less
+# than 7 * 2^-13 of its largest |product|.  The 16-bit MFMAs showed no such
+# loss (float32 rounding of the running sum only).
+FP8_ACC = 7 * 2.0 ** -13
+
+
+def compare_output(out_gpu, o64, dtype, pv_mode, o_abs=None):
     """Compare the GPU output with the emulation's unrounded float64 result.
 
     The GPU output is that value computed in float32 and rounded (RNE) to the
     16-bit output type, so each element may differ by half a spacing of that
     type (plus float32 accumulation noise); the acceptance bar is max-abs
     <= 2e-3, widened to that half spacing where the type itself is coarser.
+    In FP8 mode the matrix cores' grouped accumulation (FP8_ACC) perturbs
+    acc = sum p~ v and l = sum p~ by at most FP8_ACC * sum p~ |v| and
+    FP8_ACC * l, so O = acc / l moves by at most FP8_ACC * (a + |O|) with
+    a = sum p~ |v| / l, which is the emulation's output for |V| (o_abs); that
+    much is added to the bar when o_abs is given.
     Returns (max_abs, worst excess over the per-element bound, fraction of
     elements beyond the tight rounding-only bound, relative L2 error, its
-    bound: ulp/sqrt(12) of the type, plus 1e-3 in FP8 mode for rare e4m3
-    rounding flips of P where the hardware exp2 differs in the last bit)."""
+    bound: ulp/sqrt(12) of the type, plus 1e-3 in FP8 mode for the grouped
+    accumulation)."""
     diff = np.abs(out_gpu - o64)
     half = 0.5 * ulp16(o64, dtype) * (1 + 2.0 ** -8)
     tol = np.maximum(2e-3, half + 1e-6)
+    if pv_mode == PV_FP8 and o_abs is not None:
+        tol = np.maximum(2e-3, half + 1e-6 + FP8_ACC * (o_abs + np.abs(o64)))
     excess = float((diff - tol).max())
     tight = half + 1e-5 * float(np.abs(o64).max())
     frac = float(np.mean(diff > tight))

@@ -57,9 +57,10 @@ def test_workload_parity(lib, name, heads, R):
             continue
         Qh, Kh, Vh = Q[:, hs], K[:, hs], V[:, hs]
         o64, _ = _emulate(Qh, Kh, Vh, w, kvl[b], qp[b], rows, S)
+        o_abs = _emulate(Qh, Kh, np.abs(Vh), w, kvl[b], qp[b], rows, S)[0] if w.pv_mode == PV_FP8 else None
         og = host(o[b:b + 1, hs])
         og = og if rows is None else og[:, :, rows]
-        mx, excess, frac, rel, rel_bound = compare_output(og, o64, w.dtype, w.pv_mode)
+        mx, excess, frac, rel, rel_bound = compare_output(og, o64, w.dtype, w.pv_mode, o_abs)
         print(f"  b{b} heads {hs}: max-abs {mx:.2e} excess {excess:.2e} beyond-rounding {frac:.2e} "
               f"rel-L2 {rel:.2e}", flush=True)
         assert excess <= 0

@@ -148,7 +148,9 @@ def test_emulation_exact_inputs_match_textbook_attention():
                                                (PV_FP8, "bf16", 2.0 ** -4)])
 def test_emulation_equals_attention_on_dequantized_operands(pv_mode, dtype, eps):
     """Textbook attention on Q'=dq*qcodes, K'=dk*kcodes, V^ differs from the
-    emulation only by P's rounding: |diff| <= eps * sum p|v| / sum p."""
+    emulation only by P's rounding.  With p~ = p (1 + e_j), |e_j| <= eps, and l
+    summing p~, diff_i = sum_j p_j e_j (v_j - ref_i) / sum_j p~_j, so
+    |diff| <= eps / (1 - eps) * max_j |v_j - ref_i| <= 2 eps max|V^| (1 + eps)."""
     rng = np.random.default_rng(24)
     B, H, Nq, Nkv, d = 1, 2, 150, 333, 32
     Q, K, V = _inputs(rng, B, H, Nq, Nkv, d, dtype)
@@ -165,7 +167,7 @@ def test_emulation_equals_attention_on_dequantized_operands(pv_mode, dtype, eps)
     Qd = qc * np.repeat(dq, 128, axis=2)[:, :, :Nq, None].astype(np.float64)
     Kd = kc * np.repeat(dk, 64, axis=2)[:, :, :Nkv, None].astype(np.float64)
     ref = attention.attention_fp64(Qd, Kd, Vh, 0.3)
-    bound = eps * np.abs(Vh).max() * 1.01 + 1e-12
+    bound = 2 * eps * np.abs(Vh).max() * 1.01 + 1e-12
     assert np.abs(o64 - ref).max() <= bound
     # and the difference is real rounding noise, not a systematic error
     assert np.abs(o64 - ref).mean() < 0.25 * bound
@@ -212,5 +214,29 @@ def test_lazy_running_max_policy_by_hand():
     m, l, acc = _run_rows(S, np.array([0.5], np.float32), np.ones(len(maxima), np.float32),
                           np.array([S.shape[1]]), V, 0, len(maxima), PV_16, "bf16", trace)
     assert [float(x[0]) for x in trace] == [0.0, 0.0, 6.0, 6.0, 11.0, 11.0]
-    # output of all-ones V is exactly 1 up to P rounding
-    np.testing.assert_allclose(acc / l[:, None], 1.0, atol=2.0 ** -8)
+    # l sums the rounded weights: all-ones V gives exactly 1
+    np.testing.assert_allclose(acc / l[:, None], 1.0, rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("pv_mode,dtype", [(PV_16, "bf16"), (PV_16, "f16"), (PV_FP8, "bf16")])
+@pytest.mark.parametrize("frame_len", [0, 64])
+def test_emulation_constant_v_columns_pass_through(pv_mode, dtype, frame_len):
+    """l sums exactly the weights that multiply V^, so each output row is a
+    convex combination of visible V^ rows: a V whose every key row is the
+    same vector comes out as that vector's V^ (FP8: its e4m3 x E8M0 value),
+    bit-exactly after rounding to the output type, whatever Q and K are."""
+    rng = np.random.default_rng(27)
+    B, H, Nq, Nkv, d = 1, 2, 100, 300, 32
+    Q, K, _ = _inputs(rng, B, H, Nq, Nkv, d, dtype)
+    Q *= 3                                          # peaky rows: the lazy max moves
+    row = codecs.round_to(rng.standard_normal((1, H, 1, d)).astype(np.float32), dtype)
+    V = np.broadcast_to(row, (B, H, Nkv, d)).copy()
+    kv = [Nkv]
+    o64, o = emulate.emulate_from_inputs(Q, K, V, pv_mode, dtype, frame_len=frame_len, kv_len=kv)
+    if pv_mode == PV_FP8:
+        vc, ve, _ = quant.quantize_v_fp8(V, kv)
+        want = quant.dequant_v_fp8(vc, ve)[:, :, :1]
+    else:
+        want = V[:, :, :1].astype(np.float64)
+    want = codecs.round_to(want.astype(np.float32), dtype)
+    assert np.array_equal(o, np.broadcast_to(want, o.shape))
