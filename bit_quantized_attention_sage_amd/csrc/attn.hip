@@ -198,13 +198,14 @@ struct WaveState {
   // taken on the matrix cores in pv().
   __device__ __forceinline__ float softmax(const v16i& s0, const v16i& s1, float c, bool has, bool masked,
                                            PTile<PV>& P) {
-    int ma = max(s0[0], s0[1]), mb = max(s1[0], s1[1]);  // two v_max3 chains
+    // two v_max3 chains of 8 over the lane's 32 scores
+    int ma = max3_i32(s0[0], s0[1], s0[2]), mb = max3_i32(s1[0], s1[1], s1[2]);
 #pragma unroll
-    for (int i = 2; i < 16; i += 2) {
-      ma = max(ma, max(s0[i], s0[i + 1]));
-      mb = max(mb, max(s1[i], s1[i + 1]));
+    for (int i = 3; i < 15; i += 2) {
+      ma = max3_i32(ma, s0[i], s0[i + 1]);
+      mb = max3_i32(mb, s1[i], s1[i + 1]);
     }
-    int mx = max(ma, mb);
+    int mx = max3_i32(max(ma, s0[15]), mb, s1[15]);
     {
       const auto sw = __builtin_amdgcn_permlane32_swap(mx, mx, false, false);
       mx = max(static_cast<int>(sw[0]), static_cast<int>(sw[1]));
@@ -454,78 +455,112 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
   // the rest (the partial last chunk, frame boundaries) through the tail loop.
   const int main_hi = max(c_lo, min(wg_hi, wg_full_of(A, kv_len, q_pos0, qt)));
 
-  // Prologue: K(c_lo) and V(c_lo) in buffers 0, K(c_lo + 1) in K buffer 1.
-  dma_k(kL0, c_lo);
-  dma_v(vL0, c_lo);
-  dma_k(kL1, c_lo + 1);
+  // Main loop, software-pipelined within each wave over three chunks: step
+  // j (chunk n = c_lo + j) enters with S(n+1) and P(n) in registers, K(n+2)
+  // in K buffer j&1 and V(n) in V buffer j&1.  One straight-line region
+  // issues the DMA of K(n+3) and V(n+1), the S MFMAs of chunk n+2, the P.V
+  // MFMAs of chunk n and the softmax of chunk n+1, so the matrix cores and
+  // the vector ALUs work side by side; then the (rare) rescale by chunk
+  // n+1's alpha, the wait for this step's DMA and the barrier.
+  const int J = main_hi - c_lo;  // chunks through the main loop
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  v16i sa0{}, sa1{}, sb0{}, sb1{};
+  PTile<PV> pa, pb;
+  int n = c_lo;
   int e_cur = load_e(c_lo);
-  float ks_cur = load_ks(c_lo);
-  float ks_nxt = load_ks(c_lo + 1);
-  dma_wait();
-  __syncthreads();
-  // Every load issued so far has completed; saying so keeps the loops' own
+  float ksn1 = load_ks(c_lo + 1), ksn2 = load_ks(c_lo + 2);  // K scales of chunks n+1, n+2
+  // Prologue: K(c_lo) and V(c_lo) in buffers 0, K(c_lo + 1) in K buffer 1;
+  // with main chunks also S(c_lo + 1), P(c_lo) and K(c_lo + 2) in K buffer 0.
+  {
+    const float ks0 = load_ks(c_lo);
+    dma_k(kL0, c_lo);
+    dma_v(vL0, c_lo);
+    dma_k(kL1, c_lo + 1);
+    dma_wait();
+    __syncthreads();
+    if (J >= 1) {
+      qk_chunk<D>(kL0, qv, lane, sb0, sb1);
+      if (J >= 2) qk_chunk<D>(kL1, qv, lane, sa0, sa1);
+      __syncthreads();  // every wave has read K(c_lo) from buffer 0
+      dma_k(kL0, c_lo + 2);
+      st.rescale(st.softmax(sb0, sb1, qsc * ks0, true, false, pa));
+      dma_wait();
+      __syncthreads();
+    }
+  }
+  // Every load issued so far has completed; saying so keeps the loop's own
   // prefetch loads from being waited on before the first MFMA.
   __builtin_amdgcn_s_waitcnt(0);
 
-  // Main loop, software-pipelined within each wave: at step j (chunk
-  // n = c_lo + j) K(n+1) sits in K buffer (j+1)&1 and V(n) in V buffer j&1,
-  // and S(n) is already in registers.  One straight-line region issues the
-  // DMA of K(n+2) and V(n+1), the S MFMAs of chunk n+1 and the softmax of
-  // chunk n, so the matrix cores and the vector ALUs overlap; P(n) V(n)
-  // follows, then the wait for this step's DMA and the barrier.
-  v16i sa0{}, sa1{}, sb0{}, sb1{};
-  float ca = qsc * ks_cur;
-  if (c_lo < main_hi) qk_chunk<D>(kL0, qv, lane, sa0, sa1);
-  int n = c_lo;
-  auto step = [&](auto par, v16i& cs0, v16i& cs1, float& c_cur, v16i& ns0, v16i& ns1, float& c_nxt) {
+  auto step = [&](auto par, v16i& cs0, v16i& cs1, PTile<PV>& p_cur, v16i& ns0, v16i& ns1, PTile<PV>& p_nxt) {
     constexpr int P = decltype(par)::value;  // parity of the step
-    int8_t* k_rd = P ? kL0 : kL1;            // K(n+1)
-    int8_t* k_wr = P ? kL1 : kL0;            // receives K(n+2)
+    int8_t* k_rd = P ? kL1 : kL0;            // K(n+2)
+    int8_t* k_wr = P ? kL0 : kL1;            // receives K(n+3)
     uint8_t* v_rd = P ? vL1 : vL0;           // V(n)
     uint8_t* v_wr = P ? vL0 : vL1;           // receives V(n+1)
+    constexpr int NQK = 2 * D / 32;                               // S MFMAs
+    constexpr int NPV = (PV == PVFP8) ? NCB + 1 : 4 * NCB + 4;    // P.V and row-sum MFMAs
+    constexpr int NRD = NQK + ((PV == PVFP8) ? 2 * NCB : 4 * NCB);  // LDS operand reads
+    constexpr int VPER = (PV == PVFP8) ? 12 : 5;                  // softmax slice per MFMA
+    const float c_mid = qsc * ksn1;
     __builtin_amdgcn_sched_barrier(0);
-    dma_k(k_wr, n + 2);
+    dma_k(k_wr, n + 3);
     dma_v(v_wr, n + 1);
     const int e_nxt = load_e(n + 1);
-    const float ks_2 = load_ks(n + 2);
+    const float ks3 = load_ks(n + 3);
     qk_chunk<D>(k_rd, qv, lane, ns0, ns1);
-    PTile<PV> Pt;
-    const float alpha = st.softmax(cs0, cs1, c_cur, true, false, Pt);
+    st.pv(p_cur, v_rd, e_cur, lane);
+    const float alpha = st.softmax(cs0, cs1, c_mid, true, false, p_nxt);
     __builtin_amdgcn_sched_group_barrier(0x020, 2 + KI + VI, 0);  // the loads
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);            // the first K reads
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);            // the first operand reads
 #pragma unroll
-    for (int g = 0; g < 2 * D / 32; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one S MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);  // a slice of the softmax
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // the next K read
+    for (int g = 0; g < NQK + NPV; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, VPER, 0);  // a slice of the softmax
+      if (g + 4 < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // the next read
     }
-    // Pin the region's results here so that no earlier pass moves the MFMAs
-    // or the softmax out of it.
+    // Pin the region's results here so that no earlier pass moves the S
+    // MFMAs or the softmax out of it.
     asm volatile("" : "+v"(ns0), "+v"(ns1));
-    Pt.pin();
+    p_nxt.pin();
     __builtin_amdgcn_sched_barrier(0);
-    st.rescale(alpha);  // rare: some row's running max moved
-    c_nxt = qsc * ks_nxt;
-    st.pv(Pt, v_rd, e_cur, lane);
+    st.rescale(alpha);  // rare: some row's running max moved (after P(n) V(n))
     dma_wait();
     __syncthreads();
     e_cur = e_nxt;
-    ks_nxt = ks_2;
+    ksn1 = ksn2;
+    ksn2 = ks3;
     ++n;
   };
-  using P0 = std::integral_constant<int, 0>;
-  using P1 = std::integral_constant<int, 1>;
-  float cb_ = 0.f;
-  while (n + 1 < main_hi) {
-    step(P0{}, sa0, sa1, ca, sb0, sb1, cb_);
-    step(P1{}, sb0, sb1, cb_, sa0, sa1, ca);
+  // The last main chunk's P.V, with V(n+1) staged for the tail.
+  auto finish = [&](auto par, PTile<PV>& p_cur) {
+    constexpr int P = decltype(par)::value;
+    uint8_t* v_rd = P ? vL1 : vL0;
+    uint8_t* v_wr = P ? vL0 : vL1;
+    dma_v(v_wr, n + 1);
+    const int e_nxt = load_e(n + 1);
+    st.pv(p_cur, v_rd, e_cur, lane);
+    dma_wait();
+    __syncthreads();
+    e_cur = e_nxt;
+    ++n;
+  };
+  if (J >= 1) {
+    int left = J - 1;  // pipelined steps
+    while (left >= 2) {
+      step(P0{}, sa0, sa1, pa, sb0, sb1, pb);
+      step(P1{}, sb0, sb1, pb, sa0, sa1, pa);
+      left -= 2;
+    }
+    if (left == 1) {
+      step(P0{}, sa0, sa1, pa, sb0, sb1, pb);
+      finish(P1{}, pb);
+    } else {
+      finish(P0{}, pa);
+    }
   }
-  int j = n - c_lo;
-  if (n < main_hi) {
-    step(P0{}, sa0, sa1, ca, sb0, sb1, cb_);
-    j = n - c_lo;
-  }
-  // Tail loop: chunk n with K and V both in buffers j&1; the next chunk's K
+  // Tail loop: chunk n with K and V both in buffers (n - c_lo)&1; the next chunk's K
   // and V are staged into the other buffers.
   auto tail = [&](auto par) {
     constexpr int P = decltype(par)::value;

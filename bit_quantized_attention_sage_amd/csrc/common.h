@@ -82,8 +82,9 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float
 
 // As pack_e4m3x4, without first zeroing the destination: the first convert
 // keeps the upper half of its `old` operand, which the second overwrites.
+// `old` is a's own register (dead after that convert), so nothing is copied.
 __device__ __forceinline__ uint32_t pack_e4m3x4_into(float a, float b, float c, float d) {
-  int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __builtin_bit_cast(int, c), false);
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __builtin_bit_cast(int, a), false);
   r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
   return static_cast<uint32_t>(r);
 }
@@ -99,6 +100,13 @@ template <> struct Pack16<DT_F16> {
   static __device__ __forceinline__ float lo(uint32_t w) { return f16_bits_to_f32(w & 0xFFFFu); }
   static __device__ __forceinline__ float hi(uint32_t w) { return f16_bits_to_f32(w >> 16); }
 };
+
+// max(a, b, c) in one v_max3_i32.
+__device__ __forceinline__ int max3_i32(int a, int b, int c) {
+  int r;
+  asm("v_max3_i32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
 
 // Wave-wide (64 lanes) reductions.
 __device__ __forceinline__ float wave_max(float v) {
