@@ -42,6 +42,14 @@ namespace sage {
 
 constexpr int SENTINEL = -(1 << 30);  // masked score before the row maximum
 
+// Score bias.  The S MFMAs start their integer accumulation from the inline
+// constant 1/(2 pi), whose float32 bits are SBIAS, so they return SBIAS + S.
+// For |S| < 2292099 (|S| <= 127^2 d here) those bits are exactly the float32
+// F0 + S 2^-26 (F0 = 1/(2 pi) rounded to float32), so the softmax reads the
+// score as a float without a conversion and forms S c - mref as
+// fma(F, c 2^26, fma(-F0, c 2^26, -mref)).
+constexpr int SBIAS = 0x3E22F983;
+
 // Key held by row r of subtile u of a chunk's A operand (see above).
 __device__ __forceinline__ int a_row_key(int r, int u) {
   return 32 * u + 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3);
@@ -59,7 +67,21 @@ __device__ __forceinline__ int k_swz(int key) {
   else return (b1 ^ b2) | (b4 << 1);
 }
 
-// S^T for one 64-key chunk held in LDS (row-major [64][D], swizzled):
+// First k-step of an S chain: A B + SBIAS, the bias as the MFMA's inline
+// accumulator constant.  (Written out because the compiler, seeing the same
+// constant start two chains, keeps it in sixteen registers and copies it
+// into each accumulator every chunk instead.)  The compiler cannot see that
+// this is an 8-pass matrix op, so it inserts none of the wait states its
+// result needs: the block ends with 16 of them itself (an 8-pass XDL result
+// needs 11 before any dependent read), which also keeps later writes to its
+// source registers clear of its operand reads.
+__device__ __forceinline__ v16i mfma_i8_biased(v4i a, v4i b) {
+  v16i d;
+  asm("v_mfma_i32_32x32x32_i8 %0, %1, %2, 0.15915494\n\ts_nop 7\n\ts_nop 7" : "=&v"(d) : "v"(a), "v"(b));
+  return d;
+}
+
+// S^T + SBIAS for one 64-key chunk held in LDS (row-major [64][D], swizzled):
 // s0 = keys 16*h2 + [0,16), s1 = keys 32 + 16*h2 + [0,16), per the layout above.
 template <int D>
 __device__ __forceinline__ void qk_chunk(const int8_t* __restrict__ klds, const v4i* qv, int lane,
@@ -67,15 +89,18 @@ __device__ __forceinline__ void qk_chunk(const int8_t* __restrict__ klds, const 
   const int h2 = lane >> 5, r32 = lane & 31;
   const int key0 = a_row_key(r32, 0), key1 = a_row_key(r32, 1);
   const int sw0 = k_swz<D>(key0), sw1 = k_swz<D>(key1);
-  s0 = v16i{0};
-  s1 = v16i{0};
 #pragma unroll
   for (int ks = 0; ks < D / 32; ++ks) {
     const int g = 2 * ks + h2;
     const v4i a0 = *reinterpret_cast<const v4i*>(klds + key0 * D + ((g ^ sw0) << 4));
     const v4i a1 = *reinterpret_cast<const v4i*>(klds + key1 * D + ((g ^ sw1) << 4));
-    s0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, qv[ks], s0, 0, 0, 0);
-    s1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, qv[ks], s1, 0, 0, 0);
+    if (ks == 0) {
+      s0 = mfma_i8_biased(a0, qv[0]);
+      s1 = mfma_i8_biased(a1, qv[0]);
+    } else {
+      s0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, qv[ks], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, qv[ks], s1, 0, 0, 0);
+    }
   }
 }
 
@@ -210,16 +235,20 @@ struct WaveState {
       const auto sw = __builtin_amdgcn_permlane32_swap(mx, mx, false, false);
       mx = max(static_cast<int>(sw[0]), static_cast<int>(sw[1]));
     }
-    const float tm = static_cast<float>(mx) * c;
+    const float tm = static_cast<float>(mx - SBIAS) * c;
     const bool upd = has && (tm > m + TAU);
     const float alpha = upd ? __builtin_amdgcn_exp2f(m - tm) : 1.0f;
     m = upd ? tm : m;
     const float nmref = -(m - static_cast<float>(SHIFT));
+    const float c2 = c * 67108864.0f;                                  // c 2^26, exact
+    const float kx = __builtin_fmaf(-__builtin_bit_cast(float, SBIAS), c2, nmref);
     float p0[16], p1[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      p0[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(static_cast<float>(s0[i]), c, nmref));
-      p1[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(static_cast<float>(s1[i]), c, nmref));
+      // (copy the element out first: a bit cast of a vector subscript reads element 0)
+      const int b0 = s0[i], b1 = s1[i];
+      p0[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(__builtin_bit_cast(float, b0), c2, kx));
+      p1[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(__builtin_bit_cast(float, b1), c2, kx));
     }
     if (masked) {  // the sentinel marks the invisible keys: exactly p = 0 there
       asm volatile("");
@@ -675,8 +704,8 @@ __global__ __launch_bounds__(64) void debug_scores_kernel(AttnArgs A, DebugTiles
   int32_t* o = out + static_cast<int64_t>(blockIdx.x) * 32 * 64 + r32 * 64 + 16 * h2;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    o[i] = s0[i];
-    o[32 + i] = s1[i];
+    o[i] = s0[i] - SBIAS;
+    o[32 + i] = s1[i] - SBIAS;
   }
 }
 

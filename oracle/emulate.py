@@ -18,8 +18,17 @@ chunks of BK = 64 (chunk t = keys [64t, 64t+64)), in ascending order:
   4. lazy running max: if tm > fp32(m + TAU) the row adopts m' = tm and
      rescales its state by alpha = exp2(fp32(m - m')) (0 when m = -inf);
      otherwise m, l and acc are kept as they are.
-  5. x[i,j]   = fp32(S[i,j] * c_t - fp32(m - s))  with ONE rounding (an FMA),
-     s = 4 in FP8 mode, 0 in 16-bit mode;  p = fp32(2^x), 0 if not visible.
+  5. x[i,j]   = S[i,j] * c_t - mref, mref = fp32(m - s) (s = 4 in FP8 mode,
+     0 in 16-bit mode), evaluated on the score as the float32
+     F = F0 + S * 2^-26, where F0 is the float32 with bits 0x3E22F983 (the
+     constant 1/(2 pi)); F is exact (its bits are those of F0 plus S) for
+     |S| < 2292099.  With c2 = c_t * 2^26 (exact):
+        K = fp32(-F0 * c2 - mref)   (one FMA, per row and chunk)
+        x = fp32(F * c2 + K)        (one FMA)
+     so x is S c_t - mref up to K's rounding (half an ulp of
+     |K| <= 1.07e7 c_t + |mref|: about 0.64 c_t, under one integer step of
+     S, when the first term dominates) and x's own;  p = fp32(2^x), 0 if not
+     visible.
   6. p~       = p rounded to the P.V operand type: e4m3fn in FP8 mode (where
      p already carries the 2^s pre-scale), else the input's fp16/bf16
   7. l       += sum_j p~                     (the rounded operand itself)
@@ -87,6 +96,28 @@ def _run_rows(S_full, c_row, dk_bh, vis_end, Vhat_bh, chunk_lo, chunk_hi,
     return m, l, acc
 
 
+F0 = np.array(0x3E22F983, dtype=np.uint32).view(np.float32)  # 1/(2 pi) as float32
+S_BIAS_LIMIT = 2292099   # |S| below this keeps F0 + S 2^-26 in F0's binade
+
+
+def score_as_float(S):
+    """The float32 F0 + S 2^-26 (exact: bits(F) = bits(F0) + S) for integer
+    scores |S| < 2292099."""
+    S = np.asarray(S, dtype=np.float64)
+    if np.any(np.abs(S) >= S_BIAS_LIMIT):
+        raise ValueError("score outside the biased-float range")
+    return (np.float64(F0) + S * 2.0 ** -26).astype(_F32)
+
+
+def scaled_logit(S, c_t, mref):
+    """Step 5: x = S c_t - mref as two float32 FMAs on F = F0 + S 2^-26 (rows of
+    S pair with entries of c_t and mref)."""
+    F = score_as_float(S)
+    c2 = (np.asarray(c_t, _F32) * _F32(2.0 ** 26)).astype(_F32)      # exact
+    K = fma_f32(np.broadcast_to(-F0, c2.shape), c2, -np.asarray(mref, _F32))
+    return fma_f32(F, np.broadcast_to(c2[:, None], F.shape), np.broadcast_to(K[:, None], F.shape))
+
+
 def _chunk_step(S, c_t, vis, m, l, acc, Vc, pv_mode, p_dtype):
     """Steps 3-8 for one chunk; c_t is per row (rows may span Q blocks)."""
     shift = PSHIFT_FP8 if pv_mode == PV_FP8 else PSHIFT_16
@@ -104,8 +135,7 @@ def _chunk_step(S, c_t, vis, m, l, acc, Vc, pv_mode, p_dtype):
     acc = acc * alpha[:, None]
     # a row still at m = -inf has no visible key in this chunk; its p is 0
     mref = np.where(np.isneginf(m), _F32(0.0), (m - _F32(shift)).astype(_F32)).astype(_F32)
-    x = fma_f32(S, np.broadcast_to(c_t[:, None], S.shape),
-                np.broadcast_to(-mref[:, None], S.shape))
+    x = scaled_logit(S, c_t, mref)
     p = np.exp2(x.astype(np.float64)).astype(_F32)
     p = np.where(vis, p, _F32(0.0))
     if pv_mode == PV_FP8:

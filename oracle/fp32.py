@@ -3,8 +3,9 @@
 numpy's float32 add, subtract, multiply and divide are IEEE binary32 with
 round-to-nearest-even, so the oracle uses them directly.  The one operation
 numpy lacks is a fused multiply-add with a single rounding; ``fma_f32``
-provides it for the case the scheme needs, where the product is exact in
-float64.
+provides it: the product of two float32 values is exact in float64 (24 + 24
+significant bits, exponents well inside float64's range), so an error-free
+sum and one correction give the correctly rounded float32 result.
 """
 
 import numpy as np
@@ -23,8 +24,8 @@ def _twosum(a, b):
 def fma_f32(a, b, c):
     """fp32(a*b + c) with one rounding (RNE), for float32 operands.
 
-    Precondition: a*b is exact in float64, which holds when ``a`` holds
-    integers with |a| < 2^29 and ``b`` is float32 (24 + 29 <= 53 bits).
+    Precondition: every operand is exactly a float32 value (integers
+    |a| < 2^24 included); then a*b is exact in float64.
 
     Method: p = a*b exactly; s + err = p + c exactly (two-sum).  Rounding s
     to float32 gives the correctly rounded result unless s lies exactly on a
@@ -32,13 +33,14 @@ def fma_f32(a, b, c):
     (s - midpoint) + err -- exact in sign because s - midpoint is exact
     (Sterbenz) -- then decides the direction.
     """
-    a = np.asarray(a, dtype=np.float32)
-    b = np.asarray(b, dtype=np.float32)
-    c = np.asarray(c, dtype=np.float32)
-    ai = a.astype(np.float64)
-    if np.any(np.abs(ai) >= 2.0 ** 29) or np.any(ai != np.round(ai)):
-        raise ValueError("fma_f32: first operand must be integer-valued, |a| < 2^29")
-    p = ai * b.astype(np.float64)
+    a0, b0, c0 = (np.asarray(t) for t in (a, b, c))
+    a = a0.astype(np.float32)
+    b = b0.astype(np.float32)
+    c = c0.astype(np.float32)
+    for t0, t in ((a0, a), (b0, b), (c0, c)):
+        if np.any(t0.astype(np.float64) != t.astype(np.float64)):
+            raise ValueError("fma_f32: operands must be float32 values")
+    p = a.astype(np.float64) * b.astype(np.float64)
     s, err = _twosum(p, c.astype(np.float64))
     r = s.astype(np.float32)
     r64 = r.astype(np.float64)
