@@ -6,11 +6,15 @@ One step = one sage_attn_fwd call: the quantize pass (K mean, channel balance,
 INT8 Q/K codes and scales, V layout) plus the fused attention kernel, over the
 workload's whole batch, with the inputs already resident in HBM.  Prints ONE
 JSON line: TOPS = 4*d*(visible query-key pairs) / time, the roofline of the
-dominant kernel (the fused attention, timed with HIP events on its own stream)
-and the CPU oracle timed on a bounded sample of the same workload.
+dominant kernel (the fused attention, timed with HIP events on its own stream;
+its HBM traffic from the committed rocprofv3 counters when they were taken on
+the same kernel source, else null), the CPU oracle timed on a bounded sample
+of the same workload, and the other P.V mode timed the same way with its own
+accuracy on a small sample.
 """
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -39,7 +43,57 @@ def parse():
     p.add_argument("--profile", action="store_true", help="few steps, no CPU leg (for rocprofv3)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run one plain 256 MiB device copy (reference for HBM byte counters)")
+    p.add_argument("--single-mode", action="store_true", help="do not time the other P.V mode")
     return p.parse_args()
+
+
+def kernel_traffic(workload, pv):
+    """HBM bytes per launch of the fused kernel from profiles/traffic.json (FETCH_SIZE and
+    WRITE_SIZE scaled by the plain-copy factors), only if those counters were taken on
+    the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    t = json.load(open(path))
+    h = hashlib.sha256()
+    for f in t["source_files"]:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if h.hexdigest() != t["source_sha256"]:
+        return None
+    rec = t["launches"].get(f"{workload}/{pv}")
+    return None if rec is None else rec["bytes"]
+
+
+def time_path(sage, torch, desc, q, k, v, o, bufs, stream, steps, warm):
+    """Warm up, then time `steps` whole steps (quantize + fused kernel) with HIP
+    events on the launch stream around each part.  Returns ms per step, per
+    quantize pass and per fused-kernel launch."""
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+
+    def step(i=None):
+        if i is not None:
+            ev[i][0].record(stream)
+        sage.sage_attn_quantize(desc, q, k, v, bufs, stream)
+        if i is not None:
+            ev[i][1].record(stream)
+        sage.sage_attn_fwd_quantized(desc, bufs, o, stream)
+        if i is not None:
+            ev[i][2].record(stream)
+
+    for _ in range(warm):
+        step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        step(i)
+    end.record(stream)
+    end.synchronize()
+    ms_step = start.elapsed_time(end) / steps
+    ms_quant = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    ms_attn = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    return ms_step, ms_quant, ms_attn
 
 
 def main():
@@ -62,26 +116,15 @@ def main():
     x = workloads.make(w, dev)
     q, k, v = x["q"], x["k"], x["v"]
     o = torch.empty_like(q)
-    desc = sage.Desc.for_tensors(q, k, v, o, pv_mode=w.pv_mode, frame_len=w.frame_len,
-                                 kv_len=w.kv_len, q_pos0=w.q_pos0)
-    ws = sage.new_workspace(desc, dev)
-    bufs = sage.sage_attn_quant_layout(desc, ws)
     stream = torch.cuda.current_stream()
     steps = 2 if args.profile else args.steps
     warm = 1 if args.profile else args.warmup
-    # one step = the whole path (same work as sage_attn_fwd), with HIP events on
-    # the launch stream around each of its two parts
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
 
-    def step(i=None):
-        if i is not None:
-            ev[i][0].record(stream)
-        sage.sage_attn_quantize(desc, q, k, v, bufs, stream)
-        if i is not None:
-            ev[i][1].record(stream)
-        sage.sage_attn_fwd_quantized(desc, bufs, o, stream)
-        if i is not None:
-            ev[i][2].record(stream)
+    def setup(pv_mode):
+        desc = sage.Desc.for_tensors(q, k, v, o, pv_mode=pv_mode, frame_len=w.frame_len,
+                                     kv_len=w.kv_len, q_pos0=w.q_pos0)
+        ws = sage.new_workspace(desc, dev)
+        return desc, ws, sage.sage_attn_quant_layout(desc, ws)
 
     if args.calibrate_copy:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
@@ -89,24 +132,27 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    for _ in range(warm):
-        step()
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for i in range(steps):
-        step(i)
-    end.record(stream)
-    end.synchronize()
-    ms_step = start.elapsed_time(end) / steps
-    ms_quant = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
-    ms_attn = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
     ops = w.ops()
+    other = None
+    if not (args.profile or args.single_mode):
+        # the other P.V mode first, so that the headline mode's output stays in `o`
+        desc2, ws2, bufs2 = setup(1 - w.pv_mode)
+        t2 = time_path(sage, torch, desc2, q, k, v, o, bufs2, stream, steps, warm)
+        other = {"pv": "fp8" if w.pv_mode == 0 else "16",
+                 "value": round(ops / (t2[0] * 1e-3) / 1e12, 2),
+                 "attn_tops": round(ops / (t2[2] * 1e-3) / 1e12, 2),
+                 "ms_per_step": round(t2[0], 4)}
+        if not args.no_cpu:
+            other["accuracy"] = accuracy_sample(w, x, o, desc2, 1 - w.pv_mode, sage)
+        del ws2, bufs2
+    desc, ws, bufs = setup(w.pv_mode)
+    ms_step, ms_quant, ms_attn = time_path(sage, torch, desc, q, k, v, o, bufs, stream, steps, warm)
     tops = ops / (ms_step * 1e-3) / 1e12
 
     splits = sage.sage_attn_kv_splits(desc)
     attn_tops = ops / (ms_attn * 1e-3) / 1e12
+    pvname = "fp8" if w.pv_mode == 1 else "16"
+    traffic = kernel_traffic(w.name, pvname)
     # quantize pass algorithmic bytes: read Q, K twice (statistics, then codes),
     # V once; write Q/K codes, V layout (16-bit or e4m3) and scales
     esz = 2
@@ -128,19 +174,44 @@ def main():
         "dtype": "int8+fp8" if w.pv_mode == 1 else ("int8+" + w.dtype),
         "data": "synthetic (seeded Gaussian, video-DiT token grid)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nkv": w.Nkv, "d": w.d,
-                   "in_dtype": w.dtype, "pv": "fp8" if w.pv_mode == 1 else "16",
+                   "in_dtype": w.dtype, "pv": pvname,
                    "frame_len": w.frame_len, "kv_splits": splits,
                    "ops_per_step": ops, "pct_int8_peak": round(100 * tops / INT8_PEAK_TOPS, 2)},
         "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel", "achieved": round(attn_tops, 2),
                      "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s", "frac": round(attn_tops / INT8_PEAK_TOPS, 4),
-                     "traffic": None, "ms_per_launch": round(ms_attn, 4)},
+                     "traffic": traffic, "ms_per_launch": round(ms_attn, 4)},
         "quantize": {"ms": round(ms_quant, 4), "algorithmic_bytes": qbytes,
                      "GB_per_s": round(qbytes / (ms_quant * 1e-3) / 1e9, 1),
                      "hbm_frac": round(qbytes / (ms_quant * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
     }
+    if other is not None:
+        record["other_pv_mode"] = other
     if not args.no_cpu and not args.profile:
         record["cpu_baseline"], record["parity"] = cpu_leg(w, x, o, desc, args, sage, torch)
     print(json.dumps(record), flush=True)
+
+
+def accuracy_sample(w, x, o, desc, pv_mode, sage, heads=2, rows=256):
+    """Cosine against float64 attention and max-abs against the emulation on a
+    small sample (the first `heads` heads of batch 0, `rows` seeded rows)."""
+    from oracle import emulate, attention
+    import workloads
+    hs = list(range(min(heads, w.H)))
+    r = workloads.sample_rows(w, rows)
+    S = sage.sage_attn_kv_splits(desc)
+    Q = x["q"][0:1, hs].float().cpu().numpy()
+    K = x["k"][0:1, hs].float().cpu().numpy()
+    V = x["v"][0:1, hs].float().cpu().numpy()
+    kv, qp = [w.kv_lens()[0]], [w.q_pos0s()[0]]
+    n = -(-kv[0] // 64)
+    splits = [(s * n // S, (s + 1) * n // S) for s in range(S)] if S > 1 else None
+    o64, _ = emulate.emulate_from_inputs(Q, K, V, pv_mode, w.dtype, frame_len=w.frame_len, kv_len=kv,
+                                         q_pos0=qp, rows=r, splits=splits)
+    ref = attention.attention_fp64(Q, K, V, frame_len=w.frame_len, kv_len=kv, q_pos0=qp, rows=r)
+    og = o[0:1, hs][:, :, r].float().cpu().numpy()
+    cos = float((og * ref).sum() / np.sqrt((og ** 2).sum() * (ref ** 2).sum()))
+    return {"rows": len(r) * len(hs), "max_abs_vs_emulation": float(np.abs(og - o64).max()),
+            "cosine_vs_fp64": round(cos, 6)}
 
 
 def cpu_leg(w, x, o, desc, args, sage, torch):
