@@ -16,6 +16,15 @@ frame-block-causal mask: with frame length F > 0, query token i (absolute
 position q_pos0[b] + i) sees key j iff j < kv_len[b] and
 floor(j / F) <= floor((q_pos0[b] + i) / F) -- every earlier frame and all of
 its own frame.  F = 0 means full (non-causal) attention over kv_len[b] keys.
+
+Sliding window with sinks.  Streaming decoding keeps attention to a window of
+fixed length: a persistent reference context computed once (the analogue of
+sink tokens / sink frames), the history frames cached inside the window, and
+the frame being denoised (Vidu S1 blog, section "Infra").  Reading taken
+here, with S sink frames and W window frames: key frame fk is visible from
+query frame fq iff fk <= fq and (W == 0 or fk < S or fk >= fq - W), i.e. the
+first S frames, the W most recent history frames and the current frame;
+W == 0 keeps every earlier frame (the plain frame-block-causal mask).
 """
 
 import numpy as np
@@ -34,14 +43,27 @@ def row_end(i_rows, kv_len_b, q_pos0_b, frame_len):
     return np.minimum(int(kv_len_b), (f + 1) * int(frame_len))
 
 
-def visible(i_rows, Nkv, kv_len_b, q_pos0_b, frame_len):
-    """Boolean [len(i_rows), Nkv]: the mask of the frame-block-causal rule."""
+def frame_visible(fk, fq, sink_frames=0, window_frames=0):
+    """Key frame fk visible from query frame fq (broadcasting arrays)."""
+    fk = np.asarray(fk, dtype=np.int64)
+    fq = np.asarray(fq, dtype=np.int64)
+    ok = fk <= fq
+    if window_frames:
+        ok = ok & ((fk < int(sink_frames)) | (fk >= fq - int(window_frames)))
+    return ok
+
+
+def visible(i_rows, Nkv, kv_len_b, q_pos0_b, frame_len, sink_frames=0, window_frames=0):
+    """Boolean [len(i_rows), Nkv]: the mask (frame-block-causal, optionally
+    restricted to sink + window frames)."""
     i = np.asarray(i_rows, dtype=np.int64)
     j = np.arange(Nkv, dtype=np.int64)
     vis = np.broadcast_to(j[None, :] < int(kv_len_b), (i.shape[0], Nkv)).copy()
     if frame_len:
         fq = (int(q_pos0_b) + i) // int(frame_len)
-        vis = vis & ((j[None, :] // int(frame_len)) <= fq[:, None])
+        vis = vis & frame_visible(j[None, :] // int(frame_len), fq[:, None], sink_frames, window_frames)
+    elif window_frames:
+        raise ValueError("a window needs frames")
     return vis
 
 
@@ -54,11 +76,12 @@ def default_q_pos0(Nq, kv_len, frame_len):
 
 
 def attention_fp64(Q, K, V, sm_scale=None, frame_len=0, kv_len=None,
-                   q_pos0=None, rows=None):
+                   q_pos0=None, rows=None, sink_frames=0, window_frames=0):
     """softmax(Q K^T * sm_scale + M) V in float64 for the selected rows.
 
-    Q [B,H,Nq,d], K and V [B,H,Nkv,d] (any float dtype; widened exactly).
-    rows: indices of the query rows to compute (all when None).
+    Q [B,H,Nq,d], K and V [B,H,Nkv,d] (any float dtype; widened exactly),
+    tokens contiguous.  rows: indices of the query rows to compute (all when
+    None).
     Returns float64 [B,H,len(rows),d].
     """
     Q = np.asarray(Q, dtype=np.float64)
@@ -72,7 +95,7 @@ def attention_fp64(Q, K, V, sm_scale=None, frame_len=0, kv_len=None,
     rows = np.arange(Nq) if rows is None else np.asarray(rows, dtype=np.int64)
     out = np.empty((B, H, len(rows), d), dtype=np.float64)
     for b in range(B):
-        vis = visible(rows, Nkv, kv[b], qp[b], frame_len)
+        vis = visible(rows, Nkv, kv[b], qp[b], frame_len, sink_frames, window_frames)
         for h in range(H):
             s = (Q[b, h, rows, :] @ K[b, h].T) * scale
             s = np.where(vis, s, -np.inf)

@@ -72,8 +72,11 @@ def _run_rows(S_full, c_row, dk_bh, vis_end, Vhat_bh, chunk_lo, chunk_hi,
               pv_mode, p_dtype, trace=None):
     """Steps 1-8 over chunks [chunk_lo, chunk_hi) for a set of rows.
 
+    vis_end: per row, the exclusive end of its visible key prefix; or a
+    boolean [R, keys] visibility matrix.
     trace: optional list; receives the running max m after every chunk.
     """
+    vis_end = np.asarray(vis_end)
     R = S_full.shape[0]
     d = Vhat_bh.shape[1]
     m = np.full(R, -np.inf, dtype=_F32)
@@ -85,7 +88,7 @@ def _run_rows(S_full, c_row, dk_bh, vis_end, Vhat_bh, chunk_lo, chunk_hi,
         if j0 >= j1:
             break
         j = np.arange(j0, j1)
-        vis = j[None, :] < vis_end[:, None]
+        vis = vis_end[:, j0:j1] if vis_end.ndim == 2 else j[None, :] < vis_end[:, None]
         if not vis.any():
             continue
         c_t = (c_row * _F32(dk_bh[t])).astype(_F32)          # [R] fp32
@@ -147,9 +150,23 @@ def _chunk_step(S, c_t, vis, m, l, acc, Vc, pv_mode, p_dtype):
     return m, l, acc
 
 
+def visible_slots(rows, n_slots, kv_len_b, q_pos0_b, frame_len, frame_stride,
+                  sink_frames=0, window_frames=0):
+    """Visibility [R, n_slots] of cache slots (frames of frame_len tokens at a
+    stride of frame_stride slots) under the mask of ``attention.visible``;
+    padding slots are never visible."""
+    from .attention import frame_visible
+    slot = np.arange(n_slots, dtype=np.int64)
+    fk, r = slot // frame_stride, slot % frame_stride
+    valid = (r < frame_len) & (fk * frame_len + r < int(kv_len_b))
+    fq = (int(q_pos0_b) + np.asarray(rows, dtype=np.int64)) // frame_len
+    return valid[None, :] & frame_visible(fk[None, :], fq[:, None], sink_frames, window_frames)
+
+
 def sage_attention_emulated(qcodes, dq, kcodes, dk, Vhat, pv_mode, dtype,
                             sm_scale=None, frame_len=0, kv_len=None,
-                            q_pos0=None, rows=None, splits=None):
+                            q_pos0=None, rows=None, splits=None,
+                            frame_stride=0, sink_frames=0, window_frames=0):
     """Emulate the quantized attention for the selected query rows.
 
     qcodes int8 [B,H,Nq,d], dq float32 [B,H,ceil(Nq/128)];
@@ -158,6 +175,10 @@ def sage_attention_emulated(qcodes, dq, kcodes, dk, Vhat, pv_mode, dtype,
     mode) or dequant_v_fp8(...) (FP8 mode);  dtype: 'bf16' | 'f16' (input and
     output type, and P's type in 16-bit mode).
     splits: optional list of (chunk_lo, chunk_hi) ranges covering the keys.
+    frame_stride > 0: K/V operands are a frame cache (``quant.quantize_k_frames``
+    layout: frame f's tokens at slots f*frame_stride + [0, frame_len)); kv_len and
+    q_pos0 stay in tokens; sink_frames / window_frames restrict the visible
+    frames as in ``attention.visible``.
     Returns (O64 float64 [B,H,R,d], O rounded to dtype as float32).
     """
     qcodes = np.asarray(qcodes)
@@ -172,9 +193,18 @@ def sage_attention_emulated(qcodes, dq, kcodes, dk, Vhat, pv_mode, dtype,
     if splits is None:
         splits = [(0, nchunks)]
     out = np.empty((B, H, len(rows), d), dtype=np.float64)
+    if window_frames and not frame_stride:
+        raise ValueError("sink/window frames need the frame cache layout")
     for b in range(B):
-        vis_end = row_end(rows, kv[b], qp[b], frame_len)
-        jmax = int(vis_end.max())
+        if frame_stride:
+            vis_end = visible_slots(rows, Nkv, kv[b], qp[b], frame_len, frame_stride,
+                                    sink_frames, window_frames)
+            last = np.nonzero(vis_end.any(axis=0))[0]
+            jmax = int(last.max()) + 1 if last.size else 0
+            vis_end = vis_end[:, :jmax]
+        else:
+            vis_end = row_end(rows, kv[b], qp[b], frame_len)
+            jmax = int(vis_end.max())
         for h in range(H):
             qs = (dq[b, h, rows // BQ].astype(_F32) * sigma).astype(_F32)   # [R]
             S_full = qcodes[b, h, rows, :].astype(np.float64) @ \
@@ -206,15 +236,31 @@ def scores_int(qcodes, kcodes):
 
 def emulate_from_inputs(Q, K, V, pv_mode, dtype, sm_scale=None, frame_len=0,
                         kv_len=None, q_pos0=None, rows=None, splits=None,
-                        mu=None):
-    """Quantize the 16-bit inputs with ``quant`` and run the emulation."""
+                        mu=None, shift=None, frame_stride=0, sink_frames=0,
+                        window_frames=0):
+    """Quantize the 16-bit inputs with ``quant`` and run the emulation.
+
+    frame_stride > 0: K and V (tokens of whole frames from frame 0) go into a
+    frame cache, each frame quantized once against the given (frozen) mu and
+    shift (both required then)."""
     from . import quant
     Qf = np.asarray(Q, dtype=np.float32)
     Kf = np.asarray(K, dtype=np.float32)
     Vf = np.asarray(V, dtype=np.float32)
+    if frame_stride:
+        qc, dq = quant.quantize_q(Qf, shift)
+        kc, dk = quant.quantize_k_frames(Kf, mu, shift, frame_len, frame_stride)
+        if pv_mode == PV_FP8:
+            vc, ve = quant.quantize_v_fp8_frames(Vf, frame_len, frame_stride)
+            Vhat = quant.dequant_v_fp8(vc, ve)
+        else:
+            Vhat = quant.to_frame_slots(Vf, frame_len, frame_stride).astype(np.float64)
+        return sage_attention_emulated(qc, dq, kc, dk, Vhat, pv_mode, dtype, sm_scale,
+                                       frame_len, kv_len, q_pos0, rows, splits,
+                                       frame_stride, sink_frames, window_frames)
     if mu is None:
         mu = quant.k_mean(Kf, kv_len)
-    a = quant.channel_shift(Qf, Kf, mu, kv_len)
+    a = quant.channel_shift(Qf, Kf, mu, kv_len) if shift is None else shift
     qc, dq = quant.quantize_q(Qf, a)
     kc, dk = quant.quantize_k(Kf, mu, kv_len, a)
     if pv_mode == PV_FP8:

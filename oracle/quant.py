@@ -193,3 +193,67 @@ def dequant_v_fp8(codes, exps):
     B, H, Nkv, d = codes.shape
     e = np.repeat(np.asarray(exps), VB, axis=2)[:, :, :Nkv, :]
     return np.ldexp(codecs.e4m3_decode(codes), e)
+
+
+# ---------------------------------------------------------------------------
+# KV cache of whole frames.  Streaming decoding caches the history frames and
+# reuses them step after step (Vidu S1 blog, section "Infra"), so each frame is
+# quantized once, when it enters the cache, against a frozen K mean and
+# channel shift.  Frame f's F tokens occupy slots [f*FS, f*FS + F) of the
+# cache, FS >= F a multiple of BK; slots [f*FS + F, (f+1)*FS) are padding
+# (codes 0, never visible).  Every K block (BK slots) and V block (VB slots)
+# therefore lies inside one frame, and quantizing a frame never touches
+# another frame's codes.
+
+def frame_slot(t, frame_len, frame_stride):
+    """Cache slot of token t."""
+    t = np.asarray(t, dtype=np.int64)
+    return (t // frame_len) * frame_stride + t % frame_len
+
+
+def _frames_of(X, frame_len):
+    n = np.shape(X)[2]
+    return [(f, f * frame_len, min((f + 1) * frame_len, n)) for f in range(-(-n // frame_len))]
+
+
+def quantize_k_frames(K, mu, shift, frame_len, frame_stride, n_slots=None):
+    """K [B,H,Ntok,d] (tokens of consecutive frames from frame 0) -> codes int8
+    [B,H,n_slots,d] and scales float32 [B,H,n_slots/BK], each frame quantized
+    as its own sequence (quantize_k with the given frozen mu and shift)."""
+    B, H, n, d = np.shape(K)
+    if frame_stride % BK or frame_stride < frame_len:
+        raise ValueError("frame stride must be a multiple of BK and >= the frame length")
+    n_slots = n_slots or -(-n // frame_len) * frame_stride
+    codes = np.zeros((B, H, n_slots, d), dtype=np.int8)
+    dk = np.zeros((B, H, n_slots // BK), dtype=np.float32)
+    for f, lo, hi in _frames_of(K, frame_len):
+        c, dl = quantize_k(np.asarray(K)[:, :, lo:hi], mu, None, shift)
+        s0 = f * frame_stride
+        codes[:, :, s0:s0 + hi - lo] = c
+        dk[:, :, s0 // BK:s0 // BK + dl.shape[2]] = dl
+    return codes, dk
+
+
+def quantize_v_fp8_frames(V, frame_len, frame_stride, n_slots=None):
+    """quantize_v_fp8 per frame into cache slots: codes uint8 [B,H,n_slots,d],
+    exponents int64 [B,H,n_slots/VB,d]."""
+    B, H, n, d = np.shape(V)
+    n_slots = n_slots or -(-n // frame_len) * frame_stride
+    codes = np.zeros((B, H, n_slots, d), dtype=np.uint8)
+    exps = np.zeros((B, H, n_slots // VB, d), dtype=np.int64)
+    for f, lo, hi in _frames_of(V, frame_len):
+        c, e, _ = quantize_v_fp8(np.asarray(V)[:, :, lo:hi])
+        s0 = f * frame_stride
+        codes[:, :, s0:s0 + hi - lo] = c
+        exps[:, :, s0 // VB:s0 // VB + e.shape[2]] = e
+    return codes, exps
+
+
+def to_frame_slots(X, frame_len, frame_stride, n_slots=None):
+    """Place tokens [B,H,Ntok,...] into cache slots (padding zero)."""
+    X = np.asarray(X)
+    B, H, n = X.shape[:3]
+    n_slots = n_slots or -(-n // frame_len) * frame_stride
+    out = np.zeros((B, H, n_slots) + X.shape[3:], dtype=X.dtype)
+    out[:, :, frame_slot(np.arange(n), frame_len, frame_stride)] = X
+    return out
