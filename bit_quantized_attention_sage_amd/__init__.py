@@ -19,7 +19,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsage_attn.so")
 
-SAGE_ATTN_ABI_VERSION = 1
+SAGE_ATTN_ABI_VERSION = 2
 SAGE_F16, SAGE_BF16 = 0, 1
 SAGE_PV_16, SAGE_PV_FP8 = 0, 1
 SAGE_FLAG_DEBUG_SYNC = 0x1
@@ -38,7 +38,9 @@ class sage_attn_desc(ctypes.Structure):
                 ("kv_splits", ctypes.c_int32), ("sm_scale", ctypes.c_float), ("flags", ctypes.c_uint32),
                 ("q_stride", _i64x3), ("k_stride", _i64x3), ("v_stride", _i64x3), ("o_stride", _i64x3),
                 ("kv_len", ctypes.POINTER(ctypes.c_int32)), ("q_pos0", ctypes.POINTER(ctypes.c_int32)),
-                ("k_mean_in", ctypes.c_void_p)]
+                ("k_mean_in", ctypes.c_void_p), ("frame_stride", ctypes.c_int32),
+                ("sink_frames", ctypes.c_int32), ("window_frames", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("chan_shift_in", ctypes.c_void_p)]
 
 
 class sage_quant_bufs(ctypes.Structure):
@@ -79,6 +81,8 @@ def load(path=None):
         "sage_attn_quant_layout": (ctypes.c_int, [_DESC_P, ctypes.c_void_p, ctypes.c_size_t, _BUFS_P]),
         "sage_attn_quantize": (ctypes.c_int, [_DESC_P, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                               _BUFS_P, ctypes.c_void_p]),
+        "sage_attn_quantize_frames": (ctypes.c_int, [_DESC_P, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                                     ctypes.c_int32, ctypes.c_int32, _BUFS_P, ctypes.c_void_p]),
         "sage_attn_fwd_quantized": (ctypes.c_int, [_DESC_P, _BUFS_P, ctypes.c_void_p, ctypes.c_void_p]),
         "sage_attn_fwd": (ctypes.c_int, [_DESC_P, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
@@ -113,7 +117,8 @@ class Desc:
 
     def __init__(self, B, H, Nq, Nkv, d, dtype, pv_mode=SAGE_PV_16, frame_len=0, kv_len=None,
                  q_pos0=None, sm_scale=0.0, kv_splits=0, flags=0, k_mean_in=None,
-                 q_stride=None, k_stride=None, v_stride=None, o_stride=None):
+                 q_stride=None, k_stride=None, v_stride=None, o_stride=None,
+                 frame_stride=0, sink_frames=0, window_frames=0, chan_shift_in=None):
         c = sage_attn_desc()
         c.abi_version = SAGE_ATTN_ABI_VERSION
         c.dtype = dtype
@@ -133,7 +138,11 @@ class Desc:
         c.q_pos0 = ctypes.cast(self._qp, ctypes.POINTER(ctypes.c_int32)) if self._qp else None
         self._k_mean_in = k_mean_in
         c.k_mean_in = k_mean_in.data_ptr() if k_mean_in is not None else None
+        c.frame_stride, c.sink_frames, c.window_frames, c.reserved = frame_stride, sink_frames, window_frames, 0
+        self._chan_shift_in = chan_shift_in
+        c.chan_shift_in = chan_shift_in.data_ptr() if chan_shift_in is not None else None
         self.c = c
+        self.frame_stride, self.sink_frames, self.window_frames = frame_stride, sink_frames, window_frames
         self.B, self.H, self.Nq, self.Nkv, self.d = B, H, Nq, Nkv, d
         self.dtype, self.pv_mode, self.frame_len = dtype, pv_mode, frame_len
         self.Nq_pad = (Nq + 127) // 128 * 128
@@ -144,10 +153,11 @@ class Desc:
         return ctypes.byref(self.c)
 
     @classmethod
-    def for_tensors(cls, q, k, v, o=None, **kw):
-        """Describe [B,H,N,d] tensors (channel dim contiguous, any b/h/n strides)."""
+    def for_tensors(cls, q, k, v, o=None, nkv=None, **kw):
+        """Describe [B,H,N,d] tensors (channel dim contiguous, any b/h/n strides).
+        nkv: the key length Nkv when it is not k's (a frame cache: its slot count)."""
         B, H, Nq, d = q.shape
-        Nkv = k.shape[2]
+        Nkv = k.shape[2] if nkv is None else nkv
         for t in (q, k, v) + ((o,) if o is not None else ()):
             if t.stride(3) != 1:
                 raise ValueError("the channel dimension must be contiguous")
@@ -188,6 +198,16 @@ def sage_attn_quantize(desc, q, k, v, bufs, stream=None):
     _check(load().sage_attn_quantize(desc.ptr, ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
                                      ctypes.c_void_p(v.data_ptr()), ctypes.byref(bufs), _stream(stream)),
            "sage_attn_quantize")
+
+
+def sage_attn_quantize_frames(desc, q, k, v, frame0, nframes, bufs, stream=None):
+    """Quantize frames [frame0, frame0 + nframes) of new keys/values (k, v:
+    [B,H,nframes*frame_len,d], desc's k/v strides) into the frame cache, and
+    the queries q unless None, against the mean and exponents in bufs."""
+    _check(load().sage_attn_quantize_frames(desc.ptr, ctypes.c_void_p(q.data_ptr() if q is not None else None),
+                                            ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
+                                            int(frame0), int(nframes), ctypes.byref(bufs), _stream(stream)),
+           "sage_attn_quantize_frames")
 
 
 def sage_attn_fwd_quantized(desc, bufs, o, stream=None):

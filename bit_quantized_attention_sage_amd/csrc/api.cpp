@@ -26,6 +26,8 @@ int64_t pad128(int64_t n) { return (n + 127) / 128 * 128; }
 
 struct Plan {
   int B, H, Nq, Nkv, d, Nq_pad, Nkv_pad, splits, frame_len, dtype, pv_mode;
+  int frame_stride, sink_frames, window_frames;
+  uint32_t cpf_magic;
   float sigma;
   sage::BatchInfo bi;
   int order[sage::MAXB_ARGS];
@@ -60,6 +62,18 @@ int make_plan(const sage_attn_desc* d, Plan* p) {
   const int64_t bh = static_cast<int64_t>(d->B) * d->H;
   if (bh * pad128(d->Nq) / 128 * SAGE_MAX_SPLITS > 0x7FFFFFFF) return fail(SAGE_E_SHAPE, "too many work items");
   if (d->frame_len < 0) return fail(SAGE_E_MASK, "frame_len must be >= 0");
+  if (d->reserved != 0) return fail(SAGE_E_UNSUPPORTED, "reserved must be 0");
+  if (d->frame_stride < 0) return fail(SAGE_E_MASK, "frame_stride must be >= 0");
+  if (d->frame_stride != 0) {
+    if (d->frame_len <= 0) return fail(SAGE_E_MASK, "a frame cache needs frame_len > 0");
+    if (d->frame_stride % 64 != 0 || d->frame_stride < d->frame_len || d->frame_stride >= 131072)
+      return fail(SAGE_E_MASK, "frame_stride must be a multiple of 64, >= frame_len and < 131072");
+    if (d->Nkv % d->frame_stride != 0) return fail(SAGE_E_SHAPE, "Nkv must be a multiple of frame_stride");
+    if (d->Nkv >= (1 << 26)) return fail(SAGE_E_SHAPE, "a frame cache holds fewer than 2^26 slots");
+  }
+  if (d->sink_frames < 0 || d->window_frames < 0) return fail(SAGE_E_MASK, "sink_frames and window_frames must be >= 0");
+  if ((d->window_frames > 0 || d->sink_frames > 0) && d->frame_stride == 0)
+    return fail(SAGE_E_MASK, "sink/window frames need the frame cache (frame_stride > 0)");
   if (d->kv_splits < 0 || d->kv_splits > SAGE_MAX_SPLITS) return fail(SAGE_E_SHAPE, "kv_splits out of range");
   if (!(d->sm_scale >= 0.f) || isinf(d->sm_scale)) return fail(SAGE_E_SHAPE, "sm_scale must be finite and >= 0");
   const int64_t* strides[4] = {d->q_stride, d->k_stride, d->v_stride, d->o_stride};
@@ -77,12 +91,23 @@ int make_plan(const sage_attn_desc* d, Plan* p) {
   p->Nq_pad = static_cast<int>(pad128(d->Nq));
   p->Nkv_pad = static_cast<int>(pad128(d->Nkv));
   p->frame_len = d->frame_len;
+  p->frame_stride = d->frame_stride;
+  p->sink_frames = d->sink_frames;
+  p->window_frames = d->window_frames;
+  p->cpf_magic = 0;
+  if (d->frame_stride > 64) {  // one chunk per frame needs no division
+    const uint64_t cpf = static_cast<uint64_t>(d->frame_stride / 64);
+    p->cpf_magic = static_cast<uint32_t>(((uint64_t{1} << 32) + cpf - 1) / cpf);
+  }
   p->dtype = d->dtype;
   p->pv_mode = d->pv_mode;
   memset(&p->bi, 0, sizeof(p->bi));
+  const int kv_cap = d->frame_stride > 0 ? d->Nkv / d->frame_stride * d->frame_len : d->Nkv;
   for (int b = 0; b < d->B; ++b) {
-    const int kv = d->kv_len ? d->kv_len[b] : d->Nkv;
-    if (kv < 1 || kv > d->Nkv) return fail(SAGE_E_MASK, "kv_len[" + std::to_string(b) + "] must be in [1, Nkv]");
+    const int kv = d->kv_len ? d->kv_len[b] : kv_cap;
+    if (kv < 1 || kv > kv_cap)
+      return fail(SAGE_E_MASK, "kv_len[" + std::to_string(b) +
+                                   "] must be in [1, Nkv] (frame cache: tokens of Nkv/frame_stride frames)");
     int qp = 0;
     if (d->frame_len > 0) {
       qp = d->q_pos0 ? d->q_pos0[b] : kv - d->Nq;
@@ -187,6 +212,10 @@ sage::AttnLaunch attn_launch_of(const Plan& p, const sage_quant_bufs& b, void* o
   L.Nkv_pad = p.Nkv_pad;
   L.frame_len = p.frame_len;
   L.splits = p.splits;
+  L.frame_stride = p.frame_stride;
+  L.sink_frames = p.sink_frames;
+  L.window_frames = p.window_frames;
+  L.cpf_magic = p.cpf_magic;
   L.sigma = p.sigma;
   L.bi = p.bi;
   for (int i = 0; i < sage::MAXB_ARGS; ++i) L.order[i] = p.order[i];
@@ -194,6 +223,64 @@ sage::AttnLaunch attn_launch_of(const Plan& p, const sage_quant_bufs& b, void* o
   L.o = o;
   for (int i = 0; i < 3; ++i) L.os[i] = d->o_stride[i];
   return L;
+}
+
+int quantize_impl(const sage_attn_desc* desc, const void* q, const void* k, const void* v, int frames_only,
+                  int frame0, int nframes, const sage_quant_bufs* bufs, void* stream) {
+  try {
+    Plan p;
+    int s = make_plan(desc, &p);
+    if (s != SAGE_OK) return s;
+    if ((!frames_only && !q) || !k || !v) return fail(SAGE_E_NULL, "q, k and v must be non-NULL");
+    if ((q && !aligned16(q)) || !aligned16(k) || !aligned16(v))
+      return fail(SAGE_E_ALIGN, "q, k and v must be 16-byte aligned");
+    if ((s = check_bufs(bufs, p, true)) != SAGE_OK) return s;
+    if (desc->k_mean_in && (reinterpret_cast<uintptr_t>(desc->k_mean_in) & 3u))
+      return fail(SAGE_E_ALIGN, "k_mean_in must be 4-byte aligned");
+    if (frames_only) {
+      if (p.frame_stride == 0) return fail(SAGE_E_UNSUPPORTED, "sage_attn_quantize_frames needs a frame cache");
+      if (frame0 < 0 || nframes < 1 || static_cast<int64_t>(frame0) * p.frame_stride +
+                                            static_cast<int64_t>(nframes) * p.frame_stride > p.Nkv)
+        return fail(SAGE_E_SHAPE, "frames [frame0, frame0 + nframes) must lie inside the Nkv cache slots");
+    }
+    sage::QuantLaunch L{};
+    L.chan_shift_in = desc->chan_shift_in;
+    L.frame_len = p.frame_len;
+    L.frame_stride = p.frame_stride;
+    L.frames_only = frames_only;
+    L.frame0 = frame0;
+    L.nframes = nframes;
+    L.dtype = p.dtype;
+    L.pv_mode = p.pv_mode;
+    L.d = p.d;
+    L.B = p.B;
+    L.H = p.H;
+    L.Nq = p.Nq;
+    L.Nkv = p.Nkv;
+    L.Nq_pad = p.Nq_pad;
+    L.Nkv_pad = p.Nkv_pad;
+    L.q = q;
+    L.k = k;
+    L.v = v;
+    for (int i = 0; i < 3; ++i) {
+      L.qs[i] = desc->q_stride[i];
+      L.ks[i] = desc->k_stride[i];
+      L.vs[i] = desc->v_stride[i];
+    }
+    L.k_mean_in = desc->k_mean_in;
+    L.bi = p.bi;
+    L.bufs = *bufs;
+    const Layout lay = layout_of(p);
+    char* st = static_cast<char*>(bufs->stats);
+    L.stat_ksum = reinterpret_cast<double*>(st + lay.ksum);
+    L.stat_kmax = reinterpret_cast<float*>(st + lay.kmax);
+    L.stat_kmin = reinterpret_cast<float*>(st + lay.kmin);
+    L.stat_qamax = reinterpret_cast<float*>(st + lay.qamax);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    return finish(sage::launch_quantize(L, hs), desc, hs);
+  } catch (const std::exception& e) {
+    return fail(SAGE_E_HIP, e.what());
+  }
 }
 
 }  // namespace
@@ -281,47 +368,12 @@ int sage_attn_quant_layout(const sage_attn_desc* desc, void* ws, size_t ws_bytes
 
 int sage_attn_quantize(const sage_attn_desc* desc, const void* q, const void* k, const void* v,
                        const sage_quant_bufs* bufs, void* stream) {
-  try {
-    Plan p;
-    int s = make_plan(desc, &p);
-    if (s != SAGE_OK) return s;
-    if (!q || !k || !v) return fail(SAGE_E_NULL, "q, k and v must be non-NULL");
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return fail(SAGE_E_ALIGN, "q, k and v must be 16-byte aligned");
-    if ((s = check_bufs(bufs, p, true)) != SAGE_OK) return s;
-    if (desc->k_mean_in && (reinterpret_cast<uintptr_t>(desc->k_mean_in) & 3u))
-      return fail(SAGE_E_ALIGN, "k_mean_in must be 4-byte aligned");
-    sage::QuantLaunch L{};
-    L.dtype = p.dtype;
-    L.pv_mode = p.pv_mode;
-    L.d = p.d;
-    L.B = p.B;
-    L.H = p.H;
-    L.Nq = p.Nq;
-    L.Nkv = p.Nkv;
-    L.Nq_pad = p.Nq_pad;
-    L.Nkv_pad = p.Nkv_pad;
-    L.q = q;
-    L.k = k;
-    L.v = v;
-    for (int i = 0; i < 3; ++i) {
-      L.qs[i] = desc->q_stride[i];
-      L.ks[i] = desc->k_stride[i];
-      L.vs[i] = desc->v_stride[i];
-    }
-    L.k_mean_in = desc->k_mean_in;
-    L.bi = p.bi;
-    L.bufs = *bufs;
-    const Layout lay = layout_of(p);
-    char* st = static_cast<char*>(bufs->stats);
-    L.stat_ksum = reinterpret_cast<double*>(st + lay.ksum);
-    L.stat_kmax = reinterpret_cast<float*>(st + lay.kmax);
-    L.stat_kmin = reinterpret_cast<float*>(st + lay.kmin);
-    L.stat_qamax = reinterpret_cast<float*>(st + lay.qamax);
-    hipStream_t hs = static_cast<hipStream_t>(stream);
-    return finish(sage::launch_quantize(L, hs), desc, hs);
-  } catch (const std::exception& e) {
-    return fail(SAGE_E_HIP, e.what());
-  }
+  return quantize_impl(desc, q, k, v, 0, 0, 0, bufs, stream);
+}
+
+int sage_attn_quantize_frames(const sage_attn_desc* desc, const void* q, const void* k, const void* v,
+                              int32_t frame0, int32_t nframes, const sage_quant_bufs* bufs, void* stream) {
+  return quantize_impl(desc, q, k, v, 1, frame0, nframes, bufs, stream);
 }
 
 int sage_attn_fwd_quantized(const sage_attn_desc* desc, const sage_quant_bufs* bufs, void* o, void* stream) {

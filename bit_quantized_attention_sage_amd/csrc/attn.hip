@@ -40,7 +40,10 @@
 
 namespace sage {
 
-constexpr int SENTINEL = -(1 << 30);  // masked score before the row maximum
+// Masked score: the bits of float -infinity.  As an int it lies far below
+// every biased score (so it never wins the row maximum); as the float F it
+// gives x = -inf and p = exp2(x) = 0 with no select.
+constexpr int MASKED = static_cast<int>(0xFF800000u);
 
 // Score bias.  The S MFMAs start their integer accumulation from the inline
 // constant 1/(2 pi), whose float32 bits are SBIAS, so they return SBIAS + S.
@@ -140,6 +143,8 @@ struct AttnArgs {
   int B, H, Nq, Nq_pad, Nkv_pad, nqt, splits, total;
   float sigma;
   int frame_len;
+  int frame_stride, sink_frames, window_frames;  // frame cache and window (0: contiguous keys)
+  uint32_t cpf_magic;                            // ceil(2^32 / (frame_stride / 64)), 0 if that is 1
   BatchInfo bi;
   int order[MAXB_ARGS];
 };
@@ -201,16 +206,13 @@ struct WaveState {
   v4f ls;  // row sums of P as the P.V MFMAs see it (register 0; see lsum_select)
   float m;
 
-  // Masking of a boundary chunk: keys at or beyond this row's visible end
-  // `re` get the sentinel score (they then take no part in the maximum, and
-  // softmax() gives them p = 0).
-  __device__ __forceinline__ void mask(v16i& s0, v16i& s1, int kb, int re) {
-    asm volatile("");  // keep this a real branch: no if-conversion into every chunk
-    const int lim = re - kb;
+  // Masking of a boundary chunk: keys at or beyond `lim` (counted from this
+  // lane half's first key, 16*h2) get the MASKED score.
+  __device__ __forceinline__ void mask(v16i& s0, v16i& s1, int lim) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      s0[i] = (i < lim) ? s0[i] : SENTINEL;
-      s1[i] = (32 + i < lim) ? s1[i] : SENTINEL;
+      s0[i] = (i < lim) ? s0[i] : MASKED;
+      s1[i] = (32 + i < lim) ? s1[i] : MASKED;
     }
   }
 
@@ -221,8 +223,8 @@ struct WaveState {
   // alpha (1 for rows that kept m); the caller rescales O and the row sums
   // by it when any row of the wave moved.  The row sums of the rounded P are
   // taken on the matrix cores in pv().
-  __device__ __forceinline__ float softmax(const v16i& s0, const v16i& s1, float c, bool has, bool masked,
-                                           PTile<PV>& P) {
+  // `has`: this row has a visible key in the chunk (rows without one keep m).
+  __device__ __forceinline__ float softmax(const v16i& s0, const v16i& s1, float c, bool has, PTile<PV>& P) {
     // two v_max3 chains of 8 over the lane's 32 scores
     int ma = max3_i32(s0[0], s0[1], s0[2]), mb = max3_i32(s1[0], s1[1], s1[2]);
 #pragma unroll
@@ -240,7 +242,9 @@ struct WaveState {
     const float alpha = upd ? __builtin_amdgcn_exp2f(m - tm) : 1.0f;
     m = upd ? tm : m;
     const float nmref = -(m - static_cast<float>(SHIFT));
-    const float c2 = c * 67108864.0f;                                  // c 2^26, exact
+    // c 2^26, exact; a zero scale (all-zero Q or K block: every score 0)
+    // becomes the smallest normal float so that MASKED keys still give -inf
+    const float c2 = fmaxf(c, 1.17549435e-38f) * 67108864.0f;
     const float kx = __builtin_fmaf(-__builtin_bit_cast(float, SBIAS), c2, nmref);
     float p0[16], p1[16];
 #pragma unroll
@@ -249,14 +253,6 @@ struct WaveState {
       const int b0 = s0[i], b1 = s1[i];
       p0[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(__builtin_bit_cast(float, b0), c2, kx));
       p1[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(__builtin_bit_cast(float, b1), c2, kx));
-    }
-    if (masked) {  // the sentinel marks the invisible keys: exactly p = 0 there
-      asm volatile("");
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        p0[i] = (s0[i] != SENTINEL) ? p0[i] : 0.f;
-        p1[i] = (s1[i] != SENTINEL) ? p1[i] : 0.f;
-      }
     }
     if constexpr (PV == PVFP8) {
 #pragma unroll
@@ -336,28 +332,10 @@ struct WaveState {
     }
   }
 
-  // A whole chunk in one go (boundary chunks and the tail of the key range).
-  __device__ __forceinline__ void chunk(const int8_t* klds, const uint8_t* vlds, int e8, const v4i* qv, float c,
-                                        bool masked, int kb, int re, int lane) {
-    v16i s0, s1;
-    qk_chunk<D>(klds, qv, lane, s0, s1);
-    if (masked) mask(s0, s1, kb, re);
-    PTile<PV> P;
-    const float alpha = softmax(s0, s1, c, !masked || kb - 16 * (lane >> 5) < re, masked, P);
-    rescale(alpha);
-    pv(P, vlds, e8, lane);
-  }
 };
 
-// Number of leading 64-key chunks that every query row of tile qt sees in
-// full: the smallest visible end over the tile's rows, in whole chunks.
-__device__ __forceinline__ int wg_full_of(const AttnArgs& A, int kv_len, int q_pos0, int qt) {
-  int end = kv_len;
-  if (A.frame_len > 0) end = min(kv_len, ((q_pos0 + qt * BQ) / A.frame_len + 1) * A.frame_len);
-  return end / 64;
-}
-
-template <int D, int PV, int DT>
+// CACHE: keys in a frame cache (frame_stride > 0) rather than contiguous.
+template <int D, int PV, int DT, bool CACHE>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
   constexpr int NCB = D / 32;                    // 32-channel blocks of O
   constexpr int VBYTES = (PV == PVFP8) ? 1 : 2;  // bytes per V element
@@ -390,23 +368,83 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
 
   const int kv_len = A.bi.kv_len[b];
   const int q_pos0 = A.bi.q_pos0[b];
-  const int nch_b = (kv_len + 63) / 64;
-  const int c_lo = split * nch_b / A.splits;
-  const int c_hi = (split + 1) * nch_b / A.splits;
+  const int F = A.frame_len, FS = CACHE ? A.frame_stride : 0;
 
-  // ---- this lane's query row and the end of its visible key range
+  // ---- this lane's query row and the tile's first and last real rows
   const int qi = qt * BQ + w * 32 + (lane & 31);
   const int qi_valid = min(qi, A.Nq - 1);
-  int re = kv_len;
-  if (A.frame_len > 0) re = min(kv_len, ((q_pos0 + qi_valid) / A.frame_len + 1) * A.frame_len);
-  const int wg_end = A.frame_len > 0
-                         ? min(kv_len, ((q_pos0 + min(qt * BQ + BQ - 1, A.Nq - 1)) / A.frame_len + 1) *
-                                           A.frame_len)
-                         : kv_len;
-  // wave-uniform loop bounds, kept in scalar registers
-  const int wave_hi = __builtin_amdgcn_readfirstlane(min(c_hi, (wave_max_i(re) + 63) / 64));
-  const int wave_full = __builtin_amdgcn_readfirstlane(wave_min_i(re) / 64);  // unmasked below this
-  const int wg_hi = min(c_hi, (wg_end + 63) / 64);
+  const int row_first = qt * BQ, row_last = min(qt * BQ + BQ, A.Nq) - 1;
+
+  // ---- the key chunks this work item visits: list entry v is chunk v for
+  // v < a0, else chunk b1 + (v - a0); the split takes entries [v_lo, v_hi).
+  //  * contiguous keys: the batch's chunks [0, ceil(kv_len/64)), split on that
+  //    grid, cut at the end of the tile's last row; a row sees the prefix
+  //    [0, re) of the keys;
+  //  * frame cache: the chunks of the sink frames, then those of the window
+  //    frames through the last row's frame (up to its last token); a row sees
+  //    the valid slots of the frames of its window.
+  int re = 0, fq = 0, fq_lo = 0, fq_hi = 0, a0 = 0, b1 = 0, v_lo, v_hi, full_end = 0;
+  if constexpr (!CACHE) {
+    re = F > 0 ? min(kv_len, ((q_pos0 + qi_valid) / F + 1) * F) : kv_len;
+    const int first_end = F > 0 ? min(kv_len, ((q_pos0 + row_first) / F + 1) * F) : kv_len;
+    const int last_end = F > 0 ? min(kv_len, ((q_pos0 + row_last) / F + 1) * F) : kv_len;
+    const int nch = (kv_len + 63) / 64;
+    v_lo = split * nch / A.splits;
+    v_hi = min((split + 1) * nch / A.splits, (last_end + 63) / 64);
+    full_end = first_end;  // chunks ending at or before it are visible in full to every row
+  } else {
+    const int cpf = FS / 64;
+    fq = (q_pos0 + qi_valid) / F;
+    fq_lo = (q_pos0 + row_first) / F;
+    fq_hi = (q_pos0 + row_last) / F;
+    const int end_chunk = (fq_hi * FS + min(F, kv_len - fq_hi * F) + 63) / 64;
+    int nv = end_chunk;
+    if (A.window_frames > 0) {
+      a0 = min(min(A.sink_frames, fq_hi + 1) * cpf, end_chunk);
+      b1 = min(max(A.sink_frames, fq_lo - A.window_frames) * cpf, end_chunk);
+      b1 = max(b1, a0);
+      nv = a0 + (end_chunk - b1);
+    }
+    v_lo = split * nv / A.splits;
+    v_hi = (split + 1) * nv / A.splits;
+  }
+  const int J = max(0, v_hi - v_lo);  // chunks of this work item
+  // list entries below this one are visible in full to every row of the tile
+  // (contiguous keys: up to the first row's end; frame cache: no shortcut)
+  const int v_full = CACHE ? 0 : full_end / 64;
+  // physical chunk of list entry v; contiguous keys: v itself (the loads
+  // clamp it to the head's last chunk), frame cache: clamped to the item's
+  // range first
+  auto chunk_of = [&](int v) {
+    if constexpr (!CACHE) return v;
+    v = max(min(v, v_hi - 1), 0);
+    return v < a0 ? v : b1 + (v - a0);
+  };
+
+  // Visibility of chunk ch: every row sees all 64 keys (wave-uniform), or
+  // this row sees its first row_lim keys.
+  // frame of cache chunk ch: ch / (FS/64) by a multiply-high with the
+  // host's rounded-up reciprocal (exact for ch < 2^20, FS/64 < 2^11); with
+  // one chunk per frame the reciprocal (2^32) does not fit and f = ch
+  auto frame_of = [&](int ch) -> int {
+    return FS == 64 ? ch : static_cast<int>(__umulhi(static_cast<uint32_t>(ch), A.cpf_magic));
+  };
+  auto chunk_full = [&](int ch) -> bool {
+    if constexpr (!CACHE) return (ch + 1) * 64 <= full_end;
+    const int f = frame_of(ch);
+    const int t0 = (ch - f * (FS / 64)) * 64;
+    const int vc = min(min(F - t0, kv_len - (f * F + t0)), 64);
+    const bool all = f <= fq_lo && (A.window_frames == 0 || f < A.sink_frames || f >= fq_hi - A.window_frames);
+    return vc >= 64 && all;
+  };
+  auto row_lim = [&](int ch) -> int {
+    if constexpr (!CACHE) return re - ch * 64;
+    const int f = frame_of(ch);
+    const int t0 = (ch - f * (FS / 64)) * 64;
+    const int vc = min(min(F - t0, kv_len - (f * F + t0)), 64);
+    const bool vis = f <= fq && (A.window_frames == 0 || f < A.sink_frames || f >= fq - A.window_frames);
+    return vis ? vc : 0;
+  };
 
   v4i qv[D / 32];
   load_q<D>(qv, A.qc + (static_cast<int64_t>(bh) * A.Nq_pad + qi) * D, h2);
@@ -480,40 +518,50 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
   };
   auto dma_wait = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0): this wave's DMA landed
 
-  // Chunks every row of the workgroup sees in full run through the main loop;
-  // the rest (the partial last chunk, frame boundaries) through the tail loop.
-  const int main_hi = max(c_lo, min(wg_hi, wg_full_of(A, kv_len, q_pos0, qt)));
+  // Masking of a chunk whose scores are in (s0, s1): a wave-uniform branch,
+  // taken only at boundaries (the last chunks of a row's range, frame padding,
+  // window edges).  Returns whether this row has a visible key in the chunk.
+  auto mask_chunk = [&](int v, v16i& s0, v16i& s1) -> bool {
+    const int ch = chunk_of(v);
+    if (chunk_full(ch)) return true;
+    asm volatile("");  // keep this a real branch
+    const int lim = row_lim(ch);
+    st.mask(s0, s1, lim - 16 * h2);
+    return lim > 0;
+  };
 
-  // Main loop, software-pipelined within each wave over three chunks: step
-  // j (chunk n = c_lo + j) enters with S(n+1) and P(n) in registers, K(n+2)
-  // in K buffer j&1 and V(n) in V buffer j&1.  One straight-line region
-  // issues the DMA of K(n+3) and V(n+1), the S MFMAs of chunk n+2, the P.V
-  // MFMAs of chunk n and the softmax of chunk n+1, so the matrix cores and
-  // the vector ALUs work side by side; then the (rare) rescale by chunk
-  // n+1's alpha, the wait for this step's DMA and the barrier.
-  const int J = main_hi - c_lo;  // chunks through the main loop
+  // Software pipeline within each wave over three chunks: step j (list entry
+  // n = v_lo + j) enters with S(n+1) and P(n) in registers, K(n+2) in K buffer
+  // j&1 and V(n) in V buffer j&1.  One straight-line region issues the DMA of
+  // K(n+3) and V(n+1), the S MFMAs of entry n+2, the P.V MFMAs of entry n and
+  // the softmax of entry n+1, so the matrix cores and the vector ALUs work
+  // side by side; then the (rare) rescale by entry n+1's alpha, the (rare)
+  // masking of S(n+2), the wait for this step's DMA and the barrier.
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
   v16i sa0{}, sa1{}, sb0{}, sb1{};
   PTile<PV> pa, pb;
-  int n = c_lo;
-  int e_cur = load_e(c_lo);
-  float ksn1 = load_ks(c_lo + 1), ksn2 = load_ks(c_lo + 2);  // K scales of chunks n+1, n+2
-  // Prologue: K(c_lo) and V(c_lo) in buffers 0, K(c_lo + 1) in K buffer 1;
-  // with main chunks also S(c_lo + 1), P(c_lo) and K(c_lo + 2) in K buffer 0.
+  bool ha = true, hb = true;  // the rows' visibility flags of the chunks in sa, sb
+  int n = v_lo;
+  int e_cur = load_e(chunk_of(n));
+  float ksn1 = load_ks(chunk_of(n + 1)), ksn2 = load_ks(chunk_of(n + 2));  // K scales of n+1, n+2
+  // Prologue: K(n) and V(n) in buffers 0, K(n+1) in K buffer 1; then S(n+1),
+  // P(n) and K(n+2) in K buffer 0.
   {
-    const float ks0 = load_ks(c_lo);
-    dma_k(kL0, c_lo);
-    dma_v(vL0, c_lo);
-    dma_k(kL1, c_lo + 1);
+    const float ks0 = load_ks(chunk_of(n));
+    dma_k(kL0, chunk_of(n));
+    dma_v(vL0, chunk_of(n));
+    dma_k(kL1, chunk_of(n + 1));
     dma_wait();
     __syncthreads();
     if (J >= 1) {
       qk_chunk<D>(kL0, qv, lane, sb0, sb1);
       if (J >= 2) qk_chunk<D>(kL1, qv, lane, sa0, sa1);
-      __syncthreads();  // every wave has read K(c_lo) from buffer 0
-      dma_k(kL0, c_lo + 2);
-      st.rescale(st.softmax(sb0, sb1, qsc * ks0, true, false, pa));
+      __syncthreads();  // every wave has read K(n) from buffer 0
+      dma_k(kL0, chunk_of(n + 2));
+      hb = mask_chunk(n, sb0, sb1);
+      if (J >= 2) ha = mask_chunk(n + 1, sa0, sa1);
+      st.rescale(st.softmax(sb0, sb1, qsc * ks0, hb, pa));
       dma_wait();
       __syncthreads();
     }
@@ -522,8 +570,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
   // prefetch loads from being waited on before the first MFMA.
   __builtin_amdgcn_s_waitcnt(0);
 
-  auto step = [&](auto par, v16i& cs0, v16i& cs1, PTile<PV>& p_cur, v16i& ns0, v16i& ns1, PTile<PV>& p_nxt) {
+  // CHK false: S(n+1) and S(n+2) are visible in full to every row (no masking
+  // check, every row has keys in entry n+1).
+  auto step = [&](auto par, auto chk, v16i& cs0, v16i& cs1, bool& has_c, PTile<PV>& p_cur, v16i& ns0,
+                  v16i& ns1, bool& has_n, PTile<PV>& p_nxt) {
     constexpr int P = decltype(par)::value;  // parity of the step
+    constexpr bool CHK = decltype(chk)::value;
     int8_t* k_rd = P ? kL1 : kL0;            // K(n+2)
     int8_t* k_wr = P ? kL0 : kL1;            // receives K(n+3)
     uint8_t* v_rd = P ? vL1 : vL0;           // V(n)
@@ -533,14 +585,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
     constexpr int NRD = NQK + ((PV == PVFP8) ? 2 * NCB : 4 * NCB);  // LDS operand reads
     constexpr int VPER = (PV == PVFP8) ? 12 : 5;                  // softmax slice per MFMA
     const float c_mid = qsc * ksn1;
+    const int ch1 = chunk_of(n + 1), ch3 = chunk_of(n + 3);
     __builtin_amdgcn_sched_barrier(0);
-    dma_k(k_wr, n + 3);
-    dma_v(v_wr, n + 1);
-    const int e_nxt = load_e(n + 1);
-    const float ks3 = load_ks(n + 3);
+    dma_k(k_wr, ch3);
+    dma_v(v_wr, ch1);
+    const int e_nxt = load_e(ch1);
+    const float ks3 = load_ks(ch3);
     qk_chunk<D>(k_rd, qv, lane, ns0, ns1);
     st.pv(p_cur, v_rd, e_cur, lane);
-    const float alpha = st.softmax(cs0, cs1, c_mid, true, false, p_nxt);
+    const float alpha = st.softmax(cs0, cs1, c_mid, CHK ? has_c : true, p_nxt);
     __builtin_amdgcn_sched_group_barrier(0x020, 2 + KI + VI, 0);  // the loads
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);            // the first operand reads
 #pragma unroll
@@ -555,6 +608,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
     p_nxt.pin();
     __builtin_amdgcn_sched_barrier(0);
     st.rescale(alpha);  // rare: some row's running max moved (after P(n) V(n))
+    if constexpr (CHK) {
+      if (n + 2 >= v_full) has_n = mask_chunk(n + 2, ns0, ns1);  // rare: S(n+2) is a boundary chunk
+    }
     dma_wait();
     __syncthreads();
     e_cur = e_nxt;
@@ -562,54 +618,30 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
     ksn2 = ks3;
     ++n;
   };
-  // The last main chunk's P.V, with V(n+1) staged for the tail.
-  auto finish = [&](auto par, PTile<PV>& p_cur) {
-    constexpr int P = decltype(par)::value;
-    uint8_t* v_rd = P ? vL1 : vL0;
-    uint8_t* v_wr = P ? vL0 : vL1;
-    dma_v(v_wr, n + 1);
-    const int e_nxt = load_e(n + 1);
-    st.pv(p_cur, v_rd, e_cur, lane);
-    dma_wait();
-    __syncthreads();
-    e_cur = e_nxt;
-    ++n;
-  };
+  using NoChk = std::integral_constant<bool, false>;
+  using Chk = std::integral_constant<bool, true>;
   if (J >= 1) {
     int left = J - 1;  // pipelined steps
+    if constexpr (!CACHE) {
+      // the leading steps whose S(n+2) lies below v_full, in pairs
+      for (int fast = min(J - 1, v_full - v_lo - 2); fast >= 2; fast -= 2) {
+        step(P0{}, NoChk{}, sa0, sa1, ha, pa, sb0, sb1, hb, pb);
+        step(P1{}, NoChk{}, sb0, sb1, hb, pb, sa0, sa1, ha, pa);
+        left -= 2;
+      }
+    }
     while (left >= 2) {
-      step(P0{}, sa0, sa1, pa, sb0, sb1, pb);
-      step(P1{}, sb0, sb1, pb, sa0, sa1, pa);
+      step(P0{}, Chk{}, sa0, sa1, ha, pa, sb0, sb1, hb, pb);
+      step(P1{}, Chk{}, sb0, sb1, hb, pb, sa0, sa1, ha, pa);
       left -= 2;
     }
+    // the last entry's P.V (its V is in buffer (J-1)&1)
     if (left == 1) {
-      step(P0{}, sa0, sa1, pa, sb0, sb1, pb);
-      finish(P1{}, pb);
+      step(P0{}, Chk{}, sa0, sa1, ha, pa, sb0, sb1, hb, pb);
+      st.pv(pb, vL1, e_cur, lane);
     } else {
-      finish(P0{}, pa);
+      st.pv(pa, vL0, e_cur, lane);
     }
-  }
-  // Tail loop: chunk n with K and V both in buffers (n - c_lo)&1; the next chunk's K
-  // and V are staged into the other buffers.
-  auto tail = [&](auto par) {
-    constexpr int P = decltype(par)::value;
-    int8_t* k_rd = P ? kL1 : kL0;
-    int8_t* k_wr = P ? kL0 : kL1;
-    uint8_t* v_rd = P ? vL1 : vL0;
-    uint8_t* v_wr = P ? vL0 : vL1;
-    const float c = qsc * load_ks(n);
-    dma_k(k_wr, n + 1);
-    dma_v(v_wr, n + 1);
-    const int e_nxt = load_e(n + 1);
-    if (n < wave_hi) st.chunk(k_rd, v_rd, e_cur, qv, c, n >= wave_full, n * 64 + 16 * h2, re, lane);
-    dma_wait();
-    __syncthreads();
-    e_cur = e_nxt;
-    ++n;
-  };
-  while (n < wg_hi) {
-    if (((n - c_lo) & 1) == 0) tail(P0{});
-    else tail(P1{});
   }
   v16f* o = st.o;
   const float m = st.m;
@@ -737,6 +769,10 @@ static AttnArgs make_args(const AttnLaunch& L) {
   A.total = L.B * L.H * L.splits * A.nqt;
   A.sigma = L.sigma;
   A.frame_len = L.frame_len;
+  A.frame_stride = L.frame_stride;
+  A.sink_frames = L.sink_frames;
+  A.window_frames = L.window_frames;
+  A.cpf_magic = L.cpf_magic;
   A.bi = L.bi;
   for (int i = 0; i < MAXB_ARGS; ++i) A.order[i] = L.order[i];
   return A;
@@ -745,7 +781,10 @@ static AttnArgs make_args(const AttnLaunch& L) {
 template <int D, int PV, int DT>
 static hipError_t attn_impl(const AttnLaunch& L, hipStream_t st) {
   const AttnArgs A = make_args(L);
-  hipLaunchKernelGGL((attn_fwd_kernel<D, PV, DT>), dim3(A.total), dim3(256), 0, st, A);
+  if (L.frame_stride > 0)
+    hipLaunchKernelGGL((attn_fwd_kernel<D, PV, DT, true>), dim3(A.total), dim3(256), 0, st, A);
+  else
+    hipLaunchKernelGGL((attn_fwd_kernel<D, PV, DT, false>), dim3(A.total), dim3(256), 0, st, A);
   if (L.splits > 1) {
     const int64_t threads = static_cast<int64_t>(L.B) * L.H * L.Nq_pad * (D / 4);
     hipLaunchKernelGGL((attn_combine_kernel<D, DT>), dim3(static_cast<unsigned>((threads + 255) / 256)),

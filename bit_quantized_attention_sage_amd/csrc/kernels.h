@@ -24,6 +24,10 @@ struct QuantLaunch {
   const void *q, *k, *v;
   int64_t qs[3], ks[3], vs[3];
   const float* k_mean_in;
+  const int8_t* chan_shift_in;
+  int frame_len, frame_stride;  // frame cache when frame_stride > 0
+  int frames_only;              // 1: quantize frames [frame0, frame0 + nframes) (q optional)
+  int frame0, nframes;
   BatchInfo bi;
   sage_quant_bufs bufs;
   // views into bufs.stats
@@ -35,6 +39,8 @@ struct AttnLaunch {
   int dtype, pv_mode, d;
   int B, H, Nq, Nkv, Nq_pad, Nkv_pad;
   int frame_len, splits;
+  int frame_stride, sink_frames, window_frames;  // frame cache and window
+  uint32_t cpf_magic;  // ceil(2^32 / (frame_stride / 64)): chunk -> frame by __umulhi
   float sigma;  // fp32(sm_scale * log2 e)
   BatchInfo bi;
   int order[MAXB_ARGS];  // batches by decreasing kv_len (longest first)

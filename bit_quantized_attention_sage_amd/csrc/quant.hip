@@ -74,6 +74,7 @@ __global__ void stats_final_kernel(int H, int D, int nchunk_k, int nchunk_q, Bat
                                    const float* __restrict__ kmin,
                                    const float* __restrict__ qamax,
                                    const float* __restrict__ k_mean_in,
+                                   const int8_t* __restrict__ shift_in,
                                    float* __restrict__ mu_out, int8_t* __restrict__ shift_out) {
   const int bh = blockIdx.x, c = threadIdx.x;
   if (c >= D) return;
@@ -104,26 +105,42 @@ __global__ void stats_final_kernel(int H, int D, int nchunk_k, int nchunk_q, Bat
     const int k = ek - eq - (mk < mq ? 1 : 0);   // floor(log2(ka / qa))
     a = (k + 1) >= 0 ? (k + 1) / 2 : -((-(k + 1) + 1) / 2);  // floor((k+1)/2)
   }
+  if (shift_in) a = shift_in[static_cast<int64_t>(bh) * D + c];
   mu_out[static_cast<int64_t>(bh) * D + c] = mu;
   shift_out[static_cast<int64_t>(bh) * D + c] = static_cast<int8_t>(a);
 }
 
+// Input row of position j of the quantized operand, or -1 (zero).  Without a
+// frame cache (FS == 0) position j is input row j.  With one, position j is
+// cache slot j: frame f = j / FS holds tokens f*F .. f*F + F - 1 at its first
+// F slots (the rest are padding); the input holds tokens from tok0 on, and
+// n_valid of its rows are valid.
+__device__ __forceinline__ int slot_row(int j, int F, int FS, int tok0, int n_valid) {
+  if (FS == 0) return j < n_valid ? j : -1;
+  const int f = j / FS, t = j - f * FS;
+  if (t >= F) return -1;
+  const int r = f * F + t - tok0;
+  return (r >= 0 && r < n_valid) ? r : -1;
+}
+
 // ---------------------------------------------------------------- INT8 blocks
-// One workgroup per block of ROWS tokens of one (b, h).  Each thread holds 8
-// channels of ROWS*D/2048 rows in registers between the amax and the encode.
+// One workgroup per block of ROWS positions of one (b, h) -- block blk0 +
+// blockIdx.x; positions map to input rows through slot_row (n_in >= 0
+// overrides the count of valid input rows).  Each thread holds 8 channels of
+// ROWS*D/2048 rows in registers between the amax and the encode.
 template <typename T, int D, int ROWS, bool IS_K>
 __global__ __launch_bounds__(256) void quant_i8_kernel(
     const T* __restrict__ x, int64_t sb, int64_t sh, int64_t sn, int H, int n_all,
     int n_pad, BatchInfo bi, const float* __restrict__ mu, const int8_t* __restrict__ shift,
-    int8_t* __restrict__ codes, float* __restrict__ scale) {
+    int8_t* __restrict__ codes, float* __restrict__ scale, int F, int FS, int tok0, int n_in, int blk0) {
   constexpr int G = D / 8;
   constexpr int RPP = 256 / G;       // rows per pass
   constexpr int PASSES = ROWS / RPP;
   static_assert(ROWS % RPP == 0, "block shape");
-  const int b = blockIdx.z, h = blockIdx.y, blk = blockIdx.x;
+  const int b = blockIdx.z, h = blockIdx.y, blk = blk0 + blockIdx.x;
   const int bh = b * H + h;
   const int g = threadIdx.x % G, r0 = threadIdx.x / G;
-  const int n_valid = IS_K ? bi.kv_len[b] : n_all;
+  const int n_valid = n_in >= 0 ? n_in : (IS_K ? bi.kv_len[b] : n_all);
   float sh_mul[8], m8[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
@@ -136,8 +153,9 @@ __global__ __launch_bounds__(256) void quant_i8_kernel(
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
     const int j = blk * ROWS + p * RPP + r0;
-    if (j < n_valid) {
-      const uint4 raw = *reinterpret_cast<const uint4*>(x + b * sb + h * sh + j * sn + 8 * g);
+    const int row = slot_row(j, F, FS, tok0, n_valid);
+    if (row >= 0) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(x + b * sb + h * sh + row * sn + 8 * g);
       const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
@@ -187,17 +205,18 @@ __global__ __launch_bounds__(256) void quant_i8_kernel(
 template <typename T, int D, bool FP8>
 __global__ __launch_bounds__(2 * D) void prep_v_kernel(
     const T* __restrict__ x, int64_t sb, int64_t sh, int64_t sn, int H, int n_pad,
-    BatchInfo bi, void* __restrict__ vt, uint8_t* __restrict__ e8m0) {
+    BatchInfo bi, void* __restrict__ vt, uint8_t* __restrict__ e8m0, int F, int FS, int tok0, int n_in,
+    int ch0) {
   __shared__ uint16_t tile[64][D + 2];
-  const int b = blockIdx.z, h = blockIdx.y, ch = blockIdx.x;
+  const int b = blockIdx.z, h = blockIdx.y, ch = ch0 + blockIdx.x;
   const int bh = b * H + h;
-  const int n_valid = bi.kv_len[b];
+  const int n_valid = n_in >= 0 ? n_in : bi.kv_len[b];
   constexpr int GR = D / 8;  // 16-byte granules per key row
   for (int gi = threadIdx.x; gi < 64 * GR; gi += 2 * D) {
     const int r = gi / GR, g = gi % GR;
-    const int j = ch * 64 + r;
+    const int row = slot_row(ch * 64 + r, F, FS, tok0, n_valid);
     uint4 raw = make_uint4(0, 0, 0, 0);
-    if (j < n_valid) raw = *reinterpret_cast<const uint4*>(x + b * sb + h * sh + j * sn + 8 * g);
+    if (row >= 0) raw = *reinterpret_cast<const uint4*>(x + b * sb + h * sh + row * sn + 8 * g);
     const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
     for (int c = 0; c < 8; ++c) tile[r][8 * g + c] = static_cast<uint16_t>((w[c / 2] >> (16 * (c % 2))) & 0xFFFFu);
@@ -271,29 +290,39 @@ static hipError_t quantize_impl(const QuantLaunch& L, hipStream_t st) {
   constexpr int CPB = 256 / (D / 8);
   const int nck = (L.Nkv + KMEAN_CHUNK - 1) / KMEAN_CHUNK;
   const int ncq = (L.Nq + KMEAN_CHUNK - 1) / KMEAN_CHUNK;
-  hipLaunchKernelGGL((stats_partial_kernel<T, D, true>), dim3((nck + CPB - 1) / CPB, L.H, L.B), blk, 0, st,
-                     static_cast<const T*>(L.k), L.ks[0], L.ks[1], L.ks[2], L.H, nck, L.bi, L.Nkv,
-                     L.stat_ksum, L.stat_kmax, L.stat_kmin);
-  hipLaunchKernelGGL((stats_partial_kernel<T, D, false>), dim3((ncq + CPB - 1) / CPB, L.H, L.B), blk, 0, st,
-                     static_cast<const T*>(L.q), L.qs[0], L.qs[1], L.qs[2], L.H, ncq, L.bi, L.Nq,
-                     nullptr, L.stat_qamax, nullptr);
-  hipLaunchKernelGGL(stats_final_kernel, dim3(L.B * L.H), dim3(D), 0, st, L.H, D, nck, ncq, L.bi,
-                     L.stat_ksum, L.stat_kmax, L.stat_kmin, L.stat_qamax, L.k_mean_in,
-                     L.bufs.k_mean, L.bufs.chan_shift);
-  hipLaunchKernelGGL((quant_i8_kernel<T, D, BQ, false>), dim3(L.Nq_pad / BQ, L.H, L.B), blk, 0, st,
-                     static_cast<const T*>(L.q), L.qs[0], L.qs[1], L.qs[2], L.H, L.Nq, L.Nq_pad, L.bi,
-                     L.bufs.k_mean, L.bufs.chan_shift, L.bufs.q_codes, L.bufs.q_scale);
-  hipLaunchKernelGGL((quant_i8_kernel<T, D, BK, true>), dim3(L.Nkv_pad / BK, L.H, L.B), blk, 0, st,
+  const int F = L.frame_len, FS = L.frame_stride;
+  if (!L.frames_only) {
+    hipLaunchKernelGGL((stats_partial_kernel<T, D, true>), dim3((nck + CPB - 1) / CPB, L.H, L.B), blk, 0, st,
+                       static_cast<const T*>(L.k), L.ks[0], L.ks[1], L.ks[2], L.H, nck, L.bi, L.Nkv,
+                       L.stat_ksum, L.stat_kmax, L.stat_kmin);
+    hipLaunchKernelGGL((stats_partial_kernel<T, D, false>), dim3((ncq + CPB - 1) / CPB, L.H, L.B), blk, 0, st,
+                       static_cast<const T*>(L.q), L.qs[0], L.qs[1], L.qs[2], L.H, ncq, L.bi, L.Nq,
+                       nullptr, L.stat_qamax, nullptr);
+    hipLaunchKernelGGL(stats_final_kernel, dim3(L.B * L.H), dim3(D), 0, st, L.H, D, nck, ncq, L.bi,
+                       L.stat_ksum, L.stat_kmax, L.stat_kmin, L.stat_qamax, L.k_mean_in, L.chan_shift_in,
+                       L.bufs.k_mean, L.bufs.chan_shift);
+  }
+  if (L.q)
+    hipLaunchKernelGGL((quant_i8_kernel<T, D, BQ, false>), dim3(L.Nq_pad / BQ, L.H, L.B), blk, 0, st,
+                       static_cast<const T*>(L.q), L.qs[0], L.qs[1], L.qs[2], L.H, L.Nq, L.Nq_pad, L.bi,
+                       L.bufs.k_mean, L.bufs.chan_shift, L.bufs.q_codes, L.bufs.q_scale, 0, 0, 0, -1, 0);
+  // K and V: every position (blocks of the whole operand), or the slots of the
+  // appended frames only (their tokens are the input's rows 0 ..)
+  const int c0 = L.frames_only ? L.frame0 * FS / 64 : 0;
+  const int nc = L.frames_only ? L.nframes * FS / 64 : L.Nkv_pad / 64;
+  const int tok0 = L.frames_only ? L.frame0 * F : 0;
+  const int n_in = L.frames_only ? L.nframes * F : -1;
+  hipLaunchKernelGGL((quant_i8_kernel<T, D, BK, true>), dim3(nc, L.H, L.B), blk, 0, st,
                      static_cast<const T*>(L.k), L.ks[0], L.ks[1], L.ks[2], L.H, L.Nkv, L.Nkv_pad, L.bi,
-                     L.bufs.k_mean, L.bufs.chan_shift, L.bufs.k_codes, L.bufs.k_scale);
+                     L.bufs.k_mean, L.bufs.chan_shift, L.bufs.k_codes, L.bufs.k_scale, F, FS, tok0, n_in, c0);
   if (L.pv_mode == PVFP8)
-    hipLaunchKernelGGL((prep_v_kernel<T, D, true>), dim3(L.Nkv_pad / 64, L.H, L.B), dim3(2 * D), 0, st,
+    hipLaunchKernelGGL((prep_v_kernel<T, D, true>), dim3(nc, L.H, L.B), dim3(2 * D), 0, st,
                        static_cast<const T*>(L.v), L.vs[0], L.vs[1], L.vs[2], L.H, L.Nkv_pad, L.bi,
-                       L.bufs.v_t, L.bufs.v_e8m0);
+                       L.bufs.v_t, L.bufs.v_e8m0, F, FS, tok0, n_in, c0);
   else
-    hipLaunchKernelGGL((prep_v_kernel<T, D, false>), dim3(L.Nkv_pad / 64, L.H, L.B), dim3(2 * D), 0, st,
+    hipLaunchKernelGGL((prep_v_kernel<T, D, false>), dim3(nc, L.H, L.B), dim3(2 * D), 0, st,
                        static_cast<const T*>(L.v), L.vs[0], L.vs[1], L.vs[2], L.H, L.Nkv_pad, L.bi,
-                       L.bufs.v_t, L.bufs.v_e8m0);
+                       L.bufs.v_t, L.bufs.v_e8m0, F, FS, tok0, n_in, c0);
   return hipGetLastError();
 }
 

@@ -26,6 +26,19 @@
  * (absolute position q_pos0[b] + i) sees key j iff j < kv_len[b] and
  * floor(j/F) <= floor((q_pos0[b]+i)/F).  F = 0: every key j < kv_len[b].
  *
+ * Frame cache and sliding window (frame_stride > 0).  Streaming decoding
+ * attends within a fixed window -- a persistent reference context computed
+ * once (like sink frames), the history cached inside the window and the
+ * current frame -- over cached history (Vidu S1 blog, section "Infra").  K and
+ * V are then held as a cache of whole frames quantized once: frame f's F
+ * tokens occupy slots [f*FS, f*FS + F) of the quantized K/V operands (FS =
+ * frame_stride, a multiple of 64, >= F; the other slots are padding, never
+ * visible), so no scale block spans two frames and appending a frame
+ * (sage_attn_quantize_frames) touches no other frame's codes.  With S =
+ * sink_frames and W = window_frames > 0, query frame fq sees key frame fk iff
+ * fk <= fq and (fk < S or fk >= fq - W); W = 0 keeps every earlier frame.
+ * kv_len and q_pos0 stay in tokens; Nkv counts cache slots.
+ *
  * Tensors.  Q [B,H,Nq,d], K and V [B,H,Nkv,d], O [B,H,Nq,d], all of one
  * 16-bit type (fp16 or bf16), device memory, channel dimension contiguous,
  * strides of the b, h and n dimensions given in ELEMENTS.  d is 64 or 128.
@@ -56,7 +69,7 @@
 extern "C" {
 #endif
 
-#define SAGE_ATTN_ABI_VERSION 1
+#define SAGE_ATTN_ABI_VERSION 2
 
 typedef enum {
   SAGE_OK = 0,
@@ -89,10 +102,21 @@ typedef struct sage_attn_desc {
   float sm_scale;       /* softmax scale; 0 -> 1/sqrt(d)                      */
   uint32_t flags;       /* SAGE_FLAG_*                                        */
   int64_t q_stride[3], k_stride[3], v_stride[3], o_stride[3]; /* b, h, n     */
-  const int32_t *kv_len; /* host [B] valid keys per batch, or NULL (all Nkv)  */
+  const int32_t *kv_len; /* host [B] valid keys per batch, or NULL: all Nkv
+                            (frame cache: Nkv/frame_stride full frames)       */
   const int32_t *q_pos0; /* host [B] absolute position of query 0, or NULL:
                             kv_len[b] - Nq when frame_len > 0                 */
   const float *k_mean_in; /* device [B,H,d] fixed mean to use, or NULL      */
+  int32_t frame_stride;   /* 0: K/V tokens contiguous (Nkv = key count);
+                             > 0: frame cache of FS slots per frame (see top):
+                             multiple of 64, >= frame_len (> 0), < 131072, and
+                             Nkv = cache slots, a multiple of it               */
+  int32_t sink_frames;    /* S: leading frames always visible (window only)   */
+  int32_t window_frames;  /* W: history frames visible besides the sinks and
+                             the current frame; 0 = all (needs frame_stride)  */
+  int32_t reserved;       /* must be 0                                         */
+  const int8_t *chan_shift_in; /* device [B,H,d] fixed channel-balance exponents
+                             (in [-64, 64]) to use, or NULL: computed          */
 } sage_attn_desc;
 
 /* Quantized operands, in caller-owned device memory (normally carved out of
@@ -130,9 +154,12 @@ const char *sage_attn_last_error(void);
 int sage_attn_constant(const char *name, double *value);
 
 /* Number of KV splits the library will use for *desc (kv_splits, or its own
- * choice when kv_splits == 0).  Split s of batch b covers the 64-key chunks
- * [s*n/S, (s+1)*n/S) with n = ceil(kv_len[b]/64); partial results are merged
- * exactly as the online softmax would. */
+ * choice when kv_splits == 0).  Contiguous keys: split s of batch b covers the
+ * 64-key chunks [s*n/S, (s+1)*n/S) with n = ceil(kv_len[b]/64).  Frame cache:
+ * each 128-query tile visits the cache chunks of its sink frames, then of its
+ * window frames through its last query's frame (up to the last token), n of
+ * them in that order, and split s takes entries [s*n/S, (s+1)*n/S) of that
+ * list.  Partial results are merged exactly as the online softmax would. */
 int sage_attn_kv_splits(const sage_attn_desc *desc, int32_t *splits);
 
 /* Bytes of workspace sage_attn_fwd needs for *desc (validated first). */
@@ -143,11 +170,25 @@ int sage_attn_workspace_size(const sage_attn_desc *desc, size_t *bytes);
 int sage_attn_quant_layout(const sage_attn_desc *desc, void *ws, size_t ws_bytes,
                            sage_quant_bufs *out);
 
-/* Quantize: K mean (unless k_mean_in), channel balance, INT8 Q and K codes and
- * scales, V prepared for P.V (transposed; FP8 codes and E8M0 scales in FP8
- * mode).  q, k, v: device inputs as described by desc. */
+/* Quantize: K mean (unless k_mean_in), channel balance (unless
+ * chan_shift_in), INT8 Q and K codes and scales, V prepared for P.V
+ * (transposed; FP8 codes and E8M0 scales in FP8 mode).  q, k, v: device
+ * inputs as described by desc (with a frame cache, k and v hold the kv_len
+ * tokens contiguously; they are written into the cache slots). */
 int sage_attn_quantize(const sage_attn_desc *desc, const void *q, const void *k,
                        const void *v, const sage_quant_bufs *bufs, void *stream);
+
+/* Frame cache only (frame_stride > 0): quantize once, against the K mean and
+ * channel-balance exponents already in bufs (left there by sage_attn_quantize
+ * or written by the caller), the nframes frames [frame0, frame0 + nframes) of
+ * new keys and values -- k, v: [B,H,nframes*frame_len,d] with desc's k/v
+ * strides -- into their cache slots, for every batch; and, when q is not NULL,
+ * the queries q (as described by desc) with the same exponents.  Codes and
+ * scales of all other frames are left untouched.  Errors: SAGE_E_UNSUPPORTED
+ * without a frame cache; SAGE_E_SHAPE if the frames do not fit in Nkv slots. */
+int sage_attn_quantize_frames(const sage_attn_desc *desc, const void *q, const void *k,
+                              const void *v, int32_t frame0, int32_t nframes,
+                              const sage_quant_bufs *bufs, void *stream);
 
 /* Fused attention on already-quantized operands: writes O [B,H,Nq,d]. */
 int sage_attn_fwd_quantized(const sage_attn_desc *desc, const sage_quant_bufs *bufs,

@@ -72,6 +72,14 @@ def test_valid_desc_and_workspace(lib):
     (dict(B=1, kv_len=[0]), 6), (dict(B=1, frame_len=50, kv_len=[120], q_pos0=[30]), 6),
     (dict(q_stride=(100 * 128 * 2, 100 * 128, 127)), 4), (dict(B=129), 7),
     (dict(sm_scale=float("nan")), 2),
+    # frame cache and window
+    (dict(frame_stride=64, Nkv=320), 6),                                   # no frame_len
+    (dict(frame_len=50, frame_stride=100, Nkv=300), 6),                    # not a multiple of 64
+    (dict(frame_len=100, frame_stride=64, Nkv=320), 6),                    # shorter than a frame
+    (dict(frame_len=50, frame_stride=64, Nkv=300), 2),                     # Nkv not whole frames
+    (dict(frame_len=50, window_frames=2), 6),                              # window without a cache
+    (dict(frame_len=50, frame_stride=64, Nkv=320, Nq=50, kv_len=[260]), 6),  # beyond 5 frames
+    (dict(frame_len=50, frame_stride=64, Nkv=320, Nq=50, window_frames=-1), 6),
 ])
 def test_bad_descriptors_are_rejected(lib, kw, code):
     st, _ = _status(_desc(**kw))
@@ -116,3 +124,29 @@ def test_auto_splits(lib):
     assert sage.sage_attn_kv_splits(big) == 1
     fixed = sage.Desc(1, 2, 1024, 1024, 64, sage.SAGE_F16, kv_splits=3)
     assert sage.sage_attn_kv_splits(fixed) == 3
+
+
+def test_frame_cache_desc_and_quantize_frames_validation(lib):
+    ok = _desc(frame_len=50, frame_stride=64, Nkv=320, Nq=50, kv_len=[250], sink_frames=1, window_frames=2)
+    assert _status(ok)[0] == 0
+    d = _desc(frame_len=50, frame_stride=64, Nkv=320, Nq=50)
+    d.c.reserved = 3
+    assert _status(d)[0] == 7
+    # argument checks of sage_attn_quantize_frames (host-only; nothing enqueued)
+    n = sage.sage_attn_workspace_size(ok)
+    ws = (ctypes.c_uint8 * (n + 256))()
+    base = (ctypes.addressof(ws) + 255) // 256 * 256
+    bufs = sage.sage_quant_bufs()
+    assert lib.sage_attn_quant_layout(ok.ptr, ctypes.c_void_p(base), n, ctypes.byref(bufs)) == 0
+    fake = ctypes.c_void_p(base)  # aligned; never dereferenced on these error paths
+    st = lib.sage_attn_quantize_frames(ok.ptr, None, fake, fake, 4, 2, ctypes.byref(bufs), None)
+    assert st == 2 and b"inside" in lib.sage_attn_last_error()
+    assert lib.sage_attn_quantize_frames(ok.ptr, None, fake, fake, -1, 1, ctypes.byref(bufs), None) == 2
+    plain = _desc()
+    n2 = sage.sage_attn_workspace_size(plain)
+    ws2 = (ctypes.c_uint8 * (n2 + 256))()
+    base2 = (ctypes.addressof(ws2) + 255) // 256 * 256
+    bufs2 = sage.sage_quant_bufs()
+    assert lib.sage_attn_quant_layout(plain.ptr, ctypes.c_void_p(base2), n2, ctypes.byref(bufs2)) == 0
+    f2 = ctypes.c_void_p(base2)
+    assert lib.sage_attn_quantize_frames(plain.ptr, None, f2, f2, 0, 1, ctypes.byref(bufs2), None) == 7

@@ -1,0 +1,217 @@
+"""GPU parity of the frame cache (whole frames quantized once into padded
+slots) and the sliding window with sink frames, through the C ABI.
+
+Streaming decoding attends within a fixed window -- sink frames, the most
+recent history frames and the current frame -- over cached history (Vidu S1
+blog, section "Infra").  Bit-exact: every quantized operand in its cache
+slots, and appending frames one at a time against the same frozen mean and
+exponents gives the same buffers as quantizing the whole cache.  Outputs:
+within the output-rounding bar of the oracle's emulation run with the
+kernel's per-tile chunk lists and splits, cosine against float64 windowed
+attention."""
+
+import numpy as np
+import pytest
+import torch
+
+import bit_quantized_attention_sage_amd as sage
+from oracle import quant, emulate, attention, codecs
+from oracle.constants import PV_16, PV_FP8, BK
+from gpu_util import host, compare_output, cosine, NAME_DT
+
+pytestmark = pytest.mark.gpu
+
+
+def _rand(shape, dtype, seed, scale=1.0, offset=None):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(shape, generator=g) * scale
+    if offset is not None:
+        x = x + offset
+    return x.to(dtype)
+
+
+def _inputs(B, H, Nq, ntok, d, dt, seed):
+    q = _rand((B, H, Nq, d), dt, seed)
+    k = _rand((B, H, ntok, d), dt, seed + 1, offset=_rand((1, H, 1, d), torch.float32, seed + 2) * 1.5)
+    v = _rand((B, H, ntok, d), dt, seed + 3)
+    return q, k, v
+
+
+def _frozen(Q, K):
+    mu = quant.k_mean(K)
+    return mu, quant.channel_shift(Q, K, mu)
+
+
+def _run(q, k, v, pv_mode, F, FS, nslots, S=0, W=0, kv_len=None, q_pos0=None, splits=0, mu=None, a=None):
+    o = torch.empty_like(q)
+    desc = sage.Desc.for_tensors(q, k, v, o, nkv=nslots, pv_mode=pv_mode, frame_len=F, frame_stride=FS,
+                                 sink_frames=S, window_frames=W, kv_len=kv_len, q_pos0=q_pos0,
+                                 kv_splits=splits,
+                                 k_mean_in=torch.from_numpy(mu).cuda() if mu is not None else None,
+                                 chan_shift_in=torch.from_numpy(a.astype(np.int8)).cuda() if a is not None else None)
+    ws = sage.new_workspace(desc, q.device)
+    bufs = sage.sage_attn_quant_layout(desc, ws)
+    sage.sage_attn_quantize(desc, q, k, v, bufs)
+    sage.sage_attn_fwd_quantized(desc, bufs, o)
+    torch.cuda.synchronize()
+    return o, desc, ws, bufs
+
+
+def tile_chunk_splits(first, last, q_pos0, kv_len, F, FS, S, W, nsplit):
+    """The kernel's chunk list of one 128-query tile (rows first..last): the
+    sink frames' chunks, then the window frames' chunks through the last
+    row's frame up to its last token; split s takes entries [s*n/S, (s+1)*n/S).
+    Returned as physical chunk ranges (lo, hi) for the emulation (chunks of
+    the gap between the two parts are invisible to every row of the tile)."""
+    cpf = FS // BK
+    fq_lo, fq_hi = (q_pos0 + first) // F, (q_pos0 + last) // F
+    end = (fq_hi * FS + min(F, kv_len - fq_hi * F) + BK - 1) // BK
+    a0 = b1 = 0
+    if W > 0:
+        a0 = min(min(S, fq_hi + 1) * cpf, end)
+        b1 = max(min(max(S, fq_lo - W) * cpf, end), a0)
+    n = a0 + (end - b1)
+    phys = lambda v: v if v < a0 else b1 + (v - a0)  # noqa: E731
+    out = []
+    for s in range(nsplit):
+        lo, hi = s * n // nsplit, (s + 1) * n // nsplit
+        out.append((phys(lo), phys(hi - 1) + 1) if hi > lo else (0, 0))
+    return out
+
+
+def emulate_cache(Q, K, V, pv_mode, dtype, F, FS, S, W, kv_len, q_pos0, mu, a, nsplit):
+    B, H, Nq, d = Q.shape
+    out = np.empty((B, H, Nq, d))
+    for b in range(B):
+        for t0 in range(0, Nq, 128):
+            rows = np.arange(t0, min(t0 + 128, Nq))
+            sp = tile_chunk_splits(rows[0], rows[-1], q_pos0[b], kv_len[b], F, FS, S, W, nsplit)
+            sp = [r for r in sp if r[1] > r[0]]
+            o64, _ = emulate.emulate_from_inputs(Q[b:b + 1], K[b:b + 1], V[b:b + 1], pv_mode, dtype, frame_len=F,
+                                                 kv_len=[kv_len[b]], q_pos0=[q_pos0[b]], rows=rows,
+                                                 splits=sp if nsplit > 1 else None, mu=mu[b:b + 1],
+                                                 shift=a[b:b + 1], frame_stride=FS, sink_frames=S,
+                                                 window_frames=W)
+            out[b, :, rows] = o64[0].transpose(1, 0, 2)
+    return out
+
+
+@pytest.mark.parametrize("pv_mode", [PV_16, PV_FP8])
+def test_frame_cache_quantize_bit_exact(lib, pv_mode):
+    B, H, d, F, FS, nf = 2, 2, 128, 200, 256, 5
+    q, k, v = _inputs(B, H, F, nf * F, d, torch.bfloat16, 61)
+    Q, K, V = host(q), host(k), host(v)
+    mu, a = _frozen(Q, K)
+    _, desc, ws, bufs = _run(q.cuda(), k.cuda(), v.cuda(), pv_mode, F, FS, nf * FS, mu=mu, a=a)
+    views = sage.quant_views(desc, ws, bufs)
+    np.testing.assert_array_equal(views["chan_shift"].cpu().numpy(), a.astype(np.int8))
+    kc, dk = quant.quantize_k_frames(K, mu, a, F, FS)
+    np.testing.assert_array_equal(views["k_codes"].cpu().numpy()[:, :, :nf * FS], kc)
+    np.testing.assert_array_equal(views["k_scale"].cpu().numpy()[:, :, :nf * FS // BK], dk)
+    qc, dq = quant.quantize_q(Q, a)
+    np.testing.assert_array_equal(views["q_codes"].cpu().numpy()[:, :, :F], qc)
+    untiled = views["v_t"].cpu().permute(0, 1, 2, 4, 3).reshape(B, H, -1, d).numpy()
+    if pv_mode == PV_FP8:
+        vc, ve = quant.quantize_v_fp8_frames(V, F, FS)
+        np.testing.assert_array_equal(untiled.astype(np.uint8)[:, :, :nf * FS], vc)
+        ge = views["v_e8m0"].cpu().numpy()
+        nch = ge.shape[2]
+        g5 = ge.reshape(B, H, nch, 2, 32, 4)[..., : d // 32].transpose(0, 1, 2, 3, 5, 4).reshape(B, H, 2 * nch, d)
+        np.testing.assert_array_equal(g5[:, :, :nf * FS // 32], (ve + 127).astype(np.uint8))
+    else:
+        ref = codecs.bf16_bits(quant.to_frame_slots(V, F, FS))
+        np.testing.assert_array_equal(untiled.view(np.uint16)[:, :, :nf * FS], ref)
+
+
+@pytest.mark.parametrize("pv_mode", [PV_16, PV_FP8])
+def test_append_frames_equals_full_quantize(lib, pv_mode):
+    B, H, d, F, FS, nf = 2, 3, 64, 100, 128, 6
+    q, k, v = _inputs(B, H, F, nf * F, d, torch.float16, 62)
+    Q, K = host(q), host(k)
+    mu, a = _frozen(Q, K)
+    q, k, v = q.cuda(), k.cuda(), v.cuda()
+    _, desc, ws_full, bufs_full = _run(q, k, v, pv_mode, F, FS, nf * FS, mu=mu, a=a)
+    full = sage.quant_views(desc, ws_full, bufs_full)
+    ws = torch.zeros_like(ws_full)
+    bufs = sage.sage_attn_quant_layout(desc, ws)
+    inc = sage.quant_views(desc, ws, bufs)
+    inc["k_mean"].copy_(torch.from_numpy(mu))
+    inc["chan_shift"].copy_(torch.from_numpy(a.astype(np.int8)))
+    # frames 0..2 together, then 3 and 4 one at a time, the last with the queries
+    for f0, nfr in ((0, 3), (3, 1), (4, 1), (5, 1)):
+        kk = k[:, :, f0 * F:(f0 + nfr) * F]
+        vv = v[:, :, f0 * F:(f0 + nfr) * F]
+        d2 = sage.Desc.for_tensors(q, kk, vv, nkv=nf * FS, pv_mode=pv_mode, frame_len=F, frame_stride=FS)
+        sage.sage_attn_quantize_frames(d2, q if f0 == 5 else None, kk, vv, f0, nfr, bufs)
+    torch.cuda.synchronize()
+    for name in full:
+        if name in ("k_mean", "chan_shift"):
+            continue
+        assert torch.equal(full[name], inc[name]), name
+
+
+CASES = [
+    # (B, H, Nq, d, dtype, F, FS, frames cached, q frame0, S, W, splits)
+    (1, 2, 200, 128, torch.bfloat16, 200, 256, 8, 7, 1, 3, 0),    # sink + window, padded frames
+    (1, 2, 200, 128, torch.bfloat16, 200, 256, 8, 7, 1, 3, 3),    # ... with forced KV splits
+    (2, 2, 200, 128, torch.bfloat16, 100, 128, 8, 6, 2, 2, 0),    # queries span two frames (tiles straddle)
+    (1, 2, 200, 128, torch.bfloat16, 200, 256, 6, 5, 0, 0, 0),    # no window: causal over the padded cache
+    (1, 1, 64, 128, torch.bfloat16, 64, 64, 2, 1, 4, 1, 0),       # query frame inside the sinks
+    (1, 2, 150, 64, torch.float16, 150, 192, 9, 8, 2, 1, 2),      # d = 64, fp16, short window
+]
+
+
+def _cid(c):
+    return f"B{c[0]}H{c[1]}q{c[2]}d{c[3]}{NAME_DT[c[4]]}F{c[5]}FS{c[6]}n{c[7]}S{c[9]}W{c[10]}s{c[11]}"
+
+
+@pytest.mark.parametrize("pv_mode", [PV_16, PV_FP8], ids=["pv16", "pvfp8"])
+@pytest.mark.parametrize("case", CASES, ids=[_cid(c) for c in CASES])
+def test_window_parity(lib, case, pv_mode):
+    B, H, Nq, d, dt, F, FS, nf, qf0, S, W, splits = case
+    print(f"window case {_cid(case)} pv {pv_mode}", flush=True)
+    q, k, v = _inputs(B, H, Nq, nf * F, d, dt, hash(case) % 10000 + pv_mode)
+    Q, K, V = host(q), host(k), host(v)
+    mu, a = _frozen(Q, K)
+    kv_len, q_pos0 = [nf * F] * B, [qf0 * F] * B
+    o, desc, _, _ = _run(q.cuda(), k.cuda(), v.cuda(), pv_mode, F, FS, nf * FS, S, W, kv_len, q_pos0,
+                         splits, mu, a)
+    nsplit = sage.sage_attn_kv_splits(desc)
+    o64 = emulate_cache(Q, K, V, pv_mode, NAME_DT[dt], F, FS, S, W, kv_len, q_pos0, mu, a, nsplit)
+    o_abs = emulate_cache(Q, K, np.abs(V), pv_mode, NAME_DT[dt], F, FS, S, W, kv_len, q_pos0, mu, a, nsplit) \
+        if pv_mode == PV_FP8 else None
+    og = host(o)
+    mx, excess, frac, rel, rel_bound = compare_output(og, o64, NAME_DT[dt], pv_mode, o_abs)
+    print(f"  splits {nsplit} max-abs {mx:.3e} excess {excess:.2e} beyond-rounding {frac:.2e} rel-L2 {rel:.3e}")
+    assert excess <= 0
+    assert frac <= (1e-4 if pv_mode == PV_16 else 2e-2)
+    assert rel <= rel_bound
+    ref = attention.attention_fp64(Q, K, V, frame_len=F, kv_len=kv_len, q_pos0=q_pos0, sink_frames=S,
+                                   window_frames=W)
+    cs = cosine(og, ref)
+    print(f"  cosine vs fp64 windowed attention {cs:.6f}")
+    assert cs >= (0.999 if pv_mode == PV_16 else 0.998)
+
+
+@pytest.mark.parametrize("pv_mode", [PV_16, PV_FP8])
+def test_cache_without_padding_or_window_equals_contiguous(lib, pv_mode):
+    """Frames of a multiple of 64 tokens, no padding, no window: the cache
+    launch visits the same chunks with the same masks as the contiguous one,
+    so the outputs are identical."""
+    B, H, d, F, nf, Nq = 2, 2, 128, 256, 5, 256
+    q, k, v = _inputs(B, H, Nq, nf * F, d, torch.bfloat16, 63)
+    Q, K = host(q), host(k)
+    mu, a = _frozen(Q, K)
+    q, k, v = q.cuda(), k.cuda(), v.cuda()
+    kv, qp = [nf * F, 3 * F], [(nf - 1) * F, 2 * F]
+    o1, _, _, _ = _run(q, k, v, pv_mode, F, F, nf * F, kv_len=kv, q_pos0=qp, splits=1, mu=mu, a=a)
+    o2 = torch.empty_like(q)
+    desc = sage.Desc.for_tensors(q, k, v, o2, pv_mode=pv_mode, frame_len=F, kv_len=kv, q_pos0=qp, kv_splits=1,
+                                 k_mean_in=torch.from_numpy(mu).cuda(),
+                                 chan_shift_in=torch.from_numpy(a.astype(np.int8)).cuda())
+    ws = sage.new_workspace(desc, q.device)
+    bufs = sage.sage_attn_quant_layout(desc, ws)
+    sage.sage_attn_quantize(desc, q, k, v, bufs)
+    sage.sage_attn_fwd_quantized(desc, bufs, o2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
