@@ -270,3 +270,72 @@ def emulate_from_inputs(Q, K, V, pv_mode, dtype, sm_scale=None, frame_len=0,
         Vhat = Vf.astype(np.float64)
     return sage_attention_emulated(qc, dq, kc, dk, Vhat, pv_mode, dtype, sm_scale,
                                    frame_len, kv_len, q_pos0, rows, splits)
+
+
+def cache_tile_splits(first, last, q_pos0_b, kv_len_b, frame_len, frame_stride,
+                      sink_frames, window_frames, nsplit):
+    """Chunk ranges of the split work items of one 128-query tile (rows
+    first..last) over a frame cache.
+
+    The tile's key chunks, in order, are those of the sink frames, then those
+    of the window frames up to the last row's frame (through its last valid
+    token); with no window, every chunk up to there.  Split s takes entries
+    [s*n/nsplit, (s+1)*n/nsplit) of that list.  Each entry range is returned
+    as the physical chunk range that spans it: chunks of the gap between the
+    sinks and the window are invisible to every row of the tile, so they
+    change nothing in the emulation.  (Window reading: Vidu S1 blog, section
+    "Infra".)"""
+    cpf = frame_stride // BK
+    fq_lo = (q_pos0_b + first) // frame_len
+    fq_hi = (q_pos0_b + last) // frame_len
+    end = (fq_hi * frame_stride + min(frame_len, kv_len_b - fq_hi * frame_len) + BK - 1) // BK
+    a0 = b1 = 0
+    if window_frames > 0:
+        a0 = min(min(sink_frames, fq_hi + 1) * cpf, end)
+        b1 = max(min(max(sink_frames, fq_lo - window_frames) * cpf, end), a0)
+    n = a0 + (end - b1)
+
+    def phys(v):
+        return v if v < a0 else b1 + (v - a0)
+
+    out = []
+    for s in range(nsplit):
+        lo, hi = s * n // nsplit, (s + 1) * n // nsplit
+        if hi > lo:
+            out.append((phys(lo), phys(hi - 1) + 1))
+    return out
+
+
+def emulate_frame_cache(Q, K, V, pv_mode, dtype, frame_len, frame_stride, sink_frames,
+                        window_frames, kv_len, q_pos0, mu, shift, nsplit, rows=None):
+    """``emulate_from_inputs`` over a frame cache, tile by tile of 128 query
+    rows, each tile with the chunk ranges of its split work items
+    (``cache_tile_splits``).  Q [B,H,Nq,d]; K, V [B,H,tokens,d] of whole
+    frames from frame 0; mu, shift: the frozen mean and exponents.
+    Returns float64 O [B,H,R,d] for the selected rows (all when None)."""
+    from . import quant
+    Qf = np.asarray(Q, dtype=np.float32)
+    B, H, Nq, d = Qf.shape
+    rows = np.arange(Nq) if rows is None else np.asarray(rows, dtype=np.int64)
+    qc, dq = quant.quantize_q(Qf, shift)
+    kc, dk = quant.quantize_k_frames(np.asarray(K, dtype=np.float32), mu, shift, frame_len, frame_stride)
+    Vf = np.asarray(V, dtype=np.float32)
+    if pv_mode == PV_FP8:
+        vc, ve = quant.quantize_v_fp8_frames(Vf, frame_len, frame_stride)
+        Vhat = quant.dequant_v_fp8(vc, ve)
+    else:
+        Vhat = quant.to_frame_slots(Vf, frame_len, frame_stride).astype(np.float64)
+    out = np.empty((B, H, len(rows), d))
+    for b in range(B):
+        for t in np.unique(rows // BQ):
+            sel = np.nonzero(rows // BQ == t)[0]
+            first, last = t * BQ, min(t * BQ + BQ, Nq) - 1
+            sp = cache_tile_splits(first, last, int(q_pos0[b]), int(kv_len[b]), frame_len,
+                                   frame_stride, sink_frames, window_frames, nsplit)
+            o64, _ = sage_attention_emulated(qc[b:b + 1], dq[b:b + 1], kc[b:b + 1], dk[b:b + 1],
+                                             Vhat[b:b + 1], pv_mode, dtype, None, frame_len,
+                                             [kv_len[b]], [q_pos0[b]], rows[sel],
+                                             sp if nsplit > 1 else None, frame_stride,
+                                             sink_frames, window_frames)
+            out[b, :, sel] = o64[0].transpose(1, 0, 2)
+    return out

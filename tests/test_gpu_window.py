@@ -15,6 +15,7 @@ import pytest
 import torch
 
 import bit_quantized_attention_sage_amd as sage
+import workloads
 from oracle import quant, emulate, attention, codecs
 from oracle.constants import PV_16, PV_FP8, BK
 from gpu_util import host, compare_output, cosine, NAME_DT
@@ -57,59 +58,24 @@ def _run(q, k, v, pv_mode, F, FS, nslots, S=0, W=0, kv_len=None, q_pos0=None, sp
     return o, desc, ws, bufs
 
 
-def tile_chunk_splits(first, last, q_pos0, kv_len, F, FS, S, W, nsplit):
-    """The kernel's chunk list of one 128-query tile (rows first..last): the
-    sink frames' chunks, then the window frames' chunks through the last
-    row's frame up to its last token; split s takes entries [s*n/S, (s+1)*n/S).
-    Returned as physical chunk ranges (lo, hi) for the emulation (chunks of
-    the gap between the two parts are invisible to every row of the tile)."""
-    cpf = FS // BK
-    fq_lo, fq_hi = (q_pos0 + first) // F, (q_pos0 + last) // F
-    end = (fq_hi * FS + min(F, kv_len - fq_hi * F) + BK - 1) // BK
-    a0 = b1 = 0
-    if W > 0:
-        a0 = min(min(S, fq_hi + 1) * cpf, end)
-        b1 = max(min(max(S, fq_lo - W) * cpf, end), a0)
-    n = a0 + (end - b1)
-    phys = lambda v: v if v < a0 else b1 + (v - a0)  # noqa: E731
-    out = []
-    for s in range(nsplit):
-        lo, hi = s * n // nsplit, (s + 1) * n // nsplit
-        out.append((phys(lo), phys(hi - 1) + 1) if hi > lo else (0, 0))
-    return out
-
-
 def emulate_cache(Q, K, V, pv_mode, dtype, F, FS, S, W, kv_len, q_pos0, mu, a, nsplit):
+    return emulate.emulate_frame_cache(Q, K, V, pv_mode, dtype, F, FS, S, W, kv_len, q_pos0, mu, a, nsplit)
+
+
+def check_cache_operands(views, Q, K, V, mu, a, F, FS, pv_mode):
+    """Every quantized operand of a frame cache holding the whole frames of
+    K, V (frames 0 ..) bit-exactly against the oracle; slots past them zero."""
     B, H, Nq, d = Q.shape
-    out = np.empty((B, H, Nq, d))
-    for b in range(B):
-        for t0 in range(0, Nq, 128):
-            rows = np.arange(t0, min(t0 + 128, Nq))
-            sp = tile_chunk_splits(rows[0], rows[-1], q_pos0[b], kv_len[b], F, FS, S, W, nsplit)
-            sp = [r for r in sp if r[1] > r[0]]
-            o64, _ = emulate.emulate_from_inputs(Q[b:b + 1], K[b:b + 1], V[b:b + 1], pv_mode, dtype, frame_len=F,
-                                                 kv_len=[kv_len[b]], q_pos0=[q_pos0[b]], rows=rows,
-                                                 splits=sp if nsplit > 1 else None, mu=mu[b:b + 1],
-                                                 shift=a[b:b + 1], frame_stride=FS, sink_frames=S,
-                                                 window_frames=W)
-            out[b, :, rows] = o64[0].transpose(1, 0, 2)
-    return out
-
-
-@pytest.mark.parametrize("pv_mode", [PV_16, PV_FP8])
-def test_frame_cache_quantize_bit_exact(lib, pv_mode):
-    B, H, d, F, FS, nf = 2, 2, 128, 200, 256, 5
-    q, k, v = _inputs(B, H, F, nf * F, d, torch.bfloat16, 61)
-    Q, K, V = host(q), host(k), host(v)
-    mu, a = _frozen(Q, K)
-    _, desc, ws, bufs = _run(q.cuda(), k.cuda(), v.cuda(), pv_mode, F, FS, nf * FS, mu=mu, a=a)
-    views = sage.quant_views(desc, ws, bufs)
+    nf = K.shape[2] // F
     np.testing.assert_array_equal(views["chan_shift"].cpu().numpy(), a.astype(np.int8))
     kc, dk = quant.quantize_k_frames(K, mu, a, F, FS)
-    np.testing.assert_array_equal(views["k_codes"].cpu().numpy()[:, :, :nf * FS], kc)
+    gk = views["k_codes"].cpu().numpy()
+    np.testing.assert_array_equal(gk[:, :, :nf * FS], kc)
+    assert not gk[:, :, nf * FS:].any()
     np.testing.assert_array_equal(views["k_scale"].cpu().numpy()[:, :, :nf * FS // BK], dk)
     qc, dq = quant.quantize_q(Q, a)
-    np.testing.assert_array_equal(views["q_codes"].cpu().numpy()[:, :, :F], qc)
+    np.testing.assert_array_equal(views["q_codes"].cpu().numpy()[:, :, :Nq], qc)
+    np.testing.assert_array_equal(views["q_scale"].cpu().numpy()[:, :, :dq.shape[2]], dq)
     untiled = views["v_t"].cpu().permute(0, 1, 2, 4, 3).reshape(B, H, -1, d).numpy()
     if pv_mode == PV_FP8:
         vc, ve = quant.quantize_v_fp8_frames(V, F, FS)
@@ -121,6 +87,16 @@ def test_frame_cache_quantize_bit_exact(lib, pv_mode):
     else:
         ref = codecs.bf16_bits(quant.to_frame_slots(V, F, FS))
         np.testing.assert_array_equal(untiled.view(np.uint16)[:, :, :nf * FS], ref)
+
+
+@pytest.mark.parametrize("pv_mode", [PV_16, PV_FP8])
+def test_frame_cache_quantize_bit_exact(lib, pv_mode):
+    B, H, d, F, FS, nf = 2, 2, 128, 200, 256, 5
+    q, k, v = _inputs(B, H, F, nf * F, d, torch.bfloat16, 61)
+    Q, K, V = host(q), host(k), host(v)
+    mu, a = _frozen(Q, K)
+    _, desc, ws, bufs = _run(q.cuda(), k.cuda(), v.cuda(), pv_mode, F, FS, nf * FS, mu=mu, a=a)
+    check_cache_operands(sage.quant_views(desc, ws, bufs), Q, K, V, mu, a, F, FS, pv_mode)
 
 
 @pytest.mark.parametrize("pv_mode", [PV_16, PV_FP8])
@@ -215,3 +191,58 @@ def test_cache_without_padding_or_window_equals_contiguous(lib, pv_mode):
     sage.sage_attn_fwd_quantized(desc, bufs, o2)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("pv_mode", [PV_16, PV_FP8], ids=["pv16", "pvfp8"])
+def test_window_workload_parity(lib, pv_mode):
+    """The window workload at full size (B1 H24, 41 cached 2040-token frames at
+    a stride of 2048 slots, queries = frame 40, 1 sink + 16 window frames) in
+    the launch configuration bench.py times: the whole cache quantized once
+    (the library computes the mean and exponents), the current frame and the
+    queries quantized again through sage_attn_quantize_frames, then attention
+    with the library-chosen KV splits.  Bit-exact operands on all heads;
+    outputs of 3 seeded heads on sampled rows against the emulation, cosine
+    against float64 windowed attention."""
+    w = workloads.get("window", pv_mode=pv_mode)
+    print(f"workload window pv {pv_mode}", flush=True)
+    x = workloads.make(w, "cuda")
+    q, k, v = x["q"], x["k"], x["v"]
+    o = torch.empty_like(q)
+    F, FS, S, W = w.frame_len, w.frame_stride, w.sink_frames, w.window_frames
+    kvl, qp = w.kv_lens(), w.q_pos0s()
+    desc = sage.Desc.for_tensors(q, k, v, o, nkv=w.Nkv, pv_mode=pv_mode, frame_len=F, frame_stride=FS,
+                                 sink_frames=S, window_frames=W, kv_len=kvl, q_pos0=qp)
+    ws = sage.new_workspace(desc, q.device)
+    bufs = sage.sage_attn_quant_layout(desc, ws)
+    sage.sage_attn_quantize(desc, q, k, v, bufs)
+    fq = qp[0] // F
+    kk, vv = k[:, :, fq * F:(fq + 1) * F], v[:, :, fq * F:(fq + 1) * F]
+    d2 = sage.Desc.for_tensors(q, kk, vv, nkv=w.Nkv, pv_mode=pv_mode, frame_len=F, frame_stride=FS)
+    sage.sage_attn_quantize_frames(d2, q, kk, vv, fq, 1, bufs)
+    sage.sage_attn_fwd_quantized(desc, bufs, o)
+    torch.cuda.synchronize()
+    views = sage.quant_views(desc, ws, bufs)
+    Q, K, V = host(q), host(k), host(v)
+    mu = quant.k_mean(K)
+    np.testing.assert_array_equal(views["k_mean"].cpu().numpy(), mu)
+    a = quant.channel_shift(Q, K, mu)
+    check_cache_operands(views, Q, K, V, mu, a, F, FS, pv_mode)
+    hs = sorted(np.random.default_rng(2000).choice(w.H, 3, replace=False).tolist())
+    rows = workloads.sample_rows(w, 96)
+    nsplit = sage.sage_attn_kv_splits(desc)
+    Qh, Kh, Vh = Q[:, hs], K[:, hs], V[:, hs]
+    args = (pv_mode, w.dtype, F, FS, S, W, kvl, qp, mu[:, hs], a[:, hs], nsplit)
+    o64 = emulate.emulate_frame_cache(Qh, Kh, Vh, *args, rows=rows)
+    o_abs = emulate.emulate_frame_cache(Qh, Kh, np.abs(Vh), *args, rows=rows) if pv_mode == PV_FP8 else None
+    og = host(o[:, hs])[:, :, rows]
+    mx, excess, frac, rel, rel_bound = compare_output(og, o64, w.dtype, pv_mode, o_abs)
+    print(f"  heads {hs} splits {nsplit}: max-abs {mx:.2e} excess {excess:.2e} beyond-rounding {frac:.2e} "
+          f"rel-L2 {rel:.2e}", flush=True)
+    assert excess <= 0
+    assert rel <= rel_bound
+    ref = attention.attention_fp64(Qh, Kh, Vh, frame_len=F, kv_len=kvl, q_pos0=qp, rows=rows,
+                                   sink_frames=S, window_frames=W)
+    cs = cosine(og, ref)
+    print(f"  cosine vs fp64 windowed attention {cs:.6f}", flush=True)
+    assert cs >= (0.999 if pv_mode == PV_16 else 0.998)

@@ -163,3 +163,47 @@ def test_cache_emulation_equals_attention_on_dequantized_operands(pv_mode, eps):
     ref = attention.attention_fp64(Qd, Kd, Vh, 0.3, frame_len=F, kv_len=[nf * F], q_pos0=[q0],
                                    sink_frames=S, window_frames=W)
     assert np.abs(o64 - ref).max() <= 2 * eps * np.abs(Vh).max() * 1.01
+
+
+@pytest.mark.parametrize("F,FS,S,W,q0f,first,last,nsplit", [
+    (200, 256, 1, 3, 7, 0, 127, 1), (200, 256, 1, 3, 7, 128, 199, 3), (100, 128, 2, 2, 6, 0, 127, 4),
+    (64, 64, 4, 1, 1, 0, 63, 2), (150, 192, 2, 1, 8, 0, 127, 2), (200, 256, 0, 0, 5, 0, 127, 3),
+    (2040, 2048, 1, 16, 40, 1920, 2039, 3)])
+def test_cache_tile_splits_cover_exactly_the_visible_chunks(F, FS, S, W, q0f, first, last, nsplit):
+    """Brute force over slots: the split ranges are disjoint and ascending, they
+    cover every chunk holding a slot that some row of the tile sees, and every
+    chunk they cover that lies outside the tile's list is invisible to all of
+    its rows."""
+    kv, q0 = (q0f + 1) * F, q0f * F
+    nslots = (q0f + 1) * FS
+    rows = np.arange(first, last + 1)
+    vis = emulate.visible_slots(rows, nslots, kv, q0, F, FS, S, W)
+    vis_chunk = vis.reshape(len(rows), -1, BK).any(axis=(0, 2))
+    sp = emulate.cache_tile_splits(first, last, q0, kv, F, FS, S, W, nsplit)
+    covered = np.zeros(vis_chunk.size, bool)
+    prev_hi = 0
+    for lo, hi in sp:
+        assert prev_hi <= lo < hi
+        covered[lo:hi] = True
+        prev_hi = hi
+    assert not (vis_chunk & ~covered).any()
+    assert len(sp) == min(nsplit, int(covered.sum()))
+
+
+def test_cache_emulation_splits_merge_to_the_unsplit_result():
+    """Each split work item keeps its own running max, so P is rounded against
+    another reference than in one pass: the merged result differs from the
+    unsplit one only within P's rounding (2^-8 relative in 16-bit mode, on
+    each side of textbook attention on the same operands)."""
+    rng = np.random.default_rng(47)
+    F, FS, nf, S, W, d = 150, 192, 6, 1, 3, 32
+    Q = _rnd16(rng.standard_normal((1, 2, 2 * F, d)))
+    K = _rnd16(rng.standard_normal((1, 2, nf * F, d)))
+    V = _rnd16(rng.standard_normal((1, 2, nf * F, d)))
+    mu = quant.k_mean(K)
+    a = quant.channel_shift(Q, K, mu)
+    args = (Q, K, V, PV_16, "bf16", F, FS, S, W, [nf * F], [(nf - 2) * F], mu, a)
+    o1 = emulate.emulate_frame_cache(*args, 1)
+    o3 = emulate.emulate_frame_cache(*args, 3, rows=np.arange(0, 2 * F, 7))
+    assert np.abs(o3 - o1[:, :, ::7]).max() <= 2 * 2 * 2.0 ** -8 * np.abs(V).max()
+    assert not np.array_equal(o3, o1[:, :, ::7])  # the split ranges were really taken
