@@ -4,7 +4,12 @@
 
 One step = one sage_attn_fwd call: the quantize pass (K mean, channel balance,
 INT8 Q/K codes and scales, V layout) plus the fused attention kernel, over the
-workload's whole batch, with the inputs already resident in HBM.  Prints ONE
+workload's whole batch, with the inputs already resident in HBM.  On a frame
+cache (--workload window) a step is one streaming step instead: the current
+frame's K and V and the queries quantized into the cache once
+(sage_attn_quantize_frames, against the frozen mean and exponents of the
+cache's first quantization) plus the fused kernel over the sink and window
+frames; the whole-cache quantization is timed beside it.  Prints ONE
 JSON line: TOPS = 4*d*(visible query-key pairs) / time, the roofline of the
 dominant kernel (the fused attention, timed with HIP events on its own stream;
 its HBM traffic from the committed rocprofv3 counters when they were taken on
@@ -64,19 +69,37 @@ def kernel_traffic(workload, pv):
     return None if rec is None else rec["bytes"]
 
 
-def time_path(sage, torch, desc, q, k, v, o, bufs, stream, steps, warm):
+def step_parts(sage, w, desc, q, k, v, o, bufs, stream):
+    """The two halves of one step as callables: (quantize, attend)."""
+    if not w.frame_stride:
+        return (lambda: sage.sage_attn_quantize(desc, q, k, v, bufs, stream),
+                lambda: sage.sage_attn_fwd_quantized(desc, bufs, o, stream))
+    # streaming step: the current frame (every batch is at the same frame) and
+    # the queries into the cache
+    F = w.frame_len
+    fq = w.q_pos0s()[0] // F
+    assert all(p // F == fq for p in w.q_pos0s())
+    kk, vv = k[:, :, fq * F:(fq + 1) * F], v[:, :, fq * F:(fq + 1) * F]
+    d2 = sage.Desc.for_tensors(q, kk, vv, nkv=w.Nkv, pv_mode=desc.pv_mode, frame_len=F,
+                               frame_stride=w.frame_stride)
+    return (lambda: sage.sage_attn_quantize_frames(d2, q, kk, vv, fq, 1, bufs, stream),
+            lambda: sage.sage_attn_fwd_quantized(desc, bufs, o, stream))
+
+
+def time_path(torch, parts, stream, steps, warm):
     """Warm up, then time `steps` whole steps (quantize + fused kernel) with HIP
     events on the launch stream around each part.  Returns ms per step, per
     quantize pass and per fused-kernel launch."""
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    quant, attend = parts
 
     def step(i=None):
         if i is not None:
             ev[i][0].record(stream)
-        sage.sage_attn_quantize(desc, q, k, v, bufs, stream)
+        quant()
         if i is not None:
             ev[i][1].record(stream)
-        sage.sage_attn_fwd_quantized(desc, bufs, o, stream)
+        attend()
         if i is not None:
             ev[i][2].record(stream)
 
@@ -122,9 +145,17 @@ def main():
 
     def setup(pv_mode):
         desc = sage.Desc.for_tensors(q, k, v, o, pv_mode=pv_mode, frame_len=w.frame_len,
-                                     kv_len=w.kv_len, q_pos0=w.q_pos0)
+                                     kv_len=w.kv_len, q_pos0=w.q_pos0,
+                                     **(dict(nkv=w.Nkv, frame_stride=w.frame_stride,
+                                             sink_frames=w.sink_frames, window_frames=w.window_frames)
+                                        if w.frame_stride else {}))
         ws = sage.new_workspace(desc, dev)
-        return desc, ws, sage.sage_attn_quant_layout(desc, ws)
+        bufs = sage.sage_attn_quant_layout(desc, ws)
+        if w.frame_stride:
+            # the cache as the stream has built it: every frame quantized once,
+            # the mean and exponents computed here and frozen from now on
+            sage.sage_attn_quantize(desc, q, k, v, bufs, stream)
+        return desc, ws, bufs
 
     if args.calibrate_copy:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
@@ -137,7 +168,7 @@ def main():
     if not (args.profile or args.single_mode):
         # the other P.V mode first, so that the headline mode's output stays in `o`
         desc2, ws2, bufs2 = setup(1 - w.pv_mode)
-        t2 = time_path(sage, torch, desc2, q, k, v, o, bufs2, stream, steps, warm)
+        t2 = time_path(torch, step_parts(sage, w, desc2, q, k, v, o, bufs2, stream), stream, steps, warm)
         other = {"pv": "fp8" if w.pv_mode == 0 else "16",
                  "value": round(ops / (t2[0] * 1e-3) / 1e12, 2),
                  "attn_tops": round(ops / (t2[2] * 1e-3) / 1e12, 2),
@@ -146,20 +177,29 @@ def main():
             other["accuracy"] = accuracy_sample(w, x, o, desc2, 1 - w.pv_mode, sage)
         del ws2, bufs2
     desc, ws, bufs = setup(w.pv_mode)
-    ms_step, ms_quant, ms_attn = time_path(sage, torch, desc, q, k, v, o, bufs, stream, steps, warm)
+    ms_step, ms_quant, ms_attn = time_path(torch, step_parts(sage, w, desc, q, k, v, o, bufs, stream),
+                                           stream, steps, warm)
     tops = ops / (ms_step * 1e-3) / 1e12
+    ms_full_quant = None
+    if w.frame_stride:
+        # what re-quantizing the whole cache would cost per step
+        qfull = (lambda: sage.sage_attn_quantize(desc, q, k, v, bufs, stream), lambda: None)
+        ms_full_quant = time_path(torch, qfull, stream, steps, warm)[1]
 
     splits = sage.sage_attn_kv_splits(desc)
     attn_tops = ops / (ms_attn * 1e-3) / 1e12
     pvname = "fp8" if w.pv_mode == 1 else "16"
     traffic = kernel_traffic(w.name, pvname)
     # quantize pass algorithmic bytes: read Q, K twice (statistics, then codes),
-    # V once; write Q/K codes, V layout (16-bit or e4m3) and scales
+    # V once; write Q/K codes, V layout (16-bit or e4m3) and scales.  A
+    # streaming step reads each of the frame's K, V and the queries once.
     esz = 2
     nq = w.B * w.H * w.Nq * w.d
-    nk = w.B * w.H * w.Nkv * w.d
+    nk = w.B * w.H * (w.frame_stride if w.frame_stride else w.Nkv) * w.d
     vbytes = nk * (1 if w.pv_mode == 1 else 2)
     qbytes = 2 * nq * esz + 2 * nk * esz + nk * esz + nq + nk + vbytes
+    if w.frame_stride:
+        qbytes = nq * esz + 2 * w.B * w.H * w.frame_len * w.d * esz + nq + nk + vbytes
     record = {
         "metric": METRIC,
         "value": round(tops, 2),
@@ -176,6 +216,9 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nkv": w.Nkv, "d": w.d,
                    "in_dtype": w.dtype, "pv": pvname,
                    "frame_len": w.frame_len, "kv_splits": splits,
+                   **({"frame_stride": w.frame_stride, "sink_frames": w.sink_frames,
+                       "window_frames": w.window_frames, "kv_len": w.kv_lens(), "q_pos0": w.q_pos0s()}
+                      if w.frame_stride else {}),
                    "ops_per_step": ops, "pct_int8_peak": round(100 * tops / INT8_PEAK_TOPS, 2)},
         "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel", "achieved": round(attn_tops, 2),
                      "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s", "frac": round(attn_tops / INT8_PEAK_TOPS, 4),
@@ -184,6 +227,9 @@ def main():
                      "GB_per_s": round(qbytes / (ms_quant * 1e-3) / 1e9, 1),
                      "hbm_frac": round(qbytes / (ms_quant * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
     }
+    if ms_full_quant is not None:
+        record["quantize"]["kind"] = "append one frame + queries (sage_attn_quantize_frames)"
+        record["quantize"]["whole_cache_ms"] = round(ms_full_quant, 4)
     if other is not None:
         record["other_pv_mode"] = other
     if not args.no_cpu and not args.profile:
@@ -191,10 +237,32 @@ def main():
     print(json.dumps(record), flush=True)
 
 
+def oracle_sample(w, Q, K, V, pv_mode, b, rows, S):
+    """The oracle on a sample of batch b (Q, K, V: host arrays of some heads):
+    (emulated output with the kernel's KV splits, float64 attention, seconds
+    the emulation -- quantization included -- took)."""
+    from oracle import emulate, attention, quant
+    kv, qp = [w.kv_lens()[b]], [w.q_pos0s()[b]]
+    t0 = time.perf_counter()
+    if w.frame_stride:
+        mu = quant.k_mean(K)
+        a = quant.channel_shift(Q, K, mu)
+        o64 = emulate.emulate_frame_cache(Q, K, V, pv_mode, w.dtype, w.frame_len, w.frame_stride,
+                                          w.sink_frames, w.window_frames, kv, qp, mu, a, S, rows=rows)
+    else:
+        n = -(-kv[0] // 64)
+        splits = [(s * n // S, (s + 1) * n // S) for s in range(S)] if S > 1 else None
+        o64, _ = emulate.emulate_from_inputs(Q, K, V, pv_mode, w.dtype, frame_len=w.frame_len, kv_len=kv,
+                                             q_pos0=qp, rows=rows, splits=splits)
+    t_emul = time.perf_counter() - t0
+    ref = attention.attention_fp64(Q, K, V, frame_len=w.frame_len, kv_len=kv, q_pos0=qp, rows=rows,
+                                   sink_frames=w.sink_frames, window_frames=w.window_frames)
+    return o64, ref, t_emul
+
+
 def accuracy_sample(w, x, o, desc, pv_mode, sage, heads=2, rows=256):
     """Cosine against float64 attention and max-abs against the emulation on a
     small sample (the first `heads` heads of batch 0, `rows` seeded rows)."""
-    from oracle import emulate, attention
     import workloads
     hs = list(range(min(heads, w.H)))
     r = workloads.sample_rows(w, rows)
@@ -202,12 +270,7 @@ def accuracy_sample(w, x, o, desc, pv_mode, sage, heads=2, rows=256):
     Q = x["q"][0:1, hs].float().cpu().numpy()
     K = x["k"][0:1, hs].float().cpu().numpy()
     V = x["v"][0:1, hs].float().cpu().numpy()
-    kv, qp = [w.kv_lens()[0]], [w.q_pos0s()[0]]
-    n = -(-kv[0] // 64)
-    splits = [(s * n // S, (s + 1) * n // S) for s in range(S)] if S > 1 else None
-    o64, _ = emulate.emulate_from_inputs(Q, K, V, pv_mode, w.dtype, frame_len=w.frame_len, kv_len=kv,
-                                         q_pos0=qp, rows=r, splits=splits)
-    ref = attention.attention_fp64(Q, K, V, frame_len=w.frame_len, kv_len=kv, q_pos0=qp, rows=r)
+    o64, ref, _ = oracle_sample(w, Q, K, V, pv_mode, 0, r, S)
     og = o[0:1, hs][:, :, r].float().cpu().numpy()
     cos = float((og * ref).sum() / np.sqrt((og ** 2).sum() * (ref ** 2).sum()))
     return {"rows": len(r) * len(hs), "max_abs_vs_emulation": float(np.abs(og - o64).max()),
@@ -218,7 +281,6 @@ def cpu_leg(w, x, o, desc, args, sage, torch):
     """Time the oracle (as it stands) on a bounded sample of the same workload,
     and compare the GPU output on the same rows."""
     from threadpoolctl import threadpool_info
-    from oracle import emulate, attention
     import workloads
 
     heads = list(range(min(args.cpu_heads, w.H)))
@@ -228,24 +290,15 @@ def cpu_leg(w, x, o, desc, args, sage, torch):
     Q = x["q"][b:b + 1, heads].float().cpu().numpy()
     K = x["k"][b:b + 1, heads].float().cpu().numpy()
     V = x["v"][b:b + 1, heads].float().cpu().numpy()
-    kv = [w.kv_lens()[b]]
-    qp = [w.q_pos0s()[b]]
-    n = -(-kv[0] // 64)
-    splits = [(s * n // S, (s + 1) * n // S) for s in range(S)] if S > 1 else None
-    t0 = time.perf_counter()
-    o64, _ = emulate.emulate_from_inputs(Q, K, V, w.pv_mode, w.dtype, frame_len=w.frame_len, kv_len=kv,
-                                         q_pos0=qp, rows=rows, splits=splits)
-    t_cpu = time.perf_counter() - t0
-    ref = attention.attention_fp64(Q, K, V, frame_len=w.frame_len, kv_len=kv, q_pos0=qp, rows=rows)
+    o64, ref, t_cpu = oracle_sample(w, Q, K, V, w.pv_mode, b, rows, S)
     og = o[b:b + 1, heads][:, :, rows].float().cpu().numpy()
-    i = np.asarray(rows)
-    ends = np.minimum(kv[0], ((qp[0] + i) // w.frame_len + 1) * w.frame_len) if w.frame_len else np.full(len(i), kv[0])
-    sample_ops = 4 * w.d * int(ends.sum()) * len(heads)
+    sample_ops = 4 * w.d * int(w.row_keys(b, rows).sum()) * len(heads)
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     cos = float((og * ref).sum() / np.sqrt((og ** 2).sum() * (ref ** 2).sum()))
     cpu = {"value": round(sample_ops / t_cpu / 1e12, 6), "unit": "TOPS", "cores": threads, "kind": "oracle",
            "sample": f"batch 0, heads {heads[0]}..{heads[-1]}, {len(rows)} query rows each "
-                     f"(all keys), quantize + emulated attention, {t_cpu:.1f} s"}
+                     f"(all their visible keys), quantize + emulated attention, "
+                     f"{t_cpu:.1f} s"}
     parity = {"rows": len(rows) * len(heads), "max_abs_vs_emulation": float(np.abs(og - o64).max()),
               "cosine_vs_fp64": round(cos, 6)}
     return cpu, parity

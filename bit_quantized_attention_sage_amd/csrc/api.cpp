@@ -35,16 +35,59 @@ struct Plan {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Key chunks that query tile t of batch b visits (the fused kernel's list).
+int tile_chunks(const Plan& p, int b, int t) {
+  const int kv = p.bi.kv_len[b], qp = p.bi.q_pos0[b], F = p.frame_len;
+  const int first = t * 128, last = std::min(t * 128 + 128, p.Nq) - 1;
+  if (p.frame_stride == 0) {
+    const int end = F > 0 ? std::min(kv, ((qp + last) / F + 1) * F) : kv;
+    return (end + 63) / 64;
+  }
+  const int cpf = p.frame_stride / 64;
+  const int fq_lo = (qp + first) / F, fq_hi = (qp + last) / F;
+  const int end = (fq_hi * p.frame_stride + std::min(F, kv - fq_hi * F) + 63) / 64;
+  if (p.window_frames == 0) return end;
+  const int a0 = std::min(std::min(p.sink_frames, fq_hi + 1) * cpf, end);
+  const int b1 = std::max(std::min(std::max(p.sink_frames, fq_lo - p.window_frames) * cpf, end), a0);
+  return a0 + (end - b1);
+}
+
+// KV splits per query tile.  Work items (batch, head, split, tile) run as
+// rounds of SLOTS resident workgroups (256 CUs x 2), so the estimated time of
+// s splits is ceil(items / SLOTS) x (mean chunks per item + a prologue and
+// epilogue of about 3 chunk steps), plus for s > 1 the combine pass (reads
+// s fp32 partial outputs; one chunk step of a workgroup takes about 1.5 us at
+// d = 128, half that at d = 64).  Enough tiles for 4 rounds: no split.
 int choose_splits(const Plan& p) {
-  const int64_t work = static_cast<int64_t>(p.B) * p.H * (p.Nq_pad / 128);
-  int maxkv = 0;
-  for (int b = 0; b < p.B; ++b) maxkv = std::max(maxkv, p.bi.kv_len[b]);
-  const int nch = (maxkv + 63) / 64;
-  if (work >= 768) return 1;
-  int s = static_cast<int>((1024 + work - 1) / work);
-  s = std::min(s, nch / 8);
-  s = std::min(s, SAGE_MAX_SPLITS);
-  return std::max(s, 1);
+  constexpr int SLOTS = 512;
+  const int nqt = p.Nq_pad / 128;
+  const int64_t items1 = static_cast<int64_t>(p.B) * p.H * nqt;
+  if (items1 >= 4 * SLOTS) return 1;
+  double total = 0.0;
+  int longest = 1;
+  for (int b = 0; b < p.B; ++b)
+    for (int t = 0; t < nqt; ++t) {
+      const int n = tile_chunks(p, b, t);
+      total += n;
+      longest = std::max(longest, n);
+    }
+  const double mean = total / (static_cast<double>(p.B) * nqt);
+  const double chunk_us = 1.5 * p.d / 128.0;
+  int best = 1;
+  double best_cost = 0.0;
+  for (int s = 1; s <= SAGE_MAX_SPLITS && s <= std::max(1, longest / 8); ++s) {
+    const int64_t items = items1 * s;
+    double cost = static_cast<double>((items + SLOTS - 1) / SLOTS) * (mean / s + 3.0);
+    if (s > 1) {
+      const double bytes = static_cast<double>(s) * p.B * p.H * p.Nq_pad * (p.d + 2) * 4.0;
+      cost += bytes / 4e12 / (chunk_us * 1e-6) + 4.0;
+    }
+    if (s == 1 || cost < 0.98 * best_cost) {
+      best = s;
+      best_cost = cost;
+    }
+  }
+  return best;
 }
 
 // Validate *d and fill *p.  Pure host code; touches no device memory.

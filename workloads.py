@@ -19,6 +19,13 @@ stand in for them, with the token grids of such clips:
   batched  B8 H24 Nq 2040, each session's cache L_b ~ U{4..32} frames plus its
            own frame (kv_len = (L_b+1)*2040), KV allocated for 33 frames,
            d128 bf16, frame-block-causal, P.V in FP8
+  window   streaming step over a frame cache (Vidu S1 blog, section "Infra":
+           a fixed window of sink frames, recent history and the current
+           frame): B1 H24 d128 bf16, 2040-token frames at a stride of 2048
+           cache slots, 48 frames allocated, frames 0..40 cached, the
+           queries are frame 40; 1 sink frame and a 16-frame window, so each
+           query sees 18 frames (36720 keys).  The pages give no window
+           length; 16 frames matches the stream workload's history.
 
 Values are N(0,1) float32, then rounded to the 16-bit dtype.  Each (tensor,
 batch, head) slice has its own seed, so any subset of heads can be drawn on
@@ -52,6 +59,9 @@ class Workload:
     k_offset_std: float = 0.0
     outlier_frac: float = 0.0
     outlier_gain: float = 8.0
+    frame_stride: int = 0      # > 0: K/V live in a frame cache of Nkv slots
+    sink_frames: int = 0
+    window_frames: int = 0
     extra: dict = field(default_factory=dict)
 
     @property
@@ -61,6 +71,12 @@ class Workload:
     def kv_lens(self):
         return list(self.kv_len) if self.kv_len is not None else [self.Nkv] * self.B
 
+    @property
+    def kv_tokens(self):
+        """Rows of the K and V input tensors: Nkv, or with a frame cache the
+        longest batch's tokens (whole frames, before the slot layout)."""
+        return max(self.kv_lens()) if self.frame_stride else self.Nkv
+
     def q_pos0s(self):
         if self.q_pos0 is not None:
             return list(self.q_pos0)
@@ -68,17 +84,25 @@ class Workload:
             return [0] * self.B
         return [kv - self.Nq for kv in self.kv_lens()]
 
+    def row_keys(self, b, rows=None):
+        """Visible keys of each query row (all rows when None) of batch b."""
+        kv, qp = self.kv_lens()[b], self.q_pos0s()[b]
+        i = np.arange(self.Nq, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
+        if self.window_frames:
+            F = self.frame_len
+            fq = (qp + i) // F
+            n = np.zeros(len(i), np.int64)
+            for f in range(int(fq.max()) + 1):
+                seen = (f <= fq) & ((f < self.sink_frames) | (f >= fq - self.window_frames))
+                n += seen * max(0, min(F, kv - f * F))
+            return n
+        if self.frame_len:
+            return np.minimum(kv, ((qp + i) // self.frame_len + 1) * self.frame_len)
+        return np.full(len(i), kv, dtype=np.int64)
+
     def visible_pairs(self):
         """Number of visible (query, key) pairs over all batches and heads."""
-        total = 0
-        for kv, qp in zip(self.kv_lens(), self.q_pos0s()):
-            i = np.arange(self.Nq, dtype=np.int64)
-            if self.frame_len:
-                end = np.minimum(kv, ((qp + i) // self.frame_len + 1) * self.frame_len)
-            else:
-                end = np.full(self.Nq, kv, dtype=np.int64)
-            total += int(end.sum())
-        return total * self.H
+        return self.H * sum(int(self.row_keys(b).sum()) for b in range(self.B))
 
     def ops(self):
         """Algorithmic operations: 4*d per visible pair (QK^T and P.V)."""
@@ -104,6 +128,10 @@ def get(name, **override):
         w = Workload("batched", 8, 24, FRAME, 33 * FRAME, 128, "bf16", 1,
                      frame_len=FRAME, kv_len=kv, q_pos0=[int(x * FRAME) for x in L],
                      seed=505)
+    elif name == "window":
+        w = Workload("window", 1, 24, FRAME, 48 * 2048, 128, "bf16", 0,
+                     frame_len=FRAME, kv_len=[41 * FRAME], q_pos0=[40 * FRAME], seed=606,
+                     frame_stride=2048, sink_frames=1, window_frames=16)
     else:
         raise KeyError(name)
     for k, v in override.items():
@@ -111,7 +139,7 @@ def get(name, **override):
     return w
 
 
-NAMES = ("tiny", "small", "large", "stream", "batched")
+NAMES = ("tiny", "small", "large", "stream", "batched", "window")
 
 
 def _slice_seed(seed, tensor, b, h):
@@ -139,7 +167,7 @@ def outlier_channels(w):
 def make(w, device="cpu", heads=None, batches=None, tensors="qkv"):
     """Draw the inputs of workload ``w`` on ``device``.
 
-    Returns a dict with 'q' [B,H,Nq,d], 'k' and 'v' [B,H,Nkv,d] in the
+    Returns a dict with 'q' [B,H,Nq,d], 'k' and 'v' [B,H,kv_tokens,d] in the
     workload's 16-bit dtype (only the requested tensors), restricted to the
     given heads / batches when those are lists.  Key positions at or beyond
     kv_len[b] are zero.
@@ -153,7 +181,7 @@ def make(w, device="cpu", heads=None, batches=None, tensors="qkv"):
     kvl = w.kv_lens()
     out = {}
     for name in tensors:
-        n = w.Nq if name == "q" else w.Nkv
+        n = w.Nq if name == "q" else w.kv_tokens
         t = torch.empty((len(batches), len(heads), n, w.d), dtype=w.torch_dtype, device=device)
         for bi, b in enumerate(batches):
             for hi, h in enumerate(heads):
