@@ -25,9 +25,21 @@ here, with S sink frames and W window frames: key frame fk is visible from
 query frame fq iff fk <= fq and (W == 0 or fk < S or fk >= fq - W), i.e. the
 first S frames, the W most recent history frames and the current frame;
 W == 0 keeps every earlier frame (the plain frame-block-causal mask).
+
+Block-sparse attention.  Sparse attention kernels (SpargeAttention, and the
+sparse branch of Sparse-Linear Attention, which can be built on top of
+SageAttention: Vidu S1 blog, section "Infra"; TurboDiffusion digests) skip
+whole (query block, key block) tiles that a predictor marks as negligible.
+The pages give neither the predictor nor a sparsity level, so the mask is an
+input here: block_mask[b, h, i // 128, j // 64] != 0 keeps the tile, and key
+j is visible from row i only if its tile is kept and the mask above allows
+it.  A row left with no visible key outputs 0 (the softmax of an empty set is
+undefined; the kernel's accumulators stay zero).
 """
 
 import numpy as np
+
+from .constants import BQ, BK
 
 
 def row_end(i_rows, kv_len_b, q_pos0_b, frame_len):
@@ -67,6 +79,15 @@ def visible(i_rows, Nkv, kv_len_b, q_pos0_b, frame_len, sink_frames=0, window_fr
     return vis
 
 
+def block_visible(vis, rows, block_mask_bh):
+    """vis [R, n] restricted to the kept (query block, key block) tiles of one
+    (b, h): block_mask_bh [ceil(Nq/128), ceil(Nkv/64)]."""
+    rows = np.asarray(rows, dtype=np.int64)
+    kb = np.arange(vis.shape[1], dtype=np.int64) // BK
+    keep = np.asarray(block_mask_bh)[(rows // BQ)[:, None], kb[None, :]] != 0
+    return vis & keep
+
+
 def default_q_pos0(Nq, kv_len, frame_len):
     """Absent an explicit q_pos0, the query chunk is the tail of the keys."""
     kv = np.asarray(kv_len, dtype=np.int64)
@@ -76,12 +97,14 @@ def default_q_pos0(Nq, kv_len, frame_len):
 
 
 def attention_fp64(Q, K, V, sm_scale=None, frame_len=0, kv_len=None,
-                   q_pos0=None, rows=None, sink_frames=0, window_frames=0):
+                   q_pos0=None, rows=None, sink_frames=0, window_frames=0,
+                   block_mask=None):
     """softmax(Q K^T * sm_scale + M) V in float64 for the selected rows.
 
     Q [B,H,Nq,d], K and V [B,H,Nkv,d] (any float dtype; widened exactly),
     tokens contiguous.  rows: indices of the query rows to compute (all when
-    None).
+    None).  block_mask: optional [B,H,ceil(Nq/128),ceil(Nkv/64)], nonzero =
+    tile kept; rows with no visible key give 0.
     Returns float64 [B,H,len(rows),d].
     """
     Q = np.asarray(Q, dtype=np.float64)
@@ -95,12 +118,13 @@ def attention_fp64(Q, K, V, sm_scale=None, frame_len=0, kv_len=None,
     rows = np.arange(Nq) if rows is None else np.asarray(rows, dtype=np.int64)
     out = np.empty((B, H, len(rows), d), dtype=np.float64)
     for b in range(B):
-        vis = visible(rows, Nkv, kv[b], qp[b], frame_len, sink_frames, window_frames)
+        vis_b = visible(rows, Nkv, kv[b], qp[b], frame_len, sink_frames, window_frames)
         for h in range(H):
+            vis = vis_b if block_mask is None else block_visible(vis_b, rows, block_mask[b, h])
             s = (Q[b, h, rows, :] @ K[b, h].T) * scale
             s = np.where(vis, s, -np.inf)
-            s = s - np.max(s, axis=1, keepdims=True)
-            w = np.exp(s)
-            w = w / np.sum(w, axis=1, keepdims=True)
-            out[b, h] = w @ V[b, h]
+            mx = np.max(s, axis=1, keepdims=True)
+            w = np.exp(s - np.where(np.isneginf(mx), 0.0, mx))
+            den = np.sum(w, axis=1, keepdims=True)
+            out[b, h] = np.where(den > 0, w @ V[b, h] / np.where(den > 0, den, 1.0), 0.0)
     return out

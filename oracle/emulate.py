@@ -166,7 +166,8 @@ def visible_slots(rows, n_slots, kv_len_b, q_pos0_b, frame_len, frame_stride,
 def sage_attention_emulated(qcodes, dq, kcodes, dk, Vhat, pv_mode, dtype,
                             sm_scale=None, frame_len=0, kv_len=None,
                             q_pos0=None, rows=None, splits=None,
-                            frame_stride=0, sink_frames=0, window_frames=0):
+                            frame_stride=0, sink_frames=0, window_frames=0,
+                            block_mask=None):
     """Emulate the quantized attention for the selected query rows.
 
     qcodes int8 [B,H,Nq,d], dq float32 [B,H,ceil(Nq/128)];
@@ -179,6 +180,11 @@ def sage_attention_emulated(qcodes, dq, kcodes, dk, Vhat, pv_mode, dtype,
     layout: frame f's tokens at slots f*frame_stride + [0, frame_len)); kv_len and
     q_pos0 stay in tokens; sink_frames / window_frames restrict the visible
     frames as in ``attention.visible``.
+    block_mask: optional [B,H,ceil(Nq/128),ceil(Nkv/64)] (contiguous keys);
+    chunks of dropped tiles are skipped -- they change neither m, l nor acc,
+    exactly as if they were absent -- and a row with no visible key gives 0.
+    splits then index the tile's list of kept chunks (see
+    ``sparse_tile_splits``).
     Returns (O64 float64 [B,H,R,d], O rounded to dtype as float32).
     """
     qcodes = np.asarray(qcodes)
@@ -195,6 +201,8 @@ def sage_attention_emulated(qcodes, dq, kcodes, dk, Vhat, pv_mode, dtype,
     out = np.empty((B, H, len(rows), d), dtype=np.float64)
     if window_frames and not frame_stride:
         raise ValueError("sink/window frames need the frame cache layout")
+    if block_mask is not None and frame_stride:
+        raise ValueError("a block mask needs contiguous keys")
     for b in range(B):
         if frame_stride:
             vis_end = visible_slots(rows, Nkv, kv[b], qp[b], frame_len, frame_stride,
@@ -206,19 +214,25 @@ def sage_attention_emulated(qcodes, dq, kcodes, dk, Vhat, pv_mode, dtype,
             vis_end = row_end(rows, kv[b], qp[b], frame_len)
             jmax = int(vis_end.max())
         for h in range(H):
+            vis_h = vis_end
+            if block_mask is not None:
+                from .attention import block_visible
+                vis_h = block_visible(np.arange(jmax)[None, :] < vis_end[:, None], rows, block_mask[b, h])
             qs = (dq[b, h, rows // BQ].astype(_F32) * sigma).astype(_F32)   # [R]
             S_full = qcodes[b, h, rows, :].astype(np.float64) @ \
                 kcodes[b, h, :jmax, :].astype(np.float64).T                # exact
             Vh = np.asarray(Vhat[b, h, :jmax, :], dtype=np.float64)
-            parts = [_run_rows(S_full, qs, dk[b, h], vis_end, Vh, lo, hi, pv_mode, dtype)
+            parts = [_run_rows(S_full, qs, dk[b, h], vis_h, Vh, lo, hi, pv_mode, dtype)
                      for (lo, hi) in splits]
             ms = np.stack([p[0] for p in parts]).astype(np.float64)        # [P, R]
             ls = np.stack([p[1] for p in parts])
             accs = np.stack([p[2] for p in parts])
             M = np.max(ms, axis=0)
-            w = np.where(np.isneginf(ms), 0.0, np.exp2(ms - M[None, :]))
+            with np.errstate(invalid="ignore"):   # rows with no key at all: M = -inf
+                w = np.where(np.isneginf(ms), 0.0, np.exp2(ms - M[None, :]))
             L = np.sum(w * ls, axis=0)
-            out[b, h] = np.sum(w[:, :, None] * accs, axis=0) / L[:, None]
+            num = np.sum(w[:, :, None] * accs, axis=0)
+            out[b, h] = np.where(L[:, None] > 0, num / np.where(L > 0, L, 1.0)[:, None], 0.0)
     rounded = codecs.round_to(out.astype(_F32), dtype)
     return out, rounded
 
@@ -237,7 +251,7 @@ def scores_int(qcodes, kcodes):
 def emulate_from_inputs(Q, K, V, pv_mode, dtype, sm_scale=None, frame_len=0,
                         kv_len=None, q_pos0=None, rows=None, splits=None,
                         mu=None, shift=None, frame_stride=0, sink_frames=0,
-                        window_frames=0):
+                        window_frames=0, block_mask=None):
     """Quantize the 16-bit inputs with ``quant`` and run the emulation.
 
     frame_stride > 0: K and V (tokens of whole frames from frame 0) go into a
@@ -269,7 +283,8 @@ def emulate_from_inputs(Q, K, V, pv_mode, dtype, sm_scale=None, frame_len=0,
     else:
         Vhat = Vf.astype(np.float64)
     return sage_attention_emulated(qc, dq, kc, dk, Vhat, pv_mode, dtype, sm_scale,
-                                   frame_len, kv_len, q_pos0, rows, splits)
+                                   frame_len, kv_len, q_pos0, rows, splits,
+                                   block_mask=block_mask)
 
 
 def cache_tile_splits(first, last, q_pos0_b, kv_len_b, frame_len, frame_stride,
@@ -338,4 +353,65 @@ def emulate_frame_cache(Q, K, V, pv_mode, dtype, frame_len, frame_stride, sink_f
                                              sp if nsplit > 1 else None, frame_stride,
                                              sink_frames, window_frames)
             out[b, :, sel] = o64[0].transpose(1, 0, 2)
+    return out
+
+
+def sparse_tile_splits(mask_row, n_chunks, nsplit):
+    """Chunk ranges of the split work items of one 128-query tile under a
+    block mask: the tile's list is its kept chunks among [0, n_chunks) (the
+    chunks its last row can see), in ascending order; split s takes entries
+    [s*n/nsplit, (s+1)*n/nsplit) of it, returned as the physical chunk range
+    that spans them (the dropped chunks inside are invisible to the tile)."""
+    kept = np.nonzero(np.asarray(mask_row)[:n_chunks] != 0)[0]
+    n = kept.size
+    out = []
+    for s in range(nsplit):
+        lo, hi = s * n // nsplit, (s + 1) * n // nsplit
+        if hi > lo:
+            out.append((int(kept[lo]), int(kept[hi - 1]) + 1))
+    return out
+
+
+def emulate_block_sparse(Q, K, V, pv_mode, dtype, block_mask, nsplit, frame_len=0, kv_len=None,
+                         q_pos0=None, rows=None, mu=None, shift=None):
+    """``emulate_from_inputs`` with a block mask, tile by tile of 128 query
+    rows, each tile with the chunk ranges of its split work items
+    (``sparse_tile_splits``).  Returns float64 O [B,H,R,d]."""
+    from . import quant
+    from .attention import row_end
+    Qf = np.asarray(Q, dtype=np.float32)
+    Kf = np.asarray(K, dtype=np.float32)
+    Vf = np.asarray(V, dtype=np.float32)
+    B, H, Nq, d = Qf.shape
+    Nkv = Kf.shape[2]
+    kv = np.full(B, Nkv, np.int64) if kv_len is None else np.asarray(kv_len, np.int64)
+    qp = default_q_pos0(Nq, kv, frame_len) if q_pos0 is None else np.asarray(q_pos0, np.int64)
+    rows = np.arange(Nq) if rows is None else np.asarray(rows, dtype=np.int64)
+    if mu is None:
+        mu = quant.k_mean(Kf, kv)
+    a = quant.channel_shift(Qf, Kf, mu, kv) if shift is None else shift
+    qc, dq = quant.quantize_q(Qf, a)
+    kc, dk = quant.quantize_k(Kf, mu, kv, a)
+    if pv_mode == PV_FP8:
+        vc, ve, _ = quant.quantize_v_fp8(Vf, kv)
+        Vhat = quant.dequant_v_fp8(vc, ve)
+    else:
+        Vhat = Vf.astype(np.float64)
+    out = np.empty((B, H, len(rows), d))
+    for b in range(B):
+        for t in np.unique(rows // BQ):
+            sel = np.nonzero(rows // BQ == t)[0]
+            last = min(t * BQ + BQ, Nq) - 1
+            nch = -(-int(row_end([last], kv[b], qp[b], frame_len)[0]) // BK)
+            for h in range(H):
+                sp = sparse_tile_splits(block_mask[b, h, t], nch, nsplit)
+                if not sp:
+                    out[b, h, sel] = 0.0
+                    continue
+                o64, _ = sage_attention_emulated(qc[b:b + 1, h:h + 1], dq[b:b + 1, h:h + 1], kc[b:b + 1, h:h + 1],
+                                                 dk[b:b + 1, h:h + 1], Vhat[b:b + 1, h:h + 1], pv_mode, dtype,
+                                                 None, frame_len, [kv[b]], [qp[b]], rows[sel],
+                                                 sp if nsplit > 1 else None,
+                                                 block_mask=block_mask[b:b + 1, h:h + 1])
+                out[b, h, sel] = o64[0, 0]
     return out
