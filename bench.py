@@ -9,7 +9,9 @@ cache (--workload window) a step is one streaming step instead: the current
 frame's K and V and the queries quantized into the cache once
 (sage_attn_quantize_frames, against the frozen mean and exponents of the
 cache's first quantization) plus the fused kernel over the sink and window
-frames; the whole-cache quantization is timed beside it.  Prints ONE
+frames; the whole-cache quantization is timed beside it.  With a block mask
+(--workload sparse) the fused kernel skips the dropped tiles and TOPS counts
+the kept visible pairs only.  Prints ONE
 JSON line: TOPS = 4*d*(visible query-key pairs) / time, the roofline of the
 dominant kernel (the fused attention, timed with HIP events on its own stream;
 its HBM traffic from the committed rocprofv3 counters when they were taken on
@@ -42,8 +44,10 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="large")
     p.add_argument("--pv", default=None, choices=["16", "fp8"])
-    p.add_argument("--cpu-heads", type=int, default=8, help="heads in the CPU oracle sample")
-    p.add_argument("--cpu-rows", type=int, default=512, help="query rows per head in the CPU sample")
+    p.add_argument("--cpu-heads", type=int, default=None,
+                   help="heads in the CPU oracle sample (default 8; 2 with a block mask)")
+    p.add_argument("--cpu-rows", type=int, default=None,
+                   help="query rows per head in the CPU sample (default 512; 128 with a block mask)")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--profile", action="store_true", help="few steps, no CPU leg (for rocprofv3)")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -132,6 +136,11 @@ def main():
 
     sage.load()
     w = workloads.get(args.workload)
+    # the block-sparse emulation runs tile by tile: a smaller sample keeps it to tens of seconds
+    if args.cpu_heads is None:
+        args.cpu_heads = 2 if w.block_density else 8
+    if args.cpu_rows is None:
+        args.cpu_rows = 128 if w.block_density else 512
     if args.pv is not None:
         w.pv_mode = 1 if args.pv == "fp8" else 0
     dev = torch.device("cuda:0")
@@ -139,13 +148,15 @@ def main():
     x = workloads.make(w, dev)
     q, k, v = x["q"], x["k"], x["v"]
     o = torch.empty_like(q)
+    mask = workloads.block_mask(w)
+    mask_dev = torch.from_numpy(mask).to(dev) if mask is not None else None
     stream = torch.cuda.current_stream()
     steps = 2 if args.profile else args.steps
     warm = 1 if args.profile else args.warmup
 
     def setup(pv_mode):
         desc = sage.Desc.for_tensors(q, k, v, o, pv_mode=pv_mode, frame_len=w.frame_len,
-                                     kv_len=w.kv_len, q_pos0=w.q_pos0,
+                                     kv_len=w.kv_len, q_pos0=w.q_pos0, block_mask=mask_dev,
                                      **(dict(nkv=w.Nkv, frame_stride=w.frame_stride,
                                              sink_frames=w.sink_frames, window_frames=w.window_frames)
                                         if w.frame_stride else {}))
@@ -174,7 +185,8 @@ def main():
                  "attn_tops": round(ops / (t2[2] * 1e-3) / 1e12, 2),
                  "ms_per_step": round(t2[0], 4)}
         if not args.no_cpu:
-            other["accuracy"] = accuracy_sample(w, x, o, desc2, 1 - w.pv_mode, sage)
+            other["accuracy"] = accuracy_sample(w, x, o, desc2, 1 - w.pv_mode, sage,
+                                                rows=64 if w.block_density else 256)
         del ws2, bufs2
     desc, ws, bufs = setup(w.pv_mode)
     ms_step, ms_quant, ms_attn = time_path(torch, step_parts(sage, w, desc, q, k, v, o, bufs, stream),
@@ -216,6 +228,8 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nkv": w.Nkv, "d": w.d,
                    "in_dtype": w.dtype, "pv": pvname,
                    "frame_len": w.frame_len, "kv_splits": splits,
+                   **({"block_density": w.block_density, "kept_tiles": round(float(mask.mean()), 4)}
+                      if mask is not None else {}),
                    **({"frame_stride": w.frame_stride, "sink_frames": w.sink_frames,
                        "window_frames": w.window_frames, "kv_len": w.kv_lens(), "q_pos0": w.q_pos0s()}
                       if w.frame_stride else {}),
@@ -237,14 +251,19 @@ def main():
     print(json.dumps(record), flush=True)
 
 
-def oracle_sample(w, Q, K, V, pv_mode, b, rows, S):
-    """The oracle on a sample of batch b (Q, K, V: host arrays of some heads):
+def oracle_sample(w, Q, K, V, pv_mode, b, rows, S, heads):
+    """The oracle on a sample of batch b (Q, K, V: host arrays of the given heads):
     (emulated output with the kernel's KV splits, float64 attention, seconds
     the emulation -- quantization included -- took)."""
     from oracle import emulate, attention, quant
+    import workloads
     kv, qp = [w.kv_lens()[b]], [w.q_pos0s()[b]]
+    M = workloads.block_mask(w)
+    M = M[b:b + 1, heads] if M is not None else None
     t0 = time.perf_counter()
-    if w.frame_stride:
+    if M is not None:
+        o64 = emulate.emulate_block_sparse(Q, K, V, pv_mode, w.dtype, M, S, w.frame_len, kv, qp, rows=rows)
+    elif w.frame_stride:
         mu = quant.k_mean(K)
         a = quant.channel_shift(Q, K, mu)
         o64 = emulate.emulate_frame_cache(Q, K, V, pv_mode, w.dtype, w.frame_len, w.frame_stride,
@@ -256,7 +275,7 @@ def oracle_sample(w, Q, K, V, pv_mode, b, rows, S):
                                              q_pos0=qp, rows=rows, splits=splits)
     t_emul = time.perf_counter() - t0
     ref = attention.attention_fp64(Q, K, V, frame_len=w.frame_len, kv_len=kv, q_pos0=qp, rows=rows,
-                                   sink_frames=w.sink_frames, window_frames=w.window_frames)
+                                   sink_frames=w.sink_frames, window_frames=w.window_frames, block_mask=M)
     return o64, ref, t_emul
 
 
@@ -270,7 +289,7 @@ def accuracy_sample(w, x, o, desc, pv_mode, sage, heads=2, rows=256):
     Q = x["q"][0:1, hs].float().cpu().numpy()
     K = x["k"][0:1, hs].float().cpu().numpy()
     V = x["v"][0:1, hs].float().cpu().numpy()
-    o64, ref, _ = oracle_sample(w, Q, K, V, pv_mode, 0, r, S)
+    o64, ref, _ = oracle_sample(w, Q, K, V, pv_mode, 0, r, S, hs)
     og = o[0:1, hs][:, :, r].float().cpu().numpy()
     cos = float((og * ref).sum() / np.sqrt((og ** 2).sum() * (ref ** 2).sum()))
     return {"rows": len(r) * len(hs), "max_abs_vs_emulation": float(np.abs(og - o64).max()),
@@ -290,9 +309,12 @@ def cpu_leg(w, x, o, desc, args, sage, torch):
     Q = x["q"][b:b + 1, heads].float().cpu().numpy()
     K = x["k"][b:b + 1, heads].float().cpu().numpy()
     V = x["v"][b:b + 1, heads].float().cpu().numpy()
-    o64, ref, t_cpu = oracle_sample(w, Q, K, V, w.pv_mode, b, rows, S)
+    o64, ref, t_cpu = oracle_sample(w, Q, K, V, w.pv_mode, b, rows, S, heads)
     og = o[b:b + 1, heads][:, :, rows].float().cpu().numpy()
-    sample_ops = 4 * w.d * int(w.row_keys(b, rows).sum()) * len(heads)
+    if w.block_density:
+        sample_ops = 4 * w.d * sum(int(w.row_keys(b, rows, h).sum()) for h in heads)
+    else:
+        sample_ops = 4 * w.d * int(w.row_keys(b, rows).sum()) * len(heads)
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     cos = float((og * ref).sum() / np.sqrt((og ** 2).sum() * (ref ** 2).sum()))
     cpu = {"value": round(sample_ops / t_cpu / 1e12, 6), "unit": "TOPS", "cores": threads, "kind": "oracle",

@@ -19,7 +19,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsage_attn.so")
 
-SAGE_ATTN_ABI_VERSION = 2
+SAGE_ATTN_ABI_VERSION = 3
 SAGE_F16, SAGE_BF16 = 0, 1
 SAGE_PV_16, SAGE_PV_FP8 = 0, 1
 SAGE_FLAG_DEBUG_SYNC = 0x1
@@ -40,7 +40,8 @@ class sage_attn_desc(ctypes.Structure):
                 ("kv_len", ctypes.POINTER(ctypes.c_int32)), ("q_pos0", ctypes.POINTER(ctypes.c_int32)),
                 ("k_mean_in", ctypes.c_void_p), ("frame_stride", ctypes.c_int32),
                 ("sink_frames", ctypes.c_int32), ("window_frames", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("chan_shift_in", ctypes.c_void_p)]
+                ("reserved", ctypes.c_int32), ("chan_shift_in", ctypes.c_void_p),
+                ("block_mask", ctypes.c_void_p)]
 
 
 class sage_quant_bufs(ctypes.Structure):
@@ -118,7 +119,7 @@ class Desc:
     def __init__(self, B, H, Nq, Nkv, d, dtype, pv_mode=SAGE_PV_16, frame_len=0, kv_len=None,
                  q_pos0=None, sm_scale=0.0, kv_splits=0, flags=0, k_mean_in=None,
                  q_stride=None, k_stride=None, v_stride=None, o_stride=None,
-                 frame_stride=0, sink_frames=0, window_frames=0, chan_shift_in=None):
+                 frame_stride=0, sink_frames=0, window_frames=0, chan_shift_in=None, block_mask=None):
         c = sage_attn_desc()
         c.abi_version = SAGE_ATTN_ABI_VERSION
         c.dtype = dtype
@@ -141,6 +142,11 @@ class Desc:
         c.frame_stride, c.sink_frames, c.window_frames, c.reserved = frame_stride, sink_frames, window_frames, 0
         self._chan_shift_in = chan_shift_in
         c.chan_shift_in = chan_shift_in.data_ptr() if chan_shift_in is not None else None
+        if block_mask is not None and (block_mask.dtype != torch.uint8 or not block_mask.is_contiguous()
+                                       or tuple(block_mask.shape) != (B, H, (Nq + 127) // 128, (Nkv + 63) // 64)):
+            raise ValueError("block_mask must be a contiguous uint8 [B, H, ceil(Nq/128), ceil(Nkv/64)] tensor")
+        self._block_mask = block_mask
+        c.block_mask = block_mask.data_ptr() if block_mask is not None else None
         self.c = c
         self.frame_stride, self.sink_frames, self.window_frames = frame_stride, sink_frames, window_frames
         self.B, self.H, self.Nq, self.Nkv, self.d = B, H, Nq, Nkv, d

@@ -28,6 +28,8 @@ struct Plan {
   int B, H, Nq, Nkv, d, Nq_pad, Nkv_pad, splits, frame_len, dtype, pv_mode;
   int frame_stride, sink_frames, window_frames;
   uint32_t cpf_magic;
+  const uint8_t* block_mask;
+  int mask_nkc;
   float sigma;
   sage::BatchInfo bi;
   int order[sage::MAXB_ARGS];
@@ -106,6 +108,11 @@ int make_plan(const sage_attn_desc* d, Plan* p) {
   if (bh * pad128(d->Nq) / 128 * SAGE_MAX_SPLITS > 0x7FFFFFFF) return fail(SAGE_E_SHAPE, "too many work items");
   if (d->frame_len < 0) return fail(SAGE_E_MASK, "frame_len must be >= 0");
   if (d->reserved != 0) return fail(SAGE_E_UNSUPPORTED, "reserved must be 0");
+  if (d->block_mask) {
+    if (d->frame_stride != 0) return fail(SAGE_E_UNSUPPORTED, "a block mask needs contiguous keys (frame_stride 0)");
+    if ((d->Nkv + 63) / 64 > SAGE_MAX_MASK_CHUNKS)
+      return fail(SAGE_E_UNSUPPORTED, "a block mask allows at most SAGE_MAX_MASK_CHUNKS key blocks");
+  }
   if (d->frame_stride < 0) return fail(SAGE_E_MASK, "frame_stride must be >= 0");
   if (d->frame_stride != 0) {
     if (d->frame_len <= 0) return fail(SAGE_E_MASK, "a frame cache needs frame_len > 0");
@@ -138,6 +145,8 @@ int make_plan(const sage_attn_desc* d, Plan* p) {
   p->sink_frames = d->sink_frames;
   p->window_frames = d->window_frames;
   p->cpf_magic = 0;
+  p->block_mask = d->block_mask;
+  p->mask_nkc = (d->Nkv + 63) / 64;
   if (d->frame_stride > 64) {  // one chunk per frame needs no division
     const uint64_t cpf = static_cast<uint64_t>(d->frame_stride / 64);
     p->cpf_magic = static_cast<uint32_t>(((uint64_t{1} << 32) + cpf - 1) / cpf);
@@ -259,6 +268,8 @@ sage::AttnLaunch attn_launch_of(const Plan& p, const sage_quant_bufs& b, void* o
   L.sink_frames = p.sink_frames;
   L.window_frames = p.window_frames;
   L.cpf_magic = p.cpf_magic;
+  L.block_mask = p.block_mask;
+  L.mask_nkc = p.mask_nkc;
   L.sigma = p.sigma;
   L.bi = p.bi;
   for (int i = 0; i < sage::MAXB_ARGS; ++i) L.order[i] = p.order[i];

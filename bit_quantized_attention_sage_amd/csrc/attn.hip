@@ -145,6 +145,8 @@ struct AttnArgs {
   int frame_len;
   int frame_stride, sink_frames, window_frames;  // frame cache and window (0: contiguous keys)
   uint32_t cpf_magic;                            // ceil(2^32 / (frame_stride / 64)), 0 if that is 1
+  const uint8_t* block_mask;                     // [B*H][nqt][mask_nkc], nonzero = tile kept
+  int mask_nkc;
   BatchInfo bi;
   int order[MAXB_ARGS];
 };
@@ -334,9 +336,15 @@ struct WaveState {
 
 };
 
-// CACHE: keys in a frame cache (frame_stride > 0) rather than contiguous.
-template <int D, int PV, int DT, bool CACHE>
+// Key layouts / chunk lists of the fused kernel.
+enum { KV_DENSE = 0,    // contiguous keys, every chunk up to the tile's range end
+       KV_CACHE = 1,    // frame cache: the sink frames' chunks, then the window's
+       KV_SPARSE = 2 }; // contiguous keys, only the chunks the block mask keeps
+constexpr int MAX_LIST = 4096;  // kept-chunk list of a tile (LDS, 2 bytes each)
+
+template <int D, int PV, int DT, int MODE>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
+  constexpr bool CACHE = MODE == KV_CACHE, SPARSE = MODE == KV_SPARSE;
   constexpr int NCB = D / 32;                    // 32-channel blocks of O
   constexpr int VBYTES = (PV == PVFP8) ? 1 : 2;  // bytes per V element
   constexpr int KB = 64 * D;                     // bytes of a K chunk
@@ -350,6 +358,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
   __shared__ __attribute__((aligned(16))) int8_t kL1[KB];
   __shared__ __attribute__((aligned(16))) uint8_t vL0[VBC];
   __shared__ __attribute__((aligned(16))) uint8_t vL1[VBC];
+  __shared__ uint16_t slist[SPARSE ? MAX_LIST : 1];  // kept chunks of the tile, ascending
+  __shared__ int scnt[8];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -383,7 +393,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
   //  * frame cache: the chunks of the sink frames, then those of the window
   //    frames through the last row's frame (up to its last token); a row sees
   //    the valid slots of the frames of its window.
-  int re = 0, fq = 0, fq_lo = 0, fq_hi = 0, a0 = 0, b1 = 0, v_lo, v_hi, full_end = 0;
+  int re = 0, fq = 0, fq_lo = 0, fq_hi = 0, a0 = 0, b1 = 0, v_lo, v_hi, full_end = 0, n_full = 0;
   if constexpr (!CACHE) {
     re = F > 0 ? min(kv_len, ((q_pos0 + qi_valid) / F + 1) * F) : kv_len;
     const int first_end = F > 0 ? min(kv_len, ((q_pos0 + row_first) / F + 1) * F) : kv_len;
@@ -392,6 +402,36 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
     v_lo = split * nch / A.splits;
     v_hi = min((split + 1) * nch / A.splits, (last_end + 63) / 64);
     full_end = first_end;  // chunks ending at or before it are visible in full to every row
+    if constexpr (SPARSE) {
+      // The tile's list: the chunks among [0, ceil(last_end/64)) that the
+      // mask keeps, compacted in order into LDS by the whole workgroup
+      // (ballot + per-wave counts); `below` counts those visible in full to
+      // every row.  The split takes entries [v_lo, v_hi) of the list.
+      const int nbase = (last_end + 63) / 64, nfull = full_end / 64;
+      const uint8_t* mrow = A.block_mask + (static_cast<int64_t>(bh) * A.nqt + qt) * A.mask_nkc;
+      int total = 0, below = 0;
+      for (int c0 = 0; c0 < nbase; c0 += 256) {
+        const int c = c0 + tid;
+        const bool keep = c < nbase && mrow[c] != 0;
+        const uint64_t bk = __ballot(keep), bf = __ballot(keep && c < nfull);
+        if (lane == 0) {
+          scnt[w] = __popcll(bk);
+          scnt[4 + w] = __popcll(bf);
+        }
+        __syncthreads();
+        int off = total;
+        for (int i = 0; i < w; ++i) off += scnt[i];
+        const int rank = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bk >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bk), 0));
+        if (keep) slist[off + rank] = static_cast<uint16_t>(c);
+        total += scnt[0] + scnt[1] + scnt[2] + scnt[3];
+        below += scnt[4] + scnt[5] + scnt[6] + scnt[7];
+        __syncthreads();
+      }
+      v_lo = split * total / A.splits;
+      v_hi = (split + 1) * total / A.splits;
+      n_full = below;
+    }
   } else {
     const int cpf = FS / 64;
     fq = (q_pos0 + qi_valid) / F;
@@ -411,14 +451,21 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
   const int J = max(0, v_hi - v_lo);  // chunks of this work item
   // list entries below this one are visible in full to every row of the tile
   // (contiguous keys: up to the first row's end; frame cache: no shortcut)
-  const int v_full = CACHE ? 0 : full_end / 64;
+  const int v_full = CACHE ? 0 : SPARSE ? n_full : full_end / 64;
   // physical chunk of list entry v; contiguous keys: v itself (the loads
-  // clamp it to the head's last chunk), frame cache: clamped to the item's
-  // range first
-  auto chunk_of = [&](int v) {
-    if constexpr (!CACHE) return v;
-    v = max(min(v, v_hi - 1), 0);
-    return v < a0 ? v : b1 + (v - a0);
+  // clamp it to the head's last chunk); frame cache and block mask: clamped
+  // to the item's range first
+  auto chunk_of = [&](int v) -> int {
+    if constexpr (MODE == KV_DENSE) {
+      return v;
+    } else if constexpr (SPARSE) {
+      if (v_hi <= v_lo) return 0;
+      v = max(min(v, v_hi - 1), v_lo);
+      return __builtin_amdgcn_readfirstlane(static_cast<int>(slist[v]));
+    } else {
+      v = max(min(v, v_hi - 1), 0);
+      return v < a0 ? v : b1 + (v - a0);
+    }
   };
 
   // Visibility of chunk ch: every row sees all 64 keys (wave-uniform), or
@@ -569,6 +616,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
   // Every load issued so far has completed; saying so keeps the loop's own
   // prefetch loads from being waited on before the first MFMA.
   __builtin_amdgcn_s_waitcnt(0);
+  int pre1 = 0, pre3 = 0;  // block mask: chunks of entries n+1 and n+3 for the next step
+  if constexpr (SPARSE) {
+    pre1 = chunk_of(n + 1);
+    pre3 = chunk_of(n + 3);
+  }
 
   // CHK false: S(n+1) and S(n+2) are visible in full to every row (no masking
   // check, every row has keys in entry n+1).
@@ -585,7 +637,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
     constexpr int NRD = NQK + ((PV == PVFP8) ? 2 * NCB : 4 * NCB);  // LDS operand reads
     constexpr int VPER = (PV == PVFP8) ? 12 : 5;                  // softmax slice per MFMA
     const float c_mid = qsc * ksn1;
-    const int ch1 = chunk_of(n + 1), ch3 = chunk_of(n + 3);
+    const int ch1 = SPARSE ? pre1 : chunk_of(n + 1), ch3 = SPARSE ? pre3 : chunk_of(n + 3);
     __builtin_amdgcn_sched_barrier(0);
     dma_k(k_wr, ch3);
     dma_v(v_wr, ch1);
@@ -610,6 +662,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
     st.rescale(alpha);  // rare: some row's running max moved (after P(n) V(n))
     if constexpr (CHK) {
       if (n + 2 >= v_full) has_n = mask_chunk(n + 2, ns0, ns1);  // rare: S(n+2) is a boundary chunk
+    }
+    if constexpr (SPARSE) {  // the next step's chunks, read from LDS ahead of the wait
+      pre1 = chunk_of(n + 2);
+      pre3 = chunk_of(n + 4);
     }
     dma_wait();
     __syncthreads();
@@ -650,7 +706,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
   const float ltot = st.ls[0];  // already summed over both lane halves
   if (qi >= A.Nq) return;
   if (A.splits == 1) {
-    const float inv = 1.0f / ltot;
+    const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;  // a row with no visible key: 0
     uint16_t* orow = static_cast<uint16_t*>(A.o) + b * A.os_b + h * A.os_h + static_cast<int64_t>(qi) * A.os_n;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
@@ -710,7 +766,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs A) {
     acc[3] += wgt * v.w;
     wsum += wgt;
   }
-  const float inv = 1.0f / wsum;
+  const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;  // no split saw a key: 0
   uint16_t* orow = static_cast<uint16_t*>(A.o) + b * A.os_b + h * A.os_h + static_cast<int64_t>(qi) * A.os_n;
   *reinterpret_cast<uint2*>(orow + 4 * g) =
       make_uint2(Pack16<DT>::pack(acc[0] * inv, acc[1] * inv), Pack16<DT>::pack(acc[2] * inv, acc[3] * inv));
@@ -773,6 +829,8 @@ static AttnArgs make_args(const AttnLaunch& L) {
   A.sink_frames = L.sink_frames;
   A.window_frames = L.window_frames;
   A.cpf_magic = L.cpf_magic;
+  A.block_mask = L.block_mask;
+  A.mask_nkc = L.mask_nkc;
   A.bi = L.bi;
   for (int i = 0; i < MAXB_ARGS; ++i) A.order[i] = L.order[i];
   return A;
@@ -781,10 +839,12 @@ static AttnArgs make_args(const AttnLaunch& L) {
 template <int D, int PV, int DT>
 static hipError_t attn_impl(const AttnLaunch& L, hipStream_t st) {
   const AttnArgs A = make_args(L);
-  if (L.frame_stride > 0)
-    hipLaunchKernelGGL((attn_fwd_kernel<D, PV, DT, true>), dim3(A.total), dim3(256), 0, st, A);
+  if (L.block_mask)
+    hipLaunchKernelGGL((attn_fwd_kernel<D, PV, DT, KV_SPARSE>), dim3(A.total), dim3(256), 0, st, A);
+  else if (L.frame_stride > 0)
+    hipLaunchKernelGGL((attn_fwd_kernel<D, PV, DT, KV_CACHE>), dim3(A.total), dim3(256), 0, st, A);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<D, PV, DT, false>), dim3(A.total), dim3(256), 0, st, A);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, PV, DT, KV_DENSE>), dim3(A.total), dim3(256), 0, st, A);
   if (L.splits > 1) {
     const int64_t threads = static_cast<int64_t>(L.B) * L.H * L.Nq_pad * (D / 4);
     hipLaunchKernelGGL((attn_combine_kernel<D, DT>), dim3(static_cast<unsigned>((threads + 255) / 256)),

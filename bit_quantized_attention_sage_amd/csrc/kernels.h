@@ -41,6 +41,8 @@ struct AttnLaunch {
   int frame_len, splits;
   int frame_stride, sink_frames, window_frames;  // frame cache and window
   uint32_t cpf_magic;  // ceil(2^32 / (frame_stride / 64)): chunk -> frame by __umulhi
+  const uint8_t* block_mask;  // [B,H,Nq_pad/128,mask_nkc] or null
+  int mask_nkc;               // ceil(Nkv / 64)
   float sigma;  // fp32(sm_scale * log2 e)
   BatchInfo bi;
   int order[MAXB_ARGS];  // batches by decreasing kv_len (longest first)

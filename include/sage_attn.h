@@ -39,6 +39,18 @@
  * fk <= fq and (fk < S or fk >= fq - W); W = 0 keeps every earlier frame.
  * kv_len and q_pos0 stay in tokens; Nkv counts cache slots.
  *
+ * Block-sparse attention (block_mask != NULL, contiguous keys only).  Sparse
+ * attention built on top of SageAttention skips whole tiles (SpargeAttention
+ * and Sparse-Linear Attention in the Vidu S1 blog, section "Infra", and the
+ * TurboDiffusion digests); the pages give no predictor, so the caller passes
+ * the tile mask: byte block_mask[((b*H + h)*ceil(Nq/128) + i/128)*
+ * ceil(Nkv/64) + j/64] != 0 keeps the tile of query i and key j, which is
+ * then visible iff the mask above also allows it.  Dropped tiles cost no
+ * work.  A query row with no visible key gets an output of 0.  At most
+ * SAGE_MAX_MASK_CHUNKS key blocks (SAGE_E_UNSUPPORTED otherwise).  KV splits
+ * chosen by the library assume a dense mask (the mask is device memory and
+ * is not read on the host); kv_splits overrides.
+ *
  * Tensors.  Q [B,H,Nq,d], K and V [B,H,Nkv,d], O [B,H,Nq,d], all of one
  * 16-bit type (fp16 or bf16), device memory, channel dimension contiguous,
  * strides of the b, h and n dimensions given in ELEMENTS.  d is 64 or 128.
@@ -69,7 +81,7 @@
 extern "C" {
 #endif
 
-#define SAGE_ATTN_ABI_VERSION 2
+#define SAGE_ATTN_ABI_VERSION 3
 
 typedef enum {
   SAGE_OK = 0,
@@ -91,6 +103,7 @@ enum { SAGE_PV_16 = 0, SAGE_PV_FP8 = 1 };   /* sage_attn_desc.pv_mode        */
 #define SAGE_FLAG_DEBUG_SYNC 0x1u  /* synchronize the stream after each launch */
 #define SAGE_MAX_BATCH 128
 #define SAGE_MAX_SPLITS 16
+#define SAGE_MAX_MASK_CHUNKS 4096  /* key blocks of 64 a block mask may cover */
 
 typedef struct sage_attn_desc {
   int32_t abi_version;  /* must be SAGE_ATTN_ABI_VERSION                      */
@@ -117,6 +130,9 @@ typedef struct sage_attn_desc {
   int32_t reserved;       /* must be 0                                         */
   const int8_t *chan_shift_in; /* device [B,H,d] fixed channel-balance exponents
                              (in [-64, 64]) to use, or NULL: computed          */
+  const uint8_t *block_mask; /* device [B][H][ceil(Nq/128)][ceil(Nkv/64)] bytes,
+                             or NULL: block-sparse attention (see top); read
+                             by the attention calls only                      */
 } sage_attn_desc;
 
 /* Quantized operands, in caller-owned device memory (normally carved out of

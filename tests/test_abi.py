@@ -150,3 +150,28 @@ def test_frame_cache_desc_and_quantize_frames_validation(lib):
     assert lib.sage_attn_quant_layout(plain.ptr, ctypes.c_void_p(base2), n2, ctypes.byref(bufs2)) == 0
     f2 = ctypes.c_void_p(base2)
     assert lib.sage_attn_quantize_frames(plain.ptr, None, f2, f2, 0, 1, ctypes.byref(bufs2), None) == 7
+
+
+def test_block_mask_validation(lib):
+    d = _desc()
+    d.c.block_mask = 4096      # a device address; never read on the host
+    assert _status(d)[0] == 0
+    cache = _desc(frame_len=50, frame_stride=64, Nkv=320, Nq=50)
+    cache.c.block_mask = 4096
+    assert _status(cache)[0] == 7 and b"contiguous" in lib.sage_attn_last_error()
+    big = sage.Desc(1, 1, 128, 64 * 4096 + 1, 128, sage.SAGE_BF16)
+    big.c.block_mask = 4096
+    assert _status(big)[0] == 7
+    ok = sage.Desc(1, 1, 128, 64 * 4096, 128, sage.SAGE_BF16)
+    ok.c.block_mask = 4096
+    assert _status(ok)[0] == 0
+
+
+def test_block_mask_binding_checks_its_shape():
+    import torch
+    m = torch.ones((1, 2, 1, 3), dtype=torch.uint8)
+    sage.Desc(1, 2, 100, 150, 64, sage.SAGE_F16, block_mask=m)
+    with pytest.raises(ValueError):
+        sage.Desc(1, 2, 100, 150, 64, sage.SAGE_F16, block_mask=m[:, :, :, :2])
+    with pytest.raises(ValueError):
+        sage.Desc(1, 2, 100, 150, 64, sage.SAGE_F16, block_mask=m.bool())

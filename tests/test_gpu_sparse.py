@@ -1,0 +1,143 @@
+"""GPU parity of block-sparse attention (tiles dropped by a caller-given mask
+are skipped: sparse attention built on SageAttention, Vidu S1 blog, section
+"Infra"), through the C ABI.
+
+Outputs within the output-rounding bar of the oracle's emulation run with
+the kernel's per-tile kept-chunk lists and splits; rows with no kept visible
+key exactly 0; cosine against float64 attention under the same mask; an
+all-kept mask gives byte-identical outputs to the dense path."""
+
+import numpy as np
+import pytest
+import torch
+
+import bit_quantized_attention_sage_amd as sage
+import workloads
+from oracle import emulate, attention
+from oracle.constants import PV_16, PV_FP8
+from gpu_util import host, compare_output, cosine, NAME_DT
+
+pytestmark = pytest.mark.gpu
+
+
+def _rand(shape, dtype, seed, offset=0.0):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(shape, generator=g) + offset).to(dtype)
+
+
+def _mask(B, H, Nq, Nkv, density, seed):
+    rng = np.random.default_rng(seed)
+    return (rng.random((B, H, -(-Nq // 128), -(-Nkv // 64))) < density).astype(np.uint8)
+
+
+def _run(q, k, v, pv_mode, M, frame_len=0, kv_len=None, q_pos0=None, splits=0):
+    o = torch.full_like(q, float("nan"))
+    desc = sage.Desc.for_tensors(q, k, v, o, pv_mode=pv_mode, frame_len=frame_len, kv_len=kv_len, q_pos0=q_pos0,
+                                 kv_splits=splits,
+                                 block_mask=torch.from_numpy(M).cuda() if M is not None else None)
+    ws = sage.new_workspace(desc, q.device)
+    sage.sage_attn_fwd(desc, q, k, v, o, ws)
+    torch.cuda.synchronize()
+    return o, desc
+
+
+CASES = [
+    # (B, H, Nq, Nkv, d, dtype, F, kv_len, q_pos0, density, splits)
+    (1, 2, 300, 1000, 128, torch.bfloat16, 0, None, None, 0.4, 0),
+    (1, 2, 300, 1000, 128, torch.bfloat16, 0, None, None, 0.4, 3),            # forced splits
+    (2, 2, 256, 1300, 128, torch.bfloat16, 250, [1300, 900], [1044, 600], 0.5, 0),  # frames, ragged
+    (1, 3, 200, 700, 64, torch.float16, 0, None, None, 0.15, 2),              # d 64, empty tiles
+    (1, 1, 256, 64 * 1500, 128, torch.bfloat16, 0, [64 * 1500 - 37], None, 0.05, 0),  # long list
+]
+
+
+def _cid(c):
+    return f"B{c[0]}H{c[1]}q{c[2]}k{c[3]}d{c[4]}{NAME_DT[c[5]]}F{c[6]}p{c[9]}s{c[10]}"
+
+
+@pytest.mark.parametrize("pv_mode", [PV_16, PV_FP8], ids=["pv16", "pvfp8"])
+@pytest.mark.parametrize("case", CASES, ids=[_cid(c) for c in CASES])
+def test_sparse_parity(lib, case, pv_mode):
+    B, H, Nq, Nkv, d, dt, F, kv, qp, density, splits = case
+    print(f"sparse case {_cid(case)} pv {pv_mode}", flush=True)
+    seed = sum(map(ord, _cid(case))) + pv_mode
+    q = _rand((B, H, Nq, d), dt, seed)
+    k = _rand((B, H, Nkv, d), dt, seed + 1, offset=0.7)
+    v = _rand((B, H, Nkv, d), dt, seed + 2)
+    M = _mask(B, H, Nq, Nkv, density, seed + 3)
+    M[0, 0, 0, :] = 0                      # one query tile with nothing kept
+    if M.shape[2] > 1:
+        M[0, -1, 1, :] = 0
+        M[0, -1, 1, 0] = 1                 # one with a single kept block
+    o, desc = _run(q.cuda(), k.cuda(), v.cuda(), pv_mode, M, F, kv, qp, splits)
+    nsplit = sage.sage_attn_kv_splits(desc)
+    Q, K, V = host(q), host(k), host(v)
+    o64 = emulate.emulate_block_sparse(Q, K, V, pv_mode, NAME_DT[dt], M, nsplit, F, kv, qp)
+    o_abs = emulate.emulate_block_sparse(Q, K, np.abs(V), pv_mode, NAME_DT[dt], M, nsplit, F, kv, qp) \
+        if pv_mode == PV_FP8 else None
+    og = host(o)
+    zero = ~np.any(o64 != 0, axis=-1)      # rows with no kept visible key
+    assert zero[0, 0, :min(128, Nq)].all()
+    assert not og[zero].any()
+    mx, excess, frac, rel, rel_bound = compare_output(og, o64, NAME_DT[dt], pv_mode, o_abs)
+    print(f"  splits {nsplit} zero rows {int(zero.sum())} max-abs {mx:.3e} excess {excess:.2e} "
+          f"beyond-rounding {frac:.2e} rel-L2 {rel:.3e}", flush=True)
+    assert excess <= 0
+    # Rows here keep as few as 64 keys.  The kernel's exp2 (within an ulp of
+    # the exact value the emulation uses) lands on the other side of P's
+    # rounding for about 2^-12 of the keys, and in a 64-key row one such
+    # flip moves O by up to a P ulp / 64 of |v| -- above half an fp16 output
+    # ulp.  Dense rows dilute this below the output rounding.
+    assert frac <= (2e-3 if pv_mode == PV_16 else 2e-2)
+    assert rel <= rel_bound
+    ref = attention.attention_fp64(Q, K, V, frame_len=F, kv_len=kv, q_pos0=qp, block_mask=M)
+    cs = cosine(og, ref)
+    print(f"  cosine vs fp64 under the mask {cs:.6f}", flush=True)
+    assert cs >= (0.999 if pv_mode == PV_16 else 0.998)
+
+
+@pytest.mark.parametrize("pv_mode", [PV_16, PV_FP8])
+def test_all_kept_mask_equals_dense(lib, pv_mode):
+    """With every tile kept and one work item per tile, the sparse launch
+    visits the same chunks in the same order as the dense one."""
+    B, H, Nq, Nkv, d, F = 2, 2, 300, 900, 128, 150
+    q = _rand((B, H, Nq, d), torch.bfloat16, 81).cuda()
+    k = _rand((B, H, Nkv, d), torch.bfloat16, 82).cuda()
+    v = _rand((B, H, Nkv, d), torch.bfloat16, 83).cuda()
+    kv, qp = [900, 700], [600, 350]
+    ones = np.ones((B, H, 3, 15), np.uint8)
+    o1, _ = _run(q, k, v, pv_mode, ones, F, kv, qp, splits=1)
+    o2, _ = _run(q, k, v, pv_mode, None, F, kv, qp, splits=1)
+    assert torch.equal(o1, o2)
+
+
+@pytest.mark.slow
+def test_sparse_workload_parity(lib):
+    """The sparse workload at full size (the large workload with 25% of its
+    tiles kept) in the launch configuration bench.py times; outputs of 3
+    seeded heads on sampled rows."""
+    w = workloads.get("sparse")
+    print("workload sparse", flush=True)
+    x = workloads.make(w, "cuda")
+    q, k, v = x["q"], x["k"], x["v"]
+    M = workloads.block_mask(w)
+    o = torch.empty_like(q)
+    desc = sage.Desc.for_tensors(q, k, v, o, pv_mode=w.pv_mode, block_mask=torch.from_numpy(M).cuda())
+    ws = sage.new_workspace(desc, q.device)
+    sage.sage_attn_fwd(desc, q, k, v, o, ws)
+    torch.cuda.synchronize()
+    hs = sorted(np.random.default_rng(3000).choice(w.H, 3, replace=False).tolist())
+    rows = workloads.sample_rows(w, 48)
+    nsplit = sage.sage_attn_kv_splits(desc)
+    Q, K, V = host(q[:, hs]), host(k[:, hs]), host(v[:, hs])
+    Mh = M[:, hs]
+    o64 = emulate.emulate_block_sparse(Q, K, V, w.pv_mode, w.dtype, Mh, nsplit, rows=rows)
+    og = host(o[:, hs])[:, :, rows]
+    mx, excess, frac, rel, rel_bound = compare_output(og, o64, w.dtype, w.pv_mode)
+    print(f"  heads {hs} splits {nsplit}: max-abs {mx:.2e} excess {excess:.2e} rel-L2 {rel:.2e}", flush=True)
+    assert excess <= 0
+    assert rel <= rel_bound
+    ref = attention.attention_fp64(Q, K, V, rows=rows, block_mask=Mh)
+    cs = cosine(og, ref)
+    print(f"  cosine vs fp64 under the mask {cs:.6f}", flush=True)
+    assert cs >= 0.999

@@ -26,6 +26,12 @@ stand in for them, with the token grids of such clips:
            queries are frame 40; 1 sink frame and a 16-frame window, so each
            query sees 18 frames (36720 keys).  The pages give no window
            length; 16 frames matches the stream workload's history.
+  sparse   the large workload with a block mask over its (128-query,
+           64-key) tiles keeping a seeded 25% of each query tile's key
+           blocks, drawn independently per (head, query tile) -- a stand-in
+           for the sparse branch of sparse attention built on SageAttention
+           (Vidu S1 blog, section "Infra"), whose predictor the pages do not
+           give.
 
 Values are N(0,1) float32, then rounded to the 16-bit dtype.  Each (tensor,
 batch, head) slice has its own seed, so any subset of heads can be drawn on
@@ -62,6 +68,7 @@ class Workload:
     frame_stride: int = 0      # > 0: K/V live in a frame cache of Nkv slots
     sink_frames: int = 0
     window_frames: int = 0
+    block_density: float = 0.0  # > 0: block mask keeping this share of tiles
     extra: dict = field(default_factory=dict)
 
     @property
@@ -84,10 +91,23 @@ class Workload:
             return [0] * self.B
         return [kv - self.Nq for kv in self.kv_lens()]
 
-    def row_keys(self, b, rows=None):
-        """Visible keys of each query row (all rows when None) of batch b."""
+    def row_keys(self, b, rows=None, h=None):
+        """Visible keys of each query row (all rows when None) of batch b; with
+        a block mask, of head h (summed over heads when h is None)."""
         kv, qp = self.kv_lens()[b], self.q_pos0s()[b]
         i = np.arange(self.Nq, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
+        if self.block_density:
+            M = block_mask(self)[b]                                    # [H, nqt, nkc]
+            end = np.minimum(kv, ((qp + i) // self.frame_len + 1) * self.frame_len) if self.frame_len \
+                else np.full(len(i), kv, dtype=np.int64)
+            # kept keys of a row: the kept blocks' keys below its end; rows of
+            # one query tile with the same end share the count
+            nkc = M.shape[2]
+            pairs, inv = np.unique(np.stack([i // 128, end]), axis=1, return_inverse=True)
+            width = np.minimum(64, np.maximum(0, pairs[1][:, None] - 64 * np.arange(nkc)[None, :]))
+            hs = range(self.H) if h is None else [h]
+            per = sum((M[hh][pairs[0]].astype(np.int64) * width).sum(axis=1) for hh in hs)
+            return per[np.ravel(inv)].astype(np.int64)
         if self.window_frames:
             F = self.frame_len
             fq = (qp + i) // F
@@ -102,6 +122,8 @@ class Workload:
 
     def visible_pairs(self):
         """Number of visible (query, key) pairs over all batches and heads."""
+        if self.block_density:
+            return sum(int(self.row_keys(b).sum()) for b in range(self.B))
         return self.H * sum(int(self.row_keys(b).sum()) for b in range(self.B))
 
     def ops(self):
@@ -132,6 +154,9 @@ def get(name, **override):
         w = Workload("window", 1, 24, FRAME, 48 * 2048, 128, "bf16", 0,
                      frame_len=FRAME, kv_len=[41 * FRAME], q_pos0=[40 * FRAME], seed=606,
                      frame_stride=2048, sink_frames=1, window_frames=16)
+    elif name == "sparse":
+        w = Workload("sparse", 1, 40, 75600, 75600, 128, "bf16", 0, seed=303,
+                     outlier_frac=0.01, block_density=0.25)
     else:
         raise KeyError(name)
     for k, v in override.items():
@@ -139,7 +164,23 @@ def get(name, **override):
     return w
 
 
-NAMES = ("tiny", "small", "large", "stream", "batched", "window")
+NAMES = ("tiny", "small", "large", "stream", "batched", "window", "sparse")
+
+
+_MASKS = {}
+
+
+def block_mask(w):
+    """The workload's block mask: uint8 numpy [B, H, ceil(Nq/128), ceil(Nkv/64)],
+    each tile kept with probability block_density (seeded; None without one)."""
+    if not w.block_density:
+        return None
+    key = (w.seed, w.B, w.H, w.Nq, w.Nkv, w.block_density)
+    if key not in _MASKS:
+        rng = np.random.default_rng(w.seed * 7 + 3)
+        shape = (w.B, w.H, -(-w.Nq // 128), -(-w.Nkv // 64))
+        _MASKS[key] = (rng.random(shape, dtype=np.float32) < w.block_density).astype(np.uint8)
+    return _MASKS[key]
 
 
 def _slice_seed(seed, tensor, b, h):
