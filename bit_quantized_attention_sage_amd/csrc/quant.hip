@@ -81,17 +81,41 @@ __global__ void stats_final_kernel(int H, int D, int nchunk_k, int nchunk_q, Bat
   const int b = bh / H;
   const int n = bi.kv_len[b];
   const int nch = (n + KMEAN_CHUNK - 1) / KMEAN_CHUNK;
+  // The partials of NB chunks are loaded together (independent loads in
+  // flight), then added in ascending chunk order: the fp64 sum keeps its
+  // sequential order (adds past the end are skipped, not added as zeros).
+  constexpr int NB = 16;
   double s = 0.0;
   float mx = -__builtin_inff(), mn = __builtin_inff();
-  for (int t = 0; t < nch; ++t) {  // ascending chunk order
-    const int64_t o = (static_cast<int64_t>(bh) * nchunk_k + t) * D + c;
-    s += ksum[o];
-    mx = fmaxf(mx, kmax[o]);
-    mn = fminf(mn, kmin[o]);
+  const double* ks = ksum + static_cast<int64_t>(bh) * nchunk_k * D + c;
+  const float* kx = kmax + static_cast<int64_t>(bh) * nchunk_k * D + c;
+  const float* kn = kmin + static_cast<int64_t>(bh) * nchunk_k * D + c;
+  for (int t0 = 0; t0 < nch; t0 += NB) {
+    double v[NB];
+    float a[NB], z[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int t = min(t0 + i, nch - 1);
+      v[i] = ks[static_cast<int64_t>(t) * D];
+      a[i] = kx[static_cast<int64_t>(t) * D];
+      z[i] = kn[static_cast<int64_t>(t) * D];
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      if (t0 + i < nch) s += v[i];
+      mx = fmaxf(mx, a[i]);  // (repeats of the last chunk change no max or min)
+      mn = fminf(mn, z[i]);
+    }
   }
   float qa = 0.f;
-  for (int t = 0; t < nchunk_q; ++t)
-    qa = fmaxf(qa, qamax[(static_cast<int64_t>(bh) * nchunk_q + t) * D + c]);
+  const float* qx = qamax + static_cast<int64_t>(bh) * nchunk_q * D + c;
+  for (int t0 = 0; t0 < nchunk_q; t0 += NB) {
+    float a[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) a[i] = qx[static_cast<int64_t>(min(t0 + i, nchunk_q - 1)) * D];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) qa = fmaxf(qa, a[i]);
+  }
   const float mu = k_mean_in ? k_mean_in[static_cast<int64_t>(bh) * D + c]
                              : static_cast<float>(s / static_cast<double>(n));
   // fp32 rounding of K - mu is monotone in K, so the extreme smoothed values
