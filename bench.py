@@ -11,7 +11,9 @@ frame's K and V and the queries quantized into the cache once
 cache's first quantization) plus the fused kernel over the sink and window
 frames; the whole-cache quantization is timed beside it.  With a block mask
 (--workload sparse) the fused kernel skips the dropped tiles and TOPS counts
-the kept visible pairs only.  Prints ONE
+the kept visible pairs only.  --workload linear times the per-block W8A8
+linear layer instead (activation quantization + INT8 GEMM; weights quantized
+once beforehand), in TOPS = 2 M N K / time.  Prints ONE
 JSON line: TOPS = 4*d*(visible query-key pairs) / time, the roofline of the
 dominant kernel (the fused attention, timed with HIP events on its own stream;
 its HBM traffic from the committed rocprofv3 counters when they were taken on
@@ -135,6 +137,8 @@ def main():
     import workloads
 
     sage.load()
+    if args.workload == "linear":
+        return main_linear(args, torch, sage, workloads)
     w = workloads.get(args.workload)
     # the block-sparse emulation runs tile by tile: a smaller sample keeps it to tens of seconds
     if args.cpu_heads is None:
@@ -248,6 +252,73 @@ def main():
         record["other_pv_mode"] = other
     if not args.no_cpu and not args.profile:
         record["cpu_baseline"], record["parity"] = cpu_leg(w, x, o, desc, args, sage, torch)
+    print(json.dumps(record), flush=True)
+
+
+def main_linear(args, torch, sage, workloads):
+    """The per-block W8A8 linear layer: one step = quantize X + GEMM."""
+    w = workloads.get("linear")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t = workloads.make_linear(w, dev)
+    x, wt, bias = t["x"], t["w"], t["bias"]
+    y = torch.empty((w.M, w.N), dtype=x.dtype, device=dev)
+    d = sage.W8A8Desc.for_tensors(x, wt, y)
+    xq, xs, wq, ws = sage.w8a8_buffers(d, dev)
+    stream = torch.cuda.current_stream()
+    sage.sage_w8a8_quantize_weight(d, wt, wq, ws, stream)
+    steps = 2 if args.profile else args.steps
+    warm = 1 if args.profile else args.warmup
+    parts = (lambda: sage.sage_w8a8_quantize_act(d, x, xq, xs, stream),
+             lambda: sage.sage_w8a8_gemm(d, xq, xs, wq, ws, bias, y, stream))
+    ms_step, ms_quant, ms_gemm = time_path(torch, parts, stream, steps, warm)
+    ops = w.ops()
+    qbytes = w.M * w.K * 2 + w.M * w.K + w.M * (w.K // 128) * 4  # read X, write codes and scales
+    record = {
+        "metric": "per-block W8A8 linear layer TOPS (2·M·N·K), 14B-class video-DiT FFN shape",
+        "value": round(ops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8+" + w.dtype,
+        "data": "synthetic (seeded Gaussian, 1% activation channels x8)",
+        "config": {"workload": "linear", "M": w.M, "N": w.N, "K": w.K, "in_dtype": w.dtype, "bias": True,
+                   "ops_per_step": ops, "pct_int8_peak": round(100 * ops / (ms_step * 1e-3) / 1e12 / INT8_PEAK_TOPS, 2)},
+        "roofline": {"bound": "mfma", "kernel": "w8a8_gemm_kernel", "achieved": round(ops / (ms_gemm * 1e-3) / 1e12, 2),
+                     "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
+                     "frac": round(ops / (ms_gemm * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
+                     "traffic": kernel_traffic("linear", "16"), "ms_per_launch": round(ms_gemm, 4)},
+        "quantize": {"ms": round(ms_quant, 4), "algorithmic_bytes": qbytes,
+                     "GB_per_s": round(qbytes / (ms_quant * 1e-3) / 1e9, 1),
+                     "hbm_frac": round(qbytes / (ms_quant * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+    }
+    if not (args.no_cpu or args.profile):
+        from threadpoolctl import threadpool_info
+        from oracle import w8a8
+        rows = workloads.sample_rows(w, 1024)
+        X = x[rows].float().cpu().numpy()
+        W = wt.float().cpu().numpy()
+        B = bias.float().cpu().numpy()
+        t0 = time.perf_counter()
+        oxq, odx = w8a8.quantize_act(X)
+        owq, odw = w8a8.quantize_weight(W)
+        y64, _ = w8a8.gemm_exact(oxq, odx, owq, odw, B)
+        t_cpu = time.perf_counter() - t0
+        ref = w8a8.linear_fp64(X, W, B)
+        yg = y[rows].float().cpu().numpy()
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        record["cpu_baseline"] = {"value": round(2 * len(rows) * w.N * w.K / t_cpu / 1e12, 6), "unit": "TOPS",
+                                  "cores": threads, "kind": "oracle",
+                                  "sample": f"{len(rows)} rows of X against all of W: quantize X and W + exact "
+                                            f"quantized product, {t_cpu:.1f} s"}
+        cos = float((yg * ref).sum() / np.sqrt((yg ** 2).sum() * (ref ** 2).sum()))
+        record["parity"] = {"rows": len(rows), "max_abs_vs_exact_quantized": float(np.abs(yg - y64).max()),
+                            "cosine_vs_fp64": round(cos, 6)}
     print(json.dumps(record), flush=True)
 
 

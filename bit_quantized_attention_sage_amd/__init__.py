@@ -57,8 +57,16 @@ class SageError(RuntimeError):
         self.status = status
 
 
+class sage_w8a8_desc(ctypes.Structure):
+    _fields_ = [("abi_version", ctypes.c_int32), ("dtype", ctypes.c_int32), ("M", ctypes.c_int32),
+                ("N", ctypes.c_int32), ("K", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("x_stride", ctypes.c_int64), ("w_stride", ctypes.c_int64), ("y_stride", ctypes.c_int64),
+                ("flags", ctypes.c_uint32)]
+
+
 _lib = None
 _DESC_P = ctypes.POINTER(sage_attn_desc)
+_WDESC_P = ctypes.POINTER(sage_w8a8_desc)
 _BUFS_P = ctypes.POINTER(sage_quant_bufs)
 
 
@@ -91,6 +99,12 @@ def load(path=None):
                                                   ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]),
         "sage_attn_debug_convert": (ctypes.c_int, [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                                    ctypes.c_int64, ctypes.c_void_p]),
+        "sage_w8a8_sizes": (ctypes.c_int, [_WDESC_P] + [ctypes.POINTER(ctypes.c_size_t)] * 4),
+        "sage_w8a8_quantize_weight": (ctypes.c_int, [_WDESC_P, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                                     ctypes.c_void_p]),
+        "sage_w8a8_quantize_act": (ctypes.c_int, [_WDESC_P, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                                  ctypes.c_void_p]),
+        "sage_w8a8_gemm": (ctypes.c_int, [_WDESC_P] + [ctypes.c_void_p] * 7),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -292,3 +306,75 @@ def attention(q, k, v, pv_mode=SAGE_PV_16, frame_len=0, kv_len=None, q_pos0=None
     ws = workspace if workspace is not None else new_workspace(desc, q.device)
     sage_attn_fwd(desc, q, k, v, out, ws, stream)
     return out
+
+
+# ---------------------------------------------------------------- W8A8 linear
+class W8A8Desc:
+    """A sage_w8a8_desc for Y [M,N] = X [M,K] W [N,K]^T (+ bias)."""
+
+    def __init__(self, M, N, K, dtype, x_stride=None, w_stride=None, y_stride=None, flags=0):
+        c = sage_w8a8_desc()
+        c.abi_version = SAGE_ATTN_ABI_VERSION
+        c.dtype = dtype
+        c.M, c.N, c.K, c.reserved = M, N, K, 0
+        c.x_stride = K if x_stride is None else x_stride
+        c.w_stride = K if w_stride is None else w_stride
+        c.y_stride = N if y_stride is None else y_stride
+        c.flags = flags
+        self.c = c
+        self.M, self.N, self.K, self.dtype = M, N, K, dtype
+        self.M_pad = (M + 127) // 128 * 128
+
+    @property
+    def ptr(self):
+        return ctypes.byref(self.c)
+
+    @classmethod
+    def for_tensors(cls, x, w, y=None, **kw):
+        """Describe X [M,K] and W [N,K] (rows contiguous in the channel dim)."""
+        M, K = x.shape
+        N = w.shape[0]
+        for t in (x, w) + ((y,) if y is not None else ()):
+            if t.stride(1) != 1:
+                raise ValueError("rows must be contiguous")
+        if x.dtype not in (torch.float16, torch.bfloat16) or w.dtype != x.dtype:
+            raise ValueError("x and w must share float16 or bfloat16")
+        dt = SAGE_F16 if x.dtype == torch.float16 else SAGE_BF16
+        return cls(M, N, K, dt, x_stride=x.stride(0), w_stride=w.stride(0),
+                   y_stride=y.stride(0) if y is not None else None, **kw)
+
+
+def sage_w8a8_sizes(desc):
+    """(xq, x_scale, wq, w_scale) sizes in bytes."""
+    v = [ctypes.c_size_t() for _ in range(4)]
+    _check(load().sage_w8a8_sizes(desc.ptr, *[ctypes.byref(x) for x in v]), "sage_w8a8_sizes")
+    return tuple(x.value for x in v)
+
+
+def w8a8_buffers(desc, device="cuda"):
+    """Device tensors for the quantized operands: xq [M_pad,K] int8,
+    x_scale [K/128, M_pad] float32, wq [N,K] int8, w_scale [N/128, K/128] float32."""
+    M_pad, N, K = desc.M_pad, desc.N, desc.K
+    return (torch.empty((M_pad, K), dtype=torch.int8, device=device),
+            torch.empty((K // 128, M_pad), dtype=torch.float32, device=device),
+            torch.empty((N, K), dtype=torch.int8, device=device),
+            torch.empty((N // 128, K // 128), dtype=torch.float32, device=device))
+
+
+def sage_w8a8_quantize_weight(desc, w, wq, w_scale, stream=None):
+    _check(load().sage_w8a8_quantize_weight(desc.ptr, ctypes.c_void_p(w.data_ptr()), ctypes.c_void_p(wq.data_ptr()),
+                                            ctypes.c_void_p(w_scale.data_ptr()), _stream(stream)),
+           "sage_w8a8_quantize_weight")
+
+
+def sage_w8a8_quantize_act(desc, x, xq, x_scale, stream=None):
+    _check(load().sage_w8a8_quantize_act(desc.ptr, ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(xq.data_ptr()),
+                                         ctypes.c_void_p(x_scale.data_ptr()), _stream(stream)),
+           "sage_w8a8_quantize_act")
+
+
+def sage_w8a8_gemm(desc, xq, x_scale, wq, w_scale, bias, y, stream=None):
+    _check(load().sage_w8a8_gemm(desc.ptr, ctypes.c_void_p(xq.data_ptr()), ctypes.c_void_p(x_scale.data_ptr()),
+                                 ctypes.c_void_p(wq.data_ptr()), ctypes.c_void_p(w_scale.data_ptr()),
+                                 ctypes.c_void_p(bias.data_ptr() if bias is not None else None),
+                                 ctypes.c_void_p(y.data_ptr()), _stream(stream)), "sage_w8a8_gemm")

@@ -3,8 +3,8 @@
     python -m bit_quantized_attention_sage_amd.build
 
 Every translation unit is compiled with packed-FP32 instructions disabled;
-the quantize unit additionally with floating-point contraction off, so each
-of its operations rounds exactly as written.
+the quantize and W8A8 units additionally with floating-point contraction off,
+so each of their operations rounds exactly as written.
 """
 
 import os
@@ -23,6 +23,7 @@ COMMON = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
 UNITS = {
     "quant.hip": ["-ffp-contract=off"],
     "attn.hip": [],
+    "w8a8.hip": ["-ffp-contract=off"],
     "api.cpp": ["-x", "hip"],
 }
 

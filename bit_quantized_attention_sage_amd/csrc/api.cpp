@@ -10,6 +10,7 @@
 #include <string>
 
 #include "kernels.h"
+#include "../../include/sage_w8a8.h"
 
 namespace {
 
@@ -337,6 +338,43 @@ int quantize_impl(const sage_attn_desc* desc, const void* q, const void* k, cons
   }
 }
 
+int w8a8_plan(const sage_w8a8_desc* d, sage::W8A8Launch* L) {
+  if (!d) return fail(SAGE_E_NULL, "desc is NULL");
+  if (d->abi_version != SAGE_ATTN_ABI_VERSION)
+    return fail(SAGE_E_VERSION, "abi_version " + std::to_string(d->abi_version) + " != " +
+                                    std::to_string(SAGE_ATTN_ABI_VERSION));
+  if (d->dtype != SAGE_F16 && d->dtype != SAGE_BF16) return fail(SAGE_E_DTYPE, "dtype must be SAGE_F16 or SAGE_BF16");
+  if (d->reserved != 0) return fail(SAGE_E_UNSUPPORTED, "reserved must be 0");
+  if (d->M < 1 || d->N < SAGE_W8A8_GROUP || d->K < SAGE_W8A8_GROUP || d->N % SAGE_W8A8_GROUP || d->K % SAGE_W8A8_GROUP)
+    return fail(SAGE_E_SHAPE, "M >= 1; N and K positive multiples of 128");
+  const int64_t mpad = pad128(d->M);
+  if (mpad * d->K >= (int64_t{1} << 31) || static_cast<int64_t>(d->N) * d->K >= (int64_t{1} << 31))
+    return fail(SAGE_E_SHAPE, "M_pad * K and N * K must be below 2^31");
+  if (d->x_stride < d->K || d->w_stride < d->K || d->y_stride < d->N || d->x_stride % 8 || d->w_stride % 8 ||
+      d->y_stride % 8)
+    return fail(SAGE_E_STRIDE, "row strides must cover a row and be multiples of 8 elements");
+  L->dtype = d->dtype;
+  L->M = d->M;
+  L->M_pad = static_cast<int>(mpad);
+  L->N = d->N;
+  L->K = d->K;
+  L->xs = d->x_stride;
+  L->ws = d->w_stride;
+  L->ys = d->y_stride;
+  return SAGE_OK;
+}
+
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int finish_w8a8(hipError_t e, const sage_w8a8_desc* d, hipStream_t st) {
+  if (e == hipSuccess && (d->flags & SAGE_FLAG_DEBUG_SYNC)) {
+    e = hipStreamSynchronize(st);
+    if (e == hipSuccess) e = hipGetLastError();
+  }
+  if (e != hipSuccess) return fail(SAGE_E_HIP, hipGetErrorString(e));
+  return SAGE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -491,6 +529,69 @@ int sage_attn_debug_convert(int kind, const float* in, void* out, int64_t n, voi
     if (!in || !out) return fail(SAGE_E_NULL, "in/out is NULL");
     hipStream_t hs = static_cast<hipStream_t>(stream);
     return finish(sage::launch_convert(kind, in, out, n, hs), nullptr, hs);
+  } catch (const std::exception& e) {
+    return fail(SAGE_E_HIP, e.what());
+  }
+}
+
+// ---------------------------------------------------------------- W8A8 linear
+int sage_w8a8_sizes(const sage_w8a8_desc* desc, size_t* xq_bytes, size_t* x_scale_bytes, size_t* wq_bytes,
+                    size_t* w_scale_bytes) {
+  try {
+    sage::W8A8Launch L{};
+    const int s = w8a8_plan(desc, &L);
+    if (s != SAGE_OK) return s;
+    const size_t nkb = static_cast<size_t>(L.K) / SAGE_W8A8_GROUP;
+    if (xq_bytes) *xq_bytes = static_cast<size_t>(L.M_pad) * L.K;
+    if (x_scale_bytes) *x_scale_bytes = nkb * L.M_pad * 4;
+    if (wq_bytes) *wq_bytes = static_cast<size_t>(L.N) * L.K;
+    if (w_scale_bytes) *w_scale_bytes = static_cast<size_t>(L.N) / SAGE_W8A8_GROUP * nkb * 4;
+    return SAGE_OK;
+  } catch (const std::exception& e) {
+    return fail(SAGE_E_HIP, e.what());
+  }
+}
+
+int sage_w8a8_quantize_weight(const sage_w8a8_desc* desc, const void* w, int8_t* wq, float* w_scale, void* stream) {
+  try {
+    sage::W8A8Launch L{};
+    const int s = w8a8_plan(desc, &L);
+    if (s != SAGE_OK) return s;
+    if (!w || !wq || !w_scale) return fail(SAGE_E_NULL, "w, wq and w_scale must be non-NULL");
+    if (!aligned16(w) || !aligned16(wq) || !aligned4(w_scale)) return fail(SAGE_E_ALIGN, "w, wq 16-byte and w_scale 4-byte aligned");
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    return finish_w8a8(sage::launch_w8a8_quant_weight(L, w, wq, w_scale, hs), desc, hs);
+  } catch (const std::exception& e) {
+    return fail(SAGE_E_HIP, e.what());
+  }
+}
+
+int sage_w8a8_quantize_act(const sage_w8a8_desc* desc, const void* x, int8_t* xq, float* x_scale, void* stream) {
+  try {
+    sage::W8A8Launch L{};
+    const int s = w8a8_plan(desc, &L);
+    if (s != SAGE_OK) return s;
+    if (!x || !xq || !x_scale) return fail(SAGE_E_NULL, "x, xq and x_scale must be non-NULL");
+    if (!aligned16(x) || !aligned16(xq) || !aligned4(x_scale)) return fail(SAGE_E_ALIGN, "x, xq 16-byte and x_scale 4-byte aligned");
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    return finish_w8a8(sage::launch_w8a8_quant_act(L, x, xq, x_scale, hs), desc, hs);
+  } catch (const std::exception& e) {
+    return fail(SAGE_E_HIP, e.what());
+  }
+}
+
+int sage_w8a8_gemm(const sage_w8a8_desc* desc, const int8_t* xq, const float* x_scale, const int8_t* wq,
+                   const float* w_scale, const void* bias, void* y, void* stream) {
+  try {
+    sage::W8A8Launch L{};
+    const int s = w8a8_plan(desc, &L);
+    if (s != SAGE_OK) return s;
+    if (!xq || !x_scale || !wq || !w_scale || !y) return fail(SAGE_E_NULL, "xq, x_scale, wq, w_scale and y must be non-NULL");
+    if (!aligned16(xq) || !aligned16(wq) || !aligned16(y) || (bias && !aligned16(bias)) || !aligned4(x_scale) ||
+        !aligned4(w_scale))
+      return fail(SAGE_E_ALIGN, "xq, wq, y, bias 16-byte and scales 4-byte aligned");
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    return finish_w8a8(sage::launch_w8a8_gemm(L, xq, x_scale, wq, w_scale, bias, y, hs), desc, hs);
   } catch (const std::exception& e) {
     return fail(SAGE_E_HIP, e.what());
   }

@@ -53,22 +53,8 @@ constexpr int MASKED = static_cast<int>(0xFF800000u);
 // fma(F, c 2^26, fma(-F0, c 2^26, -mref)).
 constexpr int SBIAS = 0x3E22F983;
 
-// Key held by row r of subtile u of a chunk's A operand (see above).
-__device__ __forceinline__ int a_row_key(int r, int u) {
-  return 32 * u + 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3);
-}
-
-// 16-byte granule swizzle of the K chunk in LDS: granule g of key k is
-// stored at slot g ^ swz(k).  A ds_read_b128 is served 16 lanes at a time
-// from 64 four-byte banks; the 16 keys such a group reads (a_row_key order:
-// {0..3, 16..19, 4..7, 20..23} + 8t) then land on 16 distinct 16-byte bank
-// slots.  The same holds for 8-lane groups over 32 banks.
-template <int D>
-__device__ __forceinline__ int k_swz(int key) {
-  const int b0 = key & 1, b1 = (key >> 1) & 1, b2 = (key >> 2) & 1, b4 = (key >> 4) & 1;
-  if constexpr (D == 128) return b1 | (b4 << 1) | ((b0 ^ b2) << 2);
-  else return (b1 ^ b2) | (b4 << 1);
-}
+// a_row_key and k_swz (common.h) give the A operand's row order and the
+// chunk's LDS swizzle.
 
 // First k-step of an S chain: A B + SBIAS, the bias as the MFMA's inline
 // accumulator constant.  (Written out because the compiler, seeing the same

@@ -122,6 +122,27 @@ __device__ __forceinline__ int wave_min_i(int v) {
   return v;
 }
 
+// Row of a 64-row tile that row r of subtile u of a 32x32x32 i8 MFMA's A
+// operand loads.  With this order, accumulator register i of lane l (output
+// row 8*(i/4) + 4*(l/32) + i%4) holds tile row 32*u + 16*(l/32) + i: each
+// lane half gets 16 consecutive tile rows.
+__device__ __forceinline__ int a_row_key(int r, int u) {
+  return 32 * u + 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3);
+}
+
+// 16-byte granule swizzle of a 64-row tile of D bytes per row in LDS:
+// granule g of row k is stored at slot g ^ swz(k).  A ds_read_b128 is served
+// 16 lanes at a time from 64 four-byte banks; the 16 rows such a group reads
+// (a_row_key order: {0..3, 16..19, 4..7, 20..23} + 8t) then land on 16
+// distinct 16-byte bank slots.  The same holds for 8-lane groups over 32
+// banks.
+template <int D>
+__device__ __forceinline__ int k_swz(int key) {
+  const int b0 = key & 1, b1 = (key >> 1) & 1, b2 = (key >> 2) & 1, b4 = (key >> 4) & 1;
+  if constexpr (D == 128) return b1 | (b4 << 1) | ((b0 ^ b2) << 2);
+  else return (b1 ^ b2) | (b4 << 1);
+}
+
 // Logical tile index of a physical workgroup id so that the workgroups one XCD
 // runs (ids x, x+8, x+16, ... go to XCD x) form one contiguous logical range:
 // neighbouring query tiles of the same head then share K/V in that XCD's L2.

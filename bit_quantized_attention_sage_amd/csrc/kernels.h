@@ -51,6 +51,18 @@ struct AttnLaunch {
   int64_t os[3];
 };
 
+// Per-block W8A8 linear layer (w8a8.hip).
+struct W8A8Launch {
+  int dtype;
+  int M, M_pad, N, K;  // M_pad = ceil(M/128)*128
+  int64_t xs, ws, ys;  // row strides (elements) of X, W and Y
+};
+
+hipError_t launch_w8a8_quant_act(const W8A8Launch& L, const void* x, int8_t* xq, float* xscale, hipStream_t st);
+hipError_t launch_w8a8_quant_weight(const W8A8Launch& L, const void* w, int8_t* wq, float* wscale, hipStream_t st);
+hipError_t launch_w8a8_gemm(const W8A8Launch& L, const int8_t* xq, const float* xscale, const int8_t* wq,
+                            const float* wscale, const void* bias, void* y, hipStream_t st);
+
 hipError_t launch_quantize(const QuantLaunch& L, hipStream_t st);
 hipError_t launch_attention(const AttnLaunch& L, hipStream_t st);
 hipError_t launch_debug_scores(const AttnLaunch& L, const int32_t* tiles, int ntiles,

@@ -13,6 +13,8 @@ from oracle import constants as oc
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "sage_attn.h")
+HEADERS = [os.path.join(ROOT, "include", f) for f in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if f.endswith(".h")]
 
 
 @pytest.fixture(scope="module")
@@ -23,15 +25,20 @@ def lib():
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(sage_attn_\w+)\s*\(", text)))
+    """Every function declared by include/*.h."""
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(sage_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_the_boundary():
     names = declared_functions()
     for must in ("sage_attn_quantize", "sage_attn_fwd", "sage_attn_fwd_quantized",
-                 "sage_attn_workspace_size", "sage_attn_quant_layout", "sage_attn_debug_scores"):
+                 "sage_attn_workspace_size", "sage_attn_quant_layout", "sage_attn_debug_scores",
+                 "sage_attn_quantize_frames", "sage_w8a8_quantize_weight", "sage_w8a8_quantize_act",
+                 "sage_w8a8_gemm", "sage_w8a8_sizes"):
         assert must in names
 
 
@@ -175,3 +182,28 @@ def test_block_mask_binding_checks_its_shape():
         sage.Desc(1, 2, 100, 150, 64, sage.SAGE_F16, block_mask=m[:, :, :, :2])
     with pytest.raises(ValueError):
         sage.Desc(1, 2, 100, 150, 64, sage.SAGE_F16, block_mask=m.bool())
+
+
+def _w8(**kw):
+    base = dict(M=300, N=256, K=384, dtype=sage.SAGE_BF16)
+    base.update(kw)
+    return sage.W8A8Desc(**base)
+
+
+def test_w8a8_sizes_and_validation(lib):
+    xq, xs, wq, ws = sage.sage_w8a8_sizes(_w8())
+    assert (xq, xs, wq, ws) == (384 * 384, 3 * 384 * 4, 256 * 384, 2 * 3 * 4)
+    for kw, code in [(dict(N=200), 2), (dict(K=100), 2), (dict(M=0), 2), (dict(dtype=4), 3),
+                     (dict(x_stride=200), 4), (dict(y_stride=260), 4), (dict(M=1 << 22, K=1024), 2)]:
+        n = ctypes.c_size_t()
+        st = lib.sage_w8a8_sizes(_w8(**kw).ptr, ctypes.byref(n), None, None, None)
+        assert st == code, (kw, st, lib.sage_attn_last_error())
+    d = _w8()
+    d.c.abi_version = 1
+    assert lib.sage_w8a8_sizes(d.ptr, None, None, None, None) == 9
+    d = _w8()
+    assert lib.sage_w8a8_gemm(d.ptr, None, None, None, None, None, None, None) == 1
+    fake = ctypes.c_void_p(4096 + 8)  # misaligned; never dereferenced
+    ok = ctypes.c_void_p(4096)
+    assert lib.sage_w8a8_gemm(d.ptr, ok, ok, ok, ok, None, fake, None) == 5
+    assert lib.sage_w8a8_quantize_act(d.ptr, fake, ok, ok, None) == 5

@@ -32,6 +32,11 @@ stand in for them, with the token grids of such clips:
            for the sparse branch of sparse attention built on SageAttention
            (Vidu S1 blog, section "Infra"), whose predictor the pages do not
            give.
+  linear   the per-block W8A8 linear layer on the large workload's tokens:
+           X [75600, 5120] (1% of channels x8, as activation outliers),
+           W [13824, 5120] ~ N(0, 0.02^2), bias ~ N(0, 0.1^2), bf16 -- the
+           shape of a 14B-class video DiT's feed-forward up-projection (the
+           pages' 14B text/image-to-video models; TurboDiffusion digests).
 
 Values are N(0,1) float32, then rounded to the 16-bit dtype.  Each (tensor,
 batch, head) slice has its own seed, so any subset of heads can be drawn on
@@ -133,6 +138,8 @@ class Workload:
 
 def get(name, **override):
     """The named workload (see module docstring), fields overridable."""
+    if name == "linear":
+        return get_linear(name, **override)
     if name == "tiny":
         w = Workload("tiny", 1, 2, 1024, 1024, 64, "f16", 0, seed=101, k_offset_std=2.0)
     elif name == "small":
@@ -164,7 +171,7 @@ def get(name, **override):
     return w
 
 
-NAMES = ("tiny", "small", "large", "stream", "batched", "window", "sparse")
+NAMES = ("tiny", "small", "large", "stream", "batched", "window", "sparse", "linear")
 
 
 _MASKS = {}
@@ -181,6 +188,54 @@ def block_mask(w):
         shape = (w.B, w.H, -(-w.Nq // 128), -(-w.Nkv // 64))
         _MASKS[key] = (rng.random(shape, dtype=np.float32) < w.block_density).astype(np.uint8)
     return _MASKS[key]
+
+
+@dataclass
+class LinearWorkload:
+    name: str
+    M: int
+    N: int
+    K: int
+    dtype: str
+    seed: int
+    outlier_frac: float = 0.0
+    frame_len: int = 0        # (for sample_rows)
+
+    @property
+    def Nq(self):
+        return self.M
+
+    @property
+    def torch_dtype(self):
+        return torch.float16 if self.dtype == "f16" else torch.bfloat16
+
+    def ops(self):
+        """2 M N K: one multiply and one add per term of X W^T."""
+        return 2 * self.M * self.N * self.K
+
+
+def get_linear(name, **override):
+    if name != "linear":
+        raise KeyError(name)
+    w = LinearWorkload("linear", 75600, 13824, 5120, "bf16", seed=707, outlier_frac=0.01)
+    for k, v in override.items():
+        setattr(w, k, v)
+    return w
+
+
+def make_linear(w, device="cpu"):
+    """X [M,K], W [N,K], bias [N] of a linear workload on ``device``."""
+    out = {}
+    for name, shape, std in (("x", (w.M, w.K), 1.0), ("w", (w.N, w.K), 0.02), ("bias", (w.N,), 0.1)):
+        g = torch.Generator(device=device)
+        g.manual_seed(_slice_seed(w.seed, name, 0, 0))
+        t = torch.randn(shape, generator=g, device=device, dtype=torch.float32) * std
+        if name == "x" and w.outlier_frac:
+            n = int(round(w.outlier_frac * w.K))
+            idx = np.random.default_rng(w.seed * 7 + 4).choice(w.K, size=n, replace=False)
+            t[:, torch.from_numpy(idx).to(device)] *= 8
+        out[name] = t.to(w.torch_dtype)
+    return out
 
 
 def _slice_seed(seed, tensor, b, h):
