@@ -59,20 +59,20 @@ def parse():
 
 
 def kernel_traffic(workload, pv):
-    """HBM bytes per launch of the fused kernel from profiles/traffic.json (FETCH_SIZE and
-    WRITE_SIZE scaled by the plain-copy factors), only if those counters were taken on
-    the current kernel source; else None."""
+    """HBM bytes per launch of the workload's dominant kernel from
+    profiles/traffic.json (FETCH_SIZE and WRITE_SIZE scaled by the plain-copy
+    factors), only if those counters were taken on the current source of that
+    kernel (sha256 of the files the record lists); else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
-    t = json.load(open(path))
-    h = hashlib.sha256()
-    for f in t["source_files"]:
-        h.update(open(os.path.join(ROOT, f), "rb").read())
-    if h.hexdigest() != t["source_sha256"]:
+    rec = json.load(open(path))["launches"].get(f"{workload}/{pv}")
+    if rec is None:
         return None
-    rec = t["launches"].get(f"{workload}/{pv}")
-    return None if rec is None else rec["bytes"]
+    h = hashlib.sha256()
+    for f in rec["source_files"]:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return rec["bytes"] if h.hexdigest() == rec["source_sha256"] else None
 
 
 def step_parts(sage, w, desc, q, k, v, o, bufs, stream):
@@ -267,6 +267,12 @@ def main_linear(args, torch, sage, workloads):
     xq, xs, wq, ws = sage.w8a8_buffers(d, dev)
     stream = torch.cuda.current_stream()
     sage.sage_w8a8_quantize_weight(d, wt, wq, ws, stream)
+    if args.calibrate_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     steps = 2 if args.profile else args.steps
     warm = 1 if args.profile else args.warmup
     parts = (lambda: sage.sage_w8a8_quantize_act(d, x, xq, xs, stream),

@@ -23,7 +23,8 @@ COMMON = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
 UNITS = {
     "quant.hip": ["-ffp-contract=off"],
     "attn.hip": [],
-    "w8a8.hip": ["-ffp-contract=off"],
+    # int32 MFMA results are read by the VALU every K block: keep them in VGPRs
+    "w8a8.hip": ["-ffp-contract=off", "-mllvm", "-amdgpu-mfma-vgpr-form"],
     "api.cpp": ["-x", "hip"],
 }
 
