@@ -207,3 +207,11 @@ def test_w8a8_sizes_and_validation(lib):
     ok = ctypes.c_void_p(4096)
     assert lib.sage_w8a8_gemm(d.ptr, ok, ok, ok, ok, None, fake, None) == 5
     assert lib.sage_w8a8_quantize_act(d.ptr, fake, ok, ok, None) == 5
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    """No CPU fallback: without the built library, loading it (which every
+    entry point does first) raises."""
+    monkeypatch.setattr(sage, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        sage.load(str(tmp_path / "libsage_attn.so"))
