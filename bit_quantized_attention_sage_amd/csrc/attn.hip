@@ -352,7 +352,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
   const int h2 = lane >> 5;
 
   // ---- work item: (batch by decreasing kv_len, head, split, query tile)
-  const int L = xcd_remap(blockIdx.x, A.total);
+  const int L = xcd_group_remap(blockIdx.x, A.total, A.nqt);  // groups: the tiles of one (b, h, split)
   const int per_b = A.H * A.splits * A.nqt;
   const int b = A.order[L / per_b];
   int rem = L % per_b;

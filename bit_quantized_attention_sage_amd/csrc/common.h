@@ -152,4 +152,19 @@ __device__ __forceinline__ int xcd_remap(int pid, int total) {
   return x * q + (x < r ? x : r) + k;
 }
 
+// Logical tile index of a physical workgroup id when the logical order is a
+// sequence of groups of `gsize` consecutive tiles that should share an XCD
+// (the query tiles of one head share its K and V in that XCD's L2).  Groups
+// are dealt round-robin to the 8 XCDs -- XCD x, whose k-th workgroup is
+// physical id 8k + x, runs groups x, x + 8, ... in order, each group's tiles
+// consecutively -- so that work ordered by decreasing size is spread evenly
+// over the XCDs.  Ids beyond the last complete round of 8 groups map to
+// themselves (a bijection on [0, total)).
+__device__ __forceinline__ int xcd_group_remap(int pid, int total, int gsize) {
+  const int full = total / (8 * gsize) * (8 * gsize);
+  if (pid >= full) return pid;
+  const int x = pid % 8, k = pid / 8;
+  return (8 * (k / gsize) + x) * gsize + k % gsize;
+}
+
 }  // namespace sage
