@@ -24,6 +24,8 @@ SAGE_F16, SAGE_BF16 = 0, 1
 SAGE_PV_16, SAGE_PV_FP8 = 0, 1
 SAGE_FLAG_DEBUG_SYNC = 0x1
 SAGE_MAX_BATCH = 128
+SAGE_MAX_SPLITS = 16
+SAGE_MAX_MASK_CHUNKS = 4096
 STATUS = {0: "SAGE_OK", 1: "SAGE_E_NULL", 2: "SAGE_E_SHAPE", 3: "SAGE_E_DTYPE", 4: "SAGE_E_STRIDE",
           5: "SAGE_E_ALIGN", 6: "SAGE_E_MASK", 7: "SAGE_E_UNSUPPORTED", 8: "SAGE_E_WORKSPACE",
           9: "SAGE_E_VERSION", 10: "SAGE_E_HIP"}

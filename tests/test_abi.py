@@ -42,6 +42,13 @@ def test_header_declares_the_boundary():
         assert must in names
 
 
+def test_binding_limits_match_the_header():
+    text = open(HEADER).read()
+    for name in ("SAGE_MAX_BATCH", "SAGE_MAX_SPLITS", "SAGE_MAX_MASK_CHUNKS"):
+        m = re.search(r"#define\s+%s\s+(\d+)" % name, text)
+        assert m and int(m.group(1)) == getattr(sage, name), name
+
+
 def test_every_declared_symbol_is_exported(lib):
     raw = ctypes.CDLL(sage.LIB_PATH)
     for name in declared_functions():

@@ -1,0 +1,157 @@
+"""GPU edge cases through the C ABI: degenerate values, the scheme's special
+cases with closed forms, and the largest batch and split counts.
+
+* Q = 0: every code and scale of Q is 0, so every score is 0 and every
+  visible key gets the same weight: each output row is the mean of V^ (V in
+  16-bit mode, its FP8 reconstruction otherwise) over the row's visible keys,
+  rounded to the output type.
+* V constant along the keys: the output is that constant exactly (the row
+  sums l are taken from the same rounded weights that multiply V^).
+* K blocks equal to the mean: their smoothed codes and scale are 0, so their
+  scores are 0; checked against the emulation.
+* B = SAGE_MAX_BATCH with ragged frames, and kv_splits = SAGE_MAX_SPLITS.
+* Inputs of very large and very small magnitude.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import bit_quantized_attention_sage_amd as sage
+from oracle import quant, attention, codecs
+from oracle.constants import PV_16, PV_FP8
+from gpu_util import run_gpu, host, check_quantized, emulate_like_gpu, compare_output, cosine, ulp16
+
+pytestmark = pytest.mark.gpu
+
+
+def _rand(shape, seed, scale=1.0):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(shape, generator=g) * scale).to(torch.bfloat16)
+
+
+def _close(og, o64, pv_mode, o_abs=None):
+    mx, excess, frac, rel, rel_bound = compare_output(og, o64, "bf16", pv_mode, o_abs)
+    print(f"  max-abs {mx:.3e} excess {excess:.2e} rel-L2 {rel:.3e}", flush=True)
+    assert excess <= 0
+    assert rel <= rel_bound
+
+
+@pytest.mark.parametrize("pv_mode", [PV_16, PV_FP8])
+def test_zero_queries_average_the_visible_values(lib, pv_mode):
+    B, H, Nq, Nkv, d, F = 2, 2, 300, 900, 128, 150
+    kv, qp = [900, 640], [600, 300]
+    q = torch.zeros((B, H, Nq, d), dtype=torch.bfloat16)
+    k, v = _rand((B, H, Nkv, d), 31), _rand((B, H, Nkv, d), 32)
+    for b in range(B):
+        k[b, :, kv[b]:] = 0
+        v[b, :, kv[b]:] = 0
+    out, views, desc, _, _ = run_gpu(q.cuda(), k.cuda(), v.cuda(), pv_mode, F, kv, qp)
+    assert not views["q_codes"].cpu().numpy().any() and not views["q_scale"].cpu().numpy().any()
+    V = host(v)
+    if pv_mode == PV_FP8:
+        vc, ve, _ = quant.quantize_v_fp8(V, kv)
+        V = quant.dequant_v_fp8(vc, ve)
+    ref = np.empty((B, H, Nq, d))
+    for b in range(B):
+        for i in range(Nq):
+            end = min(kv[b], ((qp[b] + i) // F + 1) * F)
+            ref[b, :, i] = V[b, :, :end].mean(axis=1)
+    og = host(out)
+    # the mean in float32 from rounded weights that are all equal: within
+    # float32 accumulation of it, then the output rounding
+    err = np.abs(og - ref)
+    bound = 0.5 * ulp16(ref, "bf16") * (1 + 2.0 ** -8) + 1e-5 * np.abs(V).max()
+    print(f"  max |O - mean V| {err.max():.3e}", flush=True)
+    assert (err <= bound).all()
+
+
+@pytest.mark.parametrize("pv_mode", [PV_16, PV_FP8])
+def test_constant_values_pass_through(lib, pv_mode):
+    """O = sum p~ c / sum p~ = c: the float32 sums differ from exact by far
+    less than half a bf16 spacing (or, in FP8 mode, c's e4m3 reconstruction,
+    itself a bf16 value), so the rounded output is the constant itself."""
+    B, H, Nq, Nkv, d = 1, 2, 200, 777, 128
+    q, k = _rand((B, H, Nq, d), 41), _rand((B, H, Nkv, d), 42, 2.0)
+    c = _rand((1, H, 1, d), 43)
+    v = c.expand(B, H, Nkv, d).contiguous()
+    out, _, _, _, _ = run_gpu(q.cuda(), k.cuda(), v.cuda(), pv_mode)
+    C = host(c)
+    if pv_mode == PV_FP8:
+        vc, ve, _ = quant.quantize_v_fp8(np.broadcast_to(C, (B, H, Nkv, d)).copy())
+        C = quant.dequant_v_fp8(vc, ve)[:, :, :1].astype(np.float32)
+        C = codecs.round_to(C, "bf16")
+    np.testing.assert_array_equal(host(out), np.broadcast_to(C, (B, H, Nq, d)))
+
+
+@pytest.mark.parametrize("pv_mode", [PV_16, PV_FP8])
+def test_key_blocks_at_the_mean_have_zero_codes(lib, pv_mode):
+    B, H, Nq, Nkv, d = 1, 2, 256, 640, 128
+    q, k, v = _rand((B, H, Nq, d), 51), _rand((B, H, Nkv, d), 52), _rand((B, H, Nkv, d), 53)
+    mu = torch.from_numpy(np.full((B, H, d), 0.5, np.float32))
+    k[:, :, 128:256] = 0.5                  # two whole 64-key blocks equal to the (given) mean
+    out, views, desc, _, _ = run_gpu(q.cuda(), k.cuda(), v.cuda(), pv_mode, k_mean_in=mu.cuda())
+    Q, K, V = host(q), host(k), host(v)
+    check_quantized(views, Q, K, V, pv_mode, "bf16", None, mu_in=mu.numpy())
+    assert not views["k_codes"].cpu().numpy()[:, :, 128:256].any()
+    assert not views["k_scale"].cpu().numpy()[:, :, 2:4].any()
+    o64 = emulate_like_gpu(Q, K, V, pv_mode, "bf16", desc, mu=mu.numpy())
+    o_abs = emulate_like_gpu(Q, K, np.abs(V), pv_mode, "bf16", desc, mu=mu.numpy()) if pv_mode == PV_FP8 else None
+    _close(host(out), o64, pv_mode, o_abs)
+
+
+def test_max_batch_ragged_frames(lib):
+    B, H, Nq, Nkv, d, F = sage.SAGE_MAX_BATCH, 1, 40, 400, 64, 50
+    rng = np.random.default_rng(61)
+    kv = [int(x) for x in rng.integers(Nq, Nkv + 1, B)]
+    qp = [int(rng.integers(0, x - Nq + 1)) for x in kv]
+    q, k, v = _rand((B, H, Nq, d), 62), _rand((B, H, Nkv, d), 63), _rand((B, H, Nkv, d), 64)
+    for b in range(B):
+        k[b, :, kv[b]:] = 0
+        v[b, :, kv[b]:] = 0
+    q, k, v = q.to(torch.float16), k.to(torch.float16), v.to(torch.float16)
+    out, views, desc, _, _ = run_gpu(q.cuda(), k.cuda(), v.cuda(), PV_16, F, kv, qp)
+    Q, K, V = host(q), host(k), host(v)
+    check_quantized(views, Q, K, V, PV_16, "f16", kv)
+    o64 = emulate_like_gpu(Q, K, V, PV_16, "f16", desc, F, kv, qp)
+    mx, excess, frac, rel, rel_bound = compare_output(host(out), o64, "f16", PV_16)
+    print(f"  B={B}: max-abs {mx:.3e} excess {excess:.2e}", flush=True)
+    assert excess <= 0 and rel <= rel_bound
+
+
+@pytest.mark.parametrize("pv_mode", [PV_16, PV_FP8])
+def test_max_splits(lib, pv_mode):
+    B, H, Nq, Nkv, d = 1, 2, 130, 3000, 128
+    q, k, v = _rand((B, H, Nq, d), 71), _rand((B, H, Nkv, d), 72), _rand((B, H, Nkv, d), 73)
+    out, _, desc, _, _ = run_gpu(q.cuda(), k.cuda(), v.cuda(), pv_mode, kv_splits=sage.SAGE_MAX_SPLITS)
+    assert sage.sage_attn_kv_splits(desc) == sage.SAGE_MAX_SPLITS
+    Q, K, V = host(q), host(k), host(v)
+    o64 = emulate_like_gpu(Q, K, V, pv_mode, "bf16", desc)
+    o_abs = emulate_like_gpu(Q, K, np.abs(V), pv_mode, "bf16", desc) if pv_mode == PV_FP8 else None
+    _close(host(out), o64, pv_mode, o_abs)
+
+
+@pytest.mark.parametrize("scale_qk,scale_v", [(30.0, 1e-3), (1e-3, 400.0)])
+def test_extreme_magnitudes(lib, scale_qk, scale_v):
+    """Large scores (a nearly one-hot softmax, exercising the lazy running
+    max) and tiny ones (nearly uniform), with V far from unit scale."""
+    B, H, Nq, Nkv, d = 1, 2, 200, 900, 128
+    q, k = _rand((B, H, Nq, d), 81, scale_qk), _rand((B, H, Nkv, d), 82, scale_qk)
+    v = _rand((B, H, Nkv, d), 83, scale_v)
+    out, views, desc, _, _ = run_gpu(q.cuda(), k.cuda(), v.cuda(), PV_16)
+    Q, K, V = host(q), host(k), host(v)
+    check_quantized(views, Q, K, V, PV_16, "bf16")
+    o64 = emulate_like_gpu(Q, K, V, PV_16, "bf16", desc)
+    og = host(out)
+    mx, excess, frac, rel, rel_bound = compare_output(og, o64, "bf16", PV_16)
+    print(f"  max-abs {mx:.3e} excess {excess:.2e} rel-L2 {rel:.3e}", flush=True)
+    assert excess <= 0 and rel <= rel_bound
+    # With a nearly one-hot softmax, INT8 error in the scores can move the
+    # weight between near-tied keys, so the scheme itself departs from fp64;
+    # the kernel must lose nothing beyond what the exact emulation loses.
+    o_ref = attention.attention_fp64(Q, K, V)
+    cs, cs_emul = cosine(og, o_ref), cosine(o64, o_ref)
+    print(f"  cosine vs fp64 {cs:.6f} (emulation {cs_emul:.6f})", flush=True)
+    assert cs >= cs_emul - 1e-3
+    if scale_qk < 1:
+        assert cs >= 0.999
