@@ -38,10 +38,11 @@ struct Plan {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Key chunks that query tile t of batch b visits (the fused kernel's list).
-int tile_chunks(const Plan& p, int b, int t) {
+// Key chunks that query tile t (rows [t*rows, t*rows + rows)) of batch b
+// visits (the fused kernel's list).
+int tile_chunks(const Plan& p, int b, int t, int rows) {
   const int kv = p.bi.kv_len[b], qp = p.bi.q_pos0[b], F = p.frame_len;
-  const int first = t * 128, last = std::min(t * 128 + 128, p.Nq) - 1;
+  const int first = t * rows, last = std::min(t * rows + rows, p.Nq) - 1;
   if (p.frame_stride == 0) {
     const int end = F > 0 ? std::min(kv, ((qp + last) / F + 1) * F) : kv;
     return (end + 63) / 64;
@@ -56,21 +57,24 @@ int tile_chunks(const Plan& p, int b, int t) {
 }
 
 // KV splits per query tile.  Work items (batch, head, split, tile) run as
-// rounds of SLOTS resident workgroups (256 CUs x 2), so the estimated time of
-// s splits is ceil(items / SLOTS) x (mean chunks per item + a prologue and
-// epilogue of about 3 chunk steps), plus for s > 1 the combine pass (reads
-// s fp32 partial outputs; one chunk step of a workgroup takes about 1.5 us at
+// rounds of SLOTS resident workgroups: 256-row ping-pong tiles one per CU,
+// or (block mask) 128-row tiles two per CU; either way a CU steps through
+// 8 waves' chunks at a time.  The estimated time of s splits is
+// ceil(items / SLOTS) x (mean chunks per item + a prologue and epilogue of
+// about 3 chunk steps), plus for s > 1 the combine pass (reads s fp32
+// partial outputs; one chunk step of a workgroup takes about 1.5 us at
 // d = 128, half that at d = 64).  Enough tiles for 4 rounds: no split.
 int choose_splits(const Plan& p) {
-  constexpr int SLOTS = 512;
-  const int nqt = p.Nq_pad / 128;
+  const bool pingpong = p.block_mask == nullptr;
+  const int SLOTS = pingpong ? 256 : 512, rows = pingpong ? 256 : 128;
+  const int nqt = (p.Nq + rows - 1) / rows;
   const int64_t items1 = static_cast<int64_t>(p.B) * p.H * nqt;
   if (items1 >= 4 * SLOTS) return 1;
   double total = 0.0;
   int longest = 1;
   for (int b = 0; b < p.B; ++b)
     for (int t = 0; t < nqt; ++t) {
-      const int n = tile_chunks(p, b, t);
+      const int n = tile_chunks(p, b, t, rows);
       total += n;
       longest = std::max(longest, n);
     }
@@ -405,7 +409,7 @@ int sage_attn_constant(const char* name, double* value) {
   const struct { const char* n; double v; } table[] = {
       {"BQ", sage::BQ}, {"BK", sage::BK}, {"VB", sage::VB}, {"QMAX", sage::QMAX},
       {"TAU", sage::TAU}, {"PSHIFT_FP8", sage::PSHIFT_FP8}, {"PSHIFT_16", sage::PSHIFT_16},
-      {"KMEAN_CHUNK", sage::KMEAN_CHUNK}};
+      {"KMEAN_CHUNK", sage::KMEAN_CHUNK}, {"CACHE_TILE", sage::CACHE_TILE}};
   for (const auto& e : table)
     if (strcmp(e.n, name) == 0) {
       *value = e.v;

@@ -10,11 +10,23 @@
 // "模型架构", "训练方法" and "Infra").  The scheme itself is this library's own
 // (the pages give none).
 //
-// Work decomposition.  One workgroup = 4 waves = one 128-row query block (one
-// Q scale) of one (b, h), optionally one of several KV splits.  Each wave owns
-// 32 query rows.  Keys are streamed in 64-key chunks (one K scale each)
-// through LDS; per chunk a wave runs 8 i8 MFMAs 32x32x32 for S, the softmax on
-// its 32x64 scores, and the P.V MFMAs.
+// Work decomposition.  Each wave owns 32 query rows.  Keys are streamed in
+// 64-key chunks (one K scale each) through LDS; per chunk a wave runs 8 i8
+// MFMAs 32x32x32 for S, the softmax on its 32x64 scores, and the P.V MFMAs.
+// Two shapes of workgroup, for one (b, h) and optionally one of several KV
+// splits:
+//  * ping-pong (contiguous keys, frame cache): 8 waves = two 128-row query
+//    blocks (two Q scales) sharing every staged K/V chunk.  Waves w and w+4
+//    sit on the same SIMD; group 0 (waves 0-3) runs one phase ahead of group 1,
+//    and each chunk step is two phases split by a barrier: the MFMAs, then the
+//    softmax.  So on every SIMD one wave's matrix work meets the other's
+//    vector work, which the hardware overlaps, instead of each wave
+//    interleaving both (measured on gfx950: one wave issues plain FP32 VALU
+//    ops every ~5 cycles, two every ~2.5; exp and the FP8 conversion take
+//    ~8.4 cycles per wave instruction either way).
+//  * 4 waves = one 128-row block (block-sparse tiles, whose kept chunks
+//    differ from block to block); each wave interleaves its own MFMAs and
+//    softmax.
 //
 // Register layouts (32x32 MFMA, lane l, h2 = l / 32, r32 = l % 32):
 //  * S^T = K Q^T: the B operand is Q^T, so lane l holds query r32 and channel
@@ -328,9 +340,11 @@ enum { KV_DENSE = 0,    // contiguous keys, every chunk up to the tile's range e
        KV_SPARSE = 2 }; // contiguous keys, only the chunks the block mask keeps
 constexpr int MAX_LIST = 4096;  // kept-chunk list of a tile (LDS, 2 bytes each)
 
-template <int D, int PV, int DT, int MODE>
-__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
+template <int D, int PV, int DT, int MODE, bool PP>
+__global__ __launch_bounds__(PP ? 512 : 256, PP ? 1 : 2) void attn_fwd_kernel(AttnArgs A) {
   constexpr bool CACHE = MODE == KV_CACHE, SPARSE = MODE == KV_SPARSE;
+  static_assert(!(PP && SPARSE), "the two query blocks of a ping-pong tile share one chunk list");
+  constexpr int NWAVE = PP ? 8 : 4;
   constexpr int NCB = D / 32;                    // 32-channel blocks of O
   constexpr int VBYTES = (PV == PVFP8) ? 1 : 2;  // bytes per V element
   constexpr int KB = 64 * D;                     // bytes of a K chunk
@@ -352,24 +366,31 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
   const int h2 = lane >> 5;
 
   // ---- work item: (batch by decreasing kv_len, head, split, query tile)
-  const int L = xcd_group_remap(blockIdx.x, A.total, A.nqt);  // groups: the tiles of one (b, h, split)
-  const int per_b = A.H * A.splits * A.nqt;
+  const int ntile = PP ? (A.nqt + 1) / 2 : A.nqt;             // tiles of NWAVE * 32 rows
+  const int L = xcd_group_remap(blockIdx.x, A.total, ntile);  // groups: the tiles of one (b, h, split)
+  const int per_b = A.H * A.splits * ntile;
   const int b = A.order[L / per_b];
   int rem = L % per_b;
-  const int h = rem / (A.splits * A.nqt);
-  rem %= A.splits * A.nqt;
-  const int split = rem / A.nqt;
-  const int qt = rem % A.nqt;
+  const int h = rem / (A.splits * ntile);
+  rem %= A.splits * ntile;
+  const int split = rem / ntile;
+  const int qt = rem % ntile;
   const int bh = b * A.H + h;
+  // this wave's group, its place in the group and its 128-row Q block (the
+  // second block of the last tile may lie past Nq: its rows load the last
+  // real block and store nothing)
+  const int grp = PP ? (w >> 2) : 0, w4 = w & 3;
+  const int qb = PP ? 2 * qt + grp : qt;
+  const int qbl = min(qb, A.nqt - 1);
 
   const int kv_len = A.bi.kv_len[b];
   const int q_pos0 = A.bi.q_pos0[b];
   const int F = A.frame_len, FS = CACHE ? A.frame_stride : 0;
 
   // ---- this lane's query row and the tile's first and last real rows
-  const int qi = qt * BQ + w * 32 + (lane & 31);
+  const int qi = qb * BQ + w4 * 32 + (lane & 31);
   const int qi_valid = min(qi, A.Nq - 1);
-  const int row_first = qt * BQ, row_last = min(qt * BQ + BQ, A.Nq) - 1;
+  const int row_first = (PP ? 2 * qt : qt) * BQ, row_last = min(row_first + NWAVE * 32, A.Nq) - 1;
 
   // ---- the key chunks this work item visits: list entry v is chunk v for
   // v < a0, else chunk b1 + (v - a0); the split takes entries [v_lo, v_hi).
@@ -480,8 +501,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
   };
 
   v4i qv[D / 32];
-  load_q<D>(qv, A.qc + (static_cast<int64_t>(bh) * A.Nq_pad + qi) * D, h2);
-  const float qsc = A.qscale[static_cast<int64_t>(bh) * A.nqt + qt] * A.sigma;
+  load_q<D>(qv, A.qc + (static_cast<int64_t>(bh) * A.Nq_pad + qbl * BQ + w4 * 32 + (lane & 31)) * D, h2);
+  const float qsc = A.qscale[static_cast<int64_t>(bh) * A.nqt + qbl] * A.sigma;
 
   WaveState<D, PV, DT> st;
 #pragma unroll
@@ -496,7 +517,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
   const float* ksc = A.kscale + static_cast<int64_t>(bh) * nkc;
 
   // Staging: raw buffer loads that write straight into LDS (no registers),
-  // issued one step ahead.  Lane l of DMA instruction i of wave w fills LDS
+  // issued one step ahead, by the four waves of group 0 (ping-pong) or of the
+  // workgroup.  Lane l of DMA instruction i of wave w fills LDS
   // granule (4i + w)*64 + l of the buffer; its global source is chosen so that
   // the buffer ends up in the swizzled layouts above.  Every chunk index is
   // clamped to the head's last padded chunk, so all reads stay inside the
@@ -526,6 +548,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
   }
   const int last = nkc - 1;  // chunk indices are clamped: prefetches past the end go unused
   auto dma_k = [&](int8_t* dst, int ch) {
+    if (PP && grp != 0) return;  // group 0 stages every chunk
     ch = min(ch, last);
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
@@ -534,6 +557,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
     }
   };
   auto dma_v = [&](uint8_t* dst, int ch) {
+    if (PP && grp != 0) return;
     ch = min(ch, last);
 #pragma unroll
     for (int i = 0; i < VI; ++i) {
@@ -570,6 +594,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
   // the softmax of entry n+1, so the matrix cores and the vector ALUs work
   // side by side; then the (rare) rescale by entry n+1's alpha, the (rare)
   // masking of S(n+2), the wait for this step's DMA and the barrier.
+  // Ping-pong: the region is two phases instead, the MFMAs (at raised wave
+  // priority, with the operand reads 8 ahead) and, after a barrier, the
+  // softmax; group 1 runs the same steps one phase behind group 0 (one extra
+  // barrier before its first step, group 0 one after its last), so the
+  // buffers a step fills are the ones both groups finished reading in the
+  // step before.
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
   v16i sa0{}, sa1{}, sb0{}, sb1{};
@@ -629,22 +659,44 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
     dma_v(v_wr, ch1);
     const int e_nxt = load_e(ch1);
     const float ks3 = load_ks(ch3);
-    qk_chunk<D>(k_rd, qv, lane, ns0, ns1);
-    st.pv(p_cur, v_rd, e_cur, lane);
-    const float alpha = st.softmax(cs0, cs1, c_mid, CHK ? has_c : true, p_nxt);
-    __builtin_amdgcn_sched_group_barrier(0x020, 2 + KI + VI, 0);  // the loads
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);            // the first operand reads
+    float alpha;
+    if constexpr (PP) {
+      __builtin_amdgcn_s_setprio(1);
+      qk_chunk<D>(k_rd, qv, lane, ns0, ns1);
+      st.pv(p_cur, v_rd, e_cur, lane);
+      __builtin_amdgcn_sched_group_barrier(0x020, 2 + KI + VI, 0);  // the loads
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);            // the first operand reads
 #pragma unroll
-    for (int g = 0; g < NQK + NPV; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, VPER, 0);  // a slice of the softmax
-      if (g + 4 < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // the next read
+      for (int g = 0; g < NQK + NPV; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // one MFMA
+        if (g + 8 < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // the next read
+      }
+      asm volatile("" : "+v"(ns0), "+v"(ns1));
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_s_barrier();  // end of the MFMA phase
+      __builtin_amdgcn_sched_barrier(0);
+      alpha = st.softmax(cs0, cs1, c_mid, CHK ? has_c : true, p_nxt);
+      p_nxt.pin();
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      qk_chunk<D>(k_rd, qv, lane, ns0, ns1);
+      st.pv(p_cur, v_rd, e_cur, lane);
+      alpha = st.softmax(cs0, cs1, c_mid, CHK ? has_c : true, p_nxt);
+      __builtin_amdgcn_sched_group_barrier(0x020, 2 + KI + VI, 0);  // the loads
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);            // the first operand reads
+#pragma unroll
+      for (int g = 0; g < NQK + NPV; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, VPER, 0);  // a slice of the softmax
+        if (g + 4 < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // the next read
+      }
+      // Pin the region's results here so that no earlier pass moves the S
+      // MFMAs or the softmax out of it.
+      asm volatile("" : "+v"(ns0), "+v"(ns1));
+      p_nxt.pin();
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // Pin the region's results here so that no earlier pass moves the S
-    // MFMAs or the softmax out of it.
-    asm volatile("" : "+v"(ns0), "+v"(ns1));
-    p_nxt.pin();
-    __builtin_amdgcn_sched_barrier(0);
     st.rescale(alpha);  // rare: some row's running max moved (after P(n) V(n))
     if constexpr (CHK) {
       if (n + 2 >= v_full) has_n = mask_chunk(n + 2, ns0, ns1);  // rare: S(n+2) is a boundary chunk
@@ -664,6 +716,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
   using Chk = std::integral_constant<bool, true>;
   if (J >= 1) {
     int left = J - 1;  // pipelined steps
+    if (PP && grp == 1 && left > 0) __builtin_amdgcn_s_barrier();  // one phase behind group 0
     if constexpr (!CACHE) {
       // the leading steps whose S(n+2) lies below v_full, in pairs
       for (int fast = min(J - 1, v_full - v_lo - 2); fast >= 2; fast -= 2) {
@@ -677,6 +730,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs A) {
       step(P1{}, Chk{}, sb0, sb1, hb, pb, sa0, sa1, ha, pa);
       left -= 2;
     }
+    if (PP && grp == 0 && J > 1) __builtin_amdgcn_s_barrier();  // as many barriers as group 1
     // the last entry's P.V (its V is in buffer (J-1)&1)
     if (left == 1) {
       step(P0{}, Chk{}, sa0, sa1, ha, pa, sb0, sb1, hb, pb);
@@ -808,7 +862,9 @@ static AttnArgs make_args(const AttnLaunch& L) {
   A.Nkv_pad = L.Nkv_pad;
   A.nqt = L.Nq_pad / BQ;
   A.splits = L.splits;
-  A.total = L.B * L.H * L.splits * A.nqt;
+  // work items: 256-row tiles for the ping-pong shape (no block mask), else
+  // 128-row blocks
+  A.total = L.B * L.H * L.splits * (L.block_mask ? A.nqt : (A.nqt + 1) / 2);
   A.sigma = L.sigma;
   A.frame_len = L.frame_len;
   A.frame_stride = L.frame_stride;
@@ -826,11 +882,11 @@ template <int D, int PV, int DT>
 static hipError_t attn_impl(const AttnLaunch& L, hipStream_t st) {
   const AttnArgs A = make_args(L);
   if (L.block_mask)
-    hipLaunchKernelGGL((attn_fwd_kernel<D, PV, DT, KV_SPARSE>), dim3(A.total), dim3(256), 0, st, A);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, PV, DT, KV_SPARSE, false>), dim3(A.total), dim3(256), 0, st, A);
   else if (L.frame_stride > 0)
-    hipLaunchKernelGGL((attn_fwd_kernel<D, PV, DT, KV_CACHE>), dim3(A.total), dim3(256), 0, st, A);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, PV, DT, KV_CACHE, true>), dim3(A.total), dim3(512), 0, st, A);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<D, PV, DT, KV_DENSE>), dim3(A.total), dim3(256), 0, st, A);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, PV, DT, KV_DENSE, true>), dim3(A.total), dim3(512), 0, st, A);
   if (L.splits > 1) {
     const int64_t threads = static_cast<int64_t>(L.B) * L.H * L.Nq_pad * (D / 4);
     hipLaunchKernelGGL((attn_combine_kernel<D, DT>), dim3(static_cast<unsigned>((threads + 255) / 256)),

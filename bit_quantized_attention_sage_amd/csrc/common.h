@@ -11,7 +11,7 @@
 
 namespace sage {
 
-constexpr int BQ = 128;          // query tokens per Q scale block (= one workgroup)
+constexpr int BQ = 128;          // query tokens per Q scale block
 constexpr int BK = 64;           // key tokens per K scale block = softmax chunk
 constexpr int VB = 32;           // key tokens per FP8 V scale (E8M0) block
 constexpr int QMAX = 127;        // symmetric INT8 range
@@ -19,6 +19,11 @@ constexpr int KMEAN_CHUNK = 128; // tokens per first-level partial sum of the K 
 constexpr float TAU = 4.0f;      // lazy running-max threshold (log2 units)
 constexpr int PSHIFT_FP8 = 4;    // P stored as e4m3(p * 2^4) in FP8 mode
 constexpr int PSHIFT_16 = 0;
+// Query rows of one work item of the fused kernel when the keys are a frame
+// cache (and likewise contiguous keys): its KV splits cut the chunk list of
+// this many rows, so the split boundaries, and with them the rounding, depend
+// on it.
+constexpr int CACHE_TILE = 2 * BQ;
 constexpr int NPAD = 128;        // Nq and Nkv are padded to multiples of this
 constexpr int MAXB = 256;        // largest batch handled through kernel arguments
 
@@ -101,12 +106,11 @@ template <> struct Pack16<DT_F16> {
   static __device__ __forceinline__ float hi(uint32_t w) { return f16_bits_to_f32(w >> 16); }
 };
 
-// max(a, b, c) in one v_max3_i32.
-__device__ __forceinline__ int max3_i32(int a, int b, int c) {
-  int r;
-  asm("v_max3_i32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
+// max(a, b, c): the compiler emits one v_max3_i32 for it.  (Written in
+// C++, not inline asm, so that the compiler's hazard checks cover it: an asm
+// instruction that reads or overwrites the registers of a matrix op still in
+// flight gets no wait states.)
+__device__ __forceinline__ int max3_i32(int a, int b, int c) { return max(max(a, b), c); }
 
 // Wave-wide (64 lanes) reductions.
 __device__ __forceinline__ float wave_max(float v) {

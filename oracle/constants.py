@@ -15,10 +15,11 @@ KMEAN_CHUNK = 128  # tokens per first-level partial sum of the K mean
 TAU = 4.0         # lazy running-max threshold, in log2 units
 PSHIFT_FP8 = 4    # P is stored as e4m3(p * 2^4) in FP8 PV mode
 PSHIFT_16 = 0     # no pre-scale when P is rounded to fp16/bf16
+CACHE_TILE = 256  # query rows whose frame-cache chunk list KV splits divide
 LOG2E = 1.4426950408889634
 
 PV_16 = 0
 PV_FP8 = 1
 
 __all__ = ["BQ", "BK", "VB", "QMAX", "F8MAX", "KMEAN_CHUNK", "TAU",
-           "PSHIFT_FP8", "PSHIFT_16", "LOG2E", "PV_16", "PV_FP8"]
+           "PSHIFT_FP8", "PSHIFT_16", "CACHE_TILE", "LOG2E", "PV_16", "PV_FP8"]

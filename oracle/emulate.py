@@ -53,7 +53,7 @@ places where the two may differ, all far below the acceptance tolerance.
 
 import numpy as np
 
-from .constants import BQ, BK, TAU, PSHIFT_FP8, PSHIFT_16, LOG2E, PV_16, PV_FP8
+from .constants import BQ, BK, TAU, PSHIFT_FP8, PSHIFT_16, LOG2E, PV_16, PV_FP8, CACHE_TILE
 from . import codecs
 from .fp32 import fma_f32
 from .attention import row_end, default_q_pos0
@@ -289,8 +289,8 @@ def emulate_from_inputs(Q, K, V, pv_mode, dtype, sm_scale=None, frame_len=0,
 
 def cache_tile_splits(first, last, q_pos0_b, kv_len_b, frame_len, frame_stride,
                       sink_frames, window_frames, nsplit):
-    """Chunk ranges of the split work items of one 128-query tile (rows
-    first..last) over a frame cache.
+    """Chunk ranges of the split work items of one query tile (rows
+    first..last, CACHE_TILE of them) over a frame cache.
 
     The tile's key chunks, in order, are those of the sink frames, then those
     of the window frames up to the last row's frame (through its last valid
@@ -323,8 +323,8 @@ def cache_tile_splits(first, last, q_pos0_b, kv_len_b, frame_len, frame_stride,
 
 def emulate_frame_cache(Q, K, V, pv_mode, dtype, frame_len, frame_stride, sink_frames,
                         window_frames, kv_len, q_pos0, mu, shift, nsplit, rows=None):
-    """``emulate_from_inputs`` over a frame cache, tile by tile of 128 query
-    rows, each tile with the chunk ranges of its split work items
+    """``emulate_from_inputs`` over a frame cache, tile by tile of CACHE_TILE
+    query rows, each tile with the chunk ranges of its split work items
     (``cache_tile_splits``).  Q [B,H,Nq,d]; K, V [B,H,tokens,d] of whole
     frames from frame 0; mu, shift: the frozen mean and exponents.
     Returns float64 O [B,H,R,d] for the selected rows (all when None)."""
@@ -342,9 +342,9 @@ def emulate_frame_cache(Q, K, V, pv_mode, dtype, frame_len, frame_stride, sink_f
         Vhat = quant.to_frame_slots(Vf, frame_len, frame_stride).astype(np.float64)
     out = np.empty((B, H, len(rows), d))
     for b in range(B):
-        for t in np.unique(rows // BQ):
-            sel = np.nonzero(rows // BQ == t)[0]
-            first, last = t * BQ, min(t * BQ + BQ, Nq) - 1
+        for t in np.unique(rows // CACHE_TILE):
+            sel = np.nonzero(rows // CACHE_TILE == t)[0]
+            first, last = t * CACHE_TILE, min(t * CACHE_TILE + CACHE_TILE, Nq) - 1
             sp = cache_tile_splits(first, last, int(q_pos0[b]), int(kv_len[b]), frame_len,
                                    frame_stride, sink_frames, window_frames, nsplit)
             o64, _ = sage_attention_emulated(qc[b:b + 1], dq[b:b + 1], kc[b:b + 1], dk[b:b + 1],

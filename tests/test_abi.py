@@ -56,7 +56,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_constants_agree_with_oracle(lib):
-    for name in ("BQ", "BK", "VB", "QMAX", "TAU", "PSHIFT_FP8", "PSHIFT_16", "KMEAN_CHUNK"):
+    for name in ("BQ", "BK", "VB", "QMAX", "TAU", "PSHIFT_FP8", "PSHIFT_16", "KMEAN_CHUNK", "CACHE_TILE"):
         assert sage.sage_attn_constant(name) == getattr(oc, name), name
     with pytest.raises(sage.SageError):
         sage.sage_attn_constant("NOPE")

@@ -168,7 +168,8 @@ def test_cache_emulation_equals_attention_on_dequantized_operands(pv_mode, eps):
 @pytest.mark.parametrize("F,FS,S,W,q0f,first,last,nsplit", [
     (200, 256, 1, 3, 7, 0, 127, 1), (200, 256, 1, 3, 7, 128, 199, 3), (100, 128, 2, 2, 6, 0, 127, 4),
     (64, 64, 4, 1, 1, 0, 63, 2), (150, 192, 2, 1, 8, 0, 127, 2), (200, 256, 0, 0, 5, 0, 127, 3),
-    (2040, 2048, 1, 16, 40, 1920, 2039, 3)])
+    (2040, 2048, 1, 16, 40, 1920, 2039, 3), (2040, 2048, 1, 16, 40, 1792, 2039, 3),
+    (2040, 2048, 1, 4, 9, 0, 255, 5)])
 def test_cache_tile_splits_cover_exactly_the_visible_chunks(F, FS, S, W, q0f, first, last, nsplit):
     """Brute force over slots: the split ranges are disjoint and ascending, they
     cover every chunk holding a slot that some row of the tile sees, and every
