@@ -15,17 +15,26 @@
 // converted and added to a float32 running sum with one FMA by its scale
 // dx * dw (rounded to float32 once).
 //
-// GEMM decomposition.  One workgroup = 4 waves = a tile of 128 rows (tokens)
+// GEMM decomposition.  One workgroup = 8 waves = a tile of 128 rows (tokens)
 // x 256 output features; wave w takes rows 64*(w&1) + [0,64) and features
-// 128*(w>>1) + [0,128) (one weight block of N).  Per K block of 128
+// 64*(w>>1) + [0,64) (half a weight block of N).  Per K block of 128
 // channels the X tile (128 x 128 bytes) and the W tile (256 x 128 bytes) are
 // staged from HBM straight into LDS (buffer loads with an LDS destination,
-// double-buffered), and each wave runs 2 x 2 x 2 x 4 = 32 MFMAs i32
-// 32x32x32: for each 64-feature half u and 32-token group t, S^T(u, t) =
-// W_u X_t^T as in the fused attention kernel's score tile (W rows in the A
-// operand, permuted by a_row_key, X rows as the B operand), so lane l ends
-// with token 32t + l%32 and 16 consecutive features of each 32-feature
-// subtile.
+// double-buffered), and each wave runs 2 x 2 x 4 = 16 MFMAs i32 32x32x32:
+// for each 32-token group t, S^T(t) = W X_t^T as in the fused attention
+// kernel's score tile (W rows in the A operand, permuted by a_row_key, X
+// rows as the B operand), so lane l ends with token 32t + l%32 and 16
+// consecutive features of each 32-feature subtile.
+//
+// Ping-pong.  Waves w and w+4 share a SIMD.  Each K block is two phases
+// split by a barrier, the MFMAs (at raised wave priority) and the
+// dequantization into the float32 sums, and waves 4-7 run one phase behind
+// waves 0-3, so on every SIMD one wave's MFMAs overlap the other's VALU work
+// (one wave alone issues FP32 VALU ops only every ~5 cycles, and its own
+// MFMAs hide little of it).  Waves 0-3 alone stage the tiles, one DMA
+// instruction behind each of their MFMAs (issued all at once they stalled
+// the phase by ~600 cycles); the buffer a block fills was read by both
+// groups in the block before.
 #include "common.h"
 #include "kernels.h"
 
@@ -144,7 +153,7 @@ struct GemmArgs {
 };
 
 template <int DT>
-__global__ __launch_bounds__(256, 1) void w8a8_gemm_kernel(GemmArgs A) {
+__global__ __launch_bounds__(512, 1) void w8a8_gemm_kernel(GemmArgs A) {
   __shared__ __attribute__((aligned(16))) int8_t xL0[XB];
   __shared__ __attribute__((aligned(16))) int8_t xL1[XB];
   __shared__ __attribute__((aligned(16))) int8_t wL0[WB];
@@ -165,27 +174,29 @@ __global__ __launch_bounds__(256, 1) void w8a8_gemm_kernel(GemmArgs A) {
   const int mtile = first + rem % gsz, ntile = rem / gsz;
   const int m0 = mtile * TM, n0 = ntile * TN;
   const int mw = m0 + 64 * (w & 1);   // this wave's rows
-  const int nw = n0 + 128 * (w >> 1); // this wave's features (one weight block)
+  const int nw = n0 + 64 * (w >> 1);  // this wave's 64 features (half a weight block)
   const int nkb = A.K / WG;
 
-  // Staging: DMA instruction i of wave w fills LDS granule (4i + w)*64 + lane
-  // of a tile; its global source is chosen so that the tile ends up swizzled.
+  // Staging (waves 0-3): DMA instruction i of wave w fills LDS granule
+  // (4i + w)*64 + lane of a tile; its global source is chosen so that the
+  // tile ends up swizzled.
   // Rows past M (X) read zero codes from the padding rows; rows past N (W)
   // are outside the buffer and read as zero.
   const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<int8_t*>(A.xq), 0, static_cast<int>(static_cast<int64_t>(A.M_pad) * A.K), 0x00020000);
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<int8_t*>(A.wq), 0, static_cast<int>(static_cast<int64_t>(A.N) * A.K), 0x00020000);
-  constexpr int XI = XB / 4096, WI = WB / 4096;  // 1 KB DMA instructions per wave
+  constexpr int XI = XB / 4096, WI = WB / 4096;  // 1 KB DMA instructions per wave of group 0
+  const int wgrp = w >> 2;
   int xoff[XI], woff[WI];
 #pragma unroll
   for (int i = 0; i < XI; ++i) {
-    const int s = (4 * i + w) * 64 + lane, r = s / 8, gp = s % 8;
+    const int s = (4 * i + (w & 3)) * 64 + lane, r = s / 8, gp = s % 8;
     xoff[i] = (m0 + r) * A.K + ((gp ^ x_swz(r)) << 4);
   }
 #pragma unroll
   for (int i = 0; i < WI; ++i) {
-    const int s = (4 * i + w) * 64 + lane, r = s / 8, gp = s % 8;  // r: row of the 256-row tile
+    const int s = (4 * i + (w & 3)) * 64 + lane, r = s / 8, gp = s % 8;  // r: row of the 256-row tile
     const int key = r & 63;
     // a row past N points at the buffer's end, which reads as zero
     woff[i] = n0 + r < A.N ? (n0 + r) * A.K + ((gp ^ k_swz<128>(key)) << 4) : A.N * A.K;
@@ -206,13 +217,14 @@ __global__ __launch_bounds__(256, 1) void w8a8_gemm_kernel(GemmArgs A) {
   // This lane's rows in the X tile (B operand: token r32 of group t, bytes
   // [32 ks + 16 h2, +16)) and rows in the W tile (A operand, two 64-row halves).
   const int xr0 = 64 * (w & 1) + r32, xr1 = xr0 + 32;
-  const int wr_base = 128 * (w >> 1);
+  const int wr_base = 64 * (w >> 1);
   const int key0 = a_row_key(r32, 0), key1 = a_row_key(r32, 1);
   const int sw0 = k_swz<128>(key0), sw1 = k_swz<128>(key1);
 
-  v16f y[2][2][2];  // [feature half u][token group t][subtile s]
+  constexpr int NU = 1;  // 64-feature groups per wave
+  v16f y[NU][2][2];  // [feature group u][token group t][subtile s]
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
+  for (int u = 0; u < NU; ++u)
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -234,11 +246,12 @@ __global__ __launch_bounds__(256, 1) void w8a8_gemm_kernel(GemmArgs A) {
   };
 
   load_scales(0);
-  dma(xL0, wL0, 0);
+  if (wgrp == 0) dma(xL0, wL0, 0);
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
 
-  auto block = [&](const int8_t* xl, const int8_t* wl, float c0, float c1) {
+  v16i s[2][2];  // [t][subtile]: int32 products of the current K block
+  auto mma = [&](const int8_t* xl, const int8_t* wl) {
     v4i xb[2][4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -246,60 +259,79 @@ __global__ __launch_bounds__(256, 1) void w8a8_gemm_kernel(GemmArgs A) {
       xb[0][ks] = *reinterpret_cast<const v4i*>(xl + xr0 * WG + ((g ^ x_swz(xr0)) << 4));
       xb[1][ks] = *reinterpret_cast<const v4i*>(xl + xr1 * WG + ((g ^ x_swz(xr1)) << 4));
     }
+    const int8_t* wt = wl + wr_base * WG;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int8_t* wt = wl + (wr_base + 64 * u) * WG;  // 64-row half of this wave's features
-      v16i s[2][2];  // [t][subtile]
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int g = 2 * ks + h2;
-        const v4i a0 = *reinterpret_cast<const v4i*>(wt + key0 * WG + ((g ^ sw0) << 4));
-        const v4i a1 = *reinterpret_cast<const v4i*>(wt + key1 * WG + ((g ^ sw1) << 4));
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          if (ks == 0) {
-            s[t][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, xb[t][0], v16i{0}, 0, 0, 0);
-            s[t][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, xb[t][0], v16i{0}, 0, 0, 0);
-          } else {
-            s[t][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, xb[t][ks], s[t][0], 0, 0, 0);
-            s[t][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, xb[t][ks], s[t][1], 0, 0, 0);
-          }
-        }
-      }
+    for (int ks = 0; ks < 4; ++ks) {
+      const int g = 2 * ks + h2;
+      const v4i a0 = *reinterpret_cast<const v4i*>(wt + key0 * WG + ((g ^ sw0) << 4));
+      const v4i a1 = *reinterpret_cast<const v4i*>(wt + key1 * WG + ((g ^ sw1) << 4));
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const float c = t ? c1 : c0;
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            y[u][t][sub][i] = __builtin_fmaf(static_cast<float>(s[t][sub][i]), c, y[u][t][sub][i]);
+        if (ks == 0) {
+          s[t][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, xb[t][0], v16i{0}, 0, 0, 0);
+          s[t][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, xb[t][0], v16i{0}, 0, 0, 0);
+        } else {
+          s[t][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, xb[t][ks], s[t][0], 0, 0, 0);
+          s[t][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, xb[t][ks], s[t][1], 0, 0, 0);
+        }
       }
     }
   };
-
-  for (int kb = 0; kb < nkb; kb += 2) {
-    float c0 = dx0 * dwv, c1 = dx1 * dwv;  // fp32(dx dw), rounded once
+  auto deq = [&](float c0, float c1) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const float c = t ? c1 : c0;
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          y[0][t][sub][i] = __builtin_fmaf(static_cast<float>(s[t][sub][i]), c, y[0][t][sub][i]);
+    }
+  };
+  // One K block: the MFMA phase, a barrier, the dequantization phase, the
+  // DMA wait and a barrier.  Group 1 runs one phase behind group 0.
+  auto step = [&](const int8_t* xl, const int8_t* wl, int8_t* xn, int8_t* wn, int kb) {
+    const float c0 = dx0 * dwv, c1 = dx1 * dwv;  // fp32(dx dw), rounded once
     load_scales(kb + 1);
-    if (kb + 1 < nkb) dma(xL1, wL1, kb + 1);
-    block(xL0, wL0, c0, c1);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
+    if (wgrp == 0 && kb + 1 < nkb) {
+      // group 0 stages the next block: one DMA instruction behind each MFMA
+      dma(xn, wn, kb + 1);
+      mma(xl, wl);
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // the X operand reads
+#pragma unroll
+      for (int g = 0; g < 16; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                   // one MFMA
+        if (g < XI + WI) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one DMA
+        if (g < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // a W operand read
+      }
+    } else {
+      mma(xl, wl);
+    }
+    asm volatile("" : "+v"(s[0][0]), "+v"(s[0][1]), "+v"(s[1][0]), "+v"(s[1][1]));
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    deq(c0, c1);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA (and scales) landed
     __syncthreads();
+  };
+
+  if (wgrp == 1) __builtin_amdgcn_s_barrier();  // one phase behind group 0
+  for (int kb = 0; kb < nkb; kb += 2) {
+    step(xL0, wL0, xL1, wL1, kb);
     if (kb + 1 >= nkb) break;
-    c0 = dx0 * dwv;
-    c1 = dx1 * dwv;
-    load_scales(kb + 2);
-    if (kb + 2 < nkb) dma(xL0, wL0, kb + 2);
-    block(xL1, wL1, c0, c1);
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
+    step(xL1, wL1, xL0, wL0, kb + 1);
   }
+  if (wgrp == 0) __builtin_amdgcn_s_barrier();  // as many barriers as group 1
 
   // ---- epilogue: + bias, round, store (lane: token 32t + r32, features
   // nw + 64u + 32 sub + 16 h2 + [0, 16))
   if (nw >= A.N) return;
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
+  for (int u = 0; u < NU; ++u)
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       const int nf = nw + 64 * u + 32 * sub + 16 * h2;
@@ -374,9 +406,9 @@ hipError_t launch_w8a8_gemm(const W8A8Launch& L, const int8_t* xq, const float* 
   A.nt = (L.N + TN - 1) / TN;
   const dim3 grid(static_cast<unsigned>(A.mt * A.nt));
   if (L.dtype == DT_BF16)
-    hipLaunchKernelGGL(w8a8_gemm_kernel<DT_BF16>, grid, dim3(256), 0, st, A);
+    hipLaunchKernelGGL(w8a8_gemm_kernel<DT_BF16>, grid, dim3(512), 0, st, A);
   else
-    hipLaunchKernelGGL(w8a8_gemm_kernel<DT_F16>, grid, dim3(256), 0, st, A);
+    hipLaunchKernelGGL(w8a8_gemm_kernel<DT_F16>, grid, dim3(512), 0, st, A);
   return hipGetLastError();
 }
 
