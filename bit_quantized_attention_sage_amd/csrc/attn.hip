@@ -508,7 +508,13 @@ __global__ __launch_bounds__(PP ? 512 : 256, PP ? 1 : 2) void attn_fwd_kernel(At
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) st.o[cb] = v16f{0.f};
   st.ls = v4f{0.f, 0.f, 0.f, 0.f};
-  st.m = -__builtin_inff();
+  // The running max starts at the most negative finite float, not -inf: a
+  // row can meet chunks with no visible key before its first visible one (a
+  // split or a window that begins with keys of frames the row does not see),
+  // and with m = -inf the softmax's -inf scores would give -inf + inf = NaN.
+  // This way they give p = 2^-inf = 0, and the first visible chunk still
+  // moves m (its alpha = 0 scales an O and l that are still 0).
+  st.m = -3.40282347e38f;
 
   const int nkc = A.Nkv_pad / 64;
   const int8_t* kbase = A.kc + static_cast<int64_t>(bh) * A.Nkv_pad * D;

@@ -134,6 +134,13 @@ CASES = [
     (1, 2, 200, 128, torch.bfloat16, 200, 256, 6, 5, 0, 0, 0),    # no window: causal over the padded cache
     (1, 1, 64, 128, torch.bfloat16, 64, 64, 2, 1, 4, 1, 0),       # query frame inside the sinks
     (1, 2, 150, 64, torch.float16, 150, 192, 9, 8, 2, 1, 2),      # d = 64, fp16, short window
+    # queries over six frames: three 256-row work items (the last half empty),
+    # tile boundaries inside frames, forced splits of each item's chunk list
+    (1, 2, 600, 128, torch.bfloat16, 100, 128, 12, 6, 1, 2, 3),
+    # no sinks: a work item's list starts with window frames that its later
+    # rows do not see (their running max meets masked chunks first)
+    (1, 2, 600, 128, torch.bfloat16, 100, 128, 12, 6, 0, 2, 0),
+    (1, 2, 600, 64, torch.float16, 100, 128, 12, 6, 0, 1, 2),
 ]
 
 
