@@ -333,10 +333,11 @@ def emulate_frame_cache(Q, K, V, pv_mode, dtype, frame_len, frame_stride, sink_f
     B, H, Nq, d = Qf.shape
     rows = np.arange(Nq) if rows is None else np.asarray(rows, dtype=np.int64)
     qc, dq = quant.quantize_q(Qf, shift)
-    kc, dk = quant.quantize_k_frames(np.asarray(K, dtype=np.float32), mu, shift, frame_len, frame_stride)
+    kc, dk = quant.quantize_k_frames(np.asarray(K, dtype=np.float32), mu, shift, frame_len, frame_stride,
+                                     kv_len=kv_len)
     Vf = np.asarray(V, dtype=np.float32)
     if pv_mode == PV_FP8:
-        vc, ve = quant.quantize_v_fp8_frames(Vf, frame_len, frame_stride)
+        vc, ve = quant.quantize_v_fp8_frames(Vf, frame_len, frame_stride, kv_len=kv_len)
         Vhat = quant.dequant_v_fp8(vc, ve)
     else:
         Vhat = quant.to_frame_slots(Vf, frame_len, frame_stride).astype(np.float64)

@@ -35,11 +35,13 @@ from .constants import BQ, BK, VB, QMAX, KMEAN_CHUNK
 from . import codecs
 
 
-def _kv_len(B, Nkv, kv_len):
+def _kv_len(B, Nkv, kv_len, least=0):
+    """Valid tokens per batch (all when None); the block quantizers accept a
+    batch with none (every block empty: scale 0, codes 0), the mean needs one."""
     if kv_len is None:
         return np.full(B, Nkv, dtype=np.int64)
     kv = np.asarray(kv_len, dtype=np.int64)
-    assert kv.shape == (B,) and np.all(kv >= 1) and np.all(kv <= Nkv)
+    assert kv.shape == (B,) and np.all(kv >= least) and np.all(kv <= Nkv)
     return kv
 
 
@@ -52,7 +54,7 @@ def k_mean(K, kv_len=None):
     """
     K = np.asarray(K, dtype=np.float32)
     B, H, Nkv, d = K.shape
-    kv = _kv_len(B, Nkv, kv_len)
+    kv = _kv_len(B, Nkv, kv_len, least=1)
     mu = np.empty((B, H, d), dtype=np.float32)
     for b in range(B):
         n = int(kv[b])
@@ -216,10 +218,18 @@ def _frames_of(X, frame_len):
     return [(f, f * frame_len, min((f + 1) * frame_len, n)) for f in range(-(-n // frame_len))]
 
 
-def quantize_k_frames(K, mu, shift, frame_len, frame_stride, n_slots=None):
+def _frame_valid(kv_len, lo, hi):
+    """Valid tokens of the frame [lo, hi) per batch: those below kv_len[b]
+    (tokens past it are padding, as in quantize_k), or all when None."""
+    return None if kv_len is None else np.clip(np.asarray(kv_len) - lo, 0, hi - lo)
+
+
+def quantize_k_frames(K, mu, shift, frame_len, frame_stride, n_slots=None, kv_len=None):
     """K [B,H,Ntok,d] (tokens of consecutive frames from frame 0) -> codes int8
     [B,H,n_slots,d] and scales float32 [B,H,n_slots/BK], each frame quantized
-    as its own sequence (quantize_k with the given frozen mu and shift)."""
+    as its own sequence (quantize_k with the given frozen mu and shift).
+    kv_len [B]: tokens written so far per batch; a partly written frame
+    quantizes its valid tokens only (codes 0 past kv_len)."""
     B, H, n, d = np.shape(K)
     if frame_stride % BK or frame_stride < frame_len:
         raise ValueError("frame stride must be a multiple of BK and >= the frame length")
@@ -227,22 +237,22 @@ def quantize_k_frames(K, mu, shift, frame_len, frame_stride, n_slots=None):
     codes = np.zeros((B, H, n_slots, d), dtype=np.int8)
     dk = np.zeros((B, H, n_slots // BK), dtype=np.float32)
     for f, lo, hi in _frames_of(K, frame_len):
-        c, dl = quantize_k(np.asarray(K)[:, :, lo:hi], mu, None, shift)
+        c, dl = quantize_k(np.asarray(K)[:, :, lo:hi], mu, _frame_valid(kv_len, lo, hi), shift)
         s0 = f * frame_stride
         codes[:, :, s0:s0 + hi - lo] = c
         dk[:, :, s0 // BK:s0 // BK + dl.shape[2]] = dl
     return codes, dk
 
 
-def quantize_v_fp8_frames(V, frame_len, frame_stride, n_slots=None):
+def quantize_v_fp8_frames(V, frame_len, frame_stride, n_slots=None, kv_len=None):
     """quantize_v_fp8 per frame into cache slots: codes uint8 [B,H,n_slots,d],
-    exponents int64 [B,H,n_slots/VB,d]."""
+    exponents int64 [B,H,n_slots/VB,d]; kv_len as in quantize_k_frames."""
     B, H, n, d = np.shape(V)
     n_slots = n_slots or -(-n // frame_len) * frame_stride
     codes = np.zeros((B, H, n_slots, d), dtype=np.uint8)
     exps = np.zeros((B, H, n_slots // VB, d), dtype=np.int64)
     for f, lo, hi in _frames_of(V, frame_len):
-        c, e, _ = quantize_v_fp8(np.asarray(V)[:, :, lo:hi])
+        c, e, _ = quantize_v_fp8(np.asarray(V)[:, :, lo:hi], _frame_valid(kv_len, lo, hi))
         s0 = f * frame_stride
         codes[:, :, s0:s0 + hi - lo] = c
         exps[:, :, s0 // VB:s0 // VB + e.shape[2]] = e

@@ -178,6 +178,36 @@ def test_window_parity(lib, case, pv_mode):
     assert cs >= (0.999 if pv_mode == PV_16 else 0.998)
 
 
+@pytest.mark.parametrize("splits", [0, 3])
+@pytest.mark.parametrize("pv_mode", [PV_16, PV_FP8], ids=["pv16", "pvfp8"])
+def test_window_ragged_batches(lib, pv_mode, splits):
+    """Batches with their own cache lengths, two of them ending inside a frame
+    (the current frame only partly written), queries spanning frames, one
+    sink frame and a two-frame window."""
+    B, H, Nq, d, dt, F, FS, nf, S, W = 3, 2, 250, 128, torch.bfloat16, 100, 128, 10, 1, 2
+    kv_len, q_pos0 = [1000, 763, 540], [750, 513, 290]
+    print(f"ragged window batches pv {pv_mode} splits {splits}", flush=True)
+    q, k, v = _inputs(B, H, Nq, nf * F, d, dt, 4100 + 10 * pv_mode + splits)
+    Q, K, V = host(q), host(k), host(v)
+    mu, a = _frozen(Q, K)
+    o, desc, _, _ = _run(q.cuda(), k.cuda(), v.cuda(), pv_mode, F, FS, nf * FS, S, W, kv_len, q_pos0,
+                         splits, mu, a)
+    nsplit = sage.sage_attn_kv_splits(desc)
+    o64 = emulate_cache(Q, K, V, pv_mode, "bf16", F, FS, S, W, kv_len, q_pos0, mu, a, nsplit)
+    o_abs = emulate_cache(Q, K, np.abs(V), pv_mode, "bf16", F, FS, S, W, kv_len, q_pos0, mu, a, nsplit) \
+        if pv_mode == PV_FP8 else None
+    og = host(o)
+    mx, excess, frac, rel, rel_bound = compare_output(og, o64, "bf16", pv_mode, o_abs)
+    print(f"  splits {nsplit} max-abs {mx:.3e} excess {excess:.2e} beyond-rounding {frac:.2e} rel-L2 {rel:.3e}")
+    assert np.isfinite(og).all()
+    assert excess <= 0
+    assert frac <= (1e-4 if pv_mode == PV_16 else 2e-2)
+    assert rel <= rel_bound
+    ref = attention.attention_fp64(Q, K, V, frame_len=F, kv_len=kv_len, q_pos0=q_pos0, sink_frames=S,
+                                   window_frames=W)
+    assert cosine(og, ref) >= (0.999 if pv_mode == PV_16 else 0.998)
+
+
 @pytest.mark.parametrize("pv_mode", [PV_16, PV_FP8])
 def test_cache_without_padding_or_window_equals_contiguous(lib, pv_mode):
     """Frames of a multiple of 64 tokens, no padding, no window: the cache

@@ -70,6 +70,32 @@ def test_frame_cache_without_padding_equals_contiguous_quantization():
     assert np.array_equal(v1, v2) and np.array_equal(e1, e2)
 
 
+def test_partly_written_frames_equal_contiguous_quantization_with_kv_len():
+    """A frame cache holding kv_len[b] tokens quantizes like the contiguous
+    path with the same kv_len: tokens past it are padding (zero codes, outside
+    every amax), also inside the frame that holds the boundary."""
+    rng = np.random.default_rng(43)
+    F = 2 * BK
+    K = _rnd16(rng.standard_normal((2, 3, 5 * F, 16)) + rng.standard_normal((1, 3, 1, 16)))
+    V = _rnd16(rng.standard_normal((2, 3, 5 * F, 16)))
+    kv = [300, 411]  # inside frames 2 and 3
+    mu = quant.k_mean(K)
+    a = rng.integers(-2, 3, (2, 3, 16))
+    c1, d1 = quant.quantize_k_frames(K, mu, a, F, F, kv_len=kv)
+    c2, d2 = quant.quantize_k(K, mu, kv, a)
+    assert np.array_equal(c1, c2) and np.array_equal(d1, d2)
+    assert not c1[0, :, 300:].any() and not c1[1, :, 411:].any()
+    v1, e1 = quant.quantize_v_fp8_frames(V, F, F, kv_len=kv)
+    v2, e2, _ = quant.quantize_v_fp8(V, kv)
+    assert np.array_equal(v1, v2) and np.array_equal(e1, e2)
+    # the stale tokens past kv_len change nothing
+    K2, V2 = K.copy(), V.copy()
+    K2[0, :, 300:] *= 40
+    V2[1, :, 411:] *= 40
+    assert np.array_equal(quant.quantize_k_frames(K2, mu, a, F, F, kv_len=kv)[0], c1)
+    assert np.array_equal(quant.quantize_v_fp8_frames(V2, F, F, kv_len=kv)[1], e1)
+
+
 def test_frame_cache_padding_and_append_once():
     """With padding (F = 200 tokens at a stride of 256 slots) the padding slots
     hold 0, and quantizing frames one at a time into the cache gives the same
