@@ -96,6 +96,38 @@ def test_sparse_parity(lib, case, pv_mode):
     assert cs >= (0.999 if pv_mode == PV_16 else 0.998)
 
 
+@pytest.mark.parametrize("splits", [0, 2])
+@pytest.mark.parametrize("pv_mode", [PV_16, PV_FP8], ids=["pv16", "pvfp8"])
+def test_rows_whose_kept_blocks_lie_in_later_frames(lib, pv_mode, splits):
+    """One query tile over two frames (rows 0-63 in frame 2, rows 64-127 in
+    frame 3).  Head 0 keeps only frame 3's key block: the rows of frame 2
+    have no visible kept key and output 0; head 1 also keeps frame 1's
+    block, which every row sees."""
+    B, H, Nq, Nkv, d, dt, F = 1, 2, 128, 256, 128, torch.bfloat16, 64
+    kv, qp = [256], [128]
+    print(f"sparse later-frame blocks pv {pv_mode} splits {splits}", flush=True)
+    q = _rand((B, H, Nq, d), dt, 610 + pv_mode)
+    k = _rand((B, H, Nkv, d), dt, 611, offset=0.7)
+    v = _rand((B, H, Nkv, d), dt, 612)
+    M = np.zeros((B, H, 1, 4), dtype=np.uint8)
+    M[:, :, 0, 3] = 1
+    M[:, 1, 0, 1] = 1
+    o, desc = _run(q.cuda(), k.cuda(), v.cuda(), pv_mode, M, F, kv, qp, splits)
+    nsplit = sage.sage_attn_kv_splits(desc)
+    Q, K, V = host(q), host(k), host(v)
+    o64 = emulate.emulate_block_sparse(Q, K, V, pv_mode, "bf16", M, nsplit, F, kv, qp)
+    o_abs = emulate.emulate_block_sparse(Q, K, np.abs(V), pv_mode, "bf16", M, nsplit, F, kv, qp) \
+        if pv_mode == PV_FP8 else None
+    og = host(o)
+    assert np.isfinite(og).all()
+    assert not og[0, 0, :64].any() and not o64[0, 0, :64].any()
+    assert og[0, 0, 64:].any() and og[0, 1].any(axis=-1).all()
+    mx, excess, frac, rel, rel_bound = compare_output(og, o64, "bf16", pv_mode, o_abs)
+    print(f"  splits {nsplit} max-abs {mx:.3e} excess {excess:.2e} rel-L2 {rel:.3e}", flush=True)
+    assert excess <= 0
+    assert rel <= rel_bound
+
+
 @pytest.mark.parametrize("pv_mode", [PV_16, PV_FP8])
 def test_all_kept_mask_equals_dense(lib, pv_mode):
     """With every tile kept and one work item per tile, the sparse launch
