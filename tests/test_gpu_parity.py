@@ -79,6 +79,9 @@ CASES = [
     (1, 2, 250, 900, 128, torch.bfloat16, 64, None, [500], 1),    # explicit q_pos0, 64-key frames
     (2, 2, 256, 2000, 128, torch.bfloat16, 0, [2000, 1500], None, 4),     # forced KV splits
     (1, 3, 300, 1300, 128, torch.bfloat16, 250, None, None, 3),   # splits with a causal mask
+    # three 256-row work items over ragged frame-causal batches, forced splits
+    (3, 2, 600, 2000, 128, torch.bfloat16, 100, [2000, 1300, 777], None, 3),
+    (2, 2, 520, 1500, 64, torch.float16, 130, [1500, 1100], None, 2),
 ]
 
 
