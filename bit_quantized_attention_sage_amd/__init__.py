@@ -92,6 +92,9 @@ def load(path=None):
         "sage_attn_quant_layout": (ctypes.c_int, [_DESC_P, ctypes.c_void_p, ctypes.c_size_t, _BUFS_P]),
         "sage_attn_quantize": (ctypes.c_int, [_DESC_P, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                               _BUFS_P, ctypes.c_void_p]),
+        "sage_attn_quantize_frames_batched": (ctypes.c_int, [_DESC_P, ctypes.c_void_p, ctypes.c_void_p,
+                                                             ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32),
+                                                             ctypes.c_int32, _BUFS_P, ctypes.c_void_p]),
         "sage_attn_quantize_frames": (ctypes.c_int, [_DESC_P, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                                      ctypes.c_int32, ctypes.c_int32, _BUFS_P, ctypes.c_void_p]),
         "sage_attn_fwd_quantized": (ctypes.c_int, [_DESC_P, _BUFS_P, ctypes.c_void_p, ctypes.c_void_p]),
@@ -230,6 +233,16 @@ def sage_attn_quantize_frames(desc, q, k, v, frame0, nframes, bufs, stream=None)
                                             ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
                                             int(frame0), int(nframes), ctypes.byref(bufs), _stream(stream)),
            "sage_attn_quantize_frames")
+
+
+def sage_attn_quantize_frames_batched(desc, q, k, v, frame0, nframes, bufs, stream=None):
+    """As sage_attn_quantize_frames, batch b appending its nframes new frames
+    (rows [0, nframes*frame_len) of its k, v) at frame frame0[b] of its cache."""
+    f0 = (ctypes.c_int32 * len(frame0))(*[int(f) for f in frame0])
+    _check(load().sage_attn_quantize_frames_batched(
+        desc.ptr, ctypes.c_void_p(q.data_ptr() if q is not None else None), ctypes.c_void_p(k.data_ptr()),
+        ctypes.c_void_p(v.data_ptr()), f0, int(nframes), ctypes.byref(bufs), _stream(stream)),
+        "sage_attn_quantize_frames_batched")
 
 
 def sage_attn_fwd_quantized(desc, bufs, o, stream=None):

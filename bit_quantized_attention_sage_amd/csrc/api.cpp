@@ -285,7 +285,7 @@ sage::AttnLaunch attn_launch_of(const Plan& p, const sage_quant_bufs& b, void* o
 }
 
 int quantize_impl(const sage_attn_desc* desc, const void* q, const void* k, const void* v, int frames_only,
-                  int frame0, int nframes, const sage_quant_bufs* bufs, void* stream) {
+                  int frame0, const int32_t* frame0s, int nframes, const sage_quant_bufs* bufs, void* stream) {
   try {
     Plan p;
     int s = make_plan(desc, &p);
@@ -298,16 +298,24 @@ int quantize_impl(const sage_attn_desc* desc, const void* q, const void* k, cons
       return fail(SAGE_E_ALIGN, "k_mean_in must be 4-byte aligned");
     if (frames_only) {
       if (p.frame_stride == 0) return fail(SAGE_E_UNSUPPORTED, "sage_attn_quantize_frames needs a frame cache");
-      if (frame0 < 0 || nframes < 1 || static_cast<int64_t>(frame0) * p.frame_stride +
-                                            static_cast<int64_t>(nframes) * p.frame_stride > p.Nkv)
+      if (frame0s) {
+        if (nframes < 1) return fail(SAGE_E_SHAPE, "nframes must be positive");
+        for (int b = 0; b < p.B; ++b)
+          if (frame0s[b] < 0 || static_cast<int64_t>(frame0s[b]) * p.frame_stride +
+                                    static_cast<int64_t>(nframes) * p.frame_stride > p.Nkv)
+            return fail(SAGE_E_SHAPE, "batch " + std::to_string(b) +
+                                          ": frames [frame0, frame0 + nframes) must lie inside the Nkv cache slots");
+      } else if (frame0 < 0 || nframes < 1 || static_cast<int64_t>(frame0) * p.frame_stride +
+                                                   static_cast<int64_t>(nframes) * p.frame_stride > p.Nkv) {
         return fail(SAGE_E_SHAPE, "frames [frame0, frame0 + nframes) must lie inside the Nkv cache slots");
+      }
     }
     sage::QuantLaunch L{};
     L.chan_shift_in = desc->chan_shift_in;
     L.frame_len = p.frame_len;
     L.frame_stride = p.frame_stride;
     L.frames_only = frames_only;
-    L.frame0 = frame0;
+    L.frame0 = frame0s ? -1 : frame0;
     L.nframes = nframes;
     L.dtype = p.dtype;
     L.pv_mode = p.pv_mode;
@@ -328,6 +336,8 @@ int quantize_impl(const sage_attn_desc* desc, const void* q, const void* k, cons
     }
     L.k_mean_in = desc->k_mean_in;
     L.bi = p.bi;
+    if (frame0s)
+      for (int b = 0; b < p.B; ++b) L.bi.frame0[b] = frame0s[b];
     L.bufs = *bufs;
     const Layout lay = layout_of(p);
     char* st = static_cast<char*>(bufs->stats);
@@ -464,12 +474,19 @@ int sage_attn_quant_layout(const sage_attn_desc* desc, void* ws, size_t ws_bytes
 
 int sage_attn_quantize(const sage_attn_desc* desc, const void* q, const void* k, const void* v,
                        const sage_quant_bufs* bufs, void* stream) {
-  return quantize_impl(desc, q, k, v, 0, 0, 0, bufs, stream);
+  return quantize_impl(desc, q, k, v, 0, 0, nullptr, 0, bufs, stream);
 }
 
 int sage_attn_quantize_frames(const sage_attn_desc* desc, const void* q, const void* k, const void* v,
                               int32_t frame0, int32_t nframes, const sage_quant_bufs* bufs, void* stream) {
-  return quantize_impl(desc, q, k, v, 1, frame0, nframes, bufs, stream);
+  return quantize_impl(desc, q, k, v, 1, frame0, nullptr, nframes, bufs, stream);
+}
+
+int sage_attn_quantize_frames_batched(const sage_attn_desc* desc, const void* q, const void* k, const void* v,
+                                      const int32_t* frame0, int32_t nframes, const sage_quant_bufs* bufs,
+                                      void* stream) {
+  if (!frame0) return fail(SAGE_E_NULL, "frame0 is NULL");
+  return quantize_impl(desc, q, k, v, 1, 0, frame0, nframes, bufs, stream);
 }
 
 int sage_attn_fwd_quantized(const sage_attn_desc* desc, const sage_quant_bufs* bufs, void* o, void* stream) {

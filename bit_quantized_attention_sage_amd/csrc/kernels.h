@@ -16,6 +16,7 @@ constexpr int MAXB_ARGS = 128;  // batches passed by value in kernel arguments
 struct BatchInfo {
   int kv_len[MAXB_ARGS];
   int q_pos0[MAXB_ARGS];
+  int frame0[MAXB_ARGS];  // per-batch frame appends: the first frame of batch b's new frames
 };
 
 struct QuantLaunch {
@@ -27,7 +28,7 @@ struct QuantLaunch {
   const int8_t* chan_shift_in;
   int frame_len, frame_stride;  // frame cache when frame_stride > 0
   int frames_only;              // 1: quantize frames [frame0, frame0 + nframes) (q optional)
-  int frame0, nframes;
+  int frame0, nframes;          // frame0 < 0: each batch from its own bi.frame0[b]
   BatchInfo bi;
   sage_quant_bufs bufs;
   // views into bufs.stats

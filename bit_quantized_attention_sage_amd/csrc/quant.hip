@@ -161,7 +161,12 @@ __global__ __launch_bounds__(256) void quant_i8_kernel(
   constexpr int RPP = 256 / G;       // rows per pass
   constexpr int PASSES = ROWS / RPP;
   static_assert(ROWS % RPP == 0, "block shape");
-  const int b = blockIdx.z, h = blockIdx.y, blk = blk0 + blockIdx.x;
+  const int b = blockIdx.z, h = blockIdx.y;
+  if (blk0 < 0) {  // per-batch frame appends: batch b's new frames start at frame bi.frame0[b]
+    tok0 = bi.frame0[b] * F;
+    blk0 = bi.frame0[b] * (FS / ROWS);
+  }
+  const int blk = blk0 + blockIdx.x;
   const int bh = b * H + h;
   const int g = threadIdx.x % G, r0 = threadIdx.x / G;
   const int n_valid = n_in >= 0 ? n_in : (IS_K ? bi.kv_len[b] : n_all);
@@ -232,7 +237,12 @@ __global__ __launch_bounds__(2 * D) void prep_v_kernel(
     BatchInfo bi, void* __restrict__ vt, uint8_t* __restrict__ e8m0, int F, int FS, int tok0, int n_in,
     int ch0) {
   __shared__ uint16_t tile[64][D + 2];
-  const int b = blockIdx.z, h = blockIdx.y, ch = ch0 + blockIdx.x;
+  const int b = blockIdx.z, h = blockIdx.y;
+  if (ch0 < 0) {  // per-batch frame appends (as in quant_i8_kernel)
+    tok0 = bi.frame0[b] * F;
+    ch0 = bi.frame0[b] * (FS / 64);
+  }
+  const int ch = ch0 + blockIdx.x;
   const int bh = b * H + h;
   const int n_valid = n_in >= 0 ? n_in : bi.kv_len[b];
   constexpr int GR = D / 8;  // 16-byte granules per key row
@@ -331,10 +341,11 @@ static hipError_t quantize_impl(const QuantLaunch& L, hipStream_t st) {
                        static_cast<const T*>(L.q), L.qs[0], L.qs[1], L.qs[2], L.H, L.Nq, L.Nq_pad, L.bi,
                        L.bufs.k_mean, L.bufs.chan_shift, L.bufs.q_codes, L.bufs.q_scale, 0, 0, 0, -1, 0);
   // K and V: every position (blocks of the whole operand), or the slots of the
-  // appended frames only (their tokens are the input's rows 0 ..)
-  const int c0 = L.frames_only ? L.frame0 * FS / 64 : 0;
+  // appended frames only (their tokens are the input's rows 0 ..); a negative
+  // first chunk: each batch's own first frame, from bi.frame0
+  const int c0 = L.frames_only ? (L.frame0 < 0 ? -1 : L.frame0 * FS / 64) : 0;
   const int nc = L.frames_only ? L.nframes * FS / 64 : L.Nkv_pad / 64;
-  const int tok0 = L.frames_only ? L.frame0 * F : 0;
+  const int tok0 = L.frames_only && L.frame0 >= 0 ? L.frame0 * F : 0;
   const int n_in = L.frames_only ? L.nframes * F : -1;
   hipLaunchKernelGGL((quant_i8_kernel<T, D, BK, true>), dim3(nc, L.H, L.B), blk, 0, st,
                      static_cast<const T*>(L.k), L.ks[0], L.ks[1], L.ks[2], L.H, L.Nkv, L.Nkv_pad, L.bi,

@@ -206,6 +206,18 @@ int sage_attn_quantize_frames(const sage_attn_desc *desc, const void *q, const v
                               const void *v, int32_t frame0, int32_t nframes,
                               const sage_quant_bufs *bufs, void *stream);
 
+/* As sage_attn_quantize_frames, with each batch appending at its own place:
+ * batch b's nframes new frames (rows [0, nframes*frame_len) of its k, v) go to
+ * frames [frame0[b], frame0[b] + nframes) of its cache -- the step of B
+ * independent streaming sessions, each with a cache of its own length (the
+ * streaming setting of the Vidu S1 blog, section "Infra").  frame0: host
+ * array [B], read during the call.  Errors as sage_attn_quantize_frames;
+ * SAGE_E_NULL if frame0 is NULL; SAGE_E_SHAPE if some batch's frames do not
+ * fit in Nkv slots. */
+int sage_attn_quantize_frames_batched(const sage_attn_desc *desc, const void *q, const void *k,
+                                      const void *v, const int32_t *frame0, int32_t nframes,
+                                      const sage_quant_bufs *bufs, void *stream);
+
 /* Fused attention on already-quantized operands: writes O [B,H,Nq,d]. */
 int sage_attn_fwd_quantized(const sage_attn_desc *desc, const sage_quant_bufs *bufs,
                             void *o, void *stream);

@@ -37,7 +37,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for must in ("sage_attn_quantize", "sage_attn_fwd", "sage_attn_fwd_quantized",
                  "sage_attn_workspace_size", "sage_attn_quant_layout", "sage_attn_debug_scores",
-                 "sage_attn_quantize_frames", "sage_w8a8_quantize_weight", "sage_w8a8_quantize_act",
+                 "sage_attn_quantize_frames", "sage_attn_quantize_frames_batched",
+                 "sage_w8a8_quantize_weight", "sage_w8a8_quantize_act",
                  "sage_w8a8_gemm", "sage_w8a8_sizes"):
         assert must in names
 
@@ -164,6 +165,32 @@ def test_frame_cache_desc_and_quantize_frames_validation(lib):
     assert lib.sage_attn_quant_layout(plain.ptr, ctypes.c_void_p(base2), n2, ctypes.byref(bufs2)) == 0
     f2 = ctypes.c_void_p(base2)
     assert lib.sage_attn_quantize_frames(plain.ptr, None, f2, f2, 0, 1, ctypes.byref(bufs2), None) == 7
+
+
+def test_quantize_frames_batched_validation(lib):
+    d = _desc(B=2, frame_len=50, frame_stride=64, Nkv=320, Nq=50, kv_len=[250, 150])
+    assert _status(d)[0] == 0
+    n = sage.sage_attn_workspace_size(d)
+    ws = (ctypes.c_uint8 * (n + 256))()
+    base = (ctypes.addressof(ws) + 255) // 256 * 256
+    bufs = sage.sage_quant_bufs()
+    assert lib.sage_attn_quant_layout(d.ptr, ctypes.c_void_p(base), n, ctypes.byref(bufs)) == 0
+    fake = ctypes.c_void_p(base)  # aligned; never dereferenced on these error paths
+    arr = ctypes.c_int32 * 2
+    qfb = lib.sage_attn_quantize_frames_batched
+    assert qfb(d.ptr, None, fake, fake, None, 1, ctypes.byref(bufs), None) == 1
+    st = qfb(d.ptr, None, fake, fake, arr(4, 5), 1, ctypes.byref(bufs), None)  # batch 1: frame 5 of 5
+    assert st == 2 and b"batch 1" in lib.sage_attn_last_error()
+    assert qfb(d.ptr, None, fake, fake, arr(0, -1), 1, ctypes.byref(bufs), None) == 2
+    assert qfb(d.ptr, None, fake, fake, arr(0, 0), 0, ctypes.byref(bufs), None) == 2
+    plain = _desc(B=2)
+    n2 = sage.sage_attn_workspace_size(plain)
+    ws2 = (ctypes.c_uint8 * (n2 + 256))()
+    base2 = (ctypes.addressof(ws2) + 255) // 256 * 256
+    bufs2 = sage.sage_quant_bufs()
+    assert lib.sage_attn_quant_layout(plain.ptr, ctypes.c_void_p(base2), n2, ctypes.byref(bufs2)) == 0
+    f2 = ctypes.c_void_p(base2)
+    assert qfb(plain.ptr, None, f2, f2, arr(0, 0), 1, ctypes.byref(bufs2), None) == 7
 
 
 def test_block_mask_validation(lib):

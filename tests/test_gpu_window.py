@@ -148,6 +148,38 @@ def _cid(c):
     return f"B{c[0]}H{c[1]}q{c[2]}d{c[3]}{NAME_DT[c[4]]}F{c[5]}FS{c[6]}n{c[7]}S{c[9]}W{c[10]}s{c[11]}"
 
 
+@pytest.mark.parametrize("pv_mode", [PV_16, PV_FP8])
+def test_per_batch_appends_equal_full_quantize(lib, pv_mode):
+    """Each batch appends its frames at its own place
+    (sage_attn_quantize_frames_batched): three calls of two frames, batch b
+    starting at frame (2b, 2b + 2, 2b + 4) mod 6, fill every batch's six
+    frames in a different order; the buffers equal one whole-cache
+    quantization byte for byte."""
+    B, H, d, F, FS, nf = 3, 2, 128, 100, 128, 6
+    q, k, v = _inputs(B, H, F, nf * F, d, torch.bfloat16, 63)
+    Q, K = host(q), host(k)
+    mu, a = _frozen(Q, K)
+    q, k, v = q.cuda(), k.cuda(), v.cuda()
+    _, desc, ws_full, bufs_full = _run(q, k, v, pv_mode, F, FS, nf * FS, mu=mu, a=a)
+    full = sage.quant_views(desc, ws_full, bufs_full)
+    ws = torch.zeros_like(ws_full)
+    bufs = sage.sage_attn_quant_layout(desc, ws)
+    inc = sage.quant_views(desc, ws, bufs)
+    inc["k_mean"].copy_(torch.from_numpy(mu))
+    inc["chan_shift"].copy_(torch.from_numpy(a.astype(np.int8)))
+    for call in range(3):
+        f0 = [(2 * b + 2 * call) % nf for b in range(B)]
+        kk = torch.stack([k[b, :, f0[b] * F:(f0[b] + 2) * F] for b in range(B)]).contiguous()
+        vv = torch.stack([v[b, :, f0[b] * F:(f0[b] + 2) * F] for b in range(B)]).contiguous()
+        d2 = sage.Desc.for_tensors(q, kk, vv, nkv=nf * FS, pv_mode=pv_mode, frame_len=F, frame_stride=FS)
+        sage.sage_attn_quantize_frames_batched(d2, q if call == 2 else None, kk, vv, f0, 2, bufs)
+    torch.cuda.synchronize()
+    for name in full:
+        if name in ("k_mean", "chan_shift"):
+            continue
+        assert torch.equal(full[name], inc[name]), name
+
+
 @pytest.mark.parametrize("pv_mode", [PV_16, PV_FP8], ids=["pv16", "pvfp8"])
 @pytest.mark.parametrize("case", CASES, ids=[_cid(c) for c in CASES])
 def test_window_parity(lib, case, pv_mode):
