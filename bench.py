@@ -75,21 +75,35 @@ def kernel_traffic(workload, pv):
     return rec["bytes"] if h.hexdigest() == rec["source_sha256"] else None
 
 
+def torch_stack(parts):
+    import torch
+    return torch.stack(parts).contiguous()
+
+
 def step_parts(sage, w, desc, q, k, v, o, bufs, stream):
     """The two halves of one step as callables: (quantize, attend)."""
     if not w.frame_stride:
         return (lambda: sage.sage_attn_quantize(desc, q, k, v, bufs, stream),
                 lambda: sage.sage_attn_fwd_quantized(desc, bufs, o, stream))
-    # streaming step: the current frame (every batch is at the same frame) and
-    # the queries into the cache
+    # streaming step: each batch's current frame (its new keys and values, as
+    # the model would hand them over) and the queries into the cache
     F = w.frame_len
-    fq = w.q_pos0s()[0] // F
-    assert all(p // F == fq for p in w.q_pos0s())
-    kk, vv = k[:, :, fq * F:(fq + 1) * F], v[:, :, fq * F:(fq + 1) * F]
+    fq = [p // F for p in w.q_pos0s()]
+    same = all(f == fq[0] for f in fq)
+    if same:
+        kk, vv = k[:, :, fq[0] * F:(fq[0] + 1) * F], v[:, :, fq[0] * F:(fq[0] + 1) * F]
+    else:
+        kk = torch_stack([k[b, :, f * F:(f + 1) * F] for b, f in enumerate(fq)])
+        vv = torch_stack([v[b, :, f * F:(f + 1) * F] for b, f in enumerate(fq)])
     d2 = sage.Desc.for_tensors(q, kk, vv, nkv=w.Nkv, pv_mode=desc.pv_mode, frame_len=F,
                                frame_stride=w.frame_stride)
-    return (lambda: sage.sage_attn_quantize_frames(d2, q, kk, vv, fq, 1, bufs, stream),
-            lambda: sage.sage_attn_fwd_quantized(desc, bufs, o, stream))
+    if same:
+        def quant():
+            sage.sage_attn_quantize_frames(d2, q, kk, vv, fq[0], 1, bufs, stream)
+    else:
+        def quant():
+            sage.sage_attn_quantize_frames_batched(d2, q, kk, vv, fq, 1, bufs, stream)
+    return quant, lambda: sage.sage_attn_fwd_quantized(desc, bufs, o, stream)
 
 
 def time_path(torch, parts, stream, steps, warm):
@@ -246,7 +260,9 @@ def main():
                      "hbm_frac": round(qbytes / (ms_quant * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
     }
     if ms_full_quant is not None:
-        record["quantize"]["kind"] = "append one frame + queries (sage_attn_quantize_frames)"
+        per_batch = len({p // w.frame_len for p in w.q_pos0s()}) > 1
+        record["quantize"]["kind"] = ("append each session's frame + queries (sage_attn_quantize_frames_batched)"
+                                      if per_batch else "append one frame + queries (sage_attn_quantize_frames)")
         record["quantize"]["whole_cache_ms"] = round(ms_full_quant, 4)
     if other is not None:
         record["other_pv_mode"] = other
@@ -341,8 +357,8 @@ def oracle_sample(w, Q, K, V, pv_mode, b, rows, S, heads):
     if M is not None:
         o64 = emulate.emulate_block_sparse(Q, K, V, pv_mode, w.dtype, M, S, w.frame_len, kv, qp, rows=rows)
     elif w.frame_stride:
-        mu = quant.k_mean(K)
-        a = quant.channel_shift(Q, K, mu)
+        mu = quant.k_mean(K, kv)
+        a = quant.channel_shift(Q, K, mu, kv)
         o64 = emulate.emulate_frame_cache(Q, K, V, pv_mode, w.dtype, w.frame_len, w.frame_stride,
                                           w.sink_frames, w.window_frames, kv, qp, mu, a, S, rows=rows)
     else:

@@ -37,6 +37,12 @@ stand in for them, with the token grids of such clips:
            W [13824, 5120] ~ N(0, 0.02^2), bias ~ N(0, 0.1^2), bf16 -- the
            shape of a 14B-class video DiT's feed-forward up-projection (the
            pages' 14B text/image-to-video models; TurboDiffusion digests).
+  stream-cache, batched-cache
+           the stream and batched workloads over a quantize-once frame
+           cache (2048-slot frame stride, every earlier frame visible): a
+           step appends each session's current frame (its new keys and
+           values) and quantizes the queries, then attends over the cache
+           -- the cache is not re-quantized every step.
 
 Values are N(0,1) float32, then rounded to the 16-bit dtype.  Each (tensor,
 batch, head) slice has its own seed, so any subset of heads can be drawn on
@@ -164,6 +170,15 @@ def get(name, **override):
     elif name == "sparse":
         w = Workload("sparse", 1, 40, 75600, 75600, 128, "bf16", 0, seed=303,
                      outlier_frac=0.01, block_density=0.25)
+    elif name == "stream-cache":
+        w = Workload("stream-cache", 1, 24, FRAME, 17 * 2048, 128, "bf16", 0,
+                     frame_len=FRAME, kv_len=[17 * FRAME], q_pos0=[16 * FRAME], seed=404,
+                     frame_stride=2048)
+    elif name == "batched-cache":
+        L = np.random.default_rng(505).integers(4, 33, 8)
+        w = Workload("batched-cache", 8, 24, FRAME, 33 * 2048, 128, "bf16", 1,
+                     frame_len=FRAME, kv_len=[int((x + 1) * FRAME) for x in L],
+                     q_pos0=[int(x * FRAME) for x in L], seed=505, frame_stride=2048)
     else:
         raise KeyError(name)
     for k, v in override.items():
@@ -171,7 +186,8 @@ def get(name, **override):
     return w
 
 
-NAMES = ("tiny", "small", "large", "stream", "batched", "window", "sparse", "linear")
+NAMES = ("tiny", "small", "large", "stream", "batched", "window", "sparse", "linear", "stream-cache",
+         "batched-cache")
 
 
 _MASKS = {}
