@@ -109,6 +109,10 @@ int make_plan(const sage_attn_desc* d, Plan* p) {
   if (d->B < 1 || d->H < 1 || d->Nq < 1 || d->Nkv < 1) return fail(SAGE_E_SHAPE, "B, H, Nq and Nkv must be >= 1");
   if (d->B > SAGE_MAX_BATCH) return fail(SAGE_E_UNSUPPORTED, "B > SAGE_MAX_BATCH");
   if (d->Nq > (1 << 28) || d->Nkv > (1 << 28)) return fail(SAGE_E_SHAPE, "sequence length too large");
+  // The attention kernel addresses one head's staged K and V (16-bit V^T:
+  // Nkv_pad * d * 2 bytes) through buffer resources with 32-bit offsets.
+  if (pad128(d->Nkv) * d->d * 2 > 0x7FFFFFFF)
+    return fail(SAGE_E_SHAPE, "Nkv too large: ceil(Nkv/128)*128 * d * 2 must stay below 2^31");
   const int64_t bh = static_cast<int64_t>(d->B) * d->H;
   if (bh * pad128(d->Nq) / 128 * SAGE_MAX_SPLITS > 0x7FFFFFFF) return fail(SAGE_E_SHAPE, "too many work items");
   if (d->frame_len < 0) return fail(SAGE_E_MASK, "frame_len must be >= 0");

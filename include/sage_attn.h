@@ -54,6 +54,9 @@
  * Tensors.  Q [B,H,Nq,d], K and V [B,H,Nkv,d], O [B,H,Nq,d], all of one
  * 16-bit type (fp16 or bf16), device memory, channel dimension contiguous,
  * strides of the b, h and n dimensions given in ELEMENTS.  d is 64 or 128.
+ * One head's staged K/V must stay below 2 GiB: ceil(Nkv/128)*128 * d * 2 <
+ * 2^31, i.e. Nkv <= 8,388,480 for d = 128 and 16,776,960 for d = 64
+ * (SAGE_E_SHAPE otherwise).
  *
  * Ownership.  The caller allocates every device buffer (inputs, output,
  * workspace); the library never allocates, frees or synchronizes (except

@@ -77,6 +77,10 @@ def _status(desc):
 def test_valid_desc_and_workspace(lib):
     st, n = _status(_desc())
     assert st == 0 and n > 0
+    # the largest key lengths whose per-head K/V slices the kernel can address
+    for nkv, d in ((8388480, 128), (16776960, 64)):
+        st, n = _status(_desc(Nkv=nkv, d=d))
+        assert st == 0 and n > 2 * nkv * d, sage.load().sage_attn_last_error()
     st8, n8 = _status(_desc(pv_mode=sage.SAGE_PV_FP8))
     assert st8 == 0 and n8 != n
 
@@ -87,6 +91,8 @@ def test_valid_desc_and_workspace(lib):
     (dict(B=1, kv_len=[0]), 6), (dict(B=1, frame_len=50, kv_len=[120], q_pos0=[30]), 6),
     (dict(q_stride=(100 * 128 * 2, 100 * 128, 127)), 4), (dict(B=129), 7),
     (dict(sm_scale=float("nan")), 2),
+    # one head's 16-bit V^T reaches 2^31 bytes (32-bit buffer offsets)
+    (dict(Nkv=8388481), 2), (dict(Nkv=16777089, d=64), 2),
     # frame cache and window
     (dict(frame_stride=64, Nkv=320), 6),                                   # no frame_len
     (dict(frame_len=50, frame_stride=100, Nkv=300), 6),                    # not a multiple of 64
