@@ -55,6 +55,8 @@ def parse():
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run one plain 256 MiB device copy (reference for HBM byte counters)")
     p.add_argument("--single-mode", action="store_true", help="do not time the other P.V mode")
+    p.add_argument("--kv-splits", type=int, default=0,
+                   help="KV splits per query tile (0: the library's choice)")
     return p.parse_args()
 
 
@@ -175,6 +177,7 @@ def main():
     def setup(pv_mode):
         desc = sage.Desc.for_tensors(q, k, v, o, pv_mode=pv_mode, frame_len=w.frame_len,
                                      kv_len=w.kv_len, q_pos0=w.q_pos0, block_mask=mask_dev,
+                                     kv_splits=args.kv_splits,
                                      **(dict(nkv=w.Nkv, frame_stride=w.frame_stride,
                                              sink_frames=w.sink_frames, window_frames=w.window_frames)
                                         if w.frame_stride else {}))
