@@ -145,7 +145,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the path is "
-              "data-parallel over (batch, head) and needs no collectives; see DESIGN.md for sharding)",
+              "data-parallel over (batch, head): G GPUs would each run the same kernel on H/G heads "
+              "with no communication)",
               file=sys.stderr)
         sys.exit(2)
     import torch
