@@ -11,6 +11,9 @@ cases with closed forms, and the largest batch and split counts.
   scores are 0; checked against the emulation.
 * B = SAGE_MAX_BATCH with ragged frames, and kv_splits = SAGE_MAX_SPLITS.
 * Inputs of very large and very small magnitude.
+* The largest key length the kernel addresses (a head's 16-bit V^T just under
+  2^31 bytes): its last key block dominates every row, so every output row is
+  that block's V row.
 """
 
 import numpy as np
@@ -155,3 +158,30 @@ def test_extreme_magnitudes(lib, scale_qk, scale_v):
     assert cs >= cs_emul - 1e-3
     if scale_qk < 1:
         assert cs >= 0.999
+
+
+@pytest.mark.parametrize("pv_mode", [PV_16, PV_FP8])
+def test_largest_key_length_reads_its_last_block(lib, pv_mode):
+    """Nkv = 8388480, d = 128: the last 64 keys are 25 e_0 and every query has
+    20 in channel 0, so their logit is 500 / sqrt(128) = 44 nats (codes 127 x
+    127 at scales 20/127 and 25/127, exact) against at most ~5 for the 8.4M
+    random keys: all weight is on those 64 keys, equally.  With their V rows
+    equal to a constant C, O = C in bf16 (FP8: C's e4m3 reconstruction)."""
+    B, H, Nq, Nkv, d = 1, 1, 256, 8388480, 128
+    g = torch.Generator(device="cuda").manual_seed(71)
+    q = (torch.randn((B, H, Nq, d), generator=g, device="cuda") * 0.5).to(torch.bfloat16)
+    q[..., 0] = 20.0
+    k = (torch.randn((B, H, Nkv, d), generator=g, device="cuda") * 0.5).to(torch.bfloat16)
+    k[:, :, -64:, :] = 0.0
+    k[:, :, -64:, 0] = 25.0
+    v = torch.randn((B, H, Nkv, d), generator=g, device="cuda").to(torch.bfloat16)
+    c = _rand((1, 1, 1, d), 72)
+    v[:, :, -64:, :] = c.cuda()
+    print(f"  Nkv {Nkv}: V^T bytes per head {Nkv * d * 2} (< 2^31)", flush=True)
+    out, _, desc, _, _ = run_gpu(q, k, v, pv_mode)
+    print(f"  kv splits {sage.sage_attn_kv_splits(desc)}", flush=True)
+    C = host(c)
+    if pv_mode == PV_FP8:
+        vc, ve, _ = quant.quantize_v_fp8(np.broadcast_to(C, (1, 1, 64, d)).copy())
+        C = codecs.round_to(quant.dequant_v_fp8(vc, ve)[:, :, :1].astype(np.float32), "bf16")
+    np.testing.assert_array_equal(host(out), np.broadcast_to(C, (B, H, Nq, d)))
