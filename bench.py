@@ -271,7 +271,7 @@ def main():
     if other is not None:
         record["other_pv_mode"] = other
     if not args.no_cpu and not args.profile:
-        record["cpu_baseline"], record["parity"] = cpu_leg(w, x, o, desc, args, sage, torch)
+        record["cpu_baseline"], record["parity"] = cpu_leg(w, x, o, desc, args, sage, torch, ops)
     print(json.dumps(record), flush=True)
 
 
@@ -351,7 +351,8 @@ def main_linear(args, torch, sage, workloads):
 def oracle_sample(w, Q, K, V, pv_mode, b, rows, S, heads):
     """The oracle on a sample of batch b (Q, K, V: host arrays of the given heads):
     (emulated output with the kernel's KV splits, float64 attention, seconds
-    the emulation -- quantization included -- took)."""
+    the emulation -- quantization included -- took, seconds the float64
+    attention took)."""
     from oracle import emulate, attention, quant
     import workloads
     kv, qp = [w.kv_lens()[b]], [w.q_pos0s()[b]]
@@ -371,9 +372,10 @@ def oracle_sample(w, Q, K, V, pv_mode, b, rows, S, heads):
         o64, _ = emulate.emulate_from_inputs(Q, K, V, pv_mode, w.dtype, frame_len=w.frame_len, kv_len=kv,
                                              q_pos0=qp, rows=rows, splits=splits)
     t_emul = time.perf_counter() - t0
+    t0 = time.perf_counter()
     ref = attention.attention_fp64(Q, K, V, frame_len=w.frame_len, kv_len=kv, q_pos0=qp, rows=rows,
                                    sink_frames=w.sink_frames, window_frames=w.window_frames, block_mask=M)
-    return o64, ref, t_emul
+    return o64, ref, t_emul, time.perf_counter() - t0
 
 
 def accuracy_sample(w, x, o, desc, pv_mode, sage, heads=2, rows=256):
@@ -386,14 +388,25 @@ def accuracy_sample(w, x, o, desc, pv_mode, sage, heads=2, rows=256):
     Q = x["q"][0:1, hs].float().cpu().numpy()
     K = x["k"][0:1, hs].float().cpu().numpy()
     V = x["v"][0:1, hs].float().cpu().numpy()
-    o64, ref, _ = oracle_sample(w, Q, K, V, pv_mode, 0, r, S, hs)
+    o64, ref, _, _ = oracle_sample(w, Q, K, V, pv_mode, 0, r, S, hs)
     og = o[0:1, hs][:, :, r].float().cpu().numpy()
     cos = float((og * ref).sum() / np.sqrt((og ** 2).sum() * (ref ** 2).sum()))
     return {"rows": len(r) * len(hs), "max_abs_vs_emulation": float(np.abs(og - o64).max()),
             "cosine_vs_fp64": round(cos, 6)}
 
 
-def cpu_leg(w, x, o, desc, args, sage, torch):
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_leg(w, x, o, desc, args, sage, torch, full_ops):
     """Time the oracle (as it stands) on a bounded sample of the same workload,
     and compare the GPU output on the same rows."""
     from threadpoolctl import threadpool_info
@@ -406,7 +419,7 @@ def cpu_leg(w, x, o, desc, args, sage, torch):
     Q = x["q"][b:b + 1, heads].float().cpu().numpy()
     K = x["k"][b:b + 1, heads].float().cpu().numpy()
     V = x["v"][b:b + 1, heads].float().cpu().numpy()
-    o64, ref, t_cpu = oracle_sample(w, Q, K, V, w.pv_mode, b, rows, S, heads)
+    o64, ref, t_cpu, t_ref = oracle_sample(w, Q, K, V, w.pv_mode, b, rows, S, heads)
     og = o[b:b + 1, heads][:, :, rows].float().cpu().numpy()
     if w.block_density:
         sample_ops = 4 * w.d * sum(int(w.row_keys(b, rows, h).sum()) for h in heads)
@@ -417,7 +430,10 @@ def cpu_leg(w, x, o, desc, args, sage, torch):
     cpu = {"value": round(sample_ops / t_cpu / 1e12, 6), "unit": "TOPS", "cores": threads, "kind": "oracle",
            "sample": f"batch 0, heads {heads[0]}..{heads[-1]}, {len(rows)} query rows each "
                      f"(all their visible keys), quantize + emulated attention, "
-                     f"{t_cpu:.1f} s"}
+                     f"{t_cpu:.1f} s",
+           "fp64_reference": {"s": float(f"{t_ref:.4g}"), "TOPS": float(f"{sample_ops / t_ref / 1e12:.4g}")},
+           "extrapolated_full_workload_s": round(t_cpu * full_ops / sample_ops, 1),
+           "cpu_model": cpu_model(), "os_cpu_count": os.cpu_count()}
     parity = {"rows": len(rows) * len(heads), "max_abs_vs_emulation": float(np.abs(og - o64).max()),
               "cosine_vs_fp64": round(cos, 6)}
     return cpu, parity

@@ -45,3 +45,6 @@ def test_bench_json_line(lib, capsys, monkeypatch):
     cb = r["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]
     assert cb["unit"] == r["unit"]
+    # the float64 reference timed on its own; the whole workload extrapolated from the sample
+    assert cb["fp64_reference"]["s"] > 0 and cb["fp64_reference"]["TOPS"] > 0
+    assert cb["extrapolated_full_workload_s"] > 0 and cb["cpu_model"]
