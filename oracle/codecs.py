@@ -114,13 +114,19 @@ def round_e4m3(x):
 # ----------------------------------------------------------------- E8M0
 
 
+E8M0_MIN = -127  # the smallest scale an E8M0 byte holds: byte 0 is 2^-127
+
+
 def e8m0_exponent(amax):
-    """Smallest integer e with amax * 2^-e <= 448 (e = 0 when amax == 0).
+    """Smallest integer e >= -127 with amax * 2^-e <= 448 (e = 0 when
+    amax == 0).
 
     With amax = m * 2^k, m in [0.5, 1): amax * 2^-e <= 0.875 * 2^9 holds for
-    e >= k - 9 when m <= 0.875 and for e >= k - 8 otherwise.
+    e >= k - 9 when m <= 0.875 and for e >= k - 8 otherwise.  A block whose
+    amax lies below 448 * 2^-127 keeps the scale 2^-127 (byte 0): its values
+    then round to e4m3 subnormals or zero.
     """
     a = np.asarray(amax, dtype=np.float64)
     m, k = np.frexp(a)
-    e = np.where(m <= 0.875, k - 9, k - 8)
+    e = np.maximum(np.where(m <= 0.875, k - 9, k - 8), E8M0_MIN)
     return np.where(a == 0, 0, e).astype(np.int64)

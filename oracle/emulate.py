@@ -1,10 +1,13 @@
 """Quantized attention, emulated on the CPU step by step.
 
+Test infrastructure: only tests/, the smoke check and the bench's CPU
+baseline use this module; the library never does.
+
 The pages describe SageAttention only as low-bit quantized attention that
 keeps the output of the FlashAttention it replaces ("37:54 One line of code,
 twice the speed"; "02:48 There were clearly faster compute units on the
-hardware").  This module is the library's own stated algorithm, written out so
-that each rounding the GPU performs happens here in the same precision:
+hardware").  This module is the library's own stated algorithm, written out
+step by step in the precision the scheme fixes:
 
 Given the INT8 codes and scales of ``quant`` (and V^, the P.V operand:
 V itself in 16-bit mode, or its dequantized FP8 codes), for every query row i
@@ -16,19 +19,12 @@ chunks of BK = 64 (chunk t = keys [64t, 64t+64)), in ascending order:
      c_t      = fp32(qs * dk[t])             (log2-domain scale of chunk t)
   3. tm       = max over visible j of fp32(S[i,j] * c_t)  (-inf if none)
   4. lazy running max: if tm > fp32(m + TAU) the row adopts m' = tm and
-     rescales its state by alpha = exp2(fp32(m - m')) (0 when m = -inf);
+     rescales its state by alpha = fp32(2^fp32(m - m')) (0 when m = -inf);
      otherwise m, l and acc are kept as they are.
-  5. x[i,j]   = S[i,j] * c_t - mref, mref = fp32(m - s) (s = 4 in FP8 mode,
-     0 in 16-bit mode), evaluated on the score as the float32
-     F = F0 + S * 2^-26, where F0 is the float32 with bits 0x3E22F983 (the
-     constant 1/(2 pi)); F is exact (its bits are those of F0 plus S) for
-     |S| < 2292099.  With c2 = c_t * 2^26 (exact):
-        K = fp32(-F0 * c2 - mref)   (one FMA, per row and chunk)
-        x = fp32(F * c2 + K)        (one FMA)
-     so x is S c_t - mref up to K's rounding (half an ulp of
-     |K| <= 1.07e7 c_t + |mref|: about 0.64 c_t, under one integer step of
-     S, when the first term dominates) and x's own;  p = fp32(2^x), 0 if not
-     visible.
+  5. x[i,j]   = fp32(S[i,j] * c_t - mref), rounded once from the exact value
+              (|S| < 2^24, so S is a float32 and this is a fused multiply-add),
+     with mref = fp32(m - s) (s = 4 in FP8 mode, 0 in 16-bit mode);
+     p = fp32(2^x), 0 if not visible.
   6. p~       = p rounded to the P.V operand type: e4m3fn in FP8 mode (where
      p already carries the 2^s pre-scale), else the input's fp16/bf16
   7. l       += sum_j p~                     (the rounded operand itself)
@@ -42,18 +38,31 @@ Because m only moves when a chunk maximum exceeds it by more than TAU, the
 exponent argument is at most TAU + s = 8, so p~ never exceeds 2^8 -- inside
 both e4m3fn (448) and the 16-bit types.
 
-Split-KV: when ``splits`` lists chunk ranges, each range runs steps 1-8 from a
-fresh state and the partial results are merged exactly (float64):
-M = max_s m_s, O = sum_s acc_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
+Split-KV: each batch's key chunks form one ordered list (``split_ranges``,
+``cache_splits``); split s takes entries [s*n/S, (s+1)*n/S) of it, runs steps
+1-8 from a fresh state, and the partial results are merged exactly (float64):
+M = max_s m_s, O = sum_s acc_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).  Where
+the cut falls changes which keys share a running max, hence how P rounds; the
+list depends only on the batch (its key range, frames and window), not on how
+query rows are grouped into work.
 
-Accumulations (l, acc) are float64 here; the GPU keeps them in float32.  That,
-the GPU's hardware exp2 (within ~1 ulp) and the final division are the only
-places where the two may differ, all far below the acceptance tolerance.
+Accumulations (l, acc) are float64 here.
+
+Sensitivity bound.  An implementation that evaluates step 5 with extra
+rounding (its exponent argument within dx of x) and 2^x with a relative error
+up to rel_exp can round some p differently in step 6, because p~ is a
+rounding of p: such a flip moves p~ by one step of the P.V operand type.  With
+``slack`` given, the emulation also carries, per row, the interval of every
+p~ reachable that way -- W_j = round(p_hi) - round(p_lo), rounding being
+monotone -- and returns the bound that follows from
+O' - O = sum_j (p~'_j - p~_j)(V^_j - O) / l':
+    |O' - O| <= (sum_j W_j |V^_j| + |O| sum_j W_j) / (l - sum_j W_j),
+both sums taken with the same rescalings and split weights as acc and l.
 """
 
 import numpy as np
 
-from .constants import BQ, BK, TAU, PSHIFT_FP8, PSHIFT_16, LOG2E, PV_16, PV_FP8, CACHE_TILE
+from .constants import BQ, BK, TAU, PSHIFT_FP8, PSHIFT_16, LOG2E, PV_16, PV_FP8
 from . import codecs
 from .fp32 import fma_f32
 from .attention import row_end, default_q_pos0
@@ -68,20 +77,80 @@ def log2_scale(sm_scale, d):
     return _F32(np.float64(_F32(sm_scale)) * LOG2E)
 
 
+def exponent_arg(S, c_t, mref):
+    """Step 5: x = fp32(S c_t - mref), one rounding (rows of S pair with
+    entries of c_t and mref; S integer scores, |S| < 2^24)."""
+    S = np.asarray(S, dtype=np.float64)
+    if np.any(np.abs(S) >= 2.0 ** 24):
+        raise ValueError("score outside float32's exact integers")
+    R, n = S.shape
+    c = np.broadcast_to(np.asarray(c_t, _F32)[:, None], (R, n))
+    k = np.broadcast_to((-np.asarray(mref, _F32))[:, None], (R, n))
+    return fma_f32(S.astype(_F32), c, k)
+
+
+class Slack:
+    """How far an implementation may deviate from steps 4-5 (see the module
+    docstring): dx(c_t, mref, x) -> per-element bound on |x' - x| (arrays of
+    shape [R, n] from c_t, mref [R] and x [R, n]); rel_exp: relative error of
+    its 2^x (and of alpha and the split weights); flush: results below 2^-126
+    may be flushed to zero."""
+
+    def __init__(self, dx, rel_exp, flush=True):
+        self.dx = dx
+        self.rel_exp = float(rel_exp)
+        self.flush = flush
+
+
+class _State:
+    """Running state of a set of rows: m, l, acc, and with ``aux`` the sums
+    that bound an implementation's deviation: a = sum p~ |V^| (rows x d),
+    wl = sum W, wa = sum W |V^|, and the visible-key count."""
+
+    def __init__(self, R, d, aux):
+        self.m = np.full(R, -np.inf, dtype=_F32)
+        self.l = np.zeros(R, dtype=np.float64)
+        self.acc = np.zeros((R, d), dtype=np.float64)
+        self.aux = aux
+        if aux:
+            self.a = np.zeros((R, d))
+            self.wl = np.zeros(R)
+            self.wa = np.zeros((R, d))
+            self.nvis = np.zeros(R, dtype=np.int64)
+            self.nres = np.zeros(R, dtype=np.int64)
+
+    def scale(self, alpha):
+        self.l = self.l * alpha
+        self.acc = self.acc * alpha[:, None]
+        if self.aux:
+            self.a = self.a * alpha[:, None]
+            self.wl = self.wl * alpha
+            self.wa = self.wa * alpha[:, None]
+
+
+def _round_p(p, pv_mode, p_dtype):
+    """Step 6 on float64 values (monotone in p)."""
+    if pv_mode == PV_FP8:
+        return codecs.round_e4m3(p)
+    return codecs.round_to(p.astype(_F32), p_dtype).astype(np.float64)
+
+
 def _run_rows(S_full, c_row, dk_bh, vis_end, Vhat_bh, chunk_lo, chunk_hi,
-              pv_mode, p_dtype, trace=None):
+              pv_mode, p_dtype, trace=None, slack=None, perturb=None):
     """Steps 1-8 over chunks [chunk_lo, chunk_hi) for a set of rows.
 
     vis_end: per row, the exclusive end of its visible key prefix; or a
     boolean [R, keys] visibility matrix.
     trace: optional list; receives the running max m after every chunk.
+    slack: optional ``Slack``; the state then carries the deviation sums.
+    perturb: test hook, f(x, c_t, mref) -> x' standing in for an
+    implementation's step 5 (its result is then rounded by exp2 as usual).
+    Returns the final ``_State``.
     """
     vis_end = np.asarray(vis_end)
     R = S_full.shape[0]
     d = Vhat_bh.shape[1]
-    m = np.full(R, -np.inf, dtype=_F32)
-    l = np.zeros(R, dtype=np.float64)
-    acc = np.zeros((R, d), dtype=np.float64)
+    st = _State(R, d, slack is not None)
     for t in range(chunk_lo, chunk_hi):
         j0 = t * BK
         j1 = min(j0 + BK, S_full.shape[1])
@@ -92,40 +161,17 @@ def _run_rows(S_full, c_row, dk_bh, vis_end, Vhat_bh, chunk_lo, chunk_hi,
         if not vis.any():
             continue
         c_t = (c_row * _F32(dk_bh[t])).astype(_F32)          # [R] fp32
-        S = S_full[:, j0:j1]
-        m, l, acc = _chunk_step(S, c_t, vis, m, l, acc, Vhat_bh[j0:j1], pv_mode, p_dtype)
+        _chunk_step(S_full[:, j0:j1], c_t, vis, st, Vhat_bh[j0:j1], pv_mode, p_dtype, slack, perturb)
         if trace is not None:
-            trace.append(m.copy())
-    return m, l, acc
+            trace.append(st.m.copy())
+    return st
 
 
-F0 = np.array(0x3E22F983, dtype=np.uint32).view(np.float32)  # 1/(2 pi) as float32
-S_BIAS_LIMIT = 2292099   # |S| below this keeps F0 + S 2^-26 in F0's binade
-
-
-def score_as_float(S):
-    """The float32 F0 + S 2^-26 (exact: bits(F) = bits(F0) + S) for integer
-    scores |S| < 2292099."""
-    S = np.asarray(S, dtype=np.float64)
-    if np.any(np.abs(S) >= S_BIAS_LIMIT):
-        raise ValueError("score outside the biased-float range")
-    return (np.float64(F0) + S * 2.0 ** -26).astype(_F32)
-
-
-def scaled_logit(S, c_t, mref):
-    """Step 5: x = S c_t - mref as two float32 FMAs on F = F0 + S 2^-26 (rows of
-    S pair with entries of c_t and mref)."""
-    F = score_as_float(S)
-    c2 = (np.asarray(c_t, _F32) * _F32(2.0 ** 26)).astype(_F32)      # exact
-    K = fma_f32(np.broadcast_to(-F0, c2.shape), c2, -np.asarray(mref, _F32))
-    return fma_f32(F, np.broadcast_to(c2[:, None], F.shape), np.broadcast_to(K[:, None], F.shape))
-
-
-def _chunk_step(S, c_t, vis, m, l, acc, Vc, pv_mode, p_dtype):
+def _chunk_step(S, c_t, vis, st, Vc, pv_mode, p_dtype, slack=None, perturb=None):
     """Steps 3-8 for one chunk; c_t is per row (rows may span Q blocks)."""
     shift = PSHIFT_FP8 if pv_mode == PV_FP8 else PSHIFT_16
-    c64 = c_t.astype(np.float64)[:, None]
-    logit = (S * c64).astype(_F32)
+    m = st.m
+    logit = (S * c_t.astype(np.float64)[:, None]).astype(_F32)       # exact product, one rounding
     tm = np.where(vis, logit, -np.inf).max(axis=1).astype(_F32)
     upd = tm > (m + _F32(TAU)).astype(_F32)
     with np.errstate(invalid="ignore"):
@@ -133,21 +179,43 @@ def _chunk_step(S, c_t, vis, m, l, acc, Vc, pv_mode, p_dtype):
     alpha = np.where(np.isneginf(m), _F32(0.0),
                      np.exp2(np.where(upd, diff, _F32(0)).astype(np.float64)).astype(_F32))
     alpha = np.where(upd, alpha, _F32(1.0)).astype(np.float64)
-    m = np.where(upd, tm, m).astype(_F32)
-    l = l * alpha
-    acc = acc * alpha[:, None]
+    st.m = m = np.where(upd, tm, m).astype(_F32)
+    st.scale(alpha)
     # a row still at m = -inf has no visible key in this chunk; its p is 0
     mref = np.where(np.isneginf(m), _F32(0.0), (m - _F32(shift)).astype(_F32)).astype(_F32)
-    x = scaled_logit(S, c_t, mref)
+    x = exponent_arg(S, c_t, mref)
+    if perturb is not None:
+        x = np.asarray(perturb(x, c_t, mref), dtype=_F32)
     p = np.exp2(x.astype(np.float64)).astype(_F32)
     p = np.where(vis, p, _F32(0.0))
-    if pv_mode == PV_FP8:
-        pt = codecs.round_e4m3(p.astype(np.float64))
-    else:
-        pt = codecs.round_to(p, p_dtype).astype(np.float64)
-    l = l + pt.sum(axis=1)
-    acc = acc + pt @ Vc
-    return m, l, acc
+    pt = _round_p(p.astype(np.float64), pv_mode, p_dtype)
+    st.l = st.l + pt.sum(axis=1)
+    st.acc = st.acc + pt @ Vc
+    if st.aux:
+        x64 = x.astype(np.float64)
+        dx = np.asarray(slack.dx(c_t, mref, x), dtype=np.float64)
+        r = slack.rel_exp
+        lo = np.exp2(x64 - dx) * (1 - r)
+        hi = np.exp2(x64 + dx) * (1 + r)
+        if slack.flush:
+            lo = np.where(lo < 2.0 ** -126, 0.0, lo)
+        W = np.where(vis, _round_p(hi, pv_mode, p_dtype) - _round_p(lo, pv_mode, p_dtype), 0.0)
+        aV = np.abs(Vc)
+        st.a = st.a + pt @ aV
+        st.wl = st.wl + W.sum(axis=1)
+        st.wa = st.wa + W @ aV
+        st.nvis = st.nvis + vis.sum(axis=1)
+        st.nres = st.nres + upd
+
+
+def split_ranges(kv_len_b, nsplit):
+    """Chunk ranges of the KV splits over contiguous keys: the batch's chunks
+    [0, ceil(kv_len/64)) cut into nsplit equal parts (split s takes
+    [s*n/nsplit, (s+1)*n/nsplit)); None for one split."""
+    n = -(-int(kv_len_b) // BK)
+    if nsplit <= 1:
+        return None
+    return [(s * n // nsplit, (s + 1) * n // nsplit) for s in range(nsplit)]
 
 
 def visible_slots(rows, n_slots, kv_len_b, q_pos0_b, frame_len, frame_stride,
@@ -167,7 +235,7 @@ def sage_attention_emulated(qcodes, dq, kcodes, dk, Vhat, pv_mode, dtype,
                             sm_scale=None, frame_len=0, kv_len=None,
                             q_pos0=None, rows=None, splits=None,
                             frame_stride=0, sink_frames=0, window_frames=0,
-                            block_mask=None):
+                            block_mask=None, slack=None, perturb=None):
     """Emulate the quantized attention for the selected query rows.
 
     qcodes int8 [B,H,Nq,d], dq float32 [B,H,ceil(Nq/128)];
@@ -175,7 +243,9 @@ def sage_attention_emulated(qcodes, dq, kcodes, dk, Vhat, pv_mode, dtype,
     Vhat: the P.V right operand as exact values [B,H,Nkv,d] -- V (16-bit
     mode) or dequant_v_fp8(...) (FP8 mode);  dtype: 'bf16' | 'f16' (input and
     output type, and P's type in 16-bit mode).
-    splits: optional list of (chunk_lo, chunk_hi) ranges covering the keys.
+    splits: optional list of (chunk_lo, chunk_hi) ranges covering the keys,
+    or a list of such lists, one per batch (see ``split_ranges`` and
+    ``cache_splits``).
     frame_stride > 0: K/V operands are a frame cache (``quant.quantize_k_frames``
     layout: frame f's tokens at slots f*frame_stride + [0, frame_len)); kv_len and
     q_pos0 stay in tokens; sink_frames / window_frames restrict the visible
@@ -183,9 +253,11 @@ def sage_attention_emulated(qcodes, dq, kcodes, dk, Vhat, pv_mode, dtype,
     block_mask: optional [B,H,ceil(Nq/128),ceil(Nkv/64)] (contiguous keys);
     chunks of dropped tiles are skipped -- they change neither m, l nor acc,
     exactly as if they were absent -- and a row with no visible key gives 0.
-    splits then index the tile's list of kept chunks (see
-    ``sparse_tile_splits``).
-    Returns (O64 float64 [B,H,R,d], O rounded to dtype as float32).
+    slack, perturb: see ``Slack`` and ``_run_rows``.
+    Returns (O64 float64 [B,H,R,d], O rounded to dtype as float32); with
+    slack, a third item: a dict of float64 arrays [B,H,R(,d)] -- 'a' =
+    sum p~ |V^| / l, 'flip' = the sensitivity bound of the module docstring,
+    'nvis' = visible keys of the row, 'nres' = rescales of its running max.
     """
     qcodes = np.asarray(qcodes)
     kcodes = np.asarray(kcodes)
@@ -196,9 +268,12 @@ def sage_attention_emulated(qcodes, dq, kcodes, dk, Vhat, pv_mode, dtype,
     qp = default_q_pos0(Nq, kv, frame_len) if q_pos0 is None else np.asarray(q_pos0, np.int64)
     rows = np.arange(Nq) if rows is None else np.asarray(rows, dtype=np.int64)
     nchunks = -(-Nkv // BK)
-    if splits is None:
-        splits = [(0, nchunks)]
+    if splits is not None and len(splits) and isinstance(splits[0], tuple):
+        splits = [splits] * B
     out = np.empty((B, H, len(rows), d), dtype=np.float64)
+    if slack is not None:
+        aux = {k: np.zeros((B, H, len(rows), d)) for k in ("a", "flip")}
+        aux.update({k: np.zeros((B, H, len(rows)), np.int64) for k in ("nvis", "nres")})
     if window_frames and not frame_stride:
         raise ValueError("sink/window frames need the frame cache layout")
     if block_mask is not None and frame_stride:
@@ -213,6 +288,7 @@ def sage_attention_emulated(qcodes, dq, kcodes, dk, Vhat, pv_mode, dtype,
         else:
             vis_end = row_end(rows, kv[b], qp[b], frame_len)
             jmax = int(vis_end.max())
+        parts_b = [(0, nchunks)] if splits is None or splits[b] is None else splits[b]
         for h in range(H):
             vis_h = vis_end
             if block_mask is not None:
@@ -222,18 +298,37 @@ def sage_attention_emulated(qcodes, dq, kcodes, dk, Vhat, pv_mode, dtype,
             S_full = qcodes[b, h, rows, :].astype(np.float64) @ \
                 kcodes[b, h, :jmax, :].astype(np.float64).T                # exact
             Vh = np.asarray(Vhat[b, h, :jmax, :], dtype=np.float64)
-            parts = [_run_rows(S_full, qs, dk[b, h], vis_h, Vh, lo, hi, pv_mode, dtype)
-                     for (lo, hi) in splits]
-            ms = np.stack([p[0] for p in parts]).astype(np.float64)        # [P, R]
-            ls = np.stack([p[1] for p in parts])
-            accs = np.stack([p[2] for p in parts])
+            parts = [_run_rows(S_full, qs, dk[b, h], vis_h, Vh, lo, hi, pv_mode, dtype,
+                               slack=slack, perturb=perturb)
+                     for (lo, hi) in parts_b]
+            ms = np.stack([p.m for p in parts]).astype(np.float64)         # [P, R]
             M = np.max(ms, axis=0)
             with np.errstate(invalid="ignore"):   # rows with no key at all: M = -inf
                 w = np.where(np.isneginf(ms), 0.0, np.exp2(ms - M[None, :]))
-            L = np.sum(w * ls, axis=0)
-            num = np.sum(w[:, :, None] * accs, axis=0)
-            out[b, h] = np.where(L[:, None] > 0, num / np.where(L > 0, L, 1.0)[:, None], 0.0)
+
+            def merged(get, vec):
+                tot = sum((w[i][:, None] if vec else w[i]) * get(p) for i, p in enumerate(parts))
+                return tot
+
+            L = merged(lambda p: p.l, False)
+            num = merged(lambda p: p.acc, True)
+            has = L > 0
+            Ls = np.where(has, L, 1.0)
+            O = np.where(has[:, None], num / Ls[:, None], 0.0)
+            out[b, h] = O
+            if slack is not None:
+                WL = merged(lambda p: p.wl, False)
+                aux["a"][b, h] = np.where(has[:, None], merged(lambda p: p.a, True) / Ls[:, None], 0.0)
+                lo = np.maximum(L - WL, 0.0)
+                flip = (merged(lambda p: p.wa, True) + np.abs(O) * WL[:, None])
+                with np.errstate(divide="ignore", invalid="ignore"):
+                    flip = np.where(flip > 0, flip / np.where(lo > 0, lo, 0.0)[:, None], 0.0)
+                aux["flip"][b, h] = np.where(has[:, None], flip, 0.0)
+                aux["nvis"][b, h] = sum(p.nvis for p in parts)
+                aux["nres"][b, h] = sum(p.nres for p in parts)
     rounded = codecs.round_to(out.astype(_F32), dtype)
+    if slack is not None:
+        return out, rounded, aux
     return out, rounded
 
 
@@ -251,7 +346,7 @@ def scores_int(qcodes, kcodes):
 def emulate_from_inputs(Q, K, V, pv_mode, dtype, sm_scale=None, frame_len=0,
                         kv_len=None, q_pos0=None, rows=None, splits=None,
                         mu=None, shift=None, frame_stride=0, sink_frames=0,
-                        window_frames=0, block_mask=None):
+                        window_frames=0, block_mask=None, slack=None, perturb=None):
     """Quantize the 16-bit inputs with ``quant`` and run the emulation.
 
     frame_stride > 0: K and V (tokens of whole frames from frame 0) go into a
@@ -263,15 +358,16 @@ def emulate_from_inputs(Q, K, V, pv_mode, dtype, sm_scale=None, frame_len=0,
     Vf = np.asarray(V, dtype=np.float32)
     if frame_stride:
         qc, dq = quant.quantize_q(Qf, shift)
-        kc, dk = quant.quantize_k_frames(Kf, mu, shift, frame_len, frame_stride)
+        kc, dk = quant.quantize_k_frames(Kf, mu, shift, frame_len, frame_stride, kv_len=kv_len)
         if pv_mode == PV_FP8:
-            vc, ve = quant.quantize_v_fp8_frames(Vf, frame_len, frame_stride)
+            vc, ve = quant.quantize_v_fp8_frames(Vf, frame_len, frame_stride, kv_len=kv_len)
             Vhat = quant.dequant_v_fp8(vc, ve)
         else:
             Vhat = quant.to_frame_slots(Vf, frame_len, frame_stride).astype(np.float64)
         return sage_attention_emulated(qc, dq, kc, dk, Vhat, pv_mode, dtype, sm_scale,
                                        frame_len, kv_len, q_pos0, rows, splits,
-                                       frame_stride, sink_frames, window_frames)
+                                       frame_stride, sink_frames, window_frames,
+                                       slack=slack, perturb=perturb)
     if mu is None:
         mu = quant.k_mean(Kf, kv_len)
     a = quant.channel_shift(Qf, Kf, mu, kv_len) if shift is None else shift
@@ -284,30 +380,39 @@ def emulate_from_inputs(Q, K, V, pv_mode, dtype, sm_scale=None, frame_len=0,
         Vhat = Vf.astype(np.float64)
     return sage_attention_emulated(qc, dq, kc, dk, Vhat, pv_mode, dtype, sm_scale,
                                    frame_len, kv_len, q_pos0, rows, splits,
-                                   block_mask=block_mask)
+                                   block_mask=block_mask, slack=slack, perturb=perturb)
 
 
-def cache_tile_splits(first, last, q_pos0_b, kv_len_b, frame_len, frame_stride,
-                      sink_frames, window_frames, nsplit):
-    """Chunk ranges of the split work items of one query tile (rows
-    first..last, CACHE_TILE of them) over a frame cache.
-
-    The tile's key chunks, in order, are those of the sink frames, then those
-    of the window frames up to the last row's frame (through its last valid
-    token); with no window, every chunk up to there.  Split s takes entries
-    [s*n/nsplit, (s+1)*n/nsplit) of that list.  Each entry range is returned
-    as the physical chunk range that spans it: chunks of the gap between the
-    sinks and the window are invisible to every row of the tile, so they
-    change nothing in the emulation.  (Window reading: Vidu S1 blog, section
-    "Infra".)"""
+def cache_list(Nq, q_pos0_b, kv_len_b, frame_len, frame_stride, sink_frames, window_frames):
+    """The ordered key-chunk list of one batch over a frame cache: every chunk
+    that some query row of the batch can see, ascending -- the chunks of the
+    sink frames, then those of the window frames from the first row's window
+    start through the last row's frame (up to its last valid token); with no
+    window, every chunk up to there.  Returns (a0, b1, end): entry v is chunk
+    v for v < a0, else chunk b1 + (v - a0); n = a0 + end - b1 entries.
+    (Window reading: Vidu S1 blog, section "Infra".)"""
     cpf = frame_stride // BK
-    fq_lo = (q_pos0_b + first) // frame_len
-    fq_hi = (q_pos0_b + last) // frame_len
+    fq_lo = q_pos0_b // frame_len
+    fq_hi = (q_pos0_b + Nq - 1) // frame_len
     end = (fq_hi * frame_stride + min(frame_len, kv_len_b - fq_hi * frame_len) + BK - 1) // BK
     a0 = b1 = 0
     if window_frames > 0:
         a0 = min(min(sink_frames, fq_hi + 1) * cpf, end)
         b1 = max(min(max(sink_frames, fq_lo - window_frames) * cpf, end), a0)
+    return a0, b1, end
+
+
+def cache_splits(Nq, q_pos0_b, kv_len_b, frame_len, frame_stride, sink_frames, window_frames,
+                 nsplit):
+    """Chunk ranges of the KV splits of one batch over a frame cache: split s
+    takes entries [s*n/nsplit, (s+1)*n/nsplit) of ``cache_list``, returned as
+    the physical chunk range that spans them (chunks of the gap between the
+    sinks and the window are invisible to every row, so they change nothing
+    in the emulation); None for one split."""
+    if nsplit <= 1:
+        return None
+    a0, b1, end = cache_list(Nq, q_pos0_b, kv_len_b, frame_len, frame_stride, sink_frames,
+                             window_frames)
     n = a0 + (end - b1)
 
     def phys(v):
@@ -322,97 +427,27 @@ def cache_tile_splits(first, last, q_pos0_b, kv_len_b, frame_len, frame_stride,
 
 
 def emulate_frame_cache(Q, K, V, pv_mode, dtype, frame_len, frame_stride, sink_frames,
-                        window_frames, kv_len, q_pos0, mu, shift, nsplit, rows=None):
-    """``emulate_from_inputs`` over a frame cache, tile by tile of CACHE_TILE
-    query rows, each tile with the chunk ranges of its split work items
-    (``cache_tile_splits``).  Q [B,H,Nq,d]; K, V [B,H,tokens,d] of whole
-    frames from frame 0; mu, shift: the frozen mean and exponents.
-    Returns float64 O [B,H,R,d] for the selected rows (all when None)."""
-    from . import quant
-    Qf = np.asarray(Q, dtype=np.float32)
-    B, H, Nq, d = Qf.shape
-    rows = np.arange(Nq) if rows is None else np.asarray(rows, dtype=np.int64)
-    qc, dq = quant.quantize_q(Qf, shift)
-    kc, dk = quant.quantize_k_frames(np.asarray(K, dtype=np.float32), mu, shift, frame_len, frame_stride,
-                                     kv_len=kv_len)
-    Vf = np.asarray(V, dtype=np.float32)
-    if pv_mode == PV_FP8:
-        vc, ve = quant.quantize_v_fp8_frames(Vf, frame_len, frame_stride, kv_len=kv_len)
-        Vhat = quant.dequant_v_fp8(vc, ve)
-    else:
-        Vhat = quant.to_frame_slots(Vf, frame_len, frame_stride).astype(np.float64)
-    out = np.empty((B, H, len(rows), d))
-    for b in range(B):
-        for t in np.unique(rows // CACHE_TILE):
-            sel = np.nonzero(rows // CACHE_TILE == t)[0]
-            first, last = t * CACHE_TILE, min(t * CACHE_TILE + CACHE_TILE, Nq) - 1
-            sp = cache_tile_splits(first, last, int(q_pos0[b]), int(kv_len[b]), frame_len,
-                                   frame_stride, sink_frames, window_frames, nsplit)
-            o64, _ = sage_attention_emulated(qc[b:b + 1], dq[b:b + 1], kc[b:b + 1], dk[b:b + 1],
-                                             Vhat[b:b + 1], pv_mode, dtype, None, frame_len,
-                                             [kv_len[b]], [q_pos0[b]], rows[sel],
-                                             sp if nsplit > 1 else None, frame_stride,
-                                             sink_frames, window_frames)
-            out[b, :, sel] = o64[0].transpose(1, 0, 2)
-    return out
-
-
-def sparse_tile_splits(mask_row, n_chunks, nsplit):
-    """Chunk ranges of the split work items of one 128-query tile under a
-    block mask: the tile's list is its kept chunks among [0, n_chunks) (the
-    chunks its last row can see), in ascending order; split s takes entries
-    [s*n/nsplit, (s+1)*n/nsplit) of it, returned as the physical chunk range
-    that spans them (the dropped chunks inside are invisible to the tile)."""
-    kept = np.nonzero(np.asarray(mask_row)[:n_chunks] != 0)[0]
-    n = kept.size
-    out = []
-    for s in range(nsplit):
-        lo, hi = s * n // nsplit, (s + 1) * n // nsplit
-        if hi > lo:
-            out.append((int(kept[lo]), int(kept[hi - 1]) + 1))
-    return out
+                        window_frames, kv_len, q_pos0, mu, shift, nsplit, rows=None, slack=None):
+    """``emulate_from_inputs`` over a frame cache with each batch's KV splits
+    (``cache_splits``).  Q [B,H,Nq,d]; K, V [B,H,tokens,d] of whole frames
+    from frame 0; mu, shift: the frozen mean and exponents.  Returns what
+    ``sage_attention_emulated`` returns."""
+    Nq = np.shape(Q)[2]
+    sp = [cache_splits(Nq, int(q_pos0[b]), int(kv_len[b]), frame_len, frame_stride, sink_frames,
+                       window_frames, nsplit) for b in range(np.shape(Q)[0])]
+    return emulate_from_inputs(Q, K, V, pv_mode, dtype, None, frame_len, kv_len, q_pos0, rows, sp,
+                               mu, shift, frame_stride, sink_frames, window_frames, slack=slack)
 
 
 def emulate_block_sparse(Q, K, V, pv_mode, dtype, block_mask, nsplit, frame_len=0, kv_len=None,
-                         q_pos0=None, rows=None, mu=None, shift=None):
-    """``emulate_from_inputs`` with a block mask, tile by tile of 128 query
-    rows, each tile with the chunk ranges of its split work items
-    (``sparse_tile_splits``).  Returns float64 O [B,H,R,d]."""
-    from . import quant
-    from .attention import row_end
-    Qf = np.asarray(Q, dtype=np.float32)
-    Kf = np.asarray(K, dtype=np.float32)
-    Vf = np.asarray(V, dtype=np.float32)
-    B, H, Nq, d = Qf.shape
-    Nkv = Kf.shape[2]
+                         q_pos0=None, rows=None, mu=None, shift=None, slack=None):
+    """``emulate_from_inputs`` with a block mask and nsplit KV splits: split s
+    covers the batch's chunks [s*n/nsplit, (s+1)*n/nsplit) (n =
+    ceil(kv_len/64), as without a mask) and, inside them, each query tile's
+    kept chunks.  Returns what ``sage_attention_emulated`` returns."""
+    B, _, _, _ = np.shape(Q)
+    Nkv = np.shape(K)[2]
     kv = np.full(B, Nkv, np.int64) if kv_len is None else np.asarray(kv_len, np.int64)
-    qp = default_q_pos0(Nq, kv, frame_len) if q_pos0 is None else np.asarray(q_pos0, np.int64)
-    rows = np.arange(Nq) if rows is None else np.asarray(rows, dtype=np.int64)
-    if mu is None:
-        mu = quant.k_mean(Kf, kv)
-    a = quant.channel_shift(Qf, Kf, mu, kv) if shift is None else shift
-    qc, dq = quant.quantize_q(Qf, a)
-    kc, dk = quant.quantize_k(Kf, mu, kv, a)
-    if pv_mode == PV_FP8:
-        vc, ve, _ = quant.quantize_v_fp8(Vf, kv)
-        Vhat = quant.dequant_v_fp8(vc, ve)
-    else:
-        Vhat = Vf.astype(np.float64)
-    out = np.empty((B, H, len(rows), d))
-    for b in range(B):
-        for t in np.unique(rows // BQ):
-            sel = np.nonzero(rows // BQ == t)[0]
-            last = min(t * BQ + BQ, Nq) - 1
-            nch = -(-int(row_end([last], kv[b], qp[b], frame_len)[0]) // BK)
-            for h in range(H):
-                sp = sparse_tile_splits(block_mask[b, h, t], nch, nsplit)
-                if not sp:
-                    out[b, h, sel] = 0.0
-                    continue
-                o64, _ = sage_attention_emulated(qc[b:b + 1, h:h + 1], dq[b:b + 1, h:h + 1], kc[b:b + 1, h:h + 1],
-                                                 dk[b:b + 1, h:h + 1], Vhat[b:b + 1, h:h + 1], pv_mode, dtype,
-                                                 None, frame_len, [kv[b]], [qp[b]], rows[sel],
-                                                 sp if nsplit > 1 else None,
-                                                 block_mask=block_mask[b:b + 1, h:h + 1])
-                out[b, h, sel] = o64[0, 0]
-    return out
+    sp = [split_ranges(kv[b], nsplit) for b in range(B)]
+    return emulate_from_inputs(Q, K, V, pv_mode, dtype, None, frame_len, kv, q_pos0, rows, sp,
+                               mu, shift, block_mask=block_mask, slack=slack)

@@ -211,8 +211,9 @@ def test_lazy_running_max_policy_by_hand():
         S[0, 64 * t + 7] = mx * 2                  # integer scores, c = 0.5
     trace = []
     V = np.ones((S.shape[1], 4))
-    m, l, acc = _run_rows(S, np.array([0.5], np.float32), np.ones(len(maxima), np.float32),
-                          np.array([S.shape[1]]), V, 0, len(maxima), PV_16, "bf16", trace)
+    st = _run_rows(S, np.array([0.5], np.float32), np.ones(len(maxima), np.float32),
+                   np.array([S.shape[1]]), V, 0, len(maxima), PV_16, "bf16", trace)
+    l, acc = st.l, st.acc
     assert [float(x[0]) for x in trace] == [0.0, 0.0, 6.0, 6.0, 11.0, 11.0]
     # l sums the rounded weights: all-ones V gives exactly 1
     np.testing.assert_allclose(acc / l[:, None], 1.0, rtol=0, atol=1e-15)
@@ -240,3 +241,57 @@ def test_emulation_constant_v_columns_pass_through(pv_mode, dtype, frame_len):
         want = V[:, :, :1].astype(np.float64)
     want = codecs.round_to(want.astype(np.float32), dtype)
     assert np.array_equal(o, np.broadcast_to(want, o.shape))
+
+
+@pytest.mark.parametrize("pv_mode,dtype", [(PV_16, "bf16"), (PV_16, "f16"), (PV_FP8, "bf16")])
+def test_sensitivity_bound_holds_under_perturbed_exponents(pv_mode, dtype):
+    """An implementation whose exponent argument is off by up to dx and whose
+    2^x is off by up to rel_exp (relative) rounds some p differently; the
+    emulation's 'flip' bound must contain every such output.  The perturbed
+    runs push each x towards a rounding boundary by (almost) the full slack,
+    in random directions, with splits and frames, and the slack is made
+    large (many flips) so that a missing term of the bound shows."""
+    rng = np.random.default_rng(28)
+    B, H, Nq, Nkv, d = 2, 2, 70, 400, 32
+    Q, K, V = _inputs(rng, B, H, Nq, Nkv, d, dtype)
+    Q *= 2
+    kv, F = [400, 333], 64
+    slack = emulate.Slack(lambda c, mref, x: 2e-3 + 1e-4 * np.abs(x), 1e-3)
+    sp = [emulate.split_ranges(k, 3) for k in kv]
+    o, _, aux = emulate.emulate_from_inputs(Q, K, V, pv_mode, dtype, frame_len=F, kv_len=kv,
+                                            splits=sp, slack=slack)
+    flip = aux["flip"]
+    assert np.all(flip >= 0) and flip.max() > 0
+    worst = 0.0
+    for trial in range(4):
+        r = np.random.default_rng(100 + trial)
+
+        def perturb(x, c, mref):
+            x64 = x.astype(np.float64)
+            dx = 0.999 * (2e-3 + 1e-4 * np.abs(x64))
+            sgn = r.choice([-1.0, 1.0], size=x.shape)
+            eps = r.uniform(-0.999e-3, 0.999e-3, size=x.shape)
+            # float32 rounding of x' stays inside the slack (0.1% margin)
+            return (x64 + sgn * dx + np.log2(1 + eps)).astype(np.float32)
+
+        o2, _ = emulate.emulate_from_inputs(Q, K, V, pv_mode, dtype, frame_len=F, kv_len=kv,
+                                            splits=sp, perturb=perturb)
+        d_ = np.abs(o2 - o)
+        assert np.all(d_ <= flip * (1 + 1e-9) + 1e-15)
+        worst = max(worst, float((d_ / np.where(flip > 0, flip, 1)).max()))
+    assert worst > 0.02       # the perturbations really moved outputs towards the bound
+
+
+def test_sensitivity_sums_match_their_definitions():
+    """'a' is the emulation run on |V| (the same weights times |V^|); with no
+    slack nothing can flip; nvis counts each row's visible keys."""
+    rng = np.random.default_rng(29)
+    Q, K, V = _inputs(rng, 1, 2, 50, 300, 16, "bf16")
+    kv, F = [290], 64
+    zero = emulate.Slack(lambda c, mref, x: np.zeros_like(x, dtype=np.float64), 0.0, flush=False)
+    for pv_mode in (PV_16, PV_FP8):
+        o, _, aux = emulate.emulate_from_inputs(Q, K, V, pv_mode, "bf16", frame_len=F, kv_len=kv, slack=zero)
+        oa, _ = emulate.emulate_from_inputs(Q, K, np.abs(V), pv_mode, "bf16", frame_len=F, kv_len=kv)
+        assert np.array_equal(aux["a"], oa)
+        assert not aux["flip"].any()
+        assert np.array_equal(aux["nvis"][0, 0], attention.row_end(np.arange(50), 290, 240, F))

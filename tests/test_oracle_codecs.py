@@ -120,6 +120,10 @@ def test_e8m0_exponent_is_smallest_fitting_power():
         assert Fraction(ai) * Fraction(2) ** (-int(ei)) <= 448
         assert Fraction(ai) * Fraction(2) ** (-int(ei) + 1) > 448
     assert codecs.e8m0_exponent(np.array([0.0]))[0] == 0
+    # below 448 * 2^-127 the scale stays at the E8M0 minimum 2^-127 (byte 0)
+    tiny = np.array([448 * 2.0 ** -127, np.nextafter(448 * 2.0 ** -127, 0), 1e-37, 2.0 ** -149])
+    assert list(codecs.e8m0_exponent(tiny)) == [-127, -127, -127, -127]
+    assert codecs.e8m0_exponent(np.array([np.nextafter(448 * 2.0 ** -127, 1)]))[0] == -126
 
 
 # ------------------------------------------------------------------ fp32 FMA
@@ -175,42 +179,37 @@ def test_fma_f32_double_rounding_cases():
     assert math.isfinite(ref)
 
 
-def test_score_as_float_is_the_biased_bit_pattern():
-    """F0 + S 2^-26 is exactly the float32 whose bits are 0x3E22F983 + S, over
-    the whole score range (|S| <= 127^2 d for d <= 128) and to the limit."""
-    from oracle.emulate import score_as_float, S_BIAS_LIMIT
-    rng = np.random.default_rng(31)
-    S = np.concatenate([rng.integers(-S_BIAS_LIMIT + 1, S_BIAS_LIMIT, 20000),
-                        [0, 1, -1, 127 * 127 * 128, -127 * 127 * 128, S_BIAS_LIMIT - 1, -S_BIAS_LIMIT + 1]])
-    F = score_as_float(S)
-    assert np.array_equal(F.view(np.uint32).astype(np.int64), 0x3E22F983 + S.astype(np.int64))
-    with pytest.raises(ValueError):
-        score_as_float(np.array([S_BIAS_LIMIT]))
-
-
-def test_scaled_logit_two_fma_error_bound():
-    """x = fma(F, c 2^26, fma(-F0, c 2^26, -mref)) against the exact rational
-    S c - mref: off by at most half an ulp of K (its one intermediate
-    rounding) plus half an ulp of x, and x equals the single-rounded value
-    whenever K is exact (c = 0 or mref = 0 with a power-of-two c)."""
+def test_exponent_argument_is_rounded_once():
+    """Step 5 of the emulation: x = fp32(S c - mref) is the float32 nearest to
+    the exact rational S c - mref (ties to even), over the whole score range
+    (|S| <= 127^2 d for d <= 128) and scales from 1e-8 to 1e-1, including
+    cases where a float64 evaluation followed by a float32 rounding would
+    round twice (tiny c against a large mref)."""
     from fractions import Fraction
-    from oracle.emulate import scaled_logit, F0
+    from oracle.emulate import exponent_arg
     rng = np.random.default_rng(32)
     n = 3000
     S = rng.integers(-2_064_512, 2_064_513, (n, 1)).astype(np.float64)
     c = (10.0 ** rng.uniform(-8, -1, n)).astype(np.float32)
     mref = rng.uniform(-40, 40, n).astype(np.float32)
-    x = scaled_logit(S, c, mref)[:, 0]
-
-    def ulp(v):
-        return Fraction(2) ** (int(np.floor(np.log2(abs(float(v))))) - 23) if v != 0 else Fraction(0)
+    # double-rounding traps: S c = (2^22 + a)(2^22 - a) 2^-68 = 2^-24 - a^2 2^-68
+    # lies just below half an ulp of -mref = 1 + (2k+1) 2^-23 (odd last bit);
+    # a float64 sum rounds to the midpoint, whose float32 rounding then goes
+    # up to the even neighbour, while the exact value rounds down
+    a = np.arange(1, 51)
+    S[:50, 0] = 2 ** 22 + a
+    c[:50] = ((2 ** 22 - a) * 2.0 ** -68).astype(np.float32)
+    mref[:50] = -(1.0 + (2 * a + 1) * 2.0 ** -23)
+    twice = ((S[:50, 0] * c[:50].astype(np.float64) - mref[:50].astype(np.float64))).astype(np.float32)
+    x = exponent_arg(S, c, mref)[:, 0]
+    assert np.all(twice != x[:50])
     for i in range(n):
         exact = Fraction(int(S[i, 0])) * Fraction(float(c[i])) - Fraction(float(mref[i]))
-        k_exact = -Fraction(float(F0)) * Fraction(float(c[i])) * 2 ** 26 - Fraction(float(mref[i]))
-        err = abs(Fraction(float(x[i])) - exact)
-        assert err <= ulp(k_exact) / 2 + ulp(float(x[i])) / 2 + Fraction(1, 2 ** 140)
-    # K exact: c = 0 gives x = -mref; c = 2^-20, mref = 0 gives x = S 2^-20 exactly
-    z = scaled_logit(S[:5], np.zeros(5, np.float32), mref[:5])[:, 0]
+        assert float(x[i]) == _round_fraction_to_f32(exact), i
+    # c = 0 gives x = -mref; a power-of-two c with mref = 0 gives S c exactly
+    z = exponent_arg(S[:5], np.zeros(5, np.float32), mref[:5])[:, 0]
     assert np.array_equal(z, -mref[:5])
-    w = scaled_logit(S[:5], np.full(5, 2.0 ** -20, np.float32), np.zeros(5, np.float32))[:, 0]
+    w = exponent_arg(S[:5], np.full(5, 2.0 ** -20, np.float32), np.zeros(5, np.float32))[:, 0]
     assert np.array_equal(w.astype(np.float64), S[:5, 0] * 2.0 ** -20)
+    with pytest.raises(ValueError):
+        exponent_arg(np.array([[2.0 ** 24]]), np.ones(1, np.float32), np.zeros(1, np.float32))

@@ -181,3 +181,25 @@ def test_v_fp8_scales_and_codes():
                 ref = np.ldexp(codecs.round_e4m3(np.ldexp(blk, -ee)), ee)
                 np.testing.assert_array_equal(deq[0, h, lo:hi, c], ref)
     assert not codes[0, :, 90:].any()
+
+
+def test_v_fp8_tiny_block_keeps_the_smallest_scale():
+    """A V block whose amax is below 448 * 2^-127 (bf16 goes down to 2^-133)
+    gets E8M0 byte 0 (2^-127), finite codes, and values rounded to e4m3 at
+    that scale -- never a wrapped byte or a NaN."""
+    V = np.zeros((1, 1, 64, 4), np.float32)
+    V[0, 0, :32, 0] = codecs.round_bf16(np.float32(1e-37))
+    V[0, 0, :32, 1] = codecs.round_bf16(np.linspace(-3e-38, 3e-38, 32).astype(np.float32))
+    V[0, 0, 32:, 2] = codecs.round_bf16(np.float32(2.0 ** -133))
+    codes, e, e8 = quant.quantize_v_fp8(V)
+    assert e[0, 0, 0, 0] == -127 and e[0, 0, 0, 1] == -127 and e[0, 0, 1, 2] == -127
+    assert e8[0, 0, 0, 0] == 0 and e8[0, 0, 1, 2] == 0
+    deq = quant.dequant_v_fp8(codes, e)
+    assert np.all(np.isfinite(deq))
+    for c in range(3):
+        blk = V[0, 0, :, c].astype(np.float64)
+        ee = np.repeat(e[0, 0, :, c], 32)
+        ref = np.ldexp(codecs.round_e4m3(np.ldexp(blk, -ee)), ee)
+        np.testing.assert_array_equal(deq[0, 0, :, c], ref)
+    # bf16's smallest subnormal 2^-133 is 2^-6 at this scale: an e4m3 normal, kept exactly
+    assert deq[0, 0, 0, 0] > 0 and deq[0, 0, 32, 2] == 2.0 ** -133

@@ -56,7 +56,7 @@ def test_all_kept_mask_is_the_dense_path(pv_mode):
     a, _ = emulate.emulate_from_inputs(Q, K, V, pv_mode, "bf16", kv_len=[320])
     b, _ = emulate.emulate_from_inputs(Q, K, V, pv_mode, "bf16", kv_len=[320], block_mask=ones)
     assert np.array_equal(a, b)
-    c = emulate.emulate_block_sparse(Q, K, V, pv_mode, "bf16", ones, 1, kv_len=[320])
+    c = emulate.emulate_block_sparse(Q, K, V, pv_mode, "bf16", ones, 1, kv_len=[320])[0]
     assert np.array_equal(a, c)
     r1 = attention.attention_fp64(Q, K, V, kv_len=[320])
     r2 = attention.attention_fp64(Q, K, V, kv_len=[320], block_mask=ones)
@@ -116,21 +116,23 @@ def test_dropped_key_blocks_are_as_if_deleted(pv_mode):
     assert not np.array_equal(sparse, other)
 
 
-def test_sparse_splits_cover_the_kept_chunks():
+@pytest.mark.parametrize("pv_mode", [PV_16, PV_FP8])
+def test_sparse_splits_are_the_dense_grid(pv_mode):
+    """KV splits under a block mask cut the batch's chunk grid exactly as
+    without one: with every tile kept, the split emulation is bit-identical
+    to the dense emulation over the same split ranges."""
     rng = np.random.default_rng(74)
-    for _ in range(50):
-        n = int(rng.integers(1, 40))
-        row = (rng.random(n + 5) < rng.random()).astype(np.uint8)
-        S = int(rng.integers(1, 6))
-        sp = emulate.sparse_tile_splits(row, n, S)
-        kept = set(np.nonzero(row[:n])[0].tolist())
-        got, prev = set(), -1
-        for lo, hi in sp:
-            assert prev < lo < hi and row[lo] and row[hi - 1]
-            got |= {c for c in range(lo, hi) if row[c]}
-            prev = hi - 1
-        assert got == kept
-        assert len(sp) == min(S, len(kept))
+    Q = _rnd16(rng.standard_normal((2, 1, 200, 32)))
+    K = _rnd16(rng.standard_normal((2, 1, 900, 32)))
+    V = _rnd16(rng.standard_normal((2, 1, 900, 32)))
+    kv = [900, 517]
+    ones = np.ones((2, 1, 2, -(-900 // BK)), np.uint8)
+    for S in (2, 3, 5):
+        sparse = emulate.emulate_block_sparse(Q, K, V, pv_mode, "bf16", ones, S, kv_len=kv)[0]
+        dense = emulate.emulate_from_inputs(Q, K, V, pv_mode, "bf16", kv_len=kv,
+                                            splits=[emulate.split_ranges(k, S) for k in kv])[0]
+        assert np.array_equal(sparse, dense)
+        assert emulate.split_ranges(517, S) == [(s * 9 // S, (s + 1) * 9 // S) for s in range(S)]
 
 
 def test_sparse_split_emulation_within_p_rounding():
@@ -141,7 +143,7 @@ def test_sparse_split_emulation_within_p_rounding():
     K = _rnd16(rng.standard_normal((1, 2, 1280, 32)))
     V = _rnd16(rng.standard_normal((1, 2, 1280, 32)))
     M = _mask(rng, 1, 2, 256, 1280, 0.5)
-    o1 = emulate.emulate_block_sparse(Q, K, V, PV_16, "bf16", M, 1)
-    o3 = emulate.emulate_block_sparse(Q, K, V, PV_16, "bf16", M, 3)
+    o1 = emulate.emulate_block_sparse(Q, K, V, PV_16, "bf16", M, 1)[0]
+    o3 = emulate.emulate_block_sparse(Q, K, V, PV_16, "bf16", M, 3)[0]
     assert np.abs(o3 - o1).max() <= 2 * 2 * 2.0 ** -8 * np.abs(V).max()
     assert not np.array_equal(o1, o3)

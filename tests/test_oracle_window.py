@@ -191,22 +191,31 @@ def test_cache_emulation_equals_attention_on_dequantized_operands(pv_mode, eps):
     assert np.abs(o64 - ref).max() <= 2 * eps * np.abs(Vh).max() * 1.01
 
 
-@pytest.mark.parametrize("F,FS,S,W,q0f,first,last,nsplit", [
-    (200, 256, 1, 3, 7, 0, 127, 1), (200, 256, 1, 3, 7, 128, 199, 3), (100, 128, 2, 2, 6, 0, 127, 4),
-    (64, 64, 4, 1, 1, 0, 63, 2), (150, 192, 2, 1, 8, 0, 127, 2), (200, 256, 0, 0, 5, 0, 127, 3),
-    (2040, 2048, 1, 16, 40, 1920, 2039, 3), (2040, 2048, 1, 16, 40, 1792, 2039, 3),
-    (2040, 2048, 1, 4, 9, 0, 255, 5)])
-def test_cache_tile_splits_cover_exactly_the_visible_chunks(F, FS, S, W, q0f, first, last, nsplit):
-    """Brute force over slots: the split ranges are disjoint and ascending, they
-    cover every chunk holding a slot that some row of the tile sees, and every
-    chunk they cover that lies outside the tile's list is invisible to all of
-    its rows."""
-    kv, q0 = (q0f + 1) * F, q0f * F
-    nslots = (q0f + 1) * FS
-    rows = np.arange(first, last + 1)
+@pytest.mark.parametrize("F,FS,S,W,q0,Nq,kv,nsplit", [
+    (200, 256, 1, 3, 1400, 200, 1600, 1), (200, 256, 1, 3, 1250, 350, 1600, 3),
+    (100, 128, 2, 2, 300, 300, 600, 4), (64, 64, 4, 1, 64, 128, 192, 2),
+    (150, 192, 2, 1, 1200, 150, 1350, 2), (200, 256, 0, 0, 1000, 200, 1200, 3),
+    (2040, 2048, 1, 16, 40 * 2040, 2040, 41 * 2040, 3), (2040, 2048, 1, 16, 40 * 2040, 2040, 41 * 2040, 16),
+    (2040, 2048, 1, 4, 8 * 2040 + 1740, 600, 9 * 2040 + 340, 5), (150, 192, 3, 2, 0, 450, 450, 3)])
+def test_cache_splits_cover_exactly_the_visible_chunks(F, FS, S, W, q0, Nq, kv, nsplit):
+    """Brute force over slots, for the batch's whole query range: the split
+    ranges are disjoint and ascending, they cover every chunk holding a slot
+    that some query row sees, every chunk they cover that no row sees lies in
+    the gap between the sink frames and the window, and there are
+    min(nsplit, list length) of them."""
+    nslots = -(-kv // F) * FS
+    rows = np.arange(Nq)
     vis = emulate.visible_slots(rows, nslots, kv, q0, F, FS, S, W)
     vis_chunk = vis.reshape(len(rows), -1, BK).any(axis=(0, 2))
-    sp = emulate.cache_tile_splits(first, last, q0, kv, F, FS, S, W, nsplit)
+    a0, b1, end = emulate.cache_list(Nq, q0, kv, F, FS, S, W)
+    listed = np.zeros(vis_chunk.size, bool)
+    listed[:a0] = True
+    listed[b1:end] = True
+    assert np.array_equal(listed, vis_chunk)      # the list is exactly the visible chunks
+    sp = emulate.cache_splits(Nq, q0, kv, F, FS, S, W, nsplit)
+    if nsplit == 1:
+        assert sp is None
+        return
     covered = np.zeros(vis_chunk.size, bool)
     prev_hi = 0
     for lo, hi in sp:
@@ -214,7 +223,9 @@ def test_cache_tile_splits_cover_exactly_the_visible_chunks(F, FS, S, W, q0f, fi
         covered[lo:hi] = True
         prev_hi = hi
     assert not (vis_chunk & ~covered).any()
-    assert len(sp) == min(nsplit, int(covered.sum()))
+    extra = np.nonzero(covered & ~vis_chunk)[0]
+    assert np.all((extra >= a0) & (extra < b1))
+    assert len(sp) == min(nsplit, int(vis_chunk.sum()))
 
 
 def test_cache_emulation_splits_merge_to_the_unsplit_result():
@@ -230,7 +241,7 @@ def test_cache_emulation_splits_merge_to_the_unsplit_result():
     mu = quant.k_mean(K)
     a = quant.channel_shift(Q, K, mu)
     args = (Q, K, V, PV_16, "bf16", F, FS, S, W, [nf * F], [(nf - 2) * F], mu, a)
-    o1 = emulate.emulate_frame_cache(*args, 1)
-    o3 = emulate.emulate_frame_cache(*args, 3, rows=np.arange(0, 2 * F, 7))
+    o1 = emulate.emulate_frame_cache(*args, 1)[0]
+    o3 = emulate.emulate_frame_cache(*args, 3, rows=np.arange(0, 2 * F, 7))[0]
     assert np.abs(o3 - o1[:, :, ::7]).max() <= 2 * 2 * 2.0 ** -8 * np.abs(V).max()
     assert not np.array_equal(o3, o1[:, :, ::7])  # the split ranges were really taken
