@@ -195,11 +195,12 @@ def _chunk_step(S, c_t, vis, st, Vc, pv_mode, p_dtype, slack=None, perturb=None)
         x64 = x.astype(np.float64)
         dx = np.asarray(slack.dx(c_t, mref, x), dtype=np.float64)
         r = slack.rel_exp
-        lo = np.exp2(x64 - dx) * (1 - r)
-        hi = np.exp2(x64 + dx) * (1 + r)
+        # masked keys take no part (their exponent argument is unbounded)
+        lo = np.where(vis, np.exp2(x64 - dx) * (1 - r), 0.0)
+        hi = np.where(vis, np.exp2(x64 + dx) * (1 + r), 0.0)
         if slack.flush:
             lo = np.where(lo < 2.0 ** -126, 0.0, lo)
-        W = np.where(vis, _round_p(hi, pv_mode, p_dtype) - _round_p(lo, pv_mode, p_dtype), 0.0)
+        W = _round_p(hi, pv_mode, p_dtype) - _round_p(lo, pv_mode, p_dtype)
         aV = np.abs(Vc)
         st.a = st.a + pt @ aV
         st.wl = st.wl + W.sum(axis=1)

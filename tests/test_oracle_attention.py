@@ -295,3 +295,18 @@ def test_sensitivity_sums_match_their_definitions():
         assert np.array_equal(aux["a"], oa)
         assert not aux["flip"].any()
         assert np.array_equal(aux["nvis"][0, 0], attention.row_end(np.arange(50), 290, 240, F))
+
+
+def test_sensitivity_bound_ignores_masked_keys():
+    """Under a causal frame mask a row's invisible keys may score far above
+    its running max (their exponent argument exceeds the range of P); they
+    take no part in the bound.  Keys of later frames are made to dominate."""
+    rng = np.random.default_rng(30)
+    Q, K, V = _inputs(rng, 1, 1, 200, 300, 16, "bf16")
+    Q[..., 0] = 8.0
+    K[0, 0, 200:, 0] = 12.0      # frame 2: seen by the rows of frame 2 only, in chunks shared with frame 1
+    slack = emulate.Slack(lambda c, mref, x: 1e-3 + 0 * x, 1e-4)
+    for pv_mode in (PV_16, PV_FP8):
+        o, _, aux = emulate.emulate_from_inputs(Q, K, V, pv_mode, "bf16", frame_len=100, kv_len=[300],
+                                                q_pos0=[100], slack=slack)
+        assert np.isfinite(aux["flip"]).all()
