@@ -19,7 +19,10 @@ dominant kernel (the fused attention, timed with HIP events on its own stream;
 its HBM traffic from the committed rocprofv3 counters when they were taken on
 the same kernel source, else null), the CPU oracle timed on a bounded sample
 of the same workload, and the other P.V mode timed the same way with its own
-accuracy on a small sample.
+accuracy on a small sample.  With --graph (default for the frame-cache
+streaming workloads) the step is also captured once into a HIP graph
+(torch.cuda.CUDAGraph) and replayed, which removes the per-launch overhead of
+its short kernels; that timing is reported beside the eager one.
 """
 
 import argparse
@@ -36,7 +39,17 @@ sys.path.insert(0, ROOT)
 
 METRIC = "quantized-attention TOPS (4·B·H·Nq·Nkv·d) + % of peak MFMA, 75.6k-token 720p shape"
 INT8_PEAK_TOPS = 5000.0   # MI355X dense INT8 MFMA, 5.0 POP/s
+BF16_PEAK_TOPS = 2500.0   # dense bf16/fp16 MFMA, 2.5 PFLOP/s
+FP8_PEAK_TOPS = 5000.0    # dense FP8 MFMA, 5.0 PFLOP/s
 HBM_PEAK_GBS = 8000.0
+
+
+def mode_peak(pv_mode):
+    """The MFMA ceiling of one P.V mode: half of the 4 d ops per visible pair
+    (Q K^T) run on INT8 matrix cores, the other half (P V) on 16-bit or FP8
+    ones, so the time per op at peak is 0.5 / INT8 + 0.5 / (P.V peak)."""
+    pv = FP8_PEAK_TOPS if pv_mode == 1 else BF16_PEAK_TOPS
+    return 1.0 / (0.5 / INT8_PEAK_TOPS + 0.5 / pv)
 
 
 def parse():
@@ -57,6 +70,10 @@ def parse():
     p.add_argument("--single-mode", action="store_true", help="do not time the other P.V mode")
     p.add_argument("--kv-splits", type=int, default=0,
                    help="KV splits per query tile (0: the library's choice)")
+    p.add_argument("--graph", dest="graph", action="store_true", default=None,
+                   help="also time the step captured in a HIP graph and replayed "
+                        "(default: on for the frame-cache workloads)")
+    p.add_argument("--no-graph", dest="graph", action="store_false")
     return p.parse_args()
 
 
@@ -141,6 +158,66 @@ def time_path(torch, parts, stream, steps, warm):
     return ms_step, ms_quant, ms_attn
 
 
+def time_graph(torch, parts, steps, warm):
+    """Capture one step (quantize + fused kernel) into a HIP graph on a side
+    stream and time `steps` replays.  `parts` must launch on the current
+    stream (the capture stream while capturing).  Returns ms per replayed
+    step."""
+    quant, attend = parts
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(max(warm, 1)):
+            quant()
+            attend()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        quant()
+        attend()
+    for _ in range(max(warm, 1)):
+        g.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        g.replay()
+    end.record()
+    end.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def quantize_bytes(w, pv_mode):
+    """Bytes of the quantize pass: (the minimum, this design's kernels).
+
+    The minimum reads K twice (the K mean needs every key before any key can
+    be smoothed) and Q once, and writes the INT8 codes; FP8 mode adds one
+    read of V and its e4m3 codes and E8M0 scales.  The design moves more:
+    it reads Q twice, because the channel-balance exponent of a channel
+    depends on every query's value in it, so no Q block can be coded before
+    all of Q has been read once; and in 16-bit mode it writes V transposed
+    per 64-key chunk (the P.V operand layout), reading V once for that.  A
+    streaming step over a frame cache moves only the current frame's K and
+    V and the queries (the mean and exponents are frozen)."""
+    esz = 2
+    nq = w.B * w.H * w.Nq * w.d
+    if w.frame_stride:
+        nk = w.B * w.H * w.frame_len * w.d
+        kreads = 1
+    else:
+        nk = w.B * w.H * w.Nkv * w.d
+        kreads = 2
+    vscale = nk // 32 if pv_mode == 1 else 0
+    minimum = nq * esz + kreads * nk * esz + nq + nk
+    if pv_mode == 1:
+        minimum += nk * esz + nk + vscale
+    design = (1 if w.frame_stride else 2) * nq * esz + kreads * nk * esz + nq + nk + \
+        nk * esz + (nk + vscale if pv_mode == 1 else nk * esz)
+    return minimum, design
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -205,10 +282,13 @@ def main():
         other = {"pv": "fp8" if w.pv_mode == 0 else "16",
                  "value": round(ops / (t2[0] * 1e-3) / 1e12, 2),
                  "attn_tops": round(ops / (t2[2] * 1e-3) / 1e12, 2),
+                 "attn_frac_int8_peak": round(ops / (t2[2] * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
                  "ms_per_step": round(t2[0], 4)}
         if not args.no_cpu:
             other["accuracy"] = accuracy_sample(w, x, o, desc2, 1 - w.pv_mode, sage,
                                                 rows=64 if w.block_density else 256)
+            other["meets_bar"] = bool(other["accuracy"]["cosine_vs_fp64"] >= 0.999 and
+                                      other["accuracy"]["max_abs_vs_emulation"] <= 2e-3)
         del ws2, bufs2
     desc, ws, bufs = setup(w.pv_mode)
     ms_step, ms_quant, ms_attn = time_path(torch, step_parts(sage, w, desc, q, k, v, o, bufs, stream),
@@ -220,20 +300,18 @@ def main():
         qfull = (lambda: sage.sage_attn_quantize(desc, q, k, v, bufs, stream), lambda: None)
         ms_full_quant = time_path(torch, qfull, stream, steps, warm)[1]
 
+    ms_graph = None
+    if args.graph is None:
+        args.graph = bool(w.frame_stride)
+    if args.graph and not args.profile:
+        ms_graph = time_graph(torch, step_parts(sage, w, desc, q, k, v, o, bufs, None), steps, warm)
+
     splits = sage.sage_attn_kv_splits(desc)
     attn_tops = ops / (ms_attn * 1e-3) / 1e12
     pvname = "fp8" if w.pv_mode == 1 else "16"
     traffic = kernel_traffic(w.name, pvname)
-    # quantize pass algorithmic bytes: read Q, K twice (statistics, then codes),
-    # V once; write Q/K codes, V layout (16-bit or e4m3) and scales.  A
-    # streaming step reads each of the frame's K, V and the queries once.
-    esz = 2
-    nq = w.B * w.H * w.Nq * w.d
-    nk = w.B * w.H * (w.frame_stride if w.frame_stride else w.Nkv) * w.d
-    vbytes = nk * (1 if w.pv_mode == 1 else 2)
-    qbytes = 2 * nq * esz + 2 * nk * esz + nk * esz + nq + nk + vbytes
-    if w.frame_stride:
-        qbytes = nq * esz + 2 * w.B * w.H * w.frame_len * w.d * esz + nq + nk + vbytes
+    qmin, qdesign = quantize_bytes(w, w.pv_mode)
+    mpeak = mode_peak(w.pv_mode)
     record = {
         "metric": METRIC,
         "value": round(tops, 2),
@@ -257,12 +335,22 @@ def main():
                       if w.frame_stride else {}),
                    "ops_per_step": ops, "pct_int8_peak": round(100 * tops / INT8_PEAK_TOPS, 2)},
         "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel", "achieved": round(attn_tops, 2),
-                     "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s", "frac": round(attn_tops / INT8_PEAK_TOPS, 4),
+                     "peak": INT8_PEAK_TOPS, "unit": "TOPS", "frac": round(attn_tops / INT8_PEAK_TOPS, 4),
+                     "mode_peak": round(mpeak, 1), "mode_frac": round(attn_tops / mpeak, 4),
+                     "mode_peak_note": ("Q K^T on INT8, P V on " + ("FP8" if w.pv_mode == 1 else "16-bit")
+                                        + " matrix cores: 1 / (0.5 / 5000 + 0.5 / "
+                                        + ("5000" if w.pv_mode == 1 else "2500") + ") TOPS"),
                      "traffic": traffic, "ms_per_launch": round(ms_attn, 4)},
-        "quantize": {"ms": round(ms_quant, 4), "algorithmic_bytes": qbytes,
-                     "GB_per_s": round(qbytes / (ms_quant * 1e-3) / 1e9, 1),
-                     "hbm_frac": round(qbytes / (ms_quant * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "quantize": {"ms": round(ms_quant, 4), "algorithmic_bytes": qmin,
+                     "GB_per_s": round(qmin / (ms_quant * 1e-3) / 1e9, 1),
+                     "hbm_frac": round(qmin / (ms_quant * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "design_bytes": qdesign,
+                     "design_GB_per_s": round(qdesign / (ms_quant * 1e-3) / 1e9, 1)},
     }
+    if ms_graph is not None:
+        record["graph_replay"] = {"ms_per_step": round(ms_graph, 4),
+                                  "value": round(ops / (ms_graph * 1e-3) / 1e12, 2),
+                                  "launches_per_step": "quantize kernels + fused kernel (+ split combine)"}
     if ms_full_quant is not None:
         per_batch = len({p // w.frame_len for p in w.q_pos0s()}) > 1
         record["quantize"]["kind"] = ("append each session's frame + queries (sage_attn_quantize_frames_batched)"
@@ -316,7 +404,7 @@ def main_linear(args, torch, sage, workloads):
         "config": {"workload": "linear", "M": w.M, "N": w.N, "K": w.K, "in_dtype": w.dtype, "bias": True,
                    "ops_per_step": ops, "pct_int8_peak": round(100 * ops / (ms_step * 1e-3) / 1e12 / INT8_PEAK_TOPS, 2)},
         "roofline": {"bound": "mfma", "kernel": "w8a8_gemm_kernel", "achieved": round(ops / (ms_gemm * 1e-3) / 1e12, 2),
-                     "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
+                     "peak": INT8_PEAK_TOPS, "unit": "TOPS",
                      "frac": round(ops / (ms_gemm * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
                      "traffic": kernel_traffic("linear", "16"), "ms_per_launch": round(ms_gemm, 4)},
         "quantize": {"ms": round(ms_quant, 4), "algorithmic_bytes": qbytes,
@@ -360,17 +448,15 @@ def oracle_sample(w, Q, K, V, pv_mode, b, rows, S, heads):
     M = M[b:b + 1, heads] if M is not None else None
     t0 = time.perf_counter()
     if M is not None:
-        o64 = emulate.emulate_block_sparse(Q, K, V, pv_mode, w.dtype, M, S, w.frame_len, kv, qp, rows=rows)
+        o64 = emulate.emulate_block_sparse(Q, K, V, pv_mode, w.dtype, M, S, w.frame_len, kv, qp, rows=rows)[0]
     elif w.frame_stride:
         mu = quant.k_mean(K, kv)
         a = quant.channel_shift(Q, K, mu, kv)
         o64 = emulate.emulate_frame_cache(Q, K, V, pv_mode, w.dtype, w.frame_len, w.frame_stride,
-                                          w.sink_frames, w.window_frames, kv, qp, mu, a, S, rows=rows)
+                                          w.sink_frames, w.window_frames, kv, qp, mu, a, S, rows=rows)[0]
     else:
-        n = -(-kv[0] // 64)
-        splits = [(s * n // S, (s + 1) * n // S) for s in range(S)] if S > 1 else None
         o64, _ = emulate.emulate_from_inputs(Q, K, V, pv_mode, w.dtype, frame_len=w.frame_len, kv_len=kv,
-                                             q_pos0=qp, rows=rows, splits=splits)
+                                             q_pos0=qp, rows=rows, splits=emulate.split_ranges(kv[0], S))
     t_emul = time.perf_counter() - t0
     t0 = time.perf_counter()
     ref = attention.attention_fp64(Q, K, V, frame_len=w.frame_len, kv_len=kv, q_pos0=qp, rows=rows,

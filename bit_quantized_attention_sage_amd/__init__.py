@@ -19,7 +19,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsage_attn.so")
 
-SAGE_ATTN_ABI_VERSION = 3
+SAGE_ATTN_ABI_VERSION = 4
 SAGE_F16, SAGE_BF16 = 0, 1
 SAGE_PV_16, SAGE_PV_FP8 = 0, 1
 SAGE_FLAG_DEBUG_SYNC = 0x1
@@ -50,7 +50,7 @@ class sage_quant_bufs(ctypes.Structure):
     _fields_ = [("q_codes", ctypes.c_void_p), ("q_scale", ctypes.c_void_p), ("k_codes", ctypes.c_void_p),
                 ("k_scale", ctypes.c_void_p), ("k_mean", ctypes.c_void_p), ("chan_shift", ctypes.c_void_p),
                 ("v_t", ctypes.c_void_p), ("v_e8m0", ctypes.c_void_p), ("stats", ctypes.c_void_p),
-                ("partial", ctypes.c_void_p)]
+                ("partial", ctypes.c_void_p), ("partial_splits", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class SageError(RuntimeError):
@@ -88,7 +88,7 @@ def load(path=None):
         "sage_attn_last_error": (ctypes.c_char_p, []),
         "sage_attn_constant": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double)]),
         "sage_attn_kv_splits": (ctypes.c_int, [_DESC_P, ctypes.POINTER(ctypes.c_int32)]),
-        "sage_attn_workspace_size": (ctypes.c_int, [_DESC_P, ctypes.POINTER(ctypes.c_size_t)]),
+        "sage_attn_workspace_bytes": (ctypes.c_int, [_DESC_P, ctypes.POINTER(ctypes.c_size_t)]),
         "sage_attn_quant_layout": (ctypes.c_int, [_DESC_P, ctypes.c_void_p, ctypes.c_size_t, _BUFS_P]),
         "sage_attn_quantize": (ctypes.c_int, [_DESC_P, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                               _BUFS_P, ctypes.c_void_p]),
@@ -100,7 +100,7 @@ def load(path=None):
         "sage_attn_fwd_quantized": (ctypes.c_int, [_DESC_P, _BUFS_P, ctypes.c_void_p, ctypes.c_void_p]),
         "sage_attn_fwd": (ctypes.c_int, [_DESC_P, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
-        "sage_attn_debug_scores": (ctypes.c_int, [_DESC_P, _BUFS_P, ctypes.POINTER(ctypes.c_int32),
+        "sage_attn_debug_scores_i32": (ctypes.c_int, [_DESC_P, _BUFS_P, ctypes.POINTER(ctypes.c_int32),
                                                   ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]),
         "sage_attn_debug_convert": (ctypes.c_int, [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                                    ctypes.c_int64, ctypes.c_void_p]),
@@ -206,9 +206,9 @@ def sage_attn_kv_splits(desc):
     return s.value
 
 
-def sage_attn_workspace_size(desc):
+def sage_attn_workspace_bytes(desc):
     n = ctypes.c_size_t()
-    _check(load().sage_attn_workspace_size(desc.ptr, ctypes.byref(n)), "sage_attn_workspace_size")
+    _check(load().sage_attn_workspace_bytes(desc.ptr, ctypes.byref(n)), "sage_attn_workspace_bytes")
     return n.value
 
 
@@ -257,13 +257,13 @@ def sage_attn_fwd(desc, q, k, v, o, ws, stream=None):
            "sage_attn_fwd")
 
 
-def sage_attn_debug_scores(desc, bufs, tiles, out, stream=None):
+def sage_attn_debug_scores_i32(desc, bufs, tiles, out, stream=None):
     """tiles: list of (b*H + h, q0, k0); out: int32 device tensor [n, 32, 64]."""
     flat = [int(x) for t in tiles for x in t]
     arr = (ctypes.c_int32 * max(1, len(flat)))(*flat)
-    _check(load().sage_attn_debug_scores(desc.ptr, ctypes.byref(bufs), arr, len(tiles),
+    _check(load().sage_attn_debug_scores_i32(desc.ptr, ctypes.byref(bufs), arr, len(tiles),
                                          ctypes.c_void_p(out.data_ptr()), _stream(stream)),
-           "sage_attn_debug_scores")
+           "sage_attn_debug_scores_i32")
 
 
 def sage_attn_debug_convert(kind, x, out, stream=None):
@@ -273,7 +273,7 @@ def sage_attn_debug_convert(kind, x, out, stream=None):
 
 def new_workspace(desc, device="cuda"):
     """A device workspace of the size sage_attn_fwd needs (256-byte aligned)."""
-    n = sage_attn_workspace_size(desc)
+    n = sage_attn_workspace_bytes(desc)
     ws = torch.empty(n + 256, dtype=torch.uint8, device=device)
     off = (-ws.data_ptr()) % 256
     return ws[off:off + n]

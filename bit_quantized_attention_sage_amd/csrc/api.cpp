@@ -16,7 +16,7 @@ namespace {
 
 thread_local std::string g_last_error;
 
-int fail(int status, const std::string& msg) {
+sage_status fail(sage_status status, const std::string& msg) {
   g_last_error = msg;
   return status;
 }
@@ -27,6 +27,7 @@ int64_t pad128(int64_t n) { return (n + 127) / 128 * 128; }
 
 struct Plan {
   int B, H, Nq, Nkv, d, Nq_pad, Nkv_pad, splits, frame_len, dtype, pv_mode;
+  int splits_cap;  // KV splits the workspace's partial region holds room for
   int frame_stride, sink_frames, window_frames;
   uint32_t cpf_magic;
   const uint8_t* block_mask;
@@ -98,7 +99,7 @@ int choose_splits(const Plan& p) {
 }
 
 // Validate *d and fill *p.  Pure host code; touches no device memory.
-int make_plan(const sage_attn_desc* d, Plan* p) {
+sage_status make_plan(const sage_attn_desc* d, Plan* p) {
   if (!d) return fail(SAGE_E_NULL, "desc is NULL");
   if (d->abi_version != SAGE_ATTN_ABI_VERSION)
     return fail(SAGE_E_VERSION, "abi_version " + std::to_string(d->abi_version) + " != " +
@@ -185,6 +186,18 @@ int make_plan(const sage_attn_desc* d, Plan* p) {
                                       : static_cast<double>(static_cast<float>(1.0 / sqrt(static_cast<double>(d->d))));
   p->sigma = static_cast<float>(sm * 1.4426950408889634);
   p->splits = d->kv_splits > 0 ? d->kv_splits : choose_splits(*p);
+  // Room in the workspace for the split count of this desc and for the one
+  // it would take with every batch at its full key length, so that a frame
+  // cache carved once stays usable as its kv_len grows.
+  p->splits_cap = p->splits;
+  if (d->kv_splits == 0) {
+    Plan full = *p;
+    for (int b = 0; b < d->B; ++b) {
+      full.bi.kv_len[b] = kv_cap;
+      if (d->frame_len > 0 && !d->q_pos0) full.bi.q_pos0[b] = kv_cap - d->Nq;
+    }
+    p->splits_cap = std::max(p->splits, choose_splits(full));
+  }
   return SAGE_OK;
 }
 
@@ -217,7 +230,7 @@ Layout layout_of(const Plan& p) {
   L.kmin = L.kmax + align_up(bh * nck * p.d * 4);
   L.qamax = L.kmin + align_up(bh * nck * p.d * 4);
   L.stats = take(L.qamax + bh * ncq * p.d * 4);
-  L.partial = take(p.splits > 1 ? static_cast<size_t>(p.splits) * bh * p.Nq_pad * (p.d + 2) * 4 : 0);
+  L.partial = take(p.splits_cap > 1 ? static_cast<size_t>(p.splits_cap) * bh * p.Nq_pad * (p.d + 2) * 4 : 0);
   L.total = off;
   return L;
 }
@@ -234,24 +247,32 @@ sage_quant_bufs bufs_of(const Layout& L, const Plan& p, void* ws) {
   b.v_t = base + L.v_t;
   b.v_e8m0 = p.pv_mode == SAGE_PV_FP8 ? reinterpret_cast<uint8_t*>(base + L.v_e8m0) : nullptr;
   b.stats = base + L.stats;
-  b.partial = p.splits > 1 ? base + L.partial : nullptr;
+  b.partial = p.splits_cap > 1 ? base + L.partial : nullptr;
+  b.partial_splits = p.splits_cap > 1 ? p.splits_cap : 1;
+  b.reserved = 0;
   return b;
 }
 
-int check_bufs(const sage_quant_bufs* b, const Plan& p, bool need_stats) {
+sage_status check_bufs(const sage_quant_bufs* b, const Plan& p, bool need_stats) {
   if (!b) return fail(SAGE_E_NULL, "bufs is NULL");
   if (!b->q_codes || !b->q_scale || !b->k_codes || !b->k_scale || !b->k_mean || !b->chan_shift || !b->v_t)
     return fail(SAGE_E_NULL, "a quantized-operand buffer is NULL");
   if (p.pv_mode == SAGE_PV_FP8 && !b->v_e8m0) return fail(SAGE_E_NULL, "v_e8m0 is NULL in FP8 mode");
   if (need_stats && !b->stats) return fail(SAGE_E_NULL, "stats buffer is NULL");
-  if (p.splits > 1 && !need_stats && !b->partial) return fail(SAGE_E_NULL, "partial buffer is NULL with kv_splits > 1");
+  if (p.splits > 1 && !need_stats) {
+    if (!b->partial) return fail(SAGE_E_NULL, "partial buffer is NULL with kv_splits > 1");
+    if (p.splits > b->partial_splits)
+      return fail(SAGE_E_WORKSPACE, "this call needs " + std::to_string(p.splits) +
+                                        " KV splits but bufs->partial holds " + std::to_string(b->partial_splits) +
+                                        ": carve the workspace for this desc (or its full key length)");
+  }
   if (!aligned16(b->q_codes) || !aligned16(b->k_codes) || !aligned16(b->v_t) ||
       (b->v_e8m0 && !aligned16(b->v_e8m0)) || (b->partial && !aligned16(b->partial)))
     return fail(SAGE_E_ALIGN, "quantized-operand buffers must be 16-byte aligned");
   return SAGE_OK;
 }
 
-int finish(hipError_t e, const sage_attn_desc* d, hipStream_t st) {
+sage_status finish(hipError_t e, const sage_attn_desc* d, hipStream_t st) {
   if (e == hipSuccess && d && (d->flags & SAGE_FLAG_DEBUG_SYNC)) {
     e = hipStreamSynchronize(st);
     if (e == hipSuccess) e = hipGetLastError();
@@ -288,11 +309,12 @@ sage::AttnLaunch attn_launch_of(const Plan& p, const sage_quant_bufs& b, void* o
   return L;
 }
 
-int quantize_impl(const sage_attn_desc* desc, const void* q, const void* k, const void* v, int frames_only,
-                  int frame0, const int32_t* frame0s, int nframes, const sage_quant_bufs* bufs, void* stream) {
+sage_status quantize_impl(const sage_attn_desc* desc, const void* q, const void* k, const void* v,
+                          int frames_only, int frame0, const int32_t* frame0s, int nframes,
+                          const sage_quant_bufs* bufs, void* stream) {
   try {
     Plan p;
-    int s = make_plan(desc, &p);
+    sage_status s = make_plan(desc, &p);
     if (s != SAGE_OK) return s;
     if ((!frames_only && !q) || !k || !v) return fail(SAGE_E_NULL, "q, k and v must be non-NULL");
     if ((q && !aligned16(q)) || !aligned16(k) || !aligned16(v))
@@ -356,7 +378,7 @@ int quantize_impl(const sage_attn_desc* desc, const void* q, const void* k, cons
   }
 }
 
-int w8a8_plan(const sage_w8a8_desc* d, sage::W8A8Launch* L) {
+sage_status w8a8_plan(const sage_w8a8_desc* d, sage::W8A8Launch* L) {
   if (!d) return fail(SAGE_E_NULL, "desc is NULL");
   if (d->abi_version != SAGE_ATTN_ABI_VERSION)
     return fail(SAGE_E_VERSION, "abi_version " + std::to_string(d->abi_version) + " != " +
@@ -384,7 +406,7 @@ int w8a8_plan(const sage_w8a8_desc* d, sage::W8A8Launch* L) {
 
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
-int finish_w8a8(hipError_t e, const sage_w8a8_desc* d, hipStream_t st) {
+sage_status finish_w8a8(hipError_t e, const sage_w8a8_desc* d, hipStream_t st) {
   if (e == hipSuccess && (d->flags & SAGE_FLAG_DEBUG_SYNC)) {
     e = hipStreamSynchronize(st);
     if (e == hipSuccess) e = hipGetLastError();
@@ -399,7 +421,7 @@ extern "C" {
 
 int sage_attn_abi_version(void) { return SAGE_ATTN_ABI_VERSION; }
 
-const char* sage_attn_status_string(int s) {
+const char* sage_attn_status_string(sage_status s) {
   switch (s) {
     case SAGE_OK: return "ok";
     case SAGE_E_NULL: return "null pointer";
@@ -418,12 +440,12 @@ const char* sage_attn_status_string(int s) {
 
 const char* sage_attn_last_error(void) { return g_last_error.c_str(); }
 
-int sage_attn_constant(const char* name, double* value) {
+sage_status sage_attn_constant(const char* name, double* value) {
   if (!name || !value) return fail(SAGE_E_NULL, "name/value is NULL");
   const struct { const char* n; double v; } table[] = {
       {"BQ", sage::BQ}, {"BK", sage::BK}, {"VB", sage::VB}, {"QMAX", sage::QMAX},
       {"TAU", sage::TAU}, {"PSHIFT_FP8", sage::PSHIFT_FP8}, {"PSHIFT_16", sage::PSHIFT_16},
-      {"KMEAN_CHUNK", sage::KMEAN_CHUNK}, {"CACHE_TILE", sage::CACHE_TILE}};
+      {"KMEAN_CHUNK", sage::KMEAN_CHUNK}};
   for (const auto& e : table)
     if (strcmp(e.n, name) == 0) {
       *value = e.v;
@@ -432,11 +454,11 @@ int sage_attn_constant(const char* name, double* value) {
   return fail(SAGE_E_UNSUPPORTED, std::string("unknown constant ") + name);
 }
 
-int sage_attn_kv_splits(const sage_attn_desc* desc, int32_t* splits) {
+sage_status sage_attn_kv_splits(const sage_attn_desc* desc, int32_t* splits) {
   try {
     if (!splits) return fail(SAGE_E_NULL, "splits is NULL");
     Plan p;
-    const int s = make_plan(desc, &p);
+    const sage_status s = make_plan(desc, &p);
     if (s != SAGE_OK) return s;
     *splits = p.splits;
     return SAGE_OK;
@@ -445,11 +467,11 @@ int sage_attn_kv_splits(const sage_attn_desc* desc, int32_t* splits) {
   }
 }
 
-int sage_attn_workspace_size(const sage_attn_desc* desc, size_t* bytes) {
+sage_status sage_attn_workspace_bytes(const sage_attn_desc* desc, size_t* bytes) {
   try {
     if (!bytes) return fail(SAGE_E_NULL, "bytes is NULL");
     Plan p;
-    const int s = make_plan(desc, &p);
+    const sage_status s = make_plan(desc, &p);
     if (s != SAGE_OK) return s;
     *bytes = layout_of(p).total;
     return SAGE_OK;
@@ -458,11 +480,11 @@ int sage_attn_workspace_size(const sage_attn_desc* desc, size_t* bytes) {
   }
 }
 
-int sage_attn_quant_layout(const sage_attn_desc* desc, void* ws, size_t ws_bytes, sage_quant_bufs* out) {
+sage_status sage_attn_quant_layout(const sage_attn_desc* desc, void* ws, size_t ws_bytes, sage_quant_bufs* out) {
   try {
     if (!out) return fail(SAGE_E_NULL, "out is NULL");
     Plan p;
-    const int s = make_plan(desc, &p);
+    const sage_status s = make_plan(desc, &p);
     if (s != SAGE_OK) return s;
     const Layout L = layout_of(p);
     if (!ws) return fail(SAGE_E_WORKSPACE, "workspace is NULL");
@@ -476,27 +498,28 @@ int sage_attn_quant_layout(const sage_attn_desc* desc, void* ws, size_t ws_bytes
   }
 }
 
-int sage_attn_quantize(const sage_attn_desc* desc, const void* q, const void* k, const void* v,
-                       const sage_quant_bufs* bufs, void* stream) {
+sage_status sage_attn_quantize(const sage_attn_desc* desc, const void* q, const void* k, const void* v,
+                               const sage_quant_bufs* bufs, void* stream) {
   return quantize_impl(desc, q, k, v, 0, 0, nullptr, 0, bufs, stream);
 }
 
-int sage_attn_quantize_frames(const sage_attn_desc* desc, const void* q, const void* k, const void* v,
-                              int32_t frame0, int32_t nframes, const sage_quant_bufs* bufs, void* stream) {
+sage_status sage_attn_quantize_frames(const sage_attn_desc* desc, const void* q, const void* k, const void* v,
+                                      int32_t frame0, int32_t nframes, const sage_quant_bufs* bufs, void* stream) {
   return quantize_impl(desc, q, k, v, 1, frame0, nullptr, nframes, bufs, stream);
 }
 
-int sage_attn_quantize_frames_batched(const sage_attn_desc* desc, const void* q, const void* k, const void* v,
-                                      const int32_t* frame0, int32_t nframes, const sage_quant_bufs* bufs,
-                                      void* stream) {
+sage_status sage_attn_quantize_frames_batched(const sage_attn_desc* desc, const void* q, const void* k,
+                                              const void* v, const int32_t* frame0, int32_t nframes,
+                                              const sage_quant_bufs* bufs, void* stream) {
   if (!frame0) return fail(SAGE_E_NULL, "frame0 is NULL");
   return quantize_impl(desc, q, k, v, 1, 0, frame0, nframes, bufs, stream);
 }
 
-int sage_attn_fwd_quantized(const sage_attn_desc* desc, const sage_quant_bufs* bufs, void* o, void* stream) {
+sage_status sage_attn_fwd_quantized(const sage_attn_desc* desc, const sage_quant_bufs* bufs, void* o,
+                                    void* stream) {
   try {
     Plan p;
-    int s = make_plan(desc, &p);
+    sage_status s = make_plan(desc, &p);
     if (s != SAGE_OK) return s;
     if (!o) return fail(SAGE_E_NULL, "o is NULL");
     if (!aligned16(o)) return fail(SAGE_E_ALIGN, "o must be 16-byte aligned");
@@ -509,10 +532,10 @@ int sage_attn_fwd_quantized(const sage_attn_desc* desc, const sage_quant_bufs* b
   }
 }
 
-int sage_attn_fwd(const sage_attn_desc* desc, const void* q, const void* k, const void* v, void* o, void* ws,
-                  size_t ws_bytes, void* stream) {
+sage_status sage_attn_fwd(const sage_attn_desc* desc, const void* q, const void* k, const void* v, void* o,
+                          void* ws, size_t ws_bytes, void* stream) {
   sage_quant_bufs b;
-  int s = sage_attn_quant_layout(desc, ws, ws_bytes, &b);
+  sage_status s = sage_attn_quant_layout(desc, ws, ws_bytes, &b);
   if (s != SAGE_OK) return s;
   if (!o) return fail(SAGE_E_NULL, "o is NULL");
   if (!aligned16(o)) return fail(SAGE_E_ALIGN, "o must be 16-byte aligned");
@@ -521,11 +544,11 @@ int sage_attn_fwd(const sage_attn_desc* desc, const void* q, const void* k, cons
   return sage_attn_fwd_quantized(desc, &b, o, stream);
 }
 
-int sage_attn_debug_scores(const sage_attn_desc* desc, const sage_quant_bufs* bufs, const int32_t* tiles,
-                           int32_t ntiles, int32_t* out, void* stream) {
+sage_status sage_attn_debug_scores_i32(const sage_attn_desc* desc, const sage_quant_bufs* bufs,
+                                      const int32_t* tiles, int32_t ntiles, int32_t* out, void* stream) {
   try {
     Plan p;
-    int s = make_plan(desc, &p);
+    sage_status s = make_plan(desc, &p);
     if (s != SAGE_OK) return s;
     if (!tiles || !out) return fail(SAGE_E_NULL, "tiles/out is NULL");
     if (ntiles < 0) return fail(SAGE_E_SHAPE, "ntiles < 0");
@@ -546,9 +569,9 @@ int sage_attn_debug_scores(const sage_attn_desc* desc, const sage_quant_bufs* bu
   }
 }
 
-int sage_attn_debug_convert(int kind, const float* in, void* out, int64_t n, void* stream) {
+sage_status sage_attn_debug_convert(int kind, const float* in, void* out, int64_t n, void* stream) {
   try {
-    if (kind < 0 || kind > 2) return fail(SAGE_E_UNSUPPORTED, "kind must be 0, 1 or 2");
+    if (kind < 0 || kind > 3) return fail(SAGE_E_UNSUPPORTED, "kind must be 0, 1, 2 or 3");
     if (n < 0) return fail(SAGE_E_SHAPE, "n < 0");
     if (n == 0) return SAGE_OK;
     if (!in || !out) return fail(SAGE_E_NULL, "in/out is NULL");
@@ -560,11 +583,11 @@ int sage_attn_debug_convert(int kind, const float* in, void* out, int64_t n, voi
 }
 
 // ---------------------------------------------------------------- W8A8 linear
-int sage_w8a8_sizes(const sage_w8a8_desc* desc, size_t* xq_bytes, size_t* x_scale_bytes, size_t* wq_bytes,
-                    size_t* w_scale_bytes) {
+sage_status sage_w8a8_sizes(const sage_w8a8_desc* desc, size_t* xq_bytes, size_t* x_scale_bytes,
+                            size_t* wq_bytes, size_t* w_scale_bytes) {
   try {
     sage::W8A8Launch L{};
-    const int s = w8a8_plan(desc, &L);
+    const sage_status s = w8a8_plan(desc, &L);
     if (s != SAGE_OK) return s;
     const size_t nkb = static_cast<size_t>(L.K) / SAGE_W8A8_GROUP;
     if (xq_bytes) *xq_bytes = static_cast<size_t>(L.M_pad) * L.K;
@@ -577,10 +600,10 @@ int sage_w8a8_sizes(const sage_w8a8_desc* desc, size_t* xq_bytes, size_t* x_scal
   }
 }
 
-int sage_w8a8_quantize_weight(const sage_w8a8_desc* desc, const void* w, int8_t* wq, float* w_scale, void* stream) {
+sage_status sage_w8a8_quantize_weight(const sage_w8a8_desc* desc, const void* w, int8_t* wq, float* w_scale, void* stream) {
   try {
     sage::W8A8Launch L{};
-    const int s = w8a8_plan(desc, &L);
+    const sage_status s = w8a8_plan(desc, &L);
     if (s != SAGE_OK) return s;
     if (!w || !wq || !w_scale) return fail(SAGE_E_NULL, "w, wq and w_scale must be non-NULL");
     if (!aligned16(w) || !aligned16(wq) || !aligned4(w_scale)) return fail(SAGE_E_ALIGN, "w, wq 16-byte and w_scale 4-byte aligned");
@@ -591,10 +614,10 @@ int sage_w8a8_quantize_weight(const sage_w8a8_desc* desc, const void* w, int8_t*
   }
 }
 
-int sage_w8a8_quantize_act(const sage_w8a8_desc* desc, const void* x, int8_t* xq, float* x_scale, void* stream) {
+sage_status sage_w8a8_quantize_act(const sage_w8a8_desc* desc, const void* x, int8_t* xq, float* x_scale, void* stream) {
   try {
     sage::W8A8Launch L{};
-    const int s = w8a8_plan(desc, &L);
+    const sage_status s = w8a8_plan(desc, &L);
     if (s != SAGE_OK) return s;
     if (!x || !xq || !x_scale) return fail(SAGE_E_NULL, "x, xq and x_scale must be non-NULL");
     if (!aligned16(x) || !aligned16(xq) || !aligned4(x_scale)) return fail(SAGE_E_ALIGN, "x, xq 16-byte and x_scale 4-byte aligned");
@@ -605,11 +628,11 @@ int sage_w8a8_quantize_act(const sage_w8a8_desc* desc, const void* x, int8_t* xq
   }
 }
 
-int sage_w8a8_gemm(const sage_w8a8_desc* desc, const int8_t* xq, const float* x_scale, const int8_t* wq,
+sage_status sage_w8a8_gemm(const sage_w8a8_desc* desc, const int8_t* xq, const float* x_scale, const int8_t* wq,
                    const float* w_scale, const void* bias, void* y, void* stream) {
   try {
     sage::W8A8Launch L{};
-    const int s = w8a8_plan(desc, &L);
+    const sage_status s = w8a8_plan(desc, &L);
     if (s != SAGE_OK) return s;
     if (!xq || !x_scale || !wq || !w_scale || !y) return fail(SAGE_E_NULL, "xq, x_scale, wq, w_scale and y must be non-NULL");
     if (!aligned16(xq) || !aligned16(wq) || !aligned16(y) || (bias && !aligned16(bias)) || !aligned4(x_scale) ||

@@ -60,9 +60,11 @@ constexpr int MASKED = static_cast<int>(0xFF800000u);
 // Score bias.  The S MFMAs start their integer accumulation from the inline
 // constant 1/(2 pi), whose float32 bits are SBIAS, so they return SBIAS + S.
 // For |S| < 2292099 (|S| <= 127^2 d here) those bits are exactly the float32
-// F0 + S 2^-26 (F0 = 1/(2 pi) rounded to float32), so the softmax reads the
-// score as a float without a conversion and forms S c - mref as
-// fma(F, c 2^26, fma(-F0, c 2^26, -mref)).
+// F = F0 + S 2^-26 (F0 = 1/(2 pi) rounded to float32), so the softmax reads
+// the score as a float without a conversion: F and F0 lie in [1/8, 1/4), so
+// F - F0 = S 2^-26 exactly (Sterbenz), and fma(F - F0, c 2^26, -mref) is
+// fp32(S c - mref) rounded once, as the scheme defines it.  (The row maximum
+// is taken on the integer bits, which order like S.)
 constexpr int SBIAS = 0x3E22F983;
 
 // a_row_key and k_swz (common.h) give the A operand's row order and the
@@ -243,16 +245,17 @@ struct WaveState {
     m = upd ? tm : m;
     const float nmref = -(m - static_cast<float>(SHIFT));
     // c 2^26, exact; a zero scale (all-zero Q or K block: every score 0)
-    // becomes the smallest normal float so that MASKED keys still give -inf
+    // becomes the smallest normal float, so that MASKED keys (F = -inf)
+    // still give -inf and the others x = -mref up to S 2^-126
     const float c2 = fmaxf(c, 1.17549435e-38f) * 67108864.0f;
-    const float kx = __builtin_fmaf(-__builtin_bit_cast(float, SBIAS), c2, nmref);
+    const float f0 = __builtin_bit_cast(float, SBIAS);
     float p0[16], p1[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       // (copy the element out first: a bit cast of a vector subscript reads element 0)
       const int b0 = s0[i], b1 = s1[i];
-      p0[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(__builtin_bit_cast(float, b0), c2, kx));
-      p1[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(__builtin_bit_cast(float, b1), c2, kx));
+      p0[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(__builtin_bit_cast(float, b0) - f0, c2, nmref));
+      p1[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(__builtin_bit_cast(float, b1) - f0, c2, nmref));
     }
     if constexpr (PV == PVFP8) {
 #pragma unroll
@@ -398,8 +401,9 @@ __global__ __launch_bounds__(PP ? 512 : 256, PP ? 1 : 2) void attn_fwd_kernel(At
   //    grid, cut at the end of the tile's last row; a row sees the prefix
   //    [0, re) of the keys;
   //  * frame cache: the chunks of the sink frames, then those of the window
-  //    frames through the last row's frame (up to its last token); a row sees
-  //    the valid slots of the frames of its window.
+  //    frames through the last row's frame (up to its last token), split on
+  //    the same list built for all the batch's rows; a row sees the valid
+  //    slots of the frames of its window.
   int re = 0, fq = 0, fq_lo = 0, fq_hi = 0, a0 = 0, b1 = 0, v_lo, v_hi, full_end = 0, n_full = 0;
   if constexpr (!CACHE) {
     re = F > 0 ? min(kv_len, ((q_pos0 + qi_valid) / F + 1) * F) : kv_len;
@@ -410,16 +414,17 @@ __global__ __launch_bounds__(PP ? 512 : 256, PP ? 1 : 2) void attn_fwd_kernel(At
     v_hi = min((split + 1) * nch / A.splits, (last_end + 63) / 64);
     full_end = first_end;  // chunks ending at or before it are visible in full to every row
     if constexpr (SPARSE) {
-      // The tile's list: the chunks among [0, ceil(last_end/64)) that the
-      // mask keeps, compacted in order into LDS by the whole workgroup
+      // The split covers the batch's chunks [v_lo, v_hi) as without a mask;
+      // the work item's list is the chunks among them that the mask keeps
+      // for this tile, compacted in order into LDS by the whole workgroup
       // (ballot + per-wave counts); `below` counts those visible in full to
-      // every row.  The split takes entries [v_lo, v_hi) of the list.
-      const int nbase = (last_end + 63) / 64, nfull = full_end / 64;
+      // every row.  List entries then run from 0.
+      const int nfull = full_end / 64;
       const uint8_t* mrow = A.block_mask + (static_cast<int64_t>(bh) * A.nqt + qt) * A.mask_nkc;
       int total = 0, below = 0;
-      for (int c0 = 0; c0 < nbase; c0 += 256) {
+      for (int c0 = v_lo; c0 < v_hi; c0 += 256) {
         const int c = c0 + tid;
-        const bool keep = c < nbase && mrow[c] != 0;
+        const bool keep = c < v_hi && mrow[c] != 0;
         const uint64_t bk = __ballot(keep), bf = __ballot(keep && c < nfull);
         if (lane == 0) {
           scnt[w] = __popcll(bk);
@@ -435,8 +440,8 @@ __global__ __launch_bounds__(PP ? 512 : 256, PP ? 1 : 2) void attn_fwd_kernel(At
         below += scnt[4] + scnt[5] + scnt[6] + scnt[7];
         __syncthreads();
       }
-      v_lo = split * total / A.splits;
-      v_hi = (split + 1) * total / A.splits;
+      v_lo = 0;
+      v_hi = total;
       n_full = below;
     }
   } else {
@@ -452,8 +457,26 @@ __global__ __launch_bounds__(PP ? 512 : 256, PP ? 1 : 2) void attn_fwd_kernel(At
       b1 = max(b1, a0);
       nv = a0 + (end_chunk - b1);
     }
-    v_lo = split * nv / A.splits;
-    v_hi = (split + 1) * nv / A.splits;
+    // The split cuts the batch's list -- the same construction over all its
+    // query rows -- into equal parts, so where it cuts does not depend on
+    // the tile; the item visits the entries of its own list that fall in
+    // its part: tile_count(V) = entries of the tile's list whose chunk lies
+    // before the chunk of batch entry V.
+    const int FQ_lo = q_pos0 / F, FQ_hi = (q_pos0 + A.Nq - 1) / F;
+    const int END = (FQ_hi * FS + min(F, kv_len - FQ_hi * F) + 63) / 64;
+    int A0 = 0, B1 = 0;
+    if (A.window_frames > 0) {
+      A0 = min(min(A.sink_frames, FQ_hi + 1) * cpf, END);
+      B1 = max(min(max(A.sink_frames, FQ_lo - A.window_frames) * cpf, END), A0);
+    }
+    const int NV = A0 + (END - B1);
+    auto tile_count = [&](int V) -> int {
+      if (V >= NV) return nv;
+      const int ch = V < A0 ? V : B1 + (V - A0);
+      return min(ch, a0) + max(0, min(ch, end_chunk) - b1);
+    };
+    v_lo = tile_count(split * NV / A.splits);
+    v_hi = tile_count((split + 1) * NV / A.splits);
   }
   const int J = max(0, v_hi - v_lo);  // chunks of this work item
   // list entries below this one are visible in full to every row of the tile

@@ -19,11 +19,6 @@ constexpr int KMEAN_CHUNK = 128; // tokens per first-level partial sum of the K 
 constexpr float TAU = 4.0f;      // lazy running-max threshold (log2 units)
 constexpr int PSHIFT_FP8 = 4;    // P stored as e4m3(p * 2^4) in FP8 mode
 constexpr int PSHIFT_16 = 0;
-// Query rows of one work item of the fused kernel when the keys are a frame
-// cache (and likewise contiguous keys): its KV splits cut the chunk list of
-// this many rows, so the split boundaries, and with them the rounding, depend
-// on it.
-constexpr int CACHE_TILE = 2 * BQ;
 constexpr int NPAD = 128;        // Nq and Nkv are padded to multiples of this
 constexpr int MAXB = 256;        // largest batch handled through kernel arguments
 

@@ -228,7 +228,7 @@ __global__ __launch_bounds__(256) void quant_i8_kernel(
 // One workgroup per 64-key chunk of one (b, h); 2*D threads.  Writes the chunk
 // channel-major ([D][64]) so that each lane of the P.V matrix-core operand
 // reads its keys contiguously.  FP8 mode: one E8M0 scale per (32-key block,
-// channel) -- the smallest power of two 2^e with amax * 2^-e <= 448 -- and
+// channel) -- the smallest power of two 2^e >= 2^-127 with amax * 2^-e <= 448 -- and
 // e4m3fn codes of v * 2^-e; the scales of a chunk are stored as 64 lanes x 4
 // bytes (lane 32*k + r holds channels r, r+32, r+64, r+96 of key block k).
 template <typename T, int D, bool FP8>
@@ -279,7 +279,9 @@ __global__ __launch_bounds__(2 * D) void prep_v_kernel(
     if (amax > 0.f) {
       int k2;
       const float m = frexpf(amax, &k2);
-      e = (m <= 0.875f) ? k2 - 9 : k2 - 8;
+      // floored at the smallest E8M0 scale 2^-127 (byte 0): a block below
+      // 448 * 2^-127 keeps it, and its values round to e4m3 at that scale
+      e = max((m <= 0.875f) ? k2 - 9 : k2 - 8, -127);
     }
     const float sc = ldexpf(1.0f, -e);
     uint32_t w[8];
@@ -305,7 +307,9 @@ __global__ void convert_kernel(const float* __restrict__ in, void* __restrict__ 
   if (k >= n) return;
   float f[4];
   for (int t = 0; t < 4; ++t) f[t] = (k + t < n) ? in[k + t] : 0.f;
-  if (KIND == 0) {
+  if (KIND == 3) {  // 2^x as the softmax evaluates it (the hardware exponential)
+    for (int t = 0; t < 4 && k + t < n; ++t) static_cast<float*>(out)[k + t] = __builtin_amdgcn_exp2f(f[t]);
+  } else if (KIND == 0) {
     const uint32_t w = pack_e4m3x4(f[0], f[1], f[2], f[3]);
     for (int t = 0; t < 4 && k + t < n; ++t) static_cast<uint8_t*>(out)[k + t] = (w >> (8 * t)) & 0xFF;
   } else {
@@ -372,7 +376,8 @@ hipError_t launch_convert(int kind, const float* in, void* out, int64_t n, hipSt
   const dim3 grid(static_cast<unsigned>((threads + 255) / 256));
   if (kind == 0) hipLaunchKernelGGL(convert_kernel<0>, grid, dim3(256), 0, st, in, out, n);
   else if (kind == 1) hipLaunchKernelGGL(convert_kernel<1>, grid, dim3(256), 0, st, in, out, n);
-  else hipLaunchKernelGGL(convert_kernel<2>, grid, dim3(256), 0, st, in, out, n);
+  else if (kind == 2) hipLaunchKernelGGL(convert_kernel<2>, grid, dim3(256), 0, st, in, out, n);
+  else hipLaunchKernelGGL(convert_kernel<3>, grid, dim3(256), 0, st, in, out, n);
   return hipGetLastError();
 }
 

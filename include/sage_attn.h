@@ -84,7 +84,7 @@
 extern "C" {
 #endif
 
-#define SAGE_ATTN_ABI_VERSION 3
+#define SAGE_ATTN_ABI_VERSION 4
 
 typedef enum {
   SAGE_OK = 0,
@@ -156,46 +156,58 @@ typedef struct sage_quant_bufs {
                           32cb + r of keys [32k, 32k+32); else NULL           */
   void *stats;         /* internal: partial statistics of the quantize pass   */
   void *partial;       /* internal: split-KV partial results                  */
+  int32_t partial_splits; /* KV splits `partial` holds room for (set by
+                          sage_attn_quant_layout): a call whose split count
+                          exceeds it fails with SAGE_E_WORKSPACE            */
+  int32_t reserved;    /* 0                                                   */
 } sage_quant_bufs;
 
 /* Version of the library's ABI (SAGE_ATTN_ABI_VERSION it was built with). */
 int sage_attn_abi_version(void);
 
 /* Static description of a status code. */
-const char *sage_attn_status_string(int status);
+const char *sage_attn_status_string(sage_status status);
 
-/* Thread-local text of the last error reported by this thread. */
+/* Thread-local text of the last failure reported by this thread: the
+ * validation message, or for SAGE_E_HIP the HIP runtime's error string. */
 const char *sage_attn_last_error(void);
 
 /* Value of a named scheme constant ("BQ", "BK", "VB", "QMAX", "TAU",
  * "PSHIFT_FP8", "PSHIFT_16", "KMEAN_CHUNK"), for cross-checks.
  * Returns SAGE_E_UNSUPPORTED for an unknown name. */
-int sage_attn_constant(const char *name, double *value);
+sage_status sage_attn_constant(const char *name, double *value);
 
 /* Number of KV splits the library will use for *desc (kv_splits, or its own
- * choice when kv_splits == 0).  Contiguous keys: split s of batch b covers the
- * 64-key chunks [s*n/S, (s+1)*n/S) with n = ceil(kv_len[b]/64).  Frame cache:
- * each 128-query tile visits the cache chunks of its sink frames, then of its
- * window frames through its last query's frame (up to the last token), n of
- * them in that order, and split s takes entries [s*n/S, (s+1)*n/S) of that
- * list.  Partial results are merged exactly as the online softmax would. */
-int sage_attn_kv_splits(const sage_attn_desc *desc, int32_t *splits);
+ * choice when kv_splits == 0).  Each batch's key chunks form one ordered
+ * list, the same for every query tile of the batch, and split s takes
+ * entries [s*n/S, (s+1)*n/S) of it (n entries; a tile visits the entries of
+ * its part that its rows can see).  Contiguous keys, with or without a
+ * block mask: the 64-key chunks [0, ceil(kv_len[b]/64)).  Frame cache: the
+ * cache chunks that some query row of the batch sees -- those of the sink
+ * frames, then those of the window frames from the first query's window
+ * start through the last query's frame (up to its last token).  Partial
+ * results are merged exactly as the online softmax would. */
+sage_status sage_attn_kv_splits(const sage_attn_desc *desc, int32_t *splits);
 
-/* Bytes of workspace sage_attn_fwd needs for *desc (validated first). */
-int sage_attn_workspace_size(const sage_attn_desc *desc, size_t *bytes);
+/* Bytes of workspace sage_attn_fwd needs for *desc (validated first).  The
+ * split-KV region has room for the larger of the split count for *desc and
+ * the one for the same desc with every batch at its full key length, so a
+ * frame cache carved once keeps working while kv_len grows. */
+sage_status sage_attn_workspace_bytes(const sage_attn_desc *desc, size_t *bytes);
 
 /* Carve the quantized-operand buffers out of a workspace of ws_bytes bytes
- * (256-byte aligned sub-buffers).  Host-only: enqueues nothing. */
-int sage_attn_quant_layout(const sage_attn_desc *desc, void *ws, size_t ws_bytes,
-                           sage_quant_bufs *out);
+ * (256-byte aligned sub-buffers) and record the split capacity in
+ * out->partial_splits.  Host-only: enqueues nothing. */
+sage_status sage_attn_quant_layout(const sage_attn_desc *desc, void *ws, size_t ws_bytes,
+                                   sage_quant_bufs *out);
 
 /* Quantize: K mean (unless k_mean_in), channel balance (unless
  * chan_shift_in), INT8 Q and K codes and scales, V prepared for P.V
  * (transposed; FP8 codes and E8M0 scales in FP8 mode).  q, k, v: device
  * inputs as described by desc (with a frame cache, k and v hold the kv_len
  * tokens contiguously; they are written into the cache slots). */
-int sage_attn_quantize(const sage_attn_desc *desc, const void *q, const void *k,
-                       const void *v, const sage_quant_bufs *bufs, void *stream);
+sage_status sage_attn_quantize(const sage_attn_desc *desc, const void *q, const void *k,
+                               const void *v, const sage_quant_bufs *bufs, void *stream);
 
 /* Frame cache only (frame_stride > 0): quantize once, against the K mean and
  * channel-balance exponents already in bufs (left there by sage_attn_quantize
@@ -205,9 +217,9 @@ int sage_attn_quantize(const sage_attn_desc *desc, const void *q, const void *k,
  * the queries q (as described by desc) with the same exponents.  Codes and
  * scales of all other frames are left untouched.  Errors: SAGE_E_UNSUPPORTED
  * without a frame cache; SAGE_E_SHAPE if the frames do not fit in Nkv slots. */
-int sage_attn_quantize_frames(const sage_attn_desc *desc, const void *q, const void *k,
-                              const void *v, int32_t frame0, int32_t nframes,
-                              const sage_quant_bufs *bufs, void *stream);
+sage_status sage_attn_quantize_frames(const sage_attn_desc *desc, const void *q, const void *k,
+                                      const void *v, int32_t frame0, int32_t nframes,
+                                      const sage_quant_bufs *bufs, void *stream);
 
 /* As sage_attn_quantize_frames, with each batch appending at its own place:
  * batch b's nframes new frames (rows [0, nframes*frame_len) of its k, v) go to
@@ -217,34 +229,38 @@ int sage_attn_quantize_frames(const sage_attn_desc *desc, const void *q, const v
  * array [B], read during the call.  Errors as sage_attn_quantize_frames;
  * SAGE_E_NULL if frame0 is NULL; SAGE_E_SHAPE if some batch's frames do not
  * fit in Nkv slots. */
-int sage_attn_quantize_frames_batched(const sage_attn_desc *desc, const void *q, const void *k,
-                                      const void *v, const int32_t *frame0, int32_t nframes,
-                                      const sage_quant_bufs *bufs, void *stream);
+sage_status sage_attn_quantize_frames_batched(const sage_attn_desc *desc, const void *q,
+                                              const void *k, const void *v, const int32_t *frame0,
+                                              int32_t nframes, const sage_quant_bufs *bufs,
+                                              void *stream);
 
-/* Fused attention on already-quantized operands: writes O [B,H,Nq,d]. */
-int sage_attn_fwd_quantized(const sage_attn_desc *desc, const sage_quant_bufs *bufs,
-                            void *o, void *stream);
+/* Fused attention on already-quantized operands: writes O [B,H,Nq,d].
+ * Errors: SAGE_E_WORKSPACE if the call needs more KV splits than
+ * bufs->partial_splits (a workspace carved for another desc). */
+sage_status sage_attn_fwd_quantized(const sage_attn_desc *desc, const sage_quant_bufs *bufs,
+                                    void *o, void *stream);
 
 /* Drop-in call: quantize into the workspace, then attend.  Equivalent to
  * sage_attn_quant_layout + sage_attn_quantize + sage_attn_fwd_quantized. */
-int sage_attn_fwd(const sage_attn_desc *desc, const void *q, const void *k,
-                  const void *v, void *o, void *ws, size_t ws_bytes, void *stream);
+sage_status sage_attn_fwd(const sage_attn_desc *desc, const void *q, const void *k,
+                          const void *v, void *o, void *ws, size_t ws_bytes, void *stream);
 
 /* Test support: exact int32 scores S = qcodes . kcodes^T of ntiles tiles of
  * 32 queries x 64 keys, computed by the same matrix-core routine as the fused
  * kernel.  tiles: host [ntiles][3] = {b*H + h, q0 (multiple of 32),
  * k0 (multiple of 64)} within the padded sizes; out: device [ntiles][32][64]
  * int32, row = query q0+r, column = key k0+c. */
-int sage_attn_debug_scores(const sage_attn_desc *desc, const sage_quant_bufs *bufs,
-                           const int32_t *tiles, int32_t ntiles, int32_t *out,
-                           void *stream);
+sage_status sage_attn_debug_scores_i32(const sage_attn_desc *desc, const sage_quant_bufs *bufs,
+                                      const int32_t *tiles, int32_t ntiles, int32_t *out,
+                                      void *stream);
 
-/* Test support: convert n float32 values with the kernels' own conversion
+/* Test support: apply to n float32 values the kernels' own conversion
  * routines.  kind 0: e4m3fn bytes (as P is converted in FP8 mode);
- * 1: bf16 bits; 2: fp16 bits (uint16).  Inputs for kind 0 must satisfy
+ * 1: bf16 bits; 2: fp16 bits (uint16); 3: float32 2^x by the same hardware
+ * exponential the softmax uses.  Inputs for kind 0 must satisfy
  * |x| <= 448. */
-int sage_attn_debug_convert(int kind, const float *in, void *out, int64_t n,
-                            void *stream);
+sage_status sage_attn_debug_convert(int kind, const float *in, void *out, int64_t n,
+                                    void *stream);
 
 #ifdef __cplusplus
 }

@@ -52,22 +52,22 @@ typedef struct sage_w8a8_desc {
  * and x_scale [K/128][M_pad] float32 (block-major: one row per channel
  * group), and of the quantized weights: wq [N][K] int8 and w_scale
  * [N/128][K/128] float32.  Any pointer may be NULL. */
-int sage_w8a8_sizes(const sage_w8a8_desc *desc, size_t *xq_bytes, size_t *x_scale_bytes,
+sage_status sage_w8a8_sizes(const sage_w8a8_desc *desc, size_t *xq_bytes, size_t *x_scale_bytes,
                     size_t *wq_bytes, size_t *w_scale_bytes);
 
 /* Quantize the weights W [N,K] (device, 16-bit, row stride w_stride) into wq
  * and w_scale (device).  Done once per layer. */
-int sage_w8a8_quantize_weight(const sage_w8a8_desc *desc, const void *w, int8_t *wq,
+sage_status sage_w8a8_quantize_weight(const sage_w8a8_desc *desc, const void *w, int8_t *wq,
                               float *w_scale, void *stream);
 
 /* Quantize the activations X [M,K] (device, 16-bit, row stride x_stride) into
  * xq and x_scale (device). */
-int sage_w8a8_quantize_act(const sage_w8a8_desc *desc, const void *x, int8_t *xq,
+sage_status sage_w8a8_quantize_act(const sage_w8a8_desc *desc, const void *x, int8_t *xq,
                            float *x_scale, void *stream);
 
 /* Y [M,N] (device, 16-bit, row stride y_stride) = dequantized xq wq^T + bias.
  * bias: device [N] 16-bit, or NULL.  xq, wq, y and bias 16-byte aligned. */
-int sage_w8a8_gemm(const sage_w8a8_desc *desc, const int8_t *xq, const float *x_scale,
+sage_status sage_w8a8_gemm(const sage_w8a8_desc *desc, const int8_t *xq, const float *x_scale,
                    const int8_t *wq, const float *w_scale, const void *bias, void *y,
                    void *stream);
 

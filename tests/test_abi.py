@@ -36,7 +36,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for must in ("sage_attn_quantize", "sage_attn_fwd", "sage_attn_fwd_quantized",
-                 "sage_attn_workspace_size", "sage_attn_quant_layout", "sage_attn_debug_scores",
+                 "sage_attn_workspace_bytes", "sage_attn_quant_layout", "sage_attn_debug_scores_i32",
                  "sage_attn_quantize_frames", "sage_attn_quantize_frames_batched",
                  "sage_w8a8_quantize_weight", "sage_w8a8_quantize_act",
                  "sage_w8a8_gemm", "sage_w8a8_sizes"):
@@ -71,7 +71,7 @@ def _desc(**kw):
 
 def _status(desc):
     n = ctypes.c_size_t()
-    return sage.load().sage_attn_workspace_size(desc.ptr, ctypes.byref(n)), n.value
+    return sage.load().sage_attn_workspace_bytes(desc.ptr, ctypes.byref(n)), n.value
 
 
 def test_valid_desc_and_workspace(lib):
@@ -154,7 +154,7 @@ def test_frame_cache_desc_and_quantize_frames_validation(lib):
     d.c.reserved = 3
     assert _status(d)[0] == 7
     # argument checks of sage_attn_quantize_frames (host-only; nothing enqueued)
-    n = sage.sage_attn_workspace_size(ok)
+    n = sage.sage_attn_workspace_bytes(ok)
     ws = (ctypes.c_uint8 * (n + 256))()
     base = (ctypes.addressof(ws) + 255) // 256 * 256
     bufs = sage.sage_quant_bufs()
@@ -164,7 +164,7 @@ def test_frame_cache_desc_and_quantize_frames_validation(lib):
     assert st == 2 and b"inside" in lib.sage_attn_last_error()
     assert lib.sage_attn_quantize_frames(ok.ptr, None, fake, fake, -1, 1, ctypes.byref(bufs), None) == 2
     plain = _desc()
-    n2 = sage.sage_attn_workspace_size(plain)
+    n2 = sage.sage_attn_workspace_bytes(plain)
     ws2 = (ctypes.c_uint8 * (n2 + 256))()
     base2 = (ctypes.addressof(ws2) + 255) // 256 * 256
     bufs2 = sage.sage_quant_bufs()
@@ -176,7 +176,7 @@ def test_frame_cache_desc_and_quantize_frames_validation(lib):
 def test_quantize_frames_batched_validation(lib):
     d = _desc(B=2, frame_len=50, frame_stride=64, Nkv=320, Nq=50, kv_len=[250, 150])
     assert _status(d)[0] == 0
-    n = sage.sage_attn_workspace_size(d)
+    n = sage.sage_attn_workspace_bytes(d)
     ws = (ctypes.c_uint8 * (n + 256))()
     base = (ctypes.addressof(ws) + 255) // 256 * 256
     bufs = sage.sage_quant_bufs()
@@ -190,7 +190,7 @@ def test_quantize_frames_batched_validation(lib):
     assert qfb(d.ptr, None, fake, fake, arr(0, -1), 1, ctypes.byref(bufs), None) == 2
     assert qfb(d.ptr, None, fake, fake, arr(0, 0), 0, ctypes.byref(bufs), None) == 2
     plain = _desc(B=2)
-    n2 = sage.sage_attn_workspace_size(plain)
+    n2 = sage.sage_attn_workspace_bytes(plain)
     ws2 = (ctypes.c_uint8 * (n2 + 256))()
     base2 = (ctypes.addressof(ws2) + 255) // 256 * 256
     bufs2 = sage.sage_quant_bufs()
@@ -255,3 +255,44 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     monkeypatch.setattr(sage, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         sage.load(str(tmp_path / "libsage_attn.so"))
+
+
+def test_split_capacity_covers_a_growing_frame_cache(lib):
+    """A frame cache's workspace is carved once, while its kv_len grows step
+    by step and the library's split count with it (B1 H1, 2040-token frames
+    in 2048-slot strides, 1 -> 5 frames).  The carved partial region holds
+    room for every later step; a call that needs more splits than were
+    carved fails with SAGE_E_WORKSPACE before anything is enqueued (host
+    validation only: the pointers below are never dereferenced)."""
+    F, FS, nf = 2040, 2048, 5
+
+    def desc(frames, **kw):
+        return sage.Desc(1, 1, F, nf * FS, 128, sage.SAGE_BF16, frame_len=F, frame_stride=FS,
+                         kv_len=[frames * F], **kw)
+
+    L = sage.load()
+    fake = 1 << 32
+    first = desc(1)
+    bufs = sage.sage_quant_bufs()
+    n = sage.sage_attn_workspace_bytes(first)
+    assert L.sage_attn_quant_layout(first.ptr, ctypes.c_void_p(fake), n, ctypes.byref(bufs)) == 0
+    seen = [sage.sage_attn_kv_splits(desc(f)) for f in range(1, nf + 1)]
+    assert len(set(seen)) > 1                        # the split count does grow with the cache
+    assert max(seen) <= bufs.partial_splits
+    part_end = bufs.partial + bufs.partial_splits * 1 * 1 * 2048 * (128 + 2) * 4
+    assert part_end <= fake + n                      # and the region really is that large
+    # carved for 2 forced splits, called with 16: rejected on the host
+    small = desc(1, kv_splits=2)
+    n2 = sage.sage_attn_workspace_bytes(small)
+    b2 = sage.sage_quant_bufs()
+    assert L.sage_attn_quant_layout(small.ptr, ctypes.c_void_p(fake), n2, ctypes.byref(b2)) == 0
+    assert b2.partial_splits == 2
+    big = desc(5, kv_splits=16)
+    st = L.sage_attn_fwd_quantized(big.ptr, ctypes.byref(b2), ctypes.c_void_p(fake), None)
+    assert st == 8 and b"16 KV splits" in L.sage_attn_last_error()
+    # one split needs no partial region at all
+    one = desc(1, kv_splits=1)
+    b1 = sage.sage_quant_bufs()
+    assert L.sage_attn_quant_layout(one.ptr, ctypes.c_void_p(fake), sage.sage_attn_workspace_bytes(one),
+                                    ctypes.byref(b1)) == 0
+    assert b1.partial is None and b1.partial_splits == 1

@@ -6,8 +6,9 @@ recent history frames and the current frame -- over cached history (Vidu S1
 blog, section "Infra").  Bit-exact: every quantized operand in its cache
 slots, and appending frames one at a time against the same frozen mean and
 exponents gives the same buffers as quantizing the whole cache.  Outputs:
-within the output-rounding bar of the oracle's emulation run with the
-kernel's per-tile chunk lists and splits, cosine against float64 windowed
+every element within the derived bound of gpu_util of the oracle's
+emulation with the same KV splits (each batch's chunk list cut into the
+library's split count), cosine >= 0.999 against float64 windowed
 attention."""
 
 import numpy as np
@@ -18,7 +19,7 @@ import bit_quantized_attention_sage_amd as sage
 import workloads
 from oracle import quant, emulate, attention, codecs
 from oracle.constants import PV_16, PV_FP8, BK
-from gpu_util import host, compare_output, cosine, NAME_DT
+from gpu_util import host, assert_close, cosine, NAME_DT, KERNEL_SLACK
 
 pytestmark = pytest.mark.gpu
 
@@ -58,8 +59,11 @@ def _run(q, k, v, pv_mode, F, FS, nslots, S=0, W=0, kv_len=None, q_pos0=None, sp
     return o, desc, ws, bufs
 
 
-def emulate_cache(Q, K, V, pv_mode, dtype, F, FS, S, W, kv_len, q_pos0, mu, a, nsplit):
-    return emulate.emulate_frame_cache(Q, K, V, pv_mode, dtype, F, FS, S, W, kv_len, q_pos0, mu, a, nsplit)
+def emulate_cache(Q, K, V, pv_mode, dtype, F, FS, S, W, kv_len, q_pos0, mu, a, nsplit, rows=None):
+    """(O64, aux) of the frame-cache emulation with the kernel's slack."""
+    o64, _, aux = emulate.emulate_frame_cache(Q, K, V, pv_mode, dtype, F, FS, S, W, kv_len, q_pos0, mu, a,
+                                              nsplit, rows=rows, slack=KERNEL_SLACK)
+    return o64, aux
 
 
 def check_cache_operands(views, Q, K, V, mu, a, F, FS, pv_mode):
@@ -192,22 +196,15 @@ def test_window_parity(lib, case, pv_mode):
     o, desc, _, _ = _run(q.cuda(), k.cuda(), v.cuda(), pv_mode, F, FS, nf * FS, S, W, kv_len, q_pos0,
                          splits, mu, a)
     nsplit = sage.sage_attn_kv_splits(desc)
-    o64 = emulate_cache(Q, K, V, pv_mode, NAME_DT[dt], F, FS, S, W, kv_len, q_pos0, mu, a, nsplit)
-    o_abs = emulate_cache(Q, K, np.abs(V), pv_mode, NAME_DT[dt], F, FS, S, W, kv_len, q_pos0, mu, a, nsplit) \
-        if pv_mode == PV_FP8 else None
+    o64, aux = emulate_cache(Q, K, V, pv_mode, NAME_DT[dt], F, FS, S, W, kv_len, q_pos0, mu, a, nsplit)
     og = host(o)
-    mx, excess, frac, rel, rel_bound = compare_output(og, o64, NAME_DT[dt], pv_mode, o_abs)
-    print(f"  splits {nsplit} max-abs {mx:.3e} excess {excess:.2e} beyond-rounding {frac:.2e} rel-L2 {rel:.3e}")
-    assert excess <= 0
-    # fp16's output spacing is 8x finer than bf16's, so float32 accumulation
-    # differences cross its rounding boundaries more often
-    assert frac <= ((1e-3 if dt == torch.float16 else 1e-4) if pv_mode == PV_16 else 2e-2)
-    assert rel <= rel_bound
+    print(f"  splits {nsplit}")
+    assert_close(og, o64, aux, NAME_DT[dt], pv_mode, nsplit)
     ref = attention.attention_fp64(Q, K, V, frame_len=F, kv_len=kv_len, q_pos0=q_pos0, sink_frames=S,
                                    window_frames=W)
     cs = cosine(og, ref)
-    print(f"  cosine vs fp64 windowed attention {cs:.6f}")
-    assert cs >= (0.999 if pv_mode == PV_16 else 0.998)
+    print(f"  cosine vs fp64 windowed attention {cs:.6f} (emulation {cosine(o64, ref):.6f})")
+    assert cs >= 0.999
 
 
 @pytest.mark.parametrize("splits", [0, 3])
@@ -225,19 +222,16 @@ def test_window_ragged_batches(lib, pv_mode, splits):
     o, desc, _, _ = _run(q.cuda(), k.cuda(), v.cuda(), pv_mode, F, FS, nf * FS, S, W, kv_len, q_pos0,
                          splits, mu, a)
     nsplit = sage.sage_attn_kv_splits(desc)
-    o64 = emulate_cache(Q, K, V, pv_mode, "bf16", F, FS, S, W, kv_len, q_pos0, mu, a, nsplit)
-    o_abs = emulate_cache(Q, K, np.abs(V), pv_mode, "bf16", F, FS, S, W, kv_len, q_pos0, mu, a, nsplit) \
-        if pv_mode == PV_FP8 else None
+    o64, aux = emulate_cache(Q, K, V, pv_mode, "bf16", F, FS, S, W, kv_len, q_pos0, mu, a, nsplit)
     og = host(o)
-    mx, excess, frac, rel, rel_bound = compare_output(og, o64, "bf16", pv_mode, o_abs)
-    print(f"  splits {nsplit} max-abs {mx:.3e} excess {excess:.2e} beyond-rounding {frac:.2e} rel-L2 {rel:.3e}")
+    print(f"  splits {nsplit}")
     assert np.isfinite(og).all()
-    assert excess <= 0
-    assert frac <= (1e-4 if pv_mode == PV_16 else 2e-2)
-    assert rel <= rel_bound
+    assert_close(og, o64, aux, "bf16", pv_mode, nsplit)
     ref = attention.attention_fp64(Q, K, V, frame_len=F, kv_len=kv_len, q_pos0=q_pos0, sink_frames=S,
                                    window_frames=W)
-    assert cosine(og, ref) >= (0.999 if pv_mode == PV_16 else 0.998)
+    cs = cosine(og, ref)
+    print(f"  cosine vs fp64 windowed attention {cs:.6f} (emulation {cosine(o64, ref):.6f})")
+    assert cs >= 0.999
 
 
 @pytest.mark.parametrize("pv_mode", [PV_16, PV_FP8])
@@ -303,17 +297,13 @@ def test_window_workload_parity(lib, pv_mode):
     rows = workloads.sample_rows(w, 96)
     nsplit = sage.sage_attn_kv_splits(desc)
     Qh, Kh, Vh = Q[:, hs], K[:, hs], V[:, hs]
-    args = (pv_mode, w.dtype, F, FS, S, W, kvl, qp, mu[:, hs], a[:, hs], nsplit)
-    o64 = emulate.emulate_frame_cache(Qh, Kh, Vh, *args, rows=rows)
-    o_abs = emulate.emulate_frame_cache(Qh, Kh, np.abs(Vh), *args, rows=rows) if pv_mode == PV_FP8 else None
+    o64, aux = emulate_cache(Qh, Kh, Vh, pv_mode, w.dtype, F, FS, S, W, kvl, qp, mu[:, hs], a[:, hs], nsplit,
+                             rows=rows)
     og = host(o[:, hs])[:, :, rows]
-    mx, excess, frac, rel, rel_bound = compare_output(og, o64, w.dtype, pv_mode, o_abs)
-    print(f"  heads {hs} splits {nsplit}: max-abs {mx:.2e} excess {excess:.2e} beyond-rounding {frac:.2e} "
-          f"rel-L2 {rel:.2e}", flush=True)
-    assert excess <= 0
-    assert rel <= rel_bound
+    print(f"  heads {hs} splits {nsplit}:", flush=True)
+    assert_close(og, o64, aux, w.dtype, pv_mode, nsplit, max_abs=2e-3)
     ref = attention.attention_fp64(Qh, Kh, Vh, frame_len=F, kv_len=kvl, q_pos0=qp, rows=rows,
                                    sink_frames=S, window_frames=W)
     cs = cosine(og, ref)
     print(f"  cosine vs fp64 windowed attention {cs:.6f}", flush=True)
-    assert cs >= (0.999 if pv_mode == PV_16 else 0.998)
+    assert cs >= 0.999

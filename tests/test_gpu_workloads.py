@@ -5,9 +5,10 @@ configuration bench.py times (library-chosen KV splits).
   layout or FP8 codes and E8M0 scales) is compared bit-exactly with the oracle
   on the FULL tensors, one batch at a time.
 * Outputs are compared on sampled rows (the oracle computes them one by one):
-  within max(2e-3, half an output-type spacing) of the emulation with the same
-  KV splits, and cosine >= 0.999 against float64 attention over the sample
-  for the P.V mode each workload is reported with.
+  every element within the derived bound of gpu_util of the emulation with
+  the same KV splits, max-abs <= 2e-3 against it, and cosine >= 0.999
+  against float64 attention over the sample, for the P.V mode each workload
+  is reported with and for the other mode where the scheme reaches 0.999.
 """
 
 import numpy as np
@@ -18,18 +19,33 @@ import bit_quantized_attention_sage_amd as sage
 import workloads
 from oracle import attention
 from oracle.constants import PV_FP8
-from gpu_util import (host, check_quantized, emulate_like_gpu, compare_output, cosine, split_ranges)
+from gpu_util import host, check_quantized, assert_close, cosine, KERNEL_SLACK
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
-# (workload, number of heads sampled for outputs (seeded choice), rows per head)
-CASES = [("tiny", None, None), ("small", 3, 96), ("large", 6, 48), ("stream", 3, 96), ("batched", 2, 48)]
+# (workload, P.V mode (None: the workload's own), heads sampled for outputs
+# (seeded choice), rows per head)
+LARGE_FP8_REASON = ("FP8 P.V on the large workload misses cosine 0.999 by the scheme itself: the "
+                    "emulation reaches 0.99865 on 40 heads x 32 rows (kernel 0.99794 on its outlier "
+                    "heads 0-1); INT8 scores of the 24 outlier-channel heads cost 7.5e-4 of 1 - cos and "
+                    "e4m3 P and V another 7e-4 (accuracy decomposition in the design notes)")
+CASES = [("tiny", None, None, None), ("tiny", 1, None, None), ("small", None, 3, 96), ("small", 1, 2, 64),
+         ("large", None, 6, 48),
+         pytest.param("large", 1, 4, 48, marks=pytest.mark.skip(reason=LARGE_FP8_REASON)),
+         ("stream", None, 3, 96), ("stream", 1, 2, 64), ("batched", None, 2, 48)]
 
 
-@pytest.mark.parametrize("name,heads,R", CASES, ids=[c[0] for c in CASES])
-def test_workload_parity(lib, name, heads, R):
+def _cid(c):
+    c = c.values if hasattr(c, "values") else c
+    return c[0] + ("" if c[1] is None else "-pvfp8")
+
+
+@pytest.mark.parametrize("name,pv,heads,R", CASES, ids=[_cid(c) for c in CASES])
+def test_workload_parity(lib, name, pv, heads, R):
     w = workloads.get(name)
-    print(f"workload {name}", flush=True)
+    if pv is not None:
+        w.pv_mode = pv
+    print(f"workload {name} pv_mode {w.pv_mode}", flush=True)
     x = workloads.make(w, "cuda")
     q, k, v = x["q"], x["k"], x["v"]
     o = torch.empty_like(q)
@@ -56,15 +72,11 @@ def test_workload_parity(lib, name, heads, R):
         if name == "batched" and b not in (0, w.B - 1):
             continue
         Qh, Kh, Vh = Q[:, hs], K[:, hs], V[:, hs]
-        o64, _ = _emulate(Qh, Kh, Vh, w, kvl[b], qp[b], rows, S)
-        o_abs = _emulate(Qh, Kh, np.abs(Vh), w, kvl[b], qp[b], rows, S)[0] if w.pv_mode == PV_FP8 else None
+        o64, aux = _emulate(Qh, Kh, Vh, w, kvl[b], qp[b], rows, S)
         og = host(o[b:b + 1, hs])
         og = og if rows is None else og[:, :, rows]
-        mx, excess, frac, rel, rel_bound = compare_output(og, o64, w.dtype, w.pv_mode, o_abs)
-        print(f"  b{b} heads {hs}: max-abs {mx:.2e} excess {excess:.2e} beyond-rounding {frac:.2e} "
-              f"rel-L2 {rel:.2e}", flush=True)
-        assert excess <= 0
-        assert rel <= rel_bound
+        print(f"  b{b} heads {hs}:", flush=True)
+        assert_close(og, o64, aux, w.dtype, w.pv_mode, S, max_abs=2e-3)
         ref = attention.attention_fp64(Qh, Kh, Vh, frame_len=w.frame_len, kv_len=[kvl[b]],
                                        q_pos0=[qp[b]], rows=rows)
         num += float((og.astype(np.float64) * ref).sum())
@@ -78,6 +90,7 @@ def test_workload_parity(lib, name, heads, R):
 
 def _emulate(Q, K, V, w, kv_b, qp_b, rows, S):
     from oracle import emulate
-    splits = split_ranges(kv_b, S) if S > 1 else None
-    return emulate.emulate_from_inputs(Q, K, V, w.pv_mode, w.dtype, frame_len=w.frame_len, kv_len=[kv_b],
-                                       q_pos0=[qp_b], rows=rows, splits=splits)
+    o64, _, aux = emulate.emulate_from_inputs(Q, K, V, w.pv_mode, w.dtype, frame_len=w.frame_len,
+                                              kv_len=[kv_b], q_pos0=[qp_b], rows=rows,
+                                              splits=emulate.split_ranges(kv_b, S), slack=KERNEL_SLACK)
+    return o64, aux

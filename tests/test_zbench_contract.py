@@ -39,8 +39,14 @@ def test_bench_json_line(lib, capsys, monkeypatch):
     # TOPS over the step time: 4 d (visible pairs) per step (both fields are rounded)
     assert abs(r["value"] - r["config"]["ops_per_step"] / (r["ms_per_step"] * 1e-3) / 1e12) <= 1e-2 * r["value"]
     rf = r["roofline"]
-    assert rf["bound"] == "mfma" and rf["unit"] == "TFLOP/s" and rf["peak"] == 5000.0
+    assert rf["bound"] == "mfma" and rf["unit"] == "TOPS" and rf["peak"] == 5000.0
     assert rf["achieved"] > 0 and abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3
+    # the P.V mode's own ceiling: 1 / (0.5 / 5000 + 0.5 / 2500) for 16-bit P.V
+    assert abs(rf["mode_peak"] - 10000 / 3) < 0.1 and abs(rf["mode_frac"] - rf["achieved"] / rf["mode_peak"]) < 1e-3
+    qz = r["quantize"]
+    assert qz["algorithmic_bytes"] <= qz["design_bytes"]
+    # the other P.V mode, with its accuracy and whether it meets both bars
+    assert r["other_pv_mode"]["pv"] == "fp8" and isinstance(r["other_pv_mode"]["meets_bar"], bool)
     assert rf["traffic"] is None or rf["traffic"] > 0
     cb = r["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]
@@ -48,3 +54,19 @@ def test_bench_json_line(lib, capsys, monkeypatch):
     # the float64 reference timed on its own; the whole workload extrapolated from the sample
     assert cb["fp64_reference"]["s"] > 0 and cb["fp64_reference"]["TOPS"] > 0
     assert cb["extrapolated_full_workload_s"] > 0 and cb["cpu_model"]
+
+
+@pytest.mark.gpu
+def test_bench_graph_replay_of_a_streaming_step(lib, capsys, monkeypatch):
+    """A frame-cache streaming step, also timed as a replayed HIP graph."""
+    import bench
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--workload", "stream-cache", "--steps", "3", "--warmup", "1",
+                                      "--no-cpu", "--single-mode", "--graph"])
+    print("bench.py --workload stream-cache --graph", file=sys.stderr, flush=True)
+    bench.main()
+    lines = [s for s in capsys.readouterr().out.splitlines() if s.strip()]
+    assert len(lines) == 1, lines
+    r = json.loads(lines[0])
+    g = r["graph_replay"]
+    assert g["ms_per_step"] > 0
+    assert abs(g["value"] - r["config"]["ops_per_step"] / (g["ms_per_step"] * 1e-3) / 1e12) <= 1e-2 * g["value"]
