@@ -98,6 +98,7 @@ def load(path=None):
         "sage_attn_quantize_frames": (ctypes.c_int, [_DESC_P, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                                      ctypes.c_int32, ctypes.c_int32, _BUFS_P, ctypes.c_void_p]),
         "sage_attn_fwd_quantized": (ctypes.c_int, [_DESC_P, _BUFS_P, ctypes.c_void_p, ctypes.c_void_p]),
+        "sage_attn_fwd_quantized_noalloc": (ctypes.c_int, [_DESC_P, _BUFS_P, ctypes.c_void_p, ctypes.c_void_p]),
         "sage_attn_fwd": (ctypes.c_int, [_DESC_P, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
         "sage_attn_debug_scores_i32": (ctypes.c_int, [_DESC_P, _BUFS_P, ctypes.POINTER(ctypes.c_int32),
@@ -248,6 +249,13 @@ def sage_attn_quantize_frames_batched(desc, q, k, v, frame0, nframes, bufs, stre
 def sage_attn_fwd_quantized(desc, bufs, o, stream=None):
     _check(load().sage_attn_fwd_quantized(desc.ptr, ctypes.byref(bufs), ctypes.c_void_p(o.data_ptr()),
                                           _stream(stream)), "sage_attn_fwd_quantized")
+
+
+def sage_attn_fwd_quantized_noalloc(desc, bufs, o, stream=None):
+    """sage_attn_fwd_quantized with its split-KV partials in the library's
+    device scratch: no workspace partial region is needed."""
+    _check(load().sage_attn_fwd_quantized_noalloc(desc.ptr, ctypes.byref(bufs), ctypes.c_void_p(o.data_ptr()),
+                                                  _stream(stream)), "sage_attn_fwd_quantized_noalloc")
 
 
 def sage_attn_fwd(desc, q, k, v, o, ws, stream=None):

@@ -532,6 +532,45 @@ sage_status sage_attn_fwd_quantized(const sage_attn_desc* desc, const sage_quant
   }
 }
 
+sage_status sage_attn_fwd_quantized_noalloc(const sage_attn_desc* desc, const sage_quant_bufs* bufs, void* o,
+                                            void* stream) {
+  try {
+    Plan p;
+    sage_status s = make_plan(desc, &p);
+    if (s != SAGE_OK) return s;
+    if (!o) return fail(SAGE_E_NULL, "o is NULL");
+    if (!aligned16(o)) return fail(SAGE_E_ALIGN, "o must be 16-byte aligned");
+    const size_t need = p.splits > 1 ? static_cast<size_t>(p.splits) * p.B * p.H * p.Nq_pad * (p.d + 2) * 4 : 0;
+    if (need > sage::SCRATCH_BYTES)
+      return fail(SAGE_E_WORKSPACE, "split-KV partials need " + std::to_string(need) +
+                                        " bytes, more than the " + std::to_string(sage::SCRATCH_BYTES) +
+                                        "-byte device scratch of sage_attn_fwd_quantized_noalloc");
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (hs) {
+      int sdev = 0, cur = 0;
+      hipError_t e = hipStreamGetDevice(hs, &sdev);
+      if (e == hipSuccess) e = hipGetDevice(&cur);
+      if (e != hipSuccess) return fail(SAGE_E_HIP, std::string("HIP error: ") + hipGetErrorString(e));
+      if (sdev != cur) return fail(SAGE_E_UNSUPPORTED, "the stream must belong to the current device");
+    }
+    sage_quant_bufs b = bufs ? *bufs : sage_quant_bufs{};
+    b.partial = nullptr;
+    b.partial_splits = 1;
+    if (need > 0) {
+      void* ptr = nullptr;
+      const hipError_t e = sage::scratch_address(&ptr);
+      if (e != hipSuccess) return fail(SAGE_E_HIP, std::string("device scratch: ") + hipGetErrorString(e));
+      b.partial = ptr;
+      b.partial_splits = p.splits;
+    }
+    if ((s = check_bufs(bufs ? &b : nullptr, p, false)) != SAGE_OK) return s;
+    const sage::AttnLaunch L = attn_launch_of(p, b, o, desc);
+    return finish(sage::launch_attention(L, hs), desc, hs);
+  } catch (const std::exception& e) {
+    return fail(SAGE_E_HIP, e.what());
+  }
+}
+
 sage_status sage_attn_fwd(const sage_attn_desc* desc, const void* q, const void* k, const void* v, void* o,
                           void* ws, size_t ws_bytes, void* stream) {
   sage_quant_bufs b;

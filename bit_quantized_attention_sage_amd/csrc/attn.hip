@@ -45,6 +45,7 @@
 //    32*(mu/2) + 16*h2 + 8*(mu%2) + [0, 8) in lane half h2 for step mu.
 //  * O^T accumulator: lane l holds query r32 and channels
 //    32*cb + 8*(i/4) + 4*h2 + i%4, so per-row factors (alpha, 1/l) are per lane.
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
@@ -864,6 +865,31 @@ __global__ __launch_bounds__(64) void debug_scores_kernel(AttnArgs A, DebugTiles
     o[i] = s0[i] - SBIAS;
     o[32 + i] = s1[i] - SBIAS;
   }
+}
+
+// ------------------------------------------------- allocation-free scratch
+// Split-KV partial results of sage_attn_fwd_quantized_noalloc: a file-scope
+// device array, one copy per GPU, held until the process ends.  In host code
+// `scratch` is only a stand-in for the symbol: its device address comes from
+// hipGetSymbolAddress, fetched once per device with that device current.
+static __device__ __align__(256) uint8_t scratch[SCRATCH_BYTES];
+
+hipError_t scratch_address(void** ptr) {
+  static std::mutex mu;
+  static void* addr[MAX_DEVICES] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 // ---------------------------------------------------------------- launchers

@@ -64,6 +64,12 @@ hipError_t launch_w8a8_quant_weight(const W8A8Launch& L, const void* w, int8_t* 
 hipError_t launch_w8a8_gemm(const W8A8Launch& L, const int8_t* xq, const float* xscale, const int8_t* wq,
                             const float* wscale, const void* bias, void* y, hipStream_t st);
 
+// Device scratch of the allocation-free entry point (attn.hip): its size, and
+// its address on the current device (fetched once per device).
+constexpr size_t SCRATCH_BYTES = size_t{128} << 20;
+constexpr int MAX_DEVICES = 64;
+hipError_t scratch_address(void** ptr);
+
 hipError_t launch_quantize(const QuantLaunch& L, hipStream_t st);
 hipError_t launch_attention(const AttnLaunch& L, hipStream_t st);
 hipError_t launch_debug_scores(const AttnLaunch& L, const int32_t* tiles, int ntiles,

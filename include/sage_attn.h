@@ -240,6 +240,22 @@ sage_status sage_attn_quantize_frames_batched(const sage_attn_desc *desc, const 
 sage_status sage_attn_fwd_quantized(const sage_attn_desc *desc, const sage_quant_bufs *bufs,
                                     void *o, void *stream);
 
+/* For callers that cannot allocate device memory (code under hipGraph
+ * capture, tight serving loops, harnesses that forbid allocation): as
+ * sage_attn_fwd_quantized, except that the split-KV partial results go to a
+ * device scratch array inside the library (128 MiB, one per GPU, held until
+ * the process ends) instead of bufs->partial, which may be NULL.  The call
+ * allocates and frees nothing.  Its split count (kv_splits or the library's
+ * choice) needs splits * B * H * ceil(Nq/128)*128 * (d + 2) * 4 bytes of
+ * that scratch when splits > 1: more fails with SAGE_E_WORKSPACE, before
+ * anything is enqueued.  Every call on one GPU shares that GPU's scratch:
+ * calls that overlap on one GPU (concurrent streams, threads) race; the
+ * kernels write every partial they read, so nothing needs clearing between
+ * calls.  The stream must belong to the current device
+ * (SAGE_E_UNSUPPORTED otherwise). */
+sage_status sage_attn_fwd_quantized_noalloc(const sage_attn_desc *desc, const sage_quant_bufs *bufs,
+                                            void *o, void *stream);
+
 /* Drop-in call: quantize into the workspace, then attend.  Equivalent to
  * sage_attn_quant_layout + sage_attn_quantize + sage_attn_fwd_quantized. */
 sage_status sage_attn_fwd(const sage_attn_desc *desc, const void *q, const void *k,
