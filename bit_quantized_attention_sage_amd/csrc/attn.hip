@@ -219,15 +219,20 @@ struct WaveState {
     }
   }
 
-  // Softmax step of one chunk on its integer scores: the row maximum (the
-  // two lane halves hold the same query), the lazy running-max update (the
-  // row adopts the chunk maximum only when it exceeds m by more than TAU),
-  // p = 2^(S c - (m - s)) and P rounded to the P.V operand type.  Returns
-  // alpha (1 for rows that kept m); the caller rescales O and the row sums
-  // by it when any row of the wave moved.  The row sums of the rounded P are
-  // taken on the matrix cores in pv().
+  // Softmax of one chunk, in two halves.  head: the row maximum over the
+  // chunk (the two lane halves hold the same query), the lazy running-max
+  // update (the row adopts the chunk maximum only when it exceeds m by more
+  // than TAU), then p = 2^x for the scores in s0 rounded into P's first half;
+  // returns alpha (1 for rows that kept m), by which the caller rescales O
+  // and the row sums when any row of the wave moved.  tail: the same for s1
+  // into P's second half.  x = fp32(S c - mref) is rounded once, as the
+  // scheme defines it: F - F0 = S 2^-26 exactly, then one FMA.  The row
+  // sums of the rounded P are taken on the matrix cores in pv().
   // `has`: this row has a visible key in the chunk (rows without one keep m).
-  __device__ __forceinline__ float softmax(const v16i& s0, const v16i& s1, float c, bool has, PTile<PV>& P) {
+  float xc_, xk_;  // c 2^26 and -mref of the chunk being converted
+
+  __device__ __forceinline__ float softmax_head(const v16i& s0, const v16i& s1, float c, bool has,
+                                                PTile<PV>& P) {
     // two v_max3 chains of 8 over the lane's 32 scores
     int ma = max3_i32(s0[0], s0[1], s0[2]), mb = max3_i32(s1[0], s1[1], s1[2]);
 #pragma unroll
@@ -244,34 +249,39 @@ struct WaveState {
     const bool upd = has && (tm > m + TAU);
     const float alpha = upd ? __builtin_amdgcn_exp2f(m - tm) : 1.0f;
     m = upd ? tm : m;
-    const float nmref = -(m - static_cast<float>(SHIFT));
+    xk_ = -(m - static_cast<float>(SHIFT));
     // c 2^26, exact; a zero scale (all-zero Q or K block: every score 0)
     // becomes the smallest normal float, so that MASKED keys (F = -inf)
     // still give -inf and the others x = -mref up to S 2^-126
-    const float c2 = fmaxf(c, 1.17549435e-38f) * 67108864.0f;
+    xc_ = fmaxf(c, 1.17549435e-38f) * 67108864.0f;
+    exps<0>(s0, P);
+    return alpha;
+  }
+  __device__ __forceinline__ void softmax_tail(const v16i& s1, PTile<PV>& P) { exps<1>(s1, P); }
+  __device__ __forceinline__ float softmax(const v16i& s0, const v16i& s1, float c, bool has, PTile<PV>& P) {
+    const float alpha = softmax_head(s0, s1, c, has, P);
+    softmax_tail(s1, P);
+    return alpha;
+  }
+
+  template <int HALF>
+  __device__ __forceinline__ void exps(const v16i& s, PTile<PV>& P) {
     const float f0 = __builtin_bit_cast(float, SBIAS);
-    float p0[16], p1[16];
+    float p[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       // (copy the element out first: a bit cast of a vector subscript reads element 0)
-      const int b0 = s0[i], b1 = s1[i];
-      p0[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(__builtin_bit_cast(float, b0) - f0, c2, nmref));
-      p1[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(__builtin_bit_cast(float, b1) - f0, c2, nmref));
+      const int bi = s[i];
+      p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(__builtin_bit_cast(float, bi) - f0, xc_, xk_));
     }
     if constexpr (PV == PVFP8) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        P.b[k] = static_cast<int>(pack_e4m3x4_into(p0[4 * k], p0[4 * k + 1], p0[4 * k + 2], p0[4 * k + 3]));
-        P.b[4 + k] = static_cast<int>(pack_e4m3x4_into(p1[4 * k], p1[4 * k + 1], p1[4 * k + 2], p1[4 * k + 3]));
-      }
+      for (int k = 0; k < 4; ++k)
+        P.b[4 * HALF + k] = static_cast<int>(pack_e4m3x4_into(p[4 * k], p[4 * k + 1], p[4 * k + 2], p[4 * k + 3]));
     } else {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        P.w[k] = Pack16<DT>::pack(p0[2 * k], p0[2 * k + 1]);
-        P.w[8 + k] = Pack16<DT>::pack(p1[2 * k], p1[2 * k + 1]);
-      }
+      for (int k = 0; k < 8; ++k) P.w[8 * HALF + k] = Pack16<DT>::pack(p[2 * k], p[2 * k + 1]);
     }
-    return alpha;
   }
 
   __device__ __forceinline__ void rescale(float alpha) {
@@ -344,92 +354,118 @@ enum { KV_DENSE = 0,    // contiguous keys, every chunk up to the tile's range e
        KV_SPARSE = 2 }; // contiguous keys, only the chunks the block mask keeps
 constexpr int MAX_LIST = 4096;  // kept-chunk list of a tile (LDS, 2 bytes each)
 
-template <int D, int PV, int DT, int MODE, bool PP>
-__global__ __launch_bounds__(PP ? 512 : 256, PP ? 1 : 2) void attn_fwd_kernel(AttnArgs A) {
-  constexpr bool CACHE = MODE == KV_CACHE, SPARSE = MODE == KV_SPARSE;
-  static_assert(!(PP && SPARSE), "the two query blocks of a ping-pong tile share one chunk list");
-  constexpr int NWAVE = PP ? 8 : 4;
-  constexpr int NCB = D / 32;                    // 32-channel blocks of O
-  constexpr int VBYTES = (PV == PVFP8) ? 1 : 2;  // bytes per V element
-  constexpr int KB = 64 * D;                     // bytes of a K chunk
-  constexpr int VBC = 64 * D * VBYTES;           // bytes of a V^T chunk
-  constexpr int KI = KB / 4096;                  // 1 KB DMA instructions per wave, K
-  constexpr int VI = VBC / 4096;                 // ... and V
-  static_assert(KI >= 1 && KI <= 2 && VI >= 1 && VI <= 4, "staging shape");
-  // Two buffers each, as separate objects so that the compiler can tell the
-  // buffer being filled by DMA from the one being read.
-  __shared__ __attribute__((aligned(16))) int8_t kL0[KB];
-  __shared__ __attribute__((aligned(16))) int8_t kL1[KB];
-  __shared__ __attribute__((aligned(16))) uint8_t vL0[VBC];
-  __shared__ __attribute__((aligned(16))) uint8_t vL1[VBC];
-  __shared__ uint16_t slist[SPARSE ? MAX_LIST : 1];  // kept chunks of the tile, ascending
-  __shared__ int scnt[8];
+// The key chunks one work item visits, in order, and which keys of a chunk
+// each query row sees.  A work item is a tile of query rows [row_first,
+// row_last] of one (b, h) and one KV split.  Each batch's chunks form one
+// ordered list, the same for every tile; split s takes entries
+// [s*n/S, (s+1)*n/S) of it, and the tile visits the entries of that part that
+// its rows can see, as entries [v_lo, v_hi) of its own list:
+//  * contiguous keys: the batch's chunks [0, ceil(kv_len/64)); the tile's
+//    list is the prefix up to its last row's range end; entry v is chunk v;
+//    a row sees the prefix [0, re) of the keys;
+//  * block mask: the same parts of the batch's chunks; the tile's list is
+//    the chunks of its part that the mask keeps (and its last row can see),
+//    compacted in order into LDS; entries then run from 0;
+//  * frame cache: the chunks some row of the batch sees -- the sink frames',
+//    then the window frames' from the first query's window start through the
+//    last query's frame (up to its last token); the tile's own list is built
+//    the same way over its rows (entry v is chunk v for v < a0, else chunk
+//    b1 + (v - a0)); a row sees the valid slots of the frames of its window.
+// List entries below v_full are visible in full to every row of the tile.
+template <int MODE>
+struct WorkList {
+  int v_lo, v_hi, v_full;
+  int kv_len, F, FS, sink, window;
+  uint32_t cpf_magic;
+  int re;                 // contiguous keys: this row's range end
+  int full_end;           // contiguous keys: the first row's range end
+  int fq, fq_lo, fq_hi;   // frame cache: this row's frame, the tile's first / last rows' frames
+  int a0, b1;             // frame cache: the tile list's sink / window cut
+  const uint16_t* slist;  // block mask: the kept chunks of the tile
 
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h2 = lane >> 5;
+  // physical chunk of list entry v; contiguous keys: v itself (the loads
+  // clamp it to the head's last chunk); frame cache and block mask: clamped
+  // to the item's range first
+  __device__ __forceinline__ int chunk_of(int v) const {
+    if constexpr (MODE == KV_DENSE) {
+      return v;
+    } else if constexpr (MODE == KV_SPARSE) {
+      if (v_hi <= v_lo) return 0;
+      v = max(min(v, v_hi - 1), v_lo);
+      return __builtin_amdgcn_readfirstlane(static_cast<int>(slist[v]));
+    } else {
+      v = max(min(v, v_hi - 1), 0);
+      return v < a0 ? v : b1 + (v - a0);
+    }
+  }
+  // frame of cache chunk ch: ch / (FS/64) by a multiply-high with the host's
+  // rounded-up reciprocal (exact for ch < 2^20, FS/64 < 2^11); with one chunk
+  // per frame the reciprocal (2^32) does not fit and f = ch
+  __device__ __forceinline__ int frame_of(int ch) const {
+    return FS == 64 ? ch : static_cast<int>(__umulhi(static_cast<uint32_t>(ch), cpf_magic));
+  }
+  // every row of the tile sees all 64 keys of chunk ch (wave-uniform)
+  __device__ __forceinline__ bool chunk_full(int ch) const {
+    if constexpr (MODE != KV_CACHE) return (ch + 1) * 64 <= full_end;
+    const int f = frame_of(ch);
+    const int t0 = (ch - f * (FS / 64)) * 64;
+    const int vc = min(min(F - t0, kv_len - (f * F + t0)), 64);
+    const bool all = f <= fq_lo && (window == 0 || f < sink || f >= fq_hi - window);
+    return vc >= 64 && all;
+  }
+  // this row sees the first row_lim(ch) keys of chunk ch
+  __device__ __forceinline__ int row_lim(int ch) const {
+    if constexpr (MODE != KV_CACHE) return re - ch * 64;
+    const int f = frame_of(ch);
+    const int t0 = (ch - f * (FS / 64)) * 64;
+    const int vc = min(min(F - t0, kv_len - (f * F + t0)), 64);
+    const bool vis = f <= fq && (window == 0 || f < sink || f >= fq - window);
+    return vis ? vc : 0;
+  }
+};
 
-  // ---- work item: (batch by decreasing kv_len, head, split, query tile)
-  const int ntile = PP ? (A.nqt + 1) / 2 : A.nqt;             // tiles of NWAVE * 32 rows
-  const int L = xcd_group_remap(blockIdx.x, A.total, ntile);  // groups: the tiles of one (b, h, split)
-  const int per_b = A.H * A.splits * ntile;
-  const int b = A.order[L / per_b];
-  int rem = L % per_b;
-  const int h = rem / (A.splits * ntile);
-  rem %= A.splits * ntile;
-  const int split = rem / ntile;
-  const int qt = rem % ntile;
-  const int bh = b * A.H + h;
-  // this wave's group, its place in the group and its 128-row Q block (the
-  // second block of the last tile may lie past Nq: its rows load the last
-  // real block and store nothing)
-  const int grp = PP ? (w >> 2) : 0, w4 = w & 3;
-  const int qb = PP ? 2 * qt + grp : qt;
-  const int qbl = min(qb, A.nqt - 1);
-
-  const int kv_len = A.bi.kv_len[b];
-  const int q_pos0 = A.bi.q_pos0[b];
-  const int F = A.frame_len, FS = CACHE ? A.frame_stride : 0;
-
-  // ---- this lane's query row and the tile's first and last real rows
-  const int qi = qb * BQ + w4 * 32 + (lane & 31);
-  const int qi_valid = min(qi, A.Nq - 1);
-  const int row_first = (PP ? 2 * qt : qt) * BQ, row_last = min(row_first + NWAVE * 32, A.Nq) - 1;
-
-  // ---- the key chunks this work item visits: list entry v is chunk v for
-  // v < a0, else chunk b1 + (v - a0); the split takes entries [v_lo, v_hi).
-  //  * contiguous keys: the batch's chunks [0, ceil(kv_len/64)), split on that
-  //    grid, cut at the end of the tile's last row; a row sees the prefix
-  //    [0, re) of the keys;
-  //  * frame cache: the chunks of the sink frames, then those of the window
-  //    frames through the last row's frame (up to its last token), split on
-  //    the same list built for all the batch's rows; a row sees the valid
-  //    slots of the frames of its window.
-  int re = 0, fq = 0, fq_lo = 0, fq_hi = 0, a0 = 0, b1 = 0, v_lo, v_hi, full_end = 0, n_full = 0;
-  if constexpr (!CACHE) {
-    re = F > 0 ? min(kv_len, ((q_pos0 + qi_valid) / F + 1) * F) : kv_len;
+// Build the list of one work item (see WorkList).  NT threads take part
+// (the block-mask list is compacted by the whole workgroup; the call holds
+// barriers then, so every thread of the workgroup must make it).
+template <int MODE, int NT>
+__device__ __forceinline__ WorkList<MODE> make_worklist(const AttnArgs& A, int b, int bh, int mask_tile, int split,
+                                                        int row_first, int row_last, int qi_valid, int tid,
+                                                        uint16_t* slist, int* scnt) {
+  WorkList<MODE> L;
+  const int kv_len = A.bi.kv_len[b], q_pos0 = A.bi.q_pos0[b], F = A.frame_len;
+  L.kv_len = kv_len;
+  L.F = F;
+  L.FS = MODE == KV_CACHE ? A.frame_stride : 0;
+  L.sink = A.sink_frames;
+  L.window = A.window_frames;
+  L.cpf_magic = A.cpf_magic;
+  L.re = L.full_end = L.fq = L.fq_lo = L.fq_hi = L.a0 = L.b1 = 0;
+  L.slist = slist;
+  if constexpr (MODE != KV_CACHE) {
+    L.re = F > 0 ? min(kv_len, ((q_pos0 + qi_valid) / F + 1) * F) : kv_len;
     const int first_end = F > 0 ? min(kv_len, ((q_pos0 + row_first) / F + 1) * F) : kv_len;
     const int last_end = F > 0 ? min(kv_len, ((q_pos0 + row_last) / F + 1) * F) : kv_len;
     const int nch = (kv_len + 63) / 64;
-    v_lo = split * nch / A.splits;
-    v_hi = min((split + 1) * nch / A.splits, (last_end + 63) / 64);
-    full_end = first_end;  // chunks ending at or before it are visible in full to every row
-    if constexpr (SPARSE) {
-      // The split covers the batch's chunks [v_lo, v_hi) as without a mask;
-      // the work item's list is the chunks among them that the mask keeps
-      // for this tile, compacted in order into LDS by the whole workgroup
-      // (ballot + per-wave counts); `below` counts those visible in full to
-      // every row.  List entries then run from 0.
-      const int nfull = full_end / 64;
-      const uint8_t* mrow = A.block_mask + (static_cast<int64_t>(bh) * A.nqt + qt) * A.mask_nkc;
+    L.v_lo = split * nch / A.splits;
+    L.v_hi = min((split + 1) * nch / A.splits, (last_end + 63) / 64);
+    L.full_end = first_end;
+    L.v_full = first_end / 64;
+    if constexpr (MODE == KV_SPARSE) {
+      // the chunks of [v_lo, v_hi) the mask keeps, compacted in order by the
+      // whole workgroup (ballot + per-wave counts); `below` counts those
+      // visible in full to every row
+      constexpr int NW = NT / 64;
+      const int lane = tid & 63, w = tid >> 6;
+      const int nfull = first_end / 64;
+      const uint8_t* mrow = A.block_mask + (static_cast<int64_t>(bh) * A.nqt + mask_tile) * A.mask_nkc;
       int total = 0, below = 0;
-      for (int c0 = v_lo; c0 < v_hi; c0 += 256) {
+      for (int c0 = L.v_lo; c0 < L.v_hi; c0 += NT) {
         const int c = c0 + tid;
-        const bool keep = c < v_hi && mrow[c] != 0;
+        const bool keep = c < L.v_hi && mrow[c] != 0;
         const uint64_t bk = __ballot(keep), bf = __ballot(keep && c < nfull);
         if (lane == 0) {
           scnt[w] = __popcll(bk);
-          scnt[4 + w] = __popcll(bf);
+          scnt[NW + w] = __popcll(bf);
         }
         __syncthreads();
         int off = total;
@@ -437,32 +473,31 @@ __global__ __launch_bounds__(PP ? 512 : 256, PP ? 1 : 2) void attn_fwd_kernel(At
         const int rank = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bk >> 32),
                                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bk), 0));
         if (keep) slist[off + rank] = static_cast<uint16_t>(c);
-        total += scnt[0] + scnt[1] + scnt[2] + scnt[3];
-        below += scnt[4] + scnt[5] + scnt[6] + scnt[7];
+        for (int i = 0; i < NW; ++i) {
+          total += scnt[i];
+          below += scnt[NW + i];
+        }
         __syncthreads();
       }
-      v_lo = 0;
-      v_hi = total;
-      n_full = below;
+      L.v_lo = 0;
+      L.v_hi = total;
+      L.v_full = below;
     }
   } else {
-    const int cpf = FS / 64;
-    fq = (q_pos0 + qi_valid) / F;
-    fq_lo = (q_pos0 + row_first) / F;
-    fq_hi = (q_pos0 + row_last) / F;
-    const int end_chunk = (fq_hi * FS + min(F, kv_len - fq_hi * F) + 63) / 64;
+    const int FS = L.FS, cpf = FS / 64;
+    L.fq = (q_pos0 + qi_valid) / F;
+    L.fq_lo = (q_pos0 + row_first) / F;
+    L.fq_hi = (q_pos0 + row_last) / F;
+    const int end_chunk = (L.fq_hi * FS + min(F, kv_len - L.fq_hi * F) + 63) / 64;
     int nv = end_chunk;
     if (A.window_frames > 0) {
-      a0 = min(min(A.sink_frames, fq_hi + 1) * cpf, end_chunk);
-      b1 = min(max(A.sink_frames, fq_lo - A.window_frames) * cpf, end_chunk);
-      b1 = max(b1, a0);
-      nv = a0 + (end_chunk - b1);
+      L.a0 = min(min(A.sink_frames, L.fq_hi + 1) * cpf, end_chunk);
+      L.b1 = max(min(max(A.sink_frames, L.fq_lo - A.window_frames) * cpf, end_chunk), L.a0);
+      nv = L.a0 + (end_chunk - L.b1);
     }
-    // The split cuts the batch's list -- the same construction over all its
-    // query rows -- into equal parts, so where it cuts does not depend on
-    // the tile; the item visits the entries of its own list that fall in
-    // its part: tile_count(V) = entries of the tile's list whose chunk lies
-    // before the chunk of batch entry V.
+    // the batch's list over all its query rows, cut into the splits' parts;
+    // tile_count(V): entries of the tile's list whose chunk lies before the
+    // chunk of batch entry V
     const int FQ_lo = q_pos0 / F, FQ_hi = (q_pos0 + A.Nq - 1) / F;
     const int END = (FQ_hi * FS + min(F, kv_len - FQ_hi * F) + 63) / 64;
     int A0 = 0, B1 = 0;
@@ -471,58 +506,196 @@ __global__ __launch_bounds__(PP ? 512 : 256, PP ? 1 : 2) void attn_fwd_kernel(At
       B1 = max(min(max(A.sink_frames, FQ_lo - A.window_frames) * cpf, END), A0);
     }
     const int NV = A0 + (END - B1);
+    const int a0 = L.a0, b1 = L.b1;
     auto tile_count = [&](int V) -> int {
       if (V >= NV) return nv;
       const int ch = V < A0 ? V : B1 + (V - A0);
       return min(ch, a0) + max(0, min(ch, end_chunk) - b1);
     };
-    v_lo = tile_count(split * NV / A.splits);
-    v_hi = tile_count((split + 1) * NV / A.splits);
+    L.v_lo = tile_count(split * NV / A.splits);
+    L.v_hi = tile_count((split + 1) * NV / A.splits);
+    L.v_full = 0;  // no shortcut over a frame cache
   }
-  const int J = max(0, v_hi - v_lo);  // chunks of this work item
-  // list entries below this one are visible in full to every row of the tile
-  // (contiguous keys: up to the first row's end; frame cache: no shortcut)
-  const int v_full = CACHE ? 0 : SPARSE ? n_full : full_end / 64;
-  // physical chunk of list entry v; contiguous keys: v itself (the loads
-  // clamp it to the head's last chunk); frame cache and block mask: clamped
-  // to the item's range first
-  auto chunk_of = [&](int v) -> int {
-    if constexpr (MODE == KV_DENSE) {
-      return v;
-    } else if constexpr (SPARSE) {
-      if (v_hi <= v_lo) return 0;
-      v = max(min(v, v_hi - 1), v_lo);
-      return __builtin_amdgcn_readfirstlane(static_cast<int>(slist[v]));
-    } else {
-      v = max(min(v, v_hi - 1), 0);
-      return v < a0 ? v : b1 + (v - a0);
-    }
-  };
+  return L;
+}
 
-  // Visibility of chunk ch: every row sees all 64 keys (wave-uniform), or
-  // this row sees its first row_lim keys.
-  // frame of cache chunk ch: ch / (FS/64) by a multiply-high with the
-  // host's rounded-up reciprocal (exact for ch < 2^20, FS/64 < 2^11); with
-  // one chunk per frame the reciprocal (2^32) does not fit and f = ch
-  auto frame_of = [&](int ch) -> int {
-    return FS == 64 ? ch : static_cast<int>(__umulhi(static_cast<uint32_t>(ch), A.cpf_magic));
-  };
-  auto chunk_full = [&](int ch) -> bool {
-    if constexpr (!CACHE) return (ch + 1) * 64 <= full_end;
-    const int f = frame_of(ch);
-    const int t0 = (ch - f * (FS / 64)) * 64;
-    const int vc = min(min(F - t0, kv_len - (f * F + t0)), 64);
-    const bool all = f <= fq_lo && (A.window_frames == 0 || f < A.sink_frames || f >= fq_hi - A.window_frames);
-    return vc >= 64 && all;
-  };
-  auto row_lim = [&](int ch) -> int {
-    if constexpr (!CACHE) return re - ch * 64;
-    const int f = frame_of(ch);
-    const int t0 = (ch - f * (FS / 64)) * 64;
-    const int vc = min(min(F - t0, kv_len - (f * F + t0)), 64);
-    const bool vis = f <= fq && (A.window_frames == 0 || f < A.sink_frames || f >= fq - A.window_frames);
-    return vis ? vc : 0;
-  };
+// Staging of K and V^T chunks from HBM straight into LDS: raw buffer loads
+// that write LDS (no registers), issued by the four waves 0-3.  Lane l of DMA
+// instruction i of wave w fills LDS granule (4i + w)*64 + l of the buffer;
+// its global source is chosen so that the buffer ends up in the swizzled
+// layouts above.  Every chunk index is clamped to the head's last padded
+// chunk, so all reads stay inside the head's slice; the prefetches that the
+// clamp redirects are never consumed.  The K scale and this lane's four E8M0
+// bytes of a chunk are plain loads into registers.
+template <int D, int PV>
+struct Stager {
+  static constexpr int VBYTES = (PV == PVFP8) ? 1 : 2;
+  static constexpr int KB = 64 * D;            // bytes of a K chunk
+  static constexpr int VBC = 64 * D * VBYTES;  // bytes of a V^T chunk
+  static constexpr int KI = KB / 4096;         // 1 KB DMA instructions per wave, K
+  static constexpr int VI = VBC / 4096;        // ... and V
+  static_assert(KI >= 1 && KI <= 2 && VI >= 1 && VI <= 4, "staging shape");
+  __amdgpu_buffer_rsrc_t krs, vrs, ers, srs;
+  int last, w, lane;
+  // source offset, inside a chunk, of the 16 bytes this lane's DMA
+  // instruction i brings to LDS granule (4i + w)*64 + lane
+  __device__ __forceinline__ int koff(int i) const {
+    constexpr int G = D / 16;
+    const int sidx = (4 * i + w) * 64 + lane, key = sidx / G, gp = sidx % G;
+    return key * D + ((gp ^ k_swz<D>(key)) << 4);
+  }
+  __device__ __forceinline__ int voff(int i) const {
+    constexpr int GR = VRow<PV>::GR;
+    const int sidx = (4 * i + w) * 64 + lane, c = sidx / GR, gp = sidx % GR;
+    return c * VRow<PV>::BYTES + ((gp ^ VRow<PV>::swz(c)) << 4);
+  }
+
+  __device__ __forceinline__ void init(const AttnArgs& A, int bh, int wave, int lane) {
+    const int nkc = A.Nkv_pad / 64;
+    const int8_t* kbase = A.kc + static_cast<int64_t>(bh) * A.Nkv_pad * D;
+    const uint8_t* vbase = static_cast<const uint8_t*>(A.vt) + static_cast<int64_t>(bh) * nkc * VBC;
+    const uint8_t* ebase = A.ve + static_cast<int64_t>(bh) * nkc * 256;
+    const float* ksc = A.kscale + static_cast<int64_t>(bh) * nkc;
+    krs = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(kbase), 0, nkc * KB, 0x00020000);
+    vrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(vbase), 0, nkc * VBC, 0x00020000);
+    ers = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(ebase), 0, PV == PVFP8 ? nkc * 256 : 0,
+                                            0x00020000);
+    srs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(ksc), 0, nkc * 4, 0x00020000);
+    w = wave & 3;
+    this->lane = lane;
+    last = nkc - 1;  // chunk indices are clamped: prefetches past the end go unused
+  }
+  __device__ __forceinline__ void dma_k(int8_t* dst, int ch) const {
+    ch = min(ch, last);
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      // (the offset goes through a local: any other expression as this
+      // builtin's argument makes the host pass drop the kernel's launch stub)
+      const int off = koff(i);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, dst + (4 * i + w) * 1024, 16, off, ch * KB, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void dma_v(uint8_t* dst, int ch) const {
+    ch = min(ch, last);
+#pragma unroll
+    for (int i = 0; i < VI; ++i) {
+      const int off = voff(i);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, dst + (4 * i + w) * 1024, 16, off, ch * VBC, 0, 0);
+    }
+  }
+  __device__ __forceinline__ float load_ks(int ch) const {
+    ch = min(ch, last);
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, 0, ch * 4, 0));
+  }
+  __device__ __forceinline__ int load_e(int ch, int lane) const {
+    ch = min(ch, last);
+    return PV == PVFP8 ? __builtin_amdgcn_raw_buffer_load_b32(ers, lane * 4, ch * 256, 0) : 0;
+  }
+};
+
+__device__ __forceinline__ void dma_wait() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+// Decode a work item (batch by decreasing kv_len, head, split, query tile)
+// from a physical workgroup id: the tiles of one (b, h, split) share an XCD.
+struct Item {
+  int b, h, split, qt, bh;
+  __device__ __forceinline__ Item(const AttnArgs& A, int ntile) {
+    const int L = xcd_group_remap(blockIdx.x, A.total, ntile);
+    const int per_b = A.H * A.splits * ntile;
+    b = A.order[L / per_b];
+    int rem = L % per_b;
+    h = rem / (A.splits * ntile);
+    rem %= A.splits * ntile;
+    split = rem / ntile;
+    qt = rem % ntile;
+    bh = b * A.H + h;
+  }
+};
+
+// Normalise and store this lane's row of O, or (with KV splits) its
+// unnormalised-by-merge partial: O / l and (m, l).
+template <int D, int DT>
+__device__ __forceinline__ void store_row(const AttnArgs& A, const v16f* o, float m, float ltot, int b, int h,
+                                          int bh, int split, int qi, int h2) {
+  constexpr int NCB = D / 32;
+  const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;  // a row with no visible key: 0
+  if (A.splits == 1) {
+    uint16_t* orow = static_cast<uint16_t*>(A.o) + b * A.os_b + h * A.os_h + static_cast<int64_t>(qi) * A.os_n;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int chn = 32 * cb + 8 * g + 4 * h2;
+        const uint32_t w0 = Pack16<DT>::pack(o[cb][4 * g] * inv, o[cb][4 * g + 1] * inv);
+        const uint32_t w1 = Pack16<DT>::pack(o[cb][4 * g + 2] * inv, o[cb][4 * g + 3] * inv);
+        *reinterpret_cast<uint2*>(orow + chn) = make_uint2(w0, w1);
+      }
+  } else {
+    const int64_t prow = (static_cast<int64_t>(split) * A.B * A.H + bh) * A.Nq_pad + qi;
+    float* po = A.part_o + prow * D;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int chn = 32 * cb + 8 * g + 4 * h2;
+        *reinterpret_cast<float4*>(po + chn) =
+            make_float4(o[cb][4 * g] * inv, o[cb][4 * g + 1] * inv, o[cb][4 * g + 2] * inv, o[cb][4 * g + 3] * inv);
+      }
+    if (h2 == 0) *reinterpret_cast<float2*>(A.part_ml + 2 * prow) = make_float2(m, ltot);
+  }
+}
+
+// Masking of a chunk whose scores are in (s0, s1): taken only at boundaries
+// (the last chunks of a row's range, frame padding, window edges); keys a
+// row does not see get the MASKED score.  Returns whether this row has a
+// visible key in the chunk.
+template <int D, int PV, int DT, int MODE>
+__device__ __forceinline__ bool mask_chunk(const WorkList<MODE>& wl, WaveState<D, PV, DT>& st, int v, v16i& s0,
+                                           v16i& s1, int h2) {
+  const int ch = wl.chunk_of(v);
+  if (wl.chunk_full(ch)) return true;
+  asm volatile("");  // keep this a real branch
+  const int lim = wl.row_lim(ch);
+  st.mask(s0, s1, lim - 16 * h2);
+  return lim > 0;
+}
+
+template <int D, int PV, int DT, int MODE, bool PP>
+__global__ __launch_bounds__(PP ? 512 : 256, PP ? 1 : 2) void attn_fwd_kernel(AttnArgs A) {
+  constexpr bool SPARSE = MODE == KV_SPARSE;
+  static_assert(!(PP && SPARSE), "the two query blocks of a ping-pong tile share one chunk list");
+  constexpr int NWAVE = PP ? 8 : 4;
+  constexpr int NCB = D / 32;                    // 32-channel blocks of O
+  using SG = Stager<D, PV>;
+  // Two buffers each, as separate objects so that the compiler can tell the
+  // buffer being filled by DMA from the one being read.
+  __shared__ __attribute__((aligned(16))) int8_t kL0[SG::KB];
+  __shared__ __attribute__((aligned(16))) int8_t kL1[SG::KB];
+  __shared__ __attribute__((aligned(16))) uint8_t vL0[SG::VBC];
+  __shared__ __attribute__((aligned(16))) uint8_t vL1[SG::VBC];
+  __shared__ uint16_t slist[SPARSE ? MAX_LIST : 1];  // kept chunks of the tile, ascending
+  __shared__ int scnt[2 * NWAVE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h2 = lane >> 5;
+
+  const int ntile = PP ? (A.nqt + 1) / 2 : A.nqt;  // tiles of NWAVE * 32 rows
+  const Item it(A, ntile);
+  const int b = it.b, h = it.h, split = it.split, qt = it.qt, bh = it.bh;
+  // this wave's group, its place in the group and its 128-row Q block (the
+  // second block of the last tile may lie past Nq: its rows load the last
+  // real block and store nothing)
+  const int grp = PP ? (w >> 2) : 0, w4 = w & 3;
+  const int qb = PP ? 2 * qt + grp : qt;
+  const int qbl = min(qb, A.nqt - 1);
+  const int qi = qb * BQ + w4 * 32 + (lane & 31);
+  const int qi_valid = min(qi, A.Nq - 1);
+  const int row_first = (PP ? 2 * qt : qt) * BQ, row_last = min(row_first + NWAVE * 32, A.Nq) - 1;
+  const WorkList<MODE> wl = make_worklist<MODE, NWAVE * 64>(A, b, bh, qt, split, row_first, row_last, qi_valid,
+                                                            tid, slist, scnt);
+  const int v_lo = wl.v_lo, v_hi = wl.v_hi, v_full = wl.v_full;
+  const int J = max(0, v_hi - v_lo);  // chunks of this work item
 
   v4i qv[D / 32];
   load_q<D>(qv, A.qc + (static_cast<int64_t>(bh) * A.Nq_pad + qbl * BQ + w4 * 32 + (lane & 31)) * D, h2);
@@ -540,82 +713,13 @@ __global__ __launch_bounds__(PP ? 512 : 256, PP ? 1 : 2) void attn_fwd_kernel(At
   // moves m (its alpha = 0 scales an O and l that are still 0).
   st.m = -3.40282347e38f;
 
-  const int nkc = A.Nkv_pad / 64;
-  const int8_t* kbase = A.kc + static_cast<int64_t>(bh) * A.Nkv_pad * D;
-  const uint8_t* vbase = static_cast<const uint8_t*>(A.vt) + static_cast<int64_t>(bh) * nkc * VBC;
-  const uint8_t* ebase = A.ve + static_cast<int64_t>(bh) * nkc * 256;
-  const float* ksc = A.kscale + static_cast<int64_t>(bh) * nkc;
-
-  // Staging: raw buffer loads that write straight into LDS (no registers),
-  // issued one step ahead, by the four waves of group 0 (ping-pong) or of the
-  // workgroup.  Lane l of DMA instruction i of wave w fills LDS
-  // granule (4i + w)*64 + l of the buffer; its global source is chosen so that
-  // the buffer ends up in the swizzled layouts above.  Every chunk index is
-  // clamped to the head's last padded chunk, so all reads stay inside the
-  // head's slice; the prefetches that the clamp redirects are never consumed.
-  // The K scale and this lane's four E8M0 bytes of a chunk are plain loads
-  // into registers.
-  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<int8_t*>(kbase), 0, nkc * KB, 0x00020000);
-  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(vbase), 0, nkc * VBC, 0x00020000);
-  const __amdgpu_buffer_rsrc_t ers = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(ebase), 0, PV == PVFP8 ? nkc * 256 : 0, 0x00020000);
-  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float*>(ksc), 0, nkc * 4, 0x00020000);
-  int koff[KI], voff[VI];
-#pragma unroll
-  for (int i = 0; i < KI; ++i) {
-    constexpr int G = D / 16;
-    const int sidx = (4 * i + w) * 64 + lane, key = sidx / G, gp = sidx % G;
-    koff[i] = key * D + ((gp ^ k_swz<D>(key)) << 4);
-  }
-#pragma unroll
-  for (int i = 0; i < VI; ++i) {
-    constexpr int GR = VRow<PV>::GR;
-    const int sidx = (4 * i + w) * 64 + lane, c = sidx / GR, gp = sidx % GR;
-    voff[i] = c * VRow<PV>::BYTES + ((gp ^ VRow<PV>::swz(c)) << 4);
-  }
-  const int last = nkc - 1;  // chunk indices are clamped: prefetches past the end go unused
-  auto dma_k = [&](int8_t* dst, int ch) {
-    if (PP && grp != 0) return;  // group 0 stages every chunk
-    ch = min(ch, last);
-#pragma unroll
-    for (int i = 0; i < KI; ++i) {
-      const int off = koff[i];  // an array element as the builtin's argument drops the host stub
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, dst + (4 * i + w) * 1024, 16, off, ch * KB, 0, 0);
-    }
-  };
-  auto dma_v = [&](uint8_t* dst, int ch) {
-    if (PP && grp != 0) return;
-    ch = min(ch, last);
-#pragma unroll
-    for (int i = 0; i < VI; ++i) {
-      const int off = voff[i];
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, dst + (4 * i + w) * 1024, 16, off, ch * VBC, 0, 0);
-    }
-  };
-  auto load_ks = [&](int ch) -> float {
-    ch = min(ch, last);
-    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, 0, ch * 4, 0));
-  };
-  auto load_e = [&](int ch) -> int {
-    ch = min(ch, last);
-    return PV == PVFP8 ? __builtin_amdgcn_raw_buffer_load_b32(ers, lane * 4, ch * 256, 0) : 0;
-  };
-  auto dma_wait = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0): this wave's DMA landed
-
-  // Masking of a chunk whose scores are in (s0, s1): a wave-uniform branch,
-  // taken only at boundaries (the last chunks of a row's range, frame padding,
-  // window edges).  Returns whether this row has a visible key in the chunk.
-  auto mask_chunk = [&](int v, v16i& s0, v16i& s1) -> bool {
-    const int ch = chunk_of(v);
-    if (chunk_full(ch)) return true;
-    asm volatile("");  // keep this a real branch
-    const int lim = row_lim(ch);
-    st.mask(s0, s1, lim - 16 * h2);
-    return lim > 0;
-  };
+  SG sg;
+  sg.init(A, bh, w, lane);
+  const bool stager = !(PP && grp != 0);  // group 0 (ping-pong) or every wave stages the chunks
+  auto dma_k = [&](int8_t* dst, int ch) { if (stager) sg.dma_k(dst, ch); };
+  auto dma_v = [&](uint8_t* dst, int ch) { if (stager) sg.dma_v(dst, ch); };
+  auto chunk_of = [&](int v) { return wl.chunk_of(v); };
+  auto mask_at = [&](int v, v16i& s0, v16i& s1) { return mask_chunk(wl, st, v, s0, s1, h2); };
 
   // Software pipeline within each wave over three chunks: step j (list entry
   // n = v_lo + j) enters with S(n+1) and P(n) in registers, K(n+2) in K buffer
@@ -636,12 +740,12 @@ __global__ __launch_bounds__(PP ? 512 : 256, PP ? 1 : 2) void attn_fwd_kernel(At
   PTile<PV> pa, pb;
   bool ha = true, hb = true;  // the rows' visibility flags of the chunks in sa, sb
   int n = v_lo;
-  int e_cur = load_e(chunk_of(n));
-  float ksn1 = load_ks(chunk_of(n + 1)), ksn2 = load_ks(chunk_of(n + 2));  // K scales of n+1, n+2
+  int e_cur = sg.load_e(chunk_of(n), lane);
+  float ksn1 = sg.load_ks(chunk_of(n + 1)), ksn2 = sg.load_ks(chunk_of(n + 2));  // K scales of n+1, n+2
   // Prologue: K(n) and V(n) in buffers 0, K(n+1) in K buffer 1; then S(n+1),
   // P(n) and K(n+2) in K buffer 0.
   {
-    const float ks0 = load_ks(chunk_of(n));
+    const float ks0 = sg.load_ks(chunk_of(n));
     dma_k(kL0, chunk_of(n));
     dma_v(vL0, chunk_of(n));
     dma_k(kL1, chunk_of(n + 1));
@@ -652,8 +756,8 @@ __global__ __launch_bounds__(PP ? 512 : 256, PP ? 1 : 2) void attn_fwd_kernel(At
       if (J >= 2) qk_chunk<D>(kL1, qv, lane, sa0, sa1);
       __syncthreads();  // every wave has read K(n) from buffer 0
       dma_k(kL0, chunk_of(n + 2));
-      hb = mask_chunk(n, sb0, sb1);
-      if (J >= 2) ha = mask_chunk(n + 1, sa0, sa1);
+      hb = mask_at(n, sb0, sb1);
+      if (J >= 2) ha = mask_at(n + 1, sa0, sa1);
       st.rescale(st.softmax(sb0, sb1, qsc * ks0, hb, pa));
       dma_wait();
       __syncthreads();
@@ -687,15 +791,15 @@ __global__ __launch_bounds__(PP ? 512 : 256, PP ? 1 : 2) void attn_fwd_kernel(At
     __builtin_amdgcn_sched_barrier(0);
     dma_k(k_wr, ch3);
     dma_v(v_wr, ch1);
-    const int e_nxt = load_e(ch1);
-    const float ks3 = load_ks(ch3);
+    const int e_nxt = sg.load_e(ch1, lane);
+    const float ks3 = sg.load_ks(ch3);
     float alpha;
     if constexpr (PP) {
       __builtin_amdgcn_s_setprio(1);
       qk_chunk<D>(k_rd, qv, lane, ns0, ns1);
       st.pv(p_cur, v_rd, e_cur, lane);
-      __builtin_amdgcn_sched_group_barrier(0x020, 2 + KI + VI, 0);  // the loads
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);            // the first operand reads
+      __builtin_amdgcn_sched_group_barrier(0x020, 2 + SG::KI + SG::VI, 0);  // the loads
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);                    // the first operand reads
 #pragma unroll
       for (int g = 0; g < NQK + NPV; ++g) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // one MFMA
@@ -713,8 +817,8 @@ __global__ __launch_bounds__(PP ? 512 : 256, PP ? 1 : 2) void attn_fwd_kernel(At
       qk_chunk<D>(k_rd, qv, lane, ns0, ns1);
       st.pv(p_cur, v_rd, e_cur, lane);
       alpha = st.softmax(cs0, cs1, c_mid, CHK ? has_c : true, p_nxt);
-      __builtin_amdgcn_sched_group_barrier(0x020, 2 + KI + VI, 0);  // the loads
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);            // the first operand reads
+      __builtin_amdgcn_sched_group_barrier(0x020, 2 + SG::KI + SG::VI, 0);  // the loads
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);                    // the first operand reads
 #pragma unroll
       for (int g = 0; g < NQK + NPV; ++g) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one MFMA
@@ -729,7 +833,7 @@ __global__ __launch_bounds__(PP ? 512 : 256, PP ? 1 : 2) void attn_fwd_kernel(At
     }
     st.rescale(alpha);  // rare: some row's running max moved (after P(n) V(n))
     if constexpr (CHK) {
-      if (n + 2 >= v_full) has_n = mask_chunk(n + 2, ns0, ns1);  // rare: S(n+2) is a boundary chunk
+      if (n + 2 >= v_full) has_n = mask_at(n + 2, ns0, ns1);  // rare: S(n+2) is a boundary chunk
     }
     if constexpr (SPARSE) {  // the next step's chunks, read from LDS ahead of the wait
       pre1 = chunk_of(n + 2);
@@ -747,7 +851,7 @@ __global__ __launch_bounds__(PP ? 512 : 256, PP ? 1 : 2) void attn_fwd_kernel(At
   if (J >= 1) {
     int left = J - 1;  // pipelined steps
     if (PP && grp == 1 && left > 0) __builtin_amdgcn_s_barrier();  // one phase behind group 0
-    if constexpr (!CACHE) {
+    if constexpr (MODE != KV_CACHE) {
       // the leading steps whose S(n+2) lies below v_full, in pairs
       for (int fast = min(J - 1, v_full - v_lo - 2); fast >= 2; fast -= 2) {
         step(P0{}, NoChk{}, sa0, sa1, ha, pa, sb0, sb1, hb, pb);
@@ -769,38 +873,8 @@ __global__ __launch_bounds__(PP ? 512 : 256, PP ? 1 : 2) void attn_fwd_kernel(At
       st.pv(pa, vL0, e_cur, lane);
     }
   }
-  v16f* o = st.o;
-  const float m = st.m;
-
-  // ---- epilogue: normalise, store
-  const float ltot = st.ls[0];  // already summed over both lane halves
   if (qi >= A.Nq) return;
-  if (A.splits == 1) {
-    const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;  // a row with no visible key: 0
-    uint16_t* orow = static_cast<uint16_t*>(A.o) + b * A.os_b + h * A.os_h + static_cast<int64_t>(qi) * A.os_n;
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int chn = 32 * cb + 8 * g + 4 * h2;
-        const uint32_t w0 = Pack16<DT>::pack(o[cb][4 * g] * inv, o[cb][4 * g + 1] * inv);
-        const uint32_t w1 = Pack16<DT>::pack(o[cb][4 * g + 2] * inv, o[cb][4 * g + 3] * inv);
-        *reinterpret_cast<uint2*>(orow + chn) = make_uint2(w0, w1);
-      }
-  } else {
-    const int64_t prow = (static_cast<int64_t>(split) * A.B * A.H + bh) * A.Nq_pad + qi;
-    const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
-    float* po = A.part_o + prow * D;
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int chn = 32 * cb + 8 * g + 4 * h2;
-        *reinterpret_cast<float4*>(po + chn) =
-            make_float4(o[cb][4 * g] * inv, o[cb][4 * g + 1] * inv, o[cb][4 * g + 2] * inv, o[cb][4 * g + 3] * inv);
-      }
-    if (h2 == 0) *reinterpret_cast<float2*>(A.part_ml + 2 * prow) = make_float2(m, ltot);
-  }
+  store_row<D, DT>(A, st.o, st.m, st.ls[0], b, h, bh, split, qi, h2);
 }
 
 // Merge split partials: O = sum_s w_s O_s / sum_s w_s with w_s = l_s 2^(m_s - M).
