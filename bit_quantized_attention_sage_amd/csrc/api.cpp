@@ -58,16 +58,15 @@ int tile_chunks(const Plan& p, int b, int t, int rows) {
 }
 
 // KV splits per query tile.  Work items (batch, head, split, tile) run as
-// rounds of SLOTS resident workgroups: 256-row ping-pong tiles one per CU,
-// or (block mask) 128-row tiles two per CU; either way a CU steps through
-// 8 waves' chunks at a time.  The estimated time of s splits is
+// rounds of SLOTS resident workgroups: 256-row ping-pong tiles, one per CU
+// (under a block mask each of its two 128-row blocks walks its own kept
+// chunks).  The estimated time of s splits is
 // ceil(items / SLOTS) x (mean chunks per item + a prologue and epilogue of
 // about 3 chunk steps), plus for s > 1 the combine pass (reads s fp32
 // partial outputs; one chunk step of a workgroup takes about 1.5 us at
 // d = 128, half that at d = 64).  Enough tiles for 4 rounds: no split.
 int choose_splits(const Plan& p) {
-  const bool pingpong = p.block_mask == nullptr;
-  const int SLOTS = pingpong ? 256 : 512, rows = pingpong ? 256 : 128;
+  const int SLOTS = 256, rows = 256;
   const int nqt = (p.Nq + rows - 1) / rows;
   const int64_t items1 = static_cast<int64_t>(p.B) * p.H * nqt;
   if (items1 >= 4 * SLOTS) return 1;

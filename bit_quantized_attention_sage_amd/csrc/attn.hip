@@ -13,20 +13,19 @@
 // Work decomposition.  Each wave owns 32 query rows.  Keys are streamed in
 // 64-key chunks (one K scale each) through LDS; per chunk a wave runs 8 i8
 // MFMAs 32x32x32 for S, the softmax on its 32x64 scores, and the P.V MFMAs.
-// Two shapes of workgroup, for one (b, h) and optionally one of several KV
-// splits:
-//  * ping-pong (contiguous keys, frame cache): 8 waves = two 128-row query
-//    blocks (two Q scales) sharing every staged K/V chunk.  Waves w and w+4
-//    sit on the same SIMD; group 0 (waves 0-3) runs one phase ahead of group 1,
-//    and each chunk step is two phases split by a barrier: the MFMAs, then the
-//    softmax.  So on every SIMD one wave's matrix work meets the other's
-//    vector work, which the hardware overlaps, instead of each wave
-//    interleaving both (measured on gfx950: one wave issues plain FP32 VALU
-//    ops every ~5 cycles, two every ~2.5; exp and the FP8 conversion take
-//    ~8.4 cycles per wave instruction either way).
-//  * 4 waves = one 128-row block (block-sparse tiles, whose kept chunks
-//    differ from block to block); each wave interleaves its own MFMAs and
-//    softmax.
+// A workgroup ("ping-pong") is 8 waves = two 128-row query blocks (two Q
+// scales) of one (b, h) and optionally one of several KV splits.  Waves w
+// and w+4 sit on the same SIMD; group 0 (waves 0-3) runs one phase ahead of
+// group 1, and each chunk step is two phases split by a barrier: the MFMAs,
+// then the softmax.  So on every SIMD one wave's matrix work meets the
+// other's vector work, which the hardware overlaps, instead of each wave
+// interleaving both (measured on gfx950: one wave issues plain FP32 VALU ops
+// every ~5 cycles, two every ~2.5; exp and the FP8 conversion take ~8.4
+// cycles per wave instruction either way).  On contiguous keys and over a
+// frame cache the two blocks share every staged K/V chunk (group 0 stages
+// them); under a block mask each block walks its own kept chunks, staged by
+// its own group into its own buffers, for as many steps as the longer list
+// has (the shorter list's missing entries are masked out).
 //
 // Register layouts (32x32 MFMA, lane l, h2 = l / 32, r32 = l % 32):
 //  * S^T = K Q^T: the B operand is Q^T, so lane l holds query r32 and channel
@@ -398,6 +397,12 @@ struct WorkList {
       return v < a0 ? v : b1 + (v - a0);
     }
   }
+  // block mask: the list entry of v (clamped like chunk_of) as a vector
+  // register, for a read issued well before its value is needed
+  __device__ __forceinline__ int entry_of(int v) const {
+    const int e = slist[max(min(v, v_hi - 1), v_lo)];  // (an empty list reads entry 0, unused)
+    return v_hi > v_lo ? e : 0;
+  }
   // frame of cache chunk ch: ch / (FS/64) by a multiply-high with the host's
   // rounded-up reciprocal (exact for ch < 2^20, FS/64 < 2^11); with one chunk
   // per frame the reciprocal (2^32) does not fit and f = ch
@@ -458,8 +463,11 @@ __device__ __forceinline__ WorkList<MODE> make_worklist(const AttnArgs& A, int b
       const int lane = tid & 63, w = tid >> 6;
       const int nfull = first_end / 64;
       const uint8_t* mrow = A.block_mask + (static_cast<int64_t>(bh) * A.nqt + mask_tile) * A.mask_nkc;
+      // (the loop runs to the split's end, the same for every thread of the
+      // workgroup: its barriers are the workgroup's)
+      const int split_hi = (split + 1) * nch / A.splits;
       int total = 0, below = 0;
-      for (int c0 = L.v_lo; c0 < L.v_hi; c0 += NT) {
+      for (int c0 = L.v_lo; c0 < split_hi; c0 += NT) {
         const int c = c0 + tid;
         const bool keep = c < L.v_hi && mrow[c] != 0;
         const uint64_t bk = __ballot(keep), bf = __ballot(keep && c < nfull);
@@ -520,8 +528,9 @@ __device__ __forceinline__ WorkList<MODE> make_worklist(const AttnArgs& A, int b
 }
 
 // Staging of K and V^T chunks from HBM straight into LDS: raw buffer loads
-// that write LDS (no registers), issued by the four waves 0-3.  Lane l of DMA
-// instruction i of wave w fills LDS granule (4i + w)*64 + l of the buffer;
+// that write LDS (no registers), issued by the four waves of one group.
+// Lane l of DMA instruction i of the group's wave w fills LDS granule
+// (4i + w)*64 + l of the buffer;
 // its global source is chosen so that the buffer ends up in the swizzled
 // layouts above.  Every chunk index is clamped to the head's last padded
 // chunk, so all reads stay inside the head's slice; the prefetches that the
@@ -652,6 +661,12 @@ __device__ __forceinline__ void store_row(const AttnArgs& A, const v16f* o, floa
 template <int D, int PV, int DT, int MODE>
 __device__ __forceinline__ bool mask_chunk(const WorkList<MODE>& wl, WaveState<D, PV, DT>& st, int v, v16i& s0,
                                            v16i& s1, int h2) {
+  if constexpr (MODE == KV_SPARSE) {
+    if (v >= wl.v_hi) {  // past this block's list (the pair's other list is longer)
+      st.mask(s0, s1, -64);
+      return false;
+    }
+  }
   const int ch = wl.chunk_of(v);
   if (wl.chunk_full(ch)) return true;
   asm volatile("");  // keep this a real branch
@@ -660,42 +675,67 @@ __device__ __forceinline__ bool mask_chunk(const WorkList<MODE>& wl, WaveState<D
   return lim > 0;
 }
 
-template <int D, int PV, int DT, int MODE, bool PP>
-__global__ __launch_bounds__(PP ? 512 : 256, PP ? 1 : 2) void attn_fwd_kernel(AttnArgs A) {
+template <int D, int PV, int DT, int MODE>
+__global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs A) {
   constexpr bool SPARSE = MODE == KV_SPARSE;
-  static_assert(!(PP && SPARSE), "the two query blocks of a ping-pong tile share one chunk list");
-  constexpr int NWAVE = PP ? 8 : 4;
+  constexpr int NWAVE = 8;
   constexpr int NCB = D / 32;                    // 32-channel blocks of O
+  // Under a block mask each 128-row Q block keeps its own chunks: a ping-pong
+  // workgroup then holds two chunk lists, and each group stages its own
+  // list's chunks into its own buffers.
+  constexpr int NLIST = SPARSE ? 2 : 1;
   using SG = Stager<D, PV>;
-  // Two buffers each, as separate objects so that the compiler can tell the
-  // buffer being filled by DMA from the one being read.
-  __shared__ __attribute__((aligned(16))) int8_t kL0[SG::KB];
-  __shared__ __attribute__((aligned(16))) int8_t kL1[SG::KB];
-  __shared__ __attribute__((aligned(16))) uint8_t vL0[SG::VBC];
-  __shared__ __attribute__((aligned(16))) uint8_t vL1[SG::VBC];
-  __shared__ uint16_t slist[SPARSE ? MAX_LIST : 1];  // kept chunks of the tile, ascending
+  // Two buffers each (per list), as separate objects so that the compiler can
+  // tell the buffer being filled by DMA from the one being read.
+  __shared__ __attribute__((aligned(16))) int8_t kLs0[NLIST * SG::KB];
+  __shared__ __attribute__((aligned(16))) int8_t kLs1[NLIST * SG::KB];
+  __shared__ __attribute__((aligned(16))) uint8_t vLs0[NLIST * SG::VBC];
+  __shared__ __attribute__((aligned(16))) uint8_t vLs1[NLIST * SG::VBC];
+  __shared__ uint16_t slist[SPARSE ? NLIST * MAX_LIST : 1];  // kept chunks of each list, ascending
   __shared__ int scnt[2 * NWAVE];
+  __shared__ int slen[2 * NLIST];  // block mask + ping-pong: each list's length and fully visible prefix
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h2 = lane >> 5;
 
-  const int ntile = PP ? (A.nqt + 1) / 2 : A.nqt;  // tiles of NWAVE * 32 rows
+  const int ntile = (A.nqt + 1) / 2;  // tiles of two 128-row Q blocks
   const Item it(A, ntile);
   const int b = it.b, h = it.h, split = it.split, qt = it.qt, bh = it.bh;
   // this wave's group, its place in the group and its 128-row Q block (the
   // second block of the last tile may lie past Nq: its rows load the last
   // real block and store nothing)
-  const int grp = PP ? (w >> 2) : 0, w4 = w & 3;
-  const int qb = PP ? 2 * qt + grp : qt;
+  const int grp = w >> 2, w4 = w & 3;
+  const int qb = 2 * qt + grp;
   const int qbl = min(qb, A.nqt - 1);
   const int qi = qb * BQ + w4 * 32 + (lane & 31);
   const int qi_valid = min(qi, A.Nq - 1);
-  const int row_first = (PP ? 2 * qt : qt) * BQ, row_last = min(row_first + NWAVE * 32, A.Nq) - 1;
-  const WorkList<MODE> wl = make_worklist<MODE, NWAVE * 64>(A, b, bh, qt, split, row_first, row_last, qi_valid,
-                                                            tid, slist, scnt);
-  const int v_lo = wl.v_lo, v_hi = wl.v_hi, v_full = wl.v_full;
-  const int J = max(0, v_hi - v_lo);  // chunks of this work item
+  const int lst = NLIST > 1 ? grp : 0;  // this wave's list
+  int8_t* const kL0 = kLs0 + lst * SG::KB;
+  int8_t* const kL1 = kLs1 + lst * SG::KB;
+  uint8_t* const vL0 = vLs0 + lst * SG::VBC;
+  uint8_t* const vL1 = vLs1 + lst * SG::VBC;
+  const int row_first = (NLIST > 1 ? qbl : 2 * qt) * BQ;
+  const int row_last = min(row_first + (NLIST > 1 ? BQ : NWAVE * 32), A.Nq) - 1;
+  const WorkList<MODE> wl =
+      NLIST > 1 ? make_worklist<MODE, 256>(A, b, bh, qbl, split, row_first, row_last, qi_valid, tid & 255,
+                                           slist + lst * MAX_LIST, scnt + 8 * lst)
+                : make_worklist<MODE, NWAVE * 64>(A, b, bh, qt, split, row_first, row_last, qi_valid, tid, slist,
+                                                  scnt);
+  const int v_lo = wl.v_lo;
+  // The loop's trip counts are the workgroup's (its barriers are shared):
+  // with two lists, the longer list's length and the shorter fully visible
+  // prefix; the shorter list's missing entries are masked out.
+  int J = max(0, wl.v_hi - v_lo), v_full = wl.v_full;
+  if constexpr (NLIST > 1) {
+    if (tid == 256 * lst) {
+      slen[lst] = J;
+      slen[2 + lst] = v_full;
+    }
+    __syncthreads();
+    J = max(slen[0], slen[1]);
+    v_full = min(slen[2], slen[3]);
+  }
 
   v4i qv[D / 32];
   load_q<D>(qv, A.qc + (static_cast<int64_t>(bh) * A.Nq_pad + qbl * BQ + w4 * 32 + (lane & 31)) * D, h2);
@@ -715,7 +755,8 @@ __global__ __launch_bounds__(PP ? 512 : 256, PP ? 1 : 2) void attn_fwd_kernel(At
 
   SG sg;
   sg.init(A, bh, w, lane);
-  const bool stager = !(PP && grp != 0);  // group 0 (ping-pong) or every wave stages the chunks
+  // group 0 stages the chunks of a shared list, each group those of its own
+  const bool stager = NLIST > 1 || grp == 0;
   auto dma_k = [&](int8_t* dst, int ch) { if (stager) sg.dma_k(dst, ch); };
   auto dma_v = [&](uint8_t* dst, int ch) { if (stager) sg.dma_v(dst, ch); };
   auto chunk_of = [&](int v) { return wl.chunk_of(v); };
@@ -723,17 +764,16 @@ __global__ __launch_bounds__(PP ? 512 : 256, PP ? 1 : 2) void attn_fwd_kernel(At
 
   // Software pipeline within each wave over three chunks: step j (list entry
   // n = v_lo + j) enters with S(n+1) and P(n) in registers, K(n+2) in K buffer
-  // j&1 and V(n) in V buffer j&1.  One straight-line region issues the DMA of
-  // K(n+3) and V(n+1), the S MFMAs of entry n+2, the P.V MFMAs of entry n and
-  // the softmax of entry n+1, so the matrix cores and the vector ALUs work
-  // side by side; then the (rare) rescale by entry n+1's alpha, the (rare)
-  // masking of S(n+2), the wait for this step's DMA and the barrier.
-  // Ping-pong: the region is two phases instead, the MFMAs (at raised wave
-  // priority, with the operand reads 8 ahead) and, after a barrier, the
-  // softmax; group 1 runs the same steps one phase behind group 0 (one extra
-  // barrier before its first step, group 0 one after its last), so the
-  // buffers a step fills are the ones both groups finished reading in the
-  // step before.
+  // j&1 and V(n) in V buffer j&1.  It issues the DMA of K(n+3) and V(n+1),
+  // then two phases split by a barrier: the S MFMAs of entry n+2 and the P.V
+  // MFMAs of entry n (at raised wave priority, with the operand reads 8
+  // ahead), and the softmax of entry n+1; then the (rare) rescale by entry
+  // n+1's alpha, the (rare) masking of S(n+2), the wait for this step's DMA
+  // and the barrier.  Group 1 runs the same steps one phase behind group 0
+  // (one extra barrier before its first step, group 0 one after its last),
+  // so on every SIMD one wave's matrix work meets the other wave's softmax,
+  // and the buffers a step fills are the ones their readers finished with in
+  // the step before.
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
   v16i sa0{}, sa1{}, sb0{}, sb1{};
@@ -785,7 +825,6 @@ __global__ __launch_bounds__(PP ? 512 : 256, PP ? 1 : 2) void attn_fwd_kernel(At
     constexpr int NQK = 2 * D / 32;                               // S MFMAs
     constexpr int NPV = (PV == PVFP8) ? NCB + 1 : 4 * NCB + 4;    // P.V and row-sum MFMAs
     constexpr int NRD = NQK + ((PV == PVFP8) ? 2 * NCB : 4 * NCB);  // LDS operand reads
-    constexpr int VPER = (PV == PVFP8) ? 12 : 5;                  // softmax slice per MFMA
     const float c_mid = qsc * ksn1;
     const int ch1 = SPARSE ? pre1 : chunk_of(n + 1), ch3 = SPARSE ? pre3 : chunk_of(n + 3);
     __builtin_amdgcn_sched_barrier(0);
@@ -794,50 +833,34 @@ __global__ __launch_bounds__(PP ? 512 : 256, PP ? 1 : 2) void attn_fwd_kernel(At
     const int e_nxt = sg.load_e(ch1, lane);
     const float ks3 = sg.load_ks(ch3);
     float alpha;
-    if constexpr (PP) {
-      __builtin_amdgcn_s_setprio(1);
-      qk_chunk<D>(k_rd, qv, lane, ns0, ns1);
-      st.pv(p_cur, v_rd, e_cur, lane);
-      __builtin_amdgcn_sched_group_barrier(0x020, 2 + SG::KI + SG::VI, 0);  // the loads
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);                    // the first operand reads
+    __builtin_amdgcn_s_setprio(1);
+    qk_chunk<D>(k_rd, qv, lane, ns0, ns1);
+    st.pv(p_cur, v_rd, e_cur, lane);
+    __builtin_amdgcn_sched_group_barrier(0x020, 2 + SG::KI + SG::VI, 0);  // the loads
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);                    // the first operand reads
 #pragma unroll
-      for (int g = 0; g < NQK + NPV; ++g) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // one MFMA
-        if (g + 8 < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // the next read
-      }
-      asm volatile("" : "+v"(ns0), "+v"(ns1));
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_setprio(0);
-      __builtin_amdgcn_s_barrier();  // end of the MFMA phase
-      __builtin_amdgcn_sched_barrier(0);
-      alpha = st.softmax(cs0, cs1, c_mid, CHK ? has_c : true, p_nxt);
-      p_nxt.pin();
-      __builtin_amdgcn_sched_barrier(0);
-    } else {
-      qk_chunk<D>(k_rd, qv, lane, ns0, ns1);
-      st.pv(p_cur, v_rd, e_cur, lane);
-      alpha = st.softmax(cs0, cs1, c_mid, CHK ? has_c : true, p_nxt);
-      __builtin_amdgcn_sched_group_barrier(0x020, 2 + SG::KI + SG::VI, 0);  // the loads
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);                    // the first operand reads
-#pragma unroll
-      for (int g = 0; g < NQK + NPV; ++g) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, VPER, 0);  // a slice of the softmax
-        if (g + 4 < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // the next read
-      }
-      // Pin the region's results here so that no earlier pass moves the S
-      // MFMAs or the softmax out of it.
-      asm volatile("" : "+v"(ns0), "+v"(ns1));
-      p_nxt.pin();
-      __builtin_amdgcn_sched_barrier(0);
+    for (int g = 0; g < NQK + NPV; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // one MFMA
+      if (g + 8 < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // the next read
+    }
+    asm volatile("" : "+v"(ns0), "+v"(ns1));
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_s_barrier();  // end of the MFMA phase
+    __builtin_amdgcn_sched_barrier(0);
+    // block mask: the next step's chunks, read from LDS here and moved to
+    // scalar registers after the softmax, which hides the read's latency
+    const int e1 = SPARSE ? wl.entry_of(n + 2) : 0, e3 = SPARSE ? wl.entry_of(n + 4) : 0;
+    alpha = st.softmax(cs0, cs1, c_mid, CHK ? has_c : true, p_nxt);
+    p_nxt.pin();
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (SPARSE) {
+      pre1 = __builtin_amdgcn_readfirstlane(e1);
+      pre3 = __builtin_amdgcn_readfirstlane(e3);
     }
     st.rescale(alpha);  // rare: some row's running max moved (after P(n) V(n))
     if constexpr (CHK) {
       if (n + 2 >= v_full) has_n = mask_at(n + 2, ns0, ns1);  // rare: S(n+2) is a boundary chunk
-    }
-    if constexpr (SPARSE) {  // the next step's chunks, read from LDS ahead of the wait
-      pre1 = chunk_of(n + 2);
-      pre3 = chunk_of(n + 4);
     }
     dma_wait();
     __syncthreads();
@@ -850,7 +873,7 @@ __global__ __launch_bounds__(PP ? 512 : 256, PP ? 1 : 2) void attn_fwd_kernel(At
   using Chk = std::integral_constant<bool, true>;
   if (J >= 1) {
     int left = J - 1;  // pipelined steps
-    if (PP && grp == 1 && left > 0) __builtin_amdgcn_s_barrier();  // one phase behind group 0
+    if (grp == 1 && left > 0) __builtin_amdgcn_s_barrier();  // one phase behind group 0
     if constexpr (MODE != KV_CACHE) {
       // the leading steps whose S(n+2) lies below v_full, in pairs
       for (int fast = min(J - 1, v_full - v_lo - 2); fast >= 2; fast -= 2) {
@@ -864,7 +887,7 @@ __global__ __launch_bounds__(PP ? 512 : 256, PP ? 1 : 2) void attn_fwd_kernel(At
       step(P1{}, Chk{}, sb0, sb1, hb, pb, sa0, sa1, ha, pa);
       left -= 2;
     }
-    if (PP && grp == 0 && J > 1) __builtin_amdgcn_s_barrier();  // as many barriers as group 1
+    if (grp == 0 && J > 1) __builtin_amdgcn_s_barrier();  // as many barriers as group 1
     // the last entry's P.V (its V is in buffer (J-1)&1)
     if (left == 1) {
       step(P0{}, Chk{}, sa0, sa1, ha, pa, sb0, sb1, hb, pb);
@@ -991,9 +1014,8 @@ static AttnArgs make_args(const AttnLaunch& L) {
   A.Nkv_pad = L.Nkv_pad;
   A.nqt = L.Nq_pad / BQ;
   A.splits = L.splits;
-  // work items: 256-row tiles for the ping-pong shape (no block mask), else
-  // 128-row blocks
-  A.total = L.B * L.H * L.splits * (L.block_mask ? A.nqt : (A.nqt + 1) / 2);
+  // work items: 256-row tiles of the ping-pong workgroup
+  A.total = L.B * L.H * L.splits * ((A.nqt + 1) / 2);
   A.sigma = L.sigma;
   A.frame_len = L.frame_len;
   A.frame_stride = L.frame_stride;
@@ -1011,11 +1033,11 @@ template <int D, int PV, int DT>
 static hipError_t attn_impl(const AttnLaunch& L, hipStream_t st) {
   const AttnArgs A = make_args(L);
   if (L.block_mask)
-    hipLaunchKernelGGL((attn_fwd_kernel<D, PV, DT, KV_SPARSE, false>), dim3(A.total), dim3(256), 0, st, A);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, PV, DT, KV_SPARSE>), dim3(A.total), dim3(512), 0, st, A);
   else if (L.frame_stride > 0)
-    hipLaunchKernelGGL((attn_fwd_kernel<D, PV, DT, KV_CACHE, true>), dim3(A.total), dim3(512), 0, st, A);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, PV, DT, KV_CACHE>), dim3(A.total), dim3(512), 0, st, A);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<D, PV, DT, KV_DENSE, true>), dim3(A.total), dim3(512), 0, st, A);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, PV, DT, KV_DENSE>), dim3(A.total), dim3(512), 0, st, A);
   if (L.splits > 1) {
     const int64_t threads = static_cast<int64_t>(L.B) * L.H * L.Nq_pad * (D / 4);
     hipLaunchKernelGGL((attn_combine_kernel<D, DT>), dim3(static_cast<unsigned>((threads + 255) / 256)),

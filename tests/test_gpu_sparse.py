@@ -120,6 +120,38 @@ def test_rows_whose_kept_blocks_lie_in_later_frames(lib, pv_mode, splits):
     assert_close(og, o64, aux, "bf16", pv_mode, nsplit)
 
 
+@pytest.mark.parametrize("pv_mode", [PV_16, PV_FP8], ids=["pv16", "pvfp8"])
+def test_paired_blocks_with_lists_of_different_lengths(lib, pv_mode):
+    """One workgroup walks two query blocks, each over its own kept key
+    blocks, for as many steps as the longer list has.  Head 0: block 0 keeps
+    every key block, block 1 none (its rows output 0); head 1 the other way
+    round; head 2: block 0 keeps one key block, block 1 all but one; head 3:
+    the last block (rows 256-299) alone in its pair."""
+    B, H, Nq, Nkv, d, dt = 1, 4, 300, 1000, 128, torch.bfloat16
+    print(f"sparse paired lists pv {pv_mode}", flush=True)
+    q = _rand((B, H, Nq, d), dt, 710 + pv_mode)
+    k = _rand((B, H, Nkv, d), dt, 711, offset=0.7)
+    v = _rand((B, H, Nkv, d), dt, 712)
+    M = np.zeros((B, H, 3, 16), dtype=np.uint8)
+    M[0, 0, 0, :] = 1
+    M[0, 1, 1, :] = 1
+    M[0, 2, 0, 5] = 1
+    M[0, 2, 1, :] = 1
+    M[0, 2, 1, 9] = 0
+    M[0, 3, 2, ::3] = 1
+    o, desc = _run(q.cuda(), k.cuda(), v.cuda(), pv_mode, M)
+    nsplit = sage.sage_attn_kv_splits(desc)
+    Q, K, V = host(q), host(k), host(v)
+    o64, aux = _emulate(Q, K, V, pv_mode, "bf16", M, nsplit)
+    og = host(o)
+    assert np.isfinite(og).all()
+    assert not og[0, 0, 128:256].any() and not og[0, 1, :128].any() and not og[0, 3, :256].any()
+    assert og[0, 0, :128].any(axis=-1).all() and og[0, 1, 128:256].any(axis=-1).all()
+    assert og[0, 2, :256].any(axis=-1).all() and og[0, 3, 256:].any(axis=-1).all()
+    print(f"  splits {nsplit}", flush=True)
+    assert_close(og, o64, aux, "bf16", pv_mode, nsplit)
+
+
 @pytest.mark.parametrize("pv_mode", [PV_16, PV_FP8])
 def test_all_kept_mask_equals_dense(lib, pv_mode):
     """With every tile kept and one work item per tile, the sparse launch

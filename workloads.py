@@ -27,8 +27,9 @@ stand in for them, with the token grids of such clips:
            query sees 18 frames (36720 keys).  The pages give no window
            length; 16 frames matches the stream workload's history.
   sparse   the large workload with a block mask over its (128-query,
-           64-key) tiles keeping a seeded 25% of each query tile's key
-           blocks, drawn independently per (head, query tile) -- a stand-in
+           64-key) tiles keeping exactly 25% of each query tile's key
+           blocks (296 of 1182), drawn uniformly and independently per
+           (head, query tile) -- a stand-in
            for the sparse branch of sparse attention built on SageAttention
            (Vidu S1 blog, section "Infra"), whose predictor the pages do not
            give.
@@ -194,15 +195,23 @@ _MASKS = {}
 
 
 def block_mask(w):
-    """The workload's block mask: uint8 numpy [B, H, ceil(Nq/128), ceil(Nkv/64)],
-    each tile kept with probability block_density (seeded; None without one)."""
+    """The workload's block mask: uint8 numpy [B, H, ceil(Nq/128), ceil(Nkv/64)]
+    that keeps, for every (batch, head, query tile), exactly
+    round(block_density * ceil(Nkv/64)) key blocks chosen uniformly without
+    replacement (seeded; None without a density) -- a fixed share per query
+    tile, as a top-k block selection keeps."""
     if not w.block_density:
         return None
     key = (w.seed, w.B, w.H, w.Nq, w.Nkv, w.block_density)
     if key not in _MASKS:
         rng = np.random.default_rng(w.seed * 7 + 3)
         shape = (w.B, w.H, -(-w.Nq // 128), -(-w.Nkv // 64))
-        _MASKS[key] = (rng.random(shape, dtype=np.float32) < w.block_density).astype(np.uint8)
+        keep = int(round(w.block_density * shape[-1]))
+        r = rng.random(shape, dtype=np.float32)
+        m = np.zeros(shape, dtype=np.uint8)
+        if keep > 0:
+            np.put_along_axis(m, np.argpartition(r, keep - 1, axis=-1)[..., :keep], 1, axis=-1)
+        _MASKS[key] = m
     return _MASKS[key]
 
 
