@@ -229,6 +229,7 @@ struct WaveState {
   // sums of the rounded P are taken on the matrix cores in pv().
   // `has`: this row has a visible key in the chunk (rows without one keep m).
   float xc_, xk_;  // c 2^26 and -mref of the chunk being converted
+  bool moved_;     // some row of the wave adopted a new maximum in the last softmax
 
   __device__ __forceinline__ float softmax_head(const v16i& s0, const v16i& s1, float c, bool has,
                                                 PTile<PV>& P) {
@@ -244,9 +245,14 @@ struct WaveState {
       const auto sw = __builtin_amdgcn_permlane32_swap(mx, mx, false, false);
       mx = max(static_cast<int>(sw[0]), static_cast<int>(sw[1]));
     }
-    const float tm = static_cast<float>(mx - SBIAS) * c;
-    const bool upd = has && (tm > m + TAU);
-    const float alpha = upd ? __builtin_amdgcn_exp2f(m - tm) : 1.0f;
+    // tm = fp32(S c), m + TAU and m - tm each rounded on their own, as the
+    // scheme defines them (the _rn forms keep the compiler from fusing them)
+    const float tm = __fmul_rn(static_cast<float>(mx - SBIAS), c);
+    const bool upd = has && (tm > __fadd_rn(m, TAU));
+    // (a ballot here, long before the rescale test reads it: a test on a
+    // compare issued after the softmax would wait for the whole softmax)
+    moved_ = __ballot(upd) != 0;
+    const float alpha = upd ? __builtin_amdgcn_exp2f(__fsub_rn(m, tm)) : 1.0f;
     m = upd ? tm : m;
     xk_ = -(m - static_cast<float>(SHIFT));
     // c 2^26, exact; a zero scale (all-zero Q or K block: every score 0)
@@ -283,8 +289,9 @@ struct WaveState {
     }
   }
 
+  // O and l times alpha, when some row moved (alpha is 1 for the others)
   __device__ __forceinline__ void rescale(float alpha) {
-    if (__any(alpha != 1.0f)) {
+    if (moved_) {
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
@@ -654,25 +661,33 @@ __device__ __forceinline__ void store_row(const AttnArgs& A, const v16f* o, floa
   }
 }
 
-// Masking of a chunk whose scores are in (s0, s1): taken only at boundaries
-// (the last chunks of a row's range, frame padding, window edges); keys a
-// row does not see get the MASKED score.  Returns whether this row has a
-// visible key in the chunk.
+// Masking at boundaries (the last chunks of a row's range, frame padding,
+// window edges, entries past the shorter list of a block-mask pair), in two
+// parts.  needs_mask: whether list entry v needs masking for some row of the
+// workgroup (wave-uniform, scalar work).  apply_mask: keys a row does not see
+// get the MASKED score; returns whether this row has a visible key in the
+// chunk.
+// (ch: the chunk of entry v)
+template <int MODE>
+__device__ __forceinline__ bool needs_mask(const WorkList<MODE>& wl, int v, int ch) {
+  if constexpr (MODE == KV_SPARSE) {
+    if (v >= wl.v_hi) return true;  // past this block's list (the pair's other list is longer)
+  }
+  return !wl.chunk_full(ch);
+}
+template <int D, int PV, int DT, int MODE>
+__device__ __forceinline__ bool apply_mask(const WorkList<MODE>& wl, WaveState<D, PV, DT>& st, int v, v16i& s0,
+                                           v16i& s1, int h2) {
+  const int lim = (MODE == KV_SPARSE && v >= wl.v_hi) ? 0 : wl.row_lim(wl.chunk_of(v));
+  st.mask(s0, s1, lim - 16 * h2);
+  return lim > 0;
+}
 template <int D, int PV, int DT, int MODE>
 __device__ __forceinline__ bool mask_chunk(const WorkList<MODE>& wl, WaveState<D, PV, DT>& st, int v, v16i& s0,
                                            v16i& s1, int h2) {
-  if constexpr (MODE == KV_SPARSE) {
-    if (v >= wl.v_hi) {  // past this block's list (the pair's other list is longer)
-      st.mask(s0, s1, -64);
-      return false;
-    }
-  }
-  const int ch = wl.chunk_of(v);
-  if (wl.chunk_full(ch)) return true;
+  if (!needs_mask(wl, v, wl.chunk_of(v))) return true;
   asm volatile("");  // keep this a real branch
-  const int lim = wl.row_lim(ch);
-  st.mask(s0, s1, lim - 16 * h2);
-  return lim > 0;
+  return apply_mask(wl, st, v, s0, s1, h2);
 }
 
 template <int D, int PV, int DT, int MODE>
@@ -778,7 +793,8 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs A) {
   using P1 = std::integral_constant<int, 1>;
   v16i sa0{}, sa1{}, sb0{}, sb1{};
   PTile<PV> pa, pb;
-  bool ha = true, hb = true;  // the rows' visibility flags of the chunks in sa, sb
+  bool ha = true, hb = true;    // the rows' visibility flags of the chunks in sa, sb
+  bool na = false, nb = false;  // the chunks in sa, sb still need masking (decided a step ahead)
   int n = v_lo;
   int e_cur = sg.load_e(chunk_of(n), lane);
   float ksn1 = sg.load_ks(chunk_of(n + 1)), ksn2 = sg.load_ks(chunk_of(n + 2));  // K scales of n+1, n+2
@@ -814,8 +830,8 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs A) {
 
   // CHK false: S(n+1) and S(n+2) are visible in full to every row (no masking
   // check, every row has keys in entry n+1).
-  auto step = [&](auto par, auto chk, v16i& cs0, v16i& cs1, bool& has_c, PTile<PV>& p_cur, v16i& ns0,
-                  v16i& ns1, bool& has_n, PTile<PV>& p_nxt) {
+  auto step = [&](auto par, auto chk, v16i& cs0, v16i& cs1, bool& has_c, bool& nd_c, PTile<PV>& p_cur,
+                  v16i& ns0, v16i& ns1, bool& has_n, bool& nd_n, PTile<PV>& p_nxt) {
     constexpr int P = decltype(par)::value;  // parity of the step
     constexpr bool CHK = decltype(chk)::value;
     int8_t* k_rd = P ? kL1 : kL0;            // K(n+2)
@@ -827,6 +843,14 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs A) {
     constexpr int NRD = NQK + ((PV == PVFP8) ? 2 * NCB : 4 * NCB);  // LDS operand reads
     const float c_mid = qsc * ksn1;
     const int ch1 = SPARSE ? pre1 : chunk_of(n + 1), ch3 = SPARSE ? pre3 : chunk_of(n + 3);
+    // S(n+2) a boundary chunk?  Scalar work, placed in the phase that has
+    // room for it: the MFMA phase in FP8 mode (its softmax phase is the longer
+    // one), after the softmax with 16-bit P.V (the other way round).
+    constexpr bool DECIDE_EARLY = PV == PVFP8 && !SPARSE;
+    if constexpr (CHK && DECIDE_EARLY) {
+      nd_n = n + 2 >= v_full && needs_mask(wl, n + 2, chunk_of(n + 2));
+      has_n = true;
+    }
     __builtin_amdgcn_sched_barrier(0);
     dma_k(k_wr, ch3);
     dma_v(v_wr, ch1);
@@ -851,6 +875,12 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs A) {
     // block mask: the next step's chunks, read from LDS here and moved to
     // scalar registers after the softmax, which hides the read's latency
     const int e1 = SPARSE ? wl.entry_of(n + 2) : 0, e3 = SPARSE ? wl.entry_of(n + 4) : 0;
+    if constexpr (CHK) {
+      if (nd_c) {  // rare: entry n+1 is a boundary chunk
+        asm volatile("");  // keep this a real branch
+        has_c = apply_mask(wl, st, n + 1, cs0, cs1, h2);
+      }
+    }
     alpha = st.softmax(cs0, cs1, c_mid, CHK ? has_c : true, p_nxt);
     p_nxt.pin();
     __builtin_amdgcn_sched_barrier(0);
@@ -858,10 +888,11 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs A) {
       pre1 = __builtin_amdgcn_readfirstlane(e1);
       pre3 = __builtin_amdgcn_readfirstlane(e3);
     }
-    st.rescale(alpha);  // rare: some row's running max moved (after P(n) V(n))
-    if constexpr (CHK) {
-      if (n + 2 >= v_full) has_n = mask_at(n + 2, ns0, ns1);  // rare: S(n+2) is a boundary chunk
+    if constexpr (CHK && !DECIDE_EARLY) {  // (block mask: the chunk of entry n+2 is pre1)
+      nd_n = n + 2 >= v_full && needs_mask(wl, n + 2, SPARSE ? pre1 : chunk_of(n + 2));
+      has_n = true;
     }
+    st.rescale(alpha);  // rare: some row's running max moved (after P(n) V(n))
     dma_wait();
     __syncthreads();
     e_cur = e_nxt;
@@ -877,20 +908,20 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs A) {
     if constexpr (MODE != KV_CACHE) {
       // the leading steps whose S(n+2) lies below v_full, in pairs
       for (int fast = min(J - 1, v_full - v_lo - 2); fast >= 2; fast -= 2) {
-        step(P0{}, NoChk{}, sa0, sa1, ha, pa, sb0, sb1, hb, pb);
-        step(P1{}, NoChk{}, sb0, sb1, hb, pb, sa0, sa1, ha, pa);
+        step(P0{}, NoChk{}, sa0, sa1, ha, na, pa, sb0, sb1, hb, nb, pb);
+        step(P1{}, NoChk{}, sb0, sb1, hb, nb, pb, sa0, sa1, ha, na, pa);
         left -= 2;
       }
     }
     while (left >= 2) {
-      step(P0{}, Chk{}, sa0, sa1, ha, pa, sb0, sb1, hb, pb);
-      step(P1{}, Chk{}, sb0, sb1, hb, pb, sa0, sa1, ha, pa);
+      step(P0{}, Chk{}, sa0, sa1, ha, na, pa, sb0, sb1, hb, nb, pb);
+      step(P1{}, Chk{}, sb0, sb1, hb, nb, pb, sa0, sa1, ha, na, pa);
       left -= 2;
     }
     if (grp == 0 && J > 1) __builtin_amdgcn_s_barrier();  // as many barriers as group 1
     // the last entry's P.V (its V is in buffer (J-1)&1)
     if (left == 1) {
-      step(P0{}, Chk{}, sa0, sa1, ha, pa, sb0, sb1, hb, pb);
+      step(P0{}, Chk{}, sa0, sa1, ha, na, pa, sb0, sb1, hb, nb, pb);
       st.pv(pb, vL1, e_cur, lane);
     } else {
       st.pv(pa, vL0, e_cur, lane);
