@@ -31,10 +31,17 @@
 // dequantization into the float32 sums, and waves 4-7 run one phase behind
 // waves 0-3, so on every SIMD one wave's MFMAs overlap the other's VALU work
 // (one wave alone issues FP32 VALU ops only every ~5 cycles, and its own
-// MFMAs hide little of it).  Waves 0-3 alone stage the tiles, one DMA
-// instruction behind each of their MFMAs (issued all at once they stalled
-// the phase by ~600 cycles); the buffer a block fills was read by both
-// groups in the block before.
+// MFMAs hide little of it).
+//
+// Staging.  Three buffers per tile: while the MFMAs of block kb read buffer
+// kb % 3, every wave stages its share of block kb + 2 (6 DMA instructions,
+// one behind each of its first MFMAs) into buffer (kb + 2) % 3, which both
+// groups finished reading in block kb - 1.  A wave waits for its DMA of
+// block kb + 1 at the barrier that ends its own MFMA phase of block kb, which
+// is before either group's first read of block kb + 1; the DMA of block
+// kb + 2 stays in flight.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -154,10 +161,14 @@ struct GemmArgs {
 
 template <int DT>
 __global__ __launch_bounds__(512, 1) void w8a8_gemm_kernel(GemmArgs A) {
+  // (separate objects, so that the compiler can tell the buffer being filled
+  // by DMA from the ones being read)
   __shared__ __attribute__((aligned(16))) int8_t xL0[XB];
   __shared__ __attribute__((aligned(16))) int8_t xL1[XB];
+  __shared__ __attribute__((aligned(16))) int8_t xL2[XB];
   __shared__ __attribute__((aligned(16))) int8_t wL0[WB];
   __shared__ __attribute__((aligned(16))) int8_t wL1[WB];
+  __shared__ __attribute__((aligned(16))) int8_t wL2[WB];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -177,8 +188,8 @@ __global__ __launch_bounds__(512, 1) void w8a8_gemm_kernel(GemmArgs A) {
   const int nw = n0 + 64 * (w >> 1);  // this wave's 64 features (half a weight block)
   const int nkb = A.K / WG;
 
-  // Staging (waves 0-3): DMA instruction i of wave w fills LDS granule
-  // (4i + w)*64 + lane of a tile; its global source is chosen so that the
+  // Staging (all 8 waves): DMA instruction i of wave w fills LDS granule
+  // (8i + w)*64 + lane of a tile; its global source is chosen so that the
   // tile ends up swizzled.
   // Rows past M (X) read zero codes from the padding rows; rows past N (W)
   // are outside the buffer and read as zero.
@@ -186,17 +197,18 @@ __global__ __launch_bounds__(512, 1) void w8a8_gemm_kernel(GemmArgs A) {
       const_cast<int8_t*>(A.xq), 0, static_cast<int>(static_cast<int64_t>(A.M_pad) * A.K), 0x00020000);
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<int8_t*>(A.wq), 0, static_cast<int>(static_cast<int64_t>(A.N) * A.K), 0x00020000);
-  constexpr int XI = XB / 4096, WI = WB / 4096;  // 1 KB DMA instructions per wave of group 0
+  constexpr int XI = XB / 8192, WI = WB / 8192;  // 1 KB DMA instructions per wave and block
+  constexpr int NDMA = XI + WI;
   const int wgrp = w >> 2;
   int xoff[XI], woff[WI];
 #pragma unroll
   for (int i = 0; i < XI; ++i) {
-    const int s = (4 * i + (w & 3)) * 64 + lane, r = s / 8, gp = s % 8;
+    const int s = (8 * i + w) * 64 + lane, r = s / 8, gp = s % 8;
     xoff[i] = (m0 + r) * A.K + ((gp ^ x_swz(r)) << 4);
   }
 #pragma unroll
   for (int i = 0; i < WI; ++i) {
-    const int s = (4 * i + (w & 3)) * 64 + lane, r = s / 8, gp = s % 8;  // r: row of the 256-row tile
+    const int s = (8 * i + w) * 64 + lane, r = s / 8, gp = s % 8;  // r: row of the 256-row tile
     const int key = r & 63;
     // a row past N points at the buffer's end, which reads as zero
     woff[i] = n0 + r < A.N ? (n0 + r) * A.K + ((gp ^ k_swz<128>(key)) << 4) : A.N * A.K;
@@ -205,21 +217,16 @@ __global__ __launch_bounds__(512, 1) void w8a8_gemm_kernel(GemmArgs A) {
 #pragma unroll
     for (int i = 0; i < XI; ++i) {
       const int off = xoff[i];
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, xd + (4 * i + w) * 1024, 16, off, kb * WG, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, xd + (8 * i + w) * 1024, 16, off, kb * WG, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < WI; ++i) {
       const int off = woff[i];
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, wd + (4 * i + w) * 1024, 16, off, kb * WG, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, wd + (8 * i + w) * 1024, 16, off, kb * WG, 0, 0);
     }
   };
 
-  // This lane's rows in the X tile (B operand: token r32 of group t, bytes
-  // [32 ks + 16 h2, +16)) and rows in the W tile (A operand, two 64-row halves).
-  const int xr0 = 64 * (w & 1) + r32, xr1 = xr0 + 32;
   const int wr_base = 64 * (w >> 1);
-  const int key0 = a_row_key(r32, 0), key1 = a_row_key(r32, 1);
-  const int sw0 = k_swz<128>(key0), sw1 = k_swz<128>(key1);
 
   constexpr int NU = 1;  // 64-feature groups per wave
   v16f y[NU][2][2];  // [feature group u][token group t][subtile s]
@@ -231,8 +238,8 @@ __global__ __launch_bounds__(512, 1) void w8a8_gemm_kernel(GemmArgs A) {
       for (int s = 0; s < 2; ++s) y[u][t][s] = v16f{0.f};
 
   // Scales of K block kb: this lane's two tokens x the wave's weight block.
-  // They are loaded one block ahead, before that block's DMA, so that the
-  // wait for the DMA covers them and no wait for them holds the DMA back.
+  // They are loaded one block ahead, at the start of a dequantization phase,
+  // so that the next step's wait for its DMA covers them.
   const float* dxp = A.xscale + mw + r32;
   // (a wave whose features lie past N computes on zero weights and stores
   // nothing; it reads the last weight block's scales)
@@ -246,23 +253,31 @@ __global__ __launch_bounds__(512, 1) void w8a8_gemm_kernel(GemmArgs A) {
   };
 
   load_scales(0);
-  if (wgrp == 0) dma(xL0, wL0, 0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);
+  dma(xL0, wL0, 0);
+  if (nkb > 1) dma(xL1, wL1, 1);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
 
   v16i s[2][2];  // [t][subtile]: int32 products of the current K block
-  auto mma = [&](const int8_t* xl, const int8_t* wl) {
+  // ln: the lane.  This lane's rows in the X tile (B operand: token r32 of
+  // group t, bytes [32 ks + 16 h2, +16)) and rows in the W tile (A operand,
+  // two 64-row halves).
+  auto mma = [&](const int8_t* xl, const int8_t* wl, int ln) {
+    const int r32l = ln & 31, h2l = ln >> 5;
+    const int xr0 = 64 * (w & 1) + r32l, xr1 = xr0 + 32;
+    const int key0 = a_row_key(r32l, 0), key1 = a_row_key(r32l, 1);
+    const int sw0 = k_swz<128>(key0), sw1 = k_swz<128>(key1);
     v4i xb[2][4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const int g = 2 * ks + h2;
+      const int g = 2 * ks + h2l;
       xb[0][ks] = *reinterpret_cast<const v4i*>(xl + xr0 * WG + ((g ^ x_swz(xr0)) << 4));
       xb[1][ks] = *reinterpret_cast<const v4i*>(xl + xr1 * WG + ((g ^ x_swz(xr1)) << 4));
     }
     const int8_t* wt = wl + wr_base * WG;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const int g = 2 * ks + h2;
+      const int g = 2 * ks + h2l;
       const v4i a0 = *reinterpret_cast<const v4i*>(wt + key0 * WG + ((g ^ sw0) << 4));
       const v4i a1 = *reinterpret_cast<const v4i*>(wt + key1 * WG + ((g ^ sw1) << 4));
 #pragma unroll
@@ -288,42 +303,91 @@ __global__ __launch_bounds__(512, 1) void w8a8_gemm_kernel(GemmArgs A) {
           y[0][t][sub][i] = __builtin_fmaf(static_cast<float>(s[t][sub][i]), c, y[0][t][sub][i]);
     }
   };
-  // One K block: the MFMA phase, a barrier, the dequantization phase, the
-  // DMA wait and a barrier.  Group 1 runs one phase behind group 0.
-  auto step = [&](const int8_t* xl, const int8_t* wl, int8_t* xn, int8_t* wn, int kb) {
-    const float c0 = dx0 * dwv, c1 = dx1 * dwv;  // fp32(dx dw), rounded once
-    load_scales(kb + 1);
+  // One K block: the MFMA phase (with this wave's DMA of block kb + 2), the
+  // wait for its DMA of block kb + 1, a barrier, the dequantization phase and
+  // a barrier.  Group 1 runs one phase behind group 0.  B: the buffer of
+  // block kb (kb % 3).
+  auto step = [&](auto bc, auto sc, int kb) {
+    constexpr int B = decltype(bc)::value;
+    constexpr bool stage = decltype(sc)::value;  // kb + 2 < nkb
+    const int8_t* xl = B == 0 ? xL0 : B == 1 ? xL1 : xL2;
+    const int8_t* wl = B == 0 ? wL0 : B == 1 ? wL1 : wL2;
+    int8_t* xn = B == 0 ? xL2 : B == 1 ? xL0 : xL1;  // buffer (kb + 2) % 3
+    int8_t* wn = B == 0 ? wL2 : B == 1 ? wL0 : wL1;
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(1);
-    if (wgrp == 0 && kb + 1 < nkb) {
-      // group 0 stages the next block: one DMA instruction behind each MFMA
-      dma(xn, wn, kb + 1);
-      mma(xl, wl);
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // the X operand reads
+    if constexpr (stage) {
+      dma(xn, wn, kb + 2);
+      mma(xl, wl, lane);
+      // the X operand reads and the first two k-steps' W reads, then the
+      // other W reads and this wave's DMA one behind each MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
 #pragma unroll
       for (int g = 0; g < 16; ++g) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                   // one MFMA
-        if (g < XI + WI) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one DMA
-        if (g < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // a W operand read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                // one MFMA
+        if (g < NDMA) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one DMA
+        if (g < 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // a W operand read
       }
     } else {
-      mma(xl, wl);
+      mma(xl, wl, lane);
     }
     asm volatile("" : "+v"(s[0][0]), "+v"(s[0][1]), "+v"(s[1][0]), "+v"(s[1][1]));
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(0);
+    // this wave's DMA of block kb + 1 (and the scales) landed; that of block
+    // kb + 2 (the NDMA loads issued last) may still be in flight
+    if constexpr (stage)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | NDMA);  // vmcnt(NDMA)
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70);         // vmcnt(0)
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
+    // block kb's scales (loaded one step ahead, waited for with the DMA);
+    // then the next block's, which the next step's DMA wait covers
+    const float c0 = dx0 * dwv, c1 = dx1 * dwv;  // fp32(dx dw), rounded once
+    load_scales(kb + 1);
     deq(c0, c1);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA (and scales) landed
-    __syncthreads();
+    // the sums are final here: without this the compiler sinks the
+    // dequantization into the next block and keeps several blocks' int32
+    // tiles alive
+    asm volatile("" : "+v"(y[0][0][0]), "+v"(y[0][0][1]), "+v"(y[0][1][0]), "+v"(y[0][1][1]));
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
   };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  using B2 = std::integral_constant<int, 2>;
 
+  using Stage = std::integral_constant<bool, true>;
+  using Last = std::integral_constant<bool, false>;
+
+  // The blocks that stage block kb + 2 (all but the last two), then the last
+  // two; each in its own copy of the step, so that no branch inside a step
+  // leaves the compiler unsure which loads are still in flight.
   if (wgrp == 1) __builtin_amdgcn_s_barrier();  // one phase behind group 0
-  for (int kb = 0; kb < nkb; kb += 2) {
-    step(xL0, wL0, xL1, wL1, kb);
-    if (kb + 1 >= nkb) break;
-    step(xL1, wL1, xL0, wL0, kb + 1);
+  const int nst = max(nkb - 2, 0);
+  int kb = 0;
+  for (; kb + 3 <= nst; kb += 3) {
+    step(B0{}, Stage{}, kb);
+    step(B1{}, Stage{}, kb + 1);
+    step(B2{}, Stage{}, kb + 2);
+  }
+  if (kb < nst) step(B0{}, Stage{}, kb++);
+  if (kb < nst) step(B1{}, Stage{}, kb++);
+  // kb = nst here: at most two blocks left, starting in buffer kb % 3
+  switch (kb % 3) {
+    case 0:
+      step(B0{}, Last{}, kb);
+      if (kb + 1 < nkb) step(B1{}, Last{}, kb + 1);
+      break;
+    case 1:
+      step(B1{}, Last{}, kb);
+      if (kb + 1 < nkb) step(B2{}, Last{}, kb + 1);
+      break;
+    default:
+      step(B2{}, Last{}, kb);
+      if (kb + 1 < nkb) step(B0{}, Last{}, kb + 1);
+      break;
   }
   if (wgrp == 0) __builtin_amdgcn_s_barrier();  // as many barriers as group 1
 
