@@ -822,8 +822,12 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs A) {
   // Every load issued so far has completed; saying so keeps the loop's own
   // prefetch loads from being waited on before the first MFMA.
   __builtin_amdgcn_s_waitcnt(0);
-  int pre1 = 0, pre3 = 0;  // block mask: chunks of entries n+1 and n+3 for the next step
-  if constexpr (SPARSE) {
+  // The next step's chunks of entries n+1 and n+3, computed a phase ahead:
+  // under a block mask (LDS reads), and over a frame cache with 16-bit P.V
+  // (frame arithmetic, moved out of that mode's longer MFMA phase).
+  constexpr bool AHEAD = SPARSE || (MODE == KV_CACHE && PV != PVFP8);
+  int pre1 = 0, pre3 = 0;
+  if constexpr (AHEAD) {
     pre1 = chunk_of(n + 1);
     pre3 = chunk_of(n + 3);
   }
@@ -842,7 +846,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs A) {
     constexpr int NPV = (PV == PVFP8) ? NCB + 1 : 4 * NCB + 4;    // P.V and row-sum MFMAs
     constexpr int NRD = NQK + ((PV == PVFP8) ? 2 * NCB : 4 * NCB);  // LDS operand reads
     const float c_mid = qsc * ksn1;
-    const int ch1 = SPARSE ? pre1 : chunk_of(n + 1), ch3 = SPARSE ? pre3 : chunk_of(n + 3);
+    const int ch1 = AHEAD ? pre1 : chunk_of(n + 1), ch3 = AHEAD ? pre3 : chunk_of(n + 3);
     // S(n+2) a boundary chunk?  Scalar work, placed in the phase that has
     // room for it: the MFMA phase in FP8 mode (its softmax phase is the longer
     // one), after the softmax with 16-bit P.V (the other way round).
@@ -887,9 +891,12 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs A) {
     if constexpr (SPARSE) {
       pre1 = __builtin_amdgcn_readfirstlane(e1);
       pre3 = __builtin_amdgcn_readfirstlane(e3);
+    } else if constexpr (AHEAD) {
+      pre1 = chunk_of(n + 2);
+      pre3 = chunk_of(n + 4);
     }
     if constexpr (CHK && !DECIDE_EARLY) {  // (block mask: the chunk of entry n+2 is pre1)
-      nd_n = n + 2 >= v_full && needs_mask(wl, n + 2, SPARSE ? pre1 : chunk_of(n + 2));
+      nd_n = n + 2 >= v_full && needs_mask(wl, n + 2, AHEAD ? pre1 : chunk_of(n + 2));
       has_n = true;
     }
     st.rescale(alpha);  // rare: some row's running max moved (after P(n) V(n))
