@@ -126,33 +126,36 @@ def step_parts(sage, w, desc, q, k, v, o, bufs, stream):
 
 
 def time_path(torch, parts, stream, steps, warm):
-    """Warm up, then time `steps` whole steps (quantize + fused kernel) with HIP
-    events on the launch stream around each part.  Returns ms per step, per
-    quantize pass and per fused-kernel launch."""
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    """Warm up, then time `steps` whole steps (quantize + fused kernel) with
+    HIP events on the launch stream around them: ms per step.  Then `steps`
+    more with events around each part as well: ms per quantize pass and per
+    fused-kernel launch.  (Events between launches add idle time to a short
+    step -- 0.07 ms of a 0.74 ms frame-cache step -- so the step time comes
+    from the first pass.)  Returns ms per step, per quantize pass and per
+    fused-kernel launch."""
     quant, attend = parts
-
-    def step(i=None):
-        if i is not None:
-            ev[i][0].record(stream)
-        quant()
-        if i is not None:
-            ev[i][1].record(stream)
-        attend()
-        if i is not None:
-            ev[i][2].record(stream)
-
     for _ in range(warm):
-        step()
+        quant()
+        attend()
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record(stream)
-    for i in range(steps):
-        step(i)
+    for _ in range(steps):
+        quant()
+        attend()
     end.record(stream)
     end.synchronize()
     ms_step = start.elapsed_time(end) / steps
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for e in ev:
+        e[0].record(stream)
+        quant()
+        e[1].record(stream)
+        attend()
+        e[2].record(stream)
+    torch.cuda.synchronize()
     ms_quant = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
     ms_attn = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
     return ms_step, ms_quant, ms_attn
