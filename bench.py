@@ -125,6 +125,22 @@ def step_parts(sage, w, desc, q, k, v, o, bufs, stream):
     return quant, lambda: sage.sage_attn_fwd_quantized(desc, bufs, o, stream)
 
 
+def warm_up(torch, parts, warm, seconds=0.3):
+    """Untimed steps: at least `warm`, and at least `seconds` of them, so that
+    a short step (a frame-cache step takes under a millisecond) is timed at
+    the clock the GPU holds under load, not while it ramps up."""
+    import time
+    quant, attend = parts
+    t0 = time.perf_counter()
+    n = 0
+    while n < warm or time.perf_counter() - t0 < seconds:
+        for _ in range(max(1, warm)):
+            quant()
+            attend()
+        n += max(1, warm)
+        torch.cuda.synchronize()
+
+
 def time_path(torch, parts, stream, steps, warm):
     """Warm up, then time `steps` whole steps (quantize + fused kernel) with
     HIP events on the launch stream around them: ms per step.  Then `steps`
@@ -134,10 +150,7 @@ def time_path(torch, parts, stream, steps, warm):
     from the first pass.)  Returns ms per step, per quantize pass and per
     fused-kernel launch."""
     quant, attend = parts
-    for _ in range(warm):
-        quant()
-        attend()
-    torch.cuda.synchronize()
+    warm_up(torch, parts, warm)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record(stream)
@@ -179,9 +192,7 @@ def time_graph(torch, parts, steps, warm):
     with torch.cuda.graph(g):
         quant()
         attend()
-    for _ in range(max(warm, 1)):
-        g.replay()
-    torch.cuda.synchronize()
+    warm_up(torch, (g.replay, lambda: None), warm)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record()
