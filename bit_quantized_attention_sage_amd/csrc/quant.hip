@@ -67,54 +67,84 @@ __global__ __launch_bounds__(256) void stats_partial_kernel(
   }
 }
 
-// One thread per (b, h, channel): mean, then the channel-balance exponent.
-__global__ void stats_final_kernel(int H, int D, int nchunk_k, int nchunk_q, BatchInfo bi,
-                                   const double* __restrict__ ksum,
-                                   const float* __restrict__ kmax,
-                                   const float* __restrict__ kmin,
-                                   const float* __restrict__ qamax,
-                                   const float* __restrict__ k_mean_in,
-                                   const int8_t* __restrict__ shift_in,
-                                   float* __restrict__ mu_out, int8_t* __restrict__ shift_out) {
-  const int bh = blockIdx.x, c = threadIdx.x;
-  if (c >= D) return;
+// One workgroup of SF_THREADS per (b, h): the mean and the channel-balance
+// exponent of every channel.  The partials are staged through LDS in tiles
+// of SF_TILE runs, loaded by the whole workgroup (consecutive threads take
+// consecutive channels: coalesced, many loads in flight), and thread c adds
+// channel c's sums from LDS in ascending run order: the fp64 sum keeps its
+// sequential order (runs past the end are not added).  Maxima and minima,
+// which no order changes, are reduced while staging and merged at the end.
+constexpr int SF_THREADS = 512;
+constexpr int SF_TILE = 64;  // runs per LDS tile: 64 x 128 channels x 8 B = 64 KB
+template <int D>
+__global__ __launch_bounds__(SF_THREADS) void stats_final_kernel(int H, int nchunk_k, int nchunk_q,
+                                                                 BatchInfo bi, const double* __restrict__ ksum,
+                                                                 const float* __restrict__ kmax,
+                                                                 const float* __restrict__ kmin,
+                                                                 const float* __restrict__ qamax,
+                                                                 const float* __restrict__ k_mean_in,
+                                                                 const int8_t* __restrict__ shift_in,
+                                                                 float* __restrict__ mu_out,
+                                                                 int8_t* __restrict__ shift_out) {
+  constexpr int PER = SF_TILE * D / SF_THREADS;  // elements of a tile per thread
+  __shared__ double tile[SF_TILE * D];
+  __shared__ float red[3][SF_THREADS];
+  const int bh = blockIdx.x, tid = threadIdx.x;
   const int b = bh / H;
   const int n = bi.kv_len[b];
   const int nch = (n + KMEAN_CHUNK - 1) / KMEAN_CHUNK;
-  // The partials of NB chunks are loaded together (independent loads in
-  // flight), then added in ascending chunk order: the fp64 sum keeps its
-  // sequential order (adds past the end are skipped, not added as zeros).
-  constexpr int NB = 16;
+  const int64_t base_k = static_cast<int64_t>(bh) * nchunk_k * D;
+  float mx = -__builtin_inff(), mn = __builtin_inff(), qa = 0.f;
   double s = 0.0;
-  float mx = -__builtin_inff(), mn = __builtin_inff();
-  const double* ks = ksum + static_cast<int64_t>(bh) * nchunk_k * D + c;
-  const float* kx = kmax + static_cast<int64_t>(bh) * nchunk_k * D + c;
-  const float* kn = kmin + static_cast<int64_t>(bh) * nchunk_k * D + c;
-  for (int t0 = 0; t0 < nch; t0 += NB) {
-    double v[NB];
-    float a[NB], z[NB];
+  for (int t0 = 0; t0 < nch; t0 += SF_TILE) {
+    const int nt = min(SF_TILE, nch - t0);
+    // all of this thread's loads of the tile first, then their use (element
+    // e = run t0 + e / D, channel e % D = tid % D; elements past the last run
+    // repeat that channel's last run, which changes no maximum and is never
+    // summed)
+    double v[PER];
+    float x[PER], z[PER];
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int t = min(t0 + i, nch - 1);
-      v[i] = ks[static_cast<int64_t>(t) * D];
-      a[i] = kx[static_cast<int64_t>(t) * D];
-      z[i] = kn[static_cast<int64_t>(t) * D];
+    for (int k = 0; k < PER; ++k) {
+      const int r = min((tid + k * SF_THREADS) / D, nt - 1);
+      const int64_t g = base_k + static_cast<int64_t>(t0 + r) * D + tid % D;
+      v[k] = ksum[g];
+      x[k] = kmax[g];
+      z[k] = kmin[g];
     }
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      if (t0 + i < nch) s += v[i];
-      mx = fmaxf(mx, a[i]);  // (repeats of the last chunk change no max or min)
-      mn = fminf(mn, z[i]);
+    for (int k = 0; k < PER; ++k) {
+      tile[tid + k * SF_THREADS] = v[k];
+      mx = fmaxf(mx, x[k]);
+      mn = fminf(mn, z[k]);
     }
+    __syncthreads();
+    if (tid < D)
+      for (int t = 0; t < nt; ++t) s += tile[t * D + tid];
+    __syncthreads();
   }
-  float qa = 0.f;
-  const float* qx = qamax + static_cast<int64_t>(bh) * nchunk_q * D + c;
-  for (int t0 = 0; t0 < nchunk_q; t0 += NB) {
-    float a[NB];
+  // Q's channel maxima: 16 loads in flight per thread (runs past the end
+  // repeat the thread's channel in the last run)
+  const float* qx = qamax + static_cast<int64_t>(bh) * nchunk_q * D + tid % D;
+  constexpr int RPT = SF_THREADS / D;  // runs per pass of the workgroup
+  for (int r0 = tid / D; r0 < nchunk_q; r0 += 16 * RPT) {
+    float a[16];
 #pragma unroll
-    for (int i = 0; i < NB; ++i) a[i] = qx[static_cast<int64_t>(min(t0 + i, nchunk_q - 1)) * D];
+    for (int k = 0; k < 16; ++k) a[k] = qx[static_cast<int64_t>(min(r0 + k * RPT, nchunk_q - 1)) * D];
 #pragma unroll
-    for (int i = 0; i < NB; ++i) qa = fmaxf(qa, a[i]);
+    for (int k = 0; k < 16; ++k) qa = fmaxf(qa, a[k]);
+  }
+  // (SF_THREADS is a multiple of D, so thread tid only ever saw channel tid % D)
+  red[0][tid] = mx;
+  red[1][tid] = mn;
+  red[2][tid] = qa;
+  __syncthreads();
+  if (tid >= D) return;
+  const int c = tid;
+  for (int j = c + D; j < SF_THREADS; j += D) {
+    mx = fmaxf(mx, red[0][j]);
+    mn = fminf(mn, red[1][j]);
+    qa = fmaxf(qa, red[2][j]);
   }
   const float mu = k_mean_in ? k_mean_in[static_cast<int64_t>(bh) * D + c]
                              : static_cast<float>(s / static_cast<double>(n));
@@ -336,7 +366,7 @@ static hipError_t quantize_impl(const QuantLaunch& L, hipStream_t st) {
     hipLaunchKernelGGL((stats_partial_kernel<T, D, false>), dim3((ncq + CPB - 1) / CPB, L.H, L.B), blk, 0, st,
                        static_cast<const T*>(L.q), L.qs[0], L.qs[1], L.qs[2], L.H, ncq, L.bi, L.Nq,
                        nullptr, L.stat_qamax, nullptr);
-    hipLaunchKernelGGL(stats_final_kernel, dim3(L.B * L.H), dim3(D), 0, st, L.H, D, nck, ncq, L.bi,
+    hipLaunchKernelGGL(stats_final_kernel<D>, dim3(L.B * L.H), dim3(SF_THREADS), 0, st, L.H, nck, ncq, L.bi,
                        L.stat_ksum, L.stat_kmax, L.stat_kmin, L.stat_qamax, L.k_mean_in, L.chan_shift_in,
                        L.bufs.k_mean, L.bufs.chan_shift);
   }
