@@ -782,9 +782,9 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs A) {
   // j&1 and V(n) in V buffer j&1.  It issues the DMA of K(n+3) and V(n+1),
   // then two phases split by a barrier: the S MFMAs of entry n+2 and the P.V
   // MFMAs of entry n (at raised wave priority, with the operand reads 8
-  // ahead), and the softmax of entry n+1; then the (rare) rescale by entry
-  // n+1's alpha, the (rare) masking of S(n+2), the wait for this step's DMA
-  // and the barrier.  Group 1 runs the same steps one phase behind group 0
+  // ahead), and the softmax of entry n+1 (preceded, for a boundary chunk, by
+  // its masking, decided a step earlier); then the (rare) rescale by entry
+  // n+1's alpha, the wait for this step's DMA and the barrier.  Group 1 runs the same steps one phase behind group 0
   // (one extra barrier before its first step, group 0 one after its last),
   // so on every SIMD one wave's matrix work meets the other wave's softmax,
   // and the buffers a step fills are the ones their readers finished with in
