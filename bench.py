@@ -125,10 +125,14 @@ def step_parts(sage, w, desc, q, k, v, o, bufs, stream):
     return quant, lambda: sage.sage_attn_fwd_quantized(desc, bufs, o, stream)
 
 
-def warm_up(torch, parts, warm, seconds=0.3):
+WARM_SECONDS = 0.3  # 0 under --profile: a profiled run keeps its few dispatches
+
+
+def warm_up(torch, parts, warm, seconds=None):
     """Untimed steps: at least `warm`, and at least `seconds` of them, so that
     a short step (a frame-cache step takes under a millisecond) is timed at
     the clock the GPU holds under load, not while it ramps up."""
+    seconds = WARM_SECONDS if seconds is None else seconds
     import time
     quant, attend = parts
     t0 = time.perf_counter()
@@ -233,7 +237,10 @@ def quantize_bytes(w, pv_mode):
 
 
 def main():
+    global WARM_SECONDS
     args = parse()
+    if args.profile:
+        WARM_SECONDS = 0.0
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the path is "
               "data-parallel over (batch, head): G GPUs would each run the same kernel on H/G heads "
