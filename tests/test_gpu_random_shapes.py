@@ -2,10 +2,10 @@
 
 Each case draws batch, heads, query and key lengths (not multiples of the
 128-row and 64-key tiles), per-batch key lengths, head dim, input type, P.V
-mode, an optional frame length with per-batch query positions (frame-block
-causal mask, Magi-1 / streaming reading of the SageAttention pages), forced or
-library-chosen KV splits and an optional block mask (tile skipping, Vidu S1
-blog, section "Infra").  For every case: each quantized operand bit-exact
+mode, an optional frame length with per-batch query positions (the
+frame-block-causal mask of streaming generation over a KV cache, Vidu S1
+blog, sections "模型架构" and "训练方法"), forced or library-chosen KV splits
+and an optional block mask (tile skipping, same blog, section "Infra").  For every case: each quantized operand bit-exact
 against the oracle's quantizer, every output element within the derived
 bound of gpu_util of the oracle's emulation with the same splits, and the
 cosine against float64 attention no worse than the emulation's.
@@ -22,8 +22,7 @@ import torch
 import bit_quantized_attention_sage_amd as sage
 from oracle import emulate, attention
 from oracle.constants import PV_16, PV_FP8
-from gpu_util import (host, check_quantized, emulate_like_gpu, assert_close, cosine, NAME_DT,
-                      KERNEL_SLACK)
+from gpu_util import host, check_quantized, emulate_like_gpu, assert_close, cosine, KERNEL_SLACK
 
 pytestmark = pytest.mark.gpu
 
