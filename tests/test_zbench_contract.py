@@ -41,12 +41,17 @@ def test_bench_json_line(lib, capsys, monkeypatch):
     rf = r["roofline"]
     assert rf["bound"] == "mfma" and rf["unit"] == "TOPS" and rf["peak"] == 5000.0
     assert rf["achieved"] > 0 and abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3
-    # the P.V mode's own ceiling: 1 / (0.5 / 5000 + 0.5 / 2500) for 16-bit P.V
-    assert abs(rf["mode_peak"] - 10000 / 3) < 0.1 and abs(rf["mode_frac"] - rf["achieved"] / rf["mode_peak"]) < 1e-3
+    # the P.V mode's own ceiling: 1 / (0.5 / 5000 + 0.5 / P) with P = 2500 (16-bit P.V) or 5000 (FP8)
+    import workloads
+    pv = r["config"]["pv"]
+    assert pv == ("fp8" if workloads.get("tiny").pv_mode == 1 else "16")   # the workload's own mode
+    want = 5000.0 if pv == "fp8" else 10000 / 3
+    assert abs(rf["mode_peak"] - want) < 0.1 and abs(rf["mode_frac"] - rf["achieved"] / rf["mode_peak"]) < 1e-3
     qz = r["quantize"]
     assert qz["algorithmic_bytes"] <= qz["design_bytes"]
     # the other P.V mode, with its accuracy and whether it meets both bars
-    assert r["other_pv_mode"]["pv"] == "fp8" and isinstance(r["other_pv_mode"]["meets_bar"], bool)
+    assert r["other_pv_mode"]["pv"] == ("16" if pv == "fp8" else "fp8")
+    assert isinstance(r["other_pv_mode"]["meets_bar"], bool)
     assert rf["traffic"] is None or rf["traffic"] > 0
     cb = r["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]

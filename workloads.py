@@ -18,7 +18,7 @@ stand in for them, with the token grids of such clips:
            d128 bf16, frame-block-causal mask with F = 2040
   batched  B8 H24 Nq 2040, each session's cache L_b ~ U{4..32} frames plus its
            own frame (kv_len = (L_b+1)*2040), KV allocated for 33 frames,
-           d128 bf16, frame-block-causal, P.V in FP8
+           d128 bf16, frame-block-causal
   window   streaming step over a frame cache (Vidu S1 blog, section "Infra":
            a fixed window of sink frames, recent history and the current
            frame): B1 H24 d128 bf16, 2040-token frames at a stride of 2048
@@ -44,6 +44,12 @@ stand in for them, with the token grids of such clips:
            step appends each session's current frame (its new keys and
            values) and quantizes the queries, then attends over the cache
            -- the cache is not re-quantized every step.
+
+P.V mode of each workload (bench.py's default for it): the faster mode that
+meets both accuracy bars (cosine >= 0.999 against float64 attention, max-abs
+<= 2e-3 against the oracle's emulation) on the workload, measured at full
+size -- FP8 everywhere except large and sparse, whose outlier-channel heads
+keep FP8 below 0.999 (there the 16-bit mode).  Either mode can be asked for.
 
 Values are N(0,1) float32, then rounded to the 16-bit dtype.  Each (tensor,
 batch, head) slice has its own seed, so any subset of heads can be drawn on
@@ -148,15 +154,15 @@ def get(name, **override):
     if name == "linear":
         return get_linear(name, **override)
     if name == "tiny":
-        w = Workload("tiny", 1, 2, 1024, 1024, 64, "f16", 0, seed=101, k_offset_std=2.0)
+        w = Workload("tiny", 1, 2, 1024, 1024, 64, "f16", 1, seed=101, k_offset_std=2.0)
     elif name == "small":
-        w = Workload("small", 1, 12, 32760, 32760, 128, "bf16", 0, seed=202,
+        w = Workload("small", 1, 12, 32760, 32760, 128, "bf16", 1, seed=202,
                      k_offset_std=float(np.sqrt(3.0)))
     elif name == "large":
         w = Workload("large", 1, 40, 75600, 75600, 128, "bf16", 0, seed=303,
                      outlier_frac=0.01)
     elif name == "stream":
-        w = Workload("stream", 1, 24, FRAME, 17 * FRAME, 128, "bf16", 0,
+        w = Workload("stream", 1, 24, FRAME, 17 * FRAME, 128, "bf16", 1,
                      frame_len=FRAME, kv_len=[17 * FRAME], q_pos0=[16 * FRAME], seed=404)
     elif name == "batched":
         L = np.random.default_rng(505).integers(4, 33, 8)
@@ -165,14 +171,14 @@ def get(name, **override):
                      frame_len=FRAME, kv_len=kv, q_pos0=[int(x * FRAME) for x in L],
                      seed=505)
     elif name == "window":
-        w = Workload("window", 1, 24, FRAME, 48 * 2048, 128, "bf16", 0,
+        w = Workload("window", 1, 24, FRAME, 48 * 2048, 128, "bf16", 1,
                      frame_len=FRAME, kv_len=[41 * FRAME], q_pos0=[40 * FRAME], seed=606,
                      frame_stride=2048, sink_frames=1, window_frames=16)
     elif name == "sparse":
         w = Workload("sparse", 1, 40, 75600, 75600, 128, "bf16", 0, seed=303,
                      outlier_frac=0.01, block_density=0.25)
     elif name == "stream-cache":
-        w = Workload("stream-cache", 1, 24, FRAME, 17 * 2048, 128, "bf16", 0,
+        w = Workload("stream-cache", 1, 24, FRAME, 17 * 2048, 128, "bf16", 1,
                      frame_len=FRAME, kv_len=[17 * FRAME], q_pos0=[16 * FRAME], seed=404,
                      frame_stride=2048)
     elif name == "batched-cache":
