@@ -152,7 +152,8 @@ def time_path(torch, parts, stream, steps, warm):
     fused-kernel launch.  (Events between launches add idle time to a short
     step -- 0.07 ms of a 0.74 ms frame-cache step -- so the step time comes
     from the first pass.)  Returns ms per step, per quantize pass and per
-    fused-kernel launch."""
+    fused-kernel launch (means), and the fused kernel's launch times (ms,
+    sorted) of the second pass."""
     quant, attend = parts
     warm_up(torch, parts, warm)
     start = torch.cuda.Event(enable_timing=True)
@@ -174,8 +175,15 @@ def time_path(torch, parts, stream, steps, warm):
         e[2].record(stream)
     torch.cuda.synchronize()
     ms_quant = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
-    ms_attn = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
-    return ms_step, ms_quant, ms_attn
+    launches = sorted(e[1].elapsed_time(e[2]) for e in ev)
+    return ms_step, ms_quant, sum(launches) / steps, launches
+
+
+def launch_spread(launches):
+    """Median and minimum of the timed launches (ms) beside their mean."""
+    n = len(launches)
+    med = launches[n // 2] if n % 2 else 0.5 * (launches[n // 2 - 1] + launches[n // 2])
+    return {"ms_per_launch_median": round(med, 4), "ms_per_launch_min": round(launches[0], 4)}
 
 
 def time_graph(torch, parts, steps, warm):
@@ -312,8 +320,8 @@ def main():
                                       other["accuracy"]["max_abs_vs_emulation"] <= 2e-3)
         del ws2, bufs2
     desc, ws, bufs = setup(w.pv_mode)
-    ms_step, ms_quant, ms_attn = time_path(torch, step_parts(sage, w, desc, q, k, v, o, bufs, stream),
-                                           stream, steps, warm)
+    ms_step, ms_quant, ms_attn, launches = time_path(torch, step_parts(sage, w, desc, q, k, v, o, bufs, stream),
+                                                     stream, steps, warm)
     tops = ops / (ms_step * 1e-3) / 1e12
     ms_full_quant = None
     if w.frame_stride:
@@ -361,7 +369,7 @@ def main():
                      "mode_peak_note": ("Q K^T on INT8, P V on " + ("FP8" if w.pv_mode == 1 else "16-bit")
                                         + " matrix cores: 1 / (0.5 / 5000 + 0.5 / "
                                         + ("5000" if w.pv_mode == 1 else "2500") + ") TOPS"),
-                     "traffic": traffic, "ms_per_launch": round(ms_attn, 4)},
+                     "traffic": traffic, "ms_per_launch": round(ms_attn, 4), **launch_spread(launches)},
         "quantize": {"ms": round(ms_quant, 4), "algorithmic_bytes": qmin,
                      "GB_per_s": round(qmin / (ms_quant * 1e-3) / 1e9, 1),
                      "hbm_frac": round(qmin / (ms_quant * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -406,7 +414,7 @@ def main_linear(args, torch, sage, workloads):
     warm = 1 if args.profile else args.warmup
     parts = (lambda: sage.sage_w8a8_quantize_act(d, x, xq, xs, stream),
              lambda: sage.sage_w8a8_gemm(d, xq, xs, wq, ws, bias, y, stream))
-    ms_step, ms_quant, ms_gemm = time_path(torch, parts, stream, steps, warm)
+    ms_step, ms_quant, ms_gemm, launches = time_path(torch, parts, stream, steps, warm)
     ops = w.ops()
     qbytes = w.M * w.K * 2 + w.M * w.K + w.M * (w.K // 128) * 4  # read X, write codes and scales
     record = {
@@ -427,7 +435,8 @@ def main_linear(args, torch, sage, workloads):
         "roofline": {"bound": "mfma", "kernel": "w8a8_gemm_kernel", "achieved": round(ops / (ms_gemm * 1e-3) / 1e12, 2),
                      "peak": INT8_PEAK_TOPS, "unit": "TOPS",
                      "frac": round(ops / (ms_gemm * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
-                     "traffic": kernel_traffic("linear", "16"), "ms_per_launch": round(ms_gemm, 4)},
+                     "traffic": kernel_traffic("linear", "16"), "ms_per_launch": round(ms_gemm, 4),
+                     **launch_spread(launches)},
         "quantize": {"ms": round(ms_quant, 4), "algorithmic_bytes": qbytes,
                      "GB_per_s": round(qbytes / (ms_quant * 1e-3) / 1e9, 1),
                      "hbm_frac": round(qbytes / (ms_quant * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},

@@ -41,6 +41,8 @@ def test_bench_json_line(lib, capsys, monkeypatch):
     rf = r["roofline"]
     assert rf["bound"] == "mfma" and rf["unit"] == "TOPS" and rf["peak"] == 5000.0
     assert rf["achieved"] > 0 and abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3
+    # the fused kernel's launches: mean, median and minimum
+    assert 0 < rf["ms_per_launch_min"] <= rf["ms_per_launch_median"] and rf["ms_per_launch"] >= rf["ms_per_launch_min"]
     # the P.V mode's own ceiling: 1 / (0.5 / 5000 + 0.5 / P) with P = 2500 (16-bit P.V) or 5000 (FP8)
     import workloads
     pv = r["config"]["pv"]
