@@ -179,6 +179,18 @@ def time_path(torch, parts, stream, steps, warm):
     return ms_step, ms_quant, sum(launches) / steps, launches
 
 
+def input_digests(torch, tensors):
+    """SHA-256 per input tensor, of a digest taken on the GPU: the sum of the
+    16-bit patterns (as integers) of every row along the last dimension, so
+    that a changed element changes it, without copying the tensors to the
+    host."""
+    out = {}
+    for name, t in tensors.items():
+        rows = t.contiguous().view(torch.int16).to(torch.int32).sum(dim=-1, dtype=torch.int64)
+        out[name] = hashlib.sha256(rows.cpu().numpy().tobytes()).hexdigest()
+    return out
+
+
 def launch_spread(launches):
     """Median and minimum of the timed launches (ms) beside their mean."""
     n = len(launches)
@@ -354,6 +366,7 @@ def main():
         "vs_baseline": None,
         "dtype": "int8+fp8" if w.pv_mode == 1 else ("int8+" + w.dtype),
         "data": "synthetic (seeded Gaussian, video-DiT token grid)",
+        "input_digests": input_digests(torch, {"q": q, "k": k, "v": v}),
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nkv": w.Nkv, "d": w.d,
                    "in_dtype": w.dtype, "pv": pvname,
                    "frame_len": w.frame_len, "kv_splits": splits,
@@ -430,6 +443,7 @@ def main_linear(args, torch, sage, workloads):
         "vs_baseline": None,
         "dtype": "int8+" + w.dtype,
         "data": "synthetic (seeded Gaussian, 1% activation channels x8)",
+        "input_digests": input_digests(torch, {"x": x, "w": wt, "bias": bias.view(1, -1)}),
         "config": {"workload": "linear", "M": w.M, "N": w.N, "K": w.K, "in_dtype": w.dtype, "bias": True,
                    "ops_per_step": ops, "pct_int8_peak": round(100 * ops / (ms_step * 1e-3) / 1e12 / INT8_PEAK_TOPS, 2)},
         "roofline": {"bound": "mfma", "kernel": "w8a8_gemm_kernel", "achieved": round(ops / (ms_gemm * 1e-3) / 1e12, 2),

@@ -36,6 +36,7 @@ def test_bench_json_line(lib, capsys, monkeypatch):
     assert r["n_gpus"] == 1 and r["steps"] == 3 and r["warmup"] == 1
     assert r["value"] > 0 and r["ms_per_step"] > 0 and r["higher_is_better"] is True
     assert r["config"]["workload"] == "tiny"
+    assert sorted(r["input_digests"]) == ["k", "q", "v"] and all(len(h) == 64 for h in r["input_digests"].values())
     # TOPS over the step time: 4 d (visible pairs) per step (both fields are rounded)
     assert abs(r["value"] - r["config"]["ops_per_step"] / (r["ms_per_step"] * 1e-3) / 1e12) <= 1e-2 * r["value"]
     rf = r["roofline"]
