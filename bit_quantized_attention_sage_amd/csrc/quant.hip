@@ -15,7 +15,10 @@ namespace sage {
 // ---------------------------------------------------------------- statistics
 // One thread per (128-token chunk, group of 8 channels).  K: float64 sums in
 // ascending token order, plus max and min; Q: max |x|.  Tokens at or beyond
-// n_valid take no part.
+// n_valid take no part.  A thread loads SP_BATCH rows before using any (a
+// mid-size tensor gives about two waves per SIMD, so the loads in flight per
+// thread set the bandwidth), then adds them in token order.
+constexpr int SP_BATCH = 16;
 template <typename T, int D, bool IS_K>
 __global__ __launch_bounds__(256) void stats_partial_kernel(
     const T* __restrict__ x, int64_t sb, int64_t sh, int64_t sn, int H, int nchunk,
@@ -39,20 +42,28 @@ __global__ __launch_bounds__(256) void stats_partial_kernel(
     mx[c] = -__builtin_inff();
     mn[c] = __builtin_inff();
   }
-#pragma unroll 4
-  for (int j = j0; j < j1; ++j) {
-    const uint4 raw = *reinterpret_cast<const uint4*>(base + j * sn);
-    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  for (int jb = j0; jb < j1; jb += SP_BATCH) {
+    // rows past j1 repeat row j1 - 1 (in bounds) and are not used
+    uint4 raw[SP_BATCH];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const uint32_t bits = (w[c / 2] >> (16 * (c % 2))) & 0xFFFFu;
-      const float v = to_f32(T{static_cast<uint16_t>(bits)});
-      if (IS_K) {
-        s[c] += static_cast<double>(v);
-        mx[c] = fmaxf(mx[c], v);
-        mn[c] = fminf(mn[c], v);
-      } else {
-        mx[c] = fmaxf(mx[c], fabsf(v));
+    for (int k = 0; k < SP_BATCH; ++k)
+      raw[k] = *reinterpret_cast<const uint4*>(base + static_cast<int64_t>(min(jb + k, j1 - 1)) * sn);
+#pragma unroll
+    for (int k = 0; k < SP_BATCH; ++k) {
+      const uint32_t w[4] = {raw[k].x, raw[k].y, raw[k].z, raw[k].w};
+      const bool use = jb + k < j1;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const uint32_t bits = (w[c / 2] >> (16 * (c % 2))) & 0xFFFFu;
+        const float v = to_f32(T{static_cast<uint16_t>(bits)});
+        if (IS_K) {
+          // (a repeated row changes no maximum or minimum; it is not summed)
+          if (use) s[c] += static_cast<double>(v);
+          mx[c] = fmaxf(mx[c], v);
+          mn[c] = fminf(mn[c], v);
+        } else {
+          mx[c] = fmaxf(mx[c], fabsf(v));
+        }
       }
     }
   }
