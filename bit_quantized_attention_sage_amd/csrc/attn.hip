@@ -289,6 +289,15 @@ struct WaveState {
     }
   }
 
+  // O and l as the MFMA phase leaves them: without this the compiler may sink
+  // the phase's P.V MFMAs (pure operations whose results are next used a step
+  // later) past the phase's barrier into the softmax phase
+  __device__ __forceinline__ void pin_acc() {
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) asm volatile("" : "+v"(o[cb]));
+    asm volatile("" : "+v"(ls));
+  }
+
   // O and l times alpha, when some row moved (alpha is 1 for the others)
   __device__ __forceinline__ void rescale(float alpha) {
     if (moved_) {
@@ -906,6 +915,9 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs A) {
       if (g + 8 < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // the next read
     }
     asm volatile("" : "+v"(ns0), "+v"(ns1));
+    // (FP8 P.V over a frame cache: the boundary checks of every step let the
+    // compiler sink the P.V MFMAs into the softmax phase, the longer one)
+    if constexpr (PV == PVFP8 && MODE == KV_CACHE) st.pin_acc();
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_s_barrier();  // end of the MFMA phase
