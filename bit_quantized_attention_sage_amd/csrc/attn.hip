@@ -915,9 +915,10 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs A) {
       if (g + 8 < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // the next read
     }
     asm volatile("" : "+v"(ns0), "+v"(ns1));
-    // (FP8 P.V over a frame cache: the boundary checks of every step let the
-    // compiler sink the P.V MFMAs into the softmax phase, the longer one)
-    if constexpr (PV == PVFP8 && MODE == KV_CACHE) st.pin_acc();
+    // (FP8 P.V, boundary-checked steps -- every step over a frame cache: the
+    // checks let the compiler sink the P.V MFMAs into the softmax phase, the
+    // longer one)
+    if constexpr (PV == PVFP8 && CHK && !SPARSE) st.pin_acc();
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_s_barrier();  // end of the MFMA phase

@@ -169,3 +169,41 @@ def test_no_mfma_result_hazards(unit, required_waits, tmp_path):
     assert not unknown, f"MFMA shapes without a calibrated wait: {unknown}"
     hits = _scan(lines, required_waits)
     assert not hits, "\n".join(hits[:20])
+
+
+def _softmax_phase_mfmas(lines):
+    """Per fused-kernel function, the MFMAs found after a matrix phase's end
+    (`s_setprio 0` then `s_barrier`) and before the next barrier, priority
+    raise, branch or loop header, in text order."""
+    out, func = {}, None
+    instrs = list(_instructions(lines))
+    for i, (kind, op, rest) in enumerate(instrs):
+        if kind == "func":
+            func = op
+            continue
+        if kind != "instr" or op != "s_setprio" or rest.strip() != "0" or "attn_fwd_kernel" not in str(func):
+            continue
+        if i + 1 >= len(instrs) or instrs[i + 1][1] != "s_barrier":
+            continue
+        for kind2, op2, _ in instrs[i + 2:]:
+            if kind2 == "func" or op2 in ("s_barrier", "s_branch", "s_endpgm") or (op2 == "s_setprio"):
+                break
+            if kind2 == "instr" and op2.startswith("v_mfma"):
+                out.setdefault(func, []).append(op2)
+    return out
+
+
+def test_scanner_finds_an_mfma_in_a_softmax_phase():
+    lines = ["_ZN4sage15attn_fwd_kernelX:", "s_setprio 0", "s_barrier", "v_exp_f32_e32 v1, v1",
+             "v_mfma_f32_32x32x16_bf16 v[2:17], v[20:23], v[24:27], v[2:17]", "s_barrier", "s_endpgm"]
+    assert _softmax_phase_mfmas(lines) == {"_ZN4sage15attn_fwd_kernelX": ["v_mfma_f32_32x32x16_bf16"]}
+
+
+def test_fused_kernel_phases_keep_their_mfmas(tmp_path):
+    """The ping-pong kernel's matrix work belongs to its MFMA phase: the
+    compiler may sink a pure MFMA past the phase barrier (it did, for the FP8
+    P.V MFMAs of boundary-checked steps), which puts matrix work and its
+    operand waits into the softmax phase.  No instantiation may have any."""
+    lines = _assemble(os.path.join(B.CSRC, "attn.hip"), B.UNITS["attn.hip"], str(tmp_path / "a.s"))
+    found = _softmax_phase_mfmas(lines)
+    assert not found, {f: len(v) for f, v in found.items()}
