@@ -167,13 +167,19 @@ def test_all_kept_mask_equals_dense(lib, pv_mode):
     assert torch.equal(o1, o2)
 
 
+SPARSE_FP8_REASON = ("FP8 P.V on the sparse workload (the large workload's outlier-channel heads) misses "
+                     "cosine 0.999 by the scheme itself, as on the large workload: 0.99861 on the bench's sample")
+
+
 @pytest.mark.slow
-def test_sparse_workload_parity(lib):
+@pytest.mark.parametrize("pv_mode", [PV_16, pytest.param(PV_FP8, marks=pytest.mark.skip(reason=SPARSE_FP8_REASON))],
+                         ids=["pv16", "pvfp8"])
+def test_sparse_workload_parity(lib, pv_mode):
     """The sparse workload at full size (the large workload with 25% of its
     tiles kept) in the launch configuration bench.py times; outputs of 3
     seeded heads on sampled rows."""
-    w = workloads.get("sparse")
-    print("workload sparse", flush=True)
+    w = workloads.get("sparse", pv_mode=pv_mode)
+    print(f"workload sparse pv {pv_mode}", flush=True)
     x = workloads.make(w, "cuda")
     q, k, v = x["q"], x["k"], x["v"]
     M = workloads.block_mask(w)

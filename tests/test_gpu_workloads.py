@@ -32,7 +32,7 @@ LARGE_FP8_REASON = ("FP8 P.V on the large workload misses cosine 0.999 by the sc
 CASES = [("tiny", 1, None, None), ("tiny", 0, None, None), ("small", 1, 3, 96), ("small", 0, 2, 64),
          ("large", 0, 6, 48),
          pytest.param("large", 1, 4, 48, marks=pytest.mark.skip(reason=LARGE_FP8_REASON)),
-         ("stream", 1, 3, 96), ("stream", 0, 2, 64), ("batched", 1, 2, 48)]
+         ("stream", 1, 3, 96), ("stream", 0, 2, 64), ("batched", 1, 2, 48), ("batched", 0, 2, 32)]
 
 
 def _cid(c):
