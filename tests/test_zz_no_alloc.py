@@ -3,8 +3,9 @@ callers that cannot allocate device memory: its output equals
 sage_attn_fwd_quantized's bit for bit (the same kernels; only the split-KV
 partials live in the library's device scratch instead of the workspace), on
 two calls in a row, the second with a smaller input, both with KV splits so
-that the scratch is really used; and a call whose partials exceed the
-scratch is refused on the host."""
+that the scratch is really used; a call whose partials exceed the scratch
+is refused on the host; and a streaming step captured into a HIP graph
+replays like the workspace entry point."""
 
 import ctypes
 
@@ -61,3 +62,57 @@ def test_noalloc_rejects_partials_beyond_the_scratch(lib):
     b = sage.sage_quant_bufs()
     st = sage.load().sage_attn_fwd_quantized_noalloc(d.ptr, ctypes.byref(b), ctypes.c_void_p(1 << 20), None)
     assert st == 8 and b"device scratch" in sage.load().sage_attn_last_error()
+
+
+def _capture(fn):
+    """Warm fn up on a side stream (the scratch address is looked up on a
+    device's first call), then capture it into a graph."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+@pytest.mark.parametrize("pv_mode", [0, 1], ids=["pv16", "pvfp8"])
+def test_noalloc_streaming_step_replays_from_a_graph(lib, pv_mode):
+    """The use the entry point exists for: a frame-cache attention step (4 KV
+    splits, partials in the device scratch) captured once into a HIP graph
+    and replayed four times, the cache's current frame and the queries
+    quantized again eagerly between replays; every replay equals the
+    workspace entry point run eagerly on the same buffers, bit for bit."""
+    B, H, F, FS, nf, d = 1, 4, 200, 256, 6, 128
+    q = _rand((B, H, F, d), 40 + pv_mode)
+    k, v = _rand((B, H, nf * F, d), 41), _rand((B, H, nf * F, d), 42)
+    o_na, o_ref = torch.full_like(q, float("nan")), torch.empty_like(q)
+    desc = sage.Desc.for_tensors(q, k, v, o_ref, nkv=nf * FS, pv_mode=pv_mode, frame_len=F, frame_stride=FS,
+                                 kv_len=[nf * F], q_pos0=[(nf - 1) * F], kv_splits=4)
+    assert sage.sage_attn_kv_splits(desc) == 4
+    ws = sage.new_workspace(desc, q.device)
+    bufs = sage.sage_attn_quant_layout(desc, ws)
+    sage.sage_attn_quantize(desc, q, k, v, bufs)      # the cache, once
+    nb = sage.sage_quant_bufs.from_buffer_copy(bufs)
+    nb.partial = None
+    nb.partial_splits = 1
+    kk, vv = k[:, :, (nf - 1) * F:], v[:, :, (nf - 1) * F:]
+    d2 = sage.Desc.for_tensors(q, kk, vv, nkv=nf * FS, pv_mode=pv_mode, frame_len=F, frame_stride=FS)
+    g = _capture(lambda: sage.sage_attn_fwd_quantized_noalloc(desc, nb, o_na))
+    for r in range(4):
+        q.copy_(_rand((B, H, F, d), 50 + r))
+        kk.copy_(_rand((B, H, F, d), 60 + r))
+        vv.copy_(_rand((B, H, F, d), 70 + r))
+        sage.sage_attn_quantize_frames(d2, q, kk, vv, nf - 1, 1, bufs)
+        o_na.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        sage.sage_attn_fwd_quantized(desc, bufs, o_ref)
+        torch.cuda.synchronize()
+        print(f"  replay {r}: equal {torch.equal(o_na, o_ref)}", flush=True)
+        assert torch.isfinite(o_ref).all() and torch.equal(o_na, o_ref)
