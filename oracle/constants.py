@@ -19,6 +19,7 @@ LOG2E = 1.4426950408889634
 
 PV_16 = 0
 PV_FP8 = 1
+PV_AUTO = 2      # per (b,h): FP8 unless channel balance moved a channel (quant.pv_modes_auto)
 
 __all__ = ["BQ", "BK", "VB", "QMAX", "F8MAX", "KMEAN_CHUNK", "TAU",
-           "PSHIFT_FP8", "PSHIFT_16", "LOG2E", "PV_16", "PV_FP8"]
+           "PSHIFT_FP8", "PSHIFT_16", "LOG2E", "PV_16", "PV_FP8", "PV_AUTO"]

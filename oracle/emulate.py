@@ -29,7 +29,8 @@ chunks of BK = 64 (chunk t = keys [64t, 64t+64)), in ascending order:
      p already carries the 2^s pre-scale), else the input's fp16/bf16
   7. l       += sum_j p~                     (the rounded operand itself)
   8. acc     += sum_j p~[i,j] * V^[j,:]
-Finally O[i] = acc / l; the 2^s pre-scale cancels in that ratio.  The output
+Finally O[i] = acc / l; the 2^s pre-scale cancels in that ratio.  Under
+PV_AUTO every (b,h) runs these steps in the mode quant.pv_modes_auto gives it.  The output
 is rounded (RNE) to the input dtype.  Because l sums exactly the weights that
 multiply V^, every output row is a convex combination of the visible V^ rows
 (a constant V^ column comes out unchanged).
@@ -62,7 +63,7 @@ both sums taken with the same rescalings and split weights as acc and l.
 
 import numpy as np
 
-from .constants import BQ, BK, TAU, PSHIFT_FP8, PSHIFT_16, LOG2E, PV_16, PV_FP8
+from .constants import BQ, BK, TAU, PSHIFT_FP8, PSHIFT_16, LOG2E, PV_16, PV_FP8, PV_AUTO
 from . import codecs
 from .fp32 import fma_f32
 from .attention import row_end, default_q_pos0
@@ -244,6 +245,8 @@ def sage_attention_emulated(qcodes, dq, kcodes, dk, Vhat, pv_mode, dtype,
     Vhat: the P.V right operand as exact values [B,H,Nkv,d] -- V (16-bit
     mode) or dequant_v_fp8(...) (FP8 mode);  dtype: 'bf16' | 'f16' (input and
     output type, and P's type in 16-bit mode).
+    pv_mode: PV_16, PV_FP8, or an int array [B,H] giving each head's mode
+    (Vhat[b,h] must then be that head's operand).
     splits: optional list of (chunk_lo, chunk_hi) ranges covering the keys,
     or a list of such lists, one per batch (see ``split_ranges`` and
     ``cache_splits``).
@@ -269,6 +272,7 @@ def sage_attention_emulated(qcodes, dq, kcodes, dk, Vhat, pv_mode, dtype,
     qp = default_q_pos0(Nq, kv, frame_len) if q_pos0 is None else np.asarray(q_pos0, np.int64)
     rows = np.arange(Nq) if rows is None else np.asarray(rows, dtype=np.int64)
     nchunks = -(-Nkv // BK)
+    pvm = np.broadcast_to(np.asarray(pv_mode, dtype=np.int64), (B, H))
     if splits is not None and len(splits) and isinstance(splits[0], tuple):
         splits = [splits] * B
     out = np.empty((B, H, len(rows), d), dtype=np.float64)
@@ -299,7 +303,7 @@ def sage_attention_emulated(qcodes, dq, kcodes, dk, Vhat, pv_mode, dtype,
             S_full = qcodes[b, h, rows, :].astype(np.float64) @ \
                 kcodes[b, h, :jmax, :].astype(np.float64).T                # exact
             Vh = np.asarray(Vhat[b, h, :jmax, :], dtype=np.float64)
-            parts = [_run_rows(S_full, qs, dk[b, h], vis_h, Vh, lo, hi, pv_mode, dtype,
+            parts = [_run_rows(S_full, qs, dk[b, h], vis_h, Vh, lo, hi, int(pvm[b, h]), dtype,
                                slack=slack, perturb=perturb)
                      for (lo, hi) in parts_b]
             ms = np.stack([p.m for p in parts]).astype(np.float64)         # [P, R]
@@ -352,11 +356,15 @@ def emulate_from_inputs(Q, K, V, pv_mode, dtype, sm_scale=None, frame_len=0,
 
     frame_stride > 0: K and V (tokens of whole frames from frame 0) go into a
     frame cache, each frame quantized once against the given (frozen) mu and
-    shift (both required then)."""
+    shift (both required then).
+    pv_mode PV_AUTO (contiguous keys only): each (b,h) in the mode
+    quant.pv_modes_auto gives it; with slack, aux['pv_modes'] holds them."""
     from . import quant
     Qf = np.asarray(Q, dtype=np.float32)
     Kf = np.asarray(K, dtype=np.float32)
     Vf = np.asarray(V, dtype=np.float32)
+    if frame_stride and pv_mode == PV_AUTO:
+        raise ValueError("PV_AUTO needs contiguous keys")
     if frame_stride:
         qc, dq = quant.quantize_q(Qf, shift)
         kc, dk = quant.quantize_k_frames(Kf, mu, shift, frame_len, frame_stride, kv_len=kv_len)
@@ -374,14 +382,18 @@ def emulate_from_inputs(Q, K, V, pv_mode, dtype, sm_scale=None, frame_len=0,
     a = quant.channel_shift(Qf, Kf, mu, kv_len) if shift is None else shift
     qc, dq = quant.quantize_q(Qf, a)
     kc, dk = quant.quantize_k(Kf, mu, kv_len, a)
-    if pv_mode == PV_FP8:
+    modes = quant.pv_modes_auto(a) if pv_mode == PV_AUTO else pv_mode
+    Vhat = Vf.astype(np.float64)
+    if np.any(np.asarray(modes) == PV_FP8):
         vc, ve, _ = quant.quantize_v_fp8(Vf, kv_len)
-        Vhat = quant.dequant_v_fp8(vc, ve)
-    else:
-        Vhat = Vf.astype(np.float64)
-    return sage_attention_emulated(qc, dq, kc, dk, Vhat, pv_mode, dtype, sm_scale,
-                                   frame_len, kv_len, q_pos0, rows, splits,
-                                   block_mask=block_mask, slack=slack, perturb=perturb)
+        V8 = quant.dequant_v_fp8(vc, ve)
+        Vhat = V8 if pv_mode == PV_FP8 else np.where((modes == PV_FP8)[:, :, None, None], V8, Vhat)
+    res = sage_attention_emulated(qc, dq, kc, dk, Vhat, modes, dtype, sm_scale,
+                                  frame_len, kv_len, q_pos0, rows, splits,
+                                  block_mask=block_mask, slack=slack, perturb=perturb)
+    if slack is not None:
+        res[2]["pv_modes"] = np.broadcast_to(np.asarray(modes, dtype=np.int64), qc.shape[:2])
+    return res
 
 
 def cache_list(Nq, q_pos0_b, kv_len_b, frame_len, frame_stride, sink_frames, window_frames):

@@ -23,6 +23,9 @@ library's stated design:
    rint(x * (127 / amax)) in [-127, 127].
 4. FP8 P.V mode only: V in OCP e4m3fn with one power-of-two (E8M0) scale per
    (32-key block, channel), the smallest that keeps the block within 448.
+5. Per-head P.V mode (PV_AUTO): FP8 for a (b,h) whose channel-balance
+   exponents are all 0, the input's 16-bit type for one where some a_c != 0
+   (``pv_modes_auto``).
 
 Shapes: Q [B,H,Nq,d]; K, V [B,H,Nkv,d]; kv_len [B] with 1 <= kv_len[b] <= Nkv.
 Keys at positions >= kv_len[b] are padding: they take no part in the mean or
@@ -31,7 +34,7 @@ any amax, and their codes are 0.
 
 import numpy as np
 
-from .constants import BQ, BK, VB, QMAX, KMEAN_CHUNK
+from .constants import BQ, BK, VB, QMAX, KMEAN_CHUNK, PV_16, PV_FP8
 from . import codecs
 
 
@@ -128,6 +131,23 @@ def channel_shift(Q, K, mu, kv_len=None):
     k = eB - eA - (mB < mA).astype(np.int64)
     a = np.floor_divide(k + 1, 2)
     return np.where((A == 0) | (Bm == 0), 0, a).astype(np.int64)
+
+
+def pv_modes_auto(shift):
+    """P.V mode of every (b,h) under PV_AUTO, from its channel-balance
+    exponents a [B,H,d]: PV_FP8 where every a_c is 0, PV_16 where some a_c is
+    not.  (int64 [B,H].)
+
+    The library's reading, not the pages' (they fix no bit widths).  a_c != 0
+    means the range of K~ and Q in channel c differ by a factor of 2 or more
+    -- an outlier channel, as in the large workload's x8 channels -- and such
+    a head's INT8 scores already spend much of the output's error budget
+    (cosine 0.999 against exact attention); the 3-bit mantissas of e4m3 P and
+    V would add about as much again.  A head with no such channel keeps the
+    FP8 P.V, which runs at the INT8 matrix rate.
+    """
+    a = np.asarray(shift)
+    return np.where(np.all(a == 0, axis=-1), PV_FP8, PV_16).astype(np.int64)
 
 
 def quantize_q(Q, shift=None):
