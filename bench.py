@@ -1,6 +1,6 @@
 """Throughput of the quantized attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload large] [--pv 16|fp8]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload large] [--pv 16|fp8|auto]
 
 One step = one sage_attn_fwd call: the quantize pass (K mean, channel balance,
 INT8 Q/K codes and scales, V layout) plus the fused attention kernel, over the
@@ -44,12 +44,20 @@ FP8_PEAK_TOPS = 5000.0    # dense FP8 MFMA, 5.0 PFLOP/s
 HBM_PEAK_GBS = 8000.0
 
 
-def mode_peak(pv_mode):
+PV_NAMES = {0: "16", 1: "fp8", 2: "auto"}
+
+
+def mode_peak(pv_mode, f8=None):
     """The MFMA ceiling of one P.V mode: half of the 4 d ops per visible pair
     (Q K^T) run on INT8 matrix cores, the other half (P V) on 16-bit or FP8
-    ones, so the time per op at peak is 0.5 / INT8 + 0.5 / (P.V peak)."""
-    pv = FP8_PEAK_TOPS if pv_mode == 1 else BF16_PEAK_TOPS
-    return 1.0 / (0.5 / INT8_PEAK_TOPS + 0.5 / pv)
+    ones, so the time per op at peak is 0.5 / INT8 + 0.5 / (P.V peak).  The
+    per-head mode (2) runs a share f8 of the heads' ops in FP8 and the rest
+    in 16 bits: the time per op is the share-weighted sum."""
+    t16 = 0.5 / INT8_PEAK_TOPS + 0.5 / BF16_PEAK_TOPS
+    t8 = 0.5 / INT8_PEAK_TOPS + 0.5 / FP8_PEAK_TOPS
+    if pv_mode == 2:
+        return 1.0 / (f8 * t8 + (1.0 - f8) * t16)
+    return 1.0 / (t8 if pv_mode == 1 else t16)
 
 
 def parse():
@@ -58,7 +66,9 @@ def parse():
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="large")
-    p.add_argument("--pv", default=None, choices=["16", "fp8"])
+    p.add_argument("--pv", default=None, choices=["16", "fp8", "auto"],
+                   help="P.V mode (default: the workload's own); auto = FP8 per head unless "
+                        "channel balance moved one of its channels")
     p.add_argument("--cpu-heads", type=int, default=None,
                    help="heads in the CPU oracle sample (default 8; 2 with a block mask)")
     p.add_argument("--cpu-rows", type=int, default=None,
@@ -227,7 +237,7 @@ def time_graph(torch, parts, steps, warm):
     return start.elapsed_time(end) / steps
 
 
-def quantize_bytes(w, pv_mode):
+def quantize_bytes(w, pv_mode, f8=None):
     """Bytes of the quantize pass: (the minimum, this design's kernels).
 
     The minimum reads K twice (the K mean needs every key before any key can
@@ -238,7 +248,9 @@ def quantize_bytes(w, pv_mode):
     all of Q has been read once; and in 16-bit mode it writes V transposed
     per 64-key chunk (the P.V operand layout), reading V once for that.  A
     streaming step over a frame cache moves only the current frame's K and
-    V and the queries (the mean and exponents are frozen)."""
+    V and the queries (the mean and exponents are frozen).  The per-head mode
+    (2) prepares V of a share f8 of the heads as in FP8 mode, the rest as in
+    16-bit mode."""
     esz = 2
     nq = w.B * w.H * w.Nq * w.d
     if w.frame_stride:
@@ -247,13 +259,12 @@ def quantize_bytes(w, pv_mode):
     else:
         nk = w.B * w.H * w.Nkv * w.d
         kreads = 2
-    vscale = nk // 32 if pv_mode == 1 else 0
-    minimum = nq * esz + kreads * nk * esz + nq + nk
-    if pv_mode == 1:
-        minimum += nk * esz + nk + vscale
+    s8 = {0: 0.0, 1: 1.0}.get(pv_mode, f8)      # share of V prepared as FP8
+    vscale = nk // 32
+    minimum = nq * esz + kreads * nk * esz + nq + nk + s8 * (nk * esz + nk + vscale)
     design = (1 if w.frame_stride else 2) * nq * esz + kreads * nk * esz + nq + nk + \
-        nk * esz + (nk + vscale if pv_mode == 1 else nk * esz)
-    return minimum, design
+        nk * esz + s8 * (nk + vscale) + (1 - s8) * nk * esz
+    return int(round(minimum)), int(round(design))
 
 
 def main():
@@ -281,7 +292,7 @@ def main():
     if args.cpu_rows is None:
         args.cpu_rows = 128 if w.block_density else 512
     if args.pv is not None:
-        w.pv_mode = 1 if args.pv == "fp8" else 0
+        w.pv_mode = {v: k for k, v in PV_NAMES.items()}[args.pv]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     x = workloads.make(w, dev)
@@ -315,22 +326,24 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     ops = w.ops()
-    other = None
+    others = []
     if not (args.profile or args.single_mode):
-        # the other P.V mode first, so that the headline mode's output stays in `o`
-        desc2, ws2, bufs2 = setup(1 - w.pv_mode)
-        t2 = time_path(torch, step_parts(sage, w, desc2, q, k, v, o, bufs2, stream), stream, steps, warm)
-        other = {"pv": "fp8" if w.pv_mode == 0 else "16",
-                 "value": round(ops / (t2[0] * 1e-3) / 1e12, 2),
-                 "attn_tops": round(ops / (t2[2] * 1e-3) / 1e12, 2),
-                 "attn_frac_int8_peak": round(ops / (t2[2] * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
-                 "ms_per_step": round(t2[0], 4)}
-        if not args.no_cpu:
-            other["accuracy"] = accuracy_sample(w, x, o, desc2, 1 - w.pv_mode, sage,
-                                                rows=64 if w.block_density else 256)
-            other["meets_bar"] = bool(other["accuracy"]["cosine_vs_fp64"] >= 0.999 and
-                                      other["accuracy"]["max_abs_vs_emulation"] <= 2e-3)
-        del ws2, bufs2
+        # the other P.V modes first, so that the headline mode's output stays in `o`
+        for m2 in ((0, 1) if w.pv_mode == 2 else (1 - w.pv_mode,)):
+            desc2, ws2, bufs2 = setup(m2)
+            t2 = time_path(torch, step_parts(sage, w, desc2, q, k, v, o, bufs2, stream), stream, steps, warm)
+            other = {"pv": PV_NAMES[m2],
+                     "value": round(ops / (t2[0] * 1e-3) / 1e12, 2),
+                     "attn_tops": round(ops / (t2[2] * 1e-3) / 1e12, 2),
+                     "attn_frac_int8_peak": round(ops / (t2[2] * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
+                     "ms_per_step": round(t2[0], 4)}
+            if not args.no_cpu:
+                other["accuracy"] = accuracy_sample(w, x, o, desc2, m2, sage,
+                                                    rows=64 if w.block_density else 256)
+                other["meets_bar"] = bool(other["accuracy"]["cosine_vs_fp64"] >= 0.999 and
+                                          other["accuracy"]["max_abs_vs_emulation"] <= 2e-3)
+            others.append(other)
+            del ws2, bufs2
     desc, ws, bufs = setup(w.pv_mode)
     ms_step, ms_quant, ms_attn, launches = time_path(torch, step_parts(sage, w, desc, q, k, v, o, bufs, stream),
                                                      stream, steps, warm)
@@ -349,10 +362,20 @@ def main():
 
     splits = sage.sage_attn_kv_splits(desc)
     attn_tops = ops / (ms_attn * 1e-3) / 1e12
-    pvname = "fp8" if w.pv_mode == 1 else "16"
+    pvname = PV_NAMES[w.pv_mode]
     traffic = kernel_traffic(w.name, pvname)
-    qmin, qdesign = quantize_bytes(w, w.pv_mode)
-    mpeak = mode_peak(w.pv_mode)
+    f8 = heads8 = None
+    if w.pv_mode == 2:
+        # which heads ran FP8 P.V (every channel-balance exponent 0), read
+        # back from the quantized operands after the timed steps; their share
+        # of the visible pairs weights the mode's ceiling
+        shift = sage.quant_views(desc, ws, bufs)["chan_shift"].cpu().numpy()
+        is8 = ~(shift != 0).any(axis=-1)                                   # [B,H]
+        heads8 = int(is8.sum())
+        pairs = np.asarray([1.0 if w.block_density else float(w.row_keys(b).sum()) for b in range(w.B)])
+        f8 = float((is8 * pairs[:, None]).sum() / (pairs.sum() * w.H))
+    qmin, qdesign = quantize_bytes(w, w.pv_mode, f8)
+    mpeak = mode_peak(w.pv_mode, f8)
     record = {
         "metric": METRIC,
         "value": round(tops, 2),
@@ -364,11 +387,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8+fp8" if w.pv_mode == 1 else ("int8+" + w.dtype),
+        "dtype": {0: "int8+" + w.dtype, 1: "int8+fp8", 2: "int8+fp8|" + w.dtype}[w.pv_mode],
         "data": "synthetic (seeded Gaussian, video-DiT token grid)",
         "input_digests": input_digests(torch, {"q": q, "k": k, "v": v}),
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nkv": w.Nkv, "d": w.d,
                    "in_dtype": w.dtype, "pv": pvname,
+                   **({"pv_heads": {"fp8": heads8, "16": w.B * w.H - heads8}} if heads8 is not None else {}),
                    "frame_len": w.frame_len, "kv_splits": splits,
                    **({"block_density": w.block_density, "kept_tiles": round(float(mask.mean()), 4)}
                       if mask is not None else {}),
@@ -379,9 +403,13 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel", "achieved": round(attn_tops, 2),
                      "peak": INT8_PEAK_TOPS, "unit": "TOPS", "frac": round(attn_tops / INT8_PEAK_TOPS, 4),
                      "mode_peak": round(mpeak, 1), "mode_frac": round(attn_tops / mpeak, 4),
-                     "mode_peak_note": ("Q K^T on INT8, P V on " + ("FP8" if w.pv_mode == 1 else "16-bit")
-                                        + " matrix cores: 1 / (0.5 / 5000 + 0.5 / "
-                                        + ("5000" if w.pv_mode == 1 else "2500") + ") TOPS"),
+                     "mode_peak_note": (("Q K^T on INT8, P V on " + ("FP8" if w.pv_mode == 1 else "16-bit")
+                                         + " matrix cores: 1 / (0.5 / 5000 + 0.5 / "
+                                         + ("5000" if w.pv_mode == 1 else "2500") + ") TOPS")
+                                        if w.pv_mode != 2 else
+                                        f"Q K^T on INT8; P V on FP8 for {f8:.3f} of the ops and on 16-bit "
+                                        "matrix cores for the rest: 1 / (f8 (0.5/5000 + 0.5/5000) + "
+                                        "(1 - f8) (0.5/5000 + 0.5/2500)) TOPS"),
                      "traffic": traffic, "ms_per_launch": round(ms_attn, 4), **launch_spread(launches)},
         "quantize": {"ms": round(ms_quant, 4), "algorithmic_bytes": qmin,
                      "GB_per_s": round(qmin / (ms_quant * 1e-3) / 1e9, 1),
@@ -398,8 +426,8 @@ def main():
         record["quantize"]["kind"] = ("append each session's frame + queries (sage_attn_quantize_frames_batched)"
                                       if per_batch else "append one frame + queries (sage_attn_quantize_frames)")
         record["quantize"]["whole_cache_ms"] = round(ms_full_quant, 4)
-    if other is not None:
-        record["other_pv_mode"] = other
+    if others:
+        record["other_pv_modes"] = others
     if not args.no_cpu and not args.profile:
         record["cpu_baseline"], record["parity"] = cpu_leg(w, x, o, desc, args, sage, torch, ops)
     print(json.dumps(record), flush=True)

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libsage_attn.so")
 
 SAGE_ATTN_ABI_VERSION = 4
 SAGE_F16, SAGE_BF16 = 0, 1
-SAGE_PV_16, SAGE_PV_FP8 = 0, 1
+SAGE_PV_16, SAGE_PV_FP8, SAGE_PV_AUTO = 0, 1, 2
 SAGE_FLAG_DEBUG_SYNC = 0x1
 SAGE_MAX_BATCH = 128
 SAGE_MAX_SPLITS = 16
@@ -298,6 +298,10 @@ def quant_views(desc, ws, bufs):
         return ws[off:off + n * esz].view(dtype).view(*shape)
 
     fp8 = desc.pv_mode == SAGE_PV_FP8
+    auto = desc.pv_mode == SAGE_PV_AUTO
+    # SAGE_PV_AUTO: raw bytes, Nkv_pad * d * 2 per head (a 16-bit head's
+    # values, or an FP8 head's codes in the first half)
+    vt_shape = (B, H, desc.Nkv_pad * d * 2) if auto else (B, H, desc.Nkv_pad // 64, d, 64)
     out = {
         "q_codes": view(bufs.q_codes, B * H * desc.Nq_pad * d, torch.int8, (B, H, desc.Nq_pad, d)),
         "q_scale": view(bufs.q_scale, B * H * desc.Nq_pad // 128, torch.float32, (B, H, desc.Nq_pad // 128)),
@@ -305,10 +309,10 @@ def quant_views(desc, ws, bufs):
         "k_scale": view(bufs.k_scale, B * H * desc.Nkv_pad // 64, torch.float32, (B, H, desc.Nkv_pad // 64)),
         "k_mean": view(bufs.k_mean, B * H * d, torch.float32, (B, H, d)),
         "chan_shift": view(bufs.chan_shift, B * H * d, torch.int8, (B, H, d)),
-        "v_t": view(bufs.v_t, B * H * desc.Nkv_pad * d, torch.uint8 if fp8 else torch.int16,
-                    (B, H, desc.Nkv_pad // 64, d, 64)),
+        "v_t": view(bufs.v_t, B * H * desc.Nkv_pad * d * (2 if auto else 1),
+                    torch.uint8 if fp8 or auto else torch.int16, vt_shape),
     }
-    if fp8:
+    if fp8 or auto:
         out["v_e8m0"] = view(bufs.v_e8m0, B * H * desc.Nkv_pad // 64 * 256, torch.uint8,
                              (B, H, desc.Nkv_pad // 64, 64, 4))
     return out

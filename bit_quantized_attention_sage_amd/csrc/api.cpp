@@ -104,7 +104,10 @@ sage_status make_plan(const sage_attn_desc* d, Plan* p) {
     return fail(SAGE_E_VERSION, "abi_version " + std::to_string(d->abi_version) + " != " +
                                     std::to_string(SAGE_ATTN_ABI_VERSION));
   if (d->dtype != SAGE_F16 && d->dtype != SAGE_BF16) return fail(SAGE_E_DTYPE, "dtype must be SAGE_F16 or SAGE_BF16");
-  if (d->pv_mode != SAGE_PV_16 && d->pv_mode != SAGE_PV_FP8) return fail(SAGE_E_DTYPE, "pv_mode must be SAGE_PV_16 or SAGE_PV_FP8");
+  if (d->pv_mode != SAGE_PV_16 && d->pv_mode != SAGE_PV_FP8 && d->pv_mode != SAGE_PV_AUTO)
+    return fail(SAGE_E_DTYPE, "pv_mode must be SAGE_PV_16, SAGE_PV_FP8 or SAGE_PV_AUTO");
+  if (d->pv_mode == SAGE_PV_AUTO && d->frame_stride != 0)
+    return fail(SAGE_E_UNSUPPORTED, "SAGE_PV_AUTO needs contiguous keys (frame_stride 0)");
   if (d->d != 64 && d->d != 128) return fail(SAGE_E_UNSUPPORTED, "head dim d must be 64 or 128");
   if (d->B < 1 || d->H < 1 || d->Nq < 1 || d->Nkv < 1) return fail(SAGE_E_SHAPE, "B, H, Nq and Nkv must be >= 1");
   if (d->B > SAGE_MAX_BATCH) return fail(SAGE_E_UNSUPPORTED, "B > SAGE_MAX_BATCH");
@@ -202,7 +205,7 @@ sage_status make_plan(const sage_attn_desc* d, Plan* p) {
 
 struct Layout {
   size_t q_codes, q_scale, k_codes, k_scale, k_mean, chan_shift, v_t, v_e8m0, stats, partial, total;
-  size_t ksum, kmax, kmin, qamax;  // offsets inside stats
+  size_t ksum, kmax, kmin, qamax, pick;  // offsets inside stats
 };
 
 Layout layout_of(const Plan& p) {
@@ -223,12 +226,13 @@ Layout layout_of(const Plan& p) {
   L.k_mean = take(bh * p.d * 4);
   L.chan_shift = take(bh * p.d);
   L.v_t = take(bh * p.Nkv_pad * p.d * (p.pv_mode == SAGE_PV_FP8 ? 1 : 2));
-  L.v_e8m0 = take(p.pv_mode == SAGE_PV_FP8 ? bh * (p.Nkv_pad / 64) * 256 : 0);
+  L.v_e8m0 = take(p.pv_mode != SAGE_PV_16 ? bh * (p.Nkv_pad / 64) * 256 : 0);
   L.ksum = 0;
   L.kmax = align_up(bh * nck * p.d * 8);
   L.kmin = L.kmax + align_up(bh * nck * p.d * 4);
   L.qamax = L.kmin + align_up(bh * nck * p.d * 4);
-  L.stats = take(L.qamax + bh * ncq * p.d * 4);
+  L.pick = L.qamax + align_up(bh * ncq * p.d * 4);
+  L.stats = take(L.pick + (p.pv_mode == SAGE_PV_AUTO ? 2 * (1 + bh) * 4 : 0));
   L.partial = take(p.splits_cap > 1 ? static_cast<size_t>(p.splits_cap) * bh * p.Nq_pad * (p.d + 2) * 4 : 0);
   L.total = off;
   return L;
@@ -244,7 +248,7 @@ sage_quant_bufs bufs_of(const Layout& L, const Plan& p, void* ws) {
   b.k_mean = reinterpret_cast<float*>(base + L.k_mean);
   b.chan_shift = reinterpret_cast<int8_t*>(base + L.chan_shift);
   b.v_t = base + L.v_t;
-  b.v_e8m0 = p.pv_mode == SAGE_PV_FP8 ? reinterpret_cast<uint8_t*>(base + L.v_e8m0) : nullptr;
+  b.v_e8m0 = p.pv_mode != SAGE_PV_16 ? reinterpret_cast<uint8_t*>(base + L.v_e8m0) : nullptr;
   b.stats = base + L.stats;
   b.partial = p.splits_cap > 1 ? base + L.partial : nullptr;
   b.partial_splits = p.splits_cap > 1 ? p.splits_cap : 1;
@@ -256,8 +260,11 @@ sage_status check_bufs(const sage_quant_bufs* b, const Plan& p, bool need_stats)
   if (!b) return fail(SAGE_E_NULL, "bufs is NULL");
   if (!b->q_codes || !b->q_scale || !b->k_codes || !b->k_scale || !b->k_mean || !b->chan_shift || !b->v_t)
     return fail(SAGE_E_NULL, "a quantized-operand buffer is NULL");
-  if (p.pv_mode == SAGE_PV_FP8 && !b->v_e8m0) return fail(SAGE_E_NULL, "v_e8m0 is NULL in FP8 mode");
-  if (need_stats && !b->stats) return fail(SAGE_E_NULL, "stats buffer is NULL");
+  if (p.pv_mode != SAGE_PV_16 && !b->v_e8m0) return fail(SAGE_E_NULL, "v_e8m0 is NULL in FP8 and AUTO modes");
+  if ((need_stats || p.pv_mode == SAGE_PV_AUTO) && !b->stats)
+    return fail(SAGE_E_NULL, need_stats ? "stats buffer is NULL" : "stats buffer is NULL (SAGE_PV_AUTO keeps its head lists there)");
+  if (p.pv_mode == SAGE_PV_AUTO && (reinterpret_cast<uintptr_t>(b->stats) & 3u))
+    return fail(SAGE_E_ALIGN, "stats must be 4-byte aligned");
   if (p.splits > 1 && !need_stats) {
     if (!b->partial) return fail(SAGE_E_NULL, "partial buffer is NULL with kv_splits > 1");
     if (p.splits > b->partial_splits)
@@ -305,6 +312,9 @@ sage::AttnLaunch attn_launch_of(const Plan& p, const sage_quant_bufs& b, void* o
   L.bufs = b;
   L.o = o;
   for (int i = 0; i < 3; ++i) L.os[i] = d->o_stride[i];
+  L.vt_hb = static_cast<int64_t>(p.Nkv_pad) * p.d * (p.pv_mode == SAGE_PV_FP8 ? 1 : 2);
+  L.pick = p.pv_mode == SAGE_PV_AUTO ? reinterpret_cast<int*>(static_cast<char*>(b.stats) + layout_of(p).pick)
+                                     : nullptr;
   return L;
 }
 

@@ -149,6 +149,9 @@ struct AttnArgs {
   int mask_nkc;
   BatchInfo bi;
   int order[MAXB_ARGS];
+  int64_t vt_hb;    // bytes of one (b,h)'s V^T operand
+  const int* pick;  // per-head P.V mode: this launch's heads ([0] = count,
+                    // then b*H + h in batch order); null: every head
 };
 
 // LDS layout of a staged chunk.  K: [64 keys][D] bytes with the granule
@@ -605,7 +608,7 @@ struct Stager {
   __device__ __forceinline__ void init(const AttnArgs& A, int bh, int wave, int lane) {
     const int nkc = A.Nkv_pad / 64;
     const int8_t* kbase = A.kc + static_cast<int64_t>(bh) * A.Nkv_pad * D;
-    const uint8_t* vbase = static_cast<const uint8_t*>(A.vt) + static_cast<int64_t>(bh) * nkc * VBC;
+    const uint8_t* vbase = static_cast<const uint8_t*>(A.vt) + static_cast<int64_t>(bh) * A.vt_hb;
     const uint8_t* ebase = A.ve + static_cast<int64_t>(bh) * nkc * 256;
     const float* ksc = A.kscale + static_cast<int64_t>(bh) * nkc;
     krs = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(kbase), 0, nkc * KB, 0x00020000);
@@ -649,6 +652,9 @@ __device__ __forceinline__ void dma_wait() { __builtin_amdgcn_s_waitcnt(0x0F70);
 
 // Decode a work item (batch by decreasing kv_len, head, split, query tile)
 // from a physical workgroup id: the tiles of one (b, h, split) share an XCD.
+// With a head list (PICK: per-head P.V mode) the items are those of the
+// listed heads, in list order; the launch has room for every head, and
+// workgroups past the list's items have nothing to do (pick_live).
 struct Item {
   int b, h, split, qt, bh;
   __device__ __forceinline__ Item(const AttnArgs& A, int ntile) {
@@ -662,7 +668,19 @@ struct Item {
     qt = rem % ntile;
     bh = b * A.H + h;
   }
+  __device__ __forceinline__ Item(const AttnArgs& A, int ntile, int total) {
+    const int per_bh = A.splits * ntile;
+    const int L = xcd_group_remap(blockIdx.x, total, ntile);
+    bh = A.pick[1 + L / per_bh];
+    b = bh / A.H;
+    h = bh - b * A.H;
+    const int rem = L % per_bh;
+    split = rem / ntile;
+    qt = rem % ntile;
+  }
 };
+
+__device__ __forceinline__ int pick_items(const AttnArgs& A, int ntile) { return A.pick[0] * A.splits * ntile; }
 
 // Normalise and store this lane's row of O, or (with KV splits) its
 // unnormalised-by-merge partial: O / l and (m, l).
@@ -726,7 +744,7 @@ __device__ __forceinline__ bool mask_chunk(const WorkList<MODE>& wl, WaveState<D
   return apply_mask(wl, st, v, s0, s1, h2);
 }
 
-template <int D, int PV, int DT, int MODE>
+template <int D, int PV, int DT, int MODE, bool PICK>
 __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs A) {
   constexpr bool SPARSE = MODE == KV_SPARSE;
   constexpr int NWAVE = 8;
@@ -751,7 +769,12 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs A) {
   const int h2 = lane >> 5;
 
   const int ntile = (A.nqt + 1) / 2;  // tiles of two 128-row Q blocks
-  const Item it(A, ntile);
+  int pick_total = 0;
+  if constexpr (PICK) {
+    pick_total = pick_items(A, ntile);
+    if (static_cast<int>(blockIdx.x) >= pick_total) return;  // uniform, before any barrier
+  }
+  const Item it = PICK ? Item(A, ntile, pick_total) : Item(A, ntile);
   const int b = it.b, h = it.h, split = it.split, qt = it.qt, bh = it.bh;
   // this wave's group, its place in the group and its 128-row Q block (the
   // second block of the last tile may lie past Nq: its rows load the last
@@ -1080,6 +1103,56 @@ hipError_t scratch_address(void** ptr) {
   return hipSuccess;
 }
 
+// ------------------------------------------------- per-head P.V mode lists
+// One workgroup lists the heads of each mode, in batch order (A.order) and
+// head order: pick[0] = count and pick[1..] the 16-bit heads (some
+// channel-balance exponent != 0), pick[1 + BH] = count and pick[2 + BH..] the
+// FP8 heads (every exponent 0).
+template <int D>
+__global__ __launch_bounds__(256) void pick_heads_kernel(AttnArgs A, const int8_t* __restrict__ shift,
+                                                         int* __restrict__ pick) {
+  __shared__ int cnt[2][4];
+  const int n = A.B * A.H, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const uint64_t below = lane ? (~uint64_t{0} >> (64 - lane)) : 0;
+  int base16 = 0, base8 = 0;
+  for (int i0 = 0; i0 < n; i0 += 256) {
+    const int i = i0 + threadIdx.x;
+    const bool valid = i < n;
+    int bh = 0;
+    bool moved = false;
+    if (valid) {
+      bh = A.order[i / A.H] * A.H + i % A.H;
+      const int8_t* sp = shift + static_cast<int64_t>(bh) * D;
+#pragma unroll 8
+      for (int c = 0; c < D; ++c) moved |= sp[c] != 0;
+    }
+    const uint64_t m16 = __ballot(valid && moved), m8 = __ballot(valid && !moved);
+    if (lane == 0) {
+      cnt[0][w] = __popcll(m16);
+      cnt[1][w] = __popcll(m8);
+    }
+    __syncthreads();
+    int o16 = base16, o8 = base8;
+    for (int k = 0; k < w; ++k) {
+      o16 += cnt[0][k];
+      o8 += cnt[1][k];
+    }
+    if (valid) {
+      if (moved) pick[1 + o16 + __popcll(m16 & below)] = bh;
+      else pick[2 + n + o8 + __popcll(m8 & below)] = bh;
+    }
+    for (int k = 0; k < 4; ++k) {
+      base16 += cnt[0][k];
+      base8 += cnt[1][k];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    pick[0] = base16;
+    pick[1 + n] = base8;
+  }
+}
+
 // ---------------------------------------------------------------- launchers
 static AttnArgs make_args(const AttnLaunch& L) {
   AttnArgs A{};
@@ -1117,18 +1190,40 @@ static AttnArgs make_args(const AttnLaunch& L) {
   A.mask_nkc = L.mask_nkc;
   A.bi = L.bi;
   for (int i = 0; i < MAXB_ARGS; ++i) A.order[i] = L.order[i];
+  A.vt_hb = L.vt_hb;
+  A.pick = nullptr;
   return A;
 }
 
-template <int D, int PV, int DT>
-static hipError_t attn_impl(const AttnLaunch& L, hipStream_t st) {
-  const AttnArgs A = make_args(L);
-  if (L.block_mask)
-    hipLaunchKernelGGL((attn_fwd_kernel<D, PV, DT, KV_SPARSE>), dim3(A.total), dim3(512), 0, st, A);
-  else if (L.frame_stride > 0)
-    hipLaunchKernelGGL((attn_fwd_kernel<D, PV, DT, KV_CACHE>), dim3(A.total), dim3(512), 0, st, A);
+template <int D, int PV, int DT, bool PICK>
+static void attn_launch(const AttnArgs& A, bool sparse, bool cache, hipStream_t st) {
+  if (sparse)
+    hipLaunchKernelGGL((attn_fwd_kernel<D, PV, DT, KV_SPARSE, PICK>), dim3(A.total), dim3(512), 0, st, A);
+  else if (cache)
+    hipLaunchKernelGGL((attn_fwd_kernel<D, PV, DT, KV_CACHE, false>), dim3(A.total), dim3(512), 0, st, A);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<D, PV, DT, KV_DENSE>), dim3(A.total), dim3(512), 0, st, A);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, PV, DT, KV_DENSE, PICK>), dim3(A.total), dim3(512), 0, st, A);
+}
+
+// One launch of the fused kernel in the P.V mode of the call, or (PVAUTO) the
+// head lists, then one launch per mode over its own heads; then the merge of
+// the KV splits.
+template <int D, int DT>
+static hipError_t attn_impl(const AttnLaunch& L, hipStream_t st) {
+  AttnArgs A = make_args(L);
+  const bool sparse = L.block_mask != nullptr, cache = L.frame_stride > 0;
+  if (L.pv_mode == PVAUTO) {
+    hipLaunchKernelGGL(pick_heads_kernel<D>, dim3(1), dim3(256), 0, st, A, L.bufs.chan_shift, L.pick);
+    A.pick = L.pick;
+    attn_launch<D, PV16, DT, true>(A, sparse, cache, st);
+    A.pick = L.pick + 1 + L.B * L.H;
+    attn_launch<D, PVFP8, DT, true>(A, sparse, cache, st);
+    A.pick = nullptr;
+  } else if (L.pv_mode == PVFP8) {
+    attn_launch<D, PVFP8, DT, false>(A, sparse, cache, st);
+  } else {
+    attn_launch<D, PV16, DT, false>(A, sparse, cache, st);
+  }
   if (L.splits > 1) {
     const int64_t threads = static_cast<int64_t>(L.B) * L.H * L.Nq_pad * (D / 4);
     hipLaunchKernelGGL((attn_combine_kernel<D, DT>), dim3(static_cast<unsigned>((threads + 255) / 256)),
@@ -1139,9 +1234,7 @@ static hipError_t attn_impl(const AttnLaunch& L, hipStream_t st) {
 
 template <int D>
 static hipError_t attn_d(const AttnLaunch& L, hipStream_t st) {
-  if (L.pv_mode == PVFP8)
-    return L.dtype == DT_BF16 ? attn_impl<D, PVFP8, DT_BF16>(L, st) : attn_impl<D, PVFP8, DT_F16>(L, st);
-  return L.dtype == DT_BF16 ? attn_impl<D, PV16, DT_BF16>(L, st) : attn_impl<D, PV16, DT_F16>(L, st);
+  return L.dtype == DT_BF16 ? attn_impl<D, DT_BF16>(L, st) : attn_impl<D, DT_F16>(L, st);
 }
 
 hipError_t launch_attention(const AttnLaunch& L, hipStream_t st) {

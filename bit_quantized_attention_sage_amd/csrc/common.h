@@ -23,7 +23,7 @@ constexpr int NPAD = 128;        // Nq and Nkv are padded to multiples of this
 constexpr int MAXB = 256;        // largest batch handled through kernel arguments
 
 enum { DT_F16 = 0, DT_BF16 = 1 };
-enum { PV16 = 0, PVFP8 = 1 };
+enum { PV16 = 0, PVFP8 = 1, PVAUTO = 2 };  // PVAUTO: per (b,h) from the channel-balance exponents
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));

@@ -50,6 +50,9 @@ struct AttnLaunch {
   sage_quant_bufs bufs;
   void* o;
   int64_t os[3];
+  int64_t vt_hb;  // bytes of one (b,h)'s V^T operand in bufs.v_t
+  int* pick;      // SAGE_PV_AUTO: [1 + B*H] 16-bit heads then [1 + B*H] FP8
+                  // heads (count, then b*H + h in batch order); else null
 };
 
 // Per-block W8A8 linear layer (w8a8.hip).

@@ -272,11 +272,15 @@ __global__ __launch_bounds__(256) void quant_i8_kernel(
 // channel) -- the smallest power of two 2^e >= 2^-127 with amax * 2^-e <= 448 -- and
 // e4m3fn codes of v * 2^-e; the scales of a chunk are stored as 64 lanes x 4
 // bytes (lane 32*k + r holds channels r, r+32, r+64, r+96 of key block k).
-template <typename T, int D, bool FP8>
+//
+// VM: PV16, PVFP8, or PVAUTO -- each (b,h) in FP8 when its channel-balance
+// exponents (shift) are all 0, else in 16 bits; every head then has a 16-bit
+// sized slot, an FP8 head's codes filling its first half.
+template <typename T, int D, int VM>
 __global__ __launch_bounds__(2 * D) void prep_v_kernel(
     const T* __restrict__ x, int64_t sb, int64_t sh, int64_t sn, int H, int n_pad,
-    BatchInfo bi, void* __restrict__ vt, uint8_t* __restrict__ e8m0, int F, int FS, int tok0, int n_in,
-    int ch0) {
+    BatchInfo bi, void* __restrict__ vt, uint8_t* __restrict__ e8m0, const int8_t* __restrict__ shift, int F,
+    int FS, int tok0, int n_in, int ch0) {
   __shared__ uint16_t tile[64][D + 2];
   const int b = blockIdx.z, h = blockIdx.y;
   if (ch0 < 0) {  // per-batch frame appends (as in quant_i8_kernel)
@@ -297,15 +301,23 @@ __global__ __launch_bounds__(2 * D) void prep_v_kernel(
     for (int c = 0; c < 8; ++c) tile[r][8 * g + c] = static_cast<uint16_t>((w[c / 2] >> (16 * (c % 2))) & 0xFFFFu);
   }
   __syncthreads();
+  bool fp8 = VM == PVFP8;
+  if constexpr (VM == PVAUTO) {
+    bool moved = false;
+    if (threadIdx.x < D) moved = shift[static_cast<int64_t>(bh) * D + threadIdx.x] != 0;
+    fp8 = !__syncthreads_or(moved);
+  }
   const int c = threadIdx.x >> 1, kh = threadIdx.x & 1;
-  const int64_t chunk_base = (static_cast<int64_t>(bh) * (n_pad / 64) + ch) * D * 64;
-  if (!FP8) {
+  const int64_t head_bytes = static_cast<int64_t>(n_pad) * D * (VM == PVFP8 ? 1 : 2);
+  uint8_t* const vhead = static_cast<uint8_t*>(vt) + static_cast<int64_t>(bh) * head_bytes;
+  const int64_t chunk_base = static_cast<int64_t>(ch) * D * 64;  // elements into the head
+  if (!fp8) {
     uint32_t w[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k)
       w[k] = static_cast<uint32_t>(tile[32 * kh + 2 * k][c]) |
              (static_cast<uint32_t>(tile[32 * kh + 2 * k + 1][c]) << 16);
-    uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(vt) + chunk_base + c * 64 + 32 * kh);
+    uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(vhead) + chunk_base + c * 64 + 32 * kh);
 #pragma unroll
     for (int k = 0; k < 4; ++k) dst[k] = make_uint4(w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]);
   } else {
@@ -329,7 +341,7 @@ __global__ __launch_bounds__(2 * D) void prep_v_kernel(
 #pragma unroll
     for (int k = 0; k < 8; ++k)
       w[k] = pack_e4m3x4(f[4 * k] * sc, f[4 * k + 1] * sc, f[4 * k + 2] * sc, f[4 * k + 3] * sc);
-    uint4* dst = reinterpret_cast<uint4*>(static_cast<uint8_t*>(vt) + chunk_base + c * 64 + 32 * kh);
+    uint4* dst = reinterpret_cast<uint4*>(vhead + chunk_base + c * 64 + 32 * kh);
     dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
     dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
     // E8M0 layout per chunk: [lane = 32*kh + c%32][byte = c/32], four bytes per
@@ -396,13 +408,17 @@ static hipError_t quantize_impl(const QuantLaunch& L, hipStream_t st) {
                      static_cast<const T*>(L.k), L.ks[0], L.ks[1], L.ks[2], L.H, L.Nkv, L.Nkv_pad, L.bi,
                      L.bufs.k_mean, L.bufs.chan_shift, L.bufs.k_codes, L.bufs.k_scale, F, FS, tok0, n_in, c0);
   if (L.pv_mode == PVFP8)
-    hipLaunchKernelGGL((prep_v_kernel<T, D, true>), dim3(nc, L.H, L.B), dim3(2 * D), 0, st,
+    hipLaunchKernelGGL((prep_v_kernel<T, D, PVFP8>), dim3(nc, L.H, L.B), dim3(2 * D), 0, st,
                        static_cast<const T*>(L.v), L.vs[0], L.vs[1], L.vs[2], L.H, L.Nkv_pad, L.bi,
-                       L.bufs.v_t, L.bufs.v_e8m0, F, FS, tok0, n_in, c0);
+                       L.bufs.v_t, L.bufs.v_e8m0, L.bufs.chan_shift, F, FS, tok0, n_in, c0);
+  else if (L.pv_mode == PVAUTO)
+    hipLaunchKernelGGL((prep_v_kernel<T, D, PVAUTO>), dim3(nc, L.H, L.B), dim3(2 * D), 0, st,
+                       static_cast<const T*>(L.v), L.vs[0], L.vs[1], L.vs[2], L.H, L.Nkv_pad, L.bi,
+                       L.bufs.v_t, L.bufs.v_e8m0, L.bufs.chan_shift, F, FS, tok0, n_in, c0);
   else
-    hipLaunchKernelGGL((prep_v_kernel<T, D, false>), dim3(nc, L.H, L.B), dim3(2 * D), 0, st,
+    hipLaunchKernelGGL((prep_v_kernel<T, D, PV16>), dim3(nc, L.H, L.B), dim3(2 * D), 0, st,
                        static_cast<const T*>(L.v), L.vs[0], L.vs[1], L.vs[2], L.H, L.Nkv_pad, L.bi,
-                       L.bufs.v_t, L.bufs.v_e8m0, F, FS, tok0, n_in, c0);
+                       L.bufs.v_t, L.bufs.v_e8m0, L.bufs.chan_shift, F, FS, tok0, n_in, c0);
   return hipGetLastError();
 }
 

@@ -19,7 +19,11 @@
  *     fp32, online softmax in fp32 over 64-key chunks with a lazy running max;
  *   - P V on 16-bit matrix cores (P rounded to the input type) or, in FP8
  *     mode, on scaled FP8 matrix cores: P as OCP e4m3fn (pre-scaled by 2^4),
- *     V as e4m3fn with one E8M0 scale per (32-key block, channel).
+ *     V as e4m3fn with one E8M0 scale per (32-key block, channel);
+ *   - per-head mode (SAGE_PV_AUTO, contiguous keys only): FP8 P V for a
+ *     (b,h) whose channel-balance exponents are all 0, 16-bit P V for one
+ *     with an outlier channel (some a != 0), whose INT8 scores already take
+ *     much of the output's error budget.
  * Frame-block-causal mask for streaming against a KV cache (the Vidu S1 blog,
  * sections "模型架构", "训练方法" and "Infra": frame-by-frame causal
  * generation over cached history): with frame length F > 0, query i
@@ -101,7 +105,8 @@ typedef enum {
 } sage_status;
 
 enum { SAGE_F16 = 0, SAGE_BF16 = 1 };       /* sage_attn_desc.dtype          */
-enum { SAGE_PV_16 = 0, SAGE_PV_FP8 = 1 };   /* sage_attn_desc.pv_mode        */
+enum { SAGE_PV_16 = 0, SAGE_PV_FP8 = 1,     /* sage_attn_desc.pv_mode        */
+       SAGE_PV_AUTO = 2 };                  /* per (b,h), from chan_shift    */
 
 #define SAGE_FLAG_DEBUG_SYNC 0x1u  /* synchronize the stream after each launch */
 #define SAGE_MAX_BATCH 128
@@ -111,7 +116,8 @@ enum { SAGE_PV_16 = 0, SAGE_PV_FP8 = 1 };   /* sage_attn_desc.pv_mode        */
 typedef struct sage_attn_desc {
   int32_t abi_version;  /* must be SAGE_ATTN_ABI_VERSION                      */
   int32_t dtype;        /* SAGE_F16 | SAGE_BF16: Q, K, V and O share it       */
-  int32_t pv_mode;      /* SAGE_PV_16 | SAGE_PV_FP8                           */
+  int32_t pv_mode;      /* SAGE_PV_16 | SAGE_PV_FP8 | SAGE_PV_AUTO (the last
+                           with frame_stride 0 only: SAGE_E_UNSUPPORTED)     */
   int32_t B, H, Nq, Nkv, d; /* Nkv = allocated key length (>= every kv_len) */
   int32_t frame_len;    /* 0: no mask; > 0: frame-block-causal, F tokens      */
   int32_t kv_splits;    /* 0: chosen by the library; 1..SAGE_MAX_SPLITS       */
@@ -150,11 +156,18 @@ typedef struct sage_quant_bufs {
   int8_t *chan_shift;  /* [B,H,d] channel-balance exponents a                 */
   void *v_t;           /* [B,H,Nkv_pad/64,d,64]: per 64-key chunk, V transposed
                           (channel-major); 16-bit values in SAGE_PV_16 mode,
-                          e4m3fn codes in SAGE_PV_FP8 mode                    */
-  uint8_t *v_e8m0;     /* FP8 mode: E8M0 scale bytes, [B,H,Nkv_pad/64,64,4]:
-                          per 64-key chunk, byte [32k + r][cb] scales channel
-                          32cb + r of keys [32k, 32k+32); else NULL           */
-  void *stats;         /* internal: partial statistics of the quantize pass   */
+                          e4m3fn codes in SAGE_PV_FP8 mode.  SAGE_PV_AUTO:
+                          Nkv_pad*d*2 bytes per (b,h), holding that head's
+                          16-bit values, or its e4m3fn codes in the first
+                          Nkv_pad*d bytes                                    */
+  uint8_t *v_e8m0;     /* FP8 and AUTO modes: E8M0 scale bytes,
+                          [B,H,Nkv_pad/64,64,4]: per 64-key chunk, byte
+                          [32k + r][cb] scales channel 32cb + r of keys
+                          [32k, 32k+32) (AUTO: written for the FP8 heads
+                          only); else NULL                                   */
+  void *stats;         /* internal: partial statistics of the quantize pass;
+                          SAGE_PV_AUTO also keeps each mode's head list here,
+                          so the attention calls need it in that mode        */
   void *partial;       /* internal: split-KV partial results                  */
   int32_t partial_splits; /* KV splits `partial` holds room for (set by
                           sage_attn_quant_layout): a call whose split count
@@ -235,8 +248,11 @@ sage_status sage_attn_quantize_frames_batched(const sage_attn_desc *desc, const 
                                               void *stream);
 
 /* Fused attention on already-quantized operands: writes O [B,H,Nq,d].
- * Errors: SAGE_E_WORKSPACE if the call needs more KV splits than
- * bufs->partial_splits (a workspace carved for another desc). */
+ * SAGE_PV_AUTO: the heads are split by their exponents in bufs->chan_shift
+ * on the device (lists in bufs->stats) and each mode runs as its own launch
+ * over its own heads.  Errors: SAGE_E_WORKSPACE if the call needs more KV
+ * splits than bufs->partial_splits (a workspace carved for another desc);
+ * SAGE_E_NULL for SAGE_PV_AUTO without bufs->stats. */
 sage_status sage_attn_fwd_quantized(const sage_attn_desc *desc, const sage_quant_bufs *bufs,
                                     void *o, void *stream);
 

@@ -6,7 +6,7 @@ import torch
 
 import bit_quantized_attention_sage_amd as sage
 from oracle import quant, emulate, attention, codecs
-from oracle.constants import BK, PV_FP8
+from oracle.constants import BK, PV_16, PV_FP8, PV_AUTO
 
 SAGE_DT = {torch.float16: sage.SAGE_F16, torch.bfloat16: sage.SAGE_BF16}
 NAME_DT = {torch.float16: "f16", torch.bfloat16: "bf16"}
@@ -52,6 +52,32 @@ def check_quantized(views, Q, K, V, pv_mode, dtype, kv_len=None, mu_in=None):
     gks = views["k_scale"].cpu().numpy()
     np.testing.assert_array_equal(gks[:, :, :dk.shape[2]], dk)
     assert not gks[:, :, dk.shape[2]:].any()
+    if pv_mode == PV_AUTO:
+        # each head in its own mode, in a 16-bit sized slot (an FP8 head's
+        # codes in its first half); E8M0 scales written for FP8 heads only
+        modes = quant.pv_modes_auto(a)
+        raw = views["v_t"].cpu()                                  # [B,H,Nkv_pad*d*2] bytes
+        nch = raw.shape[2] // (2 * 64 * d)
+        for m in (PV_16, PV_FP8):
+            for b in range(B):
+                hs = [h for h in range(H) if modes[b, h] == m]
+                if not hs:
+                    continue
+                sub = {"v_e8m0": views["v_e8m0"][b:b + 1, hs]}
+                if m == PV_FP8:
+                    sub["v_t"] = raw[b:b + 1, hs, :nch * 64 * d].reshape(1, len(hs), nch, d, 64)
+                else:
+                    sub["v_t"] = raw[b:b + 1, hs].view(torch.int16).reshape(1, len(hs), nch, d, 64)
+                _check_v(sub, V[b:b + 1, hs], m, dtype, None if kv_len is None else [kv_len[b]])
+        return mu
+    _check_v(views, V, pv_mode, dtype, kv_len)
+    return mu
+
+
+def _check_v(views, V, pv_mode, dtype, kv_len):
+    """V's P.V operand in one mode: FP8 codes and E8M0 scales, or the 16-bit
+    values, in the chunked transposed layout."""
+    B, H, Nkv, d = V.shape
     vt = views["v_t"].cpu()
     untiled = vt.permute(0, 1, 2, 4, 3).reshape(B, H, -1, d)
     if pv_mode == PV_FP8:
@@ -74,7 +100,6 @@ def check_quantized(views, Q, K, V, pv_mode, dtype, kv_len=None, mu_in=None):
         ref_bits = codecs.bf16_bits(vv) if dtype == "bf16" else vv.astype(np.float16).view(np.uint16)
         np.testing.assert_array_equal(g[:, :, :Nkv], ref_bits)
         assert not g[:, :, Nkv:].any()
-    return mu
 
 
 # ---------------------------------------------------------------- tolerances
@@ -152,13 +177,14 @@ def output_bound(o64, aux, dtype, pv_mode, splits=None):
     S = aux.get("splits", 1) if splits is None else splits
     O = np.abs(o64)
     a = aux["a"]
-    keys_per_op = 64 if pv_mode == PV_FP8 else 16
+    # per head under PV_AUTO (the modes the emulation ran), else one mode
+    fp8 = (aux["pv_modes"] == PV_FP8)[:, :, None] if pv_mode == PV_AUTO else pv_mode == PV_FP8
+    keys_per_op = np.where(fp8, 64, 16)
     steps = (np.ceil(aux["nvis"] / keys_per_op) + aux["nres"] + 8)[..., None]
     fac = steps * 2.0 ** -24 + 2 * aux["nres"][..., None] * REL_EXP
     if S > 1:
         fac = fac + (2 * S + 4) * 2.0 ** -24 + 2 * REL_EXP
-    if pv_mode == PV_FP8:
-        fac = fac + FP8_ACC
+    fac = fac + np.where(np.asarray(fp8)[..., None], FP8_ACC, 0.0)
     other = aux["flip"] + fac * (a + O)
     return other + 0.5 * ulp16(O + other, dtype) + 1e-30
 

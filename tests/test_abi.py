@@ -108,6 +108,27 @@ def test_bad_descriptors_are_rejected(lib, kw, code):
     assert sage.load().sage_attn_last_error()
 
 
+def test_per_head_mode_layout_and_validation(lib):
+    """SAGE_PV_AUTO: a 16-bit sized V^T slot per head, the E8M0 region and
+    the head lists; refused over a frame cache; its attention call needs the
+    stats buffer (where the lists live)."""
+    assert sage.SAGE_PV_AUTO == oc.PV_AUTO
+    st16, n16 = _status(_desc())
+    st8, n8 = _status(_desc(pv_mode=sage.SAGE_PV_FP8))
+    sta, na = _status(_desc(pv_mode=sage.SAGE_PV_AUTO))
+    assert st16 == st8 == sta == 0 and na > n16 > n8
+    d = _desc(pv_mode=sage.SAGE_PV_AUTO)
+    b = sage.sage_quant_bufs()
+    fake = 1 << 20
+    L = sage.load()
+    assert L.sage_attn_quant_layout(d.ptr, ctypes.c_void_p(fake), na, ctypes.byref(b)) == 0
+    assert b.v_e8m0 and b.stats and b.v_e8m0 - b.v_t >= 2 * 2 * 384 * 128
+    b.stats = None
+    assert L.sage_attn_fwd_quantized(d.ptr, ctypes.byref(b), ctypes.c_void_p(fake), None) == 1
+    assert "stats" in L.sage_attn_last_error().decode()
+    assert _status(_desc(pv_mode=sage.SAGE_PV_AUTO, frame_len=50, frame_stride=64, Nkv=320, Nq=50))[0] == 7
+
+
 def test_version_mismatch(lib):
     d = _desc()
     d.c.abi_version = 7
