@@ -400,7 +400,9 @@ def main():
                        "window_frames": w.window_frames, "kv_len": w.kv_lens(), "q_pos0": w.q_pos0s()}
                       if w.frame_stride else {}),
                    "ops_per_step": ops, "pct_int8_peak": round(100 * tops / INT8_PEAK_TOPS, 2)},
-        "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel", "achieved": round(attn_tops, 2),
+        "roofline": {"bound": "mfma",
+                     "kernel": "attn_fwd_kernel" + (" (one launch per P.V mode)" if w.pv_mode == 2 else ""),
+                     "achieved": round(attn_tops, 2),
                      "peak": INT8_PEAK_TOPS, "unit": "TOPS", "frac": round(attn_tops / INT8_PEAK_TOPS, 4),
                      "mode_peak": round(mpeak, 1), "mode_frac": round(attn_tops / mpeak, 4),
                      "mode_peak_note": (("Q K^T on INT8, P V on " + ("FP8" if w.pv_mode == 1 else "16-bit")

@@ -15,7 +15,7 @@ import torch
 import bit_quantized_attention_sage_amd as sage
 import workloads
 from oracle import emulate, attention
-from oracle.constants import PV_16, PV_FP8
+from oracle.constants import PV_16, PV_FP8, PV_AUTO
 from gpu_util import host, assert_close, cosine, NAME_DT, KERNEL_SLACK
 
 pytestmark = pytest.mark.gpu
@@ -172,8 +172,8 @@ SPARSE_FP8_REASON = ("FP8 P.V on the sparse workload (the large workload's outli
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("pv_mode", [PV_16, pytest.param(PV_FP8, marks=pytest.mark.skip(reason=SPARSE_FP8_REASON))],
-                         ids=["pv16", "pvfp8"])
+@pytest.mark.parametrize("pv_mode", [PV_16, PV_AUTO, pytest.param(PV_FP8, marks=pytest.mark.skip(reason=SPARSE_FP8_REASON))],
+                         ids=["pv16", "pvauto", "pvfp8"])
 def test_sparse_workload_parity(lib, pv_mode):
     """The sparse workload at full size (the large workload with 25% of its
     tiles kept) in the launch configuration bench.py times; outputs of 3
