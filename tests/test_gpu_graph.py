@@ -15,7 +15,7 @@ import pytest
 import torch
 
 import bit_quantized_attention_sage_amd as sage
-from oracle.constants import PV_16, PV_FP8
+from oracle.constants import PV_16, PV_FP8, PV_AUTO
 
 pytestmark = pytest.mark.gpu
 
@@ -64,6 +64,38 @@ def test_drop_in_call_replays_like_eager(lib, pv_mode):
         sage.sage_attn_fwd(desc, q, k, v, ref, ws_ref)
         torch.cuda.synchronize()
         print(f"  replay {r}: equal {torch.equal(got, ref)}", flush=True)
+        assert torch.equal(got, ref)
+
+
+def test_per_head_mode_replays_like_eager(lib):
+    """sage_attn_fwd in the per-head P.V mode (head lists built on the device,
+    one fused-kernel launch per mode, 2 KV splits).  Between replays the
+    inputs change which heads carry an outlier K channel, so each replay
+    must take its head split from the device, not from the capture."""
+    B, H, Nq, Nkv, d = 1, 4, 400, 1500, 128
+    q, k, v = _rand((B, H, Nq, d), 21), _rand((B, H, Nkv, d), 22), _rand((B, H, Nkv, d), 23)
+    base = k.clone()
+    o = torch.empty_like(q)
+    desc = sage.Desc.for_tensors(q, k, v, o, pv_mode=PV_AUTO, kv_splits=2)
+    ws = sage.new_workspace(desc, q.device)
+    g = _capture(lambda: sage.sage_attn_fwd(desc, q, k, v, o, ws))
+    for r, heads in enumerate([[0], [1, 3], [], [0, 1, 2, 3]]):
+        k.copy_(base)
+        for h in heads:
+            k[0, h, :, 17] *= 8                  # an outlier channel: 16-bit P.V for that head
+        o.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = o.clone()
+        ref = torch.empty_like(q)
+        ws_ref = sage.new_workspace(desc, q.device)
+        sage.sage_attn_fwd(desc, q, k, v, ref, ws_ref)
+        torch.cuda.synchronize()
+        moved = (sage.quant_views(desc, ws, sage.sage_attn_quant_layout(desc, ws))["chan_shift"] != 0)
+        split = moved.any(dim=-1)[0].nonzero().flatten().tolist()
+        print(f"  replay {r}: 16-bit heads {split}, equal {torch.equal(got, ref)}", flush=True)
+        assert split == heads
         assert torch.equal(got, ref)
 
 
