@@ -435,6 +435,38 @@ def main():
     print(json.dumps(record), flush=True)
 
 
+def library_gemms(torch, w, x, wt, steps, warm):
+    """The ROCm libraries on the same shape, for context (not the metric):
+    torch._int_mm (INT8 codes -> int32, no scales, no bias) and the
+    unquantized bf16 layer (torch.nn.functional.linear), each timed like a
+    step (HIP events around `steps` calls after `warm`)."""
+    ops = w.ops()
+    out = {}
+
+    def clock(fn):
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(steps):
+            fn()
+        e.record()
+        e.synchronize()
+        return s.elapsed_time(e) / steps
+
+    g = torch.Generator(device=x.device).manual_seed(w.seed)
+    a8 = torch.randint(-127, 128, (w.M, w.K), dtype=torch.int8, device=x.device, generator=g)
+    b8 = torch.randint(-127, 128, (w.N, w.K), dtype=torch.int8, device=x.device, generator=g).t()
+    ms = clock(lambda: torch._int_mm(a8, b8))
+    out["int8_int_mm"] = {"ms": round(ms, 4), "TOPS": round(ops / (ms * 1e-3) / 1e12, 1),
+                          "note": "INT8 x INT8 -> int32, no block scales, no bias"}
+    del a8, b8
+    ms = clock(lambda: torch.nn.functional.linear(x, wt))
+    out["bf16_linear"] = {"ms": round(ms, 4), "TFLOPS": round(ops / (ms * 1e-3) / 1e12, 1)}
+    return out
+
+
 def main_linear(args, torch, sage, workloads):
     """The per-block W8A8 linear layer: one step = quantize X + GEMM."""
     w = workloads.get("linear")
@@ -485,6 +517,8 @@ def main_linear(args, torch, sage, workloads):
                      "GB_per_s": round(qbytes / (ms_quant * 1e-3) / 1e9, 1),
                      "hbm_frac": round(qbytes / (ms_quant * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
     }
+    if not args.profile:
+        record["library_gemms"] = library_gemms(torch, w, x, wt, steps, warm)
     if not (args.no_cpu or args.profile):
         from threadpoolctl import threadpool_info
         from oracle import w8a8
