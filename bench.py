@@ -430,9 +430,43 @@ def main():
         record["quantize"]["whole_cache_ms"] = round(ms_full_quant, 4)
     if others:
         record["other_pv_modes"] = others
+    if not args.profile:
+        ex = exact_attention(torch, w, q, k, v, steps, warm, ms_step)
+        if ex is not None:
+            record["exact_attention"] = ex
     if not args.no_cpu and not args.profile:
         record["cpu_baseline"], record["parity"] = cpu_leg(w, x, o, desc, args, sage, torch, ops)
     print(json.dumps(record), flush=True)
+
+
+def exact_attention(torch, w, q, k, v, steps, warm, ms_step):
+    """torch's fused exact attention (scaled_dot_product_attention with the
+    flash or memory-efficient backend only -- never the math path) on the
+    same 16-bit inputs: the operation this library stands in for, timed like
+    a step.  Full attention over every key only (no mask, cache or block
+    mask); else None."""
+    if w.frame_len or w.frame_stride or w.block_density or w.kv_len is not None:
+        return None
+    from torch.nn.attention import sdpa_kernel, SDPBackend
+    ops = w.ops()
+    try:
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION]):
+            fn = lambda: torch.nn.functional.scaled_dot_product_attention(q, k, v)  # noqa: E731
+            for _ in range(warm):
+                fn()
+            torch.cuda.synchronize()
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            for _ in range(steps):
+                fn()
+            e.record()
+            e.synchronize()
+            ms = s.elapsed_time(e) / steps
+    except RuntimeError as ex:
+        return {"error": str(ex)[:200]}
+    return {"kernel": "torch scaled_dot_product_attention (flash / memory-efficient backend)",
+            "ms": round(ms, 4), "TFLOPS": round(ops / (ms * 1e-3) / 1e12, 1),
+            "step_speedup": round(ms / ms_step, 3)}
 
 
 def library_gemms(torch, w, x, wt, steps, warm):
