@@ -50,7 +50,7 @@ class sage_quant_bufs(ctypes.Structure):
     _fields_ = [("q_codes", ctypes.c_void_p), ("q_scale", ctypes.c_void_p), ("k_codes", ctypes.c_void_p),
                 ("k_scale", ctypes.c_void_p), ("k_mean", ctypes.c_void_p), ("chan_shift", ctypes.c_void_p),
                 ("v_t", ctypes.c_void_p), ("v_e8m0", ctypes.c_void_p), ("stats", ctypes.c_void_p),
-                ("partial", ctypes.c_void_p), ("partial_splits", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("partial", ctypes.c_void_p), ("partial_splits", ctypes.c_int32), ("pv_layout", ctypes.c_int32)]
 
 
 class SageError(RuntimeError):

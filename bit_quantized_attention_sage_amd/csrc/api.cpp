@@ -252,7 +252,7 @@ sage_quant_bufs bufs_of(const Layout& L, const Plan& p, void* ws) {
   b.stats = base + L.stats;
   b.partial = p.splits_cap > 1 ? base + L.partial : nullptr;
   b.partial_splits = p.splits_cap > 1 ? p.splits_cap : 1;
-  b.reserved = 0;
+  b.pv_layout = p.pv_mode;
   return b;
 }
 
@@ -263,6 +263,9 @@ sage_status check_bufs(const sage_quant_bufs* b, const Plan& p, bool need_stats)
   if (p.pv_mode != SAGE_PV_16 && !b->v_e8m0) return fail(SAGE_E_NULL, "v_e8m0 is NULL in FP8 and AUTO modes");
   if ((need_stats || p.pv_mode == SAGE_PV_AUTO) && !b->stats)
     return fail(SAGE_E_NULL, need_stats ? "stats buffer is NULL" : "stats buffer is NULL (SAGE_PV_AUTO keeps its head lists there)");
+  if (p.pv_mode == SAGE_PV_AUTO && b->pv_layout != SAGE_PV_AUTO)
+    return fail(SAGE_E_WORKSPACE, "SAGE_PV_AUTO needs buffers carved for it (bufs->pv_layout " +
+                                      std::to_string(b->pv_layout) + ")");
   if (p.pv_mode == SAGE_PV_AUTO && (reinterpret_cast<uintptr_t>(b->stats) & 3u))
     return fail(SAGE_E_ALIGN, "stats must be 4-byte aligned");
   if (p.splits > 1 && !need_stats) {

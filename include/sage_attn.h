@@ -172,7 +172,10 @@ typedef struct sage_quant_bufs {
   int32_t partial_splits; /* KV splits `partial` holds room for (set by
                           sage_attn_quant_layout): a call whose split count
                           exceeds it fails with SAGE_E_WORKSPACE            */
-  int32_t reserved;    /* 0                                                   */
+  int32_t pv_layout;   /* pv_mode the buffers were carved for (set by
+                          sage_attn_quant_layout): a SAGE_PV_AUTO call needs
+                          SAGE_PV_AUTO here (its V slots and head lists are
+                          larger), else SAGE_E_WORKSPACE                     */
 } sage_quant_bufs;
 
 /* Version of the library's ABI (SAGE_ATTN_ABI_VERSION it was built with). */

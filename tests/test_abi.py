@@ -123,9 +123,19 @@ def test_per_head_mode_layout_and_validation(lib):
     L = sage.load()
     assert L.sage_attn_quant_layout(d.ptr, ctypes.c_void_p(fake), na, ctypes.byref(b)) == 0
     assert b.v_e8m0 and b.stats and b.v_e8m0 - b.v_t >= 2 * 2 * 384 * 128
+    assert b.pv_layout == sage.SAGE_PV_AUTO
     b.stats = None
     assert L.sage_attn_fwd_quantized(d.ptr, ctypes.byref(b), ctypes.c_void_p(fake), None) == 1
     assert "stats" in L.sage_attn_last_error().decode()
+    # buffers carved for a single P.V mode have smaller V slots and no head
+    # lists: a per-head call refuses them before anything is enqueued
+    d8 = _desc(pv_mode=sage.SAGE_PV_FP8)
+    b8 = sage.sage_quant_bufs()
+    assert L.sage_attn_quant_layout(d8.ptr, ctypes.c_void_p(fake), n8, ctypes.byref(b8)) == 0
+    assert b8.pv_layout == sage.SAGE_PV_FP8
+    assert L.sage_attn_fwd_quantized(d.ptr, ctypes.byref(b8), ctypes.c_void_p(fake), None) == 8
+    assert L.sage_attn_quantize(d.ptr, ctypes.c_void_p(fake), ctypes.c_void_p(fake), ctypes.c_void_p(fake),
+                                ctypes.byref(b8), None) == 8
     assert _status(_desc(pv_mode=sage.SAGE_PV_AUTO, frame_len=50, frame_stride=64, Nkv=320, Nq=50))[0] == 7
 
 
