@@ -25,8 +25,10 @@ def _rand(shape, seed):
     return torch.randn(shape, generator=g).to(torch.bfloat16).cuda()
 
 
-def _pair(B, H, Nq, Nkv, d, pv_mode, splits, seed, F=0, kv_len=None):
+def _pair(B, H, Nq, Nkv, d, pv_mode, splits, seed, F=0, kv_len=None, outlier_heads=()):
     q, k, v = _rand((B, H, Nq, d), seed), _rand((B, H, Nkv, d), seed + 1), _rand((B, H, Nkv, d), seed + 2)
+    for h in outlier_heads:                 # (per-head mode: those heads take 16-bit P.V)
+        k[:, h, :, 3] *= 8
     o_ref, o_na = torch.empty_like(q), torch.full_like(q, float("nan"))
     desc = sage.Desc.for_tensors(q, k, v, o_ref, pv_mode=pv_mode, kv_splits=splits, frame_len=F, kv_len=kv_len)
     assert sage.sage_attn_kv_splits(desc) == splits
@@ -46,12 +48,13 @@ def _pair(B, H, Nq, Nkv, d, pv_mode, splits, seed, F=0, kv_len=None):
     return o_ref, o_na
 
 
-@pytest.mark.parametrize("pv_mode", [0, 1], ids=["pv16", "pvfp8"])
+@pytest.mark.parametrize("pv_mode", [0, 1, 2], ids=["pv16", "pvfp8", "pvauto"])
 def test_noalloc_equals_workspace_entry_point(lib, pv_mode):
     # a streaming-sized call, then a smaller one: the second reads only what it wrote
-    o1, n1 = _pair(1, 24, 2040, 34680, 128, pv_mode, 4, 10 + pv_mode, F=2040, kv_len=[34680])
+    o1, n1 = _pair(1, 24, 2040, 34680, 128, pv_mode, 4, 10 + pv_mode, F=2040, kv_len=[34680],
+                   outlier_heads=(1, 5, 23))
     assert torch.equal(o1, n1)
-    o2, n2 = _pair(2, 3, 300, 2500, 64, pv_mode, 3, 20 + pv_mode)
+    o2, n2 = _pair(2, 3, 300, 2500, 64, pv_mode, 3, 20 + pv_mode, outlier_heads=(0,))
     assert torch.equal(o2, n2)
 
 
