@@ -20,6 +20,31 @@ def test_more_than_one_gpu_is_refused():
     assert "one GPU" in r.stderr and r.stdout == ""
 
 
+def test_mode_ceilings_and_quantize_bytes():
+    """Host arithmetic of the bench line: the MFMA ceiling of each P.V mode
+    (half the ops on INT8, half on the P.V type) and of the per-head mode at
+    a share f8 of FP8 heads, which reduces to the single modes at f8 = 0 and
+    1; the quantize pass's bytes likewise."""
+    sys.path.insert(0, ROOT)
+    import bench
+    import workloads
+    assert abs(bench.mode_peak(0) - 10000 / 3) < 1e-6 and abs(bench.mode_peak(1) - 5000) < 1e-6
+    assert abs(bench.mode_peak(2, 0.0) - bench.mode_peak(0)) < 1e-6
+    assert abs(bench.mode_peak(2, 1.0) - bench.mode_peak(1)) < 1e-6
+    f8 = 15 / 40   # time per op is the share-weighted sum of the two modes'
+    want = 1 / (f8 / 5000 + (1 - f8) * (0.5 / 5000 + 0.5 / 2500))
+    assert abs(bench.mode_peak(2, f8) - want) < 1e-6
+    assert bench.mode_peak(0) < bench.mode_peak(2, f8) < bench.mode_peak(1)
+    w = workloads.get("large")
+    for pv in (0, 1):
+        assert bench.quantize_bytes(w, 2, float(pv)) == bench.quantize_bytes(w, pv)
+    lo, mid, hi = (bench.quantize_bytes(w, 2, f)[0] for f in (0.0, f8, 1.0))
+    assert lo < mid < hi
+    # the minimum in 16-bit mode: K read twice, Q once, codes written
+    n = w.B * w.H * w.Nkv * w.d
+    assert lo == 2 * n + 2 * 2 * n + n + n
+
+
 @pytest.mark.gpu
 def test_bench_json_line(lib, capsys, monkeypatch):
     import bench
