@@ -125,3 +125,25 @@ def test_auto_many_heads(lib):
     assert all(aux["pv_modes"][b, h] == PV_16 for b, h, _ in outl)
     print(f"  16-bit heads: {int((aux['pv_modes'] == PV_16).sum())} of {B * H}", flush=True)
     assert_close(host(out), o64, aux, "f16", PV_AUTO)
+
+
+def test_auto_degenerate_heads(lib):
+    """Heads whose exponents are 0 by definition take FP8 P.V: Q = 0 (every
+    row's output is the mean of the visible V^ rows) and K constant along
+    the keys (K~ = 0: zero codes and scales); beside them one head with an
+    outlier channel (16-bit P.V) and one ordinary head (FP8)."""
+    B, H, N, d = 1, 4, 333, 128
+    q, k, v = _inputs(B, H, N, N, d, torch.bfloat16, 71, [(0, 2, 9)])
+    q[0, 0] = 0
+    k[0, 1] = k[0, 1, :1].expand(N, d)
+    out, views, desc, _, _ = run_gpu(q.cuda(), k.cuda(), v.cuda(), PV_AUTO)
+    Q, K, V = host(q), host(k), host(v)
+    check_quantized(views, Q, K, V, PV_AUTO, "bf16")
+    assert not views["k_codes"][0, 1].any()
+    o64, aux = emulate_like_gpu(Q, K, V, PV_AUTO, "bf16", desc)
+    np.testing.assert_array_equal(aux["pv_modes"], [[PV_FP8, PV_FP8, PV_16, PV_FP8]])
+    og = host(out)
+    assert_close(og, o64, aux, "bf16", PV_AUTO)
+    # Q = 0: every row is the mean of the (FP8-rounded) V rows
+    vhat = quant.dequant_v_fp8(*quant.quantize_v_fp8(V)[:2])[0, 0]
+    np.testing.assert_allclose(o64[0, 0], np.broadcast_to(vhat.mean(axis=0), (N, d)), rtol=0, atol=1e-12)
