@@ -6,15 +6,18 @@ that should see it, and requires that pin to fail: a dropped mask term, a
 truncation for a rounding, a mean over padding, a tie rule, an exponent
 rounded twice, the lazy-max threshold ignored, a reversed block index, the
 caller's softmax scale ignored, a block mask ignored, a sliding window one
-frame short or without its sink frames.  A pin that still
+frame short or without its sink frames, the per-head P.V rule inverted or
+blind to channels moved towards Q.  A pin that still
 passed would not be pinning anything."""
 
 import numpy as np
 import pytest
 
 from oracle import attention, codecs, emulate, quant, w8a8
+from oracle.constants import PV_16, PV_FP8
 
 import test_oracle_attention as TA
+import test_oracle_auto as TAUTO
 import test_oracle_codecs as TC
 import test_oracle_quant as TQ
 import test_oracle_sparse as TS
@@ -94,6 +97,12 @@ def _cases():
          TWIN.test_full_window_has_constant_frame_count, {}),
         ("sink frames ignored", attention, "frame_visible", sinks_ignored,
          TWIN.test_full_window_has_constant_frame_count, {}),
+        ("per-head P.V rule inverted", quant, "pv_modes_auto",
+         lambda a: np.where(np.all(np.asarray(a) == 0, axis=-1), PV_16, PV_FP8),
+         TAUTO.test_auto_is_each_head_in_its_own_mode, {}),
+        ("per-head P.V rule blind to channels moved towards Q", quant, "pv_modes_auto",
+         lambda a: np.where(np.all(np.asarray(a) <= 0, axis=-1), PV_FP8, PV_16),
+         TAUTO.test_rule_switches_at_the_exact_ratios, {}),
     ]
 
 
