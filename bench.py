@@ -293,6 +293,10 @@ def main():
         args.cpu_rows = 128 if w.block_density else 512
     if args.pv is not None:
         w.pv_mode = {v: k for k, v in PV_NAMES.items()}[args.pv]
+    if w.pv_mode == 2 and w.frame_stride:
+        print(f"bench.py: --pv auto needs contiguous keys; the {w.name} workload attends over a frame "
+              "cache (use --pv 16 or --pv fp8)", file=sys.stderr)
+        sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     x = workloads.make(w, dev)
