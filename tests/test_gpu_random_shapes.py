@@ -21,7 +21,7 @@ import torch
 
 import bit_quantized_attention_sage_amd as sage
 from oracle import emulate, attention
-from oracle.constants import PV_16, PV_FP8
+from oracle.constants import PV_16, PV_FP8, PV_AUTO
 from gpu_util import host, check_quantized, emulate_like_gpu, assert_close, cosine, KERNEL_SLACK
 
 pytestmark = pytest.mark.gpu
@@ -63,6 +63,20 @@ def case_id(c):
 
 
 CASES = [draw_case(i) for i in range(N_CASES)]
+
+
+def draw_auto_case(i):
+    """A random case in the per-head P.V mode, with a x8 K channel in about
+    half of the (b,h) pairs, so that both head lists are usually filled."""
+    c = draw_case(100 + i)
+    c["pv"] = PV_AUTO
+    rng = np.random.default_rng(9500 + i)
+    c["outliers"] = [(b, h, int(rng.integers(0, c["d"]))) for b in range(c["B"]) for h in range(c["H"])
+                     if rng.random() < 0.5]
+    return c
+
+
+AUTO_CASES = [draw_auto_case(i) for i in range(8)]
 TORCH_DT = {"bf16": torch.bfloat16, "f16": torch.float16}
 
 
@@ -70,7 +84,10 @@ def _inputs(c):
     g = torch.Generator().manual_seed(7100 + c["seed"])
     dt = TORCH_DT[c["dt"]]
     q = (torch.randn(c["B"], c["H"], c["Nq"], c["d"], generator=g) * c["qscale"]).to(dt)
-    k = (torch.randn(c["B"], c["H"], c["Nkv"], c["d"], generator=g) + 0.7).to(dt)
+    k = torch.randn(c["B"], c["H"], c["Nkv"], c["d"], generator=g) + 0.7
+    for b, h, ch in c.get("outliers", ()):
+        k[b, h, :, ch] *= 8
+    k = k.to(dt)
     v = torch.randn(c["B"], c["H"], c["Nkv"], c["d"], generator=g).to(dt)
     M = None
     if c["density"]:
@@ -105,7 +122,7 @@ def test_cases_are_varied():
     assert any(min(c["kv"]) < c["Nkv"] for c in CASES)
 
 
-@pytest.mark.parametrize("c", CASES, ids=[case_id(c) for c in CASES])
+@pytest.mark.parametrize("c", CASES + AUTO_CASES, ids=[case_id(c) for c in CASES + AUTO_CASES])
 def test_random_shape_parity(lib, c):
     print(f"random case {case_id(c)} kv {c['kv']} q_pos0 {c['qp']}", flush=True)
     q, k, v, M = _inputs(c)
