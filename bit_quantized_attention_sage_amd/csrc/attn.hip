@@ -653,8 +653,8 @@ __device__ __forceinline__ void dma_wait() { __builtin_amdgcn_s_waitcnt(0x0F70);
 // Decode a work item (batch by decreasing kv_len, head, split, query tile)
 // from a physical workgroup id: the tiles of one (b, h, split) share an XCD.
 // With a head list (PICK: per-head P.V mode) the items are those of the
-// listed heads, in list order; the launch has room for every head, and
-// workgroups past the list's items have nothing to do (pick_live).
+// listed heads, in list order; the launch has room for every head, and the
+// kernel returns at once in workgroups past the list's items.
 struct Item {
   int b, h, split, qt, bh;
   __device__ __forceinline__ Item(const AttnArgs& A, int ntile) {
